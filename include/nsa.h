@@ -1,0 +1,180 @@
+/*
+ * nsa.h — C ABI of the MI355X (gfx950) Native Sparse Attention forward pass.
+ *
+ * Native Sparse Attention runs three attention branches per query over one KV
+ * cache and mixes them with per-head gates:
+ *
+ *   o_t = g_cmp * Attn(q_t, compressed K/V) + g_slc * Attn(q_t, selected K/V)
+ *       + g_win * Attn(q_t, window K/V)
+ *
+ * Sources: lesson 5.5/02 "Разреженное внимание — NSA и DSA" (ai.flicky.cc),
+ * section "NSA: три ветви" (the output equation and the paragraphs on the
+ * compressed branch, the selection branch and the sliding window); lesson
+ * "Native Sparse Attention (DeepSeek NSA)" (AI Engineering from Scratch, phase
+ * 10 · 17), sections "Concept — three parallel branches" and "Build it".
+ *
+ * Conventions shared by every entry point
+ *  - bf16 tensors are passed as uint16_t bit patterns; gates are float32.
+ *  - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *    never allocates or frees device memory and never synchronises; all work is
+ *    enqueued on `stream` (a hipStream_t; NULL means the default stream) and the
+ *    pointers must stay valid until that work has finished.
+ *  - Arguments are validated on the host before anything is enqueued.  On any
+ *    error nothing is launched, outputs are untouched, and nsa_last_error()
+ *    (thread-local) describes the problem.  Device faults surface at the
+ *    caller's next synchronisation.
+ *  - Workspace: a caller-provided device buffer of at least the size the
+ *    matching *_workspace_size query returns.  It must be zero-filled once
+ *    before its first use; every call leaves its leading counter words at zero
+ *    again, so later calls need no clearing.  Calls that share a workspace must
+ *    not overlap in time.
+ *  - Query head h belongs to KV group g = h / G with G = num_q_heads /
+ *    num_kv_heads; all heads of a group select the same blocks (selection
+ *    paragraph of "NSA: три ветви").
+ *  - Supported set: (d_k, d_v) in {(64,64), (128,128), (192,128)}; 1 <= G <= 16;
+ *    d divides l and l'; l <= l'; l'/d a power of two; l' in {16,32,64,128};
+ *    1 <= n_sel <= 64; n_local + force_initial <= n_sel.  Anything else returns
+ *    NSA_ERROR_UNSUPPORTED.
+ */
+#ifndef NSA_H_
+#define NSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NSA_SUCCESS = 0,
+  NSA_ERROR_INVALID_VALUE = 1, /* null pointer, non-positive size, inconsistent shape */
+  NSA_ERROR_UNSUPPORTED = 2,   /* valid but outside the supported set above */
+  NSA_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  NSA_ERROR_HIP = 4            /* a HIP launch failed; message in nsa_last_error() */
+} nsa_status_t;
+
+/* NSA parameters ("NSA: три ветви": l=32, d=16, l'=64, n=16 incl. the initial
+ * and two local blocks, w=512). */
+typedef struct {
+  int32_t l;             /* compression block length (tokens per compressed key) */
+  int32_t d;             /* compression stride; blocks overlap when d < l */
+  int32_t l_sel;         /* selection block length l' */
+  int32_t n_sel;         /* blocks selected per (query, KV group), forced ones included */
+  int32_t n_local;       /* trailing blocks (the query's own and the ones before) always selected */
+  int32_t force_initial; /* 1: block 0 is always selected */
+  int32_t w;             /* sliding-window length: keys x with t - w < x <= t */
+  float softmax_scale;   /* 0 selects 1/sqrt(d_k) for all three branches */
+} nsa_config_t;
+
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t d_k;
+  int32_t d_v;
+} nsa_dims_t;
+
+/*
+ * nsa_compress_kv — token-block compression ("NSA: три ветви", compressed
+ * branch: blocks of l tokens with stride d, each folded by a learned MLP into
+ * one key and one value).  The MLP is one bias-free linear layer on the block
+ * plus a learned intra-block position embedding, flattened token-major:
+ *
+ *   k_cmp[i] = sum_{j<l} (K[i*d + j] + pe_k[j]) . w_k[j*d_k : (j+1)*d_k, :]
+ *
+ * and likewise for values with (w_v, pe_v).  Accumulates in fp32 and rounds the
+ * result to bf16 (round to nearest even).
+ *
+ *   k, v        bf16 caches.  Token x of sequence b, KV head g is row
+ *               Hkv*cu_seqlens[b] + g*cap_b + x of a [rows, d_k] (resp. d_v)
+ *               row-major array, cap_b = cu_seqlens[b+1] - cu_seqlens[b].
+ *               cu_seqlens == NULL means cap_b = max_len for every b
+ *               (i.e. the dense layout [B, Hkv, max_len, D]).
+ *   seq_lens    int32 [B] tokens present per sequence (device); NULL = cap_b.
+ *   max_len     host upper bound of every seq_lens[b] (and of cap_b).
+ *   w_k [l*d_k, d_k], pe_k [l, d_k], w_v [l*d_v, d_v], pe_v [l, d_v]: bf16.
+ *   k_cmp, v_cmp  outputs; block i of (b, g) is row Hkv*cu_cmp[b] + g*ccap_b + i,
+ *               ccap_b = cu_cmp[b+1] - cu_cmp[b]; cu_cmp == NULL means
+ *               ccap_b = floor((max_len - l)/d) + 1.  Blocks i < floor((L_b-l)/d)+1
+ *               (and i < ccap_b) are written; other rows are untouched.
+ */
+nsa_status_t nsa_compress_kv(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                             const uint16_t* k, const uint16_t* v,
+                             const int64_t* cu_seqlens, const int32_t* seq_lens, int64_t max_len,
+                             const uint16_t* w_k, const uint16_t* pe_k,
+                             const uint16_t* w_v, const uint16_t* pe_v,
+                             uint16_t* k_cmp, uint16_t* v_cmp, const int64_t* cu_cmp,
+                             void* stream);
+
+/*
+ * nsa_decode_fwd — one decode step: each sequence b has one query at position
+ * t = seq_lens[b] - 1 whose key/value are already in the cache.
+ *
+ *   q         bf16 [B, Hq, d_k]
+ *   k_cache, v_cache      bf16, layout of nsa_compress_kv's k/v (cu_seqlens,
+ *                         NULL = dense with capacity max_seq_len).
+ *   k_cmp_cache, v_cmp_cache  bf16 compressed cache, layout of nsa_compress_kv's
+ *                         outputs (cu_cmp); must hold the floor((L_b-l)/d)+1
+ *                         complete blocks of each sequence.
+ *   seq_lens  int32 [B] on the device, 1 <= seq_lens[b] <= cap_b.
+ *   max_seq_len  host upper bound of seq_lens (sizes the launch).
+ *   gates     float32 [B, Hq, 3] = (g_cmp, g_slc, g_win), used as given.
+ *   out       bf16 [B, Hq, d_v].
+ *   sel_idx_out  nullable int32 [B, Hkv, n_sel]: the selected block ids,
+ *             ascending, padded with -1 when fewer than n_sel blocks exist.
+ *
+ * Selection: candidates are blocks 0..J, J = floor(t/l'); block 0 (if
+ * force_initial) and J, J-1, ... (n_local of them) are always taken and count
+ * toward n_sel; the remaining slots take the highest group scores (compressed-
+ * branch probabilities folded onto l'-blocks by token overlap / l and summed
+ * over the group's heads), equal scores to the lower block id; if J+1 <= n_sel
+ * all candidates are taken.
+ */
+nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                            const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const uint16_t* k_cmp_cache, const uint16_t* v_cmp_cache,
+                            const int32_t* seq_lens, const int64_t* cu_seqlens, const int64_t* cu_cmp,
+                            int64_t max_seq_len, const float* gates, uint16_t* out,
+                            int32_t* sel_idx_out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * nsa_prefill_fwd — causal prefill of B sequences of seq_len tokens each: every
+ * position t attends per the three branches (compressed blocks whose last token
+ * is <= t; the selected blocks' tokens <= t; the window t-w < x <= t).
+ *
+ *   q      bf16 [B, T, Hq, d_k]
+ *   k, v   bf16 [B, Hkv, T, d_k] and [B, Hkv, T, d_v]
+ *   k_cmp, v_cmp  bf16 [B, Hkv, floor((T-l)/d)+1, D] precomputed compressed
+ *          cache, or both NULL to compress in the call from (w_k, pe_k, w_v,
+ *          pe_v) into the workspace (the weights are ignored otherwise).
+ *   gates  float32 [B, T, Hq, 3]
+ *   out    bf16 [B, T, Hq, d_v]
+ *   sel_idx_out  nullable int32 [B, T, Hkv, n_sel], ascending, -1 padded.
+ */
+nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
+                             const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* k_cmp, const uint16_t* v_cmp,
+                             const uint16_t* w_k, const uint16_t* pe_k,
+                             const uint16_t* w_v, const uint16_t* pe_v,
+                             const float* gates, uint16_t* out, int32_t* sel_idx_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by nsa_decode_fwd / nsa_prefill_fwd for these sizes
+ * (host-only; no device call).  `compress_in_call` = 1 when k_cmp/v_cmp will be
+ * NULL.  Returns NSA_SUCCESS and writes *bytes, or a validation error. */
+nsa_status_t nsa_decode_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                                       int64_t max_seq_len, size_t* bytes);
+nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                                        int64_t seq_len, int32_t compress_in_call, size_t* bytes);
+
+/* Human-readable name of a status code (static storage). */
+const char* nsa_status_string(nsa_status_t status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* nsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NSA_H_ */

@@ -1,0 +1,27 @@
+"""MI355X (gfx950) Native Sparse Attention forward pass.
+
+The compute lives in libnsa.so (hand-written HIP kernels behind the C ABI of
+include/nsa.h); this package only marshals torch tensors into that ABI.
+"""
+from ._abi import (  # noqa: F401
+    EXPORTS,
+    NSAError,
+    compressed_count,
+    lib_path,
+    load_library,
+    make_config,
+    make_dims,
+    new_workspace,
+    nsa_compress_kv,
+    nsa_config_t,
+    nsa_decode_fwd,
+    nsa_decode_workspace_size,
+    nsa_dims_t,
+    nsa_last_error,
+    nsa_prefill_fwd,
+    nsa_prefill_workspace_size,
+    nsa_status_string,
+)
+
+__all__ = [n for n in dir() if n.startswith("nsa_")] + ["NSAError", "load_library", "make_config", "make_dims",
+                                                        "new_workspace", "compressed_count", "EXPORTS"]

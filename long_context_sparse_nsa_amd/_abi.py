@@ -1,0 +1,192 @@
+"""ctypes binding of libnsa.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/nsa.h)
+and takes torch tensors where the C function takes device pointers.  Nothing is
+computed in Python; a missing library raises instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+NSA_SUCCESS = 0
+NSA_ERROR_INVALID_VALUE = 1
+NSA_ERROR_UNSUPPORTED = 2
+NSA_ERROR_WORKSPACE = 3
+NSA_ERROR_HIP = 4
+
+
+class NSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+class nsa_config_t(ctypes.Structure):
+    _fields_ = [("l", ctypes.c_int32), ("d", ctypes.c_int32), ("l_sel", ctypes.c_int32),
+                ("n_sel", ctypes.c_int32), ("n_local", ctypes.c_int32), ("force_initial", ctypes.c_int32),
+                ("w", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class nsa_dims_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+def make_config(l, d, l_sel, n_sel, n_local, force_initial, w, softmax_scale=0.0) -> nsa_config_t:
+    return nsa_config_t(l, d, l_sel, n_sel, n_local, force_initial, w, softmax_scale)
+
+
+def make_dims(batch, num_q_heads, num_kv_heads, d_k, d_v) -> nsa_dims_t:
+    return nsa_dims_t(batch, num_q_heads, num_kv_heads, d_k, d_v)
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libnsa.so")
+
+
+_VP = ctypes.c_void_p
+_SIGS = {
+    "nsa_compress_kv": [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "nsa_decode_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP,
+                       ctypes.c_size_t, _VP],
+    "nsa_prefill_fwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                        _VP, ctypes.c_size_t, _VP],
+    "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
+    "nsa_prefill_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "nsa_status_string": [ctypes.c_int],
+    "nsa_last_error": [],
+}
+EXPORTS = tuple(_SIGS)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libnsa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        p = lib_path()
+        if not os.path.exists(p):
+            raise RuntimeError(f"NSA HIP library not found at {p}; build it with "
+                               "`python -m long_context_sparse_nsa_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, args in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name in ("nsa_status_string", "nsa_last_error") else ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def status_name(status: int) -> str:
+    return load_library().nsa_status_string(int(status)).decode()
+
+
+def nsa_status_string(status: int) -> str:
+    return status_name(status)
+
+
+def nsa_last_error() -> str:
+    return load_library().nsa_last_error().decode()
+
+
+def _check(status: int):
+    if status != NSA_SUCCESS:
+        raise NSAError(status, nsa_last_error())
+
+
+_ITEM = {torch.bfloat16: 2, torch.int16: 2, torch.uint16: 2, torch.float32: 4, torch.int32: 4, torch.int64: 8,
+         torch.uint8: 1}
+
+
+def _ptr(t: Optional[torch.Tensor], what: str, itemsize: Optional[int] = None, numel: Optional[int] = None):
+    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if itemsize is not None and _ITEM.get(t.dtype) != itemsize:
+        raise ValueError(f"{what}: element size must be {itemsize} bytes (got {t.dtype})")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{what}: needs at least {numel} elements, has {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> Optional[ctypes.c_void_p]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def nsa_decode_workspace_size(dims: nsa_dims_t, cfg: nsa_config_t, max_seq_len: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().nsa_decode_workspace_size(ctypes.byref(dims), ctypes.byref(cfg), int(max_seq_len),
+                                                    ctypes.byref(out)))
+    return int(out.value)
+
+
+def nsa_prefill_workspace_size(dims: nsa_dims_t, cfg: nsa_config_t, seq_len: int, compress_in_call: bool) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().nsa_prefill_workspace_size(ctypes.byref(dims), ctypes.byref(cfg), int(seq_len),
+                                                     int(bool(compress_in_call)), ctypes.byref(out)))
+    return int(out.value)
+
+
+def nsa_compress_kv(dims, cfg, k, v, cu_seqlens, seq_lens, max_len, w_k, pe_k, w_v, pe_v, k_cmp, v_cmp, cu_cmp,
+                    stream=None):
+    lib = load_library()
+    _check(lib.nsa_compress_kv(ctypes.byref(dims), ctypes.byref(cfg), _ptr(k, "k", 2), _ptr(v, "v", 2),
+                               _ptr(cu_seqlens, "cu_seqlens", 8), _ptr(seq_lens, "seq_lens", 4), int(max_len),
+                               _ptr(w_k, "w_k", 2), _ptr(pe_k, "pe_k", 2), _ptr(w_v, "w_v", 2), _ptr(pe_v, "pe_v", 2),
+                               _ptr(k_cmp, "k_cmp", 2), _ptr(v_cmp, "v_cmp", 2), _ptr(cu_cmp, "cu_cmp", 8),
+                               _stream(stream)))
+
+
+def nsa_decode_fwd(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, cu_seqlens, cu_cmp,
+                   max_seq_len, gates, out, sel_idx_out, workspace, stream=None):
+    lib = load_library()
+    B, Hq, H = dims.batch, dims.num_q_heads, dims.num_kv_heads
+    _check(lib.nsa_decode_fwd(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q, "q", 2, B * Hq * dims.d_k),
+                              _ptr(k_cache, "k_cache", 2), _ptr(v_cache, "v_cache", 2),
+                              _ptr(k_cmp_cache, "k_cmp_cache", 2), _ptr(v_cmp_cache, "v_cmp_cache", 2),
+                              _ptr(seq_lens, "seq_lens", 4, B), _ptr(cu_seqlens, "cu_seqlens", 8, B + 1),
+                              _ptr(cu_cmp, "cu_cmp", 8, B + 1), int(max_seq_len),
+                              _ptr(gates, "gates", 4, B * Hq * 3), _ptr(out, "out", 2, B * Hq * dims.d_v),
+                              _ptr(sel_idx_out, "sel_idx_out", 4, B * H * cfg.n_sel),
+                              _ptr(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                              _stream(stream)))
+
+
+def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, pe_v, gates, out, sel_idx_out,
+                    workspace, stream=None):
+    lib = load_library()
+    B, Hq, H, T = dims.batch, dims.num_q_heads, dims.num_kv_heads, int(seq_len)
+    _check(lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), T, _ptr(q, "q", 2, B * T * Hq * dims.d_k),
+                               _ptr(k, "k", 2, B * H * T * dims.d_k), _ptr(v, "v", 2, B * H * T * dims.d_v),
+                               _ptr(k_cmp, "k_cmp", 2), _ptr(v_cmp, "v_cmp", 2),
+                               _ptr(w_k, "w_k", 2), _ptr(pe_k, "pe_k", 2), _ptr(w_v, "w_v", 2), _ptr(pe_v, "pe_v", 2),
+                               _ptr(gates, "gates", 4, B * T * Hq * 3), _ptr(out, "out", 2, B * T * Hq * dims.d_v),
+                               _ptr(sel_idx_out, "sel_idx_out", 4, B * T * H * cfg.n_sel),
+                               _ptr(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                               _stream(stream)))
+
+
+def compressed_count(L: int, l: int, d: int) -> int:
+    """Complete compression blocks among L tokens (buffer sizing for callers)."""
+    return (L - l) // d + 1 if L >= l else 0
+
+
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace buffer (the zero fill is required once before first use)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)

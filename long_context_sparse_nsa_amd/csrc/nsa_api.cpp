@@ -1,0 +1,318 @@
+// C ABI of the NSA forward pass: argument validation (host only, before any
+// HIP call), workspace planning and kernel launches on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/nsa.h"
+#include "nsa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nsa_status_t fail(nsa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+nsa_status_t fail(nsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+nsa_status_t ok() {
+  g_last_error.clear();
+  return NSA_SUCCESS;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int64_t n_compressed(int64_t L, int l, int d) { return L >= l ? (L - l) / d + 1 : 0; }
+
+// Checks shared by every entry point.
+nsa_status_t check_common(const nsa_dims_t* dims, const nsa_config_t* cfg, bool need_cfg) {
+  if (!dims) return fail(NSA_ERROR_INVALID_VALUE, "dims is NULL");
+  if (need_cfg && !cfg) return fail(NSA_ERROR_INVALID_VALUE, "cfg is NULL");
+  if (dims->batch < 1 || dims->num_q_heads < 1 || dims->num_kv_heads < 1 || dims->d_k < 1 || dims->d_v < 1)
+    return fail(NSA_ERROR_INVALID_VALUE, "dims must be positive (batch=%d, q_heads=%d, kv_heads=%d, d_k=%d, d_v=%d)",
+                dims->batch, dims->num_q_heads, dims->num_kv_heads, dims->d_k, dims->d_v);
+  if (dims->num_q_heads % dims->num_kv_heads != 0)
+    return fail(NSA_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                dims->num_q_heads, dims->num_kv_heads);
+  const int G = dims->num_q_heads / dims->num_kv_heads;
+  if (G > nsa::kGPad) return fail(NSA_ERROR_UNSUPPORTED, "group size %d > 16 query heads per KV head", G);
+  const int dk = dims->d_k, dv = dims->d_v;
+  if (!((dk == 64 && dv == 64) || (dk == 128 && dv == 128) || (dk == 192 && dv == 128)))
+    return fail(NSA_ERROR_UNSUPPORTED, "(d_k, d_v) = (%d, %d) not in {(64,64), (128,128), (192,128)}", dk, dv);
+  if (!cfg) return NSA_SUCCESS;
+  if (cfg->l < 1 || cfg->d < 1 || cfg->l_sel < 1 || cfg->n_sel < 1 || cfg->n_local < 0 ||
+      (cfg->force_initial != 0 && cfg->force_initial != 1) || cfg->w < 1)
+    return fail(NSA_ERROR_INVALID_VALUE,
+                "bad NSA parameters (l=%d, d=%d, l_sel=%d, n_sel=%d, n_local=%d, force_initial=%d, w=%d)", cfg->l,
+                cfg->d, cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->force_initial, cfg->w);
+  if (!(cfg->softmax_scale >= 0.f) || !std::isfinite(cfg->softmax_scale))
+    return fail(NSA_ERROR_INVALID_VALUE, "softmax_scale must be finite and >= 0");
+  if (cfg->l % cfg->d != 0 || cfg->l_sel % cfg->d != 0 || cfg->l > cfg->l_sel || !is_pow2(cfg->l_sel / cfg->d))
+    return fail(NSA_ERROR_UNSUPPORTED, "need d | l, d | l_sel, l <= l_sel and l_sel/d a power of two (l=%d d=%d l_sel=%d)",
+                cfg->l, cfg->d, cfg->l_sel);
+  if (cfg->l_sel != 16 && cfg->l_sel != 32 && cfg->l_sel != 64 && cfg->l_sel != 128)
+    return fail(NSA_ERROR_UNSUPPORTED, "l_sel=%d not in {16, 32, 64, 128}", cfg->l_sel);
+  if (cfg->n_sel > nsa::kMaxSel) return fail(NSA_ERROR_UNSUPPORTED, "n_sel=%d > %d", cfg->n_sel, nsa::kMaxSel);
+  if (cfg->n_local + cfg->force_initial > cfg->n_sel)
+    return fail(NSA_ERROR_UNSUPPORTED, "n_local + force_initial (%d) > n_sel (%d)", cfg->n_local + cfg->force_initial,
+                cfg->n_sel);
+  if ((int64_t)cfg->n_sel + (cfg->w + cfg->l_sel - 1) / cfg->l_sel + 1 > nsa::kMaxUnion)
+    return fail(NSA_ERROR_UNSUPPORTED, "n_sel + window blocks exceeds %d", nsa::kMaxUnion);
+  return NSA_SUCCESS;
+}
+
+float scale_log2(const nsa_dims_t* dims, const nsa_config_t* cfg) {
+  const float s = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / std::sqrt((float)dims->d_k);
+  return s * 1.4426950408889634f;
+}
+
+nsa_status_t check_decode_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t max_seq_len) {
+  if (max_seq_len < 1) return fail(NSA_ERROR_INVALID_VALUE, "max_seq_len must be >= 1");
+  if ((max_seq_len - 1) / cfg->l_sel + 1 > nsa::kMaxBlocks)
+    return fail(NSA_ERROR_UNSUPPORTED, "max_seq_len %lld gives more than %d selection blocks", (long long)max_seq_len,
+                nsa::kMaxBlocks);
+  const int64_t nc = n_compressed(max_seq_len, cfg->l, cfg->d);
+  if ((nc + nsa::kChunk - 1) / nsa::kChunk > nsa::kMaxChunks)
+    return fail(NSA_ERROR_UNSUPPORTED, "max_seq_len %lld gives more than %d compressed blocks", (long long)max_seq_len,
+                nsa::kMaxChunks * nsa::kChunk);
+  if ((int64_t)dims->batch * dims->num_kv_heads * ((nc + nsa::kChunk - 1) / nsa::kChunk + 1) > (int64_t)INT32_MAX / 2)
+    return fail(NSA_ERROR_UNSUPPORTED, "launch too large");
+  return NSA_SUCCESS;
+}
+
+constexpr int kPfMaxSlices = 64, kPfMaxSlots = 72, kPfMaxBlocks = 4096;
+
+nsa_status_t check_prefill_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
+  if (T < 1) return fail(NSA_ERROR_INVALID_VALUE, "seq_len must be >= 1");
+  const int64_t nc = n_compressed(T, cfg->l, cfg->d);
+  if ((nc + 63) / 64 > kPfMaxSlices)
+    return fail(NSA_ERROR_UNSUPPORTED, "prefill supports at most %d compressed blocks (got %lld)", kPfMaxSlices * 64,
+                (long long)nc);
+  if ((T - 1) / cfg->l_sel + 1 > kPfMaxBlocks)
+    return fail(NSA_ERROR_UNSUPPORTED, "prefill supports at most %d selection blocks", kPfMaxBlocks);
+  if ((63 * cfg->d + cfg->l - 1) / cfg->l_sel + 2 > kPfMaxSlots)
+    return fail(NSA_ERROR_UNSUPPORTED, "compression stride too large for the prefill fold");
+  if ((int64_t)dims->batch * dims->num_kv_heads * T > (int64_t)INT32_MAX)
+    return fail(NSA_ERROR_UNSUPPORTED, "batch * kv_heads * seq_len too large");
+  return NSA_SUCCESS;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t prefill_ws_bytes(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, bool compress) {
+  if (!compress) return 0;
+  const int64_t nc = n_compressed(T, cfg->l, cfg->d);
+  const size_t rows = (size_t)dims->batch * dims->num_kv_heads * (size_t)nc;
+  return align256(rows * dims->d_k * 2) + align256(rows * dims->d_v * 2);
+}
+
+nsa_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(NSA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nsa_status_string(nsa_status_t s) {
+  switch (s) {
+    case NSA_SUCCESS: return "NSA_SUCCESS";
+    case NSA_ERROR_INVALID_VALUE: return "NSA_ERROR_INVALID_VALUE";
+    case NSA_ERROR_UNSUPPORTED: return "NSA_ERROR_UNSUPPORTED";
+    case NSA_ERROR_WORKSPACE: return "NSA_ERROR_WORKSPACE";
+    case NSA_ERROR_HIP: return "NSA_ERROR_HIP";
+  }
+  return "NSA_UNKNOWN_STATUS";
+}
+
+const char* nsa_last_error(void) { return g_last_error.c_str(); }
+
+nsa_status_t nsa_decode_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t max_seq_len,
+                                       size_t* bytes) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
+  if ((st = check_decode_sizes(dims, cfg, max_seq_len)) != NSA_SUCCESS) return st;
+  *bytes = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d, cfg->l_sel, cfg->n_sel,
+                              cfg->w, max_seq_len)
+               .total;
+  return ok();
+}
+
+nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
+                                        int32_t compress_in_call, size_t* bytes) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
+  if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
+  *bytes = prefill_ws_bytes(dims, cfg, seq_len, compress_in_call != 0);
+  return ok();
+}
+
+nsa_status_t nsa_compress_kv(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* k, const uint16_t* v,
+                             const int64_t* cu_seqlens, const int32_t* seq_lens, int64_t max_len,
+                             const uint16_t* w_k, const uint16_t* pe_k, const uint16_t* w_v, const uint16_t* pe_v,
+                             uint16_t* k_cmp, uint16_t* v_cmp, const int64_t* cu_cmp, void* stream) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!k || !v || !w_k || !pe_k || !w_v || !pe_v || !k_cmp || !v_cmp)
+    return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if (max_len < 1) return fail(NSA_ERROR_INVALID_VALUE, "max_len must be >= 1");
+  const int64_t nc = n_compressed(max_len, cfg->l, cfg->d);
+  if ((nc + 63) / 64 > 65535 || (int64_t)dims->batch * dims->num_kv_heads > 65535)
+    return fail(NSA_ERROR_UNSUPPORTED, "compression launch too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int which = 0; which < 2; ++which) {
+    nsa::CompressParams p{};
+    p.B = dims->batch;
+    p.H = dims->num_kv_heads;
+    p.D = which == 0 ? dims->d_k : dims->d_v;
+    p.l = cfg->l;
+    p.d = cfg->d;
+    p.x = which == 0 ? k : v;
+    p.cu = cu_seqlens;
+    p.seq_lens = seq_lens;
+    p.cap = max_len;
+    p.w = which == 0 ? w_k : w_v;
+    p.pe = which == 0 ? pe_k : pe_v;
+    p.y = which == 0 ? k_cmp : v_cmp;
+    p.cuc = cu_cmp;
+    p.ccap = nc;
+    p.max_nc = (int)nc;
+    hipError_t e = nsa::launch_compress(p, s);
+    if (e != hipSuccess) return hip_fail(e, "compression launch");
+  }
+  return ok();
+}
+
+nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* q,
+                            const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_cmp_cache,
+                            const uint16_t* v_cmp_cache, const int32_t* seq_lens, const int64_t* cu_seqlens,
+                            const int64_t* cu_cmp, int64_t max_seq_len, const float* gates, uint16_t* out,
+                            int32_t* sel_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!q || !k_cache || !v_cache || !k_cmp_cache || !v_cmp_cache || !seq_lens || !gates || !out)
+    return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if ((st = check_decode_sizes(dims, cfg, max_seq_len)) != NSA_SUCCESS) return st;
+  const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
+                                                   cfg->l_sel, cfg->n_sel, cfg->w, max_seq_len);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  nsa::DecodeParams p{};
+  p.B = dims->batch;
+  p.Hq = dims->num_q_heads;
+  p.H = dims->num_kv_heads;
+  p.G = p.Hq / p.H;
+  p.l = cfg->l;
+  p.d = cfg->d;
+  p.lsel = cfg->l_sel;
+  p.n = cfg->n_sel;
+  p.nloc = cfg->n_local;
+  p.finit = cfg->force_initial;
+  p.w = cfg->w;
+  p.scale_log2 = scale_log2(dims, cfg);
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.kc = k_cmp_cache;
+  p.vc = v_cmp_cache;
+  p.seq_lens = seq_lens;
+  p.cu = cu_seqlens;
+  p.cuc = cu_cmp;
+  p.cap = max_seq_len;
+  p.ccap = n_compressed(max_seq_len, cfg->l, cfg->d);
+  p.gates = gates;
+  p.out = out;
+  p.sel_out = sel_idx_out;
+  p.cnt1 = reinterpret_cast<uint32_t*>(ws + lay.off_cnt1);
+  p.cnt2 = reinterpret_cast<uint32_t*>(ws + lay.off_cnt2);
+  p.m1 = reinterpret_cast<float*>(ws + lay.off_m1);
+  p.l1 = reinterpret_cast<float*>(ws + lay.off_l1);
+  p.o1 = reinterpret_cast<float*>(ws + lay.off_o1);
+  p.sc1 = reinterpret_cast<float*>(ws + lay.off_sc1);
+  p.ocmp = reinterpret_cast<float*>(ws + lay.off_ocmp);
+  p.sel = reinterpret_cast<int32_t*>(ws + lay.off_sel);
+  p.part2 = reinterpret_cast<float*>(ws + lay.off_part2);
+  p.nch = lay.nch;
+  p.nbo = lay.nbo;
+  p.nw2 = lay.nw2;
+  hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len, const uint16_t* q,
+                             const uint16_t* k, const uint16_t* v, const uint16_t* k_cmp, const uint16_t* v_cmp,
+                             const uint16_t* w_k, const uint16_t* pe_k, const uint16_t* w_v, const uint16_t* pe_v,
+                             const float* gates, uint16_t* out, int32_t* sel_idx_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!q || !k || !v || !gates || !out) return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if ((k_cmp == nullptr) != (v_cmp == nullptr))
+    return fail(NSA_ERROR_INVALID_VALUE, "k_cmp and v_cmp must both be given or both be NULL");
+  const bool compress = k_cmp == nullptr;
+  if (compress && (!w_k || !pe_k || !w_v || !pe_v))
+    return fail(NSA_ERROR_INVALID_VALUE, "compression weights are NULL and no compressed cache was given");
+  if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
+  const size_t need = prefill_ws_bytes(dims, cfg, seq_len, compress);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nc = n_compressed(seq_len, cfg->l, cfg->d);
+  if (compress && nc == 0) {
+    k_cmp = k;  // no complete compressed block exists; the cache is never read
+    v_cmp = v;
+  } else if (compress) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t rows = (size_t)dims->batch * dims->num_kv_heads * (size_t)nc;
+    uint16_t* kcw = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* vcw = reinterpret_cast<uint16_t*>(ws + align256(rows * dims->d_k * 2));
+    st = nsa_compress_kv(dims, cfg, k, v, nullptr, nullptr, seq_len, w_k, pe_k, w_v, pe_v, kcw, vcw, nullptr, stream);
+    if (st != NSA_SUCCESS) return st;
+    k_cmp = kcw;
+    v_cmp = vcw;
+  }
+  nsa::PrefillParams p{};
+  p.B = dims->batch;
+  p.T = (int)seq_len;
+  p.Hq = dims->num_q_heads;
+  p.H = dims->num_kv_heads;
+  p.G = p.Hq / p.H;
+  p.l = cfg->l;
+  p.d = cfg->d;
+  p.lsel = cfg->l_sel;
+  p.n = cfg->n_sel;
+  p.nloc = cfg->n_local;
+  p.finit = cfg->force_initial;
+  p.w = cfg->w;
+  p.scale_log2 = scale_log2(dims, cfg);
+  p.nc = (int)nc;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.kc = k_cmp;
+  p.vc = v_cmp;
+  p.gates = gates;
+  p.out = out;
+  p.sel_out = sel_idx_out;
+  hipError_t e = nsa::launch_prefill(p, dims->d_k, dims->d_v, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+}  // extern "C"

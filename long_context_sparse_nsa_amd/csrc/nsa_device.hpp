@@ -1,0 +1,93 @@
+// Device helpers shared by the NSA kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA tile conventions used throughout (v_mfma_f32_16x16x32_bf16):
+//   lane l, lg = l / 16 (k-slot group), lr = l % 16
+//   A operand (16 x 32): row lr, eight k-slots of group lg
+//   B operand (32 x 16): column lr, the same eight k-slots of group lg
+//   D (16 x 16 fp32):    element i (0..3) is row 4*lg + i, column lr
+// Only the pairing of A and B k-slots matters for the product, so the kernels
+// choose whichever key/channel order makes the global loads contiguous.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+typedef short bf16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Global loads of 16 / 8 bytes.  Every caller proves the address in bounds
+// before calling; out-of-range rows are replaced by zeros at the call site.
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x2_t ld8(const uint16_t* p) {
+  return *reinterpret_cast<const u32x2_t*>(p);
+}
+
+// Cross-lane reductions over the four lane groups (lanes lr, lr+16, lr+32, lr+48).
+__device__ __forceinline__ float max_over_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Select 16-bit half `h` (0 low, 1 high) of a and b and pack as (a_h | b_h << 16).
+__device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int h) {
+  return h ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+}
+
+// Exclusive prefix sum over the 256 threads of a block (4 waves).  `scratch`
+// holds at least 4 ints in LDS.  Returns the exclusive prefix; *total gets the sum.
+__device__ __forceinline__ int block_scan_256(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int s = scratch[w];
+    if (w < wave) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+}  // namespace nsa

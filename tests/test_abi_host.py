@@ -1,0 +1,138 @@
+"""Host-only checks of the C ABI: the library loads, exports what include/nsa.h
+declares, and rejects invalid arguments before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_nsa_amd as N
+from long_context_sparse_nsa_amd import _abi as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsa.h")
+
+lib_missing = not os.path.exists(A.lib_path())
+pytestmark = pytest.mark.skipif(lib_missing, reason="libnsa.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    fns = declared_functions()
+    for name in ("nsa_compress_kv", "nsa_prefill_fwd", "nsa_decode_fwd", "nsa_decode_workspace_size",
+                 "nsa_prefill_workspace_size", "nsa_status_string", "nsa_last_error"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(A.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(A.EXPORTS)
+
+
+def test_status_strings():
+    assert N.nsa_status_string(0) == "NSA_SUCCESS"
+    assert N.nsa_status_string(3) == "NSA_ERROR_WORKSPACE"
+
+
+STD = dict(l=32, d=16, l_sel=64, n_sel=16, n_local=2, force_initial=1, w=512)
+
+
+def _cfg(**kw):
+    a = dict(STD)
+    a.update(kw)
+    return N.make_config(**a)
+
+
+def _dims(**kw):
+    a = dict(batch=8, num_q_heads=64, num_kv_heads=4, d_k=192, d_v=128)
+    a.update(kw)
+    return N.make_dims(**a)
+
+
+def _ws(dims, cfg, L=65536):
+    return N.nsa_decode_workspace_size(dims, cfg, L)
+
+
+def test_workspace_sizes_are_positive_and_monotone():
+    a = _ws(_dims(), _cfg(), 4096)
+    b = _ws(_dims(), _cfg(), 65536)
+    c = _ws(_dims(batch=16), _cfg(), 65536)
+    assert 0 < a < b < c
+    assert N.nsa_prefill_workspace_size(_dims(batch=1), _cfg(), 32768, False) == 0
+    assert N.nsa_prefill_workspace_size(_dims(batch=1), _cfg(), 32768, True) >= 4 * 2047 * (192 + 128) * 2
+
+
+@pytest.mark.parametrize("dims_kw,cfg_kw,L,status", [
+    (dict(num_q_heads=63), {}, 100, A.NSA_ERROR_INVALID_VALUE),
+    (dict(batch=0), {}, 100, A.NSA_ERROR_INVALID_VALUE),
+    (dict(d_k=100), {}, 100, A.NSA_ERROR_UNSUPPORTED),
+    (dict(num_q_heads=128), {}, 100, A.NSA_ERROR_UNSUPPORTED),        # group of 32 heads
+    ({}, dict(d=0), 100, A.NSA_ERROR_INVALID_VALUE),
+    ({}, dict(force_initial=2), 100, A.NSA_ERROR_INVALID_VALUE),
+    ({}, dict(l=24), 100, A.NSA_ERROR_UNSUPPORTED),                    # l_sel/d=4 ok, d does not divide l? 24%16
+    ({}, dict(l=128), 100, A.NSA_ERROR_UNSUPPORTED),                   # l > l_sel
+    ({}, dict(l_sel=48, d=16), 100, A.NSA_ERROR_UNSUPPORTED),          # l_sel/d = 3
+    ({}, dict(n_sel=65), 100, A.NSA_ERROR_UNSUPPORTED),
+    ({}, dict(n_sel=2, n_local=2), 100, A.NSA_ERROR_UNSUPPORTED),      # forced blocks exceed n
+    ({}, {}, 0, A.NSA_ERROR_INVALID_VALUE),
+    ({}, {}, 64 * 8192 + 1, A.NSA_ERROR_UNSUPPORTED),                  # too many selection blocks
+])
+def test_validation_errors(dims_kw, cfg_kw, L, status):
+    with pytest.raises(N.NSAError) as e:
+        _ws(_dims(**dims_kw), _cfg(**cfg_kw), L)
+    assert e.value.status == status
+    assert N.nsa_last_error() != ""
+
+
+def _raw_decode(dims, cfg, ptr, L, ws, ws_bytes):
+    lib = A.load_library()
+    return lib.nsa_decode_fwd(ctypes.byref(dims), ctypes.byref(cfg), ptr, ptr, ptr, ptr, ptr, ptr, None, None,
+                              L, ptr, ptr, None, ws, ws_bytes, None)
+
+
+def test_decode_rejects_null_tensor_and_small_workspace_without_launching():
+    dims, cfg = _dims(), _cfg()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    lib = A.load_library()
+    st = lib.nsa_decode_fwd(ctypes.byref(dims), ctypes.byref(cfg), None, fake, fake, fake, fake, fake, None, None,
+                            65536, fake, fake, None, fake, 1 << 30, None)
+    assert st == A.NSA_ERROR_INVALID_VALUE and "NULL" in N.nsa_last_error()
+    need = _ws(dims, cfg, 65536)
+    assert _raw_decode(dims, cfg, fake, 65536, fake, need - 1) == A.NSA_ERROR_WORKSPACE
+    assert _raw_decode(dims, cfg, fake, 65536, None, need) == A.NSA_ERROR_WORKSPACE
+    assert str(need) in N.nsa_last_error()
+
+
+def test_prefill_rejects_half_given_cache_and_missing_weights():
+    lib = A.load_library()
+    dims, cfg = _dims(batch=1), _cfg()
+    f = ctypes.c_void_p(0x1000)
+    st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, f, None, f, f, f, f, f, f, None,
+                             f, 1 << 30, None)
+    assert st == A.NSA_ERROR_INVALID_VALUE
+    st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, None, None, None, f, f, f, f, f,
+                             None, f, 1 << 30, None)
+    assert st == A.NSA_ERROR_INVALID_VALUE
+    st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 70000, f, f, f, f, f, None, None, None, None, f,
+                             f, None, None, 0, None)
+    assert st == A.NSA_ERROR_UNSUPPORTED
+
+
+def test_null_dims_and_config():
+    lib = A.load_library()
+    out = ctypes.c_size_t(0)
+    assert lib.nsa_decode_workspace_size(None, ctypes.byref(_cfg()), 100, ctypes.byref(out)) == A.NSA_ERROR_INVALID_VALUE
+    assert lib.nsa_decode_workspace_size(ctypes.byref(_dims()), None, 100, ctypes.byref(out)) == A.NSA_ERROR_INVALID_VALUE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        A._ptr(torch.zeros(4), "x")

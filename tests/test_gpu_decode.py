@@ -1,0 +1,111 @@
+"""GPU parity of nsa_decode_fwd / nsa_compress_kv against the float64 oracle."""
+import numpy as np
+import pytest
+
+import nsa_inputs as I
+from oracle import nsa_oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+STD = "decode_64k_b8"
+
+
+def _check_decode(case, out, sel, groups=None, Kc_o=None, gates=None):
+    """Compare every (or the given) (b, g) with the oracle."""
+    wl, p = case.wl, case.p
+    G = wl.num_q_heads // wl.num_kv_heads
+    pairs = groups or [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    errs = []
+    for b, g in pairs:
+        if gates is not None:
+            saved = case.gates
+            case.gates = gates
+        res = O.decode_group(case, b, g)
+        t = int(case.seq_lens[b]) - 1
+        res = U.check_selection(res, sel[b, g], t, p, lambda idx: O.decode_group(case, b, g, override_idx=idx))
+        if gates is not None:
+            case.gates = saved
+        errs.append(U.assert_close(out[b, g * G:(g + 1) * G], res.out, f"b={b} g={g} t={t}"))
+    return errs
+
+
+@pytest.mark.parametrize("seed,L", [(0, 9000), (1, 4097), (2, 20000)])
+def test_decode_matches_oracle_with_oracle_cache(seed, L):
+    """Decode alone: the GPU reads the oracle's compressed cache."""
+    case = I.generate(I.workload(STD, batch=2, seq_len=L), seed)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    out, sel, _ = U.run_decode(case, kc, vc)
+    _check_decode(case, out, sel)
+
+
+@pytest.mark.parametrize("branch", [0, 1, 2])
+def test_decode_gates_isolate_each_branch(branch):
+    case = I.generate(I.workload(STD, batch=2, seq_len=6000), 10 + branch)
+    gates = np.zeros_like(case.gates)
+    gates[..., branch] = 1.0
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    out, sel, _ = U.run_decode(case, kc, vc, gates=gates)
+    _check_decode(case, out, sel, gates=gates)
+
+
+def test_decode_end_to_end_with_gpu_compression():
+    case = I.generate(I.workload(STD, batch=2, seq_len=12345), 3)
+    out, sel, _ = U.run_decode(case)
+    _check_decode(case, out, sel)
+
+
+def test_compress_matches_oracle():
+    case = I.generate(I.workload(STD, batch=2, seq_len=5000), 4)
+    kc_o, vc_o, cuc = U.oracle_cmp_cache(case)
+    _, _, (kc, vc) = U.run_decode(case)
+    got_k = U.bits_to_f64(U.host_bits(kc))
+    got_v = U.bits_to_f64(U.host_bits(vc))
+    want_k, want_v = U.bits_to_f64(kc_o), U.bits_to_f64(vc_o)
+    # both sides round the same real number to bf16; they may differ by one bf16 ulp
+    # where the fp32 accumulation lands on the other side of a rounding midpoint
+    ulp = np.maximum(np.abs(want_k), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(got_k - want_k) <= ulp + 1e-6)
+    assert np.mean(got_k != want_k) < 0.02
+    ulpv = np.maximum(np.abs(want_v), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(got_v - want_v) <= ulpv + 1e-6)
+
+
+def test_decode_ragged_fine_selection():
+    """Ragged lengths, l' = 32, n = 32."""
+    case = I.generate(I.workload("decode_ragged_16", batch=4, seq_len=9000, ragged_min=300), 5)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    out, sel, _ = U.run_decode(case, kc, vc)
+    _check_decode(case, out, sel)
+
+
+@pytest.mark.parametrize("L", [1, 5, 31, 32, 33, 64, 65, 1024, 1025, 4096 + 16, 16 * 256 + 32])
+def test_decode_edge_lengths(L):
+    """No complete compressed block, exactly one, all candidates selected, chunk edges."""
+    case = I.generate(I.workload(STD, batch=1, seq_len=L, needles=0), 100 + L)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    out, sel, _ = U.run_decode(case, kc, vc)
+    _check_decode(case, out, sel)
+
+
+def test_decode_small_heads_group4():
+    """d_k = d_v = 64, 4 query heads per KV head (the tiny workload's head shape)."""
+    wl = I.workload(STD, batch=3, seq_len=3000, num_q_heads=8, num_kv_heads=2, d_k=64, d_v=64,
+                    params={"n_sel": 4, "n_local": 1, "w": 64})
+    case = I.generate(wl, 6)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    out, sel, _ = U.run_decode(case, kc, vc)
+    _check_decode(case, out, sel)
+
+
+def test_decode_repeat_is_bitwise_identical():
+    """Same inputs twice through the same workspace: identical bits (no atomics in sums)."""
+    case = I.generate(I.workload(STD, batch=2, seq_len=7000), 7)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    import long_context_sparse_nsa_amd as N
+    dims, cfg = U.dims_cfg(case)
+    ws = N.new_workspace(N.nsa_decode_workspace_size(dims, cfg, 7000))
+    a = U.run_decode(case, kc, vc, ws=ws)
+    b = U.run_decode(case, kc, vc, ws=ws)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
