@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""NSA forward-pass benchmark on one MI355X.
+
+Headline: decode step at 64k context, batch 8, 64 query heads / 4 KV heads,
+d_k=192, d_v=128, l=32, d=16, l'=64, n=16, w=512 (the compressed cache is
+precomputed and resident, as in a serving loop).  One step = one
+nsa_decode_fwd call = one new token for each of the 8 sequences, i.e. the whole
+hot path: compressed attention, group scores, top-n, selected and window
+attention, gated sum.  value = tokens/s = 8 / step time.
+
+Timing: K back-to-back steps replayed from a HIP graph, each step on its own copy
+of the KV cache (6 copies, 8.6 GB, far beyond the 256 MB Infinity Cache) so every
+step reads HBM cold, bracketed by torch.cuda.synchronize().  Per-pass durations
+come from HIP events the library records at its phase boundaries on the call's
+stream, in an eager run queued behind a sleep kernel so the passes run back to back.
+
+Also reported: the causal prefill of 32768 tokens (in-call compression) and the
+float64 CPU oracle on a bounded sample (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+METRIC = "NSA decode tokens/sec at 64k ctx (HBM GB/s %peak); prefill TFLOP/s (%MFMA)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "long_context_sparse_nsa_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them; torch's Event cannot time those)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h)
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
+def upload_case(case, torch, N):
+    """Device tensors of a decode case plus its GPU-computed compressed cache."""
+    wl, p = case.wl, case.p
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    dims = N.make_dims(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.d_k, wl.d_v)
+    cfg = N.make_config(p.l, p.d, p.l_sel, p.n_sel, p.n_local, p.force_initial, p.w)
+    caps = np.diff(case.cu_seqlens)
+    ncap = np.array([N.compressed_count(int(c), p.l, p.d) for c in caps], dtype=np.int64)
+    cuc = np.zeros(len(caps) + 1, dtype=np.int64)
+    cuc[1:] = np.cumsum(ncap)
+    T = dict(q=dev(case.q), k=dev(case.k), v=dev(case.v), w_k=dev(case.w_k), pe_k=dev(case.pe_k),
+             w_v=dev(case.w_v), pe_v=dev(case.pe_v),
+             gates=torch.from_numpy(case.gates).cuda(), seq=torch.from_numpy(case.seq_lens).cuda(),
+             cu=torch.from_numpy(case.cu_seqlens).cuda(), cuc=torch.from_numpy(cuc).cuda())
+    rows = int(wl.num_kv_heads * cuc[-1])
+    T["kc"] = torch.zeros((max(rows, 1), wl.d_k), dtype=torch.bfloat16, device="cuda")
+    T["vc"] = torch.zeros((max(rows, 1), wl.d_v), dtype=torch.bfloat16, device="cuda")
+    max_len = int(caps.max())
+    N.nsa_compress_kv(dims, cfg, T["k"], T["v"], T["cu"], T["seq"], max_len, T["w_k"], T["pe_k"], T["w_v"],
+                      T["pe_v"], T["kc"], T["vc"], T["cuc"])
+    torch.cuda.synchronize()
+    return dims, cfg, T, max_len, cuc
+
+
+def decode_bytes(case, sel, cuc_unused=None):
+    """Algorithmic HBM bytes of one decode step: compressed cache, the union of selected
+    and window tokens (each read once), q, gates, out; and the compressed-pass part."""
+    wl, p = case.wl, case.p
+    row = 2 * (wl.d_k + wl.d_v)
+    cmp_b, sw_b = 0, 0
+    for b in range(wl.batch):
+        L = int(case.seq_lens[b])
+        t = L - 1
+        nc = (L - p.l) // p.d + 1 if L >= p.l else 0
+        for g in range(wl.num_kv_heads):
+            cmp_b += nc * row
+            toks = set(range(max(0, t - p.w + 1), t + 1))
+            for j in sel[b, g]:
+                if j >= 0:
+                    toks.update(range(j * p.l_sel, min((j + 1) * p.l_sel, L)))
+            sw_b += len(toks) * row
+    io = wl.batch * wl.num_q_heads * (wl.d_k * 2 + 3 * 4 + wl.d_v * 2)
+    q_bytes = wl.batch * wl.num_q_heads * wl.d_k * 2
+    return cmp_b + sw_b + io, cmp_b + q_bytes, sw_b
+
+
+def bench_decode(args, torch, N, I):
+    wl = I.workload(args.workload)
+    seed = list(I.WORKLOADS).index(args.workload)
+    t0 = time.time()
+    case = I.generate(wl, seed)
+    log(f"[bench] generated {wl.name} (seed {seed}) in {time.time() - t0:.1f}s")
+    dims, cfg, T, max_len, cuc = upload_case(case, torch, N)
+    ws = N.new_workspace(N.nsa_decode_workspace_size(dims, cfg, max_len))
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    sel = torch.full((wl.batch, wl.num_kv_heads, cfg.n_sel), -1, dtype=torch.int32, device="cuda")
+    copies = [(T["k"], T["v"], T["kc"], T["vc"])]
+    for _ in range(args.copies - 1):
+        copies.append(tuple(x.clone() for x in copies[0]))
+    torch.cuda.synchronize()
+    log(f"[bench] {len(copies)} cache copies resident "
+        f"({sum(x.numel() * 2 for x in copies[0]) * len(copies) / 1e9:.1f} GB)")
+
+    def step(i):
+        k, v, kc, vc = copies[i % len(copies)]
+        N.nsa_decode_fwd(dims, cfg, T["q"], k, v, kc, vc, T["seq"], T["cu"], T["cuc"], max_len, T["gates"], out,
+                         sel, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+
+    # graph of one step per copy, replayed
+    timing = "hip_graph"
+    K = args.steps
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(len(copies)):
+                    step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref_out):
+            raise RuntimeError("graph replay differs from eager result")
+        reps = max(1, (K + len(copies) - 1) // len(copies))
+        K = reps * len(copies)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        ev0.record()
+        for _ in range(reps):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        total_ms = ev0.elapsed_time(ev1)
+        if not torch.equal(out, ref_out):
+            raise RuntimeError("graph replay differs from eager result")
+    except Exception as e:  # graph capture unavailable: eager steps queued behind a sleep kernel
+        log(f"[bench] graph timing unavailable ({e}); eager timing")
+        timing = "eager_queued"
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        torch.cuda._sleep(int(2e7))
+        ev0.record()
+        for i in range(K):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        total_ms = ev0.elapsed_time(ev1)
+    ms_step = total_ms / K
+
+    # per-pass durations from the library's phase events (eager, queued behind a sleep)
+    n_ph = min(K, 60)
+    hev = HipEvents(3 * n_ph)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e7))
+    for i in range(n_ph):
+        N.nsa_set_decode_phase_events(hev.ev[3 * i:3 * i + 3])
+        step(i)
+    N.nsa_set_decode_phase_events(None)
+    torch.cuda.synchronize()
+    ph = [float(np.mean([hev.ms(3 * i + k, 3 * i + k + 1) for i in range(n_ph)])) for k in range(2)]
+    hev.close()
+    p1 = ph[0]
+    p2 = ph[1]
+    sel_h = sel.cpu().numpy()
+    b_step, b_cmp, b_sw = decode_bytes(case, sel_h)
+    gbs_step = b_step / (ms_step * 1e-3) / 1e9
+    gbs_cmp = b_cmp / (p1 * 1e-3) / 1e9
+    res = dict(
+        ms_per_step=ms_step, wall_s=wall, steps=K, timing=timing,
+        tokens_per_s=wl.batch / (ms_step * 1e-3),
+        step_bytes=b_step, step_gbs=gbs_step, step_frac=gbs_step / HBM_PEAK_GBS,
+        pass1_us=p1 * 1e3, pass2_us=p2 * 1e3, pass1_bytes=b_cmp, pass2_bytes=b_sw,
+
+        pass1_gbs=gbs_cmp, pass2_gbs=b_sw / (p2 * 1e-3) / 1e9,
+    )
+    log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step ({timing}), {res['tokens_per_s']:.4g} tok/s, "
+        f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: cmp {p1 * 1e3:.1f} us "
+        f"({gbs_cmp:.0f} GB/s), finish {p2 * 1e3:.1f} us")
+    return case, res, T
+
+
+def prefill_flops(wl):
+    """Algorithmic FLOPs of the causal prefill (2*(d_k+d_v) per key visit per head)."""
+    p = wl.params
+    T = wl.seq_len
+    t = np.arange(T, dtype=np.int64)
+    nc = np.where(t + 1 >= p.l, (t + 1 - p.l) // p.d + 1, 0)
+    J = t // p.l_sel
+    sel = np.where(J + 1 <= p.n_sel, t + 1, (p.n_sel - 1) * p.l_sel + (t % p.l_sel) + 1)
+    win = np.minimum(p.w, t + 1)
+    per = 2 * (wl.d_k + wl.d_v) * wl.num_q_heads * wl.batch
+    ncmp = (T - p.l) // p.d + 1 if T >= p.l else 0
+    comp = 2 * wl.batch * wl.num_kv_heads * ncmp * p.l * (wl.d_k * wl.d_k + wl.d_v * wl.d_v)
+    return dict(cmp=float(per * nc.sum()), slc=float(per * sel.sum()), win=float(per * win.sum()),
+                compress=float(comp))
+
+
+def bench_prefill(args, torch, N, I):
+    wl = I.workload("prefill_32k")
+    seed = list(I.WORKLOADS).index("prefill_32k")
+    t0 = time.time()
+    case = I.generate(wl, seed)
+    log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s")
+    p = wl.params
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    dims = N.make_dims(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.d_k, wl.d_v)
+    cfg = N.make_config(p.l, p.d, p.l_sel, p.n_sel, p.n_local, p.force_initial, p.w)
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    wk, pk, wv, pv = dev(case.w_k), dev(case.pe_k), dev(case.w_v), dev(case.pe_v)
+    gates = torch.from_numpy(case.gates).cuda()
+    out = torch.empty((wl.batch, wl.seq_len, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    ws = N.new_workspace(N.nsa_prefill_workspace_size(dims, cfg, wl.seq_len, True))
+
+    def run():
+        N.nsa_prefill_fwd(dims, cfg, wl.seq_len, q, k, v, None, None, wk, pk, wv, pv, gates, out, None, ws)
+
+    run()
+    torch.cuda.synchronize()
+    reps = args.prefill_reps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    f = prefill_flops(wl)
+    tot = sum(f.values())
+    res = dict(workload=wl.name, ms=ms, flops=f, tflops=tot / (ms * 1e-3) / 1e12,
+               mfma_frac=tot / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS)
+    log(f"[bench] prefill {wl.name}: {ms:.2f} ms, {res['tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of bf16 peak)")
+    return res
+
+
+def cpu_baseline(case, min_seconds):
+    """The float64 oracle on a bounded sample of the decode workload (this host's cores)."""
+    from oracle import nsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    wl, p = case.wl, case.p
+    G = wl.num_q_heads // wl.num_kv_heads
+    seqs = [0, 1]
+    prep = {}
+    for b in seqs:
+        for g in range(wl.num_kv_heads):
+            prep[(b, g)] = O.compress_group(case, b, g)          # cache precompute, untimed
+    tokens, elapsed = 0, 0.0
+    while elapsed < min_seconds:
+        for b in seqs:
+            t = int(case.seq_lens[b]) - 1
+            t0 = time.perf_counter()
+            for g in range(wl.num_kv_heads):
+                K, V, Kc, Vc = prep[(b, g)]
+                O.nsa_query(O._widen(case.q[b, g * G:(g + 1) * G]), K, V, Kc, Vc, t,
+                            np.asarray(case.gates[b, g * G:(g + 1) * G], np.float64), p.l, p.d, p.l_sel,
+                            p.n_sel, p.n_local, p.force_initial, p.w)
+            elapsed += time.perf_counter() - t0
+            tokens += 1
+    return dict(value=tokens / elapsed, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{tokens} decode tokens (sequences {seqs} x {wl.num_kv_heads} KV groups, repeated) of "
+                       f"{wl.name}; oracle-compressed cache precomputed untimed; {elapsed:.1f} s of CPU work")
+
+
+def roofline_from_profiles(kernel_hash):
+    """HBM traffic of the compressed pass from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_cmp_traffic.json")
+    try:
+        d = json.load(open(path))
+        if d.get("kernel_src_hash") == kernel_hash:
+            return d.get("traffic_bytes_per_launch")
+    except Exception:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_64k_b8")
+    ap.add_argument("--copies", type=int, default=6)
+    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the NSA path here is single-GPU by design "
+              "(DESIGN.md describes how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_sparse_nsa_amd as N
+    import nsa_inputs as I
+    N.load_library()
+    torch.cuda.set_device(0)
+
+    case, dec, _ = bench_decode(args, torch, N, I)
+    pre = None if args.no_prefill else bench_prefill(args, torch, N, I)
+    cpu = None if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
+    if cpu:
+        log(f"[bench] cpu oracle: {cpu['value']:.3g} tok/s on {cpu['cores']} threads")
+
+    khash = src_hash("nsa_decode.hip", "nsa_tiles.hpp", "nsa_topn.hpp", "nsa_device.hpp")
+    wl = case.wl
+    p = wl.params
+    line = {
+        "metric": METRIC,
+        "value": dec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": dec["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.seq_len, "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "d_k": wl.d_k, "d_v": wl.d_v, "l": p.l, "d": p.d,
+                   "l_sel": p.l_sel, "n_sel": p.n_sel, "w": p.w, "timing": dec["timing"],
+                   "cache_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "decode_cmp_kernel (compressed branch + scores + top-n)",
+                     "achieved": dec["pass1_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dec["pass1_gbs"] / HBM_PEAK_GBS, "traffic": roofline_from_profiles(khash),
+                     "duration_us": dec["pass1_us"], "algorithmic_bytes": dec["pass1_bytes"]},
+        "decode_step": {"algorithmic_bytes": dec["step_bytes"], "GB/s": dec["step_gbs"],
+                        "hbm_frac": dec["step_frac"],
+                        "kernel_us": {"decode_cmp_kernel": dec["pass1_us"], "decode_finish_kernel": dec["pass2_us"]},
+                        "finish_GB/s": dec["pass2_gbs"], "wall_s_timed_region": dec["wall_s"]},
+        "cpu_baseline": cpu,
+    }
+    if pre:
+        line["prefill"] = {"workload": pre["workload"], "ms": pre["ms"], "TFLOP/s": pre["tflops"],
+                           "mfma_frac": pre["mfma_frac"],
+                           "flops": pre["flops"], "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,10 +24,8 @@
  *    (thread-local) describes the problem.  Device faults surface at the
  *    caller's next synchronisation.
  *  - Workspace: a caller-provided device buffer of at least the size the
- *    matching *_workspace_size query returns.  It must be zero-filled once
- *    before its first use; every call leaves its leading counter words at zero
- *    again, so later calls need no clearing.  Calls that share a workspace must
- *    not overlap in time.
+ *    matching *_workspace_size query returns; its contents on entry do not
+ *    matter.  Calls that share a workspace must not overlap in time.
  *  - Query head h belongs to KV group g = h / G with G = num_q_heads /
  *    num_kv_heads; all heads of a group select the same blocks (selection
  *    paragraph of "NSA: три ветви").
@@ -168,6 +166,16 @@ nsa_status_t nsa_decode_workspace_size(const nsa_dims_t* dims, const nsa_config_
                                        int64_t max_seq_len, size_t* bytes);
 nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                         int64_t seq_len, int32_t compress_in_call, size_t* bytes);
+
+/* Profiling hook: until called again on this thread, every nsa_decode_fwd on
+ * this thread records the caller-owned hipEvent_t handles events[0..2] on the
+ * call's stream: before the compressed-branch kernel, after it (i.e. before the
+ * kernel doing selection, selected/window attention and the gated sum) and
+ * after that one, so a caller can time each kernel with hipEventElapsedTime.
+ * count = 0 (the default) records nothing; any count other than 0 or 3, or a
+ * NULL handle, is NSA_ERROR_INVALID_VALUE.  The array is copied; the events are
+ * not. */
+nsa_status_t nsa_set_decode_phase_events(void* const* events, int32_t count);
 
 /* Human-readable name of a status code (static storage). */
 const char* nsa_status_string(nsa_status_t status);

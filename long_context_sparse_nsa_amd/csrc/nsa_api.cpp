@@ -8,12 +8,14 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/nsa.h"
+#include "nsa.h"
 #include "nsa_internal.hpp"
 
 namespace {
 
 thread_local std::string g_last_error;
+thread_local nsa::PhaseEvents g_phase_events{};
+thread_local bool g_phase_on = false;
 
 nsa_status_t fail(nsa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 nsa_status_t fail(nsa_status_t st, const char* fmt, ...) {
@@ -83,11 +85,17 @@ nsa_status_t check_decode_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg,
     return fail(NSA_ERROR_UNSUPPORTED, "max_seq_len %lld gives more than %d selection blocks", (long long)max_seq_len,
                 nsa::kMaxBlocks);
   const int64_t nc = n_compressed(max_seq_len, cfg->l, cfg->d);
-  if ((nc + nsa::kChunk - 1) / nsa::kChunk > nsa::kMaxChunks)
+  if (nc > nsa::kMaxCompressed)
     return fail(NSA_ERROR_UNSUPPORTED, "max_seq_len %lld gives more than %d compressed blocks", (long long)max_seq_len,
-                nsa::kMaxChunks * nsa::kChunk);
+                nsa::kMaxCompressed);
   if ((int64_t)dims->batch * dims->num_kv_heads * ((nc + nsa::kChunk - 1) / nsa::kChunk + 1) > (int64_t)INT32_MAX / 2)
     return fail(NSA_ERROR_UNSUPPORTED, "launch too large");
+  const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
+                                                   cfg->l_sel, cfg->n_sel, cfg->w, max_seq_len);
+  if (lay.nfin > nsa::kMaxFinish)
+    return fail(NSA_ERROR_UNSUPPORTED, "n_sel=%d with l_sel=%d needs more than %d selection workgroups", cfg->n_sel,
+                cfg->l_sel, nsa::kMaxFinish);
+
   return NSA_SUCCESS;
 }
 
@@ -137,6 +145,20 @@ const char* nsa_status_string(nsa_status_t s) {
 }
 
 const char* nsa_last_error(void) { return g_last_error.c_str(); }
+
+nsa_status_t nsa_set_decode_phase_events(void* const* events, int32_t count) {
+  if (count == 0) {
+    g_phase_on = false;
+    return ok();
+  }
+  if (count != 3 || !events) return fail(NSA_ERROR_INVALID_VALUE, "give 3 events (or count 0)");
+  for (int i = 0; i < 3; ++i) {
+    if (!events[i]) return fail(NSA_ERROR_INVALID_VALUE, "phase event %d is NULL", i);
+    g_phase_events.ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_phase_on = true;
+  return ok();
+}
 
 nsa_status_t nsa_decode_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t max_seq_len,
                                        size_t* bytes) {
@@ -238,19 +260,18 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   p.gates = gates;
   p.out = out;
   p.sel_out = sel_idx_out;
-  p.cnt1 = reinterpret_cast<uint32_t*>(ws + lay.off_cnt1);
-  p.cnt2 = reinterpret_cast<uint32_t*>(ws + lay.off_cnt2);
   p.m1 = reinterpret_cast<float*>(ws + lay.off_m1);
   p.l1 = reinterpret_cast<float*>(ws + lay.off_l1);
   p.o1 = reinterpret_cast<float*>(ws + lay.off_o1);
   p.sc1 = reinterpret_cast<float*>(ws + lay.off_sc1);
-  p.ocmp = reinterpret_cast<float*>(ws + lay.off_ocmp);
-  p.sel = reinterpret_cast<int32_t*>(ws + lay.off_sel);
-  p.part2 = reinterpret_cast<float*>(ws + lay.off_part2);
+  p.wpart = reinterpret_cast<float*>(ws + lay.off_wpart);
+  p.rpart = reinterpret_cast<float*>(ws + lay.off_rpart);
+  p.fcmp = reinterpret_cast<float*>(ws + lay.off_fcmp);
+  p.nfin = lay.nfin;
   p.nch = lay.nch;
   p.nbo = lay.nbo;
-  p.nw2 = lay.nw2;
-  hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream));
+  const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
+  hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }

@@ -1,18 +1,21 @@
-// NSA decode step on gfx950: two launches per step.
+// NSA decode step on gfx950: two launches per step; the kernel boundary is the
+// only cross-workgroup synchronisation (no device-scope fences, no counters).
 //
-// Pass 1 (decode_cmp_kernel): the compressed branch, split over chunks of 256
-//   compressed keys per (sequence, KV group).  Each workgroup streams its chunk
-//   of the compressed cache once, computes the 16-head logits with MFMA, the
-//   chunk-local softmax statistics, the partial output, and the per-head
-//   probabilities folded onto selection blocks.  The last workgroup of a
-//   (sequence, group) — found with a device-scope counter — merges the chunks
-//   exactly (per-head max / sum rescaling), writes the gated compressed output,
-//   sums the folded scores over the group's heads and runs the top-n.
-// Pass 2 (decode_sw_kernel): the selected blocks and the window blocks, as one
-//   sorted union so every token is read once; each token's logit feeds the
-//   selected-branch softmax if its block was selected and the window softmax if
-//   it lies in the last w tokens.  The last workgroup merges the partials and
-//   writes out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
+// 1. decode_cmp_kernel, two kinds of workgroups in one launch:
+//    - chunk workgroups: the compressed branch, split over chunks of compressed
+//      keys per (sequence, KV group).  Each streams its chunk of the compressed
+//      cache once, computes the 16-head logits with MFMA, the chunk-local
+//      softmax statistics, the partial output, and the per-head probabilities
+//      folded onto selection blocks;
+//    - window workgroups: everything that does not depend on the selection —
+//      the whole window branch, and the selected branch over the always-taken
+//      blocks (block 0 and the local blocks) — as 32-token steps over the
+//      sorted union of those blocks, so every token is read once and its logit
+//      feeds each branch it belongs to.
+// 2. decode_finish_kernel: per (sequence, group), exact per-head normalisers
+//    from the chunk statistics, group scores, top-n, the selected branch over
+//    the routed (not always-taken) blocks, the exact merge of every partial, and
+//    out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 //
 // Sources: lesson 5.5/02 "Разреженное внимание — NSA и DSA" (ai.flicky.cc),
 // section "NSA: три ветви" (output equation; compressed branch l=32, d=16;
@@ -67,403 +70,582 @@ __device__ __forceinline__ int n_visible(const DecodeParams& p, int b, int L) {
   return (int)(nv < ccap ? nv : ccap);
 }
 
-// LDS budget of pass 1, in floats (compute phase and merge phase share it).
+// LDS budget of the compressed pass, in floats.
 template <int DV>
 struct K1Smem {
-  static constexpr int kP = 16 * (kChunk + 4);          // probabilities for the fold
-  static constexpr int kAcc = 4 * 16 * (DV + 1);        // per-wave partial outputs
-  static constexpr int kRed = 128;                      // per-wave max / sum
-  static constexpr int kCompute = kP + kAcc + kRed;
-  static constexpr int kMerge = kMaxBlocks + kMaxChunks * 16 + kMaxBlocks / 4 + sizeof(TopnSmem) / 4 + 8;
-  static constexpr int kFloats = kCompute > kMerge ? kCompute : kMerge;
+  static constexpr int kP = 16 * (kChunk + 4);             // probabilities for the fold
+  static constexpr int kAcc = kCmpWaves * 16 * (DV + 1);   // per-wave partial outputs
+  static constexpr int kRed = 2 * kCmpWaves * 16;          // per-wave max / sum
+  static constexpr int kFloats = kP + kAcc + kRed;
 };
+
+// One 32-token step [x0, x0 + 32) of the raw cache for the group's heads.
+template <int DK, int DV>
+struct Step {
+  u32x4_t kf[2][DK / 32];
+  uint32_t vr[8][DV / 32];
+};
+
+// Tokens x < nval exist (nval already bounds x <= t and the block end).
+template <int DK, int DV>
+__device__ __forceinline__ void step_load(Step<DK, DV>& st, const uint16_t* kb, const uint16_t* vb, int64_t x0,
+                                          int64_t nval, int lg, int lr) {
+  load_k_tile<DK>(kb, x0 + lr, nval, lg, st.kf[0]);
+  load_k_tile<DK>(kb, x0 + 16 + lr, nval, lg, st.kf[1]);
+  load_v_step<DV>(vb, x0, nval, lg, lr, st.vr);
+}
+
+// Online-softmax state of one branch for the wave's 16 heads (head = lane % 16).
+template <int DV>
+struct Branch {
+  float m, l;
+  f32x4_t acc[DV / 16];
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int j = 0; j < DV / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // Fold in the step's tokens whose mask bit is set (z = -inf elsewhere).
+  __device__ __forceinline__ void update(float (&z)[2][4], const uint32_t (&vr)[8][DV / 32]) {
+    float mx = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                     fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+    mx = max_over_groups(mx);
+    const float mn = fmaxf(m, mx);
+    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = exp2f(z[tt][i] - mn);
+        z[tt][i] = e;
+        ls += e;
+      }
+    l = l * alpha + sum_over_groups(ls);
+    m = mn;
+#pragma unroll
+    for (int j = 0; j < DV / 16; ++j) acc[j] *= alpha;
+    pv_step<DV>(vr, pack_probs(z[0], z[1]), acc);
+  }
+};
+
+// Logits of a step, scaled to log2 units; element (tt, i) is token x0 + 16*tt + 4*lg + i.
+template <int DK, int DV>
+__device__ __forceinline__ void step_logits(const Step<DK, DV>& st, const u32x4_t (&qf)[DK / 32], float scale,
+                                            float (&z)[2][4]) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const f32x4_t sv = qk_tile<DK>(st.kf[tt], qf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[tt][i] = sv[i] * scale;
+  }
+}
+
+// Sorted union of two ascending block lists (a: n_a entries; b: the range [b0, b1]).
+// Writes at most cap items and a flag per item telling whether it came from list a.
+__device__ __forceinline__ int merge_blocks(const int* a, int n_a, int b0, int b1, int* items, uint8_t* from_a,
+                                            int cap) {
+  int ia = 0, cnt = 0, jb = b0;
+  while (true) {
+    const int sa = ia < n_a ? a[ia] : INT32_MAX;
+    const int sb = jb <= b1 ? jb : INT32_MAX;
+    if (sa == INT32_MAX && sb == INT32_MAX) break;
+    const int j = sa < sb ? sa : sb;
+    if (cnt < cap) {
+      items[cnt] = j;
+      from_a[cnt] = (uint8_t)(sa == j);
+    }
+    ++cnt;
+    if (sa == j) ++ia;
+    if (sb == j) ++jb;
+  }
+  return cnt < cap ? cnt : cap;
+}
+
+// Ascending list of the always-taken blocks at a query in block J.
+__device__ __forceinline__ int forced_list(int J, int nloc, int finit, int* out) {
+  int n = 0;
+  const int lo = J - nloc + 1 > 0 ? J - nloc + 1 : 0;
+  if (finit && lo > 0) out[n++] = 0;
+  for (int j = lo; j <= J; ++j) out[n++] = j;
+  return n;
+}
+
+// Workgroup merge of 4 waves' branch states into one partial
+// (m[16], l[16], o[16][DV]) written to `dst`; `buf`/`st` are LDS scratch.
+template <int DV, int NWV>
+__device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst, float* buf, float* st) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  constexpr int NTH = 64 * NWV;
+  if (lg == 0) {
+    st[wave * 16 + lr] = br.m;
+    st[(NWV + wave) * 16 + lr] = br.l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) M = fmaxf(M, st[w * 16 + lr]);
+  const float alpha = br.m == -INFINITY ? 0.f : exp2f(br.m - M);
+#pragma unroll
+  for (int j = 0; j < DV / 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = alpha * br.acc[j][i];
+  __syncthreads();
+  for (int e = tid; e < 16 * DV; e += NTH) {
+    const int h = e / DV, ch = e - h * DV;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) v += buf[(w * 16 + h) * (DV + 1) + ch];
+    dst[32 + e] = v;
+  }
+  if (tid < 16) {
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) Mh = fmaxf(Mh, st[w * 16 + tid]);
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = st[w * 16 + tid];
+      if (mw != -INFINITY) ls += exp2f(mw - Mh) * st[(NWV + w) * 16 + tid];
+    }
+    dst[tid] = Mh;
+    dst[16 + tid] = ls;
+  }
+  __syncthreads();
+}
+
+
 
 }  // namespace
 
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void decode_cmp_kernel(DecodeParams p) {
+// The blocks the window workgroup covers: the window blocks [jw0, J] and the
+// always-taken blocks (local blocks [J-nloc+1, J], and block 0) — a contiguous
+// range [lo, J] plus possibly block 0.  Item k of that sorted list:
+struct WindowBlocks {
+  int lo, J, has0, lo_local, finit;
+  __device__ __forceinline__ WindowBlocks(int t, int lsel, int w, int nloc, int fi) {
+    J = t / lsel;
+    const int wlo = t - w + 1 > 0 ? t - w + 1 : 0;
+    lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;
+    lo = min(wlo / lsel, lo_local);
+    finit = fi;
+    has0 = (fi && lo > 0) ? 1 : 0;
+  }
+  __device__ __forceinline__ int count() const { return J - lo + 1 + has0; }
+  __device__ __forceinline__ int block(int k) const { return has0 ? (k == 0 ? 0 : lo + k - 1) : lo + k; }
+  __device__ __forceinline__ bool forced(int j) const { return j >= lo_local || (finit && j == 0); }
+};
+
+// Window workgroup (one per (sequence, group)): 32-token steps over the window
+// blocks and the always-taken blocks, spread over the waves; writes one
+// partial per branch (grp 0: selected branch over the always-taken blocks,
+// grp 1: window).
+template <int DK, int DV, int LSEL>
+__device__ __forceinline__ void window_work(const DecodeParams& p, int b, int g, int bg, float* smem) {
+  constexpr int KT = DK / 32, NWV = kCmpWaves;
+  constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;
+  constexpr int PSTRIDE = 32 + 16 * DV;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int L = seq_len_clamped(p, b);
+  const int t = L - 1;
+  const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
+  const WindowBlocks wb(t, LSEL, p.w, p.nloc, p.finit);
+  const int nsteps = wb.count() * SPB;
+  const int64_t row = raw_row0(p, b, g);
+  const uint16_t* kb = p.k + row * DK;
+  const uint16_t* vb = p.v + row * DV;
+  u32x4_t qf[KT];
+  load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
+  Branch<DV> bs, bw;
+  bs.init();
+  bw.init();
+  for (int si = wave; si < nsteps; si += NWV) {
+    const int it = si / SPB, half = si - it * SPB;
+    const int jb = wb.block(it);
+    const int64_t xb = (int64_t)jb * LSEL;
+    const int64_t x0 = xb + 32 * half;
+    const int64_t nv = min((int64_t)L, xb + LSEL);
+    const bool fr = wb.forced(jb);
+    Step<DK, DV> st;
+    step_load<DK, DV>(st, kb, vb, x0, nv, lg, lr);
+    if (x0 >= nv) continue;  // uniform over the wave
+    float z[2][4], zs[2][4], zw[2][4];
+    step_logits<DK, DV>(st, qf, p.scale_log2, z);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t x = x0 + 16 * tt + 4 * lg + i;
+        const bool valid = x < nv;
+        zs[tt][i] = (valid && fr) ? z[tt][i] : -INFINITY;
+        zw[tt][i] = (valid && x >= wlo) ? z[tt][i] : -INFINITY;
+      }
+    if (fr) bs.update(zs, st.vr);
+    if (x0 + 31 >= wlo) bw.update(zw, st.vr);
+  }
+  float* dst = p.wpart + (size_t)bg * 2 * PSTRIDE;
+  float* buf = smem;
+  float* stt = smem + NWV * 16 * (DV + 1);
+  merge_waves_to<DV, NWV>(bs, dst, buf, stt);
+  merge_waves_to<DV, NWV>(bw, dst + PSTRIDE, buf, stt);
+}
+
+template <int DK, int DV, int LSEL>
+__global__ __launch_bounds__(64 * kCmpWaves, 2) void decode_cmp_kernel(DecodeParams p) {
   constexpr int KT = DK / 32, VC = DV / 16, VW = DV / 32;
+  constexpr int NWV = kCmpWaves, KPW = kCmpKeysPerWave, NTH = 64 * NWV;
+  constexpr int TPW = KPW / 16, SPW = KPW / 32;  // 16-key tiles and 32-key steps per wave
   using SM = K1Smem<DV>;
   __shared__ float smem[SM::kFloats];
-  __shared__ int s_last;
 
+  // workgroups [0, B*H) are window workgroups (scheduled first), the rest chunks
+  const int nwg_win = p.B * p.H;
+  if ((int)blockIdx.x < nwg_win) {
+    window_work<DK, DV, LSEL>(p, blockIdx.x / p.H, blockIdx.x % p.H, blockIdx.x, smem);
+    return;
+  }
   const int nch = p.nch;
-  const int c = blockIdx.x % nch;
-  const int bg = blockIdx.x / nch;
+  const int cid = blockIdx.x - nwg_win;
+  const int c = cid % nch;
+  const int bg = cid / nch;
   const int g = bg % p.H, b = bg / p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
 
   const int L = seq_len_clamped(p, b);
   const int nvis = n_visible(p, b, L);  // complete compressed blocks
   const int nch_b = (nvis + kChunk - 1) / kChunk;
+  if (c >= nch_b) return;  // uniform over the workgroup
 
-  if (c < nch_b) {
-    float* s_p = smem;
-    float* s_acc = smem + SM::kP;
-    float* s_red = s_acc + SM::kAcc;
-    const int64_t crow = cmp_row0(p, b, g);
-    const uint16_t* kc = p.kc + crow * DK;
-    const uint16_t* vc = p.vc + crow * DV;
-    const int key0 = c * kChunk + wave * 64;
+  float* s_p = smem;
+  float* s_acc = smem + SM::kP;
+  float* s_red = s_acc + SM::kAcc;  // [0, NWV*16): max; [NWV*16, 2*NWV*16): sum
+  const int64_t crow = cmp_row0(p, b, g);
+  const uint16_t* kc = p.kc + crow * DK;
+  const uint16_t* vc = p.vc + crow * DV;
+  const int key0 = c * kChunk + wave * KPW;
 
-    u32x4_t qf[KT];
-    load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
-    u32x4_t kf[4][KT];
+  u32x4_t qf[KT];
+  load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
+  u32x4_t kf[TPW][KT];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) load_k_tile<DK>(kc, key0 + 16 * tt + lr, nvis, lg, kf[tt]);
-    uint32_t vr[2][8][VW];
+  for (int tt = 0; tt < TPW; ++tt) load_k_tile<DK>(kc, key0 + 16 * tt + lr, nvis, lg, kf[tt]);
+  uint32_t vr[SPW][8][VW];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) load_v_step<DV>(vc, key0 + 32 * s, nvis, lg, lr, vr[s]);
+  for (int s = 0; s < SPW; ++s) load_v_step<DV>(vc, key0 + 32 * s, nvis, lg, lr, vr[s]);
 
-    float z[4][4];
-    float mx = -INFINITY;
+  float z[TPW][4];
+  float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const f32x4_t st = qk_tile<DK>(kf[tt], qf);
+  for (int tt = 0; tt < TPW; ++tt) {
+    const f32x4_t st = qk_tile<DK>(kf[tt], qf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 16 * tt + 4 * lg + i;
-        const float v = key < nvis ? st[i] * p.scale_log2 : -INFINITY;
-        z[tt][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    mx = max_over_groups(mx);
-    if (lg == 0) s_red[wave * 16 + lr] = mx;
-    __syncthreads();
-    // chunk max per head; finite because key c*kChunk (wave 0) is visible
-    const float m = fmaxf(fmaxf(s_red[lr], s_red[16 + lr]), fmaxf(s_red[32 + lr], s_red[48 + lr]));
-    float ls = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = exp2f(z[tt][i] - m);
-        z[tt][i] = e;
-        ls += e;
-        s_p[lr * (kChunk + 4) + wave * 64 + 16 * tt + 4 * lg + i] = e;
-      }
-    ls = sum_over_groups(ls);
-    if (lg == 0) s_red[64 + wave * 16 + lr] = ls;
-
-    f32x4_t acc[VC];
-#pragma unroll
-    for (int j = 0; j < VC; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) pv_step<DV>(vr[s], pack_probs(z[2 * s], z[2 * s + 1]), acc);
-#pragma unroll
-    for (int j = 0; j < VC; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = acc[j][i];
-    __syncthreads();
-
-    // chunk partial output [16][DV] (sum over the 4 waves, same reference max)
-    float* O = p.o1 + ((size_t)bg * nch + c) * 16 * DV;
-    for (int e = tid; e < 16 * DV; e += 256) {
-      const int h = e / DV, ch = e - h * DV;
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) v += s_acc[(w * 16 + h) * (DV + 1) + ch];
-      O[e] = v;
-    }
-    if (tid < 16) {
-      p.m1[((size_t)bg * nch + c) * 16 + tid] = m;
-      p.l1[((size_t)bg * nch + c) * 16 + tid] =
-          s_red[64 + tid] + s_red[80 + tid] + s_red[96 + tid] + s_red[112 + tid];
-    }
-    // per-head scores of the selection blocks this chunk touches:
-    // slot jj is block jb0 + jj; slot nbo receives the overhang of the last keys.
-    const int nbo = p.nbo, slots = nbo + 1;
-    const int64_t jb0 = (int64_t)c * kChunk * p.d / p.lsel;
-    const int kc0 = c * kChunk, kc1 = min(kc0 + kChunk, nvis);
-    float* SC = p.sc1 + ((size_t)bg * nch + c) * 16 * slots;
-    const float inv_l = 1.0f / (float)p.l;
-    for (int e = tid; e < 16 * slots; e += 256) {
-      const int h = e / slots, jj = e - h * slots;
-      const int64_t j = jb0 + jj;
-      const int64_t lo_tok = j * p.lsel, hi_tok = lo_tok + p.lsel;  // block j = [lo, hi)
-      const int64_t a = lo_tok - p.l;
-      int64_t ilo = a < 0 ? 0 : a / p.d + 1;  // first key with i*d + l > lo
-      if (ilo < kc0) ilo = kc0;
-      int64_t ihi = (hi_tok - 1) / p.d;       // last key with i*d < hi
-      if (ihi > kc1 - 1) ihi = kc1 - 1;
-      float s = 0.f;
-      for (int64_t i = ilo; i <= ihi; ++i) {
-        const int64_t x0 = i * p.d;
-        const int64_t ov = min(x0 + p.l, hi_tok) - max(x0, lo_tok);
-        s += (float)ov * s_p[h * (kChunk + 4) + (int)(i - kc0)];
-      }
-      SC[e] = s * inv_l;
+    for (int i = 0; i < 4; ++i) {
+      const int key = key0 + 16 * tt + 4 * lg + i;
+      const float v = key < nvis ? st[i] * p.scale_log2 : -INFINITY;
+      z[tt][i] = v;
+      mx = fmaxf(mx, v);
     }
   }
-
-  // ---- last workgroup of this (sequence, group) merges the chunks
-  __threadfence();
+  mx = max_over_groups(mx);
+  if (lg == 0) s_red[wave * 16 + lr] = mx;
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&p.cnt1[bg], 1u) == (unsigned)(nch - 1);
+  // chunk max per head; finite because key c*kChunk (wave 0) is visible
+  float m = s_red[lr];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) m = fmaxf(m, s_red[w * 16 + lr]);
+  float ls = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = exp2f(z[tt][i] - m);
+      z[tt][i] = e;
+      ls += e;
+      s_p[lr * (kChunk + 4) + wave * KPW + 16 * tt + 4 * lg + i] = e;
+    }
+  ls = sum_over_groups(ls);
+  if (lg == 0) s_red[(NWV + wave) * 16 + lr] = ls;
+
+  f32x4_t acc[VC];
+#pragma unroll
+  for (int j = 0; j < VC; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) pv_step<DV>(vr[s], pack_probs(z[2 * s], z[2 * s + 1]), acc);
+#pragma unroll
+  for (int j = 0; j < VC; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = acc[j][i];
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) p.cnt1[bg] = 0u;
 
-  float* S = smem;
-  float* f = S + kMaxBlocks;
-  uint8_t* flag = reinterpret_cast<uint8_t*>(f + kMaxChunks * 16);
-  TopnSmem& tsm = *reinterpret_cast<TopnSmem*>(flag + kMaxBlocks);
-
-  const int t = L - 1;
-  const int J = t / p.lsel;
-  const size_t cbase = (size_t)bg * nch;
+  // chunk partial output [16][DV] (sum over the waves, same reference max)
+  float* O = p.o1 + ((size_t)bg * nch + c) * 16 * DV;
+  for (int e = tid; e < 16 * DV; e += NTH) {
+    const int h = e / DV, ch = e - h * DV;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) v += s_acc[(w * 16 + h) * (DV + 1) + ch];
+    O[e] = v;
+  }
   if (tid < 16) {
-    float M = -INFINITY;
-    for (int cc = 0; cc < nch_b; ++cc) M = fmaxf(M, p.m1[(cbase + cc) * 16 + tid]);
-    float Ls = 0.f;
-    for (int cc = 0; cc < nch_b; ++cc) Ls += p.l1[(cbase + cc) * 16 + tid] * exp2f(p.m1[(cbase + cc) * 16 + tid] - M);
-    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
-    for (int cc = 0; cc < nch_b; ++cc)
-      f[cc * 16 + tid] = tid < p.G ? exp2f(p.m1[(cbase + cc) * 16 + tid] - M) * inv : 0.f;
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) lsum += s_red[(NWV + w) * 16 + tid];
+    p.m1[((size_t)bg * nch + c) * 16 + tid] = m;
+    p.l1[((size_t)bg * nch + c) * 16 + tid] = lsum;
   }
-  __syncthreads();
-  // gated compressed-branch output (zero when no block is complete yet)
-  float* oc = p.ocmp + (size_t)bg * 16 * DV;
-  for (int e = tid; e < 16 * DV; e += 256) {
-    const int h = e / DV;
-    float a = 0.f;
-    for (int cc = 0; cc < nch_b; ++cc) a += f[cc * 16 + h] * p.o1[(cbase + cc) * 16 * DV + e];
-    const float gt = h < p.G ? p.gates[((int64_t)b * p.Hq + (int64_t)g * p.G + h) * 3 + 0] : 0.f;
-    oc[e] = gt * a;
-  }
-  // group scores of candidate blocks 0..J
+  // per-head scores of the selection blocks this chunk touches, in units of the
+  // stride d (d divides l and l'): key i covers units [i, i+q), block j covers
+  // [j*r, (j+1)*r) with q = l/d, r = l'/d, and the overlap share is (units)/q.
+  // Slot jj is block jb0 + jj; slot nbo receives the overhang of the last keys.
   const int nbo = p.nbo, slots = nbo + 1;
-  for (int j = tid; j <= J; j += 256) {
-    const int cc = j / nbo, jj = j - cc * nbo;
-    float s = 0.f;
-    if (cc < nch_b) {
-      const float* SC = p.sc1 + (cbase + cc) * 16 * slots;
-      for (int h = 0; h < p.G; ++h) s += f[cc * 16 + h] * SC[h * slots + jj];
-    }
-    if (jj == 0 && cc >= 1 && cc - 1 < nch_b) {
-      const float* SC = p.sc1 + (cbase + cc - 1) * 16 * slots;
-      for (int h = 0; h < p.G; ++h) s += f[(cc - 1) * 16 + h] * SC[h * slots + nbo];
-    }
-    S[j] = s;
+  const int q = p.l / p.d, r = p.lsel / p.d;
+  const int jb0 = c * kChunk / r;
+  const int kc0 = c * kChunk, kc1 = min(kc0 + kChunk, nvis);
+  float* SC = p.sc1 + ((size_t)bg * nch + c) * 16 * slots;
+  const float inv_q = 1.0f / (float)q;
+  for (int e = tid; e < 16 * slots; e += NTH) {
+    const int h = e / slots, jj = e - h * slots;
+    const int lo = (jb0 + jj) * r, hi = lo + r;      // block j in units
+    const int ilo = max(kc0, lo - q + 1), ihi = min(kc1 - 1, hi - 1);
+    const float* ps = s_p + h * (kChunk + 4) - kc0;
+    float sacc = 0.f;
+    for (int i = ilo; i <= ihi; ++i) sacc += (float)(min(i + q, hi) - max(i, lo)) * ps[i];
+    SC[e] = sacc * inv_q;
   }
-  __syncthreads();
-  block_topn(S, J, p.n, p.nloc, p.finit, flag, tsm, p.sel + (size_t)bg * p.n,
-             p.sel_out ? p.sel_out + (size_t)bg * p.n : nullptr);
 }
 
-// LDS budget of pass 2 in floats.
-template <int DV>
-struct K2Smem {
-  static constexpr int kAcc = 4 * 16 * (DV + 1);
-  static constexpr int kStat = 4 * 4 * 16;  // [grp m/l][wave][head]
-  static constexpr int kFac = 2 * 64 * 16;  // final merge factors
-  static constexpr int kFloats = (kAcc + kStat) > kFac ? (kAcc + kStat) : kFac;
-};
-
+// Finish: nfin workgroups of 8 waves per (sequence, group).  Every one of them
+// computes the exact per-head normalisers of the compressed branch, the group
+// scores and the top-n (identical results, so no exchange is needed); then
+// workgroup k attends the routed steps [8k, 8k+8) of the selected branch (the
+// selected blocks that are not always-taken; one 32-token step per wave) and
+// writes one partial.  Spreading the routed blocks over several workgroups lets
+// their loads use many CUs' memory pipelines instead of one.
 template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(256) void decode_sw_kernel(DecodeParams p) {
-  constexpr int KT = DK / 32, VC = DV / 16, VW = DV / 32;
-  constexpr int NT = LSEL / 16, NS = (NT + 1) / 2;
-  constexpr int PSTRIDE = 32 + 16 * DV;  // one branch partial: m[16], l[16], o[16][DV]
-  using SM = K2Smem<DV>;
-  __shared__ float smem[SM::kFloats];
-  __shared__ int s_items[kMaxUnion];
-  __shared__ uint8_t s_insel[kMaxUnion];
+__global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
+  constexpr int NTH = 512, NWV = 8;
+  constexpr int KT = DK / 32;
+  constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;   // 32-token steps per selection block
+  constexpr int PSTRIDE = 32 + 16 * DV;
+  __shared__ float S[kMaxBlocks];
+  __shared__ float f[kMaxChunks * 16];
+  __shared__ float s_stat[2 * kMaxChunks * 16];    // chunk m / l staging, then wave merge scratch
+  __shared__ float s_ov[kMaxChunks * 16];          // overhang score slot of each chunk, per head
+  __shared__ float s_buf[NWV * 16 * (DV + 1)];
+  __shared__ TopnSmem tsm;
+  __shared__ int s_sel[kMaxSel];
+  __shared__ int s_items[kMaxSel];
   __shared__ int s_nitems;
-  __shared__ int s_last;
 
-  const int nw2 = p.nw2;
-  const int wg = blockIdx.x % nw2;
-  const int bg = blockIdx.x / nw2;
+  const int bg = blockIdx.x / p.nfin, kfin = blockIdx.x - bg * p.nfin;
   const int g = bg % p.H, b = bg / p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-
+  const int nch = p.nch;
   const int L = seq_len_clamped(p, b);
+  const int nvis = n_visible(p, b, L);
+  const int nch_b = (nvis + kChunk - 1) / kChunk;
   const int t = L - 1;
   const int J = t / LSEL;
-  const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;  // first window token
-  const int jw0 = wlo / LSEL;
+  const size_t cbase = (size_t)bg * nch;
+  float* s_m = s_stat;
+  float* s_l = s_stat + kMaxChunks * 16;
 
-  if (tid == 0) {  // sorted union of the selected blocks and the window blocks
-    const int32_t* sel = p.sel + (size_t)bg * p.n;
-    int a = 0, cnt = 0, jw = jw0;
-    while (true) {
-      const int sa = (a < p.n && sel[a] >= 0) ? sel[a] : INT32_MAX;
-      const int sb = jw <= J ? jw : INT32_MAX;
-      if (sa == INT32_MAX && sb == INT32_MAX) break;
-      const int j = sa < sb ? sa : sb;
-      if (cnt < kMaxUnion) {
-        s_items[cnt] = j;
-        s_insel[cnt] = (uint8_t)(sa == j);
-      }
-      ++cnt;
-      if (sa == j) ++a;
-      if (sb == j) ++jw;
+  // ---- one round of independent loads: chunk statistics, overhang slots, scores
+  const int nbo = p.nbo, slots = nbo + 1;
+  for (int idx = tid; idx < nch_b * 16; idx += NTH) {
+    s_m[idx] = p.m1[cbase * 16 + idx];
+    s_l[idx] = p.l1[cbase * 16 + idx];
+    const int cc = idx >> 4, h = idx & 15;
+    s_ov[idx] = h < p.G ? p.sc1[((cbase + cc) * 16 + h) * slots + nbo] : 0.f;
+  }
+  float vv[2][16];
+  auto load_scores = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int j = j0 + tid + NTH * r;
+      const int cc = j / nbo, jj = j - cc * nbo;
+      const bool ok = j <= J && cc < nch_b;
+      const float* SC = p.sc1 + (cbase + (ok ? cc : 0)) * 16 * slots + jj;
+#pragma unroll
+      for (int h = 0; h < 16; ++h) vv[r][h] = (ok && h < p.G) ? SC[h * slots] : 0.f;
     }
-    s_nitems = cnt < kMaxUnion ? cnt : kMaxUnion;
+  };
+  load_scores(0);
+  __syncthreads();
+  // ---- exact per-head normalisers: thread (c, h) = (tid / 16, tid % 16), passes of
+  // 32 chunks; reductions over c by shuffles in a wave and through LDS across waves
+  {
+    float* red = s_buf;  // [wave][16] scratch
+    const int h = tid & 15, cw = tid >> 4;
+    float M = -INFINITY;
+    for (int c0 = 0; c0 < nch_b; c0 += NTH / 16) {
+      const int c = c0 + cw;
+      float m = c < nch_b ? s_m[c * 16 + h] : -INFINITY;
+      m = max_over_groups(m);
+      if (lg == 0) red[wave * 16 + h] = m;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) M = fmaxf(M, red[w * 16 + h]);
+      __syncthreads();
+    }
+    float Ls = 0.f;
+    for (int c0 = 0; c0 < nch_b; c0 += NTH / 16) {
+      const int c = c0 + cw;
+      float e = c < nch_b ? s_l[c * 16 + h] * exp2f(s_m[c * 16 + h] - M) : 0.f;
+      e = sum_over_groups(e);
+      if (lg == 0) red[wave * 16 + h] = e;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) Ls += red[w * 16 + h];
+      __syncthreads();
+    }
+    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
+    for (int c = cw; c < nch_b; c += NTH / 16) {
+      const float fc = h < p.G ? exp2f(s_m[c * 16 + h] - M) * inv : 0.f;
+      f[c * 16 + h] = fc;
+      if (kfin == 0) p.fcmp[(cbase + c) * 16 + h] = fc;  // for the combine kernel
+    }
   }
   __syncthreads();
 
-  float m_s = -INFINITY, l_s = 0.f, m_w = -INFINITY, l_w = 0.f;
-  f32x4_t accS[VC], accW[VC];
+  // ---- group scores of candidate blocks 0..J, top-n
+  for (int j0 = 0; j0 <= J; j0 += NTH * 2) {
+    if (j0 > 0) load_scores(j0);
 #pragma unroll
-  for (int j = 0; j < VC; ++j) accS[j] = accW[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 2; ++r) {
+      const int j = j0 + tid + NTH * r;
+      if (j > J) continue;
+      const int cc = j / nbo, jj = j - cc * nbo;
+      float sc = 0.f;
+      if (cc < nch_b) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h) sc += f[cc * 16 + h] * vv[r][h];
+      }
+      if (jj == 0 && cc >= 1 && cc - 1 < nch_b) {  // overhang of the previous chunk
+#pragma unroll
+        for (int h = 0; h < 16; ++h) sc += f[(cc - 1) * 16 + h] * s_ov[(cc - 1) * 16 + h];
+      }
+      S[j] = sc;
+    }
+  }
+  __syncthreads();
+  block_topn<NTH, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tsm, s_sel,
+                                    (p.sel_out && kfin == 0) ? p.sel_out + (size_t)bg * p.n : nullptr);
+  __syncthreads();
+  if (wave == 0) {  // routed blocks: selected and not always-taken (lane-parallel compaction)
+    const int lo_local = J - p.nloc + 1 > 0 ? J - p.nloc + 1 : 0;
+    const int j = lane < p.n ? s_sel[lane] : -1;
+    const bool routed = j >= 0 && j < lo_local && !(p.finit && j == 0);
+    const uint64_t m = __ballot(routed);
+    if (routed) s_items[__popcll(m & ((1ull << lane) - 1ull))] = j;
+    if (lane == 0) s_nitems = __popcll(m);
+  }
+  __syncthreads();
 
-  const int item = wg * 4 + wave;
-  if (item < s_nitems) {
-    const int jblk = s_items[item];
-    const bool insel = s_insel[item] != 0;
-    const int64_t x0 = (int64_t)jblk * LSEL;
+  // ---- this workgroup's share of the routed steps: one 32-token step per wave
+  Branch<DV> br;
+  br.init();
+  const int si = kfin * NWV + wave;
+  if (si < s_nitems * SPB) {
+    const int it = si / SPB, half = si - it * SPB;
+    const int64_t xb = (int64_t)s_items[it] * LSEL;
+    const int64_t x0 = xb + 32 * half;
+    const int64_t nv = min((int64_t)L, xb + LSEL);
     const int64_t row = raw_row0(p, b, g);
-    const uint16_t* kb = p.k + row * DK;
-    const uint16_t* vb = p.v + row * DV;
-    const int64_t nval = min((int64_t)L, x0 + LSEL);  // tokens of this block that exist
-    const bool anyW = x0 + LSEL - 1 >= wlo;
-
     u32x4_t qf[KT];
     load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
-    u32x4_t kf[NT][KT];
+    Step<DK, DV> st;
+    step_load<DK, DV>(st, p.k + row * DK, p.v + row * DV, x0, nv, lg, lr);
+    if (x0 < nv) {
+      float z[2][4];
+      step_logits<DK, DV>(st, qf, p.scale_log2, z);
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) load_k_tile<DK>(kb, x0 + 16 * tt + lr, nval, lg, kf[tt]);
-    uint32_t vr[NS][8][VW];
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) load_v_step<DV>(vb, x0 + 32 * s, nval, lg, lr, vr[s]);
-
-    float zs[2 * NS][4], zw[2 * NS][4];
-    float mxs = -INFINITY, mxw = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2 * NS; ++tt) {
-      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-      if (tt < NT) st = qk_tile<DK>(kf[tt < NT ? tt : 0], qf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t x = x0 + 16 * tt + 4 * lg + i;
-        const bool valid = tt < NT && x <= t;
-        const float z = st[i] * p.scale_log2;
-        zs[tt][i] = (valid && insel) ? z : -INFINITY;
-        zw[tt][i] = (valid && x >= wlo) ? z : -INFINITY;
-        mxs = fmaxf(mxs, zs[tt][i]);
-        mxw = fmaxf(mxw, zw[tt][i]);
-      }
-    }
-    m_s = max_over_groups(mxs);
-    m_w = max_over_groups(mxw);
-    if (insel) {
-#pragma unroll
-      for (int tt = 0; tt < 2 * NS; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(zs[tt][i] - m_s);
-          zs[tt][i] = e;
-          l_s += e;
-        }
-      l_s = sum_over_groups(l_s);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) pv_step<DV>(vr[s], pack_probs(zs[2 * s], zs[2 * s + 1]), accS);
-    }
-    if (anyW) {
-#pragma unroll
-      for (int tt = 0; tt < 2 * NS; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(zw[tt][i] - m_w);
-          zw[tt][i] = e;
-          l_w += e;
-        }
-      l_w = sum_over_groups(l_w);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) pv_step<DV>(vr[s], pack_probs(zw[2 * s], zw[2 * s + 1]), accW);
+        for (int i = 0; i < 4; ++i)
+          if (x0 + 16 * tt + 4 * lg + i >= nv) z[tt][i] = -INFINITY;
+      br.update(z, st.vr);
     }
   }
+  merge_waves_to<DV, NWV>(br, p.rpart + ((size_t)bg * p.nfin + kfin) * PSTRIDE, s_buf, s_stat);
+}
 
-  // ---- workgroup merge of the 4 waves, per branch, then the partial to memory
-  float* s_acc = smem;
-  float* s_st = smem + SM::kAcc;  // [grp*2 + (0:m,1:l)][wave][16]
-  if (lg == 0) {
-    s_st[(0 * 4 + wave) * 16 + lr] = m_s;
-    s_st[(1 * 4 + wave) * 16 + lr] = l_s;
-    s_st[(2 * 4 + wave) * 16 + lr] = m_w;
-    s_st[(3 * 4 + wave) * 16 + lr] = l_w;
-  }
-  float* part = p.part2 + ((size_t)bg * nw2 + wg) * 2 * PSTRIDE;
-  for (int grp = 0; grp < 2; ++grp) {
-#pragma unroll
-    for (int j = 0; j < VC; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_acc[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = grp == 0 ? accS[j][i] : accW[j][i];
-    __syncthreads();
-    float* pp = part + grp * PSTRIDE;
-    for (int e = tid; e < 16 * DV; e += 256) {
-      const int h = e / DV, ch = e - h * DV;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_st[(grp * 2 * 4 + w) * 16 + h]);
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = s_st[(grp * 2 * 4 + w) * 16 + h];
-        if (mw != -INFINITY) v += exp2f(mw - M) * s_acc[(w * 16 + h) * (DV + 1) + ch];
-      }
-      pp[32 + e] = v;
-    }
-    if (tid < 16) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_st[(grp * 2 * 4 + w) * 16 + tid]);
-      float ls = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = s_st[(grp * 2 * 4 + w) * 16 + tid];
-        if (mw != -INFINITY) ls += exp2f(mw - M) * s_st[((grp * 2 + 1) * 4 + w) * 16 + tid];
-      }
-      pp[tid] = M;
-      pp[16 + tid] = ls;
-    }
-    __syncthreads();
-  }
+// Combine: one workgroup per query head, one thread per output channel.
+//   o_cmp = sum_c f[c] * O_c (f from the finish kernel: exact normalised factors)
+//   o_slc = exact merge of the always-taken partial and the routed partials
+//   o_win = the window partial / its sum
+//   out   = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win  (bf16)
+// All loads of a thread are issued together (one round trip).
+template <int DV>
+__global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
+  constexpr int PSTRIDE = 32 + 16 * DV;
+  constexpr int kBatch = 16;
+  constexpr int kMaxFin = kMaxFinish;
+  __shared__ float s_f[kMaxChunks];
+  __shared__ float s_rm[kMaxFin + 1], s_rl[kMaxFin + 1];
+  const int qh = blockIdx.x;
+  const int b = qh / p.Hq, hq = qh - b * p.Hq;
+  const int g = hq / p.G, h = hq - g * p.G;
+  const int bg = b * p.H + g;
+  const int ch = threadIdx.x;
+  const int nch = p.nch, nfin = p.nfin;
+  const int L = seq_len_clamped(p, b);
+  const int nvis = n_visible(p, b, L);
+  const int nch_b = (nvis + kChunk - 1) / kChunk;
+  const size_t cbase = (size_t)bg * nch;
+  const float* wp = p.wpart + (size_t)bg * 2 * PSTRIDE;
+  const float* rp = p.rpart + (size_t)bg * nfin * PSTRIDE;
 
-  // ---- last workgroup: merge all partials and apply the gates
-  __threadfence();
+  for (int c = ch; c < nch_b; c += DV) s_f[c] = p.fcmp[(cbase + c) * 16 + h];
+  if (ch < nfin) {
+    s_rm[ch] = rp[(size_t)ch * PSTRIDE + h];
+    s_rl[ch] = rp[(size_t)ch * PSTRIDE + 16 + h];
+  }
+  if (ch == DV - 1) {  // always-taken partial of the selected branch
+    s_rm[kMaxFin] = wp[h];
+    s_rl[kMaxFin] = wp[16 + h];
+  }
+  float vo[kBatch], vr[kMaxFin];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) vo[u] = u < nch_b ? p.o1[((cbase + u) * 16 + h) * DV + ch] : 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxFin; ++k) vr[k] = k < nfin ? rp[(size_t)k * PSTRIDE + 32 + h * DV + ch] : 0.f;
+  const float vf = wp[32 + h * DV + ch];                     // always-taken partial
+  const float vwin = wp[PSTRIDE + 32 + h * DV + ch];         // window partial
+  const float lwin = wp[PSTRIDE + 16 + h];
+  const float* gt = p.gates + (size_t)qh * 3;
+  const float g0 = gt[0], g1 = gt[1], g2 = gt[2];
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&p.cnt2[bg], 1u) == (unsigned)(nw2 - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) p.cnt2[bg] = 0u;
-
-  float* fac = smem;  // [grp][wg][16]
-  const float* pall = p.part2 + (size_t)bg * nw2 * 2 * PSTRIDE;
-  if (tid < 32) {
-    const int grp = tid >> 4, h = tid & 15;
-    float M = -INFINITY;
-    for (int w2 = 0; w2 < nw2; ++w2) M = fmaxf(M, pall[(w2 * 2 + grp) * PSTRIDE + h]);
-    float ls = 0.f;
-    for (int w2 = 0; w2 < nw2; ++w2) {
-      const float mw = pall[(w2 * 2 + grp) * PSTRIDE + h];
-      if (mw != -INFINITY) ls += exp2f(mw - M) * pall[(w2 * 2 + grp) * PSTRIDE + 16 + h];
-    }
-    const float inv = ls > 0.f ? 1.0f / ls : 0.f;
-    for (int w2 = 0; w2 < nw2; ++w2) {
-      const float mw = pall[(w2 * 2 + grp) * PSTRIDE + h];
-      fac[(grp * nw2 + w2) * 16 + h] = mw != -INFINITY ? exp2f(mw - M) * inv : 0.f;
+  float oc = 0.f;
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) oc += (u < nch_b ? s_f[u] : 0.f) * vo[u];
+  for (int c0 = kBatch; c0 < nch_b; c0 += kBatch) {  // long contexts: remaining chunks
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = c0 + u < nch_b ? p.o1[((cbase + c0 + u) * 16 + h) * DV + ch] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) oc += (c0 + u < nch_b ? s_f[c0 + u] : 0.f) * v[u];
+  }
+  float M = s_rm[kMaxFin];
+  for (int k = 0; k < nfin; ++k) M = fmaxf(M, s_rm[k]);
+  float vs = 0.f, ls = 0.f;
+  if (s_rm[kMaxFin] != -INFINITY) {
+    const float a = exp2f(s_rm[kMaxFin] - M);
+    vs += a * vf;
+    ls += a * s_rl[kMaxFin];
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxFin; ++k) {
+    if (k < nfin && s_rm[k] != -INFINITY) {
+      const float a = exp2f(s_rm[k] - M);
+      vs += a * vr[k];
+      ls += a * s_rl[k];
     }
   }
-  __syncthreads();
-  const float* oc = p.ocmp + (size_t)bg * 16 * DV;
-  for (int e = tid; e < p.G * DV; e += 256) {
-    const int h = e / DV;
-    float os = 0.f, ow = 0.f;
-    for (int w2 = 0; w2 < nw2; ++w2) {
-      os += fac[(0 * nw2 + w2) * 16 + h] * pall[(w2 * 2 + 0) * PSTRIDE + 32 + e];
-      ow += fac[(1 * nw2 + w2) * 16 + h] * pall[(w2 * 2 + 1) * PSTRIDE + 32 + e];
-    }
-    const int64_t qh = (int64_t)b * p.Hq + (int64_t)g * p.G + h;
-    const float r = oc[e] + p.gates[qh * 3 + 1] * os + p.gates[qh * 3 + 2] * ow;
-    p.out[qh * DV + (e - h * DV)] = (uint16_t)f32_to_bf16(r);
-  }
+  const float os = ls > 0.f ? vs / ls : 0.f;
+  const float ow = lwin > 0.f ? vwin / lwin : 0.f;
+  p.out[(size_t)qh * DV + ch] = (uint16_t)f32_to_bf16(g0 * oc + g1 * os + g2 * ow);
 }
 
 // ---------------------------------------------------------------- host side
@@ -476,44 +658,56 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   lay.nch = (int)((nc + kChunk - 1) / kChunk);
   if (lay.nch < 1) lay.nch = 1;
   lay.nbo = (int)((int64_t)kChunk * d / lsel);
-  const int umax = n + (w + lsel - 1) / lsel + 1;
-  lay.nw2 = (umax + 3) / 4;
   const size_t BH = (size_t)B * H;
   size_t off = 0;
-  lay.off_cnt1 = off; off = align256(off + BH * 4);
-  lay.off_cnt2 = off; off = align256(off + BH * 4);
   lay.off_m1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
   lay.off_l1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
   lay.off_o1 = off;   off = align256(off + BH * lay.nch * 16 * (size_t)DV * 4);
   lay.off_sc1 = off;  off = align256(off + BH * lay.nch * 16 * (size_t)(lay.nbo + 1) * 4);
-  lay.off_ocmp = off; off = align256(off + BH * 16 * (size_t)DV * 4);
-  lay.off_sel = off;  off = align256(off + BH * (size_t)n * 4);
-  lay.off_part2 = off; off = align256(off + BH * lay.nw2 * 2 * (32 + 16 * (size_t)DV) * 4);
+  // one window workgroup per (sequence, group): two branch partials
+  lay.off_wpart = off; off = align256(off + BH * 2 * (32 + 16 * (size_t)DV) * 4);
+  // finish workgroups: one partial each; normalised compressed-branch factors
+  const int spb = lsel >= 32 ? lsel / 32 : 1;
+  lay.nfin = (n * spb + 7) / 8;
+  lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
+  lay.off_fcmp = off; off = align256(off + BH * lay.nch * 16 * 4);
   lay.total = off;
   return lay;
 }
 
 template <int DK, int DV>
-static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  const dim3 blk(256);
-  hipLaunchKernelGGL((decode_cmp_kernel<DK, DV>), dim3((unsigned)(p.B * p.H * p.nch)), blk, 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 g2((unsigned)(p.B * p.H * p.nw2));
+static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const PhaseEvents* ev) {
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev->ev[0], s)) != hipSuccess) return e;
+  const dim3 g1((unsigned)(p.B * p.H * (p.nch + 1))), b1(64 * kCmpWaves);
   switch (p.lsel) {
-    case 16: hipLaunchKernelGGL((decode_sw_kernel<DK, DV, 16>), g2, blk, 0, s, p); break;
-    case 32: hipLaunchKernelGGL((decode_sw_kernel<DK, DV, 32>), g2, blk, 0, s, p); break;
-    case 64: hipLaunchKernelGGL((decode_sw_kernel<DK, DV, 64>), g2, blk, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((decode_sw_kernel<DK, DV, 128>), g2, blk, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 16>), g1, b1, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 32>), g1, b1, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 64>), g1, b1, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 128>), g1, b1, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev->ev[1], s)) != hipSuccess) return e;
+  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(512);
+  switch (p.lsel) {
+    case 16: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 16>), g2, blk, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 32>), g2, blk, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 64>), g2, blk, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 128>), g2, blk, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<DV>), dim3((unsigned)(p.B * p.Hq)), dim3(DV), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev->ev[2], s)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s) {
-  if (DK == 192 && DV == 128) return launch_decode_t<192, 128>(p, s);
-  if (DK == 128 && DV == 128) return launch_decode_t<128, 128>(p, s);
-  if (DK == 64 && DV == 64) return launch_decode_t<64, 64>(p, s);
+hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev) {
+  if (DK == 192 && DV == 128) return launch_decode_t<192, 128>(p, s, ev);
+  if (DK == 128 && DV == 128) return launch_decode_t<128, 128>(p, s, ev);
+  if (DK == 64 && DV == 64) return launch_decode_t<64, 64>(p, s, ev);
   return hipErrorInvalidValue;
 }
 

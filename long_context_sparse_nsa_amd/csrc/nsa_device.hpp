@@ -66,9 +66,11 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int h) {
   return h ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
 }
 
-// Exclusive prefix sum over the 256 threads of a block (4 waves).  `scratch`
-// holds at least 4 ints in LDS.  Returns the exclusive prefix; *total gets the sum.
-__device__ __forceinline__ int block_scan_256(int v, int* scratch, int* total) {
+// Exclusive prefix sum over the NT threads of a block (NT/64 waves).  `scratch`
+// holds at least NT/64 ints in LDS.  Returns the exclusive prefix; *total gets the sum.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, int* scratch, int* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -80,7 +82,7 @@ __device__ __forceinline__ int block_scan_256(int v, int* scratch, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     int s = scratch[w];
     if (w < wave) base += s;
     tot += s;

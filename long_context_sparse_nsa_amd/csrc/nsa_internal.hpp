@@ -7,14 +7,25 @@
 
 namespace nsa {
 
-// Compressed keys handled by one decode workgroup (4 waves x 64 keys).
-constexpr int kChunk = 256;
+// Shape of the decode compressed-branch pass: each workgroup streams one chunk
+// of kCmpWaves * kCmpKeysPerWave compressed keys.
+#ifndef NSA_CMP_KPW
+#define NSA_CMP_KPW 64
+#endif
+#ifndef NSA_CMP_NWV
+#define NSA_CMP_NWV 4
+#endif
+constexpr int kCmpKeysPerWave = NSA_CMP_KPW;
+constexpr int kCmpWaves = NSA_CMP_NWV;
+constexpr int kChunk = kCmpKeysPerWave * kCmpWaves;
 // Limits of the on-chip tables (checked by the host before any launch).
-constexpr int kMaxChunks = 128;      // chunks per sequence in decode  (Nc <= 32768)
+constexpr int kMaxCompressed = 32768;                 // compressed blocks per sequence in decode
+constexpr int kMaxChunks = kMaxCompressed / kChunk;   // chunks per sequence in decode
 constexpr int kMaxBlocks = 8192;     // selection candidates J+1
 constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query
 constexpr int kGPad = 16;            // query heads per group, padded to one MFMA tile
+constexpr int kMaxFinish = 16;       // decode finish workgroups per (sequence, group)
 
 // Everything the decode kernels need; plain values and device pointers.
 struct DecodeParams {
@@ -34,24 +45,22 @@ struct DecodeParams {
   const float* gates;                // [B, Hq, 3]
   uint16_t* out;                     // [B, Hq, DV]
   int32_t* sel_out;                  // [B, H, n] or null
-  // workspace
-  uint32_t* cnt1;                    // [B*H]
-  uint32_t* cnt2;                    // [B*H]
+  // workspace (contents on entry are irrelevant)
   float* m1;                         // [B*H, nch, 16]
   float* l1;                         // [B*H, nch, 16]
   float* o1;                         // [B*H, nch, 16, DV]
   float* sc1;                        // [B*H, nch, 16, nbo+1]
-  float* ocmp;                       // [B*H, 16, DV] gated compressed-branch output
-  int32_t* sel;                      // [B*H, n]
-  float* part2;                      // [B*H, nw2, 2, 32 + 16*DV]
-  int nch;                           // launch width of the compressed pass
+  float* wpart;                      // [B*H, 2, 32 + 16*DV] window-workgroup partials
+  float* rpart;                      // [B*H, nfin, 32 + 16*DV] routed-block partials
+  float* fcmp;                       // [B*H, nch, 16] normalised compressed-branch factors
+  int nch;                           // chunk workgroups per (sequence, group)
   int nbo;                           // selection blocks owned by one chunk = kChunk*d/lsel
-  int nw2;                           // launch width of the selected/window pass
+  int nfin;                          // finish workgroups per (sequence, group)
 };
 
 struct DecodeLayout {
-  size_t off_cnt1, off_cnt2, off_m1, off_l1, off_o1, off_sc1, off_ocmp, off_sel, off_part2, total;
-  int nch, nbo, nw2;
+  size_t off_m1, off_l1, off_o1, off_sc1, off_wpart, off_rpart, off_fcmp, total;
+  int nch, nbo, nfin;
 };
 
 // Parameters of the per-query prefill kernel and the compression kernel.
@@ -86,7 +95,13 @@ struct CompressParams {
 
 DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int w, int64_t max_len);
 
-hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s);
+// Optional events recorded before the first and after each of the two decode
+// kernels (null = none).
+struct PhaseEvents {
+  hipEvent_t ev[3];
+};
+
+hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);
 hipError_t launch_compress(const CompressParams& p, hipStream_t s);
 

@@ -173,24 +173,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      {  // fold onto the selection blocks this slice touches
-        const int64_t jlo = (int64_t)key0 * p.d / p.lsel;
+      {  // fold onto the selection blocks this slice touches (units of the stride d:
+         // key i covers [i, i+q), block j covers [j*r, (j+1)*r))
+        const int q = p.l / p.d, r = p.lsel / p.d;
+        const int jlo = key0 / r;
         const int kend = min(key0 + 64, nvis);
         if (lane < nbs) {
-          const int64_t j = jlo + lane;
-          const int64_t lo_tok = j * p.lsel, hi_tok = lo_tok + p.lsel;
-          const int64_t a = lo_tok - p.l;
-          int64_t ilo = a < 0 ? 0 : a / p.d + 1;
-          if (ilo < key0) ilo = key0;
-          int64_t ihi = (hi_tok - 1) / p.d;
-          if (ihi > kend - 1) ihi = kend - 1;
+          const int lo = (jlo + lane) * r, hi = lo + r;
+          const int ilo = max(key0, lo - q + 1), ihi = min(kend - 1, hi - 1);
           float s = 0.f;
-          for (int64_t i = ilo; i <= ihi; ++i) {
-            const int64_t x0 = i * p.d;
-            const int64_t ov = min(x0 + p.l, hi_tok) - max(x0, lo_tok);
-            s += (float)ov * psum[i - key0];
-          }
-          s_fold[sl * kPfMaxSlots + lane] = s * (1.0f / (float)p.l);
+          for (int i = ilo; i <= ihi; ++i) s += (float)(min(i + q, hi) - max(i, lo)) * psum[i - key0];
+          s_fold[sl * kPfMaxSlots + lane] = s * (1.0f / (float)q);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -202,26 +195,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 
   // ---- group scores of candidates 0..J (slice contributions added in slice order)
   const int J = t / LSEL;
-  for (int j = tid; j <= J; j += 256) {
-    float s = 0.f;
-    if (nvis > 0) {
-      const int64_t lo_tok = (int64_t)j * LSEL, hi_tok = lo_tok + LSEL;
-      const int64_t a = lo_tok - p.l;
-      int64_t ilo = a < 0 ? 0 : a / p.d + 1;
-      int64_t ihi = (hi_tok - 1) / p.d;
-      if (ihi > nvis - 1) ihi = nvis - 1;
+  {
+    const int q = p.l / p.d, r = p.lsel / p.d;
+    for (int j = tid; j <= J; j += 256) {
+      float s = 0.f;
+      const int ilo = max(0, j * r - q + 1), ihi = min(nvis - 1, (j + 1) * r - 1);
       if (ilo <= ihi) {
-        for (int64_t sl = ilo / 64; sl <= ihi / 64; ++sl) {
-          const int64_t jlo = sl * 64 * p.d / LSEL;
-          s += s_fold[sl * kPfMaxSlots + (j - jlo)];
-        }
+        for (int sl = ilo / 64; sl <= ihi / 64; ++sl) s += s_fold[sl * kPfMaxSlots + (j - sl * 64 / r)];
       }
+      S[j] = s;
     }
-    S[j] = s;
   }
   __syncthreads();
   int32_t* selg = p.sel_out ? p.sel_out + (((int64_t)b * p.T + t) * p.H + g) * p.n : nullptr;
-  block_topn(S, J, p.n, p.nloc, p.finit, flag, tsm, s_sel, selg);
+  block_topn<256, 16>(S, J, p.n, p.nloc, p.finit, tsm, s_sel, selg);
   __syncthreads();
 
   // ---- selected and window branches over the sorted union of their blocks

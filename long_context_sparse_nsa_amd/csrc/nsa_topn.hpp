@@ -1,4 +1,4 @@
-// Block-wide top-n block selection for one (query, KV group), 256 threads.
+// Block-wide top-n block selection for one (query, KV group), NT threads.
 //
 // Candidates are blocks 0..J with group scores S[j] >= 0 (in LDS).  Block 0
 // (force_initial) and the n_local trailing blocks J, J-1, ... are always taken
@@ -8,117 +8,131 @@
 // "NSA: три ветви", selection paragraph (16 best blocks, always including the
 // initial block and two local ones).
 //
-// Method: a 4-pass, 8-bit MSB-first radix select over the float bit patterns
-// (non-negative floats order like their unsigned bits) finds the value T of the
-// last routed pick and how many candidates equal to T are still needed; a
-// block-wide prefix count over candidates in index order then takes the
-// lowest-index ties.  Every step is a count, so the result is deterministic.
+// Method: every candidate gets the unique 64-bit key
+//   (bits of S[j]) << 32 | (0xFFFFFFFF - j)
+// (non-negative floats order like their bit patterns, and the low word prefers
+// the lower block id on equal scores), so "best" is simply the largest key.
+// Each wave extracts the n_r largest keys of its share of the candidates by n_r
+// rounds of a wave-wide max (DPP row operations, no LDS atomics); wave 0 then extracts
+// the n_r largest of the waves' winners the same way.  The final ascending list
+// is formed by lane-parallel ranking.  Fully deterministic.
 #pragma once
 #include "nsa_device.hpp"
 
 namespace nsa {
 
+constexpr int kTopnMaxRouted = 64;
+
 struct TopnSmem {
-  int hist[256];
-  int scratch[8];
-  int pick[2];
+  uint64_t wbest[16 * kTopnMaxRouted];  // per-wave winners
 };
 
-// flag: LDS byte per candidate (>= J+1 entries).  Writes the ascending list to
-// out[0..n) (padded with -1) and, if out2 != null, to out2 as well.
-__device__ void block_topn(const float* S, int J, int n, int nloc, int finit, uint8_t* flag, TopnSmem& sm,
-                           int32_t* out, int32_t* out2) {
-  const int tid = threadIdx.x;
-  const int ncand = J + 1;
-  for (int j = tid; j < ncand; j += 256) flag[j] = (ncand <= n) ? 1 : 0;
-  __syncthreads();
-  if (ncand > n) {
-    if (tid == 0) {
-      if (finit) flag[0] = 2;
-      for (int r = 0; r < nloc; ++r)
-        if (J - r >= 0) flag[J - r] = 2;
-    }
-    // forced count: the n_local trailing blocks (clipped at 0) plus block 0 if
-    // it is not already one of them
-    const int nl = nloc < ncand ? nloc : ncand;
-    const int nf = nl + ((finit && J - nloc + 1 > 0) ? 1 : 0);
-    int rem = n - nf;
-    __syncthreads();
-    if (rem > 0) {
-      uint32_t prefix = 0, pmask = 0;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        sm.hist[tid] = 0;
-        __syncthreads();
-        for (int j = tid; j < ncand; j += 256) {
-          if (flag[j] == 0) {
-            const uint32_t u = __float_as_uint(S[j]);
-            if ((u & pmask) == prefix) atomicAdd(&sm.hist[(u >> shift) & 255u], 1);
-          }
-        }
-        __syncthreads();
-        if (tid < 64) {
-          const int lane = tid;
-          const int c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
-                    c3 = sm.hist[4 * lane + 3];
-          const int tot = c0 + c1 + c2 + c3;
-          int suf = tot;  // inclusive suffix sum over lanes >= lane
+// Wave-wide maximum of an unsigned value with DPP row shifts and row broadcasts
+// (lane 63 accumulates the maximum of all lanes), then broadcast from lane 63.
+// Lanes whose DPP source is out of range read 0, the identity of the maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Extract the `rounds` (<= 64) largest of the keys held in k[0..K) over the
+// wave; returns the r-th winner in lane r (0 when none is left).  A key is
+// compared by its high word (score bits) and then its low word (inverted id).
+template <int K>
+__device__ __forceinline__ uint64_t wave_extract(uint64_t (&k)[K], int rounds) {
+  const int lane = threadIdx.x & 63;
+  uint64_t mine_win = 0;
+  for (int r = 0; r < rounds; ++r) {
+    uint64_t mine = k[0];
 #pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            int y = __shfl_down(suf, o);
-            if (lane + o < 64) suf += y;
-          }
-          const int above = suf - tot;  // candidates in higher bins of other lanes
-          const int g3 = above + c3, g2 = g3 + c2, g1 = g2 + c1, g0 = g1 + c0;
-          // chosen bin b: (# >= b) >= rem and (# > b) < rem
-          if (g3 >= rem && above < rem) { sm.pick[0] = 4 * lane + 3; sm.pick[1] = above; }
-          if (g2 >= rem && g3 < rem)    { sm.pick[0] = 4 * lane + 2; sm.pick[1] = g3; }
-          if (g1 >= rem && g2 < rem)    { sm.pick[0] = 4 * lane + 1; sm.pick[1] = g2; }
-          if (g0 >= rem && g1 < rem)    { sm.pick[0] = 4 * lane + 0; sm.pick[1] = g1; }
-        }
-        __syncthreads();
-        const uint32_t bin = (uint32_t)sm.pick[0];
-        rem -= sm.pick[1];
-        prefix |= bin << shift;
-        pmask |= 255u << shift;
-        __syncthreads();
-      }
-      // take every candidate above the threshold, and the `rem` lowest-index ties
-      const int R = (ncand + 255) / 256;
-      const int j0 = tid * R, j1 = min(j0 + R, ncand);
-      int eq = 0;
-      for (int j = j0; j < j1; ++j)
-        if (flag[j] == 0 && __float_as_uint(S[j]) == prefix) ++eq;
-      int total;
-      int base = block_scan_256(eq, sm.scratch, &total);
-      for (int j = j0; j < j1; ++j) {
-        if (flag[j] != 0) continue;
-        const uint32_t u = __float_as_uint(S[j]);
-        if (u > prefix) flag[j] = 1;
-        else if (u == prefix) {
-          if (base < rem) flag[j] = 1;
-          ++base;
-        }
-      }
+    for (int q = 1; q < K; ++q) mine = k[q] > mine ? k[q] : mine;
+    const uint32_t hi = (uint32_t)(mine >> 32), lo = (uint32_t)mine;
+    const uint32_t Mh = wave_max_u32(hi);
+    const uint32_t Ml = wave_max_u32(hi == Mh ? lo : 0u);
+    const uint64_t best = ((uint64_t)Mh << 32) | Ml;
+    if (best == 0) break;  // nothing left anywhere in the wave (uniform)
+#pragma unroll
+    for (int q = 0; q < K; ++q)
+      if (k[q] == best) k[q] = 0;  // keys are unique: exactly one lane holds it
+    if (lane == r) mine_win = best;
+  }
+  return mine_win;
+}
+
+// Candidates with key 0 are excluded.  MAXC bounds the candidates per lane:
+// ceil(ceil((J+1)/(NT/64)) / 64) <= MAXC.
+template <int NT, int MAXC>
+__device__ void block_topn(const float* S, int J, int n, int nloc, int finit, TopnSmem& sm, int32_t* out,
+                           int32_t* out2) {
+  static_assert(NT % 64 == 0 && NT <= 1024, "block size");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ncand = J + 1;
+  if (ncand <= n) {  // every candidate is taken
+    for (int r = tid; r < n; r += NT) {
+      const int v = r < ncand ? r : -1;
+      out[r] = v;
+      if (out2) out2[r] = v;
     }
+    return;
+  }
+  const int lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;  // local blocks are [lo_local, J]
+  const bool f0 = finit && lo_local > 0;                      // block 0 forced separately
+  const int nf = (J - lo_local + 1) + (f0 ? 1 : 0);
+  const int nr = n - nf;                                      // routed picks (uniform)
+  if (nr > 0) {
+    // ---- per-wave extraction over a contiguous share of the candidates; the
+    // number of key slots per lane is picked from the actual candidate count
+    const int per_wave = (ncand + NW - 1) / NW;
+    const int c0 = wave * per_wave;
+    auto key = [&](int q) -> uint64_t {
+      const int j = c0 + lane + 64 * q;
+      const bool ok = q * 64 + lane < per_wave && j < lo_local && !(f0 && j == 0);
+      return ok ? ((uint64_t)__float_as_uint(S[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j) : 0ull;
+    };
+    uint64_t w;
+    if (per_wave <= 128 || MAXC <= 2) {
+      uint64_t k[2] = {key(0), key(1)};
+      w = wave_extract<2>(k, nr);
+    } else if (per_wave <= 512 || MAXC <= 8) {
+      uint64_t k[8 < MAXC ? 8 : MAXC];
+#pragma unroll
+      for (int q = 0; q < (8 < MAXC ? 8 : MAXC); ++q) k[q] = key(q);
+      w = wave_extract<(8 < MAXC ? 8 : MAXC)>(k, nr);
+    } else {
+      uint64_t k[MAXC];
+#pragma unroll
+      for (int q = 0; q < MAXC; ++q) k[q] = key(q);
+      w = wave_extract<MAXC>(k, nr);
+    }
+    sm.wbest[wave * kTopnMaxRouted + lane] = w;
     __syncthreads();
   }
-  // ascending compaction of the taken blocks
-  const int R = (ncand + 255) / 256;
-  const int j0 = tid * R, j1 = min(j0 + R, ncand);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += flag[j] != 0;
-  int total;
-  int pos = block_scan_256(cnt, sm.scratch, &total);
-  for (int j = j0; j < j1; ++j) {
-    if (flag[j] != 0 && pos < n) {
-      out[pos] = j;
-      if (out2) out2[pos] = j;
-      ++pos;
+  if (wave == 0) {
+    // ---- wave 0: merge the waves' winners, add the forced blocks, rank
+    int v = INT32_MAX;
+    if (nr > 0) {
+      uint64_t k2[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) k2[w] = lane < nr ? sm.wbest[w * kTopnMaxRouted + lane] : 0ull;
+      const uint64_t best = wave_extract<NW>(k2, nr);
+      if (lane < nr) v = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
     }
-  }
-  for (int r = total + tid; r < n; r += 256) {
-    out[r] = -1;
-    if (out2) out2[r] = -1;
+    if (lane >= nr && lane < n) {
+      const int i = lane - nr;  // forced block i
+      v = f0 ? (i == 0 ? 0 : lo_local + i - 1) : lo_local + i;
+    }
+    int rank = 0;
+    for (int q = 0; q < n; ++q) rank += __builtin_amdgcn_readlane(v, q) < v;
+    if (lane < n) {
+      out[rank] = v;
+      if (out2) out2[rank] = v;
+    }
   }
 }
 

@@ -90,6 +90,9 @@ def run_decode(case, kc_bits=None, vc_bits=None, gates=None, ws=None):
         N.nsa_compress_kv(dims, cfg, k, v, cu, seq, max_len, dev_bits(case.w_k), dev_bits(case.pe_k),
                           dev_bits(case.w_v), dev_bits(case.pe_v), kc, vc, cu_c)
     else:
+        if kc_bits.shape[0] == 0:  # no complete block yet: the cache is never read, but must not be NULL
+            kc_bits = np.zeros((1, wl.d_k), np.uint16)
+            vc_bits = np.zeros((1, wl.d_v), np.uint16)
         kc, vc = dev_bits(kc_bits), dev_bits(vc_bits)
     g = torch.from_numpy(np.ascontiguousarray(case.gates if gates is None else gates, dtype=np.float32)).cuda()
     out = torch.empty((wl.batch, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")

@@ -1,0 +1,127 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The GPU runs the whole batch; the oracle recomputes sampled (sequence, group)
+pairs or query rows exactly, and every other output is checked for the
+invariants that hold at any size (forced blocks present, ascending, within
+range, finite outputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_nsa_amd as N
+import nsa_inputs as I
+from oracle import nsa_oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _seed(name):
+    return list(I.WORKLOADS).index(name)
+
+
+def _invariants(case, sel):
+    p = case.p
+    for b in range(case.wl.batch):
+        t = int(case.seq_lens[b]) - 1
+        J = t // p.l_sel
+        for g in range(case.wl.num_kv_heads):
+            s = [int(x) for x in sel[b, g] if x >= 0]
+            assert len(s) == min(p.n_sel, J + 1)
+            assert s == sorted(set(s)) and s[-1] <= J and s[0] >= 0
+            assert set(O.forced_blocks(J, p.n_local, p.force_initial)) <= set(s)
+
+
+def _decode_full(name, samples):
+    case = I.generate(I.workload(name), _seed(name))
+    print(f"[{name}] generated, running GPU", flush=True)
+    out, sel, _ = U.run_decode(case)
+    assert np.isfinite(out).all()
+    _invariants(case, sel)
+    G = case.wl.num_q_heads // case.wl.num_kv_heads
+    for b, g in samples:
+        res = O.decode_group(case, b, g)
+        t = int(case.seq_lens[b]) - 1
+        res = U.check_selection(res, sel[b, g], t, case.p, lambda idx: O.decode_group(case, b, g, override_idx=idx))
+        e = U.assert_close(out[b, g * G:(g + 1) * G], res.out, f"{name} b={b} g={g}")
+        print(f"[{name}] b={b} g={g}: max-abs {e[0]:.3g} mean-abs {e[1]:.3g}", flush=True)
+
+
+def test_decode_64k_batch8():
+    _decode_full("decode_64k_b8", [(0, 0), (7, 3)])
+
+
+def test_decode_128k_batch4():
+    _decode_full("decode_128k_b4", [(3, 1)])
+
+
+def test_decode_ragged_16():
+    _decode_full("decode_ragged_16", [(0, 2), (11, 0)])
+
+
+def test_prefill_32k_sampled_rows():
+    name = "prefill_32k"
+    case = I.generate(I.workload(name), _seed(name))
+    out, sel = U.run_prefill(case)
+    assert np.isfinite(out).all()
+    p = case.p
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 30, 31, 63, 64, 511, 512, 4095, 16383, 32766, 32767] +
+                      rng.integers(0, 32768, 5).tolist()))
+    G = case.wl.num_q_heads // case.wl.num_kv_heads
+    for g in (0, 3):
+        K, V, Kc, Vc = O.compress_group(case, 0, g)
+        res = O.prefill_rows(case, 0, g, rows, K, V, Kc, Vc)
+        got, want = [], []
+        for t, r in zip(rows, res):
+            r = U.check_selection(r, sel[0, t, g], t, p,
+                                  lambda idx, t=t: O.prefill_rows(case, 0, g, [t], K, V, Kc, Vc, [idx])[0])
+            got.append(out[0, t, g * G:(g + 1) * G])
+            want.append(r.out)
+        e = U.assert_close(np.stack(got), np.stack(want), f"prefill g={g}")
+        print(f"[{name}] g={g}: max-abs {e[0]:.3g} mean-abs {e[1]:.3g}", flush=True)
+    # every row: forced blocks present, ascending, no future block
+    T = case.wl.seq_len
+    t = np.arange(T)
+    J = t // p.l_sel
+    s = sel[0]                                            # [T, H, n]
+    valid = s >= 0
+    assert np.all(valid.sum(-1) == np.minimum(p.n_sel, J + 1)[:, None])
+    assert np.all(np.where(valid, s, -1) <= J[:, None, None])
+    assert np.all(s[:, :, 0] == 0)                        # block 0 always taken
+
+
+def test_graph_replay_matches_eager():
+    """The benchmark replays decode steps from a captured graph: every replay must equal eager."""
+    case = I.generate(I.workload("decode_64k_b8", batch=2, seq_len=9000), 21)
+    dims, cfg = U.dims_cfg(case)
+    out_e, sel_e, (kc, vc) = U.run_decode(case)
+    q, k, v = U.dev_bits(case.q), U.dev_bits(case.k), U.dev_bits(case.v)
+    seq = torch.from_numpy(case.seq_lens).cuda()
+    cu = torch.from_numpy(case.cu_seqlens).cuda()
+    cuc = torch.from_numpy(U.cmp_offsets(case)).cuda()
+    gates = torch.from_numpy(case.gates).cuda()
+    out = torch.empty((2, case.wl.num_q_heads, case.wl.d_v), dtype=torch.bfloat16, device="cuda")
+    sel = torch.empty((2, case.wl.num_kv_heads, cfg.n_sel), dtype=torch.int32, device="cuda")
+    ws = N.new_workspace(N.nsa_decode_workspace_size(dims, cfg, 9000))
+    N.nsa_decode_fwd(dims, cfg, q, k, v, kc, vc, seq, cu, cuc, 9000, gates, out, sel, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            N.nsa_decode_fwd(dims, cfg, q, k, v, kc, vc, seq, cu, cuc, 9000, gates, out, sel, ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        sel.fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(U.bits_to_f64(U.host_bits(out)), out_e)
+        np.testing.assert_array_equal(sel.cpu().numpy(), sel_e)
+        # eager work between replays
+        N.nsa_decode_fwd(dims, cfg, q, k, v, kc, vc, seq, cu, cuc, 9000, gates, out, sel, ws)
+        torch.cuda.synchronize()
