@@ -199,18 +199,18 @@ def bench_decode(args, torch, N, I):
 
     # per-pass durations from the library's phase events (eager, queued behind a sleep)
     n_ph = min(K, 60)
-    hev = HipEvents(3 * n_ph)
+    hev = HipEvents(4 * n_ph)
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e7))
     for i in range(n_ph):
-        N.nsa_set_decode_phase_events(hev.ev[3 * i:3 * i + 3])
+        N.nsa_set_decode_phase_events(hev.ev[4 * i:4 * i + 4])
         step(i)
     N.nsa_set_decode_phase_events(None)
     torch.cuda.synchronize()
-    ph = [float(np.mean([hev.ms(3 * i + k, 3 * i + k + 1) for i in range(n_ph)])) for k in range(2)]
+    ph = [float(np.mean([hev.ms(4 * i + k, 4 * i + k + 1) for i in range(n_ph)])) for k in range(3)]
     hev.close()
     p1 = ph[0]
-    p2 = ph[1]
+    p2 = ph[1] + ph[2]
     sel_h = sel.cpu().numpy()
     b_step, b_cmp, b_sw = decode_bytes(case, sel_h)
     gbs_step = b_step / (ms_step * 1e-3) / 1e9
@@ -220,12 +220,13 @@ def bench_decode(args, torch, N, I):
         tokens_per_s=wl.batch / (ms_step * 1e-3),
         step_bytes=b_step, step_gbs=gbs_step, step_frac=gbs_step / HBM_PEAK_GBS,
         pass1_us=p1 * 1e3, pass2_us=p2 * 1e3, pass1_bytes=b_cmp, pass2_bytes=b_sw,
+        finish_us=ph[1] * 1e3, combine_us=ph[2] * 1e3,
 
         pass1_gbs=gbs_cmp, pass2_gbs=b_sw / (p2 * 1e-3) / 1e9,
     )
     log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step ({timing}), {res['tokens_per_s']:.4g} tok/s, "
         f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: cmp {p1 * 1e3:.1f} us "
-        f"({gbs_cmp:.0f} GB/s), finish {p2 * 1e3:.1f} us")
+        f"({gbs_cmp:.0f} GB/s), finish {ph[1] * 1e3:.1f} us, combine {ph[2] * 1e3:.1f} us")
     return case, res, T
 
 
@@ -385,8 +386,9 @@ def main():
                      "duration_us": dec["pass1_us"], "algorithmic_bytes": dec["pass1_bytes"]},
         "decode_step": {"algorithmic_bytes": dec["step_bytes"], "GB/s": dec["step_gbs"],
                         "hbm_frac": dec["step_frac"],
-                        "kernel_us": {"decode_cmp_kernel": dec["pass1_us"], "decode_finish_kernel": dec["pass2_us"]},
-                        "finish_GB/s": dec["pass2_gbs"], "wall_s_timed_region": dec["wall_s"]},
+                        "kernel_us": {"decode_cmp_kernel": dec["pass1_us"], "decode_finish_kernel": dec["finish_us"],
+                                      "decode_combine_kernel": dec["combine_us"]},
+                        "wall_s_timed_region": dec["wall_s"]},
         "cpu_baseline": cpu,
     }
     if pre:

@@ -168,13 +168,14 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
                                         int64_t seq_len, int32_t compress_in_call, size_t* bytes);
 
 /* Profiling hook: until called again on this thread, every nsa_decode_fwd on
- * this thread records the caller-owned hipEvent_t handles events[0..2] on the
- * call's stream: before the compressed-branch kernel, after it (i.e. before the
- * kernel doing selection, selected/window attention and the gated sum) and
- * after that one, so a caller can time each kernel with hipEventElapsedTime.
- * count = 0 (the default) records nothing; any count other than 0 or 3, or a
- * NULL handle, is NSA_ERROR_INVALID_VALUE.  The array is copied; the events are
- * not. */
+ * this thread records the caller-owned hipEvent_t handles events[0..3] on the
+ * call's stream around its three kernels: before the compressed-branch kernel
+ * (which also runs the window branch), after it, after the selection kernel
+ * (top-n and the routed selected blocks) and after the combine kernel (exact
+ * merge and gated sum), so a caller can time each kernel with
+ * hipEventElapsedTime.  count = 0 (the default) records nothing; any count
+ * other than 0 or 4, or a NULL handle, is NSA_ERROR_INVALID_VALUE.  The array
+ * is copied; the events are not. */
 nsa_status_t nsa_set_decode_phase_events(void* const* events, int32_t count);
 
 /* Human-readable name of a status code (static storage). */

@@ -91,10 +91,13 @@ nsa_status_t check_decode_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg,
   if ((int64_t)dims->batch * dims->num_kv_heads * ((nc + nsa::kChunk - 1) / nsa::kChunk + 1) > (int64_t)INT32_MAX / 2)
     return fail(NSA_ERROR_UNSUPPORTED, "launch too large");
   const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
-                                                   cfg->l_sel, cfg->n_sel, cfg->w, max_seq_len);
+                                                   cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
   if (lay.nfin > nsa::kMaxFinish)
     return fail(NSA_ERROR_UNSUPPORTED, "n_sel=%d with l_sel=%d needs more than %d selection workgroups", cfg->n_sel,
                 cfg->l_sel, nsa::kMaxFinish);
+  if (lay.nwin > nsa::kMaxWindow)
+    return fail(NSA_ERROR_UNSUPPORTED, "w=%d with l_sel=%d needs more than %d window workgroups", cfg->w, cfg->l_sel,
+                nsa::kMaxWindow);
 
   return NSA_SUCCESS;
 }
@@ -151,8 +154,8 @@ nsa_status_t nsa_set_decode_phase_events(void* const* events, int32_t count) {
     g_phase_on = false;
     return ok();
   }
-  if (count != 3 || !events) return fail(NSA_ERROR_INVALID_VALUE, "give 3 events (or count 0)");
-  for (int i = 0; i < 3; ++i) {
+  if (count != 4 || !events) return fail(NSA_ERROR_INVALID_VALUE, "give 4 events (or count 0)");
+  for (int i = 0; i < 4; ++i) {
     if (!events[i]) return fail(NSA_ERROR_INVALID_VALUE, "phase event %d is NULL", i);
     g_phase_events.ev[i] = static_cast<hipEvent_t>(events[i]);
   }
@@ -167,7 +170,7 @@ nsa_status_t nsa_decode_workspace_size(const nsa_dims_t* dims, const nsa_config_
   if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
   if ((st = check_decode_sizes(dims, cfg, max_seq_len)) != NSA_SUCCESS) return st;
   *bytes = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d, cfg->l_sel, cfg->n_sel,
-                              cfg->w, max_seq_len)
+                              cfg->n_local, cfg->w, max_seq_len)
                .total;
   return ok();
 }
@@ -229,7 +232,7 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
     return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
   if ((st = check_decode_sizes(dims, cfg, max_seq_len)) != NSA_SUCCESS) return st;
   const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
-                                                   cfg->l_sel, cfg->n_sel, cfg->w, max_seq_len);
+                                                   cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
   if (!workspace || workspace_bytes < lay.total)
     return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -268,6 +271,7 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   p.rpart = reinterpret_cast<float*>(ws + lay.off_rpart);
   p.fcmp = reinterpret_cast<float*>(ws + lay.off_fcmp);
   p.nfin = lay.nfin;
+  p.nwin = lay.nwin;
   p.nch = lay.nch;
   p.nbo = lay.nbo;
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;

@@ -1,4 +1,4 @@
-// NSA decode step on gfx950: two launches per step; the kernel boundary is the
+// NSA decode step on gfx950: three launches per step; kernel boundaries are the
 // only cross-workgroup synchronisation (no device-scope fences, no counters).
 //
 // 1. decode_cmp_kernel, two kinds of workgroups in one launch:
@@ -12,9 +12,11 @@
 //      blocks (block 0 and the local blocks) — as 32-token steps over the
 //      sorted union of those blocks, so every token is read once and its logit
 //      feeds each branch it belongs to.
-// 2. decode_finish_kernel: per (sequence, group), exact per-head normalisers
-//    from the chunk statistics, group scores, top-n, the selected branch over
-//    the routed (not always-taken) blocks, the exact merge of every partial, and
+// 2. decode_finish_kernel: several workgroups per (sequence, group), each
+//    computing the exact per-head normalisers from the chunk statistics, the
+//    group scores and the top-n, then attending its share of the routed (not
+//    always-taken) selected blocks.
+// 3. decode_combine_kernel: per query head, the exact merge of every partial and
 //    out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 //
 // Sources: lesson 5.5/02 "Разреженное внимание — NSA и DSA" (ai.flicky.cc),
@@ -237,12 +239,12 @@ struct WindowBlocks {
   __device__ __forceinline__ bool forced(int j) const { return j >= lo_local || (finit && j == 0); }
 };
 
-// Window workgroup (one per (sequence, group)): 32-token steps over the window
-// blocks and the always-taken blocks, spread over the waves; writes one
-// partial per branch (grp 0: selected branch over the always-taken blocks,
+// Window workgroup wi of a (sequence, group): one 32-token step per wave over
+// the window blocks and the always-taken blocks (steps wi*4 .. wi*4+3); writes
+// one partial per branch (grp 0: selected branch over the always-taken blocks,
 // grp 1: window).
 template <int DK, int DV, int LSEL>
-__device__ __forceinline__ void window_work(const DecodeParams& p, int b, int g, int bg, float* smem) {
+__device__ __forceinline__ void window_work(const DecodeParams& p, int b, int g, int bg, int wi, float* smem) {
   constexpr int KT = DK / 32, NWV = kCmpWaves;
   constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;
   constexpr int PSTRIDE = 32 + 16 * DV;
@@ -252,39 +254,39 @@ __device__ __forceinline__ void window_work(const DecodeParams& p, int b, int g,
   const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
   const WindowBlocks wb(t, LSEL, p.w, p.nloc, p.finit);
   const int nsteps = wb.count() * SPB;
-  const int64_t row = raw_row0(p, b, g);
-  const uint16_t* kb = p.k + row * DK;
-  const uint16_t* vb = p.v + row * DV;
-  u32x4_t qf[KT];
-  load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
   Branch<DV> bs, bw;
   bs.init();
   bw.init();
-  for (int si = wave; si < nsteps; si += NWV) {
+  const int si = wi * NWV + wave;
+  if (si < nsteps) {
     const int it = si / SPB, half = si - it * SPB;
     const int jb = wb.block(it);
     const int64_t xb = (int64_t)jb * LSEL;
     const int64_t x0 = xb + 32 * half;
     const int64_t nv = min((int64_t)L, xb + LSEL);
     const bool fr = wb.forced(jb);
+    const int64_t row = raw_row0(p, b, g);
+    u32x4_t qf[KT];
+    load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
     Step<DK, DV> st;
-    step_load<DK, DV>(st, kb, vb, x0, nv, lg, lr);
-    if (x0 >= nv) continue;  // uniform over the wave
-    float z[2][4], zs[2][4], zw[2][4];
-    step_logits<DK, DV>(st, qf, p.scale_log2, z);
+    step_load<DK, DV>(st, p.k + row * DK, p.v + row * DV, x0, nv, lg, lr);
+    if (x0 < nv) {
+      float z[2][4], zs[2][4], zw[2][4];
+      step_logits<DK, DV>(st, qf, p.scale_log2, z);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t x = x0 + 16 * tt + 4 * lg + i;
-        const bool valid = x < nv;
-        zs[tt][i] = (valid && fr) ? z[tt][i] : -INFINITY;
-        zw[tt][i] = (valid && x >= wlo) ? z[tt][i] : -INFINITY;
-      }
-    if (fr) bs.update(zs, st.vr);
-    if (x0 + 31 >= wlo) bw.update(zw, st.vr);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t x = x0 + 16 * tt + 4 * lg + i;
+          const bool valid = x < nv;
+          zs[tt][i] = (valid && fr) ? z[tt][i] : -INFINITY;
+          zw[tt][i] = (valid && x >= wlo) ? z[tt][i] : -INFINITY;
+        }
+      if (fr) bs.update(zs, st.vr);
+      if (x0 + 31 >= wlo) bw.update(zw, st.vr);
+    }
   }
-  float* dst = p.wpart + (size_t)bg * 2 * PSTRIDE;
+  float* dst = p.wpart + ((size_t)bg * p.nwin + wi) * 2 * PSTRIDE;
   float* buf = smem;
   float* stt = smem + NWV * 16 * (DV + 1);
   merge_waves_to<DV, NWV>(bs, dst, buf, stt);
@@ -299,10 +301,11 @@ __global__ __launch_bounds__(64 * kCmpWaves, 2) void decode_cmp_kernel(DecodePar
   using SM = K1Smem<DV>;
   __shared__ float smem[SM::kFloats];
 
-  // workgroups [0, B*H) are window workgroups (scheduled first), the rest chunks
-  const int nwg_win = p.B * p.H;
+  // workgroups [0, B*H*nwin) are window workgroups (scheduled first), the rest chunks
+  const int nwg_win = p.B * p.H * p.nwin;
   if ((int)blockIdx.x < nwg_win) {
-    window_work<DK, DV, LSEL>(p, blockIdx.x / p.H, blockIdx.x % p.H, blockIdx.x, smem);
+    const int bgw = blockIdx.x / p.nwin;
+    window_work<DK, DV, LSEL>(p, bgw / p.H, bgw % p.H, bgw, blockIdx.x - bgw * p.nwin, smem);
     return;
   }
   const int nch = p.nch;
@@ -573,74 +576,99 @@ __global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
 
 // Combine: one workgroup per query head, one thread per output channel.
 //   o_cmp = sum_c f[c] * O_c (f from the finish kernel: exact normalised factors)
-//   o_slc = exact merge of the always-taken partial and the routed partials
-//   o_win = the window partial / its sum
+//   o_slc = exact merge of the always-taken partials and the routed partials
+//   o_win = exact merge of the window partials
 //   out   = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win  (bf16)
-// All loads of a thread are issued together (one round trip).
+// Every partial up to the launch bounds is loaded in one round (entries beyond
+// the sequence's own count are discarded by selects, never multiplied in).
 template <int DV>
 __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
   constexpr int PSTRIDE = 32 + 16 * DV;
   constexpr int kBatch = 16;
-  constexpr int kMaxFin = kMaxFinish;
+  constexpr int kMaxP = kMaxFinish + kMaxWindow;  // selected-branch partials
   __shared__ float s_f[kMaxChunks];
-  __shared__ float s_rm[kMaxFin + 1], s_rl[kMaxFin + 1];
+  __shared__ float s_pm[kMaxP], s_pl[kMaxP], s_wm[kMaxWindow], s_wl[kMaxWindow];
   const int qh = blockIdx.x;
   const int b = qh / p.Hq, hq = qh - b * p.Hq;
   const int g = hq / p.G, h = hq - g * p.G;
   const int bg = b * p.H + g;
   const int ch = threadIdx.x;
-  const int nch = p.nch, nfin = p.nfin;
-  const int L = seq_len_clamped(p, b);
-  const int nvis = n_visible(p, b, L);
-  const int nch_b = (nvis + kChunk - 1) / kChunk;
+  const int nch = p.nch, nfin = p.nfin, nwin = p.nwin;
   const size_t cbase = (size_t)bg * nch;
-  const float* wp = p.wpart + (size_t)bg * 2 * PSTRIDE;
+  const float* wp = p.wpart + (size_t)bg * nwin * 2 * PSTRIDE;
   const float* rp = p.rpart + (size_t)bg * nfin * PSTRIDE;
 
-  for (int c = ch; c < nch_b; c += DV) s_f[c] = p.fcmp[(cbase + c) * 16 + h];
+  // ---- one round of loads
+  const int L = seq_len_clamped(p, b);
+  for (int c = ch; c < nch; c += DV) s_f[c] = p.fcmp[(cbase + c) * 16 + h];
   if (ch < nfin) {
-    s_rm[ch] = rp[(size_t)ch * PSTRIDE + h];
-    s_rl[ch] = rp[(size_t)ch * PSTRIDE + 16 + h];
+    s_pm[ch] = rp[(size_t)ch * PSTRIDE + h];
+    s_pl[ch] = rp[(size_t)ch * PSTRIDE + 16 + h];
+  } else if (ch >= 32 && ch < 32 + nwin) {
+    const int wi = ch - 32;
+    s_pm[kMaxFinish + wi] = wp[(size_t)wi * 2 * PSTRIDE + h];
+    s_pl[kMaxFinish + wi] = wp[(size_t)wi * 2 * PSTRIDE + 16 + h];
+    s_wm[wi] = wp[((size_t)wi * 2 + 1) * PSTRIDE + h];
+    s_wl[wi] = wp[((size_t)wi * 2 + 1) * PSTRIDE + 16 + h];
   }
-  if (ch == DV - 1) {  // always-taken partial of the selected branch
-    s_rm[kMaxFin] = wp[h];
-    s_rl[kMaxFin] = wp[16 + h];
+  float vo[kBatch], vr[kMaxFinish], vf[kMaxWindow], vw[kMaxWindow];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) vo[u] = u < nch ? p.o1[((cbase + u) * 16 + h) * DV + ch] : 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxFinish; ++k) vr[k] = k < nfin ? rp[(size_t)k * PSTRIDE + 32 + h * DV + ch] : 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxWindow; ++k) {
+    vf[k] = k < nwin ? wp[(size_t)k * 2 * PSTRIDE + 32 + h * DV + ch] : 0.f;
+    vw[k] = k < nwin ? wp[((size_t)k * 2 + 1) * PSTRIDE + 32 + h * DV + ch] : 0.f;
   }
-  float vo[kBatch], vr[kMaxFin];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) vo[u] = u < nch_b ? p.o1[((cbase + u) * 16 + h) * DV + ch] : 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxFin; ++k) vr[k] = k < nfin ? rp[(size_t)k * PSTRIDE + 32 + h * DV + ch] : 0.f;
-  const float vf = wp[32 + h * DV + ch];                     // always-taken partial
-  const float vwin = wp[PSTRIDE + 32 + h * DV + ch];         // window partial
-  const float lwin = wp[PSTRIDE + 16 + h];
   const float* gt = p.gates + (size_t)qh * 3;
   const float g0 = gt[0], g1 = gt[1], g2 = gt[2];
+  const int nvis = n_visible(p, b, L);
+  const int nch_b = (nvis + kChunk - 1) / kChunk;
   __syncthreads();
+
+  // ---- compressed branch
   float oc = 0.f;
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) oc += (u < nch_b ? s_f[u] : 0.f) * vo[u];
+  for (int u = 0; u < kBatch; ++u) oc += u < nch_b ? s_f[u] * vo[u] : 0.f;
   for (int c0 = kBatch; c0 < nch_b; c0 += kBatch) {  // long contexts: remaining chunks
     float v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) v[u] = c0 + u < nch_b ? p.o1[((cbase + c0 + u) * 16 + h) * DV + ch] : 0.f;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) oc += (c0 + u < nch_b ? s_f[c0 + u] : 0.f) * v[u];
+    for (int u = 0; u < kBatch; ++u) oc += c0 + u < nch_b ? s_f[c0 + u] * v[u] : 0.f;
   }
-  float M = s_rm[kMaxFin];
-  for (int k = 0; k < nfin; ++k) M = fmaxf(M, s_rm[k]);
+  // ---- selected branch: routed partials (finish) + always-taken partials (window)
+  float M = -INFINITY;
+  for (int k = 0; k < nfin; ++k) M = fmaxf(M, s_pm[k]);
+  for (int k = 0; k < nwin; ++k) M = fmaxf(M, s_pm[kMaxFinish + k]);
   float vs = 0.f, ls = 0.f;
-  if (s_rm[kMaxFin] != -INFINITY) {
-    const float a = exp2f(s_rm[kMaxFin] - M);
-    vs += a * vf;
-    ls += a * s_rl[kMaxFin];
+#pragma unroll
+  for (int k = 0; k < kMaxFinish; ++k) {
+    if (k < nfin && s_pm[k] != -INFINITY) {
+      const float a = exp2f(s_pm[k] - M);
+      vs += a * vr[k];
+      ls += a * s_pl[k];
+    }
   }
 #pragma unroll
-  for (int k = 0; k < kMaxFin; ++k) {
-    if (k < nfin && s_rm[k] != -INFINITY) {
-      const float a = exp2f(s_rm[k] - M);
-      vs += a * vr[k];
-      ls += a * s_rl[k];
+  for (int k = 0; k < kMaxWindow; ++k) {
+    if (k < nwin && s_pm[kMaxFinish + k] != -INFINITY) {
+      const float a = exp2f(s_pm[kMaxFinish + k] - M);
+      vs += a * vf[k];
+      ls += a * s_pl[kMaxFinish + k];
+    }
+  }
+  // ---- window branch
+  float Mw = -INFINITY;
+  for (int k = 0; k < nwin; ++k) Mw = fmaxf(Mw, s_wm[k]);
+  float vwin = 0.f, lwin = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxWindow; ++k) {
+    if (k < nwin && s_wm[k] != -INFINITY) {
+      const float a = exp2f(s_wm[k] - Mw);
+      vwin += a * vw[k];
+      lwin += a * s_wl[k];
     }
   }
   const float os = ls > 0.f ? vs / ls : 0.f;
@@ -652,7 +680,7 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int w, int64_t max_len) {
+DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len) {
   DecodeLayout lay{};
   const int64_t nc = max_len >= l ? (max_len - l) / d + 1 : 0;
   lay.nch = (int)((nc + kChunk - 1) / kChunk);
@@ -664,10 +692,13 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   lay.off_l1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
   lay.off_o1 = off;   off = align256(off + BH * lay.nch * 16 * (size_t)DV * 4);
   lay.off_sc1 = off;  off = align256(off + BH * lay.nch * 16 * (size_t)(lay.nbo + 1) * 4);
-  // one window workgroup per (sequence, group): two branch partials
-  lay.off_wpart = off; off = align256(off + BH * 2 * (32 + 16 * (size_t)DV) * 4);
-  // finish workgroups: one partial each; normalised compressed-branch factors
+  // window workgroups: one 32-token step per wave over the window blocks and the
+  // always-taken blocks (at most ceil(w/l')+1 window blocks plus n_local+1)
   const int spb = lsel >= 32 ? lsel / 32 : 1;
+  const int wsteps = ((w + lsel - 1) / lsel + 1 + nloc + 1) * spb;
+  lay.nwin = (wsteps + kCmpWaves - 1) / kCmpWaves;
+  lay.off_wpart = off; off = align256(off + BH * lay.nwin * 2 * (32 + 16 * (size_t)DV) * 4);
+  // finish workgroups: one partial each; normalised compressed-branch factors
   lay.nfin = (n * spb + 7) / 8;
   lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
   lay.off_fcmp = off; off = align256(off + BH * lay.nch * 16 * 4);
@@ -679,7 +710,7 @@ template <int DK, int DV>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const PhaseEvents* ev) {
   hipError_t e;
   if (ev && (e = hipEventRecord(ev->ev[0], s)) != hipSuccess) return e;
-  const dim3 g1((unsigned)(p.B * p.H * (p.nch + 1))), b1(64 * kCmpWaves);
+  const dim3 g1((unsigned)(p.B * p.H * (p.nch + p.nwin))), b1(64 * kCmpWaves);
   switch (p.lsel) {
     case 16: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 16>), g1, b1, 0, s, p); break;
     case 32: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 32>), g1, b1, 0, s, p); break;
@@ -698,9 +729,10 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const Ph
     default: return hipErrorInvalidValue;
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev->ev[2], s)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<DV>), dim3((unsigned)(p.B * p.Hq)), dim3(DV), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev->ev[2], s)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev->ev[3], s)) != hipSuccess) return e;
   return hipSuccess;
 }
 

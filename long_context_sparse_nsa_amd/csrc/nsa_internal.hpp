@@ -26,6 +26,7 @@ constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query
 constexpr int kGPad = 16;            // query heads per group, padded to one MFMA tile
 constexpr int kMaxFinish = 16;       // decode finish workgroups per (sequence, group)
+constexpr int kMaxWindow = 16;       // decode window workgroups per (sequence, group)
 
 // Everything the decode kernels need; plain values and device pointers.
 struct DecodeParams {
@@ -50,17 +51,18 @@ struct DecodeParams {
   float* l1;                         // [B*H, nch, 16]
   float* o1;                         // [B*H, nch, 16, DV]
   float* sc1;                        // [B*H, nch, 16, nbo+1]
-  float* wpart;                      // [B*H, 2, 32 + 16*DV] window-workgroup partials
+  float* wpart;                      // [B*H, nwin, 2, 32 + 16*DV] window-workgroup partials
   float* rpart;                      // [B*H, nfin, 32 + 16*DV] routed-block partials
   float* fcmp;                       // [B*H, nch, 16] normalised compressed-branch factors
   int nch;                           // chunk workgroups per (sequence, group)
   int nbo;                           // selection blocks owned by one chunk = kChunk*d/lsel
   int nfin;                          // finish workgroups per (sequence, group)
+  int nwin;                          // window workgroups per (sequence, group)
 };
 
 struct DecodeLayout {
   size_t off_m1, off_l1, off_o1, off_sc1, off_wpart, off_rpart, off_fcmp, total;
-  int nch, nbo, nfin;
+  int nch, nbo, nfin, nwin;
 };
 
 // Parameters of the per-query prefill kernel and the compression kernel.
@@ -93,12 +95,12 @@ struct CompressParams {
   int max_nc;                        // launch bound on blocks per sequence
 };
 
-DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int w, int64_t max_len);
+DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len);
 
-// Optional events recorded before the first and after each of the two decode
+// Optional events recorded before the first and after each of the three decode
 // kernels (null = none).
 struct PhaseEvents {
-  hipEvent_t ev[3];
+  hipEvent_t ev[4];
 };
 
 hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);

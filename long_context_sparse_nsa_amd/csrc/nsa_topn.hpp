@@ -53,7 +53,12 @@ __device__ __forceinline__ uint64_t wave_extract(uint64_t (&k)[K], int rounds) {
     for (int q = 1; q < K; ++q) mine = k[q] > mine ? k[q] : mine;
     const uint32_t hi = (uint32_t)(mine >> 32), lo = (uint32_t)mine;
     const uint32_t Mh = wave_max_u32(hi);
-    const uint32_t Ml = wave_max_u32(hi == Mh ? lo : 0u);
+    // the index word only needs a second reduction when several lanes hold the
+    // top score; otherwise the single holder's word is read directly
+    const uint64_t holders = __ballot(hi == Mh);
+    const uint32_t Ml = __popcll(holders) == 1
+                            ? (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__ffsll((unsigned long long)holders) - 1)
+                            : wave_max_u32(hi == Mh ? lo : 0u);
     const uint64_t best = ((uint64_t)Mh << 32) | Ml;
     if (best == 0) break;  // nothing left anywhere in the wave (uniform)
 #pragma unroll
