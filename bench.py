@@ -203,9 +203,9 @@ def bench_decode(args, torch, N, I):
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e7))
     for i in range(n_ph):
-        N.nsa_set_decode_phase_events(hev.ev[4 * i:4 * i + 4])
+        N.nsa_set_phase_events(hev.ev[4 * i:4 * i + 4])
         step(i)
-    N.nsa_set_decode_phase_events(None)
+    N.nsa_set_phase_events(None)
     torch.cuda.synchronize()
     ph = [float(np.mean([hev.ms(4 * i + k, 4 * i + k + 1) for i in range(n_ph)])) for k in range(3)]
     hev.close()
@@ -278,11 +278,30 @@ def bench_prefill(args, torch, N, I):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / reps
+    # per-kernel durations from the library's phase events (compression, compressed +
+    # window + top-n kernel, selected-branch kernel)
+    hev = HipEvents(4 * reps)
+    try:
+        for i in range(reps):
+            N.nsa_set_phase_events(hev.ev[4 * i:4 * i + 4])
+            run()
+        N.nsa_set_phase_events(None)
+        torch.cuda.synchronize()
+        ph = [float(np.median([hev.ms(4 * i + a, 4 * i + a + 1) for i in range(reps)])) for a in range(3)]
+    finally:
+        N.nsa_set_phase_events(None)
+        hev.close()
     f = prefill_flops(wl)
     tot = sum(f.values())
     res = dict(workload=wl.name, ms=ms, flops=f, tflops=tot / (ms * 1e-3) / 1e12,
-               mfma_frac=tot / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS)
-    log(f"[bench] prefill {wl.name}: {ms:.2f} ms, {res['tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of bf16 peak)")
+               mfma_frac=tot / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+               kernel_ms=dict(compress=ph[0], pf_cmp_win_kernel=ph[1], pf_sel_kernel=ph[2]),
+               cmp_win_tflops=(f["cmp"] + f["win"]) / (ph[1] * 1e-3) / 1e12,
+               sel_tflops=f["slc"] / (ph[2] * 1e-3) / 1e12)
+    res["sel_mfma_frac"] = res["sel_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    log(f"[bench] prefill {wl.name}: {ms:.2f} ms, {res['tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of bf16 "
+        f"peak); compress {ph[0]:.3f} ms, cmp+win+top-n {ph[1]:.3f} ms ({res['cmp_win_tflops']:.0f} TFLOP/s), "
+        f"selected {ph[2]:.3f} ms ({res['sel_tflops']:.0f} TFLOP/s, {100 * res['sel_mfma_frac']:.1f}%)")
     return res
 
 

@@ -161,22 +161,31 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
 
 /* Workspace bytes needed by nsa_decode_fwd / nsa_prefill_fwd for these sizes
  * (host-only; no device call).  `compress_in_call` = 1 when k_cmp/v_cmp will be
- * NULL.  Returns NSA_SUCCESS and writes *bytes, or a validation error. */
+ * NULL.  Returns NSA_SUCCESS and writes *bytes, or a validation error.  Prefill
+ * always needs a workspace: it holds the fp32 partial output [B, T, Hq, d_v] of
+ * the compressed and window branches, a selection buffer [B, T, Hkv, n_sel] and,
+ * with in-call compression, the compressed cache.  Prefill supports at most
+ * 1024 selection blocks per sequence ((seq_len - 1) / l' + 1 <= 1024). */
 nsa_status_t nsa_decode_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                        int64_t max_seq_len, size_t* bytes);
 nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                         int64_t seq_len, int32_t compress_in_call, size_t* bytes);
 
-/* Profiling hook: until called again on this thread, every nsa_decode_fwd on
- * this thread records the caller-owned hipEvent_t handles events[0..3] on the
- * call's stream around its three kernels: before the compressed-branch kernel
- * (which also runs the window branch), after it, after the selection kernel
- * (top-n and the routed selected blocks) and after the combine kernel (exact
- * merge and gated sum), so a caller can time each kernel with
- * hipEventElapsedTime.  count = 0 (the default) records nothing; any count
- * other than 0 or 4, or a NULL handle, is NSA_ERROR_INVALID_VALUE.  The array
- * is copied; the events are not. */
-nsa_status_t nsa_set_decode_phase_events(void* const* events, int32_t count);
+/* Profiling hook: until called again on this thread, every nsa_decode_fwd and
+ * nsa_prefill_fwd on this thread records the caller-owned hipEvent_t handles
+ * events[0..3] on the call's stream between its kernels, so a caller can time
+ * each kernel with hipEventElapsedTime:
+ *   decode:  before the compressed-branch kernel (which also runs the window
+ *            branch), after it, after the selection kernel (top-n and the
+ *            routed selected blocks), after the combine kernel (exact merge and
+ *            gated sum);
+ *   prefill: before the in-call compression, after it (or right away when the
+ *            cache is given), after the compressed + window + top-n kernel, after
+ *            the selected-branch kernel (which writes the gated sum).
+ * count = 0 (the default) records nothing; any count other than 0 or 4, or a
+ * NULL handle, is NSA_ERROR_INVALID_VALUE.  The array is copied; the events are
+ * not. */
+nsa_status_t nsa_set_phase_events(void* const* events, int32_t count);
 
 /* Human-readable name of a status code (static storage). */
 const char* nsa_status_string(nsa_status_t status);

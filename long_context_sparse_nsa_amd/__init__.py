@@ -20,7 +20,7 @@ from ._abi import (  # noqa: F401
     nsa_last_error,
     nsa_prefill_fwd,
     nsa_prefill_workspace_size,
-    nsa_set_decode_phase_events,
+    nsa_set_phase_events,
     nsa_status_string,
 )
 

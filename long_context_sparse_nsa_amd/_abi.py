@@ -60,7 +60,7 @@ _SIGS = {
                         _VP, ctypes.c_size_t, _VP],
     "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
-    "nsa_set_decode_phase_events": [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32],
+    "nsa_set_phase_events": [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32],
     "nsa_status_string": [ctypes.c_int],
     "nsa_last_error": [],
 }
@@ -183,13 +183,14 @@ def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, p
                                _stream(stream)))
 
 
-def nsa_set_decode_phase_events(events=None):
-    """Record 5 raw hipEvent_t handles (ints or c_void_p) around the decode kernels; None disables."""
+def nsa_set_phase_events(events=None):
+    """Record 4 raw hipEvent_t handles (ints or c_void_p) between the kernels of each decode and
+    prefill call on this thread; None disables."""
     if not events:
-        _check(load_library().nsa_set_decode_phase_events(None, 0))
+        _check(load_library().nsa_set_phase_events(None, 0))
         return
     arr = (ctypes.c_void_p * len(events))(*[e.value if isinstance(e, ctypes.c_void_p) else int(e) for e in events])
-    _check(load_library().nsa_set_decode_phase_events(arr, len(events)))
+    _check(load_library().nsa_set_phase_events(arr, len(events)))
 
 
 def compressed_count(L: int, l: int, d: int) -> int:

@@ -102,30 +102,34 @@ nsa_status_t check_decode_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg,
   return NSA_SUCCESS;
 }
 
-constexpr int kPfMaxSlices = 64, kPfMaxSlots = 72, kPfMaxBlocks = 4096;
-
 nsa_status_t check_prefill_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   if (T < 1) return fail(NSA_ERROR_INVALID_VALUE, "seq_len must be >= 1");
-  const int64_t nc = n_compressed(T, cfg->l, cfg->d);
-  if ((nc + 63) / 64 > kPfMaxSlices)
-    return fail(NSA_ERROR_UNSUPPORTED, "prefill supports at most %d compressed blocks (got %lld)", kPfMaxSlices * 64,
-                (long long)nc);
-  if ((T - 1) / cfg->l_sel + 1 > kPfMaxBlocks)
-    return fail(NSA_ERROR_UNSUPPORTED, "prefill supports at most %d selection blocks", kPfMaxBlocks);
-  if ((63 * cfg->d + cfg->l - 1) / cfg->l_sel + 2 > kPfMaxSlots)
-    return fail(NSA_ERROR_UNSUPPORTED, "compression stride too large for the prefill fold");
-  if ((int64_t)dims->batch * dims->num_kv_heads * T > (int64_t)INT32_MAX)
+  if ((T - 1) / cfg->l_sel + 1 > nsa::kPfMaxBlocks)
+    return fail(NSA_ERROR_UNSUPPORTED, "prefill supports at most %d selection blocks (seq_len %lld, l_sel %d)",
+                nsa::kPfMaxBlocks, (long long)T, cfg->l_sel);
+  if ((int64_t)dims->batch * dims->num_kv_heads * ((T + 15) / 16) > (int64_t)INT32_MAX / 2)
     return fail(NSA_ERROR_UNSUPPORTED, "batch * kv_heads * seq_len too large");
   return NSA_SUCCESS;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t prefill_ws_bytes(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, bool compress) {
-  if (!compress) return 0;
+// Prefill workspace: [compressed K | compressed V] (in-call compression only),
+// then the fp32 accumulator [B, T, Hq, d_v], then the selection buffer
+// [B, T, Hkv, n_sel] (always reserved; unused when the caller passes sel_idx_out).
+struct PrefillWs {
+  size_t off_kc, off_vc, off_acc, off_sel, total;
+};
+PrefillWs prefill_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, bool compress) {
+  PrefillWs w{};
   const int64_t nc = n_compressed(T, cfg->l, cfg->d);
-  const size_t rows = (size_t)dims->batch * dims->num_kv_heads * (size_t)nc;
-  return align256(rows * dims->d_k * 2) + align256(rows * dims->d_v * 2);
+  const size_t rows = compress ? (size_t)dims->batch * dims->num_kv_heads * (size_t)nc : 0;
+  w.off_kc = 0;
+  w.off_vc = align256(rows * dims->d_k * 2);
+  w.off_acc = w.off_vc + align256(rows * dims->d_v * 2);
+  w.off_sel = w.off_acc + align256((size_t)dims->batch * T * dims->num_q_heads * dims->d_v * 4);
+  w.total = w.off_sel + align256((size_t)dims->batch * T * dims->num_kv_heads * cfg->n_sel * 4);
+  return w;
 }
 
 nsa_status_t hip_fail(hipError_t e, const char* what) {
@@ -149,7 +153,7 @@ const char* nsa_status_string(nsa_status_t s) {
 
 const char* nsa_last_error(void) { return g_last_error.c_str(); }
 
-nsa_status_t nsa_set_decode_phase_events(void* const* events, int32_t count) {
+nsa_status_t nsa_set_phase_events(void* const* events, int32_t count) {
   if (count == 0) {
     g_phase_on = false;
     return ok();
@@ -181,7 +185,7 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
   if (st != NSA_SUCCESS) return st;
   if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
   if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
-  *bytes = prefill_ws_bytes(dims, cfg, seq_len, compress_in_call != 0);
+  *bytes = prefill_ws(dims, cfg, seq_len, compress_in_call != 0).total;
   return ok();
 }
 
@@ -294,24 +298,27 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   if (compress && (!w_k || !pe_k || !w_v || !pe_v))
     return fail(NSA_ERROR_INVALID_VALUE, "compression weights are NULL and no compressed cache was given");
   if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
-  const size_t need = prefill_ws_bytes(dims, cfg, seq_len, compress);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  const PrefillWs lay = prefill_ws(dims, cfg, seq_len, compress);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : (size_t)0);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
+  if (ev) hipEventRecord(ev->ev[0], s);
   const int64_t nc = n_compressed(seq_len, cfg->l, cfg->d);
   if (compress && nc == 0) {
     k_cmp = k;  // no complete compressed block exists; the cache is never read
     v_cmp = v;
   } else if (compress) {
-    char* ws = static_cast<char*>(workspace);
-    const size_t rows = (size_t)dims->batch * dims->num_kv_heads * (size_t)nc;
-    uint16_t* kcw = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* vcw = reinterpret_cast<uint16_t*>(ws + align256(rows * dims->d_k * 2));
+    uint16_t* kcw = reinterpret_cast<uint16_t*>(ws + lay.off_kc);
+    uint16_t* vcw = reinterpret_cast<uint16_t*>(ws + lay.off_vc);
     st = nsa_compress_kv(dims, cfg, k, v, nullptr, nullptr, seq_len, w_k, pe_k, w_v, pe_v, kcw, vcw, nullptr, stream);
     if (st != NSA_SUCCESS) return st;
     k_cmp = kcw;
     v_cmp = vcw;
   }
+  if (ev) hipEventRecord(ev->ev[1], s);
   nsa::PrefillParams p{};
   p.B = dims->batch;
   p.T = (int)seq_len;
@@ -327,6 +334,7 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.w = cfg->w;
   p.scale_log2 = scale_log2(dims, cfg);
   p.nc = (int)nc;
+  p.ntile = (int)((seq_len + 15) / 16);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -334,8 +342,9 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.vc = v_cmp;
   p.gates = gates;
   p.out = out;
-  p.sel_out = sel_idx_out;
-  hipError_t e = nsa::launch_prefill(p, dims->d_k, dims->d_v, s);
+  p.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t*>(ws + lay.off_sel);
+  p.acc = reinterpret_cast<float*>(ws + lay.off_acc);
+  hipError_t e = nsa::launch_prefill(p, dims->d_k, dims->d_v, s, ev);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
 }

@@ -61,6 +61,46 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return v;
 }
 
+// The same reductions with the gfx950 lane-swap instructions (no LDS round trip):
+// permlane16_swap exchanges lane groups 0<->1 and 2<->3, permlane32_swap the two
+// wave halves; the element-wise combination of the two results is the reduction.
+__device__ __forceinline__ float max_over_groups_swap(float v) {
+  const uint32_t x = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups_swap(float v) {
+  const uint32_t x = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t y = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Sum over the 16 lanes of each lane group (a DPP row); the total lands in the
+// group's last lane (lanes 15, 31, 47, 63).  Lanes whose DPP source lies outside
+// the row read 0.
+__device__ __forceinline__ float row_sum_to_last(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));  // row_shr:1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));  // row_shr:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));  // row_shr:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));  // row_shr:8
+  return v;
+}
+
+// Wave-wide direct global -> LDS copy of 64 x 16 bytes: lane l reads 16 bytes at
+// `src` (its own address) and LDS receives them at lds_base + 16 * l.  lds_base
+// must be the same for every lane.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// Wait for all of this wave's outstanding vector-memory operations (vmcnt 0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Select 16-bit half `h` (0 low, 1 high) of a and b and pack as (a_h | b_h << 16).
 __device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int h) {
   return h ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));

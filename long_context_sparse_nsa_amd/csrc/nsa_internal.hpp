@@ -65,12 +65,15 @@ struct DecodeLayout {
   int nch, nbo, nfin, nwin;
 };
 
-// Parameters of the per-query prefill kernel and the compression kernel.
+// Parameters of the prefill kernels and the compression kernel.
+constexpr int kPfMaxBlocks = 1024;   // prefill selection candidates per position (J+1)
+
 struct PrefillParams {
   int B, T, Hq, H, G;
   int l, d, lsel, n, nloc, finit, w;
   float scale_log2;
   int nc;                            // compressed blocks per sequence: floor((T-l)/d)+1
+  int ntile;                         // position tiles per sequence: ceil(T/16)
   const uint16_t* q;                 // [B, T, Hq, DK]
   const uint16_t* k;                 // [B, H, T, DK]
   const uint16_t* v;
@@ -78,7 +81,8 @@ struct PrefillParams {
   const uint16_t* vc;
   const float* gates;                // [B, T, Hq, 3]
   uint16_t* out;                     // [B, T, Hq, DV]
-  int32_t* sel_out;                  // [B, T, H, n] or null
+  int32_t* sel;                      // [B, T, H, n] selected block ids (caller's or workspace)
+  float* acc;                        // [B, T, Hq, DV] workspace: g_win o_win + g_cmp o_cmp
 };
 
 struct CompressParams {
@@ -97,14 +101,15 @@ struct CompressParams {
 
 DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len);
 
-// Optional events recorded before the first and after each of the three decode
-// kernels (null = none).
+// Optional events recorded between the kernels of one call (null = none).
 struct PhaseEvents {
   hipEvent_t ev[4];
 };
 
 hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);
-hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);
+// With events, ev[2] is recorded after the first prefill kernel and ev[3] after
+// the second (the caller records ev[0] and ev[1] around the compression).
+hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);
 hipError_t launch_compress(const CompressParams& p, hipStream_t s);
 
 }  // namespace nsa

@@ -1,19 +1,30 @@
-// NSA causal prefill on gfx950: one workgroup per (sequence, position t, KV group).
+// NSA causal prefill on gfx950, tiled over query positions.
 //
-// Compressed branch in two exact passes over the blocks visible at t:
-//   pass 1: logits (MFMA) -> per-head running max / sum -> exact normaliser;
-//   pass 2: logits again -> normalised probabilities p -> o_cmp += p.Vc and the
-//           probabilities summed over the group's heads and folded onto
-//           selection blocks (token overlap / l), kept per 64-key slice in LDS
-//           and added up in slice order (deterministic).
-// Then the block-wide top-n, and the selected and window branches over the
-// sorted union of their blocks (each token's logit feeds the branch softmaxes it
-// belongs to), and the gated sum written in bf16.
+// Both kernels run one workgroup (4 waves) per (sequence, KV group, tile of 16
+// consecutive positions t0 .. t0+15).  Wave w owns positions t0+4w .. t0+4w+3
+// and keeps, for each, the group's query fragments and a 16-head x d_v fp32
+// accumulator in registers.  Key/value tiles of 64 rows are copied straight
+// from global memory into LDS (no register round trip), double buffered, and
+// each staged tile serves every position of the workgroup that needs it.
+//
+// Kernel 1 (compressed + window branches, group scores, selection):
+//   W   sliding window (t - w, t] over the raw keys, online softmax; the
+//       accumulator is then scaled to g_win * o_win;
+//   C1  compressed keys visible at t: logits only, exact per-head max and sum;
+//   C2  the same keys again: normalised probabilities p, accumulator += g_cmp *
+//       p . Vc, and p folded onto selection blocks by token overlap (an MFMA
+//       with the overlap counts) and summed over the group's heads into the
+//       position's score row in LDS;
+//   top-n per position (initial and local blocks forced) -> selected ids;
+//   the accumulator (g_win o_win + g_cmp o_cmp, fp32) goes to the workspace.
+// Kernel 2 (selected branch): the union of the tile's selected blocks is
+// staged block by block; each wave runs the online softmax for those of its
+// positions that chose the block, then writes bf16(acc + g_slc o_slc).
 //
 // Sources: lesson 5.5/02 "Разреженное внимание — NSA и DSA" (ai.flicky.cc),
-// section "NSA: три ветви" (output equation, the three branches, selection per
-// GQA group); lesson "Native Sparse Attention (DeepSeek NSA)" (AI Engineering
-// from Scratch, phase 10 · 17), "Build it" steps 2-5.
+// section "NSA: три ветви" (output equation, the three branches, blockwise
+// selection shared by the GQA group); lesson "Native Sparse Attention (DeepSeek
+// NSA)" (AI Engineering from Scratch, phase 10 · 17), "Build it" steps 2-5.
 #include <hip/hip_runtime.h>
 
 #include "nsa_device.hpp"
@@ -23,378 +34,620 @@
 
 namespace nsa {
 
-// Prefill limits (checked by the host): slices of 64 compressed keys, per-slice
-// fold slots, candidate blocks.
-constexpr int kPfMaxSlices = 64;     // Nc <= 4096
-constexpr int kPfMaxSlots = 72;      // selection blocks touched by one 64-key slice
-constexpr int kPfMaxBlocks = 4096;   // J+1
+namespace {
 
-template <int DV>
-struct PfSmem {
-  static constexpr int kStage = 4 * 16 * 65;                 // per-wave p staging [wave][h][64(+1)]
-  static constexpr int kPsum = 4 * 64;
-  static constexpr int kFold = kPfMaxSlices * kPfMaxSlots;   // per-slice block contributions
-  static constexpr int kS = kPfMaxBlocks;
-  static constexpr int kFlag = kPfMaxBlocks / 4;
-  static constexpr int kTopn = sizeof(TopnSmem) / 4 + 4;
-  static constexpr int kStat = 4 * 4 * 16;
-  static constexpr int kPhaseA = kStage + kPsum + kFold + kS + kFlag + kTopn + kStat;
-  static constexpr int kAcc = 4 * 16 * (DV + 1);
-  static constexpr int kFloats = kPhaseA > kAcc + kStat ? kPhaseA : kAcc + kStat;
+constexpr int kTileQ = 16;         // positions per workgroup
+constexpr int kWaveQ = 4;          // positions per wave
+constexpr float kNegBig = -1e30f;  // running-max start: finite, so exp2 never sees inf - inf
+
+template <int DK, int DV>
+struct PfShape {
+  static constexpr int KT = DK / 32;           // MFMA k-steps of a logit tile
+  static constexpr int VC = DV / 16;           // MFMAs per 32-key value step
+  static constexpr int kKBytes = 64 * DK * 2;  // 64-key K tile, MFMA fragment order
+  static constexpr int kVBytes = 64 * DV * 2;  // 64-key V tile, row-major
+  static constexpr int kBuf = kKBytes + kVBytes;
 };
 
-template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
-  constexpr int KT = DK / 32, VC = DV / 16, VW = DV / 32;
-  constexpr int NT = LSEL / 16, NS = (NT + 1) / 2;
-  using SM = PfSmem<DV>;
-  __shared__ float smem[SM::kFloats];
-  __shared__ int s_sel[kMaxSel];
-  __shared__ int s_items[kMaxUnion];
-  __shared__ uint8_t s_insel[kMaxUnion];
-  __shared__ int s_nitems;
+// ---- staging of ROWS rows [row0, row0+ROWS) of a row-major bf16 array; rows
+// past rowmax are replaced by row rowmax (the caller masks their logits).
 
-  // grid order: (b, g) outer, t inner, so workgroups running together share the
-  // group's compressed cache and window in L2
-  const int64_t bid = blockIdx.x;
-  const int t = (int)(bid % p.T);
-  const int bg = (int)(bid / p.T);
-  const int g = bg % p.H, b = bg / p.H;
+// K tile in fragment order: fragment f = m*KT + ks holds, at 16*lane, the eight
+// dims 32*ks + 8*(lane/16) .. of row 16*m + lane%16 -- the A operand of the S^T
+// MFMA, so a wave reads one contiguous KB per fragment.
+template <int DK, int ROWS = 64>
+__device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
+                                        int lane) {
+  constexpr int KT = DK / 32, NF = (ROWS / 16) * KT;
+  static_assert(NF % 4 == 0, "fragments split evenly over 4 waves");
+#pragma unroll
+  for (int ii = 0; ii < NF / 4; ++ii) {
+    const int f = wave + 4 * ii;
+    const int m = f / KT, ks = f - m * KT;
+    int64_t row = row0 + 16 * m + (lane & 15);
+    row = row < rowmax ? row : rowmax;
+    copy16_to_lds(base + row * DK + 32 * ks + 8 * (lane >> 4), dst + f * 1024);
+  }
+}
+
+// V tile row-major (DV*2 bytes per row), copied in 1 KB pieces.
+template <int DV, int ROWS = 64>
+__device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
+                                        int lane) {
+  constexpr int NI = ROWS * DV * 2 / 1024, RB = DV * 2;
+  static_assert(NI % 4 == 0, "pieces split evenly over 4 waves");
+#pragma unroll
+  for (int ii = 0; ii < NI / 4; ++ii) {
+    const int i = wave + 4 * ii;
+    const int off = i * 1024 + lane * 16;
+    int64_t row = row0 + off / RB;
+    row = row < rowmax ? row : rowmax;
+    copy16_to_lds(reinterpret_cast<const char*>(base + row * DV) + (off % RB), dst + i * 1024);
+  }
+}
+
+// ---- LDS operand reads
+
+template <int DK>
+__device__ __forceinline__ u32x4_t lds_k(const char* kt, int m, int ks, int lane) {
+  return *reinterpret_cast<const u32x4_t*>(kt + ((m * (DK / 32) + ks) * 64 + lane) * 16);
+}
+
+// The eight V rows of 32-key step ks that pair with this lane's P^T k-slots,
+// channels (DV/16)*lr .. of each.
+template <int DV>
+__device__ __forceinline__ void lds_v_step(const char* vt, int ks, int lg, int lr, uint32_t (&vr)[8][DV / 32]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const char* src = vt + (32 * ks + step_key(lg, r)) * (DV * 2) + (DV / 16) * lr * 2;
+    if constexpr (DV / 32 == 4) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src);
+      vr[r][0] = x[0]; vr[r][1] = x[1]; vr[r][2] = x[2]; vr[r][3] = x[3];
+    } else {
+      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(src);
+      vr[r][0] = x[0]; vr[r][1] = x[1];
+    }
+  }
+}
+
+// Online softmax with a lazily moved reference: the running reference m only
+// moves when a logit exceeds it by more than 8 (log2 units), so exp2(z - m)
+// stays below 2^8 and the accumulator is rescaled rarely.  The final division by
+// the sum taken against the same reference makes the result independent of m.
+// mx is the block's maximum logit of this lane's head (equal on its 4 lanes).
+template <int VC>
+__device__ __forceinline__ void lazy_rescale(float mx, float& m, float& l, f32x4_t (&acc)[VC]) {
+  const bool move = mx > m + 8.0f;
+  if (__ballot(move) != 0ull) {  // wave-uniform
+    const float mn = move ? mx : m;
+    const float alpha = exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < VC; ++j) acc[j] *= alpha;
+    m = mn;
+  }
+}
+
+// acc[q] += V^T . P_q^T over the 32-key step `ks` of the staged V tile, for the
+// wave's positions; each V^T operand is built once and used for all of them.
+template <int DV, int NQ>
+__device__ __forceinline__ void pv_half(const char* vt, int ks, int lg, int lr, const u32x4_t (&pk)[NQ],
+                                        f32x4_t (&acc)[NQ][DV / 16]) {
+  uint32_t vr[8][DV / 32];
+  lds_v_step<DV>(vt, ks, lg, lr, vr);
+#pragma unroll
+  for (int j = 0; j < DV / 16; ++j) {
+    const int wd = j >> 1, h = j & 1;
+    const u32x4_t va = u32x4_t{pack_halves(vr[0][wd], vr[1][wd], h), pack_halves(vr[2][wd], vr[3][wd], h),
+                               pack_halves(vr[4][wd], vr[5][wd], h), pack_halves(vr[6][wd], vr[7][wd], h)};
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q][j] = mfma_bf16(va, pk[q], acc[q][j]);
+  }
+}
+
+__device__ __forceinline__ int n_visible(int t, int l, int d) { return t + 1 >= l ? (t + 1 - l) / d + 1 : 0; }
+
+// Workgroup -> (sequence b, group g, tile).  Tiles are issued latest first (they
+// carry the most compressed keys); consecutive workgroup ids cycle through the
+// (b, g) pairs, so with 4 groups each XCD keeps seeing one group's keys.
+struct TileId {
+  int b, g, t0;
+};
+__device__ __forceinline__ TileId tile_id(const PrefillParams& p) {
+  const int nbg = p.B * p.H;
+  const int bid = (int)blockIdx.x;
+  const int tile = p.ntile - 1 - bid / nbg;
+  const int bg = bid - (bid / nbg) * nbg;
+  return TileId{bg / p.H, bg - (bg / p.H) * p.H, tile * kTileQ};
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Kernel 1: window + compressed branches, group scores, top-n.
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
+  using SH = PfShape<DK, DV>;
+  constexpr int KT = SH::KT, VC = SH::VC;
+  __shared__ __attribute__((aligned(1024))) char s_buf[2][SH::kBuf];
+  __shared__ float s_score[kTileQ][kPfMaxBlocks];
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const TileId ti = tile_id(p);
+  const int b = ti.b, g = ti.g, t0 = ti.t0;
+  const int T = p.T;
+  const int tlast = min(t0 + kTileQ - 1, T - 1);
+  const int64_t bg = (int64_t)b * p.H + g;
+  const uint16_t* kraw = p.k + bg * T * DK;
+  const uint16_t* vraw = p.v + bg * T * DV;
+  const uint16_t* kcmp = p.kc + bg * p.nc * DK;
+  const uint16_t* vcmp = p.vc + bg * p.nc * DV;
 
-  float* s_stage = smem;
-  float* s_psum = s_stage + SM::kStage;
-  float* s_fold = s_psum + SM::kPsum;
-  float* S = s_fold + SM::kFold;
-  uint8_t* flag = reinterpret_cast<uint8_t*>(S + SM::kS);
-  TopnSmem& tsm = *reinterpret_cast<TopnSmem*>(S + SM::kS + SM::kFlag);
-  float* s_stat = S + SM::kS + SM::kFlag + SM::kTopn;  // [4][4][16]
+  // chunk plan: window rows, then the compressed rows twice
+  const int xlo = max(0, t0 - p.w + 1);
+  const int nW = (tlast - xlo + 1 + 63) / 64;
+  const int ncT = n_visible(tlast, p.l, p.d);
+  const int nC = (ncT + 63) / 64;
+  const int nch = nW + 2 * nC;
+  const int Jtile = tlast / p.lsel;
 
-  const int64_t qrow = ((int64_t)b * p.T + t) * p.Hq + (int64_t)g * p.G;
-  u32x4_t qf[KT];
-  load_q_frags<DK>(p.q + qrow * DK, p.G, lg, lr, qf);
+  for (int e = tid; e < kTileQ * (Jtile + 1); e += 256) s_score[e / (Jtile + 1)][e % (Jtile + 1)] = 0.f;
 
-  const int nvis = t + 1 >= p.l ? (t + 1 - p.l) / p.d + 1 : 0;
-  const int nsl = (nvis + 63) / 64;
-  const int rounds = (nsl + 3) / 4;
-  const int64_t crow = ((int64_t)b * p.H + g) * p.nc;
-  const uint16_t* kc = p.kc + crow * DK;
-  const uint16_t* vc = p.vc + crow * DV;
-
-  // ---- pass 1: exact per-head normaliser of the compressed branch
-  float m_run = -INFINITY, l_run = 0.f;
-  for (int r = 0; r < rounds; ++r) {
-    const int sl = 4 * r + wave;
-    if (sl < nsl) {
-      const int key0 = sl * 64;
-      u32x4_t kf[4][KT];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) load_k_tile<DK>(kc, key0 + 16 * tt + lr, nvis, lg, kf[tt]);
-      float z[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const f32x4_t st = qk_tile<DK>(kf[tt], qf);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * tt + 4 * lg + i;
-          z[tt][i] = key < nvis ? st[i] * p.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, z[tt][i]);
-        }
-      }
-      mx = max_over_groups(mx);
-      const float mn = fmaxf(m_run, mx);
-      float ls = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ls += exp2f(z[tt][i] - mn);
-      ls = sum_over_groups(ls);
-      l_run = (m_run == -INFINITY ? 0.f : l_run * exp2f(m_run - mn)) + ls;
-      m_run = mn;
+  auto stage = [&](int c, int buf) {
+    char* kt = s_buf[buf];
+    char* vt = s_buf[buf] + SH::kKBytes;
+    if (c < nW) {
+      const int64_t r0 = xlo + 64 * c;
+      stage_k<DK>(kraw, r0, tlast, kt, wave, lane);
+      stage_v<DV>(vraw, r0, tlast, vt, wave, lane);
+    } else if (c < nW + nC) {
+      stage_k<DK>(kcmp, 64 * (c - nW), ncT - 1, kt, wave, lane);
+    } else {
+      const int64_t r0 = 64 * (c - nW - nC);
+      stage_k<DK>(kcmp, r0, ncT - 1, kt, wave, lane);
+      stage_v<DV>(vcmp, r0, ncT - 1, vt, wave, lane);
     }
-  }
-  if (lg == 0) {
-    s_stat[(0 * 4 + wave) * 16 + lr] = m_run;
-    s_stat[(1 * 4 + wave) * 16 + lr] = l_run;
-  }
-  __syncthreads();
-  float Mh = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, s_stat[(0 * 4 + w) * 16 + lr]);
-  float Lh = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = s_stat[(0 * 4 + w) * 16 + lr];
-    if (mw != -INFINITY) Lh += exp2f(mw - Mh) * s_stat[(1 * 4 + w) * 16 + lr];
-  }
-  const float invL = Lh > 0.f ? 1.0f / Lh : 0.f;
-  __syncthreads();
+  };
 
-  // ---- pass 2: normalised probabilities, o_cmp, folded group scores per slice
-  const int nbs = (63 * p.d + p.l - 1) / p.lsel + 2;  // slots per slice (host checks <= kPfMaxSlots)
-  f32x4_t accC[VC];
+  // per-position state (positions t0 + 4*wave + q)
+  int tq[kWaveQ];
+  bool act[kWaveQ];
+  u32x4_t qf[kWaveQ][KT];
+  f32x4_t acc[kWaveQ][VC];
+  float mrun[kWaveQ], lrun[kWaveQ];
 #pragma unroll
-  for (int j = 0; j < VC; ++j) accC[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float* stg = s_stage + wave * 16 * 65;
-  float* psum = s_psum + wave * 64;
-  for (int r = 0; r < rounds; ++r) {
-    const int sl = 4 * r + wave;
-    if (sl < nsl) {
-      const int key0 = sl * 64;
-      u32x4_t kf[4][KT];
+  for (int q = 0; q < kWaveQ; ++q) {
+    tq[q] = t0 + 4 * wave + q;
+    act[q] = tq[q] < T;
+    const int tt = act[q] ? tq[q] : T - 1;
+    load_q_frags<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf[q]);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) load_k_tile<DK>(kc, key0 + 16 * tt + lr, nvis, lg, kf[tt]);
-      uint32_t vr[2][8][VW];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) load_v_step<DV>(vc, key0 + 32 * s, nvis, lg, lr, vr[s]);
-      float z[4][4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const f32x4_t st = qk_tile<DK>(kf[tt], qf);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * tt + 4 * lg + i;
-          const float e = key < nvis ? exp2f(st[i] * p.scale_log2 - Mh) * invL : 0.f;
-          z[tt][i] = e;
-          stg[lr * 65 + 16 * tt + 4 * lg + i] = e;
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) pv_step<DV>(vr[s], pack_probs(z[2 * s], z[2 * s + 1]), accC);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      {  // sum over the group's heads, one key per lane
-        float sum = 0.f;
-        for (int h = 0; h < p.G; ++h) sum += stg[h * 65 + lane];
-        psum[lane] = sum;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      {  // fold onto the selection blocks this slice touches (units of the stride d:
-         // key i covers [i, i+q), block j covers [j*r, (j+1)*r))
-        const int q = p.l / p.d, r = p.lsel / p.d;
-        const int jlo = key0 / r;
-        const int kend = min(key0 + 64, nvis);
-        if (lane < nbs) {
-          const int lo = (jlo + lane) * r, hi = lo + r;
-          const int ilo = max(key0, lo - q + 1), ihi = min(kend - 1, hi - 1);
-          float s = 0.f;
-          for (int i = ilo; i <= ihi; ++i) s += (float)(min(i + q, hi) - max(i, lo)) * psum[i - key0];
-          s_fold[sl * kPfMaxSlots + lane] = s * (1.0f / (float)q);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    for (int j = 0; j < VC; ++j) acc[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mrun[q] = kNegBig;
+    lrun[q] = 0.f;
   }
-  __syncthreads();
+  auto gate = [&](int q, int br) -> float {
+    return (act[q] && lr < p.G) ? p.gates[(((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * 3 + br] : 0.f;
+  };
+  const float sc = p.scale_log2;
+  const int qd = p.l / p.d, rd = p.lsel / p.d;  // key and block lengths in stride units
+  const float invq = 1.0f / (float)qd;
 
-  // ---- group scores of candidates 0..J (slice contributions added in slice order)
-  const int J = t / LSEL;
-  {
-    const int q = p.l / p.d, r = p.lsel / p.d;
-    for (int j = tid; j <= J; j += 256) {
-      float s = 0.f;
-      const int ilo = max(0, j * r - q + 1), ihi = min(nvis - 1, (j + 1) * r - 1);
-      if (ilo <= ihi) {
-        for (int sl = ilo / 64; sl <= ihi / 64; ++sl) s += s_fold[sl * kPfMaxSlots + (j - sl * 64 / r)];
-      }
-      S[j] = s;
-    }
-  }
-  __syncthreads();
-  int32_t* selg = p.sel_out ? p.sel_out + (((int64_t)b * p.T + t) * p.H + g) * p.n : nullptr;
-  block_topn<256, 16>(S, J, p.n, p.nloc, p.finit, tsm, s_sel, selg);
-  __syncthreads();
-
-  // ---- selected and window branches over the sorted union of their blocks
-  const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
-  const int jw0 = wlo / LSEL;
-  if (tid == 0) {
-    int a = 0, cnt = 0, jw = jw0;
-    while (true) {
-      const int sa = (a < p.n && s_sel[a] >= 0) ? s_sel[a] : INT32_MAX;
-      const int sb = jw <= J ? jw : INT32_MAX;
-      if (sa == INT32_MAX && sb == INT32_MAX) break;
-      const int j = sa < sb ? sa : sb;
-      if (cnt < kMaxUnion) {
-        s_items[cnt] = j;
-        s_insel[cnt] = (uint8_t)(sa == j);
-      }
-      ++cnt;
-      if (sa == j) ++a;
-      if (sb == j) ++jw;
-    }
-    s_nitems = cnt < kMaxUnion ? cnt : kMaxUnion;
-  }
-  __syncthreads();
-
-  const int64_t row = ((int64_t)b * p.H + g) * p.T;
-  const uint16_t* kb = p.k + row * DK;
-  const uint16_t* vb = p.v + row * DV;
-  float m_s = -INFINITY, l_s = 0.f, m_w = -INFINITY, l_w = 0.f;
-  f32x4_t accS[VC], accW[VC];
-#pragma unroll
-  for (int j = 0; j < VC; ++j) accS[j] = accW[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int it = wave; it < s_nitems; it += 4) {
-    const int jblk = s_items[it];
-    const bool insel = s_insel[it] != 0;
-    const int64_t x0 = (int64_t)jblk * LSEL;
-    const int64_t nval = min((int64_t)t + 1, x0 + LSEL);
-    const bool anyW = x0 + LSEL - 1 >= wlo;
-    u32x4_t kf[NT][KT];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) load_k_tile<DK>(kb, x0 + 16 * tt + lr, nval, lg, kf[tt]);
-    uint32_t vr[NS][8][VW];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) load_v_step<DV>(vb, x0 + 32 * s, nval, lg, lr, vr[s]);
-    float zs[2 * NS][4], zw[2 * NS][4];
-    float mxs = -INFINITY, mxw = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2 * NS; ++tt) {
-      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-      if (tt < NT) st = qk_tile<DK>(kf[tt < NT ? tt : 0], qf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t x = x0 + 16 * tt + 4 * lg + i;
-        const bool valid = tt < NT && x <= t;
-        const float z = st[i] * p.scale_log2;
-        zs[tt][i] = (valid && insel) ? z : -INFINITY;
-        zw[tt][i] = (valid && x >= wlo) ? z : -INFINITY;
-        mxs = fmaxf(mxs, zs[tt][i]);
-        mxw = fmaxf(mxw, zw[tt][i]);
-      }
-    }
-    if (insel) {
-      mxs = max_over_groups(mxs);
-      const float mn = fmaxf(m_s, mxs);
-      const float alpha = m_s == -INFINITY ? 0.f : exp2f(m_s - mn);
-      float ls = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2 * NS; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(zs[tt][i] - mn);
-          zs[tt][i] = e;
-          ls += e;
-        }
-      ls = sum_over_groups(ls);
-      l_s = l_s * alpha + ls;
-      m_s = mn;
-#pragma unroll
-      for (int j = 0; j < VC; ++j) accS[j] *= alpha;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) pv_step<DV>(vr[s], pack_probs(zs[2 * s], zs[2 * s + 1]), accS);
-    }
-    if (anyW) {
-      mxw = max_over_groups(mxw);
-      const float mn = fmaxf(m_w, mxw);
-      const float alpha = m_w == -INFINITY ? 0.f : exp2f(m_w - mn);
-      float ls = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2 * NS; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(zw[tt][i] - mn);
-          zw[tt][i] = e;
-          ls += e;
-        }
-      ls = sum_over_groups(ls);
-      l_w = l_w * alpha + ls;
-      m_w = mn;
-#pragma unroll
-      for (int j = 0; j < VC; ++j) accW[j] *= alpha;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) pv_step<DV>(vr[s], pack_probs(zw[2 * s], zw[2 * s + 1]), accW);
-    }
-  }
-
-  // ---- merge the 4 waves and write the gated sum
-  __syncthreads();  // LDS of phase A is reused below
-  float* s_acc = smem;
-  float* st2 = smem + SM::kAcc;  // [grp*2 + (m,l)][wave][16]
-  if (lg == 0) {
-    st2[(0 * 4 + wave) * 16 + lr] = m_s;
-    st2[(1 * 4 + wave) * 16 + lr] = l_s;
-    st2[(2 * 4 + wave) * 16 + lr] = m_w;
-    st2[(3 * 4 + wave) * 16 + lr] = l_w;
-  }
-  // o_cmp: sum of the waves' exact partials
-#pragma unroll
-  for (int j = 0; j < VC; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = accC[j][i];
-  __syncthreads();
-  float res[(16 * DV + 255) / 256];
-  {
-    int q = 0;
-    for (int e = tid; e < 16 * DV; e += 256, ++q) {
-      const int h = e / DV, ch = e - h * DV;
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) v += s_acc[(w * 16 + h) * (DV + 1) + ch];
-      const float gt = h < p.G ? p.gates[(((int64_t)b * p.T + t) * p.Hq + (int64_t)g * p.G + h) * 3 + 0] : 0.f;
-      res[q] = gt * v;
-    }
-  }
-  for (int grp = 0; grp < 2; ++grp) {
+  // One pipeline over all chunks (window, then C1, then C2): chunk c + 1 is
+  // copied into the other buffer while chunk c is computed.
+  auto begin_chunk = [&](int c) -> const char* {
+    wait_vmem();
     __syncthreads();
+    if (c + 1 < nch) stage(c + 1, (c + 1) & 1);
+    return s_buf[c & 1];
+  };
+  // logits of one 32-key half of the staged chunk for the wave's positions
+  // (each K fragment read once from LDS and used for all of them)
+  auto logits_half = [&](const char* kt, int hh, f32x4_t (&sv)[kWaveQ][2]) {
 #pragma unroll
-    for (int j = 0; j < VC; ++j)
+    for (int q = 0; q < kWaveQ; ++q) sv[q][0] = sv[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_acc[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = grp == 0 ? accS[j][i] : accW[j][i];
-    __syncthreads();
-    int q = 0;
-    for (int e = tid; e < 16 * DV; e += 256, ++q) {
-      const int h = e / DV, ch = e - h * DV;
-      float M = -INFINITY;
+    for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, st2[(grp * 2 * 4 + w) * 16 + h]);
-      float v = 0.f, ls = 0.f;
+      for (int ks = 0; ks < KT; ++ks) {
+        const u32x4_t a = lds_k<DK>(kt, 2 * hh + mm, ks, lane);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = st2[(grp * 2 * 4 + w) * 16 + h];
-        if (mw != -INFINITY) {
-          const float a = exp2f(mw - M);
-          v += a * s_acc[(w * 16 + h) * (DV + 1) + ch];
-          ls += a * st2[((grp * 2 + 1) * 4 + w) * 16 + h];
-        }
+        for (int q = 0; q < kWaveQ; ++q) sv[q][mm] = mfma_bf16(a, qf[q][ks], sv[q][mm]);
       }
-      const float gt = h < p.G ? p.gates[(((int64_t)b * p.T + t) * p.Hq + (int64_t)g * p.G + h) * 3 + 1 + grp] : 0.f;
-      res[q] += ls > 0.f ? gt * v / ls : 0.f;
+  };
+
+  stage(0, 0);
+  int c = 0;
+  // ---- W: window (t - w, t], online softmax into acc
+  for (int cw = 0; cw < nW; ++cw, ++c) {
+    const char* kt = begin_chunk(c);
+    const char* vt = kt + SH::kKBytes;
+#pragma unroll 1
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4_t s[kWaveQ][2];
+      logits_half(kt, hh, s);
+      const int x0 = xlo + 64 * cw + 32 * hh;
+      u32x4_t pk[kWaveQ];
+#pragma unroll
+      for (int q = 0; q < kWaveQ; ++q) {
+        float z[2][4];
+        float mx = kNegBig;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int x = x0 + 16 * mm + 4 * lg + i;
+            const bool ok = act[q] && x <= tq[q] && x > tq[q] - p.w;
+            z[mm][i] = ok ? s[q][mm][i] * sc : -INFINITY;
+            mx = fmaxf(mx, z[mm][i]);
+          }
+        mx = max_over_groups_swap(mx);
+        lazy_rescale(mx, mrun[q], lrun[q], acc[q]);
+        float ls = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            z[mm][i] = exp2f(z[mm][i] - mrun[q]);
+            ls += z[mm][i];
+          }
+        lrun[q] += ls;
+        pk[q] = pack_probs(z[0], z[1]);
+      }
+      pv_half<DV>(vt, hh, lg, lr, pk, acc);
     }
   }
+  // acc <- g_win * o_win; fresh running state for C1
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    const float lt = sum_over_groups_swap(lrun[q]);
+    const float f = lt > 0.f ? gate(q, 2) / lt : 0.f;
+#pragma unroll
+    for (int j = 0; j < VC; ++j) acc[q][j] *= f;
+    mrun[q] = kNegBig;
+    lrun[q] = 0.f;
+  }
+
+  // ---- C1: exact per-head max and sum over the visible compressed keys
+  for (int c1 = 0; c1 < nC; ++c1, ++c) {
+    const char* kt = begin_chunk(c);
+#pragma unroll 1
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4_t s[kWaveQ][2];
+      logits_half(kt, hh, s);
+      const int i0 = 64 * c1 + 32 * hh;
+#pragma unroll
+      for (int q = 0; q < kWaveQ; ++q) {
+        const int nv = act[q] ? n_visible(tq[q], p.l, p.d) : 0;
+        float z[2][4];
+        float mx = kNegBig;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = i0 + 16 * mm + 4 * lg + i;
+            z[mm][i] = key < nv ? s[q][mm][i] * sc : -INFINITY;
+            mx = fmaxf(mx, z[mm][i]);
+          }
+        mx = max_over_groups_swap(mx);
+        const float mn = fmaxf(mrun[q], mx);
+        float ls = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ls += exp2f(z[mm][i] - mn);
+        lrun[q] = lrun[q] * exp2f(mrun[q] - mn) + ls;
+        mrun[q] = mn;
+      }
+    }
+  }
+  float Mc[kWaveQ], invL[kWaveQ], gC[kWaveQ];
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    const float lt = sum_over_groups_swap(lrun[q]);
+    Mc[q] = mrun[q];
+    invL[q] = lt > 0.f ? 1.0f / lt : 0.f;
+    gC[q] = gate(q, 0);
+  }
+
+  // ---- C2: normalised p; acc += g_cmp p.Vc; fold p onto selection blocks
+  for (int c2 = 0; c2 < nC; ++c2, ++c) {
+    const char* kt = begin_chunk(c);
+    const char* vt = kt + SH::kKBytes;
+#pragma unroll 1
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4_t s[kWaveQ][2];
+      logits_half(kt, hh, s);
+      const int i0 = 64 * c2 + 32 * hh;
+      u32x4_t pg[kWaveQ], ph[kWaveQ], pl[kWaveQ];
+#pragma unroll
+      for (int q = 0; q < kWaveQ; ++q) {
+        const int nv = (act[q] && lr < p.G) ? n_visible(tq[q], p.l, p.d) : 0;
+        float a[4], bb[4], ga[4], gb[4], ra[4], rb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = i0 + 4 * lg + i;
+          a[i] = key < nv ? exp2f(s[q][0][i] * sc - Mc[q]) * invL[q] : 0.f;
+          bb[i] = key + 16 < nv ? exp2f(s[q][1][i] * sc - Mc[q]) * invL[q] : 0.f;
+          ga[i] = a[i] * gC[q];
+          gb[i] = bb[i] * gC[q];
+        }
+        pg[q] = pack_probs(ga, gb);
+        ph[q] = pack_probs(a, bb);
+        // rounding residual, so that hi + lo carries p to about 16 bits
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wa = ph[q][i >> 1], wb = ph[q][2 + (i >> 1)];
+          ra[i] = a[i] - ((i & 1) ? bf16_hi(wa) : bf16_lo(wa));
+          rb[i] = bb[i] - ((i & 1) ? bf16_hi(wb) : bf16_lo(wb));
+        }
+        pl[q] = pack_probs(ra, rb);
+      }
+      pv_half<DV>(vt, hh, lg, lr, pg, acc);
+      // fold: key i covers stride units [i, i+qd), block j covers [j*rd, (j+1)*rd);
+      // F^T[block][head] = sum over the step's keys of overlap * p (overlap
+      // counts are small integers, exact in bf16), then summed over the heads
+      // (DPP row sum) into the position's score row.
+      const int jb = i0 / rd;
+      const int nrows = (i0 - jb * rd + 31 + qd - 1) / rd + 1;  // blocks the step touches (<= 32)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        if (16 * rt >= nrows) break;
+        const int ublo = (jb + 16 * rt + lr) * rd, ubhi = ublo + rd;
+        uint32_t ow[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          uint32_t bits[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int key = i0 + step_key(lg, 2 * h + e);
+            const int ov = min(key + qd, ubhi) - max(key, ublo);
+            bits[e] = __float_as_uint((float)(ov > 0 ? ov : 0)) >> 16;
+          }
+          ow[h] = bits[0] | (bits[1] << 16);
+        }
+        const u32x4_t om = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+#pragma unroll
+        for (int q = 0; q < kWaveQ; ++q) {
+          f32x4_t F = mfma_bf16(om, ph[q], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          F = mfma_bf16(om, pl[q], F);
+          const int Jq = act[q] ? tq[q] / p.lsel : -1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = row_sum_to_last(F[i]);
+            const int jrel = 16 * rt + 4 * lg + i;
+            const int j = jb + jrel;
+            if (lr == 15 && jrel < nrows && j <= Jq) s_score[4 * wave + q][j] += v * invq;
+          }
+        }
+      }
+    }
+  }
+
+  // ---- top-n per position
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    if (!act[q]) continue;
+    const int J = tq[q] / p.lsel;
+    int32_t* out = p.sel + (((int64_t)b * T + tq[q]) * p.H + g) * p.n;
+    const float* S = s_score[4 * wave + q];
+    if (J < 128) wave_topn<2>(S, J, p.n, p.nloc, p.finit, out);
+    else if (J < 256) wave_topn<4>(S, J, p.n, p.nloc, p.finit, out);
+    else if (J < 512) wave_topn<8>(S, J, p.n, p.nloc, p.finit, out);
+    else wave_topn<kPfMaxBlocks / 64>(S, J, p.n, p.nloc, p.finit, out);
+  }
+
+  // ---- accumulator (g_win o_win + g_cmp o_cmp) to the workspace
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    if (!act[q] || lr >= p.G) continue;
+    float* dst = p.acc + (((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * DV;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* d = dst + acc_channel<DV>(lg, i, 0);
+#pragma unroll
+      for (int j = 0; j < VC; j += 4)
+        *reinterpret_cast<f32x4_t*>(d + j) =
+            f32x4_t{acc[q][j][i], acc[q][j + 1][i], acc[q][j + 2][i], acc[q][j + 3][i]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: selected branch over the union of the tile's selected blocks.
+// ROWS keys are used per step: a whole block for l' = 32 or 64, half a block
+// for l' = 128, and for l' = 16 the block plus 16 masked rows.
+template <int DK, int DV, int LSEL>
+__global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
+  using SH = PfShape<DK, DV>;
+  constexpr int KT = SH::KT, VC = SH::VC;
+  constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > 64 ? 64 : LSEL);
+  constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
+  __shared__ __attribute__((aligned(1024))) char s_buf[2][SH::kBuf];
+  __shared__ uint32_t s_mask[kPfMaxBlocks];  // per block: bit q set if position t0+q chose it
+  __shared__ uint32_t s_list[kPfMaxBlocks];  // the union, ascending: block id << 16 | mask
+  __shared__ int s_scan[4];
+  __shared__ int s_nu;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const TileId ti = tile_id(p);
+  const int b = ti.b, g = ti.g, t0 = ti.t0;
+  const int T = p.T;
+  const int tlast = min(t0 + kTileQ - 1, T - 1);
+  const int Jtile = tlast / LSEL;
+  const int64_t bg = (int64_t)b * p.H + g;
+  const uint16_t* kraw = p.k + bg * T * DK;
+  const uint16_t* vraw = p.v + bg * T * DV;
+
+  // ---- union of the tile's selections
+  for (int j = tid; j <= Jtile; j += 256) s_mask[j] = 0u;
+  __syncthreads();
+  for (int e = tid; e < kTileQ * p.n; e += 256) {
+    const int q = e / p.n;
+    if (t0 + q < T) {
+      const int j = p.sel[(((int64_t)b * T + t0 + q) * p.H + g) * p.n + (e - q * p.n)];
+      if (j >= 0 && j <= Jtile) atomicOr(&s_mask[j], 1u << q);
+    }
+  }
+  __syncthreads();
   {
-    int q = 0;
-    for (int e = tid; e < 16 * DV; e += 256, ++q) {
-      const int h = e / DV, ch = e - h * DV;
-      if (h < p.G) p.out[(qrow + h) * DV + ch] = (uint16_t)f32_to_bf16(res[q]);
+    constexpr int PER = kPfMaxBlocks / 256;
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = tid * PER + k;
+      cnt += (j <= Jtile && s_mask[j] != 0u) ? 1 : 0;
+    }
+    int total;
+    int pos = block_scan<256>(cnt, s_scan, &total);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = tid * PER + k;
+      if (j <= Jtile && s_mask[j] != 0u) s_list[pos++] = ((uint32_t)j << 16) | s_mask[j];
+    }
+    if (tid == 0) s_nu = total;
+  }
+  __syncthreads();
+  const int nsteps = s_nu * SPB;
+
+  int tq[kWaveQ];
+  bool act[kWaveQ];
+  u32x4_t qf[kWaveQ][KT];
+  f32x4_t acc[kWaveQ][VC];
+  float mrun[kWaveQ], lrun[kWaveQ];
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    tq[q] = t0 + 4 * wave + q;
+    act[q] = tq[q] < T;
+    const int tt = act[q] ? tq[q] : T - 1;
+    load_q_frags<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf[q]);
+#pragma unroll
+    for (int j = 0; j < VC; ++j) acc[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mrun[q] = kNegBig;
+    lrun[q] = 0.f;
+  }
+  const float sc = p.scale_log2;
+
+  auto step_row0 = [&](int st) -> int64_t {
+    const int u = st / SPB;
+    return (int64_t)(s_list[u] >> 16) * LSEL + (int64_t)(st - u * SPB) * ROWS;
+  };
+  auto stage = [&](int st, int buf) {
+    const int64_t r0 = step_row0(st);
+    stage_k<DK, ROWS>(kraw, r0, tlast, s_buf[buf], wave, lane);
+    stage_v<DV, ROWS>(vraw, r0, tlast, s_buf[buf] + SH::kKBytes, wave, lane);
+  };
+
+  if (nsteps > 0) stage(0, 0);
+  for (int st = 0; st < nsteps; ++st) {
+    wait_vmem();
+    __syncthreads();
+    if (st + 1 < nsteps) stage(st + 1, (st + 1) & 1);
+    const char* kt = s_buf[st & 1];
+    const char* vt = s_buf[st & 1] + SH::kKBytes;
+    const uint32_t ent = s_list[st / SPB];
+    const uint32_t mine = (ent >> (4 * wave)) & 0xFu;
+    if (mine == 0u) continue;
+    const int jblk = (int)(ent >> 16);
+    const int64_t x0 = step_row0(st);
+    const int64_t xend = (int64_t)(jblk + 1) * LSEL;  // first row past the block
+#pragma unroll
+    for (int q = 0; q < kWaveQ; ++q) {
+      if (!((mine >> q) & 1u)) continue;
+      f32x4_t s[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int ks = 0; ks < KT; ++ks) s[m] = mfma_bf16(lds_k<DK>(kt, m, ks, lane), qf[q][ks], s[m]);
+      float z[MT][4];
+      float mx = kNegBig;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t x = x0 + 16 * m + 4 * lg + i;
+          z[m][i] = (x <= tq[q] && x < xend) ? s[m][i] * sc : -INFINITY;
+          mx = fmaxf(mx, z[m][i]);
+        }
+      mx = max_over_groups_swap(mx);
+      lazy_rescale(mx, mrun[q], lrun[q], acc[q]);
+      float ls = 0.f;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[m][i] = exp2f(z[m][i] - mrun[q]);
+          ls += z[m][i];
+        }
+      lrun[q] += ls;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint32_t vr[8][DV / 32];
+        lds_v_step<DV>(vt, ks, lg, lr, vr);
+        const u32x4_t pk = pack_probs(z[2 * ks], z[2 * ks + 1]);
+#pragma unroll
+        for (int j = 0; j < VC; ++j) {
+          const int wd = j >> 1, h = j & 1;
+          const u32x4_t va = u32x4_t{pack_halves(vr[0][wd], vr[1][wd], h), pack_halves(vr[2][wd], vr[3][wd], h),
+                                     pack_halves(vr[4][wd], vr[5][wd], h), pack_halves(vr[6][wd], vr[7][wd], h)};
+          acc[q][j] = mfma_bf16(va, pk, acc[q][j]);
+        }
+      }
+    }
+  }
+
+  // ---- out = bf16(acc_in + g_slc * o_slc)
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    const float lt = sum_over_groups_swap(lrun[q]);
+    if (!act[q] || lr >= p.G) continue;
+    const int64_t hrow = ((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr;
+    const float f = lt > 0.f ? p.gates[hrow * 3 + 1] / lt : 0.f;
+    const float* src = p.acc + hrow * DV;
+    uint16_t* dst = p.out + hrow * DV;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch0 = acc_channel<DV>(lg, i, 0);
+      float v[VC];
+#pragma unroll
+      for (int j = 0; j < VC; j += 4) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + ch0 + j);
+        v[j] = a[0]; v[j + 1] = a[1]; v[j + 2] = a[2]; v[j + 3] = a[3];
+      }
+      uint32_t w[VC / 2];
+#pragma unroll
+      for (int j = 0; j < VC; j += 2) w[j / 2] = pack_bf16x2(v[j] + f * acc[q][j][i], v[j + 1] + f * acc[q][j + 1][i]);
+      if constexpr (VC == 8) {
+        *reinterpret_cast<u32x4_t*>(dst + ch0) = u32x4_t{w[0], w[1], w[2], w[3]};
+      } else {
+        *reinterpret_cast<u32x2_t*>(dst + ch0) = u32x2_t{w[0], w[1]};
+      }
     }
   }
 }
 
 template <int DK, int DV>
-static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.T)), blk(256);
+static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s, const PhaseEvents* ev) {
+  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.ntile)), blk(256);
+  hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV>), grid, blk, 0, s, p);
+  if (ev) hipEventRecord(ev->ev[2], s);
   switch (p.lsel) {
-    case 16: hipLaunchKernelGGL((prefill_kernel<DK, DV, 16>), grid, blk, 0, s, p); break;
-    case 32: hipLaunchKernelGGL((prefill_kernel<DK, DV, 32>), grid, blk, 0, s, p); break;
-    case 64: hipLaunchKernelGGL((prefill_kernel<DK, DV, 64>), grid, blk, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((prefill_kernel<DK, DV, 128>), grid, blk, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 16>), grid, blk, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 32>), grid, blk, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 64>), grid, blk, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 128>), grid, blk, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
+  if (ev) hipEventRecord(ev->ev[3], s);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s) {
-  if (DK == 192 && DV == 128) return launch_prefill_t<192, 128>(p, s);
-  if (DK == 128 && DV == 128) return launch_prefill_t<128, 128>(p, s);
-  if (DK == 64 && DV == 64) return launch_prefill_t<64, 64>(p, s);
+hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev) {
+  if (DK == 192 && DV == 128) return launch_prefill_t<192, 128>(p, s, ev);
+  if (DK == 128 && DV == 128) return launch_prefill_t<128, 128>(p, s, ev);
+  if (DK == 64 && DV == 64) return launch_prefill_t<64, 64>(p, s, ev);
   return hipErrorInvalidValue;
 }
 

@@ -141,4 +141,40 @@ __device__ void block_topn(const float* S, int J, int n, int nloc, int finit, To
   }
 }
 
+// Single-wave variant for one (query, KV group): candidates 0..J with scores
+// S[j] >= 0, at most 64 * MAXC of them.  Writes the n ids ascending to out
+// (-1 fills the tail when fewer than n candidates exist).  No LDS, no barrier.
+template <int MAXC>
+__device__ void wave_topn(const float* S, int J, int n, int nloc, int finit, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int ncand = J + 1;
+  if (ncand <= n) {
+    for (int r = lane; r < n; r += 64) out[r] = r < ncand ? r : -1;
+    return;
+  }
+  const int lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;
+  const bool f0 = finit && lo_local > 0;
+  const int nf = (J - lo_local + 1) + (f0 ? 1 : 0);
+  const int nr = n - nf;
+  int v = INT32_MAX;
+  if (nr > 0) {
+    uint64_t k[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int j = lane + 64 * c;
+      const bool ok = j < lo_local && !(f0 && j == 0);
+      k[c] = ok ? ((uint64_t)__float_as_uint(S[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j) : 0ull;
+    }
+    const uint64_t best = wave_extract<MAXC>(k, nr);
+    if (lane < nr) v = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+  }
+  if (lane >= nr && lane < n) {
+    const int i = lane - nr;
+    v = f0 ? (i == 0 ? 0 : lo_local + i - 1) : lo_local + i;
+  }
+  int rank = 0;
+  for (int q = 0; q < n; ++q) rank += __builtin_amdgcn_readlane(v, q) < v;
+  if (lane < n) out[rank] = v;
+}
+
 }  // namespace nsa

@@ -65,8 +65,12 @@ def test_workspace_sizes_are_positive_and_monotone():
     b = _ws(_dims(), _cfg(), 65536)
     c = _ws(_dims(batch=16), _cfg(), 65536)
     assert 0 < a < b < c
-    assert N.nsa_prefill_workspace_size(_dims(batch=1), _cfg(), 32768, False) == 0
-    assert N.nsa_prefill_workspace_size(_dims(batch=1), _cfg(), 32768, True) >= 4 * 2047 * (192 + 128) * 2
+    # prefill: fp32 partial output [T, 64, 128] + selection ids [T, 4, 16], plus the
+    # compressed cache when compressing in the call
+    base = 32768 * 64 * 128 * 4 + 32768 * 4 * 16 * 4
+    assert N.nsa_prefill_workspace_size(_dims(batch=1), _cfg(), 32768, False) == base
+    assert N.nsa_prefill_workspace_size(_dims(batch=1), _cfg(), 32768, True) >= base + 4 * 2047 * (192 + 128) * 2
+    assert N.nsa_prefill_workspace_size(_dims(batch=1), _cfg(), 65536, False) > 0   # 1024 blocks: supported
 
 
 @pytest.mark.parametrize("dims_kw,cfg_kw,L,status", [
