@@ -98,8 +98,14 @@ __device__ __forceinline__ float row_sum_to_last(float v) {
 __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
-// Wait for all of this wave's outstanding vector-memory operations (vmcnt 0).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (they complete in issue order), leaving the export and LDS counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0070 | 0x0F00 | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
 // Select 16-bit half `h` (0 low, 1 high) of a and b and pack as (a_h | b_h << 16).
 __device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int h) {

@@ -1,9 +1,9 @@
 // NSA causal prefill on gfx950, tiled over query positions.
 //
-// Both kernels run one workgroup (4 waves) per (sequence, KV group, tile of 16
-// consecutive positions t0 .. t0+15).  Wave w owns positions t0+4w .. t0+4w+3
-// and keeps, for each, the group's query fragments and a 16-head x d_v fp32
-// accumulator in registers.  Key/value tiles of 64 rows are copied straight
+// Both kernels run one workgroup (8 waves, two per SIMD) per (sequence, KV
+// group, tile of 16 consecutive positions t0 .. t0+15).  Wave w owns positions
+// t0+2w and t0+2w+1 and keeps, for each, the group's query fragments and a
+// 16-head x d_v fp32 accumulator in registers.  Key/value tiles of 64 rows are copied straight
 // from global memory into LDS (no register round trip), double buffered, and
 // each staged tile serves every position of the workgroup that needs it.
 //
@@ -37,8 +37,15 @@ namespace nsa {
 namespace {
 
 constexpr int kTileQ = 16;         // positions per workgroup
-constexpr int kWaveQ = 4;          // positions per wave
+constexpr int kWaves = 8;          // waves per workgroup (two per SIMD)
+constexpr int kWaveQ = kTileQ / kWaves;  // positions per wave
+constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1e30f;  // running-max start: finite, so exp2 never sees inf - inf
+
+// Copy instructions every wave issues for a ROWS-row K (+ V) tile (a lower bound:
+// waiting until at most this many are outstanding covers every earlier copy).
+template <int DK, int DV, int ROWS, bool WITH_V>
+constexpr int kLdMin = ((ROWS / 16) * (DK / 32)) / kWaves + (WITH_V ? (ROWS * DV * 2 / 1024) / kWaves : 0);
 
 template <int DK, int DV>
 struct PfShape {
@@ -50,7 +57,9 @@ struct PfShape {
 };
 
 // ---- staging of ROWS rows [row0, row0+ROWS) of a row-major bf16 array; rows
-// past rowmax are replaced by row rowmax (the caller masks their logits).
+// past rowmax are replaced by row rowmax (the caller masks their logits).  The
+// kWaves waves share the copy; each wave issues at least
+// floor(NF / kWaves) + floor(NI / kWaves) copy instructions (kLdMin below).
 
 // K tile in fragment order: fragment f = m*KT + ks holds, at 16*lane, the eight
 // dims 32*ks + 8*(lane/16) .. of row 16*m + lane%16 -- the A operand of the S^T
@@ -59,10 +68,10 @@ template <int DK, int ROWS = 64>
 __device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
                                         int lane) {
   constexpr int KT = DK / 32, NF = (ROWS / 16) * KT;
-  static_assert(NF % 4 == 0, "fragments split evenly over 4 waves");
 #pragma unroll
-  for (int ii = 0; ii < NF / 4; ++ii) {
-    const int f = wave + 4 * ii;
+  for (int ii = 0; ii < (NF + kWaves - 1) / kWaves; ++ii) {
+    const int f = wave + kWaves * ii;
+    if (NF % kWaves != 0 && f >= NF) break;
     const int m = f / KT, ks = f - m * KT;
     int64_t row = row0 + 16 * m + (lane & 15);
     row = row < rowmax ? row : rowmax;
@@ -75,10 +84,10 @@ template <int DV, int ROWS = 64>
 __device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
                                         int lane) {
   constexpr int NI = ROWS * DV * 2 / 1024, RB = DV * 2;
-  static_assert(NI % 4 == 0, "pieces split evenly over 4 waves");
 #pragma unroll
-  for (int ii = 0; ii < NI / 4; ++ii) {
-    const int i = wave + 4 * ii;
+  for (int ii = 0; ii < (NI + kWaves - 1) / kWaves; ++ii) {
+    const int i = wave + kWaves * ii;
+    if (NI % kWaves != 0 && i >= NI) break;
     const int off = i * 1024 + lane * 16;
     int64_t row = row0 + off / RB;
     row = row < rowmax ? row : rowmax;
@@ -120,7 +129,7 @@ __device__ __forceinline__ void lazy_rescale(float mx, float& m, float& l, f32x4
   const bool move = mx > m + 8.0f;
   if (__ballot(move) != 0ull) {  // wave-uniform
     const float mn = move ? mx : m;
-    const float alpha = exp2f(m - mn);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[j] *= alpha;
@@ -165,12 +174,14 @@ __device__ __forceinline__ TileId tile_id(const PrefillParams& p) {
 
 // ---------------------------------------------------------------------------
 // Kernel 1: window + compressed branches, group scores, top-n.
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
+// NBUF key-tile buffers (NBUF - 1 tiles in flight); MAXB score slots per position.
+template <int DK, int DV, int NBUF, int MAXB>
+__global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p) {
   using SH = PfShape<DK, DV>;
   constexpr int KT = SH::KT, VC = SH::VC;
-  __shared__ __attribute__((aligned(1024))) char s_buf[2][SH::kBuf];
-  __shared__ float s_score[kTileQ][kPfMaxBlocks];
+  constexpr int NLD_K = kLdMin<DK, DV, 64, false>, NLD_KV = kLdMin<DK, DV, 64, true>;
+  __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
+  __shared__ float s_score[kTileQ][MAXB];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const TileId ti = tile_id(p);
@@ -191,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
   const int nch = nW + 2 * nC;
   const int Jtile = tlast / p.lsel;
 
-  for (int e = tid; e < kTileQ * (Jtile + 1); e += 256) s_score[e / (Jtile + 1)][e % (Jtile + 1)] = 0.f;
+  for (int e = tid; e < kTileQ * (Jtile + 1); e += kThreads) s_score[e / (Jtile + 1)][e % (Jtile + 1)] = 0.f;
 
   auto stage = [&](int c, int buf) {
     char* kt = s_buf[buf];
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
   float mrun[kWaveQ], lrun[kWaveQ];
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
-    tq[q] = t0 + 4 * wave + q;
+    tq[q] = t0 + kWaveQ * wave + q;
     act[q] = tq[q] < T;
     const int tt = act[q] ? tq[q] : T - 1;
     load_q_frags<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf[q]);
@@ -233,13 +244,22 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
   const int qd = p.l / p.d, rd = p.lsel / p.d;  // key and block lengths in stride units
   const float invq = 1.0f / (float)qd;
 
-  // One pipeline over all chunks (window, then C1, then C2): chunk c + 1 is
-  // copied into the other buffer while chunk c is computed.
+  // One pipeline over all chunks (window, then C1, then C2): chunks c+1 ..
+  // c+NBUF-1 are in flight while chunk c is computed.  Copies complete in issue
+  // order, so chunk c has landed once at most the later chunks' copies remain.
+  auto nld = [&](int c) -> int { return c >= nch ? 0 : ((c >= nW && c < nW + nC) ? NLD_K : NLD_KV); };
   auto begin_chunk = [&](int c) -> const char* {
-    wait_vmem();
+    if constexpr (NBUF == 3) {
+      const int later = nld(c + 1);
+      if (later == 0) wait_vmem_le<0>();
+      else if (later == NLD_K) wait_vmem_le<NLD_K>();
+      else wait_vmem_le<NLD_KV>();
+    } else {
+      wait_vmem_le<0>();
+    }
     __syncthreads();
-    if (c + 1 < nch) stage(c + 1, (c + 1) & 1);
-    return s_buf[c & 1];
+    if (c + NBUF - 1 < nch) stage(c + NBUF - 1, (c + NBUF - 1) % NBUF);
+    return s_buf[c % NBUF];
   };
   // logits of one 32-key half of the staged chunk for the wave's positions
   // (each K fragment read once from LDS and used for all of them)
@@ -256,7 +276,9 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
       }
   };
 
-  stage(0, 0);
+#pragma unroll
+  for (int c0 = 0; c0 < NBUF - 1; ++c0)
+    if (c0 < nch) stage(c0, c0);
   int c = 0;
   // ---- W: window (t - w, t], online softmax into acc
   for (int cw = 0; cw < nW; ++cw, ++c) {
@@ -288,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            z[mm][i] = exp2f(z[mm][i] - mrun[q]);
+            z[mm][i] = __builtin_amdgcn_exp2f(z[mm][i] - mrun[q]);
             ls += z[mm][i];
           }
         lrun[q] += ls;
@@ -335,8 +357,8 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ls += exp2f(z[mm][i] - mn);
-        lrun[q] = lrun[q] * exp2f(mrun[q] - mn) + ls;
+          for (int i = 0; i < 4; ++i) ls += __builtin_amdgcn_exp2f(z[mm][i] - mn);
+        lrun[q] = lrun[q] * __builtin_amdgcn_exp2f(mrun[q] - mn) + ls;
         mrun[q] = mn;
       }
     }
@@ -367,8 +389,8 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = i0 + 4 * lg + i;
-          a[i] = key < nv ? exp2f(s[q][0][i] * sc - Mc[q]) * invL[q] : 0.f;
-          bb[i] = key + 16 < nv ? exp2f(s[q][1][i] * sc - Mc[q]) * invL[q] : 0.f;
+          a[i] = key < nv ? __builtin_amdgcn_exp2f(s[q][0][i] * sc - Mc[q]) * invL[q] : 0.f;
+          bb[i] = key + 16 < nv ? __builtin_amdgcn_exp2f(s[q][1][i] * sc - Mc[q]) * invL[q] : 0.f;
           ga[i] = a[i] * gC[q];
           gb[i] = bb[i] * gC[q];
         }
@@ -417,7 +439,7 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
             const float v = row_sum_to_last(F[i]);
             const int jrel = 16 * rt + 4 * lg + i;
             const int j = jb + jrel;
-            if (lr == 15 && jrel < nrows && j <= Jq) s_score[4 * wave + q][j] += v * invq;
+            if (lr == 15 && jrel < nrows && j <= Jq) s_score[kWaveQ * wave + q][j] += v * invq;
           }
         }
       }
@@ -430,11 +452,11 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
     if (!act[q]) continue;
     const int J = tq[q] / p.lsel;
     int32_t* out = p.sel + (((int64_t)b * T + tq[q]) * p.H + g) * p.n;
-    const float* S = s_score[4 * wave + q];
+    const float* S = s_score[kWaveQ * wave + q];
     if (J < 128) wave_topn<2>(S, J, p.n, p.nloc, p.finit, out);
     else if (J < 256) wave_topn<4>(S, J, p.n, p.nloc, p.finit, out);
-    else if (J < 512) wave_topn<8>(S, J, p.n, p.nloc, p.finit, out);
-    else wave_topn<kPfMaxBlocks / 64>(S, J, p.n, p.nloc, p.finit, out);
+    else if (MAXB <= 512 || J < 512) wave_topn<8>(S, J, p.n, p.nloc, p.finit, out);
+    else wave_topn<MAXB / 64>(S, J, p.n, p.nloc, p.finit, out);
   }
 
   // ---- accumulator (g_win o_win + g_cmp o_cmp) to the workspace
@@ -458,15 +480,17 @@ __global__ __launch_bounds__(256, 1) void pf_cmp_win_kernel(PrefillParams p) {
 // ROWS keys are used per step: a whole block for l' = 32 or 64, half a block
 // for l' = 128, and for l' = 16 the block plus 16 masked rows.
 template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   using SH = PfShape<DK, DV>;
   constexpr int KT = SH::KT, VC = SH::VC;
   constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > 64 ? 64 : LSEL);
   constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
-  __shared__ __attribute__((aligned(1024))) char s_buf[2][SH::kBuf];
+  constexpr int NBUF = 3;                                   // two steps in flight
+  constexpr int NLD = kLdMin<DK, DV, ROWS, true>;
+  __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
   __shared__ uint32_t s_mask[kPfMaxBlocks];  // per block: bit q set if position t0+q chose it
   __shared__ uint32_t s_list[kPfMaxBlocks];  // the union, ascending: block id << 16 | mask
-  __shared__ int s_scan[4];
+  __shared__ int s_scan[kWaves];
   __shared__ int s_nu;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
@@ -480,9 +504,9 @@ __global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
   const uint16_t* vraw = p.v + bg * T * DV;
 
   // ---- union of the tile's selections
-  for (int j = tid; j <= Jtile; j += 256) s_mask[j] = 0u;
+  for (int j = tid; j <= Jtile; j += kThreads) s_mask[j] = 0u;
   __syncthreads();
-  for (int e = tid; e < kTileQ * p.n; e += 256) {
+  for (int e = tid; e < kTileQ * p.n; e += kThreads) {
     const int q = e / p.n;
     if (t0 + q < T) {
       const int j = p.sel[(((int64_t)b * T + t0 + q) * p.H + g) * p.n + (e - q * p.n)];
@@ -491,7 +515,7 @@ __global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
   }
   __syncthreads();
   {
-    constexpr int PER = kPfMaxBlocks / 256;
+    constexpr int PER = kPfMaxBlocks / kThreads;
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -499,7 +523,7 @@ __global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
       cnt += (j <= Jtile && s_mask[j] != 0u) ? 1 : 0;
     }
     int total;
-    int pos = block_scan<256>(cnt, s_scan, &total);
+    int pos = block_scan<kThreads>(cnt, s_scan, &total);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = tid * PER + k;
@@ -517,7 +541,7 @@ __global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
   float mrun[kWaveQ], lrun[kWaveQ];
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
-    tq[q] = t0 + 4 * wave + q;
+    tq[q] = t0 + kWaveQ * wave + q;
     act[q] = tq[q] < T;
     const int tt = act[q] ? tq[q] : T - 1;
     load_q_frags<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf[q]);
@@ -538,15 +562,18 @@ __global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
     stage_v<DV, ROWS>(vraw, r0, tlast, s_buf[buf] + SH::kKBytes, wave, lane);
   };
 
-  if (nsteps > 0) stage(0, 0);
+#pragma unroll
+  for (int s0 = 0; s0 < NBUF - 1; ++s0)
+    if (s0 < nsteps) stage(s0, s0);
   for (int st = 0; st < nsteps; ++st) {
-    wait_vmem();
+    if (st + 1 < nsteps) wait_vmem_le<NLD>();
+    else wait_vmem_le<0>();
     __syncthreads();
-    if (st + 1 < nsteps) stage(st + 1, (st + 1) & 1);
-    const char* kt = s_buf[st & 1];
-    const char* vt = s_buf[st & 1] + SH::kKBytes;
+    if (st + NBUF - 1 < nsteps) stage(st + NBUF - 1, (st + NBUF - 1) % NBUF);
+    const char* kt = s_buf[st % NBUF];
+    const char* vt = s_buf[st % NBUF] + SH::kKBytes;
     const uint32_t ent = s_list[st / SPB];
-    const uint32_t mine = (ent >> (4 * wave)) & 0xFu;
+    const uint32_t mine = (ent >> (kWaveQ * wave)) & ((1u << kWaveQ) - 1u);
     if (mine == 0u) continue;
     const int jblk = (int)(ent >> 16);
     const int64_t x0 = step_row0(st);
@@ -578,7 +605,7 @@ __global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          z[m][i] = exp2f(z[m][i] - mrun[q]);
+          z[m][i] = __builtin_amdgcn_exp2f(z[m][i] - mrun[q]);
           ls += z[m][i];
         }
       lrun[q] += ls;
@@ -630,8 +657,10 @@ __global__ __launch_bounds__(256, 1) void pf_sel_kernel(PrefillParams p) {
 
 template <int DK, int DV>
 static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s, const PhaseEvents* ev) {
-  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.ntile)), blk(256);
-  hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV>), grid, blk, 0, s, p);
+  const dim3 grid((unsigned)((int64_t)p.B * p.H * p.ntile)), blk(kThreads);
+  // up to 512 candidate blocks the score rows leave room for a third key buffer
+  if ((p.T - 1) / p.lsel < 512) hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV, 3, 512>), grid, blk, 0, s, p);
+  else hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV, 2, kPfMaxBlocks>), grid, blk, 0, s, p);
   if (ev) hipEventRecord(ev->ev[2], s);
   switch (p.lsel) {
     case 16: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 16>), grid, blk, 0, s, p); break;
