@@ -30,15 +30,16 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 // Global loads of 16 / 8 bytes.  Every caller proves the address in bounds
 // before calling; out-of-range rows are replaced by zeros at the call site.
@@ -107,9 +108,10 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
-// Select 16-bit half `h` (0 low, 1 high) of a and b and pack as (a_h | b_h << 16).
+// Select 16-bit half `h` (0 low, 1 high) of a and b and pack as (a_h | b_h << 16):
+// one v_perm_b32 (byte selectors 0-3 pick from the second operand, 4-7 from the first).
 __device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int h) {
-  return h ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+  return __builtin_amdgcn_perm(b, a, h ? 0x07060302u : 0x05040100u);
 }
 
 // Exclusive prefix sum over the NT threads of a block (NT/64 waves).  `scratch`

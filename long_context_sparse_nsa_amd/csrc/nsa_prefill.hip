@@ -36,11 +36,12 @@ namespace nsa {
 
 namespace {
 
-constexpr int kTileQ = 16;         // positions per workgroup
-constexpr int kWaves = 8;          // waves per workgroup (two per SIMD)
+constexpr int kTileQ = 16;               // positions per workgroup
+constexpr int kWaves = 8;                // waves per workgroup (two per SIMD)
 constexpr int kWaveQ = kTileQ / kWaves;  // positions per wave
 constexpr int kThreads = 64 * kWaves;
-constexpr float kNegBig = -1e30f;  // running-max start: finite, so exp2 never sees inf - inf
+constexpr float kNegBig = -1e30f;        // running-reference start: finite, so exp2 never sees inf - inf
+constexpr float kLazy = 8.0f;            // the softmax reference moves only when exceeded by this (log2 units)
 
 // Copy instructions every wave issues for a ROWS-row K (+ V) tile (a lower bound:
 // waiting until at most this many are outstanding covers every earlier copy).
@@ -58,8 +59,8 @@ struct PfShape {
 
 // ---- staging of ROWS rows [row0, row0+ROWS) of a row-major bf16 array; rows
 // past rowmax are replaced by row rowmax (the caller masks their logits).  The
-// kWaves waves share the copy; each wave issues at least
-// floor(NF / kWaves) + floor(NI / kWaves) copy instructions (kLdMin below).
+// kWaves waves share the copy (wave is wave-uniform); each issues at least
+// kLdMin copy instructions.
 
 // K tile in fragment order: fragment f = m*KT + ks holds, at 16*lane, the eight
 // dims 32*ks + 8*(lane/16) .. of row 16*m + lane%16 -- the A operand of the S^T
@@ -68,14 +69,22 @@ template <int DK, int ROWS = 64>
 __device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
                                         int lane) {
   constexpr int KT = DK / 32, NF = (ROWS / 16) * KT;
+  const bool inside = row0 + ROWS - 1 <= rowmax;
+  const int loff = (lane & 15) * DK + 8 * (lane >> 4);
 #pragma unroll
   for (int ii = 0; ii < (NF + kWaves - 1) / kWaves; ++ii) {
     const int f = wave + kWaves * ii;
     if (NF % kWaves != 0 && f >= NF) break;
     const int m = f / KT, ks = f - m * KT;
-    int64_t row = row0 + 16 * m + (lane & 15);
-    row = row < rowmax ? row : rowmax;
-    copy16_to_lds(base + row * DK + 32 * ks + 8 * (lane >> 4), dst + f * 1024);
+    const uint16_t* src;
+    if (inside) {
+      src = base + (row0 + 16 * m) * DK + 32 * ks + loff;
+    } else {
+      int64_t row = row0 + 16 * m + (lane & 15);
+      row = row < rowmax ? row : rowmax;
+      src = base + row * DK + 32 * ks + 8 * (lane >> 4);
+    }
+    copy16_to_lds(src, dst + f * 1024);
   }
 }
 
@@ -84,14 +93,22 @@ template <int DV, int ROWS = 64>
 __device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
                                         int lane) {
   constexpr int NI = ROWS * DV * 2 / 1024, RB = DV * 2;
+  const bool inside = row0 + ROWS - 1 <= rowmax;
+  const char* bb = reinterpret_cast<const char*>(base);
 #pragma unroll
   for (int ii = 0; ii < (NI + kWaves - 1) / kWaves; ++ii) {
     const int i = wave + kWaves * ii;
     if (NI % kWaves != 0 && i >= NI) break;
     const int off = i * 1024 + lane * 16;
-    int64_t row = row0 + off / RB;
-    row = row < rowmax ? row : rowmax;
-    copy16_to_lds(reinterpret_cast<const char*>(base + row * DV) + (off % RB), dst + i * 1024);
+    const char* src;
+    if (inside) {
+      src = bb + row0 * RB + off;
+    } else {
+      int64_t row = row0 + off / RB;
+      row = row < rowmax ? row : rowmax;
+      src = bb + row * RB + (off % RB);
+    }
+    copy16_to_lds(src, dst + i * 1024);
   }
 }
 
@@ -119,20 +136,37 @@ __device__ __forceinline__ void lds_v_step(const char* vt, int ks, int lg, int l
   }
 }
 
-// Online softmax with a lazily moved reference: the running reference m only
-// moves when a logit exceeds it by more than 8 (log2 units), so exp2(z - m)
-// stays below 2^8 and the accumulator is rescaled rarely.  The final division by
-// the sum taken against the same reference makes the result independent of m.
-// mx is the block's maximum logit of this lane's head (equal on its 4 lanes).
+// V^T operand j of a step (channels (DV/16)*m + j), from the rows read above.
+template <int DV>
+__device__ __forceinline__ u32x4_t v_operand(const uint32_t (&vr)[8][DV / 32], int j) {
+  const int wd = j >> 1, h = j & 1;
+  return u32x4_t{pack_halves(vr[0][wd], vr[1][wd], h), pack_halves(vr[2][wd], vr[3][wd], h),
+                 pack_halves(vr[4][wd], vr[5][wd], h), pack_halves(vr[6][wd], vr[7][wd], h)};
+}
+
+// A operand with row 0 all ones (bf16 1.0) and zeros elsewhere: MFMA'd with a
+// P^T operand it adds, in row 0 (lane lr = head, element 0), the step's sum of
+// the bf16 probabilities -- the softmax denominator of exactly the weights the
+// value product used.
+__device__ __forceinline__ u32x4_t ones_row_operand(int lr) {
+  const uint32_t v = lr == 0 ? 0x3F803F80u : 0u;
+  return u32x4_t{v, v, v, v};
+}
+
+// Online softmax with a lazily moved reference m (scaled log2 units): m only
+// moves when the block maximum ms exceeds it by more than kLazy, so exp2(z - m)
+// stays below 2^kLazy and the accumulators are rescaled rarely.  The final
+// division by the sum taken against the same reference makes the result
+// independent of m.  ms is equal on the 4 lanes of a head.
 template <int VC>
-__device__ __forceinline__ void lazy_rescale(float mx, float& m, float& l, f32x4_t (&acc)[VC]) {
-  const bool move = mx > m + 8.0f;
+__device__ __forceinline__ void lazy_rescale(float ms, float& m, f32x4_t (&acc)[VC], f32x4_t& lsum) {
+  const bool move = ms > m + kLazy;
   if (__ballot(move) != 0ull) {  // wave-uniform
-    const float mn = move ? mx : m;
+    const float mn = move ? ms : m;
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    l *= alpha;
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[j] *= alpha;
+    lsum *= alpha;
     m = mn;
   }
 }
@@ -146,15 +180,18 @@ __device__ __forceinline__ void pv_half(const char* vt, int ks, int lg, int lr, 
   lds_v_step<DV>(vt, ks, lg, lr, vr);
 #pragma unroll
   for (int j = 0; j < DV / 16; ++j) {
-    const int wd = j >> 1, h = j & 1;
-    const u32x4_t va = u32x4_t{pack_halves(vr[0][wd], vr[1][wd], h), pack_halves(vr[2][wd], vr[3][wd], h),
-                               pack_halves(vr[4][wd], vr[5][wd], h), pack_halves(vr[6][wd], vr[7][wd], h)};
+    const u32x4_t va = v_operand<DV>(vr, j);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) acc[q][j] = mfma_bf16(va, pk[q], acc[q][j]);
   }
 }
 
 __device__ __forceinline__ int n_visible(int t, int l, int d) { return t + 1 >= l ? (t + 1 - l) / d + 1 : 0; }
+
+__device__ __forceinline__ float max8(const float (&z)[2][4]) {
+  return fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+               fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+}
 
 // Workgroup -> (sequence b, group g, tile).  Tiles are issued latest first (they
 // carry the most compressed keys); consecutive workgroup ids cycle through the
@@ -183,7 +220,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
   __shared__ float s_score[kTileQ][MAXB];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const TileId ti = tile_id(p);
   const int b = ti.b, g = ti.g, t0 = ti.t0;
   const int T = p.T;
@@ -220,22 +258,24 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     }
   };
 
-  // per-position state (positions t0 + 4*wave + q)
-  int tq[kWaveQ];
+  // per-position state (positions t0 + kWaveQ*wave + q; the scalars are wave-uniform)
+  int tq[kWaveQ], nvq[kWaveQ];
   bool act[kWaveQ];
   u32x4_t qf[kWaveQ][KT];
   f32x4_t acc[kWaveQ][VC];
-  float mrun[kWaveQ], lrun[kWaveQ];
+  f32x4_t lsum[kWaveQ];
+  float mref[kWaveQ];
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
     tq[q] = t0 + kWaveQ * wave + q;
     act[q] = tq[q] < T;
+    nvq[q] = act[q] ? n_visible(tq[q], p.l, p.d) : 0;
     const int tt = act[q] ? tq[q] : T - 1;
     load_q_frags<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf[q]);
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    mrun[q] = kNegBig;
-    lrun[q] = 0.f;
+    lsum[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mref[q] = kNegBig;
   }
   auto gate = [&](int q, int br) -> float {
     return (act[q] && lr < p.G) ? p.gates[(((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * 3 + br] : 0.f;
@@ -243,6 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   const float sc = p.scale_log2;
   const int qd = p.l / p.d, rd = p.lsel / p.d;  // key and block lengths in stride units
   const float invq = 1.0f / (float)qd;
+  const u32x4_t ones_a = ones_row_operand(lr);
 
   // One pipeline over all chunks (window, then C1, then C2): chunks c+1 ..
   // c+NBUF-1 are in flight while chunk c is computed.  Copies complete in issue
@@ -280,57 +321,66 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   for (int c0 = 0; c0 < NBUF - 1; ++c0)
     if (c0 < nch) stage(c0, c0);
   int c = 0;
+
   // ---- W: window (t - w, t], online softmax into acc
   for (int cw = 0; cw < nW; ++cw, ++c) {
     const char* kt = begin_chunk(c);
     const char* vt = kt + SH::kKBytes;
 #pragma unroll 1
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < 2; ++hh) {  // the chunk's two 32-key halves (kept rolled: register budget)
       f32x4_t s[kWaveQ][2];
       logits_half(kt, hh, s);
       const int x0 = xlo + 64 * cw + 32 * hh;
       u32x4_t pk[kWaveQ];
 #pragma unroll
       for (int q = 0; q < kWaveQ; ++q) {
+        // keys x with xlo_q < x <= xhi_q are in the window (none for padding positions)
+        const int xhi = act[q] ? tq[q] : -1, xlo_q = tq[q] - p.w;
         float z[2][4];
-        float mx = kNegBig;
+        if (x0 > xlo_q && x0 + 31 <= xhi) {  // wave-uniform: no key of the half masked
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[mm][i] = s[q][mm][i];
+        } else {
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int x = x0 + 16 * mm + 4 * lg + i;
+              z[mm][i] = (x <= xhi && x > xlo_q) ? s[q][mm][i] : -INFINITY;
+            }
+        }
+        const float mx = max_over_groups_swap(max8(z));
+        lazy_rescale(mx * sc, mref[q], acc[q], lsum[q]);
+        const float nm = -mref[q];
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int x = x0 + 16 * mm + 4 * lg + i;
-            const bool ok = act[q] && x <= tq[q] && x > tq[q] - p.w;
-            z[mm][i] = ok ? s[q][mm][i] * sc : -INFINITY;
-            mx = fmaxf(mx, z[mm][i]);
-          }
-        mx = max_over_groups_swap(mx);
-        lazy_rescale(mx, mrun[q], lrun[q], acc[q]);
-        float ls = 0.f;
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            z[mm][i] = __builtin_amdgcn_exp2f(z[mm][i] - mrun[q]);
-            ls += z[mm][i];
-          }
-        lrun[q] += ls;
+          for (int i = 0; i < 4; ++i) z[mm][i] = __builtin_amdgcn_exp2f(fmaf(z[mm][i], sc, nm));
         pk[q] = pack_probs(z[0], z[1]);
       }
       pv_half<DV>(vt, hh, lg, lr, pk, acc);
+#pragma unroll
+      for (int q = 0; q < kWaveQ; ++q) lsum[q] = mfma_bf16(ones_a, pk[q], lsum[q]);
     }
   }
-  // acc <- g_win * o_win; fresh running state for C1
+  // acc <- g_win * o_win (the denominator of head lr sits in lane lr, element 0)
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
-    const float lt = sum_over_groups_swap(lrun[q]);
+    const float lt = __shfl(lsum[q][0], lr);
     const float f = lt > 0.f ? gate(q, 2) / lt : 0.f;
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[q][j] *= f;
-    mrun[q] = kNegBig;
-    lrun[q] = 0.f;
   }
 
   // ---- C1: exact per-head max and sum over the visible compressed keys
+  float lc[kWaveQ];
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    mref[q] = kNegBig;
+    lc[q] = 0.f;
+  }
   for (int c1 = 0; c1 < nC; ++c1, ++c) {
     const char* kt = begin_chunk(c);
 #pragma unroll 1
@@ -340,35 +390,40 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
       const int i0 = 64 * c1 + 32 * hh;
 #pragma unroll
       for (int q = 0; q < kWaveQ; ++q) {
-        const int nv = act[q] ? n_visible(tq[q], p.l, p.d) : 0;
         float z[2][4];
-        float mx = kNegBig;
+        if (i0 + 31 < nvq[q]) {  // wave-uniform: every key of the half visible
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
+          for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = i0 + 16 * mm + 4 * lg + i;
-            z[mm][i] = key < nv ? s[q][mm][i] * sc : -INFINITY;
-            mx = fmaxf(mx, z[mm][i]);
-          }
-        mx = max_over_groups_swap(mx);
-        const float mn = fmaxf(mrun[q], mx);
+            for (int i = 0; i < 4; ++i) z[mm][i] = s[q][mm][i];
+        } else {
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = i0 + 16 * mm + 4 * lg + i;
+              z[mm][i] = key < nvq[q] ? s[q][mm][i] : -INFINITY;
+            }
+        }
+        const float mx = max_over_groups_swap(max8(z));
+        const float mn = fmaxf(mref[q], mx * sc);
         float ls = 0.f;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ls += __builtin_amdgcn_exp2f(z[mm][i] - mn);
-        lrun[q] = lrun[q] * __builtin_amdgcn_exp2f(mrun[q] - mn) + ls;
-        mrun[q] = mn;
+          for (int i = 0; i < 4; ++i) ls += __builtin_amdgcn_exp2f(fmaf(z[mm][i], sc, -mn));
+        lc[q] = lc[q] * __builtin_amdgcn_exp2f(mref[q] - mn) + ls;
+        mref[q] = mn;
       }
     }
   }
-  float Mc[kWaveQ], invL[kWaveQ], gC[kWaveQ];
+  // p = exp2(s*sc - bias) is the normalised probability; bias = +inf zeroes the
+  // padding heads and positions without visible compressed keys
+  float bias[kWaveQ], gC[kWaveQ];
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
-    const float lt = sum_over_groups_swap(lrun[q]);
-    Mc[q] = mrun[q];
-    invL[q] = lt > 0.f ? 1.0f / lt : 0.f;
+    const float L = sum_over_groups_swap(lc[q]);
+    bias[q] = (L > 0.f && lr < p.G) ? mref[q] + __builtin_log2f(L) : INFINITY;
     gC[q] = gate(q, 0);
   }
 
@@ -384,13 +439,23 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
       u32x4_t pg[kWaveQ], ph[kWaveQ], pl[kWaveQ];
 #pragma unroll
       for (int q = 0; q < kWaveQ; ++q) {
-        const int nv = (act[q] && lr < p.G) ? n_visible(tq[q], p.l, p.d) : 0;
+        const float nb = -bias[q];
         float a[4], bb[4], ga[4], gb[4], ra[4], rb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = i0 + 4 * lg + i;
-          a[i] = key < nv ? __builtin_amdgcn_exp2f(s[q][0][i] * sc - Mc[q]) * invL[q] : 0.f;
-          bb[i] = key + 16 < nv ? __builtin_amdgcn_exp2f(s[q][1][i] * sc - Mc[q]) * invL[q] : 0.f;
+          a[i] = __builtin_amdgcn_exp2f(fmaf(s[q][0][i], sc, nb));
+          bb[i] = __builtin_amdgcn_exp2f(fmaf(s[q][1][i], sc, nb));
+        }
+        if (i0 + 31 >= nvq[q]) {  // wave-uniform: some key of the half not visible
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = i0 + 4 * lg + i;
+            a[i] = key < nvq[q] ? a[i] : 0.f;
+            bb[i] = key + 16 < nvq[q] ? bb[i] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
           ga[i] = a[i] * gC[q];
           gb[i] = bb[i] * gC[q];
         }
@@ -485,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   constexpr int KT = SH::KT, VC = SH::VC;
   constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > 64 ? 64 : LSEL);
   constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
-  constexpr int NBUF = 3;                                   // two steps in flight
+  constexpr int NBUF = 3;                    // two steps in flight
   constexpr int NLD = kLdMin<DK, DV, ROWS, true>;
   __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
   __shared__ uint32_t s_mask[kPfMaxBlocks];  // per block: bit q set if position t0+q chose it
@@ -493,7 +558,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   __shared__ int s_scan[kWaves];
   __shared__ int s_nu;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const TileId ti = tile_id(p);
   const int b = ti.b, g = ti.g, t0 = ti.t0;
   const int T = p.T;
@@ -538,7 +604,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   bool act[kWaveQ];
   u32x4_t qf[kWaveQ][KT];
   f32x4_t acc[kWaveQ][VC];
-  float mrun[kWaveQ], lrun[kWaveQ];
+  f32x4_t lsum[kWaveQ];
+  float mref[kWaveQ];
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
     tq[q] = t0 + kWaveQ * wave + q;
@@ -547,17 +614,18 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     load_q_frags<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf[q]);
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[q][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    mrun[q] = kNegBig;
-    lrun[q] = 0.f;
+    lsum[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mref[q] = kNegBig;
   }
   const float sc = p.scale_log2;
+  const u32x4_t ones_a = ones_row_operand(lr);
 
   auto step_row0 = [&](int st) -> int64_t {
     const int u = st / SPB;
     return (int64_t)(s_list[u] >> 16) * LSEL + (int64_t)(st - u * SPB) * ROWS;
   };
   auto stage = [&](int st, int buf) {
-    const int64_t r0 = step_row0(st);
+    const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane((int)step_row0(st));
     stage_k<DK, ROWS>(kraw, r0, tlast, s_buf[buf], wave, lane);
     stage_v<DV, ROWS>(vraw, r0, tlast, s_buf[buf] + SH::kKBytes, wave, lane);
   };
@@ -572,12 +640,12 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     if (st + NBUF - 1 < nsteps) stage(st + NBUF - 1, (st + NBUF - 1) % NBUF);
     const char* kt = s_buf[st % NBUF];
     const char* vt = s_buf[st % NBUF] + SH::kKBytes;
-    const uint32_t ent = s_list[st / SPB];
+    const uint32_t ent = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_list[st / SPB]);
     const uint32_t mine = (ent >> (kWaveQ * wave)) & ((1u << kWaveQ) - 1u);
     if (mine == 0u) continue;
     const int jblk = (int)(ent >> 16);
-    const int64_t x0 = step_row0(st);
-    const int64_t xend = (int64_t)(jblk + 1) * LSEL;  // first row past the block
+    const int x0 = jblk * LSEL + (st % SPB) * ROWS;
+    const int xend = (jblk + 1) * LSEL;  // first row past the block
 #pragma unroll
     for (int q = 0; q < kWaveQ; ++q) {
       if (!((mine >> q) & 1u)) continue;
@@ -589,38 +657,40 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
 #pragma unroll
         for (int ks = 0; ks < KT; ++ks) s[m] = mfma_bf16(lds_k<DK>(kt, m, ks, lane), qf[q][ks], s[m]);
       float z[MT][4];
-      float mx = kNegBig;
+      if (x0 + ROWS - 1 <= tq[q] && x0 + ROWS <= xend) {  // wave-uniform: no row masked
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[m][i] = s[m][i];
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int x = x0 + 16 * m + 4 * lg + i;
+            z[m][i] = (x <= tq[q] && x < xend) ? s[m][i] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t x = x0 + 16 * m + 4 * lg + i;
-          z[m][i] = (x <= tq[q] && x < xend) ? s[m][i] * sc : -INFINITY;
-          mx = fmaxf(mx, z[m][i]);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[m][i]);
       mx = max_over_groups_swap(mx);
-      lazy_rescale(mx, mrun[q], lrun[q], acc[q]);
-      float ls = 0.f;
+      lazy_rescale(mx * sc, mref[q], acc[q], lsum[q]);
+      const float nm = -mref[q];
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          z[m][i] = __builtin_amdgcn_exp2f(z[m][i] - mrun[q]);
-          ls += z[m][i];
-        }
-      lrun[q] += ls;
+        for (int i = 0; i < 4; ++i) z[m][i] = __builtin_amdgcn_exp2f(fmaf(z[m][i], sc, nm));
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         uint32_t vr[8][DV / 32];
         lds_v_step<DV>(vt, ks, lg, lr, vr);
         const u32x4_t pk = pack_probs(z[2 * ks], z[2 * ks + 1]);
 #pragma unroll
-        for (int j = 0; j < VC; ++j) {
-          const int wd = j >> 1, h = j & 1;
-          const u32x4_t va = u32x4_t{pack_halves(vr[0][wd], vr[1][wd], h), pack_halves(vr[2][wd], vr[3][wd], h),
-                                     pack_halves(vr[4][wd], vr[5][wd], h), pack_halves(vr[6][wd], vr[7][wd], h)};
-          acc[q][j] = mfma_bf16(va, pk, acc[q][j]);
-        }
+        for (int j = 0; j < VC; ++j) acc[q][j] = mfma_bf16(v_operand<DV>(vr, j), pk, acc[q][j]);
+        lsum[q] = mfma_bf16(ones_a, pk, lsum[q]);
       }
     }
   }
@@ -628,7 +698,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   // ---- out = bf16(acc_in + g_slc * o_slc)
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
-    const float lt = sum_over_groups_swap(lrun[q]);
+    const float lt = __shfl(lsum[q][0], lr);
     if (!act[q] || lr >= p.G) continue;
     const int64_t hrow = ((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr;
     const float f = lt > 0.f ? p.gates[hrow * 3 + 1] / lt : 0.f;
