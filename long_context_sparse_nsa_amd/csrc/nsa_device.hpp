@@ -95,10 +95,26 @@ __device__ __forceinline__ float row_sum_to_last(float v) {
 
 // Wave-wide direct global -> LDS copy of 64 x 16 bytes: lane l reads 16 bytes at
 // `src` (its own address) and LDS receives them at lds_base + 16 * l.  lds_base
-// must be the same for every lane.  Completion is tracked by vmcnt.
+// must be the same for every lane.  Completion is tracked by vmcnt only.
+//
+// Written as inline asm on purpose: the compiler then does not see an LDS store
+// here, so it does not drain every outstanding copy (vmcnt(0)) before each later
+// LDS read or barrier -- which would serialise the copy of the next tiles with
+// the compute on the current one.  The kernels order the copies themselves:
+// wait_vmem_le<N>() for their own copies, then lds_barrier() for everyone's.
+// The instruction has no register results; m0 (the LDS base) needs one wait
+// state after it is written.
 __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
 }
+// Workgroup barrier that is also a compiler memory barrier, without the implied
+// wait for outstanding vector-memory operations of __syncthreads().  LDS
+// operations issued before it by the compiler are complete once their results
+// were consumed; callers wait for their own LDS copies first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Wait until at most N of this wave's vector-memory operations are outstanding
 // (they complete in issue order), leaving the export and LDS counters alone.
 template <int N>

@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     } else {
       wait_vmem_le<0>();
     }
-    __syncthreads();
+    lds_barrier();
     if (c + NBUF - 1 < nch) stage(c + NBUF - 1, (c + NBUF - 1) % NBUF);
     return s_buf[c % NBUF];
   };
@@ -317,6 +317,11 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
       }
   };
 
+  // The query fragments must have arrived before the tile copies are queued: the
+  // compiler does not count those copies, so a wait it placed for the fragments
+  // inside the loop would also drain them.
+  wait_vmem_le<0>();
+  __syncthreads();  // score rows zeroed (each wave reads only its own rows, zeroed by all)
 #pragma unroll
   for (int c0 = 0; c0 < NBUF - 1; ++c0)
     if (c0 < nch) stage(c0, c0);
@@ -630,13 +635,14 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     stage_v<DV, ROWS>(vraw, r0, tlast, s_buf[buf] + SH::kKBytes, wave, lane);
   };
 
+  wait_vmem_le<0>();  // query fragments in (see the compressed-branch kernel)
 #pragma unroll
   for (int s0 = 0; s0 < NBUF - 1; ++s0)
     if (s0 < nsteps) stage(s0, s0);
   for (int st = 0; st < nsteps; ++st) {
     if (st + 1 < nsteps) wait_vmem_le<NLD>();
     else wait_vmem_le<0>();
-    __syncthreads();
+    lds_barrier();
     if (st + NBUF - 1 < nsteps) stage(st + NBUF - 1, (st + NBUF - 1) % NBUF);
     const char* kt = s_buf[st % NBUF];
     const char* vt = s_buf[st % NBUF] + SH::kKBytes;
