@@ -186,6 +186,56 @@ __device__ __forceinline__ void pv_half(const char* vt, int ks, int lg, int lr, 
   }
 }
 
+// The 8 logits of a 32-key half (keys x0 + step rows) with keys outside
+// (lo, hi] replaced by -inf; the test is skipped when the whole half is inside.
+__device__ __forceinline__ void mask_range(const f32x4_t (&sv)[2], int x0, int lo, int hi, int lg,
+                                           float (&z)[2][4]) {
+  if (x0 > lo && x0 + 31 <= hi) {  // wave-uniform
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[mm][i] = sv[mm][i];
+  } else {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int x = x0 + 16 * mm + 4 * lg + i;
+        z[mm][i] = (x > lo && x <= hi) ? sv[mm][i] : -INFINITY;
+      }
+  }
+}
+
+// exp2(z * sc + nm) of a half's 8 logits, packed as the P^T operand.
+__device__ __forceinline__ u32x4_t exp_pack(const float (&z)[2][4], float sc, float nm) {
+  float e[2][4];
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[mm][i] = __builtin_amdgcn_exp2f(fmaf(z[mm][i], sc, nm));
+  return pack_probs(e[0], e[1]);
+}
+
+// lazy_rescale for several positions at once (one wave-uniform branch).
+template <int VC, int NQ>
+__device__ __forceinline__ void lazy_rescale_n(const float (&ms)[NQ], float (&m)[NQ], f32x4_t (&acc)[NQ][VC],
+                                               f32x4_t (&lsum)[NQ]) {
+  bool any = false;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) any = any || (ms[q] > m[q] + kLazy);
+  if (__ballot(any) != 0ull) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const float mn = ms[q] > m[q] + kLazy ? ms[q] : m[q];
+      const float alpha = __builtin_amdgcn_exp2f(m[q] - mn);
+#pragma unroll
+      for (int j = 0; j < VC; ++j) acc[q][j] *= alpha;
+      lsum[q] *= alpha;
+      m[q] = mn;
+    }
+  }
+}
+
 __device__ __forceinline__ int n_visible(int t, int l, int d) { return t + 1 >= l ? (t + 1 - l) / d + 1 : 0; }
 
 __device__ __forceinline__ float max8(const float (&z)[2][4]) {
@@ -327,48 +377,38 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     if (c0 < nch) stage(c0, c0);
   int c = 0;
 
+  // Each chunk is processed as two 32-key halves whose logits are issued
+  // together, so the exponentials of one half can overlap the other half's MFMAs.
+
   // ---- W: window (t - w, t], online softmax into acc
   for (int cw = 0; cw < nW; ++cw, ++c) {
     const char* kt = begin_chunk(c);
     const char* vt = kt + SH::kKBytes;
-#pragma unroll 1
-    for (int hh = 0; hh < 2; ++hh) {  // the chunk's two 32-key halves (kept rolled: register budget)
-      f32x4_t s[kWaveQ][2];
-      logits_half(kt, hh, s);
-      const int x0 = xlo + 64 * cw + 32 * hh;
-      u32x4_t pk[kWaveQ];
+    f32x4_t s0[kWaveQ][2], s1[kWaveQ][2];
+    logits_half(kt, 0, s0);
+    logits_half(kt, 1, s1);
+    const int x0 = xlo + 64 * cw;
+    float z0[kWaveQ][2][4], z1[kWaveQ][2][4], ms[kWaveQ];
 #pragma unroll
-      for (int q = 0; q < kWaveQ; ++q) {
-        // keys x with xlo_q < x <= xhi_q are in the window (none for padding positions)
-        const int xhi = act[q] ? tq[q] : -1, xlo_q = tq[q] - p.w;
-        float z[2][4];
-        if (x0 > xlo_q && x0 + 31 <= xhi) {  // wave-uniform: no key of the half masked
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[mm][i] = s[q][mm][i];
-        } else {
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int x = x0 + 16 * mm + 4 * lg + i;
-              z[mm][i] = (x <= xhi && x > xlo_q) ? s[q][mm][i] : -INFINITY;
-            }
-        }
-        const float mx = max_over_groups_swap(max8(z));
-        lazy_rescale(mx * sc, mref[q], acc[q], lsum[q]);
-        const float nm = -mref[q];
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[mm][i] = __builtin_amdgcn_exp2f(fmaf(z[mm][i], sc, nm));
-        pk[q] = pack_probs(z[0], z[1]);
-      }
-      pv_half<DV>(vt, hh, lg, lr, pk, acc);
-#pragma unroll
-      for (int q = 0; q < kWaveQ; ++q) lsum[q] = mfma_bf16(ones_a, pk[q], lsum[q]);
+    for (int q = 0; q < kWaveQ; ++q) {
+      // keys x with xlo_q < x <= xhi are in the window (none for padding positions)
+      const int xhi = act[q] ? tq[q] : -1, xlo_q = tq[q] - p.w;
+      mask_range(s0[q], x0, xlo_q, xhi, lg, z0[q]);
+      mask_range(s1[q], x0 + 32, xlo_q, xhi, lg, z1[q]);
+      ms[q] = max_over_groups_swap(fmaxf(max8(z0[q]), max8(z1[q]))) * sc;
     }
+    lazy_rescale_n(ms, mref, acc, lsum);
+    u32x4_t pk[kWaveQ];
+#pragma unroll
+    for (int q = 0; q < kWaveQ; ++q) pk[q] = exp_pack(z0[q], sc, -mref[q]);
+    pv_half<DV>(vt, 0, lg, lr, pk, acc);
+#pragma unroll
+    for (int q = 0; q < kWaveQ; ++q) lsum[q] = mfma_bf16(ones_a, pk[q], lsum[q]);
+#pragma unroll
+    for (int q = 0; q < kWaveQ; ++q) pk[q] = exp_pack(z1[q], sc, -mref[q]);
+    pv_half<DV>(vt, 1, lg, lr, pk, acc);
+#pragma unroll
+    for (int q = 0; q < kWaveQ; ++q) lsum[q] = mfma_bf16(ones_a, pk[q], lsum[q]);
   }
   // acc <- g_win * o_win (the denominator of head lr sits in lane lr, element 0)
 #pragma unroll
@@ -388,30 +428,17 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   }
   for (int c1 = 0; c1 < nC; ++c1, ++c) {
     const char* kt = begin_chunk(c);
-#pragma unroll 1
+    f32x4_t s0[kWaveQ][2], s1[kWaveQ][2];
+    logits_half(kt, 0, s0);
+    logits_half(kt, 1, s1);
+#pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      f32x4_t s[kWaveQ][2];
-      logits_half(kt, hh, s);
       const int i0 = 64 * c1 + 32 * hh;
 #pragma unroll
       for (int q = 0; q < kWaveQ; ++q) {
         float z[2][4];
-        if (i0 + 31 < nvq[q]) {  // wave-uniform: every key of the half visible
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[mm][i] = s[q][mm][i];
-        } else {
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = i0 + 16 * mm + 4 * lg + i;
-              z[mm][i] = key < nvq[q] ? s[q][mm][i] : -INFINITY;
-            }
-        }
-        const float mx = max_over_groups_swap(max8(z));
-        const float mn = fmaxf(mref[q], mx * sc);
+        mask_range(hh ? s1[q] : s0[q], i0, -1, nvq[q] - 1, lg, z);
+        const float mn = fmaxf(mref[q], max_over_groups_swap(max8(z)) * sc);
         float ls = 0.f;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
@@ -432,85 +459,82 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     gC[q] = gate(q, 0);
   }
 
-  // ---- C2: normalised p; acc += g_cmp p.Vc; fold p onto selection blocks
+  // ---- C2: normalised p; acc += g_cmp p.Vc; fold p onto selection blocks.
+  // Fold: key i covers stride units [i, i+qd), block j covers [j*rd, (j+1)*rd).
+  // F[head][block] = sum over a 32-key step of p * overlap (the overlap counts are
+  // small integers, exact in bf16; p enters as bf16 hi + lo parts), then summed
+  // over the heads into the position's score row.  The overlap operand depends
+  // on the step only through i0 mod rd, so for rd <= 32 it is built once.
+  auto fold_operand = [&](int i0, int rt) -> u32x4_t {
+    const int jb = i0 / rd;
+    const int ublo = (jb + 16 * rt + lr) * rd, ubhi = ublo + rd;
+    uint32_t ow[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t bits[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int key = i0 + step_key(lg, 2 * h + e);
+        const int ov = min(key + qd, ubhi) - max(key, ublo);
+        bits[e] = __float_as_uint((float)(ov > 0 ? ov : 0)) >> 16;
+      }
+      ow[h] = bits[0] | (bits[1] << 16);
+    }
+    return u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+  };
+  const bool om_const = 32 % rd == 0;
+  const u32x4_t om_c0 = fold_operand(0, 0), om_c1 = fold_operand(0, 1);
   for (int c2 = 0; c2 < nC; ++c2, ++c) {
     const char* kt = begin_chunk(c);
     const char* vt = kt + SH::kKBytes;
-#pragma unroll 1
+    f32x4_t s0[kWaveQ][2], s1[kWaveQ][2];
+    logits_half(kt, 0, s0);
+    logits_half(kt, 1, s1);
+#pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      f32x4_t s[kWaveQ][2];
-      logits_half(kt, hh, s);
       const int i0 = 64 * c2 + 32 * hh;
       u32x4_t pg[kWaveQ], ph[kWaveQ], pl[kWaveQ];
 #pragma unroll
       for (int q = 0; q < kWaveQ; ++q) {
+        float a[2][4];
+        mask_range(hh ? s1[q] : s0[q], i0, -1, nvq[q] - 1, lg, a);
         const float nb = -bias[q];
-        float a[4], bb[4], ga[4], gb[4], ra[4], rb[4];
+        float ga[2][4], ra[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[i] = __builtin_amdgcn_exp2f(fmaf(s[q][0][i], sc, nb));
-          bb[i] = __builtin_amdgcn_exp2f(fmaf(s[q][1][i], sc, nb));
-        }
-        if (i0 + 31 >= nvq[q]) {  // wave-uniform: some key of the half not visible
+        for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = i0 + 4 * lg + i;
-            a[i] = key < nvq[q] ? a[i] : 0.f;
-            bb[i] = key + 16 < nvq[q] ? bb[i] : 0.f;
+            a[mm][i] = __builtin_amdgcn_exp2f(fmaf(a[mm][i], sc, nb));
+            ga[mm][i] = a[mm][i] * gC[q];
           }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ga[i] = a[i] * gC[q];
-          gb[i] = bb[i] * gC[q];
-        }
-        pg[q] = pack_probs(ga, gb);
-        ph[q] = pack_probs(a, bb);
+        pg[q] = pack_probs(ga[0], ga[1]);
+        ph[q] = pack_probs(a[0], a[1]);
         // rounding residual, so that hi + lo carries p to about 16 bits
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t wa = ph[q][i >> 1], wb = ph[q][2 + (i >> 1)];
-          ra[i] = a[i] - ((i & 1) ? bf16_hi(wa) : bf16_lo(wa));
-          rb[i] = bb[i] - ((i & 1) ? bf16_hi(wb) : bf16_lo(wb));
-        }
-        pl[q] = pack_probs(ra, rb);
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w = ph[q][2 * mm + (i >> 1)];
+            ra[mm][i] = a[mm][i] - ((i & 1) ? bf16_hi(w) : bf16_lo(w));
+          }
+        pl[q] = pack_probs(ra[0], ra[1]);
       }
       pv_half<DV>(vt, hh, lg, lr, pg, acc);
-      // fold: key i covers stride units [i, i+qd), block j covers [j*rd, (j+1)*rd);
-      // F^T[block][head] = sum over the step's keys of overlap * p (overlap
-      // counts are small integers, exact in bf16), then summed over the heads
-      // (DPP row sum) into the position's score row.
       const int jb = i0 / rd;
       const int nrows = (i0 - jb * rd + 31 + qd - 1) / rd + 1;  // blocks the step touches (<= 32)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         if (16 * rt >= nrows) break;
-        const int ublo = (jb + 16 * rt + lr) * rd, ubhi = ublo + rd;
-        uint32_t ow[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          uint32_t bits[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int key = i0 + step_key(lg, 2 * h + e);
-            const int ov = min(key + qd, ubhi) - max(key, ublo);
-            bits[e] = __float_as_uint((float)(ov > 0 ? ov : 0)) >> 16;
-          }
-          ow[h] = bits[0] | (bits[1] << 16);
-        }
-        const u32x4_t om = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+        const u32x4_t om = om_const ? (rt ? om_c1 : om_c0) : fold_operand(i0, rt);
+        const int j = jb + 16 * rt + lr;
 #pragma unroll
         for (int q = 0; q < kWaveQ; ++q) {
-          f32x4_t F = mfma_bf16(om, ph[q], f32x4_t{0.f, 0.f, 0.f, 0.f});
-          F = mfma_bf16(om, pl[q], F);
+          // F[head 4lg+i][block lr]: the P operand doubles as the A operand (rows = heads)
+          f32x4_t F = mfma_bf16(ph[q], om, f32x4_t{0.f, 0.f, 0.f, 0.f});
+          F = mfma_bf16(pl[q], om, F);
+          const float v = sum_over_groups_swap((F[0] + F[1]) + (F[2] + F[3]));
           const int Jq = act[q] ? tq[q] / p.lsel : -1;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = row_sum_to_last(F[i]);
-            const int jrel = 16 * rt + 4 * lg + i;
-            const int j = jb + jrel;
-            if (lr == 15 && jrel < nrows && j <= Jq) s_score[kWaveQ * wave + q][j] += v * invq;
-          }
+          if (lg == 0 && 16 * rt + lr < nrows && j <= Jq) s_score[kWaveQ * wave + q][j] += v * invq;
         }
       }
     }
