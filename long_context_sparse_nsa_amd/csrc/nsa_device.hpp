@@ -110,6 +110,18 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
                : "memory", "m0");
 }
+// The same copy with a wave-uniform base address and this lane's 32-bit byte
+// offset (the scalar-base form of the instruction: no per-lane 64-bit address
+// arithmetic).
+__device__ __forceinline__ void copy16_to_lds_sb(const void* base, uint32_t voff, void* lds_base) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(lds)
+               : "memory", "m0");
+}
 // Workgroup barrier that is also a compiler memory barrier, without the implied
 // wait for outstanding vector-memory operations of __syncthreads().  LDS
 // operations issued before it by the compiler are complete once their results

@@ -64,51 +64,70 @@ struct PfShape {
 
 // K tile in fragment order: fragment f = m*KT + ks holds, at 16*lane, the eight
 // dims 32*ks + 8*(lane/16) .. of row 16*m + lane%16 -- the A operand of the S^T
-// MFMA, so a wave reads one contiguous KB per fragment.
-template <int DK, int ROWS = 64>
+// MFMA, so a wave reads one contiguous KB per fragment.  V tile row-major
+// (DV*2 bytes per row), copied in 1 KB pieces.  Wave w copies fragments
+// w, w + kWaves, ... and pieces likewise; their per-lane byte offsets within
+// the tile are fixed, so they are computed once.
+template <int DK, int DV, int ROWS>
+struct StageOffsets {
+  static constexpr int KT = DK / 32, NF = (ROWS / 16) * KT, NI = ROWS * DV * 2 / 1024;
+  static constexpr int FK = (NF + kWaves - 1) / kWaves, FV = (NI + kWaves - 1) / kWaves;
+  uint32_t k, v;  // lane parts of the byte offsets; the fragment/piece parts are uniform
+  __device__ StageOffsets(int lane)
+      : k((uint32_t)(((lane & 15) * DK + 8 * (lane >> 4)) * 2)), v((uint32_t)(lane * 16)) {}
+};
+
+template <int DK, int DV, int ROWS = 64>
 __device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
-                                        int lane) {
-  constexpr int KT = DK / 32, NF = (ROWS / 16) * KT;
-  const bool inside = row0 + ROWS - 1 <= rowmax;
-  const int loff = (lane & 15) * DK + 8 * (lane >> 4);
+                                        int lane, const StageOffsets<DK, DV, ROWS>& so) {
+  using SO = StageOffsets<DK, DV, ROWS>;
+  constexpr int KT = SO::KT, NF = SO::NF;
+  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform: the whole tile lies inside the array
+    const uint16_t* tile = base + row0 * DK;
 #pragma unroll
-  for (int ii = 0; ii < (NF + kWaves - 1) / kWaves; ++ii) {
-    const int f = wave + kWaves * ii;
-    if (NF % kWaves != 0 && f >= NF) break;
-    const int m = f / KT, ks = f - m * KT;
-    const uint16_t* src;
-    if (inside) {
-      src = base + (row0 + 16 * m) * DK + 32 * ks + loff;
-    } else {
+    for (int ii = 0; ii < SO::FK; ++ii) {
+      const int f = wave + kWaves * ii;
+      if (NF % kWaves != 0 && f >= NF) break;
+      const int m = f / KT, ks = f - m * KT;
+      copy16_to_lds_sb(tile + 16 * m * DK + 32 * ks, so.k, dst + f * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < SO::FK; ++ii) {
+      const int f = wave + kWaves * ii;
+      if (NF % kWaves != 0 && f >= NF) break;
+      const int m = f / KT, ks = f - m * KT;
       int64_t row = row0 + 16 * m + (lane & 15);
       row = row < rowmax ? row : rowmax;
-      src = base + row * DK + 32 * ks + 8 * (lane >> 4);
+      copy16_to_lds(base + row * DK + 32 * ks + 8 * (lane >> 4), dst + f * 1024);
     }
-    copy16_to_lds(src, dst + f * 1024);
   }
 }
 
-// V tile row-major (DV*2 bytes per row), copied in 1 KB pieces.
-template <int DV, int ROWS = 64>
+template <int DK, int DV, int ROWS = 64>
 __device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
-                                        int lane) {
-  constexpr int NI = ROWS * DV * 2 / 1024, RB = DV * 2;
-  const bool inside = row0 + ROWS - 1 <= rowmax;
+                                        int lane, const StageOffsets<DK, DV, ROWS>& so) {
+  using SO = StageOffsets<DK, DV, ROWS>;
+  constexpr int NI = SO::NI, RB = DV * 2;
   const char* bb = reinterpret_cast<const char*>(base);
+  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform
+    const char* tile = bb + row0 * RB;
 #pragma unroll
-  for (int ii = 0; ii < (NI + kWaves - 1) / kWaves; ++ii) {
-    const int i = wave + kWaves * ii;
-    if (NI % kWaves != 0 && i >= NI) break;
-    const int off = i * 1024 + lane * 16;
-    const char* src;
-    if (inside) {
-      src = bb + row0 * RB + off;
-    } else {
+    for (int ii = 0; ii < SO::FV; ++ii) {
+      const int i = wave + kWaves * ii;
+      if (NI % kWaves != 0 && i >= NI) break;
+      copy16_to_lds_sb(tile + i * 1024, so.v, dst + i * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < SO::FV; ++ii) {
+      const int i = wave + kWaves * ii;
+      if (NI % kWaves != 0 && i >= NI) break;
+      const int off = i * 1024 + lane * 16;
       int64_t row = row0 + off / RB;
       row = row < rowmax ? row : rowmax;
-      src = bb + row * RB + (off % RB);
+      copy16_to_lds(bb + row * RB + (off % RB), dst + i * 1024);
     }
-    copy16_to_lds(src, dst + i * 1024);
   }
 }
 
@@ -292,19 +311,21 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
 
   for (int e = tid; e < kTileQ * (Jtile + 1); e += kThreads) s_score[e / (Jtile + 1)][e % (Jtile + 1)] = 0.f;
 
+  const StageOffsets<DK, DV, 64> so(lane);
   auto stage = [&](int c, int buf) {
     char* kt = s_buf[buf];
     char* vt = s_buf[buf] + SH::kKBytes;
+    // rows past the tile's needs but inside the arrays are copied and masked
     if (c < nW) {
       const int64_t r0 = xlo + 64 * c;
-      stage_k<DK>(kraw, r0, tlast, kt, wave, lane);
-      stage_v<DV>(vraw, r0, tlast, vt, wave, lane);
+      stage_k<DK, DV>(kraw, r0, T - 1, kt, wave, lane, so);
+      stage_v<DK, DV>(vraw, r0, T - 1, vt, wave, lane, so);
     } else if (c < nW + nC) {
-      stage_k<DK>(kcmp, 64 * (c - nW), ncT - 1, kt, wave, lane);
+      stage_k<DK, DV>(kcmp, 64 * (c - nW), p.nc - 1, kt, wave, lane, so);
     } else {
       const int64_t r0 = 64 * (c - nW - nC);
-      stage_k<DK>(kcmp, r0, ncT - 1, kt, wave, lane);
-      stage_v<DV>(vcmp, r0, ncT - 1, vt, wave, lane);
+      stage_k<DK, DV>(kcmp, r0, p.nc - 1, kt, wave, lane, so);
+      stage_v<DK, DV>(vcmp, r0, p.nc - 1, vt, wave, lane, so);
     }
   };
 
@@ -653,10 +674,11 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     const int u = st / SPB;
     return (int64_t)(s_list[u] >> 16) * LSEL + (int64_t)(st - u * SPB) * ROWS;
   };
+  const StageOffsets<DK, DV, ROWS> so(lane);
   auto stage = [&](int st, int buf) {
     const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane((int)step_row0(st));
-    stage_k<DK, ROWS>(kraw, r0, tlast, s_buf[buf], wave, lane);
-    stage_v<DV, ROWS>(vraw, r0, tlast, s_buf[buf] + SH::kKBytes, wave, lane);
+    stage_k<DK, DV, ROWS>(kraw, r0, T - 1, s_buf[buf], wave, lane, so);
+    stage_v<DK, DV, ROWS>(vraw, r0, T - 1, s_buf[buf] + SH::kKBytes, wave, lane, so);
   };
 
   wait_vmem_le<0>();  // query fragments in (see the compressed-branch kernel)
