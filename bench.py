@@ -102,26 +102,37 @@ def upload_case(case, torch, N):
     return dims, cfg, T, max_len, cuc
 
 
-def decode_bytes(case, sel, cuc_unused=None):
-    """Algorithmic HBM bytes of one decode step: compressed cache, the union of selected
-    and window tokens (each read once), q, gates, out; and the compressed-pass part."""
+def decode_bytes(case, sel):
+    """Algorithmic HBM bytes of one decode step and of its first kernel.
+
+    Step: the compressed cache, the union of selected and window tokens (each
+    read once), q, gates, out.  First kernel (compressed branch + window
+    workgroups): the compressed cache, the window tokens together with the forced
+    blocks' tokens (initial and local blocks, which that kernel also reads), q."""
     wl, p = case.wl, case.p
     row = 2 * (wl.d_k + wl.d_v)
-    cmp_b, sw_b = 0, 0
+    cmp_b, sw_b, wf_b = 0, 0, 0
     for b in range(wl.batch):
         L = int(case.seq_lens[b])
         t = L - 1
+        J = t // p.l_sel
         nc = (L - p.l) // p.d + 1 if L >= p.l else 0
+        forced = set(range(max(0, J - p.n_local + 1), J + 1)) | ({0} if p.force_initial else set())
         for g in range(wl.num_kv_heads):
             cmp_b += nc * row
-            toks = set(range(max(0, t - p.w + 1), t + 1))
+            win = set(range(max(0, t - p.w + 1), t + 1))
+            toks = set(win)
             for j in sel[b, g]:
                 if j >= 0:
                     toks.update(range(j * p.l_sel, min((j + 1) * p.l_sel, L)))
             sw_b += len(toks) * row
+            wf = set(win)
+            for j in forced:
+                wf.update(range(j * p.l_sel, min((j + 1) * p.l_sel, L)))
+            wf_b += len(wf) * row
     io = wl.batch * wl.num_q_heads * (wl.d_k * 2 + 3 * 4 + wl.d_v * 2)
     q_bytes = wl.batch * wl.num_q_heads * wl.d_k * 2
-    return cmp_b + sw_b + io, cmp_b + q_bytes, sw_b
+    return cmp_b + sw_b + io, cmp_b + wf_b + q_bytes, sw_b
 
 
 def bench_decode(args, torch, N, I):
@@ -363,8 +374,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the NSA path here is single-GPU by design "
-              "(DESIGN.md describes how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: this NSA path is single-GPU by design; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -399,7 +410,7 @@ def main():
                    "kv_heads": wl.num_kv_heads, "d_k": wl.d_k, "d_v": wl.d_v, "l": p.l, "d": p.d,
                    "l_sel": p.l_sel, "n_sel": p.n_sel, "w": p.w, "timing": dec["timing"],
                    "cache_copies": args.copies},
-        "roofline": {"bound": "hbm", "kernel": "decode_cmp_kernel (compressed branch + scores + top-n)",
+        "roofline": {"bound": "hbm", "kernel": "decode_cmp_kernel (compressed branch, folded scores, window)",
                      "achieved": dec["pass1_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dec["pass1_gbs"] / HBM_PEAK_GBS, "traffic": roofline_from_profiles(khash),
                      "duration_us": dec["pass1_us"], "algorithmic_bytes": dec["pass1_bytes"]},
@@ -412,8 +423,12 @@ def main():
     }
     if pre:
         line["prefill"] = {"workload": pre["workload"], "ms": pre["ms"], "TFLOP/s": pre["tflops"],
-                           "mfma_frac": pre["mfma_frac"],
-                           "flops": pre["flops"], "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS}
+                           "mfma_frac": pre["mfma_frac"], "flops": pre["flops"],
+                           "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS, "kernel_ms": pre["kernel_ms"],
+                           "selected_branch": {"kernel": "pf_sel_kernel", "TFLOP/s": pre["sel_tflops"],
+                                               "mfma_frac": pre["sel_mfma_frac"]},
+                           "cmp_win_topn": {"kernel": "pf_cmp_win_kernel", "TFLOP/s": pre["cmp_win_tflops"],
+                                            "mfma_frac": pre["cmp_win_tflops"] / MFMA_BF16_PEAK_TFLOPS}}
     print(json.dumps(line), flush=True)
 
 
