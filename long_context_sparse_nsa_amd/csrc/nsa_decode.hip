@@ -7,15 +7,12 @@
 //      cache once, computes the 16-head logits with MFMA, the chunk-local
 //      softmax statistics, the partial output, and the per-head probabilities
 //      folded onto selection blocks;
-//    - window workgroups: everything that does not depend on the selection —
-//      the whole window branch, and the selected branch over the always-taken
-//      blocks (block 0 and the local blocks) — as 32-token steps over the
-//      sorted union of those blocks, so every token is read once and its logit
-//      feeds each branch it belongs to.
+//    - window workgroups: the window branch, which does not depend on the
+//      selection, as 32-token steps over the window's blocks.
 // 2. decode_finish_kernel: several workgroups per (sequence, group), each
 //    computing the exact per-head normalisers from the chunk statistics, the
-//    group scores and the top-n, then attending its share of the routed (not
-//    always-taken) selected blocks.
+//    group scores and the top-n, then attending its share of the selected
+//    blocks (one 32-token step per wave).
 // 3. decode_combine_kernel: per query head, the exact merge of every partial and
 //    out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 //
@@ -144,36 +141,6 @@ __device__ __forceinline__ void step_logits(const Step<DK, DV>& st, const u32x4_
   }
 }
 
-// Sorted union of two ascending block lists (a: n_a entries; b: the range [b0, b1]).
-// Writes at most cap items and a flag per item telling whether it came from list a.
-__device__ __forceinline__ int merge_blocks(const int* a, int n_a, int b0, int b1, int* items, uint8_t* from_a,
-                                            int cap) {
-  int ia = 0, cnt = 0, jb = b0;
-  while (true) {
-    const int sa = ia < n_a ? a[ia] : INT32_MAX;
-    const int sb = jb <= b1 ? jb : INT32_MAX;
-    if (sa == INT32_MAX && sb == INT32_MAX) break;
-    const int j = sa < sb ? sa : sb;
-    if (cnt < cap) {
-      items[cnt] = j;
-      from_a[cnt] = (uint8_t)(sa == j);
-    }
-    ++cnt;
-    if (sa == j) ++ia;
-    if (sb == j) ++jb;
-  }
-  return cnt < cap ? cnt : cap;
-}
-
-// Ascending list of the always-taken blocks at a query in block J.
-__device__ __forceinline__ int forced_list(int J, int nloc, int finit, int* out) {
-  int n = 0;
-  const int lo = J - nloc + 1 > 0 ? J - nloc + 1 : 0;
-  if (finit && lo > 0) out[n++] = 0;
-  for (int j = lo; j <= J; ++j) out[n++] = j;
-  return n;
-}
-
 // Workgroup merge of 4 waves' branch states into one partial
 // (m[16], l[16], o[16][DV]) written to `dst`; `buf`/`st` are LDS scratch.
 template <int DV, int NWV>
@@ -221,28 +188,9 @@ __device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst,
 
 }  // namespace
 
-// The blocks the window workgroup covers: the window blocks [jw0, J] and the
-// always-taken blocks (local blocks [J-nloc+1, J], and block 0) — a contiguous
-// range [lo, J] plus possibly block 0.  Item k of that sorted list:
-struct WindowBlocks {
-  int lo, J, has0, lo_local, finit;
-  __device__ __forceinline__ WindowBlocks(int t, int lsel, int w, int nloc, int fi) {
-    J = t / lsel;
-    const int wlo = t - w + 1 > 0 ? t - w + 1 : 0;
-    lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;
-    lo = min(wlo / lsel, lo_local);
-    finit = fi;
-    has0 = (fi && lo > 0) ? 1 : 0;
-  }
-  __device__ __forceinline__ int count() const { return J - lo + 1 + has0; }
-  __device__ __forceinline__ int block(int k) const { return has0 ? (k == 0 ? 0 : lo + k - 1) : lo + k; }
-  __device__ __forceinline__ bool forced(int j) const { return j >= lo_local || (finit && j == 0); }
-};
-
 // Window workgroup wi of a (sequence, group): one 32-token step per wave over
-// the window blocks and the always-taken blocks (steps wi*4 .. wi*4+3); writes
-// one partial per branch (grp 0: selected branch over the always-taken blocks,
-// grp 1: window).
+// the window's blocks [wlo / l', J] (steps wi*4 .. wi*4+3); writes one partial
+// (m[16], l[16], o[16][DV]) of the window branch.
 template <int DK, int DV, int LSEL>
 __device__ __forceinline__ void window_work(const DecodeParams& p, int b, int g, int bg, int wi, float* smem) {
   constexpr int KT = DK / 32, NWV = kCmpWaves;
@@ -252,49 +200,41 @@ __device__ __forceinline__ void window_work(const DecodeParams& p, int b, int g,
   const int L = seq_len_clamped(p, b);
   const int t = L - 1;
   const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
-  const WindowBlocks wb(t, LSEL, p.w, p.nloc, p.finit);
-  const int nsteps = wb.count() * SPB;
-  Branch<DV> bs, bw;
-  bs.init();
+  const int jw0 = wlo / LSEL, J = t / LSEL;
+  const int nsteps = (J - jw0 + 1) * SPB;
+  Branch<DV> bw;
   bw.init();
   const int si = wi * NWV + wave;
   if (si < nsteps) {
     const int it = si / SPB, half = si - it * SPB;
-    const int jb = wb.block(it);
-    const int64_t xb = (int64_t)jb * LSEL;
+    const int64_t xb = (int64_t)(jw0 + it) * LSEL;
     const int64_t x0 = xb + 32 * half;
     const int64_t nv = min((int64_t)L, xb + LSEL);
-    const bool fr = wb.forced(jb);
     const int64_t row = raw_row0(p, b, g);
     u32x4_t qf[KT];
     load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
     Step<DK, DV> st;
     step_load<DK, DV>(st, p.k + row * DK, p.v + row * DV, x0, nv, lg, lr);
-    if (x0 < nv) {
-      float z[2][4], zs[2][4], zw[2][4];
+    if (x0 < nv && x0 + 31 >= wlo) {
+      float z[2][4];
       step_logits<DK, DV>(st, qf, p.scale_log2, z);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t x = x0 + 16 * tt + 4 * lg + i;
-          const bool valid = x < nv;
-          zs[tt][i] = (valid && fr) ? z[tt][i] : -INFINITY;
-          zw[tt][i] = (valid && x >= wlo) ? z[tt][i] : -INFINITY;
+          if (!(x < nv && x >= wlo)) z[tt][i] = -INFINITY;
         }
-      if (fr) bs.update(zs, st.vr);
-      if (x0 + 31 >= wlo) bw.update(zw, st.vr);
+      bw.update(z, st.vr);
     }
   }
-  float* dst = p.wpart + ((size_t)bg * p.nwin + wi) * 2 * PSTRIDE;
   float* buf = smem;
   float* stt = smem + NWV * 16 * (DV + 1);
-  merge_waves_to<DV, NWV>(bs, dst, buf, stt);
-  merge_waves_to<DV, NWV>(bw, dst + PSTRIDE, buf, stt);
+  merge_waves_to<DV, NWV>(bw, p.wpart + ((size_t)bg * p.nwin + wi) * PSTRIDE, buf, stt);
 }
 
 template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(64 * kCmpWaves, 2) void decode_cmp_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kCmpWaves, 3) void decode_cmp_kernel(DecodeParams p) {
   constexpr int KT = DK / 32, VC = DV / 16, VW = DV / 32;
   constexpr int NWV = kCmpWaves, KPW = kCmpKeysPerWave, NTH = 64 * NWV;
   constexpr int TPW = KPW / 16, SPW = KPW / 32;  // 16-key tiles and 32-key steps per wave
@@ -333,9 +273,6 @@ __global__ __launch_bounds__(64 * kCmpWaves, 2) void decode_cmp_kernel(DecodePar
   u32x4_t kf[TPW][KT];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) load_k_tile<DK>(kc, key0 + 16 * tt + lr, nvis, lg, kf[tt]);
-  uint32_t vr[SPW][8][VW];
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) load_v_step<DV>(vc, key0 + 32 * s, nvis, lg, lr, vr[s]);
 
   float z[TPW][4];
   float mx = -INFINITY;
@@ -370,6 +307,12 @@ __global__ __launch_bounds__(64 * kCmpWaves, 2) void decode_cmp_kernel(DecodePar
   ls = sum_over_groups(ls);
   if (lg == 0) s_red[(NWV + wave) * 16 + lr] = ls;
 
+  // values are loaded after the logits (the key registers are free by then), which
+  // keeps the kernel at three workgroups per CU; the other resident workgroups
+  // cover the latency
+  uint32_t vr[SPW][8][VW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) load_v_step<DV>(vc, key0 + 32 * s, nvis, lg, lr, vr[s]);
   f32x4_t acc[VC];
 #pragma unroll
   for (int j = 0; j < VC; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -418,16 +361,16 @@ __global__ __launch_bounds__(64 * kCmpWaves, 2) void decode_cmp_kernel(DecodePar
   }
 }
 
-// Finish: nfin workgroups of 8 waves per (sequence, group).  Every one of them
+// Finish: nfin workgroups of 4 waves per (sequence, group).  Every one of them
 // computes the exact per-head normalisers of the compressed branch, the group
 // scores and the top-n (identical results, so no exchange is needed); then
-// workgroup k attends the routed steps [8k, 8k+8) of the selected branch (the
-// selected blocks that are not always-taken; one 32-token step per wave) and
-// writes one partial.  Spreading the routed blocks over several workgroups lets
-// their loads use many CUs' memory pipelines instead of one.
+// workgroup k attends the selected steps [4k, 4k+4) (one 32-token step per
+// wave, over all selected blocks in ascending order) and writes one partial.
+// Spreading the selected blocks over many workgroups lets their loads use many
+// CUs' memory pipelines instead of one.
 template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
-  constexpr int NTH = 512, NWV = 8;
+__global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
+  constexpr int NTH = 256, NWV = 4;
   constexpr int KT = DK / 32;
   constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;   // 32-token steps per selection block
   constexpr int PSTRIDE = 32 + 16 * DV;
@@ -437,6 +380,7 @@ __global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
   __shared__ float s_ov[kMaxChunks * 16];          // overhang score slot of each chunk, per head
   __shared__ float s_buf[NWV * 16 * (DV + 1)];
   __shared__ TopnSmem tsm;
+  __shared__ TopnFastSmem<NWV> tfs;
   __shared__ int s_sel[kMaxSel];
   __shared__ int s_items[kMaxSel];
   __shared__ int s_nitems;
@@ -462,10 +406,11 @@ __global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
     const int cc = idx >> 4, h = idx & 15;
     s_ov[idx] = h < p.G ? p.sc1[((cbase + cc) * 16 + h) * slots + nbo] : 0.f;
   }
-  float vv[2][16];
+  constexpr int RPT = 4;  // candidate blocks per thread and load round
+  float vv[RPT][16];
   auto load_scores = [&](int j0) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < RPT; ++r) {
       const int j = j0 + tid + NTH * r;
       const int cc = j / nbo, jj = j - cc * nbo;
       const bool ok = j <= J && cc < nch_b;
@@ -513,10 +458,10 @@ __global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
   __syncthreads();
 
   // ---- group scores of candidate blocks 0..J, top-n
-  for (int j0 = 0; j0 <= J; j0 += NTH * 2) {
+  for (int j0 = 0; j0 <= J; j0 += NTH * RPT) {
     if (j0 > 0) load_scores(j0);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < RPT; ++r) {
       const int j = j0 + tid + NTH * r;
       if (j > J) continue;
       const int cc = j / nbo, jj = j - cc * nbo;
@@ -533,20 +478,18 @@ __global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  block_topn<NTH, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tsm, s_sel,
-                                    (p.sel_out && kfin == 0) ? p.sel_out + (size_t)bg * p.n : nullptr);
+  block_topn_fast<NTH, 8, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel,
+                                            (p.sel_out && kfin == 0) ? p.sel_out + (size_t)bg * p.n : nullptr);
   __syncthreads();
-  if (wave == 0) {  // routed blocks: selected and not always-taken (lane-parallel compaction)
-    const int lo_local = J - p.nloc + 1 > 0 ? J - p.nloc + 1 : 0;
+  if (wave == 0) {  // the selected blocks, ascending (the list ends at the first -1)
     const int j = lane < p.n ? s_sel[lane] : -1;
-    const bool routed = j >= 0 && j < lo_local && !(p.finit && j == 0);
-    const uint64_t m = __ballot(routed);
-    if (routed) s_items[__popcll(m & ((1ull << lane) - 1ull))] = j;
+    const uint64_t m = __ballot(j >= 0);
+    if (j >= 0) s_items[__popcll(m & ((1ull << lane) - 1ull))] = j;
     if (lane == 0) s_nitems = __popcll(m);
   }
   __syncthreads();
 
-  // ---- this workgroup's share of the routed steps: one 32-token step per wave
+  // ---- this workgroup's share of the selected steps: one 32-token step per wave
   Branch<DV> br;
   br.init();
   const int si = kfin * NWV + wave;
@@ -576,7 +519,7 @@ __global__ __launch_bounds__(512) void decode_finish_kernel(DecodeParams p) {
 
 // Combine: one workgroup per query head, one thread per output channel.
 //   o_cmp = sum_c f[c] * O_c (f from the finish kernel: exact normalised factors)
-//   o_slc = exact merge of the always-taken partials and the routed partials
+//   o_slc = exact merge of the finish workgroups' partials
 //   o_win = exact merge of the window partials
 //   out   = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win  (bf16)
 // Every partial up to the launch bounds is loaded in one round (entries beyond
@@ -585,9 +528,8 @@ template <int DV>
 __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
   constexpr int PSTRIDE = 32 + 16 * DV;
   constexpr int kBatch = 16;
-  constexpr int kMaxP = kMaxFinish + kMaxWindow;  // selected-branch partials
   __shared__ float s_f[kMaxChunks];
-  __shared__ float s_pm[kMaxP], s_pl[kMaxP], s_wm[kMaxWindow], s_wl[kMaxWindow];
+  __shared__ float s_pm[kMaxFinish], s_pl[kMaxFinish], s_wm[kMaxWindow], s_wl[kMaxWindow];
   const int qh = blockIdx.x;
   const int b = qh / p.Hq, hq = qh - b * p.Hq;
   const int g = hq / p.G, h = hq - g * p.G;
@@ -595,7 +537,7 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
   const int ch = threadIdx.x;
   const int nch = p.nch, nfin = p.nfin, nwin = p.nwin;
   const size_t cbase = (size_t)bg * nch;
-  const float* wp = p.wpart + (size_t)bg * nwin * 2 * PSTRIDE;
+  const float* wp = p.wpart + (size_t)bg * nwin * PSTRIDE;
   const float* rp = p.rpart + (size_t)bg * nfin * PSTRIDE;
 
   // ---- one round of loads
@@ -606,21 +548,16 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
     s_pl[ch] = rp[(size_t)ch * PSTRIDE + 16 + h];
   } else if (ch >= 32 && ch < 32 + nwin) {
     const int wi = ch - 32;
-    s_pm[kMaxFinish + wi] = wp[(size_t)wi * 2 * PSTRIDE + h];
-    s_pl[kMaxFinish + wi] = wp[(size_t)wi * 2 * PSTRIDE + 16 + h];
-    s_wm[wi] = wp[((size_t)wi * 2 + 1) * PSTRIDE + h];
-    s_wl[wi] = wp[((size_t)wi * 2 + 1) * PSTRIDE + 16 + h];
+    s_wm[wi] = wp[(size_t)wi * PSTRIDE + h];
+    s_wl[wi] = wp[(size_t)wi * PSTRIDE + 16 + h];
   }
-  float vo[kBatch], vr[kMaxFinish], vf[kMaxWindow], vw[kMaxWindow];
+  float vo[kBatch], vr[kMaxFinish], vw[kMaxWindow];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) vo[u] = u < nch ? p.o1[((cbase + u) * 16 + h) * DV + ch] : 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxFinish; ++k) vr[k] = k < nfin ? rp[(size_t)k * PSTRIDE + 32 + h * DV + ch] : 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxWindow; ++k) {
-    vf[k] = k < nwin ? wp[(size_t)k * 2 * PSTRIDE + 32 + h * DV + ch] : 0.f;
-    vw[k] = k < nwin ? wp[((size_t)k * 2 + 1) * PSTRIDE + 32 + h * DV + ch] : 0.f;
-  }
+  for (int k = 0; k < kMaxWindow; ++k) vw[k] = k < nwin ? wp[(size_t)k * PSTRIDE + 32 + h * DV + ch] : 0.f;
   const float* gt = p.gates + (size_t)qh * 3;
   const float g0 = gt[0], g1 = gt[1], g2 = gt[2];
   const int nvis = n_visible(p, b, L);
@@ -638,10 +575,9 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) oc += c0 + u < nch_b ? s_f[c0 + u] * v[u] : 0.f;
   }
-  // ---- selected branch: routed partials (finish) + always-taken partials (window)
+  // ---- selected branch: the finish workgroups' partials
   float M = -INFINITY;
   for (int k = 0; k < nfin; ++k) M = fmaxf(M, s_pm[k]);
-  for (int k = 0; k < nwin; ++k) M = fmaxf(M, s_pm[kMaxFinish + k]);
   float vs = 0.f, ls = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxFinish; ++k) {
@@ -649,14 +585,6 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
       const float a = exp2f(s_pm[k] - M);
       vs += a * vr[k];
       ls += a * s_pl[k];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kMaxWindow; ++k) {
-    if (k < nwin && s_pm[kMaxFinish + k] != -INFINITY) {
-      const float a = exp2f(s_pm[kMaxFinish + k] - M);
-      vs += a * vf[k];
-      ls += a * s_pl[kMaxFinish + k];
     }
   }
   // ---- window branch
@@ -681,6 +609,7 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len) {
+  (void)nloc;  // the always-taken blocks are part of the n selected blocks
   DecodeLayout lay{};
   const int64_t nc = max_len >= l ? (max_len - l) / d + 1 : 0;
   lay.nch = (int)((nc + kChunk - 1) / kChunk);
@@ -692,14 +621,15 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   lay.off_l1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
   lay.off_o1 = off;   off = align256(off + BH * lay.nch * 16 * (size_t)DV * 4);
   lay.off_sc1 = off;  off = align256(off + BH * lay.nch * 16 * (size_t)(lay.nbo + 1) * 4);
-  // window workgroups: one 32-token step per wave over the window blocks and the
-  // always-taken blocks (at most ceil(w/l')+1 window blocks plus n_local+1)
+  // window workgroups: one 32-token step per wave over the window's blocks (at
+  // most ceil(w/l')+1 of them); one partial each
   const int spb = lsel >= 32 ? lsel / 32 : 1;
-  const int wsteps = ((w + lsel - 1) / lsel + 1 + nloc + 1) * spb;
+  const int wsteps = ((w + lsel - 1) / lsel + 1) * spb;
   lay.nwin = (wsteps + kCmpWaves - 1) / kCmpWaves;
-  lay.off_wpart = off; off = align256(off + BH * lay.nwin * 2 * (32 + 16 * (size_t)DV) * 4);
-  // finish workgroups: one partial each; normalised compressed-branch factors
-  lay.nfin = (n * spb + 7) / 8;
+  lay.off_wpart = off; off = align256(off + BH * lay.nwin * (32 + 16 * (size_t)DV) * 4);
+  // finish workgroups (4 waves, one step each): one partial each; normalised
+  // compressed-branch factors
+  lay.nfin = (n * spb + 3) / 4;
   lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
   lay.off_fcmp = off; off = align256(off + BH * lay.nch * 16 * 4);
   lay.total = off;
@@ -720,7 +650,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const Ph
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev->ev[1], s)) != hipSuccess) return e;
-  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(512);
+  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(256);
   switch (p.lsel) {
     case 16: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 16>), g2, blk, 0, s, p); break;
     case 32: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 32>), g2, blk, 0, s, p); break;

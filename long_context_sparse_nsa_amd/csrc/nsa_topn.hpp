@@ -141,6 +141,167 @@ __device__ void block_topn(const float* S, int J, int n, int nloc, int finit, To
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rank-based block top-n (the fast path for up to 8 candidates per thread and
+// nr <= 16 routed picks).  Keys as above (unique, 0 = no candidate).
+//  1. every lane takes the maximum of its keys; the nr-th largest lane maximum
+//     of the wave is a threshold tau: every key among the wave's nr largest is
+//     >= tau (otherwise nr lane maxima would exceed it), and at most K*nr keys
+//     are >= tau (they lie in the <= nr lanes whose maximum is >= tau);
+//  2. the survivors (>= tau) are compacted in LDS and each is ranked by
+//     counting the survivors above it (broadcast LDS reads); ranks < nr are the
+//     wave's winners, stored in rank order;
+//  3. one wave ranks the waves' winners the same way.
+// Every step is exact and deterministic.
+template <int NW>
+struct __attribute__((aligned(16))) TopnFastSmem {
+  __attribute__((aligned(16))) uint64_t lmax[NW][64];
+  __attribute__((aligned(16))) uint64_t surv[NW][144];  // <= 128 survivors, zero padded to a multiple of 16
+  uint64_t best[NW * 16];
+  int fail;
+};
+
+typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
+
+// Number of keys greater than x among v[0 .. 16*nb) (16-byte aligned, padded
+// with zeros, which never count).  Each batch issues eight 16-byte broadcast
+// reads at once, so the LDS latency is paid once per 16 keys.
+__device__ __forceinline__ int count_greater(const uint64_t* v, int nb, uint64_t x) {
+  int c = 0;
+  for (int b = 0; b < nb; ++b) {
+    u64x2_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const u64x2_t*>(v + 16 * b + 2 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c += (a[i].x > x ? 1 : 0) + (a[i].y > x ? 1 : 0);
+  }
+  return c;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Ranks the T (<= 128) keys in surv (zero padded to a multiple of 16) and
+// writes those with rank < nr to dst[rank]; dst[T .. nr) are set to 0.
+__device__ __forceinline__ void rank_into(const uint64_t* surv, int T, int nr, uint64_t* dst) {
+  const int lane = threadIdx.x & 63;
+  const int nb = (T + 15) >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int idx = lane + 64 * s;
+    if (idx < T) {
+      const uint64_t x = surv[idx];
+      const int rk = count_greater(surv, nb, x);
+      if (rk < nr) dst[rk] = x;
+    } else if (idx < nr) {
+      dst[idx] = 0ull;
+    }
+  }
+}
+
+// Zero entries [T, roundup16(T)) of a list of at most 128 keys.
+__device__ __forceinline__ void pad16(uint64_t* v, int T) {
+  const int lane = threadIdx.x & 63;
+  const int end = (T + 15) & ~15;
+  if (T + lane < end) v[T + lane] = 0ull;
+}
+
+// Returns false (for the whole wave) when more than 128 keys survive.
+template <int K>
+__device__ __forceinline__ bool wave_rank_topn(const uint64_t (&k)[K], int nr, uint64_t* lmax, uint64_t* surv,
+                                               uint64_t* dst) {
+  const int lane = threadIdx.x & 63;
+  uint64_t km = k[0];
+#pragma unroll
+  for (int c = 1; c < K; ++c) km = k[c] > km ? k[c] : km;
+  lmax[lane] = km;
+  wave_lds_sync();
+  const int r = count_greater(lmax, 4, km);
+  const uint64_t at = __ballot(km != 0ull && r == nr - 1);
+  uint64_t tau = 0ull;
+  if (at != 0ull) {
+    const int src = __ffsll((unsigned long long)at) - 1;
+    tau = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(km >> 32), src) << 32) |
+          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)km, src);
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    const bool sv = k[c] != 0ull && k[c] >= tau;
+    const uint64_t m = __ballot(sv);
+    const int pos = base + __popcll(m & lt);
+    if (sv && pos < 128) surv[pos] = k[c];
+    base += __popcll(m);
+  }
+  if (base > 128) return false;
+  pad16(surv, base);
+  wave_lds_sync();
+  rank_into(surv, base, nr, dst);
+  wave_lds_sync();
+  return true;
+}
+
+// Block top-n with the rank-based fast path; falls back to block_topn (which
+// reads S again) when a wave has more than 128 survivors, more than K
+// candidates per thread are needed, or nr > 16.
+template <int NT, int K, int MAXC>
+__device__ void block_topn_fast(const float* S, int J, int n, int nloc, int finit, TopnFastSmem<NT / 64>& fs,
+                                TopnSmem& sm, int32_t* out, int32_t* out2) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ncand = J + 1;
+  const int lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;
+  const bool f0 = finit && lo_local > 0;
+  const int nf = (J - lo_local + 1) + (f0 ? 1 : 0);
+  const int nr = n - nf;
+  if (ncand <= n || nr <= 0 || nr > 16 || ncand > NT * K) {
+    block_topn<NT, MAXC>(S, J, n, nloc, finit, sm, out, out2);
+    return;
+  }
+  uint64_t k[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    const int j = tid + NT * c;
+    const bool ok = j < lo_local && !(f0 && j == 0);
+    k[c] = ok ? ((uint64_t)__float_as_uint(S[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j) : 0ull;
+  }
+  if (tid == 0) fs.fail = 0;
+  __syncthreads();
+  const bool ok = wave_rank_topn<K>(k, nr, fs.lmax[wave], fs.surv[wave], fs.best + wave * 16);
+  if (!ok && lane == 0) fs.fail = 1;
+  __syncthreads();
+  if (fs.fail) {
+    __syncthreads();
+    block_topn<NT, MAXC>(S, J, n, nloc, finit, sm, out, out2);
+    return;
+  }
+  if (wave == 0) {
+    // the waves' winners: NW lists of nr (zero padded); rank them together
+    uint64_t* all = fs.surv[0];
+    const int T = NW * nr;
+    for (int i = lane; i < ((T + 15) & ~15); i += 64) all[i] = i < T ? fs.best[(i / nr) * 16 + (i % nr)] : 0ull;
+    wave_lds_sync();
+    rank_into(all, T, nr, fs.best);
+    wave_lds_sync();
+    int v = INT32_MAX;
+    if (lane < nr) v = (int)(0xFFFFFFFFu - (uint32_t)(fs.best[lane] & 0xFFFFFFFFull));
+    if (lane >= nr && lane < n) {
+      const int i = lane - nr;  // forced block i
+      v = f0 ? (i == 0 ? 0 : lo_local + i - 1) : lo_local + i;
+    }
+    int rank = 0;
+    for (int q = 0; q < n; ++q) rank += __builtin_amdgcn_readlane(v, q) < v;
+    if (lane < n) {
+      out[rank] = v;
+      if (out2) out2[rank] = v;
+    }
+  }
+}
+
 // Single-wave variant for one (query, KV group): candidates 0..J with scores
 // S[j] >= 0, at most 64 * MAXC of them.  Writes the n ids ascending to out
 // (-1 fills the tail when fewer than n candidates exist).  No LDS, no barrier.
