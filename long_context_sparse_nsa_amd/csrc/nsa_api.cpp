@@ -88,10 +88,13 @@ nsa_status_t check_decode_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg,
   if (nc > nsa::kMaxCompressed)
     return fail(NSA_ERROR_UNSUPPORTED, "max_seq_len %lld gives more than %d compressed blocks", (long long)max_seq_len,
                 nsa::kMaxCompressed);
-  if ((int64_t)dims->batch * dims->num_kv_heads * ((nc + nsa::kChunk - 1) / nsa::kChunk + 1) > (int64_t)INT32_MAX / 2)
-    return fail(NSA_ERROR_UNSUPPORTED, "launch too large");
   const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
                                                    cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
+  if ((int64_t)dims->batch * dims->num_kv_heads * (lay.nch + lay.nwin + lay.nfin) > (int64_t)INT32_MAX / 2)
+    return fail(NSA_ERROR_UNSUPPORTED, "launch too large");
+  if ((int64_t)lay.nch * lay.seg < nc || lay.nch > nsa::kMaxChunks || lay.nbo + 1 > nsa::kScStrideMax - 3)
+    return fail(NSA_ERROR_UNSUPPORTED, "no segment plan for %lld compressed blocks with l_sel/d=%d", (long long)nc,
+                cfg->l_sel / cfg->d);
   if (lay.nfin > nsa::kMaxFinish)
     return fail(NSA_ERROR_UNSUPPORTED, "n_sel=%d with l_sel=%d needs more than %d selection workgroups", cfg->n_sel,
                 cfg->l_sel, nsa::kMaxFinish);
@@ -277,7 +280,9 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   p.nfin = lay.nfin;
   p.nwin = lay.nwin;
   p.nch = lay.nch;
+  p.seg = lay.seg;
   p.nbo = lay.nbo;
+  p.wtiles = lay.wtiles;
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -1,16 +1,16 @@
 // NSA decode step on gfx950: three launches per step; kernel boundaries are the
 // only cross-workgroup synchronisation (no device-scope fences, no counters).
 //
-// 1. decode_cmp_kernel, two kinds of workgroups in one launch:
-//    - chunk workgroups: the compressed branch, split over chunks of compressed
-//      keys per (sequence, KV group).  Each streams its chunk of the compressed
-//      cache once, computes the 16-head logits with MFMA, the chunk-local
-//      softmax statistics, the partial output, and the per-head probabilities
-//      folded onto selection blocks;
+// 1. decode_stream_kernel, about one workgroup per compute unit, two kinds:
+//    - segment workgroups: the compressed branch, split over segments of
+//      compressed keys per (sequence, KV group).  Each streams its segment of
+//      the compressed cache once into registers, computes the 16-head logits with
+//      MFMA, the segment's softmax statistics and partial output, and the
+//      per-head probabilities folded onto selection blocks;
 //    - window workgroups: the window branch, which does not depend on the
-//      selection, as 32-token steps over the window's blocks.
+//      selection, streamed the same way over the window's raw tokens.
 // 2. decode_finish_kernel: several workgroups per (sequence, group), each
-//    computing the exact per-head normalisers from the chunk statistics, the
+//    computing the exact per-head normalisers from the segment statistics, the
 //    group scores and the top-n, then attending its share of the selected
 //    blocks (one 32-token step per wave).
 // 3. decode_combine_kernel: per query head, the exact merge of every partial and
@@ -68,15 +68,6 @@ __device__ __forceinline__ int n_visible(const DecodeParams& p, int b, int L) {
   const int64_t ccap = p.cuc ? p.cuc[b + 1] - p.cuc[b] : p.ccap;
   return (int)(nv < ccap ? nv : ccap);
 }
-
-// LDS budget of the compressed pass, in floats.
-template <int DV>
-struct K1Smem {
-  static constexpr int kP = 16 * (kChunk + 4);             // probabilities for the fold
-  static constexpr int kAcc = kCmpWaves * 16 * (DV + 1);   // per-wave partial outputs
-  static constexpr int kRed = 2 * kCmpWaves * 16;          // per-wave max / sum
-  static constexpr int kFloats = kP + kAcc + kRed;
-};
 
 // One 32-token step [x0, x0 + 32) of the raw cache for the group's heads.
 template <int DK, int DV>
@@ -188,176 +179,337 @@ __device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst,
 
 }  // namespace
 
-// Window workgroup wi of a (sequence, group): one 32-token step per wave over
-// the window's blocks [wlo / l', J] (steps wi*4 .. wi*4+3); writes one partial
-// (m[16], l[16], o[16][DV]) of the window branch.
-template <int DK, int DV, int LSEL>
-__device__ __forceinline__ void window_work(const DecodeParams& p, int b, int g, int bg, int wi, float* smem) {
-  constexpr int KT = DK / 32, NWV = kCmpWaves;
-  constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;
-  constexpr int PSTRIDE = 32 + 16 * DV;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-  const int L = seq_len_clamped(p, b);
-  const int t = L - 1;
-  const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
-  const int jw0 = wlo / LSEL, J = t / LSEL;
-  const int nsteps = (J - jw0 + 1) * SPB;
-  Branch<DV> bw;
-  bw.init();
-  const int si = wi * NWV + wave;
-  if (si < nsteps) {
-    const int it = si / SPB, half = si - it * SPB;
-    const int64_t xb = (int64_t)(jw0 + it) * LSEL;
-    const int64_t x0 = xb + 32 * half;
-    const int64_t nv = min((int64_t)L, xb + LSEL);
-    const int64_t row = raw_row0(p, b, g);
-    u32x4_t qf[KT];
-    load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
-    Step<DK, DV> st;
-    step_load<DK, DV>(st, p.k + row * DK, p.v + row * DV, x0, nv, lg, lr);
-    if (x0 < nv && x0 + 31 >= wlo) {
-      float z[2][4];
-      step_logits<DK, DV>(st, qf, p.scale_log2, z);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t x = x0 + 16 * tt + 4 * lg + i;
-          if (!(x < nv && x >= wlo)) z[tt][i] = -INFINITY;
-        }
-      bw.update(z, st.vr);
-    }
-  }
-  float* buf = smem;
-  float* stt = smem + NWV * 16 * (DV + 1);
-  merge_waves_to<DV, NWV>(bw, p.wpart + ((size_t)bg * p.nwin + wi) * PSTRIDE, buf, stt);
+// ---------------------------------------------------------------- streaming pass
+
+// Smallest row stride >= n that is 4 mod 16: the four lane groups of a wave then
+// address disjoint LDS banks when they add into four different head rows.
+__host__ __device__ constexpr int score_stride(int n) { return n + ((20 - n % 16) % 16); }
+
+// The 16 rows of a 64-row tile that one wave owns, held in registers in MFMA
+// operand order: K row lr, dims 32*ks + 8*lg .. (A operand of S^T), and V rows
+// 4*lg + e, channels (DV/16)*lr .. (the values its P^T k-slots pair with).
+template <int DK, int DV>
+struct WaveTile {
+  u32x4_t k[DK / 32];
+  uint32_t v[4][DV / 32];
+};
+
+// A wave-uniform pointer moved into scalar registers, so that loads address it
+// as scalar base + 32-bit lane offset + immediate.
+__device__ __forceinline__ const char* scalar_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(64 * kCmpWaves, 3) void decode_cmp_kernel(DecodeParams p) {
-  constexpr int KT = DK / 32, VC = DV / 16, VW = DV / 32;
-  constexpr int NWV = kCmpWaves, KPW = kCmpKeysPerWave, NTH = 64 * NWV;
-  constexpr int TPW = KPW / 16, SPW = KPW / 32;  // 16-key tiles and 32-key steps per wave
-  using SM = K1Smem<DV>;
-  __shared__ float smem[SM::kFloats];
-
-  // workgroups [0, B*H*nwin) are window workgroups (scheduled first), the rest chunks
-  const int nwg_win = p.B * p.H * p.nwin;
-  if ((int)blockIdx.x < nwg_win) {
-    const int bgw = blockIdx.x / p.nwin;
-    window_work<DK, DV, LSEL>(p, bgw / p.H, bgw % p.H, bgw, blockIdx.x - bgw * p.nwin, smem);
-    return;
+// Rows row0 .. row0+15 (row0 wave-uniform); rows past rowmax read row rowmax
+// (their logits are masked by the caller).  koff / voff are the lane's byte
+// offsets within a full tile slice: (lr*DK + 8*lg)*2 and (4*lg*DV + (DV/16)*lr)*2.
+template <int DK, int DV>
+__device__ __forceinline__ void load_wave_tile(WaveTile<DK, DV>& T, const uint16_t* kb, const uint16_t* vb,
+                                               int64_t row0, int64_t rowmax, uint32_t koff, uint32_t voff,
+                                               int lg, int lr) {
+  constexpr int CPL = DV / 16;  // channels per lane and row
+  auto put_v = [&](int e, const char* src) {
+    if constexpr (CPL == 8) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src);
+      T.v[e][0] = x[0]; T.v[e][1] = x[1]; T.v[e][2] = x[2]; T.v[e][3] = x[3];
+    } else {
+      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(src);
+      T.v[e][0] = x[0]; T.v[e][1] = x[1];
+    }
+  };
+  if (row0 + 15 <= rowmax) {  // wave-uniform: all 16 rows exist
+    const char* kp = scalar_ptr(kb + row0 * DK) + koff;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) T.k[ks] = *reinterpret_cast<const u32x4_t*>(kp + 64 * ks);
+    const char* vp = scalar_ptr(vb + row0 * DV) + voff;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) put_v(e, vp + e * DV * 2);
+  } else {
+    const int64_t rk = min(row0 + lr, rowmax);
+    const char* kp = reinterpret_cast<const char*>(kb + rk * DK + 8 * lg);
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) T.k[ks] = *reinterpret_cast<const u32x4_t*>(kp + 64 * ks);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      put_v(e, reinterpret_cast<const char*>(vb + min(row0 + 4 * lg + e, rowmax) * DV + CPL * lr));
   }
-  const int nch = p.nch;
-  const int cid = blockIdx.x - nwg_win;
-  const int c = cid % nch;
-  const int bg = cid / nch;
+}
+
+// Workgroup of the streaming pass: kStreamWaves waves stream the rows of a
+// segment of the compressed cache (or of part of the window of the raw cache)
+// as 64-row tiles; wave w owns rows 16w .. 16w+15 of every tile and loads them
+// straight into registers, kDepth - 1 tiles ahead of the one it computes:
+//   logits  S^T = K . q^T                      (16x16x32 MFMA, d_k/32 k-steps)
+//   values  O^T += V^T . P^T                   (16x16x16 MFMA; P^T is the logit tile)
+//   scores  F^T  = Omega^T . P^T (P as bf16 hi + lo) (16x16x16 MFMA), added into the
+//           per-head score rows of the segment's selection blocks in LDS, in a
+//           fixed order, so repeated calls give identical results
+// Omega[key][block] is the number of stride units key and block share (an exact
+// small integer; divided by l/d when the scores are written out).  The four
+// waves keep one softmax reference per head: each tile's per-wave maxima are
+// exchanged through LDS (the only barrier of a tile), and the reference moves
+// (rescaling the outputs, the sums and the scores) only when a tile maximum
+// exceeds it by kLazy.
+//
+// Outputs per compressed segment: the reference m, the sum l of exp2(z - m), the
+// unnormalised output sum, and the selection-block scores (slot nbo is the
+// overhang into the first block of the next segment).  Per window workgroup:
+// the same (m, l, o) triple over its window tokens.
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(DecodeParams p) {
+  constexpr int NW = kStreamWaves, NTH = 64 * NW, KT = DK / 32, VC = DV / 16;
+#ifndef NSA_STREAM_DEPTH
+#define NSA_STREAM_DEPTH 3
+#endif
+  constexpr int kDepth = NSA_STREAM_DEPTH;  // register tiles per wave (kDepth in flight while one is awaited)
+  constexpr int PSTRIDE = 32 + 16 * DV;
+  constexpr float kLazy = 8.0f, kNegBig = -1e30f;
+  __shared__ float s_sc[16 * kScStrideMax];
+  __shared__ float s_o[NW][16][DV + 1];
+  __shared__ __attribute__((aligned(16))) float s_fw[2][NW][16][16];  // per-wave fold results [head][block row]
+  __shared__ float s_tmax[2][NW][16];
+  __shared__ float s_alpha[16];
+  __shared__ float s_l[NW][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per = p.nch + p.nwin;
+  const int bg = blockIdx.x / per, c = blockIdx.x - bg * per;
   const int g = bg % p.H, b = bg / p.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-
+  const bool fold = c < p.nch;  // workgroup-uniform: compressed segment, else window part
   const int L = seq_len_clamped(p, b);
-  const int nvis = n_visible(p, b, L);  // complete compressed blocks
-  const int nch_b = (nvis + kChunk - 1) / kChunk;
-  if (c >= nch_b) return;  // uniform over the workgroup
+  const int t = L - 1;
 
-  float* s_p = smem;
-  float* s_acc = smem + SM::kP;
-  float* s_red = s_acc + SM::kAcc;  // [0, NWV*16): max; [NWV*16, 2*NWV*16): sum
-  const int64_t crow = cmp_row0(p, b, g);
-  const uint16_t* kc = p.kc + crow * DK;
-  const uint16_t* vc = p.vc + crow * DV;
-  const int key0 = c * kChunk + wave * KPW;
+  // rows [r0, r0 + 64*nt) are streamed; keys outside [vlo, vhi] are masked
+  int64_t r0, rowmax;
+  int nt, vlo, vhi;
+  const uint16_t *kb, *vb;
+  if (fold) {
+    const int nvis = n_visible(p, b, L);
+    const int k0 = c * p.seg;
+    if (k0 >= nvis) return;  // empty segment: never read by the later kernels
+    const int k1 = min(k0 + p.seg, nvis);
+    r0 = k0;
+    nt = (k1 - k0 + 63) >> 6;
+    vlo = k0;
+    vhi = k1 - 1;
+    rowmax = nvis - 1;
+    const int64_t crow = cmp_row0(p, b, g);
+    kb = p.kc + crow * DK;
+    vb = p.vc + crow * DV;
+  } else {
+    const int wi = c - p.nch;
+    const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
+    const int T0 = (wlo >> 6) + wi * p.wtiles, T1 = min((wlo >> 6) + (wi + 1) * p.wtiles, (t >> 6) + 1);
+    r0 = (int64_t)T0 * 64;
+    nt = T1 - T0;
+    vlo = wlo;
+    vhi = t;
+    rowmax = t;
+    const int64_t row = raw_row0(p, b, g);
+    kb = p.k + row * DK;
+    vb = p.v + row * DV;
+    if (nt <= 0) {  // nothing of the window falls to this workgroup: empty partial
+      float* dst = p.wpart + ((size_t)bg * p.nwin + wi) * PSTRIDE;
+      for (int e = tid; e < PSTRIDE; e += NTH) dst[e] = e < 16 ? -INFINITY : 0.f;
+      return;
+    }
+  }
 
+  // Loads never read past the workgroup's own last row: requests for tiles
+  // beyond the range (issued so that every pipeline step has the same loads in
+  // flight) re-read that row from cache.
+  const int64_t rlast = min(rowmax, r0 + 64 * (int64_t)nt - 1);
+
+  // ---- loads first: query fragments, then the first kDepth - 1 tiles
   u32x4_t qf[KT];
   load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
-  u32x4_t kf[TPW][KT];
+  const uint32_t koff = (uint32_t)((lr * DK + 8 * lg) * 2), voff = (uint32_t)((4 * lg * DV + VC * lr) * 2);
+  WaveTile<DK, DV> tb[kDepth];
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) load_k_tile<DK>(kc, key0 + 16 * tt + lr, nvis, lg, kf[tt]);
+  for (int d = 0; d < kDepth - 1; ++d)
+    load_wave_tile<DK, DV>(tb[d], kb, vb, r0 + 64 * d + 16 * wave, rlast, koff, voff, lg, lr);
 
-  float z[TPW][4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const f32x4_t st = qk_tile<DK>(kf[tt], qf);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 16 * tt + 4 * lg + i;
-      const float v = key < nvis ? st[i] * p.scale_log2 : -INFINITY;
-      z[tt][i] = v;
-      mx = fmaxf(mx, v);
-    }
-  }
-  mx = max_over_groups(mx);
-  if (lg == 0) s_red[wave * 16 + lr] = mx;
-  __syncthreads();
-  // chunk max per head; finite because key c*kChunk (wave 0) is visible
-  float m = s_red[lr];
-#pragma unroll
-  for (int w = 1; w < NWV; ++w) m = fmaxf(m, s_red[w * 16 + lr]);
-  float ls = 0.f;
-#pragma unroll
-  for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = exp2f(z[tt][i] - m);
-      z[tt][i] = e;
-      ls += e;
-      s_p[lr * (kChunk + 4) + wave * KPW + 16 * tt + 4 * lg + i] = e;
-    }
-  ls = sum_over_groups(ls);
-  if (lg == 0) s_red[(NWV + wave) * 16 + lr] = ls;
+  const int qd = p.l / p.d, rd = p.lsel / p.d;  // key and block lengths in stride units
+  const int rsh = __builtin_ctz(rd);            // rd is a power of two
+  const int jseg0 = fold ? (int)(r0 >> rsh) : 0;
+  const int sstride = score_stride(p.nbo + 1);
+  if (fold)
+    for (int e = tid; e < 16 * sstride; e += NTH) s_sc[e] = 0.f;
 
-  // values are loaded after the logits (the key registers are free by then), which
-  // keeps the kernel at three workgroups per CU; the other resident workgroups
-  // cover the latency
-  uint32_t vr[SPW][8][VW];
+  // Adds tile i's fold results into the score rows: entry (head h, block j) is
+  // the sum over the waves, in wave order, of the rows their keys give block j
+  // (so the scores do not depend on wave timing).
+  auto fold_flush = [&](int i) {
+    const int kt0 = (int)(r0 + 64 * i);
+    const int jT0 = kt0 >> rsh;
+    const int nr = ((kt0 + 63 + qd - 1) >> rsh) - jT0 + 1;  // blocks the tile's keys touch
+    const float(*fw)[16][16] = s_fw[i & 1];
+    for (int e = tid; e < 16 * nr; e += NTH) {
+      const int h = e & 15, j = jT0 + (e >> 4);
+      float v = 0.f;
 #pragma unroll
-  for (int s = 0; s < SPW; ++s) load_v_step<DV>(vc, key0 + 32 * s, nvis, lg, lr, vr[s]);
+      for (int w = 0; w < NW; ++w) {
+        const int kw = kt0 + 16 * w, j0w = kw >> rsh;
+        const int nrw = ((kw + 15 + qd - 1) >> rsh) - j0w + 1;
+        const int row = j - j0w;
+        if (row >= 0 && row < nrw) v += fw[w][h][row];
+      }
+      s_sc[h * sstride + (j - jseg0)] += v;
+    }
+  };
+
   f32x4_t acc[VC];
 #pragma unroll
   for (int j = 0; j < VC; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f, mref = kNegBig;
+  const float sc = p.scale_log2;
+
+  auto process = [&](int i, const WaveTile<DK, DV>& T) {
+    const int64_t k0 = r0 + 64 * i + 16 * wave;  // the wave's first row
+    // ---- logits of the wave's 16 rows; element e is row k0 + 4lg + e, head lr
+    f32x4_t sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < SPW; ++s) pv_step<DV>(vr[s], pack_probs(z[2 * s], z[2 * s + 1]), acc);
+    for (int ks = 0; ks < KT; ++ks) sv = mfma_bf16(T.k[ks], qf[ks], sv);
+    float z[4];
+    if (k0 >= vlo && k0 + 15 <= vhi) {  // wave-uniform
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = sv[e] * sc;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t x = k0 + 4 * lg + e;
+        z[e] = (x >= vlo && x <= vhi) ? sv[e] * sc : -INFINITY;
+      }
+    }
+    float mw = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mw = max_over_groups_swap(mw);
+    if (lg == 0) s_tmax[i & 1][wave][lr] = mw;
+    lds_barrier();  // the tile's maxima, and the previous tile's fold results, are complete
+    if (fold && i > 0) fold_flush(i - 1);
+    float mt = s_tmax[i & 1][0][lr];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mt = fmaxf(mt, s_tmax[i & 1][w][lr]);
+
+    // ---- lazy reference move (identical decision in every wave)
+    const bool move = mt > mref + kLazy;
+    if (__ballot(move) != 0ull) {
+      const float mn = move ? mt : mref;
+      const float alpha = __builtin_amdgcn_exp2f(mref - mn);
+#pragma unroll
+      for (int j = 0; j < VC; ++j) acc[j] *= alpha;
+      lsum *= alpha;
+      mref = mn;
+      if (fold && i > 0) {
+        if (wave == 0 && lg == 0) s_alpha[lr] = alpha;
+        lds_barrier();  // also orders every thread's flush before the scaling
+        for (int e = tid; e < 16 * sstride; e += NTH) s_sc[e] *= s_alpha[e / sstride];
+        lds_barrier();
+      }
+    }
+
+    // ---- probabilities, values
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(z[e] - mref);
+    lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const u32x2_t ph = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+#pragma unroll
+    for (int j = 0; j < VC; ++j) {
+      const int wd = j >> 1, h = j & 1;
+      const u32x2_t va = {pack_halves(T.v[0][wd], T.v[1][wd], h), pack_halves(T.v[2][wd], T.v[3][wd], h)};
+      acc[j] = mfma16_bf16(va, ph, acc[j]);
+    }
+
+    // ---- fold onto selection blocks: rows of Omega^T are blocks j0 + lr
+    if (fold) {
+      const int phi = (int)k0 & (rd - 1);  // offset of the first key in its block
+      float ov[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int u0 = phi + 4 * lg + e;  // key's first unit, relative to block j0
+        const int o = min(u0 + qd, (lr + 1) * rd) - max(u0, lr * rd);
+        ov[e] = (float)(o > 0 ? o : 0);
+      }
+      const u32x2_t om = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+      float lo[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        lo[2 * e] = pr[2 * e] - bf16_lo(ph[e]);
+        lo[2 * e + 1] = pr[2 * e + 1] - bf16_hi(ph[e]);
+      }
+      const u32x2_t pl = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+      f32x4_t f = mfma16_bf16(om, ph, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      f = mfma16_bf16(om, pl, f);
+      // element e: block j0 + 4lg + e, head lr
+      *reinterpret_cast<f32x4_t*>(&s_fw[i & 1][wave][lr][4 * lg]) = f;
+    }
+  };
+
+  // ---- the pipeline: tile i+kDepth-1 is requested before tile i is computed.
+  // Every step of the main loop issues the same loads, so the compiler's wait
+  // before a tile's first use leaves the later tiles in flight; the last
+  // (nt mod kDepth) tiles were requested by the main loop and need no loads.
+  int i0 = 0;
+  for (; i0 + kDepth <= nt; i0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      load_wave_tile<DK, DV>(tb[(u + kDepth - 1) % kDepth], kb, vb, r0 + 64 * (i0 + u + kDepth - 1) + 16 * wave,
+                             rlast, koff, voff, lg, lr);
+      process(i0 + u, tb[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kDepth - 1; ++u)
+    if (i0 + u < nt) process(i0 + u, tb[u]);  // workgroup-uniform
+
+  // ---- workgroup merge: all waves share mref, so outputs and sums just add
+  lsum = sum_over_groups_swap(lsum);
+  if (lg == 0) s_l[wave][lr] = lsum;
 #pragma unroll
   for (int j = 0; j < VC; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = acc[j][i];
-  __syncthreads();
-
-  // chunk partial output [16][DV] (sum over the waves, same reference max)
-  float* O = p.o1 + ((size_t)bg * nch + c) * 16 * DV;
-  for (int e = tid; e < 16 * DV; e += NTH) {
-    const int h = e / DV, ch = e - h * DV;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) v += s_acc[(w * 16 + h) * (DV + 1) + ch];
-    O[e] = v;
+    for (int e = 0; e < 4; ++e) s_o[wave][lr][acc_channel<DV>(lg, e, j)] = acc[j][e];
+  lds_barrier();
+  if (fold) {
+    fold_flush(nt - 1);
+    lds_barrier();
   }
-  if (tid < 16) {
-    float lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) lsum += s_red[(NWV + w) * 16 + tid];
-    p.m1[((size_t)bg * nch + c) * 16 + tid] = m;
-    p.l1[((size_t)bg * nch + c) * 16 + tid] = lsum;
+  float *dm, *dl, *dox;
+  if (fold) {
+    const size_t slot = (size_t)bg * p.nch + c;
+    dm = p.m1 + slot * 16;
+    dl = p.l1 + slot * 16;
+    dox = p.o1 + slot * 16 * DV;
+  } else {
+    float* dst = p.wpart + ((size_t)bg * p.nwin + (c - p.nch)) * PSTRIDE;
+    dm = dst;
+    dl = dst + 16;
+    dox = dst + 32;
   }
-  // per-head scores of the selection blocks this chunk touches, in units of the
-  // stride d (d divides l and l'): key i covers units [i, i+q), block j covers
-  // [j*r, (j+1)*r) with q = l/d, r = l'/d, and the overlap share is (units)/q.
-  // Slot jj is block jb0 + jj; slot nbo receives the overhang of the last keys.
-  const int nbo = p.nbo, slots = nbo + 1;
-  const int q = p.l / p.d, r = p.lsel / p.d;
-  const int jb0 = c * kChunk / r;
-  const int kc0 = c * kChunk, kc1 = min(kc0 + kChunk, nvis);
-  float* SC = p.sc1 + ((size_t)bg * nch + c) * 16 * slots;
-  const float inv_q = 1.0f / (float)q;
-  for (int e = tid; e < 16 * slots; e += NTH) {
-    const int h = e / slots, jj = e - h * slots;
-    const int lo = (jb0 + jj) * r, hi = lo + r;      // block j in units
-    const int ilo = max(kc0, lo - q + 1), ihi = min(kc1 - 1, hi - 1);
-    const float* ps = s_p + h * (kChunk + 4) - kc0;
-    float sacc = 0.f;
-    for (int i = ilo; i <= ihi; ++i) sacc += (float)(min(i + q, hi) - max(i, lo)) * ps[i];
-    SC[e] = sacc * inv_q;
+  for (int h = wave; h < 16; h += NW)
+    for (int ch = lane; ch < DV; ch += 64) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += s_o[w][h][ch];
+      dox[h * DV + ch] = v;
+    }
+  if (tid < 16) {  // lane tid holds head tid's reference
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ls += s_l[w][tid];
+    dl[tid] = ls;
+    dm[tid] = mref;
+  }
+  if (fold) {
+    const int slots = p.nbo + 1;
+    const float invq = 1.0f / (float)qd;
+    float* SC = p.sc1 + ((size_t)bg * p.nch + c) * 16 * slots;
+    for (int h = wave; h < 16; h += NW)
+      for (int jj = lane; jj < slots; jj += 64) SC[h * slots + jj] = s_sc[h * sstride + jj] * invq;
   }
 }
 
@@ -391,7 +543,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
   const int nch = p.nch;
   const int L = seq_len_clamped(p, b);
   const int nvis = n_visible(p, b, L);
-  const int nch_b = (nvis + kChunk - 1) / kChunk;
+  const int nch_b = (nvis + p.seg - 1) / p.seg;
   const int t = L - 1;
   const int J = t / LSEL;
   const size_t cbase = (size_t)bg * nch;
@@ -561,7 +713,7 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
   const float* gt = p.gates + (size_t)qh * 3;
   const float g0 = gt[0], g1 = gt[1], g2 = gt[2];
   const int nvis = n_visible(p, b, L);
-  const int nch_b = (nvis + kChunk - 1) / kChunk;
+  const int nch_b = (nvis + p.seg - 1) / p.seg;
   __syncthreads();
 
   // ---- compressed branch
@@ -612,23 +764,39 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   (void)nloc;  // the always-taken blocks are part of the n selected blocks
   DecodeLayout lay{};
   const int64_t nc = max_len >= l ? (max_len - l) / d + 1 : 0;
-  lay.nch = (int)((nc + kChunk - 1) / kChunk);
+  const int r = lsel / d;
+  const int64_t gran = r > 64 ? r : 64;  // segments hold whole tiles and whole selection blocks
+  auto up = [&](int64_t x) { return (x + gran - 1) / gran * gran; };
+  // Rows per (sequence, group): the compressed keys plus the window's tiles,
+  // spread over about kStreamSlots / (B*H) workgroups (at least one segment and
+  // one window workgroup).
+  const int64_t win_tiles = (w + 63) / 64 + 1;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t per_bg = bh >= kStreamSlots / 2 ? 2 : kStreamSlots / bh;
+  int64_t seg = up((nc + 64 * win_tiles + per_bg - 1) / per_bg);
+  const int64_t seg_min = up((nc + kMaxChunks - 1) / kMaxChunks);
+  const int64_t seg_max = (int64_t)(kScStrideMax - 4) * r / gran * gran;  // score rows fit the LDS table
+  if (seg < seg_min) seg = seg_min;
+  if (seg > seg_max) seg = seg_max;  // the host rejects seg_min > seg_max
+  if (seg < gran) seg = gran;
+  lay.seg = (int)seg;
+  lay.nch = (int)((nc + seg - 1) / seg);
   if (lay.nch < 1) lay.nch = 1;
-  lay.nbo = (int)((int64_t)kChunk * d / lsel);
+  lay.nbo = (int)(seg / r);
+  int64_t wt = seg / 64;
+  if (wt * kMaxWindow < win_tiles) wt = (win_tiles + kMaxWindow - 1) / kMaxWindow;
+  lay.wtiles = (int)wt;
+  lay.nwin = (int)((win_tiles + wt - 1) / wt);
   const size_t BH = (size_t)B * H;
   size_t off = 0;
   lay.off_m1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
   lay.off_l1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
   lay.off_o1 = off;   off = align256(off + BH * lay.nch * 16 * (size_t)DV * 4);
   lay.off_sc1 = off;  off = align256(off + BH * lay.nch * 16 * (size_t)(lay.nbo + 1) * 4);
-  // window workgroups: one 32-token step per wave over the window's blocks (at
-  // most ceil(w/l')+1 of them); one partial each
-  const int spb = lsel >= 32 ? lsel / 32 : 1;
-  const int wsteps = ((w + lsel - 1) / lsel + 1) * spb;
-  lay.nwin = (wsteps + kCmpWaves - 1) / kCmpWaves;
   lay.off_wpart = off; off = align256(off + BH * lay.nwin * (32 + 16 * (size_t)DV) * 4);
-  // finish workgroups (4 waves, one step each): one partial each; normalised
-  // compressed-branch factors
+  // finish workgroups (4 waves, one 32-token step each): one partial each;
+  // normalised compressed-branch factors
+  const int spb = lsel >= 32 ? lsel / 32 : 1;
   lay.nfin = (n * spb + 3) / 4;
   lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
   lay.off_fcmp = off; off = align256(off + BH * lay.nch * 16 * 4);
@@ -640,14 +808,8 @@ template <int DK, int DV>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const PhaseEvents* ev) {
   hipError_t e;
   if (ev && (e = hipEventRecord(ev->ev[0], s)) != hipSuccess) return e;
-  const dim3 g1((unsigned)(p.B * p.H * (p.nch + p.nwin))), b1(64 * kCmpWaves);
-  switch (p.lsel) {
-    case 16: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 16>), g1, b1, 0, s, p); break;
-    case 32: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 32>), g1, b1, 0, s, p); break;
-    case 64: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 64>), g1, b1, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((decode_cmp_kernel<DK, DV, 128>), g1, b1, 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((decode_stream_kernel<DK, DV>), dim3((unsigned)(p.B * p.H * (p.nch + p.nwin))),
+                     dim3(64 * kStreamWaves), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev->ev[1], s)) != hipSuccess) return e;
   const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(256);

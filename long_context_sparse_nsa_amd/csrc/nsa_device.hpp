@@ -26,6 +26,16 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b,
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef short bf16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+
+// v_mfma_f32_16x16x16_bf16: A row lr / B column lr hold k-slots 4*lg .. 4*lg+3
+// (two packed dwords); D as above.  Its B layout is the D layout of the 16x16x32
+// product, so a logit tile feeds it directly.
+__device__ __forceinline__ f32x4_t mfma16_bf16(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                   __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

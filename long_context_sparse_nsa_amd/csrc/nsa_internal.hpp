@@ -7,20 +7,16 @@
 
 namespace nsa {
 
-// Shape of the decode compressed-branch pass: each workgroup streams one chunk
-// of kCmpWaves * kCmpKeysPerWave compressed keys.
-#ifndef NSA_CMP_KPW
-#define NSA_CMP_KPW 64
-#endif
-#ifndef NSA_CMP_NWV
-#define NSA_CMP_NWV 4
-#endif
-constexpr int kCmpKeysPerWave = NSA_CMP_KPW;
-constexpr int kCmpWaves = NSA_CMP_NWV;
-constexpr int kChunk = kCmpKeysPerWave * kCmpWaves;
+// Decode streaming pass: workgroups of kStreamWaves waves stream 64-row tiles
+// of one segment of the compressed cache (or of the window); the segment
+// length is chosen so that one launch has about kStreamSlots workgroups (one
+// per compute unit of an MI355X).
+constexpr int kStreamWaves = 4;
+constexpr int kStreamSlots = 256;
+constexpr int kScStrideMax = 548;     // LDS score row stride limit (floats): selection blocks per segment + 1
 // Limits of the on-chip tables (checked by the host before any launch).
 constexpr int kMaxCompressed = 32768;                 // compressed blocks per sequence in decode
-constexpr int kMaxChunks = kMaxCompressed / kChunk;   // chunks per sequence in decode
+constexpr int kMaxChunks = 128;                       // compressed segments per sequence in decode
 constexpr int kMaxBlocks = 8192;     // selection candidates J+1
 constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query
@@ -51,18 +47,20 @@ struct DecodeParams {
   float* l1;                         // [B*H, nch, 16]
   float* o1;                         // [B*H, nch, 16, DV]
   float* sc1;                        // [B*H, nch, 16, nbo+1]
-  float* wpart;                      // [B*H, nwin, 2, 32 + 16*DV] window-workgroup partials
+  float* wpart;                      // [B*H, nwin, 32 + 16*DV] window-workgroup partials
   float* rpart;                      // [B*H, nfin, 32 + 16*DV] routed-block partials
   float* fcmp;                       // [B*H, nch, 16] normalised compressed-branch factors
-  int nch;                           // chunk workgroups per (sequence, group)
-  int nbo;                           // selection blocks owned by one chunk = kChunk*d/lsel
+  int nch;                           // compressed segments per (sequence, group)
+  int seg;                           // compressed keys per segment (multiple of 64 and of lsel/d)
+  int nbo;                           // selection blocks owned by one segment = seg*d/lsel
+  int wtiles;                        // 64-token window tiles per window workgroup
   int nfin;                          // finish workgroups per (sequence, group)
   int nwin;                          // window workgroups per (sequence, group)
 };
 
 struct DecodeLayout {
   size_t off_m1, off_l1, off_o1, off_sc1, off_wpart, off_rpart, off_fcmp, total;
-  int nch, nbo, nfin, nwin;
+  int nch, seg, nbo, nfin, nwin, wtiles;
 };
 
 // Parameters of the prefill kernels and the compression kernel.

@@ -29,6 +29,7 @@
 
 #include "nsa_device.hpp"
 #include "nsa_internal.hpp"
+#include "nsa_stage.hpp"
 #include "nsa_tiles.hpp"
 #include "nsa_topn.hpp"
 
@@ -43,11 +44,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1e30f;        // running-reference start: finite, so exp2 never sees inf - inf
 constexpr float kLazy = 8.0f;            // the softmax reference moves only when exceeded by this (log2 units)
 
-// Copy instructions every wave issues for a ROWS-row K (+ V) tile (a lower bound:
-// waiting until at most this many are outstanding covers every earlier copy).
-template <int DK, int DV, int ROWS, bool WITH_V>
-constexpr int kLdMin = ((ROWS / 16) * (DK / 32)) / kWaves + (WITH_V ? (ROWS * DV * 2 / 1024) / kWaves : 0);
-
 template <int DK, int DV>
 struct PfShape {
   static constexpr int KT = DK / 32;           // MFMA k-steps of a logit tile
@@ -56,112 +52,6 @@ struct PfShape {
   static constexpr int kVBytes = 64 * DV * 2;  // 64-key V tile, row-major
   static constexpr int kBuf = kKBytes + kVBytes;
 };
-
-// ---- staging of ROWS rows [row0, row0+ROWS) of a row-major bf16 array; rows
-// past rowmax are replaced by row rowmax (the caller masks their logits).  The
-// kWaves waves share the copy (wave is wave-uniform); each issues at least
-// kLdMin copy instructions.
-
-// K tile in fragment order: fragment f = m*KT + ks holds, at 16*lane, the eight
-// dims 32*ks + 8*(lane/16) .. of row 16*m + lane%16 -- the A operand of the S^T
-// MFMA, so a wave reads one contiguous KB per fragment.  V tile row-major
-// (DV*2 bytes per row), copied in 1 KB pieces.  Wave w copies fragments
-// w, w + kWaves, ... and pieces likewise; their per-lane byte offsets within
-// the tile are fixed, so they are computed once.
-template <int DK, int DV, int ROWS>
-struct StageOffsets {
-  static constexpr int KT = DK / 32, NF = (ROWS / 16) * KT, NI = ROWS * DV * 2 / 1024;
-  static constexpr int FK = (NF + kWaves - 1) / kWaves, FV = (NI + kWaves - 1) / kWaves;
-  uint32_t k, v;  // lane parts of the byte offsets; the fragment/piece parts are uniform
-  __device__ StageOffsets(int lane)
-      : k((uint32_t)(((lane & 15) * DK + 8 * (lane >> 4)) * 2)), v((uint32_t)(lane * 16)) {}
-};
-
-template <int DK, int DV, int ROWS = 64>
-__device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
-                                        int lane, const StageOffsets<DK, DV, ROWS>& so) {
-  using SO = StageOffsets<DK, DV, ROWS>;
-  constexpr int KT = SO::KT, NF = SO::NF;
-  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform: the whole tile lies inside the array
-    const uint16_t* tile = base + row0 * DK;
-#pragma unroll
-    for (int ii = 0; ii < SO::FK; ++ii) {
-      const int f = wave + kWaves * ii;
-      if (NF % kWaves != 0 && f >= NF) break;
-      const int m = f / KT, ks = f - m * KT;
-      copy16_to_lds_sb(tile + 16 * m * DK + 32 * ks, so.k, dst + f * 1024);
-    }
-  } else {
-#pragma unroll
-    for (int ii = 0; ii < SO::FK; ++ii) {
-      const int f = wave + kWaves * ii;
-      if (NF % kWaves != 0 && f >= NF) break;
-      const int m = f / KT, ks = f - m * KT;
-      int64_t row = row0 + 16 * m + (lane & 15);
-      row = row < rowmax ? row : rowmax;
-      copy16_to_lds(base + row * DK + 32 * ks + 8 * (lane >> 4), dst + f * 1024);
-    }
-  }
-}
-
-template <int DK, int DV, int ROWS = 64>
-__device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
-                                        int lane, const StageOffsets<DK, DV, ROWS>& so) {
-  using SO = StageOffsets<DK, DV, ROWS>;
-  constexpr int NI = SO::NI, RB = DV * 2;
-  const char* bb = reinterpret_cast<const char*>(base);
-  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform
-    const char* tile = bb + row0 * RB;
-#pragma unroll
-    for (int ii = 0; ii < SO::FV; ++ii) {
-      const int i = wave + kWaves * ii;
-      if (NI % kWaves != 0 && i >= NI) break;
-      copy16_to_lds_sb(tile + i * 1024, so.v, dst + i * 1024);
-    }
-  } else {
-#pragma unroll
-    for (int ii = 0; ii < SO::FV; ++ii) {
-      const int i = wave + kWaves * ii;
-      if (NI % kWaves != 0 && i >= NI) break;
-      const int off = i * 1024 + lane * 16;
-      int64_t row = row0 + off / RB;
-      row = row < rowmax ? row : rowmax;
-      copy16_to_lds(bb + row * RB + (off % RB), dst + i * 1024);
-    }
-  }
-}
-
-// ---- LDS operand reads
-
-template <int DK>
-__device__ __forceinline__ u32x4_t lds_k(const char* kt, int m, int ks, int lane) {
-  return *reinterpret_cast<const u32x4_t*>(kt + ((m * (DK / 32) + ks) * 64 + lane) * 16);
-}
-
-// The eight V rows of 32-key step ks that pair with this lane's P^T k-slots,
-// channels (DV/16)*lr .. of each.
-template <int DV>
-__device__ __forceinline__ void lds_v_step(const char* vt, int ks, int lg, int lr, uint32_t (&vr)[8][DV / 32]) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const char* src = vt + (32 * ks + step_key(lg, r)) * (DV * 2) + (DV / 16) * lr * 2;
-    if constexpr (DV / 32 == 4) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src);
-      vr[r][0] = x[0]; vr[r][1] = x[1]; vr[r][2] = x[2]; vr[r][3] = x[3];
-    } else {
-      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(src);
-      vr[r][0] = x[0]; vr[r][1] = x[1];
-    }
-  }
-}
-
-// V^T operand j of a step (channels (DV/16)*m + j), from the rows read above.
-template <int DV>
-__device__ __forceinline__ u32x4_t v_operand(const uint32_t (&vr)[8][DV / 32], int j) {
-  const int wd = j >> 1, h = j & 1;
-  return u32x4_t{pack_halves(vr[0][wd], vr[1][wd], h), pack_halves(vr[2][wd], vr[3][wd], h),
-                 pack_halves(vr[4][wd], vr[5][wd], h), pack_halves(vr[6][wd], vr[7][wd], h)};
-}
 
 // A operand with row 0 all ones (bf16 1.0) and zeros elsewhere: MFMA'd with a
 // P^T operand it adds, in row 0 (lane lr = head, element 0), the step's sum of
@@ -285,7 +175,8 @@ template <int DK, int DV, int NBUF, int MAXB>
 __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p) {
   using SH = PfShape<DK, DV>;
   constexpr int KT = SH::KT, VC = SH::VC;
-  constexpr int NLD_K = kLdMin<DK, DV, 64, false>, NLD_KV = kLdMin<DK, DV, 64, true>;
+  using SO = StageOffsets<DK, DV, 64, kWaves>;
+  constexpr int NLD_K = SO::kMinCopiesK, NLD_KV = SO::kMinCopiesKV;
   __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
   __shared__ float s_score[kTileQ][MAXB];
 
@@ -311,21 +202,21 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
 
   for (int e = tid; e < kTileQ * (Jtile + 1); e += kThreads) s_score[e / (Jtile + 1)][e % (Jtile + 1)] = 0.f;
 
-  const StageOffsets<DK, DV, 64> so(lane);
+  const SO so(lane);
   auto stage = [&](int c, int buf) {
     char* kt = s_buf[buf];
     char* vt = s_buf[buf] + SH::kKBytes;
     // rows past the tile's needs but inside the arrays are copied and masked
     if (c < nW) {
       const int64_t r0 = xlo + 64 * c;
-      stage_k<DK, DV>(kraw, r0, T - 1, kt, wave, lane, so);
-      stage_v<DK, DV>(vraw, r0, T - 1, vt, wave, lane, so);
+      stage_k(kraw, r0, T - 1, kt, wave, lane, so);
+      stage_v(vraw, r0, T - 1, vt, wave, lane, so);
     } else if (c < nW + nC) {
-      stage_k<DK, DV>(kcmp, 64 * (c - nW), p.nc - 1, kt, wave, lane, so);
+      stage_k(kcmp, 64 * (c - nW), p.nc - 1, kt, wave, lane, so);
     } else {
       const int64_t r0 = 64 * (c - nW - nC);
-      stage_k<DK, DV>(kcmp, r0, p.nc - 1, kt, wave, lane, so);
-      stage_v<DK, DV>(vcmp, r0, p.nc - 1, vt, wave, lane, so);
+      stage_k(kcmp, r0, p.nc - 1, kt, wave, lane, so);
+      stage_v(vcmp, r0, p.nc - 1, vt, wave, lane, so);
     }
   };
 
@@ -601,7 +492,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > 64 ? 64 : LSEL);
   constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
   constexpr int NBUF = 3;                    // two steps in flight
-  constexpr int NLD = kLdMin<DK, DV, ROWS, true>;
+  using SO = StageOffsets<DK, DV, ROWS, kWaves>;
+  constexpr int NLD = SO::kMinCopiesKV;
   __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
   __shared__ uint32_t s_mask[kPfMaxBlocks];  // per block: bit q set if position t0+q chose it
   __shared__ uint32_t s_list[kPfMaxBlocks];  // the union, ascending: block id << 16 | mask
@@ -674,11 +566,11 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     const int u = st / SPB;
     return (int64_t)(s_list[u] >> 16) * LSEL + (int64_t)(st - u * SPB) * ROWS;
   };
-  const StageOffsets<DK, DV, ROWS> so(lane);
+  const SO so(lane);
   auto stage = [&](int st, int buf) {
     const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane((int)step_row0(st));
-    stage_k<DK, DV, ROWS>(kraw, r0, T - 1, s_buf[buf], wave, lane, so);
-    stage_v<DK, DV, ROWS>(vraw, r0, T - 1, s_buf[buf] + SH::kKBytes, wave, lane, so);
+    stage_k(kraw, r0, T - 1, s_buf[buf], wave, lane, so);
+    stage_v(vraw, r0, T - 1, s_buf[buf] + SH::kKBytes, wave, lane, so);
   };
 
   wait_vmem_le<0>();  // query fragments in (see the compressed-branch kernel)
