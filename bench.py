@@ -218,10 +218,10 @@ def bench_decode(args, torch, N, I):
         step(i)
     N.nsa_set_phase_events(None)
     torch.cuda.synchronize()
-    ph = [float(np.mean([hev.ms(4 * i + k, 4 * i + k + 1) for i in range(n_ph)])) for k in range(3)]
+    ph = [float(np.mean([hev.ms(4 * i + k, 4 * i + k + 1) for i in range(n_ph)])) for k in range(2)]
     hev.close()
     p1 = ph[0]
-    p2 = ph[1] + ph[2]
+    p2 = ph[1]
     sel_h = sel.cpu().numpy()
     b_step, b_cmp, b_sw = decode_bytes(case, sel_h)
     gbs_step = b_step / (ms_step * 1e-3) / 1e9
@@ -231,13 +231,13 @@ def bench_decode(args, torch, N, I):
         tokens_per_s=wl.batch / (ms_step * 1e-3),
         step_bytes=b_step, step_gbs=gbs_step, step_frac=gbs_step / HBM_PEAK_GBS,
         pass1_us=p1 * 1e3, pass2_us=p2 * 1e3, pass1_bytes=b_cmp, pass2_bytes=b_sw,
-        finish_us=ph[1] * 1e3, combine_us=ph[2] * 1e3,
+        finish_us=ph[1] * 1e3,
 
         pass1_gbs=gbs_cmp, pass2_gbs=b_sw / (p2 * 1e-3) / 1e9,
     )
     log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step ({timing}), {res['tokens_per_s']:.4g} tok/s, "
-        f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: cmp {p1 * 1e3:.1f} us "
-        f"({gbs_cmp:.0f} GB/s), finish {ph[1] * 1e3:.1f} us, combine {ph[2] * 1e3:.1f} us")
+        f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: stream {p1 * 1e3:.1f} us "
+        f"({gbs_cmp:.0f} GB/s), finish {ph[1] * 1e3:.1f} us")
     return case, res, T
 
 
@@ -410,14 +410,13 @@ def main():
                    "kv_heads": wl.num_kv_heads, "d_k": wl.d_k, "d_v": wl.d_v, "l": p.l, "d": p.d,
                    "l_sel": p.l_sel, "n_sel": p.n_sel, "w": p.w, "timing": dec["timing"],
                    "cache_copies": args.copies},
-        "roofline": {"bound": "hbm", "kernel": "decode_cmp_kernel (compressed branch, folded scores, window)",
+        "roofline": {"bound": "hbm", "kernel": "decode_stream_kernel (compressed branch, folded scores, window)",
                      "achieved": dec["pass1_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dec["pass1_gbs"] / HBM_PEAK_GBS, "traffic": roofline_from_profiles(khash),
                      "duration_us": dec["pass1_us"], "algorithmic_bytes": dec["pass1_bytes"]},
         "decode_step": {"algorithmic_bytes": dec["step_bytes"], "GB/s": dec["step_gbs"],
                         "hbm_frac": dec["step_frac"],
-                        "kernel_us": {"decode_cmp_kernel": dec["pass1_us"], "decode_finish_kernel": dec["finish_us"],
-                                      "decode_combine_kernel": dec["combine_us"]},
+                        "kernel_us": {"decode_stream_kernel": dec["pass1_us"], "decode_finish_kernel": dec["finish_us"]},
                         "wall_s_timed_region": dec["wall_s"]},
         "cpu_baseline": cpu,
     }

@@ -276,7 +276,8 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   p.sc1 = reinterpret_cast<float*>(ws + lay.off_sc1);
   p.wpart = reinterpret_cast<float*>(ws + lay.off_wpart);
   p.rpart = reinterpret_cast<float*>(ws + lay.off_rpart);
-  p.fcmp = reinterpret_cast<float*>(ws + lay.off_fcmp);
+  p.ocmp = reinterpret_cast<float*>(ws + lay.off_ocmp);
+  p.cnt = reinterpret_cast<uint32_t*>(ws + lay.off_cnt);
   p.nfin = lay.nfin;
   p.nwin = lay.nwin;
   p.nch = lay.nch;

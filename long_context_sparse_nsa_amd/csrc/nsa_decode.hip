@@ -1,5 +1,6 @@
-// NSA decode step on gfx950: three launches per step; kernel boundaries are the
-// only cross-workgroup synchronisation (no device-scope fences, no counters).
+// NSA decode step on gfx950: two launches per step.  Between them the kernel
+// boundary is the synchronisation; inside the second, one device-scope counter
+// per (sequence, group) finds the workgroup that finishes last.
 //
 // 1. decode_stream_kernel, about one workgroup per compute unit, two kinds:
 //    - segment workgroups: the compressed branch, split over segments of
@@ -11,9 +12,9 @@
 //      selection, streamed the same way over the window's raw tokens.
 // 2. decode_finish_kernel: several workgroups per (sequence, group), each
 //    computing the exact per-head normalisers from the segment statistics, the
-//    group scores and the top-n, then attending its share of the selected
-//    blocks (one 32-token step per wave).
-// 3. decode_combine_kernel: per query head, the exact merge of every partial and
+//    group scores and the top-n, a slice of the compressed-branch output, and
+//    its share of the selected blocks (one 32-token step per wave); the last
+//    of them to finish merges the partials and applies the gates:
 //    out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 //
 // Sources: lesson 5.5/02 "Разреженное внимание — NSA и DSA" (ai.flicky.cc),
@@ -67,6 +68,20 @@ __device__ __forceinline__ int n_visible(const DecodeParams& p, int b, int L) {
   int64_t nv = L >= p.l ? (L - p.l) / p.d + 1 : 0;
   const int64_t ccap = p.cuc ? p.cuc[b + 1] - p.cuc[b] : p.ccap;
   return (int)(nv < ccap ? nv : ccap);
+}
+
+// Stores and loads that are coherent across the whole device without cache
+// maintenance (relaxed atomics at agent scope): the finish workgroups of one
+// (sequence, group) hand their partials to the last of them this way.
+__device__ __forceinline__ void st_shared_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_shared_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2_t ld2_shared_dev(const float* p) {  // p 8-byte aligned
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x2_t{__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32))};
 }
 
 // One 32-token step [x0, x0 + 32) of the raw cache for the group's heads.
@@ -134,15 +149,19 @@ __device__ __forceinline__ void step_logits(const Step<DK, DV>& st, const u32x4_
 
 // Workgroup merge of 4 waves' branch states into one partial
 // (m[16], l[16], o[16][DV]) written to `dst`; `buf`/`st` are LDS scratch.
-template <int DV, int NWV>
+template <int DV, int NWV, bool DEV_SHARED = false>
 __device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst, float* buf, float* st) {
+  auto put = [&](float* q, float v) {
+    if constexpr (DEV_SHARED) st_shared_dev(q, v);
+    else *q = v;
+  };
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   constexpr int NTH = 64 * NWV;
   if (lg == 0) {
     st[wave * 16 + lr] = br.m;
     st[(NWV + wave) * 16 + lr] = br.l;
   }
-  __syncthreads();
+  lds_barrier();
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < NWV; ++w) M = fmaxf(M, st[w * 16 + lr]);
@@ -151,13 +170,13 @@ __device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst,
   for (int j = 0; j < DV / 16; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) buf[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = alpha * br.acc[j][i];
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < 16 * DV; e += NTH) {
     const int h = e / DV, ch = e - h * DV;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) v += buf[(w * 16 + h) * (DV + 1) + ch];
-    dst[32 + e] = v;
+    put(dst + 32 + e, v);
   }
   if (tid < 16) {
     float Mh = -INFINITY;
@@ -169,10 +188,10 @@ __device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst,
       const float mw = st[w * 16 + tid];
       if (mw != -INFINITY) ls += exp2f(mw - Mh) * st[(NWV + w) * 16 + tid];
     }
-    dst[tid] = Mh;
-    dst[16 + tid] = ls;
+    put(dst + tid, Mh);
+    put(dst + 16 + tid, ls);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 
@@ -302,6 +321,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     vb = p.vc + crow * DV;
   } else {
     const int wi = c - p.nch;
+    if (wi == 0 && tid == 0) p.cnt[bg] = 0u;  // arrival counter of the finish workgroups
     const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
     const int T0 = (wlo >> 6) + wi * p.wtiles, T1 = min((wlo >> 6) + (wi + 1) * p.wtiles, (t >> 6) + 1);
     r0 = (int64_t)T0 * 64;
@@ -507,107 +527,145 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   if (fold) {
     const int slots = p.nbo + 1;
     const float invq = 1.0f / (float)qd;
-    float* SC = p.sc1 + ((size_t)bg * p.nch + c) * 16 * slots;
-    for (int h = wave; h < 16; h += NW)
-      for (int jj = lane; jj < slots; jj += 64) SC[h * slots + jj] = s_sc[h * sstride + jj] * invq;
+    float* SC = p.sc1 + ((size_t)bg * p.nch + c) * slots * 16;  // [slot][head]
+    for (int e = tid; e < 16 * slots; e += NTH) SC[e] = s_sc[(e & 15) * sstride + (e >> 4)] * invq;
   }
 }
 
 // Finish: nfin workgroups of 4 waves per (sequence, group).  Every one of them
 // computes the exact per-head normalisers of the compressed branch, the group
 // scores and the top-n (identical results, so no exchange is needed); then
-// workgroup k attends the selected steps [4k, 4k+4) (one 32-token step per
-// wave, over all selected blocks in ascending order) and writes one partial.
-// Spreading the selected blocks over many workgroups lets their loads use many
-// CUs' memory pipelines instead of one.
+// workgroup k
+//   - sums its slice of the normalised compressed-branch output over the
+//     segments (the loads are issued before the normalisers are known),
+//   - attends the selected steps [4k, 4k+4) (one 32-token step per wave, over
+//     all selected blocks in ascending order) and writes one partial.
+// The last of the nfin workgroups to finish (a device-scope counter, cleared
+// by the streaming pass) merges the selected-branch partials and the window
+// partials and writes out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 template <int DK, int DV, int LSEL>
 __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
   constexpr int NTH = 256, NWV = 4;
   constexpr int KT = DK / 32;
   constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;   // 32-token steps per selection block
   constexpr int PSTRIDE = 32 + 16 * DV;
+  constexpr int RPT = 4;                             // candidate blocks per thread and load round
+  constexpr int OB = 8;                              // segments per compressed-output load batch
   __shared__ float S[kMaxBlocks];
-  __shared__ float f[kMaxChunks * 16];
-  __shared__ float s_stat[2 * kMaxChunks * 16];    // chunk m / l staging, then wave merge scratch
-  __shared__ float s_ov[kMaxChunks * 16];          // overhang score slot of each chunk, per head
+  __shared__ float s_f[kMaxChunks * 16];
+  __shared__ float s_ml[2 * kMaxChunks * 16];       // segment m / l, then wave-merge scratch
+  __shared__ float s_ov[kMaxChunks * 16];           // overhang score slot of each segment, per head
   __shared__ float s_buf[NWV * 16 * (DV + 1)];
   __shared__ TopnSmem tsm;
   __shared__ TopnFastSmem<NWV> tfs;
   __shared__ int s_sel[kMaxSel];
   __shared__ int s_items[kMaxSel];
   __shared__ int s_nitems;
+  __shared__ int s_last;
+  __shared__ float s_pf[kMaxFinish][16], s_wf[kMaxWindow][16];
+  __shared__ float s_gate[16][3];
 
-  const int bg = blockIdx.x / p.nfin, kfin = blockIdx.x - bg * p.nfin;
+  // Workgroups are dealt to the 8 XCDs round-robin by id; when the sizes allow,
+  // the nfin workgroups of one (sequence, group) get ids on the same XCD, so the
+  // partials they hand over stay in that XCD's L2.  Only speed depends on this.
+  int bg, kfin;
+  if (p.nfin == 8 && (p.B * p.H) % 8 == 0) {
+    const int w = blockIdx.x, xcd = w & 7, r = w >> 3;
+    bg = xcd + 8 * (r >> 3);
+    kfin = r & 7;
+  } else {
+    bg = blockIdx.x / p.nfin;
+    kfin = blockIdx.x - bg * p.nfin;
+  }
   const int g = bg % p.H, b = bg / p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-  const int nch = p.nch;
-  const int L = seq_len_clamped(p, b);
-  const int nvis = n_visible(p, b, L);
-  const int nch_b = (nvis + p.seg - 1) / p.seg;
-  const int t = L - 1;
-  const int J = t / LSEL;
+  const int nch = p.nch, nbo = p.nbo, slots = nbo + 1;
   const size_t cbase = (size_t)bg * nch;
-  float* s_m = s_stat;
-  float* s_l = s_stat + kMaxChunks * 16;
+  float* s_m = s_ml;
+  float* s_l = s_ml + kMaxChunks * 16;
 
-  // ---- one round of independent loads: chunk statistics, overhang slots, scores
-  const int nbo = p.nbo, slots = nbo + 1;
-  for (int idx = tid; idx < nch_b * 16; idx += NTH) {
-    s_m[idx] = p.m1[cbase * 16 + idx];
-    s_l[idx] = p.l1[cbase * 16 + idx];
-    const int cc = idx >> 4, h = idx & 15;
-    s_ov[idx] = h < p.G ? p.sc1[((cbase + cc) * 16 + h) * slots + nbo] : 0.f;
+  // ---- one round of loads (all issued before any is waited for): the sequence
+  // length, segment statistics and overhang slots of the first 16 segment slots,
+  // the first round of candidate scores ([segment][slot][16 heads]), this
+  // workgroup's first batch of compressed-branch outputs, the query fragments
+  const int L = seq_len_clamped(p, b);
+  float pm = 0.f, pl = 0.f, pov = 0.f;
+  if (tid < nch * 16) {
+    pm = p.m1[cbase * 16 + tid];
+    pl = p.l1[cbase * 16 + tid];
+    pov = p.sc1[((cbase + (tid >> 4)) * slots + nbo) * 16 + (tid & 15)];
   }
-  constexpr int RPT = 4;  // candidate blocks per thread and load round
-  float vv[RPT][16];
+  f32x4_t vv[RPT][4];
   auto load_scores = [&](int j0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const int j = j0 + tid + NTH * r;
-      const int cc = j / nbo, jj = j - cc * nbo;
-      const bool ok = j <= J && cc < nch_b;
-      const float* SC = p.sc1 + (cbase + (ok ? cc : 0)) * 16 * slots + jj;
+      int cc = j / nbo, jj = j - cc * nbo;
+      if (cc >= nch) cc = nch - 1, jj = 0;  // beyond every sequence: read in bounds, discarded
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.sc1 + ((cbase + cc) * slots + jj) * 16);
 #pragma unroll
-      for (int h = 0; h < 16; ++h) vv[r][h] = (ok && h < p.G) ? SC[h * slots] : 0.f;
+      for (int u = 0; u < 4; ++u) vv[r][u] = src[u];
     }
   };
   load_scores(0);
-  __syncthreads();
-  // ---- exact per-head normalisers: thread (c, h) = (tid / 16, tid % 16), passes of
-  // 32 chunks; reductions over c by shuffles in a wave and through LDS across waves
+  // compressed-branch output slice of this workgroup: outputs [e0, e1) of the
+  // group's 16 x DV, one per thread and pass
+  const int per = (16 * DV + p.nfin - 1) / p.nfin;
+  const int e0 = kfin * per, e1 = min(e0 + per, 16 * DV);
+  float vo[OB];
   {
-    float* red = s_buf;  // [wave][16] scratch
-    const int h = tid & 15, cw = tid >> 4;
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < nch_b; c0 += NTH / 16) {
-      const int c = c0 + cw;
-      float m = c < nch_b ? s_m[c * 16 + h] : -INFINITY;
-      m = max_over_groups(m);
-      if (lg == 0) red[wave * 16 + h] = m;
-      __syncthreads();
+    const int e = e0 + tid;
+    const int ee = e < e1 ? e : e0;
 #pragma unroll
-      for (int w = 0; w < NWV; ++w) M = fmaxf(M, red[w * 16 + h]);
-      __syncthreads();
-    }
-    float Ls = 0.f;
-    for (int c0 = 0; c0 < nch_b; c0 += NTH / 16) {
-      const int c = c0 + cw;
-      float e = c < nch_b ? s_l[c * 16 + h] * exp2f(s_m[c * 16 + h] - M) : 0.f;
-      e = sum_over_groups(e);
-      if (lg == 0) red[wave * 16 + h] = e;
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < NWV; ++w) Ls += red[w * 16 + h];
-      __syncthreads();
-    }
-    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
-    for (int c = cw; c < nch_b; c += NTH / 16) {
-      const float fc = h < p.G ? exp2f(s_m[c * 16 + h] - M) * inv : 0.f;
-      f[c * 16 + h] = fc;
-      if (kfin == 0) p.fcmp[(cbase + c) * 16 + h] = fc;  // for the combine kernel
-    }
+    for (int u = 0; u < OB; ++u) vo[u] = p.o1[(cbase + min(u, nch - 1)) * 16 * DV + ee];
   }
-  __syncthreads();
+  u32x4_t qf[KT];
+  load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
+  const float gv = tid < 3 * p.G ? p.gates[((size_t)b * p.Hq + (size_t)g * p.G) * 3 + tid] : 0.f;
+  if (tid < 3 * p.G) s_gate[tid / 3][tid % 3] = gv;
+  if (tid < nch * 16) {
+    s_m[tid] = pm;
+    s_l[tid] = pl;
+    s_ov[tid] = pov;
+  }
+  for (int idx = tid + NTH; idx < nch * 16; idx += NTH) {  // more than 16 segments
+    s_m[idx] = p.m1[cbase * 16 + idx];
+    s_l[idx] = p.l1[cbase * 16 + idx];
+    s_ov[idx] = p.sc1[((cbase + (idx >> 4)) * slots + nbo) * 16 + (idx & 15)];
+  }
+  const int nvis = n_visible(p, b, L);
+  const int nch_b = (nvis + p.seg - 1) / p.seg;
+  const int t = L - 1;
+  const int J = t / LSEL;
+  lds_barrier();
+
+  // ---- exact per-head normalisers (wave 0: lane = head + 16 * segment phase)
+  if (wave == 0) {
+    const int h = lr;
+    float M = -INFINITY;
+    for (int c = lg; c < nch_b; c += 4) M = fmaxf(M, s_m[c * 16 + h]);
+    M = max_over_groups_swap(M);
+    float Ls = 0.f;
+    for (int c = lg; c < nch_b; c += 4) Ls += s_l[c * 16 + h] * __builtin_amdgcn_exp2f(s_m[c * 16 + h] - M);
+    Ls = sum_over_groups_swap(Ls);
+    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
+    for (int c = lg; c < nch_b; c += 4) s_f[c * 16 + h] = h < p.G ? __builtin_amdgcn_exp2f(s_m[c * 16 + h] - M) * inv : 0.f;
+  }
+  lds_barrier();
+
+  // ---- this workgroup's slice of the compressed-branch output
+  for (int e = e0 + tid; e < e1; e += NTH) {
+    const int h = e / DV;
+    float oc = 0.f;
+    if (e == e0 + tid) {
+#pragma unroll
+      for (int u = 0; u < OB; ++u) oc += u < nch_b ? s_f[u * 16 + h] * vo[u] : 0.f;
+    } else {
+      for (int c = 0; c < min(nch_b, OB); ++c) oc += s_f[c * 16 + h] * p.o1[(cbase + c) * 16 * DV + e];
+    }
+    for (int c = OB; c < nch_b; ++c) oc += s_f[c * 16 + h] * p.o1[(cbase + c) * 16 * DV + e];
+    st_shared_dev(p.ocmp + (size_t)bg * 16 * DV + e, oc);
+  }
 
   // ---- group scores of candidate blocks 0..J, top-n
   for (int j0 = 0; j0 <= J; j0 += NTH * RPT) {
@@ -620,26 +678,28 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
       float sc = 0.f;
       if (cc < nch_b) {
 #pragma unroll
-        for (int h = 0; h < 16; ++h) sc += f[cc * 16 + h] * vv[r][h];
-      }
-      if (jj == 0 && cc >= 1 && cc - 1 < nch_b) {  // overhang of the previous chunk
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int h = 0; h < 16; ++h) sc += f[(cc - 1) * 16 + h] * s_ov[(cc - 1) * 16 + h];
+          for (int e = 0; e < 4; ++e) sc += s_f[cc * 16 + 4 * u + e] * vv[r][u][e];
+      }
+      if (jj == 0 && cc >= 1 && cc - 1 < nch_b) {  // overhang of the previous segment
+#pragma unroll
+        for (int h = 0; h < 16; ++h) sc += s_f[(cc - 1) * 16 + h] * s_ov[(cc - 1) * 16 + h];
       }
       S[j] = sc;
     }
   }
-  __syncthreads();
+  lds_barrier();
   block_topn_fast<NTH, 8, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel,
                                             (p.sel_out && kfin == 0) ? p.sel_out + (size_t)bg * p.n : nullptr);
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {  // the selected blocks, ascending (the list ends at the first -1)
     const int j = lane < p.n ? s_sel[lane] : -1;
     const uint64_t m = __ballot(j >= 0);
     if (j >= 0) s_items[__popcll(m & ((1ull << lane) - 1ull))] = j;
     if (lane == 0) s_nitems = __popcll(m);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- this workgroup's share of the selected steps: one 32-token step per wave
   Branch<DV> br;
@@ -651,8 +711,6 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
     const int64_t x0 = xb + 32 * half;
     const int64_t nv = min((int64_t)L, xb + LSEL);
     const int64_t row = raw_row0(p, b, g);
-    u32x4_t qf[KT];
-    load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
     Step<DK, DV> st;
     step_load<DK, DV>(st, p.k + row * DK, p.v + row * DV, x0, nv, lg, lr);
     if (x0 < nv) {
@@ -666,94 +724,115 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
       br.update(z, st.vr);
     }
   }
-  merge_waves_to<DV, NWV>(br, p.rpart + ((size_t)bg * p.nfin + kfin) * PSTRIDE, s_buf, s_stat);
-}
+  float* rp = p.rpart + (size_t)bg * p.nfin * PSTRIDE;
+  merge_waves_to<DV, NWV, true>(br, rp + (size_t)kfin * PSTRIDE, s_buf, s_ml);
 
-// Combine: one workgroup per query head, one thread per output channel.
-//   o_cmp = sum_c f[c] * O_c (f from the finish kernel: exact normalised factors)
-//   o_slc = exact merge of the finish workgroups' partials
-//   o_win = exact merge of the window partials
-//   out   = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win  (bf16)
-// Every partial up to the launch bounds is loaded in one round (entries beyond
-// the sequence's own count are discarded by selects, never multiplied in).
-template <int DV>
-__global__ __launch_bounds__(DV) void decode_combine_kernel(DecodeParams p) {
-  constexpr int PSTRIDE = 32 + 16 * DV;
-  constexpr int kBatch = 16;
-  __shared__ float s_f[kMaxChunks];
-  __shared__ float s_pm[kMaxFinish], s_pl[kMaxFinish], s_wm[kMaxWindow], s_wl[kMaxWindow];
-  const int qh = blockIdx.x;
-  const int b = qh / p.Hq, hq = qh - b * p.Hq;
-  const int g = hq / p.G, h = hq - g * p.G;
-  const int bg = b * p.H + g;
-  const int ch = threadIdx.x;
-  const int nch = p.nch, nfin = p.nfin, nwin = p.nwin;
-  const size_t cbase = (size_t)bg * nch;
-  const float* wp = p.wpart + (size_t)bg * nwin * PSTRIDE;
-  const float* rp = p.rpart + (size_t)bg * nfin * PSTRIDE;
-
-  // ---- one round of loads
-  const int L = seq_len_clamped(p, b);
-  for (int c = ch; c < nch; c += DV) s_f[c] = p.fcmp[(cbase + c) * 16 + h];
-  if (ch < nfin) {
-    s_pm[ch] = rp[(size_t)ch * PSTRIDE + h];
-    s_pl[ch] = rp[(size_t)ch * PSTRIDE + 16 + h];
-  } else if (ch >= 32 && ch < 32 + nwin) {
-    const int wi = ch - 32;
-    s_wm[wi] = wp[(size_t)wi * PSTRIDE + h];
-    s_wl[wi] = wp[(size_t)wi * PSTRIDE + 16 + h];
-  }
-  float vo[kBatch], vr[kMaxFinish], vw[kMaxWindow];
+  // ---- the last workgroup of this (sequence, group) applies the gates.  The
+  // partial and the output slice were stored coherently; once every thread's
+  // stores have completed, the counter is incremented, and the workgroup that
+  // sees the final count reads the others' results with coherent loads.
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(p.cnt + bg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(p.nfin - 1);
+  lds_barrier();
+  if (!s_last) return;
+  const float* wp = p.wpart + (size_t)bg * p.nwin * PSTRIDE;
+  const float* oc_src = p.ocmp + (size_t)bg * 16 * DV;
+  constexpr int FF = 8, FW = 2, NP = 16 * DV / 2 / NTH;  // fast-path partial counts; output pairs per thread
+  const bool fast = p.nfin <= FF && p.nwin <= FW;        // workgroup-uniform
+  f32x2_t ro[NP][FF], rw[NP][FW], rc[NP];
+  float fm[FF], fl[FF], wm[FW], wl[FW];
+  if (fast) {  // every load of the merge in flight at once
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) vo[u] = u < nch ? p.o1[((cbase + u) * 16 + h) * DV + ch] : 0.f;
+    for (int u = 0; u < NP; ++u) {
+      const int e2 = 2 * (tid + NTH * u);
+      rc[u] = ld2_shared_dev(oc_src + e2);
 #pragma unroll
-  for (int k = 0; k < kMaxFinish; ++k) vr[k] = k < nfin ? rp[(size_t)k * PSTRIDE + 32 + h * DV + ch] : 0.f;
+      for (int k = 0; k < FF; ++k) ro[u][k] = k < p.nfin ? ld2_shared_dev(rp + (size_t)k * PSTRIDE + 32 + e2) : f32x2_t{0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < kMaxWindow; ++k) vw[k] = k < nwin ? wp[(size_t)k * PSTRIDE + 32 + h * DV + ch] : 0.f;
-  const float* gt = p.gates + (size_t)qh * 3;
-  const float g0 = gt[0], g1 = gt[1], g2 = gt[2];
-  const int nvis = n_visible(p, b, L);
-  const int nch_b = (nvis + p.seg - 1) / p.seg;
-  __syncthreads();
-
-  // ---- compressed branch
-  float oc = 0.f;
+      for (int k = 0; k < FW; ++k) {
+        const float* src = wp + (size_t)k * PSTRIDE + 32 + e2;
+        rw[u][k] = k < p.nwin ? f32x2_t{src[0], src[1]} : f32x2_t{0.f, 0.f};
+      }
+    }
+    if (tid < 16) {
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) oc += u < nch_b ? s_f[u] * vo[u] : 0.f;
-  for (int c0 = kBatch; c0 < nch_b; c0 += kBatch) {  // long contexts: remaining chunks
-    float v[kBatch];
+      for (int k = 0; k < FF; ++k) {
+        fm[k] = k < p.nfin ? ld_shared_dev(rp + (size_t)k * PSTRIDE + tid) : -INFINITY;
+        fl[k] = k < p.nfin ? ld_shared_dev(rp + (size_t)k * PSTRIDE + 16 + tid) : 0.f;
+      }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) v[u] = c0 + u < nch_b ? p.o1[((cbase + c0 + u) * 16 + h) * DV + ch] : 0.f;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) oc += c0 + u < nch_b ? s_f[c0 + u] * v[u] : 0.f;
-  }
-  // ---- selected branch: the finish workgroups' partials
-  float M = -INFINITY;
-  for (int k = 0; k < nfin; ++k) M = fmaxf(M, s_pm[k]);
-  float vs = 0.f, ls = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxFinish; ++k) {
-    if (k < nfin && s_pm[k] != -INFINITY) {
-      const float a = exp2f(s_pm[k] - M);
-      vs += a * vr[k];
-      ls += a * s_pl[k];
+      for (int k = 0; k < FW; ++k) {
+        wm[k] = k < p.nwin ? wp[(size_t)k * PSTRIDE + tid] : -INFINITY;
+        wl[k] = k < p.nwin ? wp[(size_t)k * PSTRIDE + 16 + tid] : 0.f;
+      }
     }
   }
-  // ---- window branch
-  float Mw = -INFINITY;
-  for (int k = 0; k < nwin; ++k) Mw = fmaxf(Mw, s_wm[k]);
-  float vwin = 0.f, lwin = 0.f;
+  if (tid < 16) {  // per-head merge factors of the selected and window partials
+    const int h = tid;
+    auto mk_ = [&](int k) { return fast ? fm[k < FF ? k : 0] : ld_shared_dev(rp + (size_t)k * PSTRIDE + h); };
+    auto lk_ = [&](int k) { return fast ? fl[k < FF ? k : 0] : ld_shared_dev(rp + (size_t)k * PSTRIDE + 16 + h); };
+    auto mw_ = [&](int k) { return fast ? wm[k < FW ? k : 0] : wp[(size_t)k * PSTRIDE + h]; };
+    auto lw_ = [&](int k) { return fast ? wl[k < FW ? k : 0] : wp[(size_t)k * PSTRIDE + 16 + h]; };
+    float M = -INFINITY, Mw = -INFINITY;
+    for (int k = 0; k < p.nfin; ++k) M = fmaxf(M, mk_(k));
+    for (int k = 0; k < p.nwin; ++k) Mw = fmaxf(Mw, mw_(k));
+    float ls = 0.f, lw = 0.f;
+    for (int k = 0; k < p.nfin; ++k) {
+      const float mk = mk_(k);
+      const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+      s_pf[k][h] = a;
+      ls += a * lk_(k);
+    }
+    for (int k = 0; k < p.nwin; ++k) {
+      const float mk = mw_(k);
+      const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - Mw);
+      s_wf[k][h] = a;
+      lw += a * lw_(k);
+    }
+    const float is = ls > 0.f ? 1.0f / ls : 0.f, iw = lw > 0.f ? 1.0f / lw : 0.f;
+    for (int k = 0; k < p.nfin; ++k) s_pf[k][h] *= is;
+    for (int k = 0; k < p.nwin; ++k) s_wf[k][h] *= iw;
+  }
+  lds_barrier();
+  auto emit = [&](int e, float oc, float os, float ow) {  // output e of the group's 16 x DV
+    const int h = e / DV;
+    if (h >= p.G) return;
+    const int hq = g * p.G + h;
+    p.out[((size_t)b * p.Hq + hq) * DV + (e - h * DV)] =
+        (uint16_t)f32_to_bf16(s_gate[h][0] * oc + s_gate[h][1] * os + s_gate[h][2] * ow);
+  };
+  if (fast) {
 #pragma unroll
-  for (int k = 0; k < kMaxWindow; ++k) {
-    if (k < nwin && s_wm[k] != -INFINITY) {
-      const float a = exp2f(s_wm[k] - Mw);
-      vwin += a * vw[k];
-      lwin += a * s_wl[k];
+    for (int u = 0; u < NP; ++u) {
+      const int e2 = 2 * (tid + NTH * u), h = e2 / DV;
+      float os0 = 0.f, os1 = 0.f, ow0 = 0.f, ow1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < FF; ++k) {
+        const float a = k < p.nfin ? s_pf[k][h] : 0.f;
+        os0 += a * ro[u][k][0];
+        os1 += a * ro[u][k][1];
+      }
+#pragma unroll
+      for (int k = 0; k < FW; ++k) {
+        const float a = k < p.nwin ? s_wf[k][h] : 0.f;
+        ow0 += a * rw[u][k][0];
+        ow1 += a * rw[u][k][1];
+      }
+      emit(e2, rc[u][0], os0, ow0);
+      emit(e2 + 1, rc[u][1], os1, ow1);
+    }
+  } else {
+    for (int e = tid; e < p.G * DV; e += NTH) {
+      const int h = e / DV;
+      float os = 0.f, ow = 0.f;
+      for (int k = 0; k < p.nfin; ++k) os += s_pf[k][h] * ld_shared_dev(rp + (size_t)k * PSTRIDE + 32 + e);
+      for (int k = 0; k < p.nwin; ++k) ow += s_wf[k][h] * wp[(size_t)k * PSTRIDE + 32 + e];
+      emit(e, ld_shared_dev(oc_src + e), os, ow);
     }
   }
-  const float os = ls > 0.f ? vs / ls : 0.f;
-  const float ow = lwin > 0.f ? vwin / lwin : 0.f;
-  p.out[(size_t)qh * DV + ch] = (uint16_t)f32_to_bf16(g0 * oc + g1 * os + g2 * ow);
 }
 
 // ---------------------------------------------------------------- host side
@@ -794,12 +873,13 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   lay.off_o1 = off;   off = align256(off + BH * lay.nch * 16 * (size_t)DV * 4);
   lay.off_sc1 = off;  off = align256(off + BH * lay.nch * 16 * (size_t)(lay.nbo + 1) * 4);
   lay.off_wpart = off; off = align256(off + BH * lay.nwin * (32 + 16 * (size_t)DV) * 4);
-  // finish workgroups (4 waves, one 32-token step each): one partial each;
-  // normalised compressed-branch factors
+  // finish workgroups (4 waves, one 32-token step each): one partial each; the
+  // normalised compressed-branch output; the arrival counters
   const int spb = lsel >= 32 ? lsel / 32 : 1;
   lay.nfin = (n * spb + 3) / 4;
   lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
-  lay.off_fcmp = off; off = align256(off + BH * lay.nch * 16 * 4);
+  lay.off_ocmp = off; off = align256(off + BH * 16 * (size_t)DV * 4);
+  lay.off_cnt = off; off = align256(off + BH * 4);
   lay.total = off;
   return lay;
 }
@@ -822,8 +902,6 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const Ph
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev->ev[2], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<DV>), dim3((unsigned)(p.B * p.Hq)), dim3(DV), 0, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev->ev[3], s)) != hipSuccess) return e;
   return hipSuccess;
 }

@@ -46,10 +46,11 @@ struct DecodeParams {
   float* m1;                         // [B*H, nch, 16]
   float* l1;                         // [B*H, nch, 16]
   float* o1;                         // [B*H, nch, 16, DV]
-  float* sc1;                        // [B*H, nch, 16, nbo+1]
+  float* sc1;                        // [B*H, nch, nbo+1, 16] selection-block scores per head
   float* wpart;                      // [B*H, nwin, 32 + 16*DV] window-workgroup partials
   float* rpart;                      // [B*H, nfin, 32 + 16*DV] routed-block partials
-  float* fcmp;                       // [B*H, nch, 16] normalised compressed-branch factors
+  float* ocmp;                       // [B*H, 16, DV] normalised compressed-branch output
+  uint32_t* cnt;                     // [B*H] finish-workgroup arrival counters
   int nch;                           // compressed segments per (sequence, group)
   int seg;                           // compressed keys per segment (multiple of 64 and of lsel/d)
   int nbo;                           // selection blocks owned by one segment = seg*d/lsel
@@ -59,7 +60,7 @@ struct DecodeParams {
 };
 
 struct DecodeLayout {
-  size_t off_m1, off_l1, off_o1, off_sc1, off_wpart, off_rpart, off_fcmp, total;
+  size_t off_m1, off_l1, off_o1, off_sc1, off_wpart, off_rpart, off_ocmp, off_cnt, total;
   int nch, seg, nbo, nfin, nwin, wtiles;
 };
 

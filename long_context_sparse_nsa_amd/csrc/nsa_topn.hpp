@@ -116,7 +116,7 @@ __device__ void block_topn(const float* S, int J, int n, int nloc, int finit, To
       w = wave_extract<MAXC>(k, nr);
     }
     sm.wbest[wave * kTopnMaxRouted + lane] = w;
-    __syncthreads();
+    lds_barrier();
   }
   if (wave == 0) {
     // ---- wave 0: merge the waves' winners, add the forced blocks, rank
@@ -178,10 +178,8 @@ __device__ __forceinline__ int count_greater(const uint64_t* v, int nb, uint64_t
   return c;
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+__device__ __forceinline__ void wave_lds_sync() {  // LDS writes of this wave visible to all its lanes
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // Ranks the T (<= 128) keys in surv (zero padded to a multiple of 16) and
@@ -270,12 +268,12 @@ __device__ void block_topn_fast(const float* S, int J, int n, int nloc, int fini
     k[c] = ok ? ((uint64_t)__float_as_uint(S[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j) : 0ull;
   }
   if (tid == 0) fs.fail = 0;
-  __syncthreads();
+  lds_barrier();
   const bool ok = wave_rank_topn<K>(k, nr, fs.lmax[wave], fs.surv[wave], fs.best + wave * 16);
   if (!ok && lane == 0) fs.fail = 1;
-  __syncthreads();
+  lds_barrier();
   if (fs.fail) {
-    __syncthreads();
+    lds_barrier();
     block_topn<NT, MAXC>(S, J, n, nloc, finit, sm, out, out2);
     return;
   }
