@@ -10,9 +10,10 @@ attention, gated sum.  value = tokens/s = 8 / step time.
 
 Timing: K back-to-back steps replayed from a HIP graph, each step on its own copy
 of the KV cache (6 copies, 8.6 GB, far beyond the 256 MB Infinity Cache) so every
-step reads HBM cold, bracketed by torch.cuda.synchronize().  Per-pass durations
-come from HIP events the library records at its phase boundaries on the call's
-stream, in an eager run queued behind a sleep kernel so the passes run back to back.
+step reads HBM cold, bracketed by torch.cuda.synchronize().  Per-kernel durations
+come from HIP start / stop events the library attaches to each decode kernel's
+dispatch on the call's stream (and from events at the phase boundaries for
+prefill), in an eager run queued behind a sleep kernel.
 
 Also reported: the causal prefill of 32768 tokens (in-call compression) and the
 float64 CPU oracle on a bounded sample (cpu_baseline).
@@ -38,6 +39,10 @@ METRIC = "NSA decode tokens/sec at 64k ctx (HBM GB/s %peak); prefill TFLOP/s (%M
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# sources of the decode kernels (a counter summary taken on other sources is not used)
+DECODE_SOURCES = ("nsa_decode.hip", "nsa_tiles.hpp", "nsa_topn.hpp", "nsa_device.hpp", "nsa_internal.hpp")
 
 
 def src_hash(*names) -> str:
@@ -106,18 +111,16 @@ def decode_bytes(case, sel):
     """Algorithmic HBM bytes of one decode step and of its first kernel.
 
     Step: the compressed cache, the union of selected and window tokens (each
-    read once), q, gates, out.  First kernel (compressed branch + window
-    workgroups): the compressed cache, the window tokens together with the forced
-    blocks' tokens (initial and local blocks, which that kernel also reads), q."""
+    read once), q, gates, out.  First kernel (compressed-branch and window
+    workgroups of the streaming pass): the compressed cache, the window tokens,
+    q."""
     wl, p = case.wl, case.p
     row = 2 * (wl.d_k + wl.d_v)
-    cmp_b, sw_b, wf_b = 0, 0, 0
+    cmp_b, sw_b, w_b = 0, 0, 0
     for b in range(wl.batch):
         L = int(case.seq_lens[b])
         t = L - 1
-        J = t // p.l_sel
         nc = (L - p.l) // p.d + 1 if L >= p.l else 0
-        forced = set(range(max(0, J - p.n_local + 1), J + 1)) | ({0} if p.force_initial else set())
         for g in range(wl.num_kv_heads):
             cmp_b += nc * row
             win = set(range(max(0, t - p.w + 1), t + 1))
@@ -126,13 +129,10 @@ def decode_bytes(case, sel):
                 if j >= 0:
                     toks.update(range(j * p.l_sel, min((j + 1) * p.l_sel, L)))
             sw_b += len(toks) * row
-            wf = set(win)
-            for j in forced:
-                wf.update(range(j * p.l_sel, min((j + 1) * p.l_sel, L)))
-            wf_b += len(wf) * row
+            w_b += len(win) * row
     io = wl.batch * wl.num_q_heads * (wl.d_k * 2 + 3 * 4 + wl.d_v * 2)
     q_bytes = wl.batch * wl.num_q_heads * wl.d_k * 2
-    return cmp_b + sw_b + io, cmp_b + wf_b + q_bytes, sw_b
+    return cmp_b + sw_b + io, cmp_b + w_b + q_bytes, sw_b
 
 
 def bench_decode(args, torch, N, I):
@@ -218,7 +218,8 @@ def bench_decode(args, torch, N, I):
         step(i)
     N.nsa_set_phase_events(None)
     torch.cuda.synchronize()
-    ph = [float(np.mean([hev.ms(4 * i + k, 4 * i + k + 1) for i in range(n_ph)])) for k in range(2)]
+    # start / stop events attached to each kernel's dispatch: (0, 1) streaming, (2, 3) finish
+    ph = [float(np.mean([hev.ms(4 * i + k, 4 * i + k + 1) for i in range(n_ph)])) for k in (0, 2)]
     hev.close()
     p1 = ph[0]
     p2 = ph[1]
@@ -348,15 +349,74 @@ def cpu_baseline(case, min_seconds):
                        f"{wl.name}; oracle-compressed cache precomputed untimed; {elapsed:.1f} s of CPU work")
 
 
+def kernels_only(args, torch, N, I):
+    """A few eager calls and nothing else (for profiler runs): decode steps over
+    the cache copies, or, with --prefill, prefill calls."""
+    if args.prefill:
+        wl = I.workload("prefill_32k")
+        case = I.generate(wl, list(I.WORKLOADS).index("prefill_32k"))
+        p = wl.params
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+        dims = N.make_dims(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.d_k, wl.d_v)
+        cfg = N.make_config(p.l, p.d, p.l_sel, p.n_sel, p.n_local, p.force_initial, p.w)
+        q, k, v = dev(case.q), dev(case.k), dev(case.v)
+        wk, pk, wv, pv = dev(case.w_k), dev(case.pe_k), dev(case.w_v), dev(case.pe_v)
+        gates = torch.from_numpy(case.gates).cuda()
+        out = torch.empty((wl.batch, wl.seq_len, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
+        ws = N.new_workspace(N.nsa_prefill_workspace_size(dims, cfg, wl.seq_len, True))
+        for i in range(args.kernels_only):
+            N.nsa_prefill_fwd(dims, cfg, wl.seq_len, q, k, v, None, None, wk, pk, wv, pv, gates, out, None, ws)
+            torch.cuda.synchronize()
+            log(f"[bench] prefill call {i + 1}/{args.kernels_only} done")
+        return
+    wl = I.workload(args.workload)
+    case = I.generate(wl, list(I.WORKLOADS).index(args.workload))
+    dims, cfg, T, max_len, cuc = upload_case(case, torch, N)
+    ws = N.new_workspace(N.nsa_decode_workspace_size(dims, cfg, max_len))
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    copies = [(T["k"], T["v"], T["kc"], T["vc"])]
+    for _ in range(args.copies - 1):
+        copies.append(tuple(x.clone() for x in copies[0]))
+    torch.cuda.synchronize()
+    for i in range(args.kernels_only):
+        k, v, kc, vc = copies[i % len(copies)]
+        N.nsa_decode_fwd(dims, cfg, T["q"], k, v, kc, vc, T["seq"], T["cu"], T["cuc"], max_len, T["gates"], out,
+                         None, ws)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.kernels_only} decode steps of {wl.name} done")
+
+
+def copy_calibration(torch, mib=256, reps=4):
+    """A plain device copy of known size (torch's copy kernel), for scaling the
+    HBM byte counters of a profiler run: each launch reads and writes mib MiB."""
+    n = mib * 1024 * 1024 // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {mib} MiB done")
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_stream_kernel.decode_64k_b8.traffic.md")
+
+
 def roofline_from_profiles(kernel_hash):
-    """HBM traffic of the compressed pass from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode_cmp_traffic.json")
+    """HBM bytes per launch of the streaming kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
+    size), or None when that summary was taken on other kernel sources."""
     try:
-        d = json.load(open(path))
-        if d.get("kernel_src_hash") == kernel_hash:
-            return d.get("traffic_bytes_per_launch")
-    except Exception:
+        fields = {}
+        for ln in open(TRAFFIC_PROFILE):
+            if ":" in ln and ln.strip().startswith("- "):
+                k, v = ln.strip()[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+        if fields.get("kernel_src_hash") == kernel_hash:
+            return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
         pass
     return None
 
@@ -372,6 +432,11 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
+                    help="run N eager calls and exit (for profiler runs; no timing, no JSON line)")
+    ap.add_argument("--prefill", action="store_true", help="with --kernels-only: prefill calls instead of decode")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy a few times and exit (profiler counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this NSA path is single-GPU by design; run with --gpus 1",
@@ -383,6 +448,12 @@ def main():
     import nsa_inputs as I
     N.load_library()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    if args.kernels_only:
+        kernels_only(args, torch, N, I)
+        return
 
     case, dec, _ = bench_decode(args, torch, N, I)
     pre = None if args.no_prefill else bench_prefill(args, torch, N, I)
@@ -390,7 +461,7 @@ def main():
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']:.3g} tok/s on {cpu['cores']} threads")
 
-    khash = src_hash("nsa_decode.hip", "nsa_tiles.hpp", "nsa_topn.hpp", "nsa_device.hpp")
+    khash = src_hash(*DECODE_SOURCES)
     wl = case.wl
     p = wl.params
     line = {

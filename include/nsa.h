@@ -175,11 +175,11 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
  * nsa_prefill_fwd on this thread records the caller-owned hipEvent_t handles
  * events[0..3] on the call's stream between its kernels, so a caller can time
  * each kernel with hipEventElapsedTime:
- *   decode:  before the streaming kernel (compressed branch with the folded
- *            selection scores, and the window branch), after it, after the
- *            selection kernel (top-n, the selected blocks, and the exact merge
- *            and gated sum), and once more at the same point (the decode path
- *            has two kernels);
+ *   decode:  events[0] / events[1] are the start / stop events of the
+ *            streaming kernel's dispatch (compressed branch with the folded
+ *            selection scores, and the window branch), events[2] / events[3]
+ *            those of the selection kernel (top-n, the selected blocks, the
+ *            exact merge and the gated sum), so each pair times one kernel;
  *   prefill: before the in-call compression, after it (or right away when the
  *            cache is given), after the compressed + window + top-n kernel, after
  *            the selected-branch kernel (which writes the gated sum).

@@ -22,6 +22,7 @@
 // selection of n l'-blocks re-using the compressed-branch weights, shared by a
 // GQA group so each KV block is read once per group; window of w tokens) and
 // section "Сколько это экономит" (decode is bound by reading the KV cache).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "nsa_device.hpp"
@@ -884,26 +885,26 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   return lay;
 }
 
+// With events, each kernel is launched with its start / stop events attached
+// to the dispatch (ev[0], ev[1]: streaming kernel; ev[2], ev[3]: finish kernel),
+// so their elapsed times are the kernels' own execution times.
 template <int DK, int DV>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const PhaseEvents* ev) {
+  hipEvent_t e0 = ev ? ev->ev[0] : nullptr, e1 = ev ? ev->ev[1] : nullptr;
+  hipEvent_t e2 = ev ? ev->ev[2] : nullptr, e3 = ev ? ev->ev[3] : nullptr;
+  hipExtLaunchKernelGGL((decode_stream_kernel<DK, DV>), dim3((unsigned)(p.B * p.H * (p.nch + p.nwin))),
+                        dim3(64 * kStreamWaves), 0, s, e0, e1, 0, p);
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev->ev[0], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_stream_kernel<DK, DV>), dim3((unsigned)(p.B * p.H * (p.nch + p.nwin))),
-                     dim3(64 * kStreamWaves), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev->ev[1], s)) != hipSuccess) return e;
   const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(256);
   switch (p.lsel) {
-    case 16: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 16>), g2, blk, 0, s, p); break;
-    case 32: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 32>), g2, blk, 0, s, p); break;
-    case 64: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 64>), g2, blk, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((decode_finish_kernel<DK, DV, 128>), g2, blk, 0, s, p); break;
+    case 16: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 16>), g2, blk, 0, s, e2, e3, 0, p); break;
+    case 32: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 32>), g2, blk, 0, s, e2, e3, 0, p); break;
+    case 64: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 64>), g2, blk, 0, s, e2, e3, 0, p); break;
+    case 128: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 128>), g2, blk, 0, s, e2, e3, 0, p); break;
     default: return hipErrorInvalidValue;
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev->ev[2], s)) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev->ev[3], s)) != hipSuccess) return e;
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev) {
