@@ -34,9 +34,16 @@ namespace nsa {
 
 namespace {
 
+// Wave-uniform reads of the read-only length arrays through the scalar data
+// cache: waiting for them does not wait for outstanding vector loads.
+template <class T>
+__device__ __forceinline__ T ld_scalar(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 __device__ __forceinline__ int64_t raw_row0(const DecodeParams& p, int b, int g) {
   if (p.cu) {
-    const int64_t c0 = p.cu[b], c1 = p.cu[b + 1];
+    const int64_t c0 = ld_scalar(p.cu + b), c1 = ld_scalar(p.cu + b + 1);
     return (int64_t)p.H * c0 + (int64_t)g * (c1 - c0);
   }
   return ((int64_t)b * p.H + g) * p.cap;
@@ -44,7 +51,7 @@ __device__ __forceinline__ int64_t raw_row0(const DecodeParams& p, int b, int g)
 
 __device__ __forceinline__ int64_t cmp_row0(const DecodeParams& p, int b, int g) {
   if (p.cuc) {
-    const int64_t c0 = p.cuc[b], c1 = p.cuc[b + 1];
+    const int64_t c0 = ld_scalar(p.cuc + b), c1 = ld_scalar(p.cuc + b + 1);
     return (int64_t)p.H * c0 + (int64_t)g * (c1 - c0);
   }
   return ((int64_t)b * p.H + g) * p.ccap;
@@ -55,10 +62,10 @@ __device__ __forceinline__ int64_t cmp_row0(const DecodeParams& p, int b, int g)
 __device__ __forceinline__ int seq_len_clamped(const DecodeParams& p, int b) {
   int64_t cap = p.cap;
   if (p.cu) {
-    const int64_t c = p.cu[b + 1] - p.cu[b];
+    const int64_t c = ld_scalar(p.cu + b + 1) - ld_scalar(p.cu + b);
     if (c < cap) cap = c;
   }
-  int64_t L = p.seq_lens[b];
+  int64_t L = ld_scalar(p.seq_lens + b);
   if (L > cap) L = cap;
   if (L < 1) L = 1;
   return (int)L;
@@ -67,7 +74,7 @@ __device__ __forceinline__ int seq_len_clamped(const DecodeParams& p, int b) {
 // Complete compressed blocks among L tokens, clamped to the compressed capacity.
 __device__ __forceinline__ int n_visible(const DecodeParams& p, int b, int L) {
   int64_t nv = L >= p.l ? (L - p.l) / p.d + 1 : 0;
-  const int64_t ccap = p.cuc ? p.cuc[b + 1] - p.cuc[b] : p.ccap;
+  const int64_t ccap = p.cuc ? ld_scalar(p.cuc + b + 1) - ld_scalar(p.cuc + b) : p.ccap;
   return (int)(nv < ccap ? nv : ccap);
 }
 
@@ -300,29 +307,48 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   const int bg = blockIdx.x / per, c = blockIdx.x - bg * per;
   const int g = bg % p.H, b = bg / p.H;
   const bool fold = c < p.nch;  // workgroup-uniform: compressed segment, else window part
-  const int L = seq_len_clamped(p, b);
-  const int t = L - 1;
+  const uint32_t koff = (uint32_t)((lr * DK + 8 * lg) * 2), voff = (uint32_t)((4 * lg * DV + VC * lr) * 2);
+  u32x4_t qf[KT];
+  WaveTile<DK, DV> tb[kDepth];
+  auto load_q = [&]() { load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf); };
 
   // rows [r0, r0 + 64*nt) are streamed; keys outside [vlo, vhi] are masked
   int64_t r0, rowmax;
   int nt, vlo, vhi;
   const uint16_t *kb, *vb;
+  int L;
   if (fold) {
-    const int nvis = n_visible(p, b, L);
+    // A segment's rows and its slot's capacity do not depend on the sequence
+    // length, so the first tiles are requested while the length is read; rows
+    // past the length are masked (their values are zeroed before use).
     const int k0 = c * p.seg;
-    if (k0 >= nvis) return;  // empty segment: never read by the later kernels
+    const int64_t ccap_b = p.cuc ? ld_scalar(p.cuc + b + 1) - ld_scalar(p.cuc + b) : p.ccap;
+    if (k0 >= ccap_b) return;  // beyond the slot: never read by the later kernels
+    const int64_t rpre = min((int64_t)k0 + p.seg, ccap_b) - 1;
+    const int64_t crow = cmp_row0(p, b, g);
+    kb = p.kc + crow * DK;
+    vb = p.vc + crow * DV;
+    L = seq_len_clamped(p, b);
+    load_q();
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)
+      load_wave_tile<DK, DV>(tb[d], kb, vb, (int64_t)k0 + 64 * d + 16 * wave, rpre, koff, voff, lg, lr);
+    const int nvis = n_visible(p, b, L);
+    if (k0 >= nvis) {  // empty segment: never read by the later kernels
+      wait_vmem();
+      return;
+    }
     const int k1 = min(k0 + p.seg, nvis);
     r0 = k0;
     nt = (k1 - k0 + 63) >> 6;
     vlo = k0;
     vhi = k1 - 1;
     rowmax = nvis - 1;
-    const int64_t crow = cmp_row0(p, b, g);
-    kb = p.kc + crow * DK;
-    vb = p.vc + crow * DV;
   } else {
     const int wi = c - p.nch;
     if (wi == 0 && tid == 0) p.cnt[bg] = 0u;  // arrival counter of the finish workgroups
+    L = seq_len_clamped(p, b);
+    const int t = L - 1;
     const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
     const int T0 = (wlo >> 6) + wi * p.wtiles, T1 = min((wlo >> 6) + (wi + 1) * p.wtiles, (t >> 6) + 1);
     r0 = (int64_t)T0 * 64;
@@ -338,21 +364,17 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
       for (int e = tid; e < PSTRIDE; e += NTH) dst[e] = e < 16 ? -INFINITY : 0.f;
       return;
     }
+    load_q();
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)
+      load_wave_tile<DK, DV>(tb[d], kb, vb, r0 + 64 * d + 16 * wave, min(rowmax, r0 + 64 * (int64_t)nt - 1), koff,
+                             voff, lg, lr);
   }
 
   // Loads never read past the workgroup's own last row: requests for tiles
   // beyond the range (issued so that every pipeline step has the same loads in
   // flight) re-read that row from cache.
   const int64_t rlast = min(rowmax, r0 + 64 * (int64_t)nt - 1);
-
-  // ---- loads first: query fragments, then the first kDepth - 1 tiles
-  u32x4_t qf[KT];
-  load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
-  const uint32_t koff = (uint32_t)((lr * DK + 8 * lg) * 2), voff = (uint32_t)((4 * lg * DV + VC * lr) * 2);
-  WaveTile<DK, DV> tb[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d)
-    load_wave_tile<DK, DV>(tb[d], kb, vb, r0 + 64 * d + 16 * wave, rlast, koff, voff, lg, lr);
 
   const int qd = p.l / p.d, rd = p.lsel / p.d;  // key and block lengths in stride units
   const int rsh = __builtin_ctz(rd);            // rd is a power of two
@@ -432,16 +454,21 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
       }
     }
 
-    // ---- probabilities, values
+    // ---- probabilities, values (rows past rlast may hold values of rows past the
+    // sequence, which are zeroed: their weight is 0 but their bits are arbitrary)
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(z[e] - mref);
     lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const u32x2_t ph = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+    const bool vall = k0 + 15 <= rlast;  // wave-uniform
+    const uint32_t vm01 = (k0 + 4 * lg <= rlast ? 0x0000FFFFu : 0u) | (k0 + 4 * lg + 1 <= rlast ? 0xFFFF0000u : 0u);
+    const uint32_t vm23 = (k0 + 4 * lg + 2 <= rlast ? 0x0000FFFFu : 0u) | (k0 + 4 * lg + 3 <= rlast ? 0xFFFF0000u : 0u);
 #pragma unroll
     for (int j = 0; j < VC; ++j) {
       const int wd = j >> 1, h = j & 1;
-      const u32x2_t va = {pack_halves(T.v[0][wd], T.v[1][wd], h), pack_halves(T.v[2][wd], T.v[3][wd], h)};
+      u32x2_t va = {pack_halves(T.v[0][wd], T.v[1][wd], h), pack_halves(T.v[2][wd], T.v[3][wd], h)};
+      if (!vall) va = u32x2_t{va[0] & vm01, va[1] & vm23};
       acc[j] = mfma16_bf16(va, ph, acc[j]);
     }
 
@@ -511,8 +538,11 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     dl = dst + 16;
     dox = dst + 32;
   }
-  for (int h = wave; h < 16; h += NW)
-    for (int ch = lane; ch < DV; ch += 64) {
+#pragma unroll
+  for (int hh = 0; hh < 16 / NW; ++hh)
+#pragma unroll
+    for (int cc = 0; cc < DV / 64; ++cc) {
+      const int h = wave + NW * hh, ch = lane + 64 * cc;
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += s_o[w][h][ch];
@@ -529,7 +559,17 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     const int slots = p.nbo + 1;
     const float invq = 1.0f / (float)qd;
     float* SC = p.sc1 + ((size_t)bg * p.nch + c) * slots * 16;  // [slot][head]
-    for (int e = tid; e < 16 * slots; e += NTH) SC[e] = s_sc[(e & 15) * sstride + (e >> 4)] * invq;
+    for (int e0 = tid; e0 < 16 * slots; e0 += 4 * NTH) {  // four entries per thread and pass
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + NTH * u;
+        v[u] = e < 16 * slots ? s_sc[(e & 15) * sstride + (e >> 4)] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + NTH * u < 16 * slots) SC[e0 + NTH * u] = v[u] * invq;
+    }
   }
 }
 
@@ -773,25 +813,41 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
   }
   if (tid < 16) {  // per-head merge factors of the selected and window partials
     const int h = tid;
-    auto mk_ = [&](int k) { return fast ? fm[k < FF ? k : 0] : ld_shared_dev(rp + (size_t)k * PSTRIDE + h); };
-    auto lk_ = [&](int k) { return fast ? fl[k < FF ? k : 0] : ld_shared_dev(rp + (size_t)k * PSTRIDE + 16 + h); };
-    auto mw_ = [&](int k) { return fast ? wm[k < FW ? k : 0] : wp[(size_t)k * PSTRIDE + h]; };
-    auto lw_ = [&](int k) { return fast ? wl[k < FW ? k : 0] : wp[(size_t)k * PSTRIDE + 16 + h]; };
-    float M = -INFINITY, Mw = -INFINITY;
-    for (int k = 0; k < p.nfin; ++k) M = fmaxf(M, mk_(k));
-    for (int k = 0; k < p.nwin; ++k) Mw = fmaxf(Mw, mw_(k));
     float ls = 0.f, lw = 0.f;
-    for (int k = 0; k < p.nfin; ++k) {
-      const float mk = mk_(k);
-      const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-      s_pf[k][h] = a;
-      ls += a * lk_(k);
-    }
-    for (int k = 0; k < p.nwin; ++k) {
-      const float mk = mw_(k);
-      const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - Mw);
-      s_wf[k][h] = a;
-      lw += a * lw_(k);
+    if (fast) {  // static indexing only: the loaded values stay in registers
+      float M = -INFINITY, Mw = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < FF; ++k) M = fmaxf(M, fm[k]);
+#pragma unroll
+      for (int k = 0; k < FW; ++k) Mw = fmaxf(Mw, wm[k]);
+#pragma unroll
+      for (int k = 0; k < FF; ++k) {
+        const float a = fm[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm[k] - M);
+        s_pf[k][h] = a;
+        ls += a * fl[k];
+      }
+#pragma unroll
+      for (int k = 0; k < FW; ++k) {
+        const float a = wm[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wm[k] - Mw);
+        s_wf[k][h] = a;
+        lw += a * wl[k];
+      }
+    } else {
+      float M = -INFINITY, Mw = -INFINITY;
+      for (int k = 0; k < p.nfin; ++k) M = fmaxf(M, ld_shared_dev(rp + (size_t)k * PSTRIDE + h));
+      for (int k = 0; k < p.nwin; ++k) Mw = fmaxf(Mw, wp[(size_t)k * PSTRIDE + h]);
+      for (int k = 0; k < p.nfin; ++k) {
+        const float mk = ld_shared_dev(rp + (size_t)k * PSTRIDE + h);
+        const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+        s_pf[k][h] = a;
+        ls += a * ld_shared_dev(rp + (size_t)k * PSTRIDE + 16 + h);
+      }
+      for (int k = 0; k < p.nwin; ++k) {
+        const float mk = wp[(size_t)k * PSTRIDE + h];
+        const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - Mw);
+        s_wf[k][h] = a;
+        lw += a * wp[(size_t)k * PSTRIDE + 16 + h];
+      }
     }
     const float is = ls > 0.f ? 1.0f / ls : 0.f, iw = lw > 0.f ? 1.0f / lw : 0.f;
     for (int k = 0; k < p.nfin; ++k) s_pf[k][h] *= is;

@@ -72,7 +72,7 @@ __device__ __forceinline__ uint64_t wave_extract(uint64_t (&k)[K], int rounds) {
 // Candidates with key 0 are excluded.  MAXC bounds the candidates per lane:
 // ceil(ceil((J+1)/(NT/64)) / 64) <= MAXC.
 template <int NT, int MAXC>
-__device__ void block_topn(const float* S, int J, int n, int nloc, int finit, TopnSmem& sm, int32_t* out,
+__device__ __forceinline__ void block_topn(const float* S, int J, int n, int nloc, int finit, TopnSmem& sm, int32_t* out,
                            int32_t* out2) {
   static_assert(NT % 64 == 0 && NT <= 1024, "block size");
   constexpr int NW = NT / 64;
@@ -247,7 +247,7 @@ __device__ __forceinline__ bool wave_rank_topn(const uint64_t (&k)[K], int nr, u
 // reads S again) when a wave has more than 128 survivors, more than K
 // candidates per thread are needed, or nr > 16.
 template <int NT, int K, int MAXC>
-__device__ void block_topn_fast(const float* S, int J, int n, int nloc, int finit, TopnFastSmem<NT / 64>& fs,
+__device__ __forceinline__ void block_topn_fast(const float* S, int J, int n, int nloc, int finit, TopnFastSmem<NT / 64>& fs,
                                 TopnSmem& sm, int32_t* out, int32_t* out2) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -304,7 +304,7 @@ __device__ void block_topn_fast(const float* S, int J, int n, int nloc, int fini
 // S[j] >= 0, at most 64 * MAXC of them.  Writes the n ids ascending to out
 // (-1 fills the tail when fewer than n candidates exist).  No LDS, no barrier.
 template <int MAXC>
-__device__ void wave_topn(const float* S, int J, int n, int nloc, int finit, int32_t* out) {
+__device__ __forceinline__ void wave_topn(const float* S, int J, int n, int nloc, int finit, int32_t* out) {
   const int lane = threadIdx.x & 63;
   const int ncand = J + 1;
   if (ncand <= n) {
