@@ -694,7 +694,11 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
   }
   lds_barrier();
 
-  // ---- this workgroup's slice of the compressed-branch output
+  // ---- this workgroup's slice of the compressed-branch output.  The first
+  // output of each thread is kept in a register and stored with the partial
+  // below: a store issued here would make the top-n wait for its completion
+  // (stores are counted with the loads, and its registers get reused).
+  float oc_first = 0.f;
   for (int e = e0 + tid; e < e1; e += NTH) {
     const int h = e / DV;
     float oc = 0.f;
@@ -705,7 +709,8 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
       for (int c = 0; c < min(nch_b, OB); ++c) oc += s_f[c * 16 + h] * p.o1[(cbase + c) * 16 * DV + e];
     }
     for (int c = OB; c < nch_b; ++c) oc += s_f[c * 16 + h] * p.o1[(cbase + c) * 16 * DV + e];
-    st_shared_dev(p.ocmp + (size_t)bg * 16 * DV + e, oc);
+    if (e == e0 + tid) oc_first = oc;
+    else st_shared_dev(p.ocmp + (size_t)bg * 16 * DV + e, oc);
   }
 
   // ---- group scores of candidate blocks 0..J, top-n
@@ -731,8 +736,11 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
     }
   }
   lds_barrier();
-  block_topn_fast<NTH, 8, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel,
-                                            (p.sel_out && kfin == 0) ? p.sel_out + (size_t)bg * p.n : nullptr);
+  {
+    int32_t* so = (p.sel_out && kfin == 0) ? p.sel_out + (size_t)bg * p.n : nullptr;
+    if (J + 1 <= 4 * NTH) block_topn_fast<NTH, 4, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel, so);
+    else block_topn_fast<NTH, 8, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel, so);
+  }
   lds_barrier();
   if (wave == 0) {  // the selected blocks, ascending (the list ends at the first -1)
     const int j = lane < p.n ? s_sel[lane] : -1;
@@ -766,6 +774,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
     }
   }
   float* rp = p.rpart + (size_t)bg * p.nfin * PSTRIDE;
+  if (e0 + tid < e1) st_shared_dev(p.ocmp + (size_t)bg * 16 * DV + e0 + tid, oc_first);
   merge_waves_to<DV, NWV, true>(br, rp + (size_t)kfin * PSTRIDE, s_buf, s_ml);
 
   // ---- the last workgroup of this (sequence, group) applies the gates.  The

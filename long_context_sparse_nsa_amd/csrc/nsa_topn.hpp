@@ -157,7 +157,8 @@ template <int NW>
 struct __attribute__((aligned(16))) TopnFastSmem {
   __attribute__((aligned(16))) uint64_t lmax[NW][64];
   __attribute__((aligned(16))) uint64_t surv[NW][144];  // <= 128 survivors, zero padded to a multiple of 16
-  uint64_t best[NW * 16];
+  __attribute__((aligned(16))) uint64_t best[NW * 16];  // the waves' winners, contiguous: wave w at [w*nr, (w+1)*nr)
+  __attribute__((aligned(16))) int ids[64];
   int fail;
 };
 
@@ -269,7 +270,7 @@ __device__ __forceinline__ void block_topn_fast(const float* S, int J, int n, in
   }
   if (tid == 0) fs.fail = 0;
   lds_barrier();
-  const bool ok = wave_rank_topn<K>(k, nr, fs.lmax[wave], fs.surv[wave], fs.best + wave * 16);
+  const bool ok = wave_rank_topn<K>(k, nr, fs.lmax[wave], fs.surv[wave], fs.best + wave * nr);
   if (!ok && lane == 0) fs.fail = 1;
   lds_barrier();
   if (fs.fail) {
@@ -278,21 +279,31 @@ __device__ __forceinline__ void block_topn_fast(const float* S, int J, int n, in
     return;
   }
   if (wave == 0) {
-    // the waves' winners: NW lists of nr (zero padded); rank them together
-    uint64_t* all = fs.surv[0];
+    // the waves' winners: NW contiguous lists of nr (zero padded); rank them together
     const int T = NW * nr;
-    for (int i = lane; i < ((T + 15) & ~15); i += 64) all[i] = i < T ? fs.best[(i / nr) * 16 + (i % nr)] : 0ull;
+    pad16(fs.best, T);
     wave_lds_sync();
-    rank_into(all, T, nr, fs.best);
+    uint64_t* win = fs.surv[0];
+    rank_into(fs.best, T, nr, win);
     wave_lds_sync();
     int v = INT32_MAX;
-    if (lane < nr) v = (int)(0xFFFFFFFFu - (uint32_t)(fs.best[lane] & 0xFFFFFFFFull));
+    if (lane < nr) v = (int)(0xFFFFFFFFu - (uint32_t)(win[lane] & 0xFFFFFFFFull));
     if (lane >= nr && lane < n) {
       const int i = lane - nr;  // forced block i
       v = f0 ? (i == 0 ? 0 : lo_local + i - 1) : lo_local + i;
     }
+    // ascending order: the rank of each id among the n (distinct) ids
+    fs.ids[lane] = v;
+    wave_lds_sync();
     int rank = 0;
-    for (int q = 0; q < n; ++q) rank += __builtin_amdgcn_readlane(v, q) < v;
+    for (int q0 = 0; q0 < n; q0 += 16) {
+      int4 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const int4*>(fs.ids + q0 + 4 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rank += (a[i].x < v) + (a[i].y < v) + (a[i].z < v) + (a[i].w < v);
+    }
     if (lane < n) {
       out[rank] = v;
       if (out2) out2[rank] = v;
