@@ -109,3 +109,21 @@ def test_decode_repeat_is_bitwise_identical():
     b = U.run_decode(case, kc, vc, ws=ws)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("params,L", [
+    # selection blocks of 32 stride units (l'/d = 32 > 16 keys of a wave's row tile), keys of 2 units
+    ({"l": 8, "d": 4, "l_sel": 128, "n_sel": 8, "n_local": 1, "w": 256}, 7000),
+    # one stride unit per key and per block (l = d = l')
+    ({"l": 16, "d": 16, "l_sel": 16, "n_sel": 16, "n_local": 2, "w": 128}, 5000),
+    # compressed blocks as long as selection blocks (l = l')
+    ({"l": 64, "d": 16, "l_sel": 64, "n_sel": 16, "n_local": 2, "w": 512}, 9000),
+    # 16 finish workgroups and more than two window partials (the general merge)
+    ({"l": 32, "d": 16, "l_sel": 64, "n_sel": 32, "n_local": 2, "w": 2048}, 9000),
+])
+def test_decode_block_shapes(params, L):
+    """Other (l, d, l', n, w): fold geometry, partial counts and merge paths."""
+    case = I.generate(I.workload(STD, batch=1, seq_len=L, params=params), 40 + L % 97)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    out, sel, _ = U.run_decode(case, kc, vc)
+    _check_decode(case, out, sel)
