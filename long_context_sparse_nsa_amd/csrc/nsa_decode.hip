@@ -222,12 +222,20 @@ struct WaveTile {
 };
 
 // A wave-uniform pointer moved into scalar registers, so that loads address it
-// as scalar base + 32-bit lane offset + immediate.
-__device__ __forceinline__ const char* scalar_ptr(const void* p) {
+// as scalar base + 32-bit lane offset + immediate.  The result is typed as a
+// global-memory pointer: through a generic pointer the loads would be flat
+// loads, which also count against the LDS counter, so every LDS wait of the
+// pipeline would also wait for the tiles in flight.
+typedef const __attribute__((address_space(1))) char* gchar_ptr;
+__device__ __forceinline__ gchar_ptr scalar_ptr(const void* p) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+  return (gchar_ptr)(((uint64_t)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T ld_global(gchar_ptr p) {
+  return *(const __attribute__((address_space(1))) T*)p;
 }
 
 // Rows row0 .. row0+15 (row0 wave-uniform); rows past rowmax read row rowmax
@@ -238,30 +246,29 @@ __device__ __forceinline__ void load_wave_tile(WaveTile<DK, DV>& T, const uint16
                                                int64_t row0, int64_t rowmax, uint32_t koff, uint32_t voff,
                                                int lg, int lr) {
   constexpr int CPL = DV / 16;  // channels per lane and row
-  auto put_v = [&](int e, const char* src) {
+  auto put_v = [&](int e, gchar_ptr src) {
     if constexpr (CPL == 8) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src);
+      const u32x4_t x = ld_global<u32x4_t>(src);
       T.v[e][0] = x[0]; T.v[e][1] = x[1]; T.v[e][2] = x[2]; T.v[e][3] = x[3];
     } else {
-      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(src);
+      const u32x2_t x = ld_global<u32x2_t>(src);
       T.v[e][0] = x[0]; T.v[e][1] = x[1];
     }
   };
   if (row0 + 15 <= rowmax) {  // wave-uniform: all 16 rows exist
-    const char* kp = scalar_ptr(kb + row0 * DK) + koff;
+    const gchar_ptr kp = scalar_ptr(kb + row0 * DK) + koff;
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) T.k[ks] = *reinterpret_cast<const u32x4_t*>(kp + 64 * ks);
-    const char* vp = scalar_ptr(vb + row0 * DV) + voff;
+    for (int ks = 0; ks < DK / 32; ++ks) T.k[ks] = ld_global<u32x4_t>(kp + 64 * ks);
+    const gchar_ptr vp = scalar_ptr(vb + row0 * DV) + voff;
 #pragma unroll
     for (int e = 0; e < 4; ++e) put_v(e, vp + e * DV * 2);
   } else {
     const int64_t rk = min(row0 + lr, rowmax);
-    const char* kp = reinterpret_cast<const char*>(kb + rk * DK + 8 * lg);
+    const gchar_ptr kp = (gchar_ptr)(kb + rk * DK + 8 * lg);
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) T.k[ks] = *reinterpret_cast<const u32x4_t*>(kp + 64 * ks);
+    for (int ks = 0; ks < DK / 32; ++ks) T.k[ks] = ld_global<u32x4_t>(kp + 64 * ks);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      put_v(e, reinterpret_cast<const char*>(vb + min(row0 + 4 * lg + e, rowmax) * DV + CPL * lr));
+    for (int e = 0; e < 4; ++e) put_v(e, (gchar_ptr)(vb + min(row0 + 4 * lg + e, rowmax) * DV + CPL * lr));
   }
 }
 
