@@ -163,6 +163,15 @@ __device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst,
     if constexpr (DEV_SHARED) st_shared_dev(q, v);
     else *q = v;
   };
+  auto put2 = [&](float* q, float v0, float v1) {  // q 8-byte aligned
+    if constexpr (DEV_SHARED) {
+      const uint64_t u = (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32);
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(q), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      q[0] = v0;
+      q[1] = v1;
+    }
+  };
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   constexpr int NTH = 64 * NWV;
   if (lg == 0) {
@@ -179,12 +188,15 @@ __device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst,
 #pragma unroll
     for (int i = 0; i < 4; ++i) buf[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = alpha * br.acc[j][i];
   lds_barrier();
-  for (int e = tid; e < 16 * DV; e += NTH) {
+  for (int e = 2 * tid; e < 16 * DV; e += 2 * NTH) {  // two outputs per thread and pass
     const int h = e / DV, ch = e - h * DV;
-    float v = 0.f;
+    float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) v += buf[(w * 16 + h) * (DV + 1) + ch];
-    put(dst + 32 + e, v);
+    for (int w = 0; w < NWV; ++w) {
+      v0 += buf[(w * 16 + h) * (DV + 1) + ch];
+      v1 += buf[(w * 16 + h) * (DV + 1) + ch + 1];
+    }
+    put2(dst + 32 + e, v0, v1);
   }
   if (tid < 16) {
     float Mh = -INFINITY;
@@ -592,8 +604,11 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
 // by the streaming pass) merges the selected-branch partials and the window
 // partials and writes out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
-  constexpr int NTH = 256, NWV = 4;
+#ifndef NSA_FIN_WAVES
+#define NSA_FIN_WAVES 4
+#endif
+__global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(DecodeParams p) {
+  constexpr int NWV = NSA_FIN_WAVES, NTH = 64 * NWV;
   constexpr int KT = DK / 32;
   constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;   // 32-token steps per selection block
   constexpr int PSTRIDE = 32 + 16 * DV;
@@ -617,10 +632,10 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(DecodeParams p) {
   // the nfin workgroups of one (sequence, group) get ids on the same XCD, so the
   // partials they hand over stay in that XCD's L2.  Only speed depends on this.
   int bg, kfin;
-  if (p.nfin == 8 && (p.B * p.H) % 8 == 0) {
+  if ((p.B * p.H) % 8 == 0) {
     const int w = blockIdx.x, xcd = w & 7, r = w >> 3;
-    bg = xcd + 8 * (r >> 3);
-    kfin = r & 7;
+    bg = xcd + 8 * (r / p.nfin);
+    kfin = r - (r / p.nfin) * p.nfin;
   } else {
     bg = blockIdx.x / p.nfin;
     kfin = blockIdx.x - bg * p.nfin;
@@ -949,7 +964,7 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   // finish workgroups (4 waves, one 32-token step each): one partial each; the
   // normalised compressed-branch output; the arrival counters
   const int spb = lsel >= 32 ? lsel / 32 : 1;
-  lay.nfin = (n * spb + 3) / 4;
+  lay.nfin = (n * spb + NSA_FIN_WAVES - 1) / NSA_FIN_WAVES;
   lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
   lay.off_ocmp = off; off = align256(off + BH * 16 * (size_t)DV * 4);
   lay.off_cnt = off; off = align256(off + BH * 4);
@@ -968,7 +983,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const Ph
                         dim3(64 * kStreamWaves), 0, s, e0, e1, 0, p);
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(256);
+  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(64 * NSA_FIN_WAVES);
   switch (p.lsel) {
     case 16: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 16>), g2, blk, 0, s, e2, e3, 0, p); break;
     case 32: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 32>), g2, blk, 0, s, e2, e3, 0, p); break;
