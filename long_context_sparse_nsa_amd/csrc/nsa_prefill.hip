@@ -489,12 +489,20 @@ template <int DK, int DV, int LSEL>
 __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   using SH = PfShape<DK, DV>;
   constexpr int KT = SH::KT, VC = SH::VC;
-  constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > 64 ? 64 : LSEL);
+#ifndef NSA_PF_SEL_ROWS
+#define NSA_PF_SEL_ROWS 64
+#endif
+#ifndef NSA_PF_SEL_NBUF
+#define NSA_PF_SEL_NBUF 3
+#endif
+  constexpr int RMAX = NSA_PF_SEL_ROWS;      // rows per step (at most)
+  constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > RMAX ? RMAX : LSEL);
   constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
-  constexpr int NBUF = 3;                    // two steps in flight
+  constexpr int NBUF = NSA_PF_SEL_NBUF;      // NBUF - 1 steps in flight
   using SO = StageOffsets<DK, DV, ROWS, kWaves>;
   constexpr int NLD = SO::kMinCopiesKV;
-  __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
+  constexpr int kStepBytes = SO::kKBytes + SO::kVBytes;
+  __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][kStepBytes];
   __shared__ uint32_t s_mask[kPfMaxBlocks];  // per block: bit q set if position t0+q chose it
   __shared__ uint32_t s_list[kPfMaxBlocks];  // the union, ascending: block id << 16 | mask
   __shared__ int s_scan[kWaves];
@@ -570,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   auto stage = [&](int st, int buf) {
     const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane((int)step_row0(st));
     stage_k(kraw, r0, T - 1, s_buf[buf], wave, lane, so);
-    stage_v(vraw, r0, T - 1, s_buf[buf] + SH::kKBytes, wave, lane, so);
+    stage_v(vraw, r0, T - 1, s_buf[buf] + SO::kKBytes, wave, lane, so);
   };
 
   wait_vmem_le<0>();  // query fragments in (see the compressed-branch kernel)
@@ -578,12 +586,17 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   for (int s0 = 0; s0 < NBUF - 1; ++s0)
     if (s0 < nsteps) stage(s0, s0);
   for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) wait_vmem_le<NLD>();
-    else wait_vmem_le<0>();
+    // step st has landed once at most the later steps' copies are outstanding
+    const int later = min(nsteps - 1 - st, NBUF - 2);
+    if (later <= 0) wait_vmem_le<0>();
+    else if (NBUF < 4 || later == 1) wait_vmem_le<NLD>();
+    else if (NBUF < 5 || later == 2) wait_vmem_le<2 * NLD>();
+    else if (NBUF < 6 || later == 3) wait_vmem_le<3 * NLD>();
+    else wait_vmem_le<4 * NLD>();
     lds_barrier();
     if (st + NBUF - 1 < nsteps) stage(st + NBUF - 1, (st + NBUF - 1) % NBUF);
     const char* kt = s_buf[st % NBUF];
-    const char* vt = s_buf[st % NBUF] + SH::kKBytes;
+    const char* vt = s_buf[st % NBUF] + SO::kKBytes;
     const uint32_t ent = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_list[st / SPB]);
     const uint32_t mine = (ent >> (kWaveQ * wave)) & ((1u << kWaveQ) - 1u);
     if (mine == 0u) continue;
