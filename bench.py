@@ -239,7 +239,74 @@ def bench_decode(args, torch, N, I):
     log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step ({timing}), {res['tokens_per_s']:.4g} tok/s, "
         f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: stream {p1 * 1e3:.1f} us "
         f"({gbs_cmp:.0f} GB/s), finish {ph[1] * 1e3:.1f} us")
+    if timing == "hip_graph" and not args.no_serving:
+        res["serving"] = bench_serving(args, torch, N, case, dims, cfg, T, max_len, copies, step)
     return case, res, T
+
+
+def append_bytes(case):
+    """Algorithmic HBM bytes of one nsa_compress_append call: both weight matrices and
+    position embeddings, the l tokens of every due block, the new compressed rows."""
+    wl, p = case.wl, case.p
+    w = 2 * p.l * (wl.d_k * wl.d_k + wl.d_v * wl.d_v) + 2 * p.l * (wl.d_k + wl.d_v)
+    due = sum(1 for L in case.seq_lens if int(L) >= p.l and (int(L) - p.l) % p.d == 0)
+    rows = due * wl.num_kv_heads
+    return w + rows * (p.l + 1) * 2 * (wl.d_k + wl.d_v), rows
+
+
+def bench_serving(args, torch, N, case, dims, cfg, T, max_len, copies, step):
+    """Serving step = nsa_compress_append (the block the new token completes) +
+    nsa_decode_fwd, replayed from a graph over the cache copies.  At the headline
+    lengths every sequence completes a block at this step (it happens every d steps),
+    so this is the step with the most append work."""
+    ws_a = N.new_workspace(N.nsa_compress_append_workspace_size(dims, cfg))
+
+    def append(i):
+        k, v, kc, vc = copies[i % len(copies)]
+        N.nsa_compress_append(dims, cfg, k, v, T["cu"], T["seq"], max_len, T["w_k"], T["pe_k"], T["w_v"], T["pe_v"],
+                              kc, vc, T["cuc"], ws_a)
+
+    for i in range(len(copies)):
+        append(i)
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(len(copies)):
+                append(i)
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, (args.steps + len(copies) - 1) // len(copies))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / (reps * len(copies))
+    # the append alone, eager, each call bracketed by events on its stream (queued behind a sleep)
+    n = 30
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda._sleep(int(2e7))
+    for i in range(n):
+        evs[i][0].record()
+        append(i)
+        evs[i][1].record()
+        step(i)  # the decode between appends evicts W from the caches, as in serving
+    torch.cuda.synchronize()
+    a_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes, rows = append_bytes(case)
+    res = dict(ms_per_step=ms_step, tokens_per_s=case.wl.batch / (ms_step * 1e-3), append_us=a_ms * 1e3,
+               append_bytes=nbytes, append_rows=rows, append_gbs=nbytes / (a_ms * 1e-3) / 1e9)
+    res["append_hbm_frac"] = res["append_gbs"] / HBM_PEAK_GBS
+    log(f"[bench] serving step (append + decode): {ms_step * 1e3:.1f} us; append {a_ms * 1e3:.1f} us "
+        f"({rows} blocks, {res['append_gbs']:.0f} GB/s)")
+    return res
 
 
 def prefill_flops(wl):
@@ -381,12 +448,16 @@ def kernels_only(args, torch, N, I):
     for _ in range(args.copies - 1):
         copies.append(tuple(x.clone() for x in copies[0]))
     torch.cuda.synchronize()
+    ws_a = N.new_workspace(N.nsa_compress_append_workspace_size(dims, cfg)) if args.serving else None
     for i in range(args.kernels_only):
         k, v, kc, vc = copies[i % len(copies)]
+        if args.serving:
+            N.nsa_compress_append(dims, cfg, k, v, T["cu"], T["seq"], max_len, T["w_k"], T["pe_k"], T["w_v"],
+                                  T["pe_v"], kc, vc, T["cuc"], ws_a)
         N.nsa_decode_fwd(dims, cfg, T["q"], k, v, kc, vc, T["seq"], T["cu"], T["cuc"], max_len, T["gates"], out,
                          None, ws)
     torch.cuda.synchronize()
-    log(f"[bench] {args.kernels_only} decode steps of {wl.name} done")
+    log(f"[bench] {args.kernels_only} {'serving' if args.serving else 'decode'} steps of {wl.name} done")
 
 
 def copy_calibration(torch, mib=256, reps=4):
@@ -430,11 +501,14 @@ def main():
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-serving", action="store_true", help="skip the append + decode serving-step timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
                     help="run N eager calls and exit (for profiler runs; no timing, no JSON line)")
     ap.add_argument("--prefill", action="store_true", help="with --kernels-only: prefill calls instead of decode")
+    ap.add_argument("--serving", action="store_true",
+                    help="with --kernels-only: nsa_compress_append before every decode call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy a few times and exit (profiler counter calibration)")
     args = ap.parse_args()
@@ -491,6 +565,14 @@ def main():
                         "wall_s_timed_region": dec["wall_s"]},
         "cpu_baseline": cpu,
     }
+    if dec.get("serving"):
+        sv = dec["serving"]
+        line["serving_step"] = {
+            "calls": "nsa_compress_append + nsa_decode_fwd", "ms_per_step": sv["ms_per_step"],
+            "tokens_per_s": sv["tokens_per_s"],
+            "append": {"kernels": "append_partial_kernel + append_reduce_kernel", "us": sv["append_us"],
+                       "blocks": sv["append_rows"], "algorithmic_bytes": sv["append_bytes"],
+                       "GB/s": sv["append_gbs"], "hbm_frac": sv["append_hbm_frac"]}}
     if pre:
         line["prefill"] = {"workload": pre["workload"], "ms": pre["ms"], "TFLOP/s": pre["tflops"],
                            "mfma_frac": pre["mfma_frac"], "flops": pre["flops"],

@@ -106,6 +106,37 @@ nsa_status_t nsa_compress_kv(const nsa_dims_t* dims, const nsa_config_t* cfg,
                              void* stream);
 
 /*
+ * nsa_compress_append — streaming compression for decode ("NSA: три ветви",
+ * compressed branch: a block of l tokens with stride d is complete once its
+ * last token exists, so decode gains one compressed key/value every d tokens).
+ * Call it after token t = seq_lens[b] - 1 has been written into k/v and before
+ * nsa_decode_fwd for that step: for every sequence b with t = i*d + l - 1
+ * (seq_lens[b] >= l, (seq_lens[b] - l) divisible by d) and i < ccap_b, block i
+ * of each KV head is computed exactly as nsa_compress_kv computes it and stored
+ * at compressed row i; every other row, and every other sequence, is left
+ * untouched.  The sum over the l*D inputs is taken in a different order than
+ * in nsa_compress_kv (fp32 chunk partials added in a fixed order), so the two
+ * may differ in the last bf16 bit; repeated calls give identical bits.
+ *
+ *   k, v, cu_seqlens, max_len, w_k, pe_k, w_v, pe_v, k_cmp, v_cmp, cu_cmp:
+ *               as for nsa_compress_kv.
+ *   seq_lens    int32 [B] on the device, required (the current lengths);
+ *               a length above cap_b is treated as having no due block.
+ *   workspace   at least nsa_compress_append_workspace_size bytes of device
+ *               memory (fp32 partial sums); contents on entry do not matter.
+ */
+nsa_status_t nsa_compress_append(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                                 const uint16_t* k, const uint16_t* v,
+                                 const int64_t* cu_seqlens, const int32_t* seq_lens, int64_t max_len,
+                                 const uint16_t* w_k, const uint16_t* pe_k,
+                                 const uint16_t* w_v, const uint16_t* pe_v,
+                                 uint16_t* k_cmp, uint16_t* v_cmp, const int64_t* cu_cmp,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes for nsa_compress_append (host-only): max(ceil(l*d_k/256),
+ * ceil(l*d_v/256)) * (batch*num_kv_heads rounded up to 64) * (d_k + d_v) * 4. */
+nsa_status_t nsa_compress_append_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                                                size_t* bytes);
+/*
  * nsa_decode_fwd — one decode step: each sequence b has one query at position
  * t = seq_lens[b] - 1 whose key/value are already in the cache.
  *

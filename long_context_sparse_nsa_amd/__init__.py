@@ -12,6 +12,8 @@ from ._abi import (  # noqa: F401
     make_config,
     make_dims,
     new_workspace,
+    nsa_compress_append,
+    nsa_compress_append_workspace_size,
     nsa_compress_kv,
     nsa_config_t,
     nsa_decode_fwd,

@@ -54,6 +54,9 @@ def lib_path() -> str:
 _VP = ctypes.c_void_p
 _SIGS = {
     "nsa_compress_kv": [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "nsa_compress_append": [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                            ctypes.c_size_t, _VP],
+    "nsa_compress_append_workspace_size": [_VP, _VP, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_decode_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP,
                        ctypes.c_size_t, _VP],
     "nsa_prefill_fwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -150,6 +153,26 @@ def nsa_compress_kv(dims, cfg, k, v, cu_seqlens, seq_lens, max_len, w_k, pe_k, w
                                _ptr(w_k, "w_k", 2), _ptr(pe_k, "pe_k", 2), _ptr(w_v, "w_v", 2), _ptr(pe_v, "pe_v", 2),
                                _ptr(k_cmp, "k_cmp", 2), _ptr(v_cmp, "v_cmp", 2), _ptr(cu_cmp, "cu_cmp", 8),
                                _stream(stream)))
+
+
+def nsa_compress_append_workspace_size(dims: nsa_dims_t, cfg: nsa_config_t) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().nsa_compress_append_workspace_size(ctypes.byref(dims), ctypes.byref(cfg),
+                                                             ctypes.byref(out)))
+    return int(out.value)
+
+
+def nsa_compress_append(dims, cfg, k, v, cu_seqlens, seq_lens, max_len, w_k, pe_k, w_v, pe_v, k_cmp, v_cmp, cu_cmp,
+                        workspace, stream=None):
+    lib = load_library()
+    B = dims.batch
+    _check(lib.nsa_compress_append(ctypes.byref(dims), ctypes.byref(cfg), _ptr(k, "k", 2), _ptr(v, "v", 2),
+                                   _ptr(cu_seqlens, "cu_seqlens", 8, B + 1), _ptr(seq_lens, "seq_lens", 4, B),
+                                   int(max_len), _ptr(w_k, "w_k", 2), _ptr(pe_k, "pe_k", 2), _ptr(w_v, "w_v", 2),
+                                   _ptr(pe_v, "pe_v", 2), _ptr(k_cmp, "k_cmp", 2), _ptr(v_cmp, "v_cmp", 2),
+                                   _ptr(cu_cmp, "cu_cmp", 8, B + 1), _ptr(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                   _stream(stream)))
 
 
 def nsa_decode_fwd(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, cu_seqlens, cu_cmp,

@@ -135,6 +135,14 @@ PrefillWs prefill_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T,
   return w;
 }
 
+// Streaming-compression workspace: fp32 chunk partials
+// [max(chunks_k, chunks_v)][B*Hkv rounded up to 64][d_k + d_v].
+size_t append_ws_bytes(const nsa_dims_t* dims, const nsa_config_t* cfg) {
+  const size_t rows_pad = ((size_t)dims->batch * dims->num_kv_heads + 63) / 64 * 64;
+  const int ck = nsa::append_chunks(cfg->l, dims->d_k), cv = nsa::append_chunks(cfg->l, dims->d_v);
+  return align256((size_t)(ck > cv ? ck : cv) * rows_pad * (dims->d_k + dims->d_v) * 4);
+}
+
 nsa_status_t hip_fail(hipError_t e, const char* what) {
   return fail(NSA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -225,6 +233,63 @@ nsa_status_t nsa_compress_kv(const nsa_dims_t* dims, const nsa_config_t* cfg, co
     hipError_t e = nsa::launch_compress(p, s);
     if (e != hipSuccess) return hip_fail(e, "compression launch");
   }
+  return ok();
+}
+
+nsa_status_t nsa_compress_append_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg, size_t* bytes) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
+  *bytes = append_ws_bytes(dims, cfg);
+  return ok();
+}
+
+nsa_status_t nsa_compress_append(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* k,
+                                 const uint16_t* v, const int64_t* cu_seqlens, const int32_t* seq_lens,
+                                 int64_t max_len, const uint16_t* w_k, const uint16_t* pe_k, const uint16_t* w_v,
+                                 const uint16_t* pe_v, uint16_t* k_cmp, uint16_t* v_cmp, const int64_t* cu_cmp,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!k || !v || !seq_lens || !w_k || !pe_k || !w_v || !pe_v || !k_cmp || !v_cmp)
+    return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if (max_len < 1) return fail(NSA_ERROR_INVALID_VALUE, "max_len must be >= 1");
+  const int64_t rows = (int64_t)dims->batch * dims->num_kv_heads;
+  if ((rows + 63) / 64 > 65535 || rows * (dims->d_k + dims->d_v) / 4 * 8 > (int64_t)INT32_MAX)
+    return fail(NSA_ERROR_UNSUPPORTED, "batch * kv_heads too large");
+  if (nsa::append_chunks(cfg->l, dims->d_k) > 96 || nsa::append_chunks(cfg->l, dims->d_v) > 96)
+    return fail(NSA_ERROR_UNSUPPORTED, "l * d_k above 96 * 256");
+  const size_t need = append_ws_bytes(dims, cfg);
+  if (!workspace || workspace_bytes < need)
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  nsa::AppendParams p{};
+  p.B = dims->batch;
+  p.H = dims->num_kv_heads;
+  p.DK = dims->d_k;
+  p.DV = dims->d_v;
+  p.l = cfg->l;
+  p.d = cfg->d;
+  p.k = k;
+  p.v = v;
+  p.cu = cu_seqlens;
+  p.seq_lens = seq_lens;
+  p.cap = max_len;
+  p.wk = w_k;
+  p.pek = pe_k;
+  p.wv = w_v;
+  p.pev = pe_v;
+  p.kc = k_cmp;
+  p.vc = v_cmp;
+  p.cuc = cu_cmp;
+  p.ccap = n_compressed(max_len, cfg->l, cfg->d);
+  p.part = static_cast<float*>(workspace);
+  p.rows_pad = (int)((rows + 63) / 64 * 64);
+  p.nck_k = nsa::append_chunks(cfg->l, dims->d_k);
+  p.nck_v = nsa::append_chunks(cfg->l, dims->d_v);
+  if (p.ccap == 0) return ok();  // no sequence can hold a complete block
+  hipError_t e = nsa::launch_append(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
   return ok();
 }
 

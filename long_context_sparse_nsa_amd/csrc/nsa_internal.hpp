@@ -98,6 +98,29 @@ struct CompressParams {
   int max_nc;                        // launch bound on blocks per sequence
 };
 
+// Streaming compression (one new block per sequence and KV head when due).
+struct AppendParams {
+  int B, H, DK, DV, l, d;
+  const uint16_t* k;                 // raw caches (layout as nsa_compress_kv)
+  const uint16_t* v;
+  const int64_t* cu;                 // or null
+  const int32_t* seq_lens;           // current lengths (the newest token is seq_lens[b] - 1)
+  int64_t cap;                       // uniform capacity when cu == null
+  const uint16_t* wk;                // [l*DK, DK]
+  const uint16_t* pek;               // [l, DK]
+  const uint16_t* wv;                // [l*DV, DV]
+  const uint16_t* pev;               // [l, DV]
+  uint16_t* kc;                      // compressed caches
+  uint16_t* vc;
+  const int64_t* cuc;                // or null
+  int64_t ccap;                      // uniform compressed capacity when cuc == null
+  float* part;                       // fp32 partials [max(nck_k, nck_v)][rows_pad][DK + DV]
+  int rows_pad;                      // B*H rounded up to a multiple of 64
+  int nck_k, nck_v;                  // 256-element chunks of l*DK and l*DV
+};
+int append_chunks(int l, int D);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
 DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len);
 
 // Optional events recorded between the kernels of one call (null = none).

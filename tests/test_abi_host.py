@@ -129,6 +129,27 @@ def test_prefill_rejects_half_given_cache_and_missing_weights():
     assert st == A.NSA_ERROR_UNSUPPORTED
 
 
+def test_append_workspace_size_and_validation():
+    # fp32 partials: max(ceil(32*192/256), ceil(32*128/256)) = 24 chunks x 64 padded rows x 320 channels
+    assert N.nsa_compress_append_workspace_size(_dims(), _cfg()) == 24 * 64 * 320 * 4
+    assert N.nsa_compress_append_workspace_size(_dims(batch=17), _cfg()) == 24 * 128 * 320 * 4
+    lib = A.load_library()
+    dims, cfg = _dims(), _cfg()
+    f = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    need = N.nsa_compress_append_workspace_size(dims, cfg)
+
+    def call(seq_lens, ws, ws_bytes, max_len=65536):
+        return lib.nsa_compress_append(ctypes.byref(dims), ctypes.byref(cfg), f, f, None, seq_lens, max_len, f, f, f,
+                                       f, f, f, None, ws, ws_bytes, None)
+    assert call(None, f, need) == A.NSA_ERROR_INVALID_VALUE and "NULL" in N.nsa_last_error()
+    assert call(f, f, need - 1) == A.NSA_ERROR_WORKSPACE
+    assert call(f, None, need) == A.NSA_ERROR_WORKSPACE
+    assert call(f, f, need, max_len=0) == A.NSA_ERROR_INVALID_VALUE
+    bad = _cfg(l_sel=48)
+    assert lib.nsa_compress_append(ctypes.byref(dims), ctypes.byref(bad), f, f, None, f, 100, f, f, f, f, f, f, None,
+                                   f, need, None) == A.NSA_ERROR_UNSUPPORTED
+
+
 def test_null_dims_and_config():
     lib = A.load_library()
     out = ctypes.c_size_t(0)

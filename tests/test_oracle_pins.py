@@ -137,6 +137,31 @@ def test_nc_closed_form():
     assert O.n_compressed(31, 32, 16) == 0 and O.n_compressed(32, 32, 16) == 1
 
 
+@pytest.mark.parametrize("l,d", [(32, 16), (8, 8), (6, 2)])
+def test_one_block_completes_every_d_tokens(l, d):
+    """Growing a sequence one token at a time adds exactly one compressed block at
+    t = i*d + l - 1 (the block ending at the new token) and none otherwise; every
+    earlier block is unchanged (a block reads only its own l tokens).  This is the
+    rule the streaming append follows, checked against the batch definition."""
+    rng = np.random.default_rng(7)
+    D = 4
+    K = rng.standard_normal((120, D))
+    W = rng.standard_normal((l * D, D))
+    PE = rng.standard_normal((l, D))
+    prev = O.compress(K[:0], W, PE, l, d, round_bf16=False)
+    for L in range(1, 121):
+        cur = O.compress(K[:L], W, PE, l, d, round_bf16=False)
+        t = L - 1
+        due = t >= l - 1 and (t - (l - 1)) % d == 0
+        assert cur.shape[0] == prev.shape[0] + (1 if due else 0)
+        np.testing.assert_allclose(cur[:prev.shape[0]], prev, rtol=1e-12, atol=1e-12)  # BLAS blocking may differ
+        if due:
+            i = (t - (l - 1)) // d
+            assert cur.shape[0] == i + 1
+            np.testing.assert_allclose(cur[i], ((K[t - l + 1:t + 1] + PE).reshape(-1)) @ W, rtol=1e-12)
+        prev = cur
+
+
 # ---------------------------------------------------------------- gating
 
 def test_gates_isolate_and_are_linear():
