@@ -239,9 +239,47 @@ def bench_decode(args, torch, N, I):
     log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step ({timing}), {res['tokens_per_s']:.4g} tok/s, "
         f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: stream {p1 * 1e3:.1f} us "
         f"({gbs_cmp:.0f} GB/s), finish {ph[1] * 1e3:.1f} us")
+    if timing == "hip_graph":
+        res["gate_network_ms_per_step"] = bench_gate_network(args, torch, N, case, dims, cfg, T, max_len, copies,
+                                                             out, sel, ws)
+        log(f"[bench] decode step with the gate network: {res['gate_network_ms_per_step'] * 1e3:.1f} us")
     if timing == "hip_graph" and not args.no_serving:
         res["serving"] = bench_serving(args, torch, N, case, dims, cfg, T, max_len, copies, step)
     return case, res, T
+
+
+def bench_gate_network(args, torch, N, case, dims, cfg, T, max_len, copies, out, sel, ws):
+    """Decode step with the gates computed in the selection kernel from each query head
+    (gate network weights instead of gate values), graph-replayed like the headline."""
+    wg = torch.from_numpy(np.ascontiguousarray(case.w_gate).view(np.int16)).view(torch.bfloat16).cuda()
+    bgt = torch.from_numpy(case.b_gate).cuda()
+
+    def step(i):
+        k, v, kc, vc = copies[i % len(copies)]
+        N.nsa_decode_fwd(dims, cfg, T["q"], k, v, kc, vc, T["seq"], T["cu"], T["cuc"], max_len, None, out, sel, ws,
+                         w_gate=wg, b_gate=bgt)
+
+    for i in range(len(copies)):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(len(copies)):
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, (args.steps + len(copies) - 1) // len(copies))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / (reps * len(copies))
 
 
 def append_bytes(case):
@@ -378,6 +416,23 @@ def bench_prefill(args, torch, N, I):
                cmp_win_tflops=(f["cmp"] + f["win"]) / (ph[1] * 1e-3) / 1e12,
                sel_tflops=f["slc"] / (ph[2] * 1e-3) / 1e12)
     res["sel_mfma_frac"] = res["sel_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    # the same call with the gates computed in the kernels by the gate network
+    wg = dev(case.w_gate)
+    bgt = torch.from_numpy(case.b_gate).cuda()
+
+    def run_gn():
+        N.nsa_prefill_fwd(dims, cfg, wl.seq_len, q, k, v, None, None, wk, pk, wv, pv, None, out, None, ws,
+                          w_gate=wg, b_gate=bgt)
+
+    run_gn()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        run_gn()
+    ev1.record()
+    torch.cuda.synchronize()
+    res["gate_network_ms"] = ev0.elapsed_time(ev1) / reps
+    log(f"[bench] prefill with the gate network: {res['gate_network_ms']:.2f} ms")
     log(f"[bench] prefill {wl.name}: {ms:.2f} ms, {res['tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% of bf16 "
         f"peak); compress {ph[0]:.3f} ms, cmp+win+top-n {ph[1]:.3f} ms ({res['cmp_win_tflops']:.0f} TFLOP/s), "
         f"selected {ph[2]:.3f} ms ({res['sel_tflops']:.0f} TFLOP/s, {100 * res['sel_mfma_frac']:.1f}%)")
@@ -565,6 +620,10 @@ def main():
                         "wall_s_timed_region": dec["wall_s"]},
         "cpu_baseline": cpu,
     }
+    line["gate_network"] = {
+        "reading": "gate[h, c] = sigmoid(w_gate[h, c] . q[h] + b_gate[h, c]), computed in the kernels that apply it",
+        "decode_ms_per_step": dec.get("gate_network_ms_per_step"),
+        "prefill_ms": pre.get("gate_network_ms") if pre else None}
     if dec.get("serving"):
         sv = dec["serving"]
         line["serving_step"] = {

@@ -148,7 +148,18 @@ nsa_status_t nsa_compress_append_workspace_size(const nsa_dims_t* dims, const ns
  *                         complete blocks of each sequence.
  *   seq_lens  int32 [B] on the device, 1 <= seq_lens[b] <= cap_b.
  *   max_seq_len  host upper bound of seq_lens (sizes the launch).
- *   gates     float32 [B, Hq, 3] = (g_cmp, g_slc, g_win), used as given.
+ *   gates     float32 [B, Hq, 3] = (g_cmp, g_slc, g_win), used as given; or
+ *             NULL when the gate network computes them (see w_gate).
+ *   w_gate, b_gate  the gate network, or both NULL when gates are given.  Read
+ *             as one linear layer and a sigmoid on each query head's vector
+ *             ("Native Sparse Attention" lesson, "Build it" step 5: a small MLP
+ *             on the query yields the three gate weights; "NSA: три ветви": the
+ *             gates lie in [0, 1], from a small network with a sigmoid):
+ *               gate[b, h, c] = sigmoid(w_gate[h, c, :] . q[b, h, :] + b_gate[h, c])
+ *             w_gate bf16 [Hq, 3, d_k] (c = cmp, slc, win); b_gate float32
+ *             [Hq, 3] or NULL (no bias).  Computed in fp32 inside the kernels
+ *             that apply the gates.  Giving both gates and w_gate/b_gate is
+ *             NSA_ERROR_INVALID_VALUE.
  *   out       bf16 [B, Hq, d_v].
  *   sel_idx_out  nullable int32 [B, Hkv, n_sel]: the selected block ids,
  *             ascending, padded with -1 when fewer than n_sel blocks exist.
@@ -164,7 +175,8 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg,
                             const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                             const uint16_t* k_cmp_cache, const uint16_t* v_cmp_cache,
                             const int32_t* seq_lens, const int64_t* cu_seqlens, const int64_t* cu_cmp,
-                            int64_t max_seq_len, const float* gates, uint16_t* out,
+                            int64_t max_seq_len, const float* gates,
+                            const uint16_t* w_gate, const float* b_gate, uint16_t* out,
                             int32_t* sel_idx_out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
@@ -178,7 +190,9 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg,
  *   k_cmp, v_cmp  bf16 [B, Hkv, floor((T-l)/d)+1, D] precomputed compressed
  *          cache, or both NULL to compress in the call from (w_k, pe_k, w_v,
  *          pe_v) into the workspace (the weights are ignored otherwise).
- *   gates  float32 [B, T, Hq, 3]
+ *   gates  float32 [B, T, Hq, 3], or NULL with the gate network
+ *   w_gate, b_gate  the gate network as for nsa_decode_fwd (q is [B, T, Hq, d_k]
+ *          here, and the gates of position t come from q[b, t, h, :])
  *   out    bf16 [B, T, Hq, d_v]
  *   sel_idx_out  nullable int32 [B, T, Hkv, n_sel], ascending, -1 padded.
  */
@@ -187,7 +201,8 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
                              const uint16_t* k_cmp, const uint16_t* v_cmp,
                              const uint16_t* w_k, const uint16_t* pe_k,
                              const uint16_t* w_v, const uint16_t* pe_v,
-                             const float* gates, uint16_t* out, int32_t* sel_idx_out,
+                             const float* gates, const uint16_t* w_gate, const float* b_gate,
+                             uint16_t* out, int32_t* sel_idx_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes needed by nsa_decode_fwd / nsa_prefill_fwd for these sizes

@@ -57,10 +57,10 @@ _SIGS = {
     "nsa_compress_append": [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                             ctypes.c_size_t, _VP],
     "nsa_compress_append_workspace_size": [_VP, _VP, ctypes.POINTER(ctypes.c_size_t)],
-    "nsa_decode_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP,
-                       ctypes.c_size_t, _VP],
+    "nsa_decode_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP,
+                       _VP, ctypes.c_size_t, _VP],
     "nsa_prefill_fwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                        _VP, ctypes.c_size_t, _VP],
+                        _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_set_phase_events": [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32],
@@ -176,7 +176,8 @@ def nsa_compress_append(dims, cfg, k, v, cu_seqlens, seq_lens, max_len, w_k, pe_
 
 
 def nsa_decode_fwd(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, cu_seqlens, cu_cmp,
-                   max_seq_len, gates, out, sel_idx_out, workspace, stream=None):
+                   max_seq_len, gates, out, sel_idx_out, workspace, stream=None, w_gate=None, b_gate=None):
+    """gates=None with w_gate (and optionally b_gate) selects the in-kernel gate network."""
     lib = load_library()
     B, Hq, H = dims.batch, dims.num_q_heads, dims.num_kv_heads
     _check(lib.nsa_decode_fwd(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q, "q", 2, B * Hq * dims.d_k),
@@ -184,7 +185,8 @@ def nsa_decode_fwd(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq
                               _ptr(k_cmp_cache, "k_cmp_cache", 2), _ptr(v_cmp_cache, "v_cmp_cache", 2),
                               _ptr(seq_lens, "seq_lens", 4, B), _ptr(cu_seqlens, "cu_seqlens", 8, B + 1),
                               _ptr(cu_cmp, "cu_cmp", 8, B + 1), int(max_seq_len),
-                              _ptr(gates, "gates", 4, B * Hq * 3), _ptr(out, "out", 2, B * Hq * dims.d_v),
+                              _ptr(gates, "gates", 4, B * Hq * 3), _ptr(w_gate, "w_gate", 2, Hq * 3 * dims.d_k),
+                              _ptr(b_gate, "b_gate", 4, Hq * 3), _ptr(out, "out", 2, B * Hq * dims.d_v),
                               _ptr(sel_idx_out, "sel_idx_out", 4, B * H * cfg.n_sel),
                               _ptr(workspace, "workspace"),
                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
@@ -192,14 +194,16 @@ def nsa_decode_fwd(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq
 
 
 def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, pe_v, gates, out, sel_idx_out,
-                    workspace, stream=None):
+                    workspace, stream=None, w_gate=None, b_gate=None):
+    """gates=None with w_gate (and optionally b_gate) selects the in-kernel gate network."""
     lib = load_library()
     B, Hq, H, T = dims.batch, dims.num_q_heads, dims.num_kv_heads, int(seq_len)
     _check(lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), T, _ptr(q, "q", 2, B * T * Hq * dims.d_k),
                                _ptr(k, "k", 2, B * H * T * dims.d_k), _ptr(v, "v", 2, B * H * T * dims.d_v),
                                _ptr(k_cmp, "k_cmp", 2), _ptr(v_cmp, "v_cmp", 2),
                                _ptr(w_k, "w_k", 2), _ptr(pe_k, "pe_k", 2), _ptr(w_v, "w_v", 2), _ptr(pe_v, "pe_v", 2),
-                               _ptr(gates, "gates", 4, B * T * Hq * 3), _ptr(out, "out", 2, B * T * Hq * dims.d_v),
+                               _ptr(gates, "gates", 4, B * T * Hq * 3), _ptr(w_gate, "w_gate", 2, Hq * 3 * dims.d_k),
+                               _ptr(b_gate, "b_gate", 4, Hq * 3), _ptr(out, "out", 2, B * T * Hq * dims.d_v),
                                _ptr(sel_idx_out, "sel_idx_out", 4, B * T * H * cfg.n_sel),
                                _ptr(workspace, "workspace"),
                                workspace.numel() * workspace.element_size() if workspace is not None else 0,

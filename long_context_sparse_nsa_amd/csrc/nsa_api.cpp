@@ -117,6 +117,14 @@ nsa_status_t check_prefill_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Exactly one gate source: given values, or the gate network's weights (bias optional).
+nsa_status_t check_gates(const float* gates, const uint16_t* w_gate, const float* b_gate) {
+  if (!gates && !w_gate) return fail(NSA_ERROR_INVALID_VALUE, "give gates or the gate network's w_gate");
+  if (gates && (w_gate || b_gate))
+    return fail(NSA_ERROR_INVALID_VALUE, "gates and the gate network (w_gate / b_gate) are exclusive");
+  return NSA_SUCCESS;
+}
+
 // Prefill workspace: [compressed K | compressed V] (in-call compression only),
 // then the fp32 accumulator [B, T, Hq, d_v], then the selection buffer
 // [B, T, Hkv, n_sel] (always reserved; unused when the caller passes sel_idx_out).
@@ -296,12 +304,14 @@ nsa_status_t nsa_compress_append(const nsa_dims_t* dims, const nsa_config_t* cfg
 nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* q,
                             const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_cmp_cache,
                             const uint16_t* v_cmp_cache, const int32_t* seq_lens, const int64_t* cu_seqlens,
-                            const int64_t* cu_cmp, int64_t max_seq_len, const float* gates, uint16_t* out,
+                            const int64_t* cu_cmp, int64_t max_seq_len, const float* gates,
+                            const uint16_t* w_gate, const float* b_gate, uint16_t* out,
                             int32_t* sel_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
   nsa_status_t st = check_common(dims, cfg, true);
   if (st != NSA_SUCCESS) return st;
-  if (!q || !k_cache || !v_cache || !k_cmp_cache || !v_cmp_cache || !seq_lens || !gates || !out)
+  if (!q || !k_cache || !v_cache || !k_cmp_cache || !v_cmp_cache || !seq_lens || !out)
     return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if ((st = check_gates(gates, w_gate, b_gate)) != NSA_SUCCESS) return st;
   if ((st = check_decode_sizes(dims, cfg, max_seq_len)) != NSA_SUCCESS) return st;
   const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
                                                    cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
@@ -333,6 +343,8 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   p.cap = max_seq_len;
   p.ccap = n_compressed(max_seq_len, cfg->l, cfg->d);
   p.gates = gates;
+  p.wgate = w_gate;
+  p.bgate = b_gate;
   p.out = out;
   p.sel_out = sel_idx_out;
   p.m1 = reinterpret_cast<float*>(ws + lay.off_m1);
@@ -358,11 +370,12 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
 nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len, const uint16_t* q,
                              const uint16_t* k, const uint16_t* v, const uint16_t* k_cmp, const uint16_t* v_cmp,
                              const uint16_t* w_k, const uint16_t* pe_k, const uint16_t* w_v, const uint16_t* pe_v,
-                             const float* gates, uint16_t* out, int32_t* sel_idx_out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             const float* gates, const uint16_t* w_gate, const float* b_gate, uint16_t* out,
+                             int32_t* sel_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
   nsa_status_t st = check_common(dims, cfg, true);
   if (st != NSA_SUCCESS) return st;
-  if (!q || !k || !v || !gates || !out) return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if (!q || !k || !v || !out) return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if ((st = check_gates(gates, w_gate, b_gate)) != NSA_SUCCESS) return st;
   if ((k_cmp == nullptr) != (v_cmp == nullptr))
     return fail(NSA_ERROR_INVALID_VALUE, "k_cmp and v_cmp must both be given or both be NULL");
   const bool compress = k_cmp == nullptr;
@@ -412,6 +425,8 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.kc = k_cmp;
   p.vc = v_cmp;
   p.gates = gates;
+  p.wgate = w_gate;
+  p.bgate = b_gate;
   p.out = out;
   p.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t*>(ws + lay.off_sel);
   p.acc = reinterpret_cast<float*>(ws + lay.off_acc);

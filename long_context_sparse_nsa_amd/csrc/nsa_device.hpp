@@ -60,6 +60,35 @@ __device__ __forceinline__ u32x2_t ld8(const uint16_t* p) {
   return *reinterpret_cast<const u32x2_t*>(p);
 }
 
+// Gate network (a sigmoid of one linear layer of a query head): the part of the
+// dot product of the bf16 query row q and weight row w (both DK long) that lane
+// part `part` of four covers, elements [part*DK/4, (part+1)*DK/4).  The caller
+// adds the four parts in a fixed order.
+template <int DK>
+__device__ __forceinline__ float gate_dot_quarter(const uint16_t* q, const uint16_t* w, int part) {
+  constexpr int E = DK / 4;
+  static_assert(E % 8 == 0, "a quarter of the row must be whole 16-byte loads");
+  u32x4_t a[E / 8], c[E / 8];
+#pragma unroll
+  for (int i = 0; i < E / 8; ++i) {
+    a[i] = *reinterpret_cast<const u32x4_t*>(q + part * E + 8 * i);
+    c[i] = *reinterpret_cast<const u32x4_t*>(w + part * E + 8 * i);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < E / 8; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s = fmaf(__uint_as_float(a[i][u] << 16), __uint_as_float(c[i][u] << 16), s);
+      s = fmaf(__uint_as_float(a[i][u] & 0xFFFF0000u), __uint_as_float(c[i][u] & 0xFFFF0000u), s);
+    }
+  return s;
+}
+// Logistic sigmoid 1 / (1 + e^-z) with the hardware base-2 exponential.
+__device__ __forceinline__ float gate_sigmoid(float z) {
+  return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
 // Cross-lane reductions over the four lane groups (lanes lr, lr+16, lr+32, lr+48).
 __device__ __forceinline__ float max_over_groups(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));

@@ -39,7 +39,9 @@ struct DecodeParams {
   const int64_t* cuc;                // [B+1] or null
   int64_t cap;                       // uniform capacity when cu == null
   int64_t ccap;                      // uniform compressed capacity when cuc == null
-  const float* gates;                // [B, Hq, 3]
+  const float* gates;                // [B, Hq, 3], or null with the gate network below
+  const uint16_t* wgate;             // gate network [Hq, 3, DK] (null: gates are given)
+  const float* bgate;                // [Hq, 3] or null
   uint16_t* out;                     // [B, Hq, DV]
   int32_t* sel_out;                  // [B, H, n] or null
   // workspace (contents on entry are irrelevant)
@@ -78,7 +80,9 @@ struct PrefillParams {
   const uint16_t* v;
   const uint16_t* kc;                // [B, H, nc, DK]
   const uint16_t* vc;
-  const float* gates;                // [B, T, Hq, 3]
+  const float* gates;                // [B, T, Hq, 3], or null with the gate network below
+  const uint16_t* wgate;             // gate network [Hq, 3, DK] (null: gates are given)
+  const float* bgate;                // [Hq, 3] or null
   uint16_t* out;                     // [B, T, Hq, DV]
   int32_t* sel;                      // [B, T, H, n] selected block ids (caller's or workspace)
   float* acc;                        // [B, T, Hq, DV] workspace: g_win o_win + g_cmp o_cmp

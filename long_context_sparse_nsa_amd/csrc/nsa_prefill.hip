@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   constexpr int NLD_K = SO::kMinCopiesK, NLD_KV = SO::kMinCopiesKV;
   __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][SH::kBuf];
   __shared__ float s_score[kTileQ][MAXB];
+  __shared__ float s_gnet[kTileQ][2][16];  // gate network: (g_cmp, g_win) per position and head
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,8 +240,26 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     lsum[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     mref[q] = kNegBig;
   }
+  // gate network (when given): this lane's head lr, both positions, branches cmp
+  // and win, computed before the pipeline starts and kept in LDS (this wave's rows)
+  if (p.wgate) {
+    const int hq = g * p.G + (lr < p.G ? lr : 0);
+#pragma unroll
+    for (int q = 0; q < kWaveQ; ++q) {
+      const int tt = act[q] ? tq[q] : T - 1;
+      const uint16_t* qrow = p.q + (((int64_t)b * T + tt) * p.Hq + hq) * DK;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int br = 2 * c;
+        const float z = sum_over_groups_swap(gate_dot_quarter<DK>(qrow, p.wgate + ((size_t)hq * 3 + br) * DK, lg));
+        if (lg == 0) s_gnet[kWaveQ * wave + q][c][lr] = gate_sigmoid(z + (p.bgate ? p.bgate[hq * 3 + br] : 0.f));
+      }
+    }
+  }
   auto gate = [&](int q, int br) -> float {
-    return (act[q] && lr < p.G) ? p.gates[(((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * 3 + br] : 0.f;
+    if (!act[q] || lr >= p.G) return 0.f;
+    if (p.wgate) return s_gnet[kWaveQ * wave + q][br == 2 ? 1 : 0][lr];
+    return p.gates[(((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * 3 + br];
   };
   const float sc = p.scale_log2;
   const int qd = p.l / p.d, rd = p.lsel / p.d;  // key and block lengths in stride units
@@ -519,6 +538,21 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   const uint16_t* kraw = p.k + bg * T * DK;
   const uint16_t* vraw = p.v + bg * T * DV;
 
+  // ---- g_slc from the gate network (when given) for this lane's head lr and
+  // both of its positions, before any other load
+  float gsl[kWaveQ];
+  if (p.wgate) {
+    const int hq = g * p.G + (lr < p.G ? lr : 0);
+    const uint16_t* wrow = p.wgate + ((size_t)hq * 3 + 1) * DK;
+#pragma unroll
+    for (int q = 0; q < kWaveQ; ++q) {
+      const int tt = min(t0 + kWaveQ * wave + q, T - 1);
+      const float z = sum_over_groups_swap(
+          gate_dot_quarter<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + hq) * DK, wrow, lg));
+      gsl[q] = gate_sigmoid(z + (p.bgate ? p.bgate[hq * 3 + 1] : 0.f));
+    }
+  }
+
   // ---- union of the tile's selections
   for (int j = tid; j <= Jtile; j += kThreads) s_mask[j] = 0u;
   __syncthreads();
@@ -658,7 +692,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     const float lt = __shfl(lsum[q][0], lr);
     if (!act[q] || lr >= p.G) continue;
     const int64_t hrow = ((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr;
-    const float f = lt > 0.f ? p.gates[hrow * 3 + 1] / lt : 0.f;
+    const float f = lt > 0.f ? (p.wgate ? gsl[q] : p.gates[hrow * 3 + 1]) / lt : 0.f;
     const float* src = p.acc + hrow * DV;
     uint16_t* dst = p.out + hrow * DV;
 #pragma unroll

@@ -19,6 +19,8 @@ Draw order for every workload (one ``numpy.random.default_rng(seed)`` stream):
   4. W_k, PE_k, W_v, PE_v       W ~ N(0, 1/(l*D)), PE ~ N(0, 0.02^2)
   5. needle block positions     uniform without replacement over non-forced blocks
   6. needle noise               keys of needle tokens = scale*(sqrt(dk)*u + 0.1*eps)
+  7. gate-network weights       W_gate ~ N(0, 1/dk)/scale (unit-variance pre-activations),
+                                b_gate ~ N(0, 0.5^2); used only by cases with gate_net set
 """
 from __future__ import annotations
 
@@ -126,6 +128,9 @@ class Case:
     seq_lens: Optional[np.ndarray] = None     # decode: int32 [B], includes the current token
     cu_seqlens: Optional[np.ndarray] = None   # decode: int64 [B+1] token-capacity offsets
     needle_blocks: list = field(default_factory=list)  # per (b, g): list of l'-block ids
+    w_gate: Optional[np.ndarray] = None       # gate network weights [Hq, 3, dk] (bf16 bits)
+    b_gate: Optional[np.ndarray] = None       # gate network bias [Hq, 3] (float32)
+    gate_net: bool = False                    # True: the gates come from the gate network
     fp32: Optional[dict] = None               # unrounded float32 copies (small workloads only)
 
     @property
@@ -240,9 +245,14 @@ def generate(wl: Workload, seed: int, keep_fp32: bool = False) -> Case:
     if keep_fp32:
         fp32 = dict(q=q.copy(), k=k.copy(), v=v.copy(), w_k=w_k.copy(), pe_k=pe_k.copy(),
                     w_v=w_v.copy(), pe_v=pe_v.copy())
+    # 7. gate-network weights (drawn last, so every earlier value is unchanged):
+    #    w_gate [Hq, 3, dk] ~ N(0, 1/dk) / scale, b_gate [Hq, 3] ~ N(0, 0.5^2)
+    w_gate = rng.standard_normal(size=(Hq, 3, dk), dtype=np.float32) / np.float32(np.sqrt(dk) * s)
+    b_gate = (rng.standard_normal(size=(Hq, 3), dtype=np.float32) * np.float32(0.5))
+
     case = Case(wl=wl, seed=seed, q=_round(q), k=_round(k), v=_round(v), gates=gates,
                 w_k=_round(w_k), pe_k=_round(pe_k), w_v=_round(w_v), pe_v=_round(pe_v),
-                needle_blocks=needle_blocks, fp32=fp32)
+                needle_blocks=needle_blocks, fp32=fp32, w_gate=_round(w_gate), b_gate=b_gate)
     if wl.kind == "decode":
         case.seq_lens = lens.astype(np.int32)
         case.cu_seqlens = cu

@@ -39,7 +39,8 @@ What is computed for one query position t and one KV group g (G query heads):
                 [FLI practice spec of sliding_window_mask].
   combine       out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win with the gate values
                 as given (they need not sum to one) [FLI output equation; LES
-                "Concept"].
+                "Concept"], or computed from each head's query by the gate
+                network: sigmoid of one linear layer [LES "Build it" step 5].
   attention     scale 1/sqrt(d_k), forbidden pairs excluded, row-max-subtracted
                 softmax [FLI practice spec of sparse_attention].
 """
@@ -163,6 +164,25 @@ def select_blocks(S: np.ndarray, J: int, n: int, n_local: int, force_initial: in
     return sorted(F + rest[:n - len(F)])
 
 
+# --------------------------------------------------------------------------- gate network
+
+def gate_network(qg: np.ndarray, Wg: np.ndarray, bg: Optional[np.ndarray]) -> np.ndarray:
+    """Branch gates of G query heads from their query vectors.
+
+    qg [G, dk]; Wg [G, 3, dk] (head h's three weight rows, in the order cmp,
+    slc, win); bg [G, 3] or None.  gate[h, c] = sigmoid(Wg[h, c] . qg[h] + bg[h, c]).
+    [LES "Build it" step 5: a small MLP on the query yields the three gate
+    weights; FLI "NSA: три ветви": gates in [0, 1] from a small network with a
+    sigmoid.]  The small network is read as one linear layer with a bias.
+    """
+    q = np.asarray(qg, dtype=np.float64)
+    W = np.asarray(Wg, dtype=np.float64)
+    z = np.einsum("hck,hk->hc", W, q)
+    if bg is not None:
+        z = z + np.asarray(bg, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 # --------------------------------------------------------------------------- one query
 
 @dataclass
@@ -213,6 +233,16 @@ def _widen(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def _group_gates(case, qg, g: int, G: int, given):
+    """The gates of one position's group heads: computed by the gate network when
+    the case says so (case.gate_net), else the given values."""
+    if getattr(case, "gate_net", False):
+        Wg = _widen(case.w_gate[g * G:(g + 1) * G])
+        bg = None if case.b_gate is None else np.asarray(case.b_gate[g * G:(g + 1) * G], dtype=np.float64)
+        return gate_network(qg, Wg, bg)
+    return np.asarray(given, dtype=np.float64)
+
+
 def compress_group(case, b: int, g: int, upto: Optional[int] = None):
     """Oracle compressed cache (bf16-rounded, float64) of sequence b, KV head g."""
     p = case.wl.params
@@ -242,7 +272,7 @@ def decode_group(case, b: int, g: int, Kc=None, Vc=None, override_idx=None) -> Q
         Kc, Vc = Kc_o, Vc_o
     t = int(case.seq_lens[b]) - 1
     qg = _widen(case.q[b, g * G:(g + 1) * G])
-    gates = np.asarray(case.gates[b, g * G:(g + 1) * G], dtype=np.float64)
+    gates = _group_gates(case, qg, g, G, case.gates[b, g * G:(g + 1) * G])
     return nsa_query(qg, K, V, Kc, Vc, t, gates, p.l, p.d, p.l_sel, p.n_sel, p.n_local,
                      p.force_initial, p.w, override_idx=override_idx)
 
@@ -257,7 +287,7 @@ def prefill_rows(case, b: int, g: int, rows: Sequence[int], K=None, V=None, Kc=N
     res = []
     for r, t in enumerate(rows):
         qg = _widen(case.q[b, t, g * G:(g + 1) * G])
-        gates = np.asarray(case.gates[b, t, g * G:(g + 1) * G], dtype=np.float64)
+        gates = _group_gates(case, qg, g, G, case.gates[b, t, g * G:(g + 1) * G])
         oi = None if override_idx is None else override_idx[r]
         res.append(nsa_query(qg, K, V, Kc, Vc, int(t), gates, p.l, p.d, p.l_sel, p.n_sel,
                              p.n_local, p.force_initial, p.w, override_idx=oi))

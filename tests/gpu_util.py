@@ -94,21 +94,32 @@ def run_decode(case, kc_bits=None, vc_bits=None, gates=None, ws=None):
             kc_bits = np.zeros((1, wl.d_k), np.uint16)
             vc_bits = np.zeros((1, wl.d_v), np.uint16)
         kc, vc = dev_bits(kc_bits), dev_bits(vc_bits)
-    g = torch.from_numpy(np.ascontiguousarray(case.gates if gates is None else gates, dtype=np.float32)).cuda()
+    g, wg, bgt = gate_args(case, gates)
     out = torch.empty((wl.batch, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
     sel = torch.full((wl.batch, wl.num_kv_heads, cfg.n_sel), -7, dtype=torch.int32, device="cuda")
     if ws is None:
         ws = N.new_workspace(N.nsa_decode_workspace_size(dims, cfg, max_len))
-    N.nsa_decode_fwd(dims, cfg, q, k, v, kc, vc, seq, cu, cu_c, max_len, g, out, sel, ws)
+    N.nsa_decode_fwd(dims, cfg, q, k, v, kc, vc, seq, cu, cu_c, max_len, g, out, sel, ws, w_gate=wg, b_gate=bgt)
     torch.cuda.synchronize()
     return bits_to_f64(host_bits(out)), sel.cpu().numpy(), (kc, vc)
+
+
+def gate_args(case, gates=None):
+    """(gates, w_gate, b_gate) device arguments: the gate network's weights when the
+    case sets gate_net, else the gate values."""
+    if getattr(case, "gate_net", False):
+        bgt = torch.from_numpy(np.ascontiguousarray(case.b_gate, dtype=np.float32)).cuda() \
+            if case.b_gate is not None else None
+        return None, dev_bits(case.w_gate), bgt
+    g = torch.from_numpy(np.ascontiguousarray(case.gates if gates is None else gates, dtype=np.float32)).cuda()
+    return g, None, None
 
 
 def run_prefill(case, gates=None, kc_bits=None, vc_bits=None):
     wl = case.wl
     dims, cfg = dims_cfg(case)
     T = wl.seq_len
-    g = torch.from_numpy(np.ascontiguousarray(case.gates if gates is None else gates, dtype=np.float32)).cuda()
+    g, wg, bgt = gate_args(case, gates)
     out = torch.empty((wl.batch, T, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
     sel = torch.full((wl.batch, T, wl.num_kv_heads, cfg.n_sel), -7, dtype=torch.int32, device="cuda")
     compress = kc_bits is None
@@ -117,7 +128,7 @@ def run_prefill(case, gates=None, kc_bits=None, vc_bits=None):
     vc = None if compress else dev_bits(vc_bits)
     N.nsa_prefill_fwd(dims, cfg, T, dev_bits(case.q), dev_bits(case.k), dev_bits(case.v), kc, vc,
                       dev_bits(case.w_k), dev_bits(case.pe_k), dev_bits(case.w_v), dev_bits(case.pe_v),
-                      g, out, sel, ws)
+                      g, out, sel, ws, w_gate=wg, b_gate=bgt)
     torch.cuda.synchronize()
     return bits_to_f64(host_bits(out)), sel.cpu().numpy()
 

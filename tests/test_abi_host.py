@@ -98,7 +98,7 @@ def test_validation_errors(dims_kw, cfg_kw, L, status):
 def _raw_decode(dims, cfg, ptr, L, ws, ws_bytes):
     lib = A.load_library()
     return lib.nsa_decode_fwd(ctypes.byref(dims), ctypes.byref(cfg), ptr, ptr, ptr, ptr, ptr, ptr, None, None,
-                              L, ptr, ptr, None, ws, ws_bytes, None)
+                              L, ptr, None, None, ptr, None, ws, ws_bytes, None)
 
 
 def test_decode_rejects_null_tensor_and_small_workspace_without_launching():
@@ -106,8 +106,13 @@ def test_decode_rejects_null_tensor_and_small_workspace_without_launching():
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     lib = A.load_library()
     st = lib.nsa_decode_fwd(ctypes.byref(dims), ctypes.byref(cfg), None, fake, fake, fake, fake, fake, None, None,
-                            65536, fake, fake, None, fake, 1 << 30, None)
+                            65536, fake, None, None, fake, None, fake, 1 << 30, None)
     assert st == A.NSA_ERROR_INVALID_VALUE and "NULL" in N.nsa_last_error()
+    # gate sources: none, or both given values and the gate network
+    for gates, wg, bgt in ((None, None, None), (fake, fake, None), (fake, None, fake)):
+        st = lib.nsa_decode_fwd(ctypes.byref(dims), ctypes.byref(cfg), fake, fake, fake, fake, fake, fake, None,
+                                None, 65536, gates, wg, bgt, fake, None, fake, 1 << 30, None)
+        assert st == A.NSA_ERROR_INVALID_VALUE and "gate" in N.nsa_last_error()
     need = _ws(dims, cfg, 65536)
     assert _raw_decode(dims, cfg, fake, 65536, fake, need - 1) == A.NSA_ERROR_WORKSPACE
     assert _raw_decode(dims, cfg, fake, 65536, None, need) == A.NSA_ERROR_WORKSPACE
@@ -118,14 +123,14 @@ def test_prefill_rejects_half_given_cache_and_missing_weights():
     lib = A.load_library()
     dims, cfg = _dims(batch=1), _cfg()
     f = ctypes.c_void_p(0x1000)
-    st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, f, None, f, f, f, f, f, f, None,
-                             f, 1 << 30, None)
+    st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, f, None, f, f, f, f, f, None, None,
+                             f, None, f, 1 << 30, None)
     assert st == A.NSA_ERROR_INVALID_VALUE
-    st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, None, None, None, f, f, f, f, f,
-                             None, f, 1 << 30, None)
+    st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, None, None, None, f, f, f, f, None,
+                             None, f, None, f, 1 << 30, None)
     assert st == A.NSA_ERROR_INVALID_VALUE
     st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 70000, f, f, f, f, f, None, None, None, None, f,
-                             f, None, None, 0, None)
+                             None, None, f, None, None, 0, None)
     assert st == A.NSA_ERROR_UNSUPPORTED
 
 

@@ -162,6 +162,34 @@ def test_one_block_completes_every_d_tokens(l, d):
         prev = cur
 
 
+# ---------------------------------------------------------------- gate network
+
+def test_gate_network_closed_forms():
+    """sigmoid(0) = 1/2; a one-hot query picks weight column k of its own head
+    (a transposed or head-mixed operand fails); sigmoid(-z) = 1 - sigmoid(z);
+    saturation without overflow."""
+    rng = np.random.default_rng(11)
+    G, dk = 3, 8
+    W = rng.standard_normal((G, 3, dk))
+    b = rng.standard_normal((G, 3))
+    np.testing.assert_array_equal(O.gate_network(np.zeros((G, dk)), W, None), np.full((G, 3), 0.5))
+    for k in (0, 5):
+        q = np.zeros((G, dk))
+        q[:, k] = 1.0
+        want = 1.0 / (1.0 + np.exp(-(W[:, :, k] + b)))
+        np.testing.assert_allclose(O.gate_network(q, W, b), want, rtol=1e-15)
+    q = rng.standard_normal((G, dk))
+    np.testing.assert_allclose(O.gate_network(q, -W, -b), 1.0 - O.gate_network(q, W, b), rtol=1e-13, atol=1e-15)
+    with np.errstate(over="ignore"):
+        sat = O.gate_network(np.full((G, dk), 100.0), np.sign(W) * 10.0, None)
+    assert np.all((sat == 0.0) | (sat == 1.0) | ((sat > 0) & (sat < 1)))
+    # head independence: changing head 1's weights changes only head 1's gates
+    W2 = W.copy()
+    W2[1] += 1.0
+    d = O.gate_network(q, W2, b) - O.gate_network(q, W, b)
+    assert np.all(d[[0, 2]] == 0.0) and np.all(d[1] != 0.0)
+
+
 # ---------------------------------------------------------------- gating
 
 def test_gates_isolate_and_are_linear():
