@@ -205,6 +205,57 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
                              uint16_t* out, int32_t* sel_idx_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * DeepSeek Sparse Attention (DSA) decode step — lesson 5.5/02 "Разреженное
+ * внимание — NSA и DSA" (ai.flicky.cc), section "DSA: молниеносный индексатор",
+ * and the selection rules of its practice spec (topk_mask: only past keys, all
+ * of them when fewer than k).  For each sequence b, with t = seq_lens[b] - 1:
+ *
+ *   indexer   I[s] = sum_j w_idx[b, j] * ReLU(q_idx[b, j] . k_idx[b, s]),  s <= t
+ *             (idx_heads small heads of idx_dim FP8 numbers, no softmax);
+ *   selection the top_k positions with the largest I (ties to the lower
+ *             position); every position 0..t when t + 1 <= top_k;
+ *   attention MLA in MQA mode: every query head h attends the selected
+ *             positions' shared latent vectors c[s] (d_qk numbers):
+ *             out[b, h] = softmax_s(scale * q[b, h] . c[s]) . c[s][0 : d_v].
+ *
+ * Supported: d_qk = 576, d_v = 512 (the 576-number latent, its first 512 numbers
+ * the values); num_heads a multiple of 32 up to 256; idx_heads in {16, 32, 64};
+ * idx_dim in {64, 128}; 1 <= top_k <= 4096; 1 <= cache_len <= 65536.
+ *
+ *   q         bf16 [B, num_heads, d_qk]
+ *   q_idx     FP8 E4M3 (OCP: bias 7, no infinities, max 448) [B, idx_heads, idx_dim]
+ *   w_idx     float32 [B, idx_heads]
+ *   latent    bf16 [B, cache_len, d_qk]      (token-major: each token contiguous)
+ *   k_idx     FP8 E4M3 [B, cache_len, idx_dim]
+ *   seq_lens  int32 [B] on the device, 1 <= seq_lens[b] <= cache_len
+ *   softmax_scale  0 selects 1/sqrt(d_qk)
+ *   out       bf16 [B, num_heads, d_v]
+ *   sel_idx_out    nullable int32 [B, top_k]: the selected positions, ascending,
+ *             -1 padded when t + 1 < top_k.
+ * Indexer scores are fp32 (exact FP8 products, fp32 sums); attention is bf16
+ * MFMA with fp32 accumulation.  With nsa_set_phase_events, events[0..3] are
+ * recorded before the indexer, after it, after the selection and at the end.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t num_heads;   /* query heads, all sharing one latent per token */
+  int32_t d_qk;        /* latent length: the logit dims */
+  int32_t d_v;         /* value dims: the first d_v latent numbers */
+  int32_t idx_heads;   /* indexer heads */
+  int32_t idx_dim;     /* indexer query / key length */
+} nsa_dsa_dims_t;
+nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float softmax_scale,
+                                const uint16_t* q, const uint8_t* q_idx, const float* w_idx,
+                                const uint16_t* latent, const uint8_t* k_idx,
+                                const int32_t* seq_lens, int64_t cache_len,
+                                uint16_t* out, int32_t* sel_idx_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes for nsa_dsa_decode_fwd (host-only): fp32 scores [B, cache_len],
+ * a selection buffer [B, top_k] and the attention partials. */
+nsa_status_t nsa_dsa_decode_workspace_size(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_len,
+                                           size_t* bytes);
+
 /* Workspace bytes needed by nsa_decode_fwd / nsa_prefill_fwd for these sizes
  * (host-only; no device call).  `compress_in_call` = 1 when k_cmp/v_cmp will be
  * NULL.  Returns NSA_SUCCESS and writes *bytes, or a validation error.  Prefill

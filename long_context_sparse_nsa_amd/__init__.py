@@ -16,7 +16,11 @@ from ._abi import (  # noqa: F401
     nsa_compress_append_workspace_size,
     nsa_compress_kv,
     nsa_config_t,
+    make_dsa_dims,
     nsa_decode_fwd,
+    nsa_dsa_decode_fwd,
+    nsa_dsa_decode_workspace_size,
+    nsa_dsa_dims_t,
     nsa_decode_workspace_size,
     nsa_dims_t,
     nsa_last_error,
@@ -27,4 +31,5 @@ from ._abi import (  # noqa: F401
 )
 
 __all__ = [n for n in dir() if n.startswith("nsa_")] + ["NSAError", "load_library", "make_config", "make_dims",
+                                                        "make_dsa_dims",
                                                         "new_workspace", "compressed_count", "EXPORTS"]

@@ -43,6 +43,15 @@ def make_config(l, d, l_sel, n_sel, n_local, force_initial, w, softmax_scale=0.0
     return nsa_config_t(l, d, l_sel, n_sel, n_local, force_initial, w, softmax_scale)
 
 
+class nsa_dsa_dims_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32)]
+
+
+def make_dsa_dims(batch, num_heads, d_qk, d_v, idx_heads, idx_dim) -> nsa_dsa_dims_t:
+    return nsa_dsa_dims_t(int(batch), int(num_heads), int(d_qk), int(d_v), int(idx_heads), int(idx_dim))
+
+
 def make_dims(batch, num_q_heads, num_kv_heads, d_k, d_v) -> nsa_dims_t:
     return nsa_dims_t(batch, num_q_heads, num_kv_heads, d_k, d_v)
 
@@ -63,6 +72,9 @@ _SIGS = {
                         _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "nsa_dsa_decode_fwd": [_VP, ctypes.c_int32, ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP,
+                           _VP, _VP, ctypes.c_size_t, _VP],
+    "nsa_dsa_decode_workspace_size": [_VP, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_set_phase_events": [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32],
     "nsa_status_string": [ctypes.c_int],
     "nsa_last_error": [],
@@ -105,7 +117,9 @@ def _check(status: int):
 
 
 _ITEM = {torch.bfloat16: 2, torch.int16: 2, torch.uint16: 2, torch.float32: 4, torch.int32: 4, torch.int64: 8,
-         torch.uint8: 1}
+         torch.uint8: 1, torch.int8: 1}
+if hasattr(torch, "float8_e4m3fn"):
+    _ITEM[torch.float8_e4m3fn] = 1
 
 
 def _ptr(t: Optional[torch.Tensor], what: str, itemsize: Optional[int] = None, numel: Optional[int] = None):
@@ -208,6 +222,31 @@ def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, p
                                _ptr(workspace, "workspace"),
                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                _stream(stream)))
+
+
+def nsa_dsa_decode_workspace_size(dims: nsa_dsa_dims_t, top_k: int, cache_len: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().nsa_dsa_decode_workspace_size(ctypes.byref(dims), int(top_k), int(cache_len),
+                                                        ctypes.byref(out)))
+    return int(out.value)
+
+
+def nsa_dsa_decode_fwd(dims, top_k, q, q_idx, w_idx, latent, k_idx, seq_lens, cache_len, out, sel_idx_out,
+                       workspace, softmax_scale=0.0, stream=None):
+    """q_idx / k_idx are uint8 tensors of FP8 E4M3 bit patterns."""
+    lib = load_library()
+    B, H = dims.batch, dims.num_heads
+    _check(lib.nsa_dsa_decode_fwd(ctypes.byref(dims), int(top_k), float(softmax_scale),
+                                  _ptr(q, "q", 2, B * H * dims.d_qk), _ptr(q_idx, "q_idx", 1, B * dims.idx_heads * dims.idx_dim),
+                                  _ptr(w_idx, "w_idx", 4, B * dims.idx_heads),
+                                  _ptr(latent, "latent", 2, B * int(cache_len) * dims.d_qk),
+                                  _ptr(k_idx, "k_idx", 1, B * int(cache_len) * dims.idx_dim),
+                                  _ptr(seq_lens, "seq_lens", 4, B), int(cache_len),
+                                  _ptr(out, "out", 2, B * H * dims.d_v),
+                                  _ptr(sel_idx_out, "sel_idx_out", 4, B * int(top_k)),
+                                  _ptr(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                  _stream(stream)))
 
 
 def nsa_set_phase_events(events=None):

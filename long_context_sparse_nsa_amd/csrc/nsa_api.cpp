@@ -151,6 +151,55 @@ size_t append_ws_bytes(const nsa_dims_t* dims, const nsa_config_t* cfg) {
   return align256((size_t)(ck > cv ? ck : cv) * rows_pad * (dims->d_k + dims->d_v) * 4);
 }
 
+// DSA decode: supported shapes and the launch plan.
+nsa_status_t check_dsa(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_len) {
+  if (!dims) return fail(NSA_ERROR_INVALID_VALUE, "dims is NULL");
+  if (dims->batch < 1 || dims->num_heads < 1 || dims->d_qk < 1 || dims->d_v < 1 || dims->idx_heads < 1 ||
+      dims->idx_dim < 1)
+    return fail(NSA_ERROR_INVALID_VALUE, "DSA dims must be positive");
+  if (top_k < 1 || cache_len < 1) return fail(NSA_ERROR_INVALID_VALUE, "top_k and cache_len must be >= 1");
+  if (dims->d_qk != nsa::kDsaDqk || dims->d_v != nsa::kDsaDv)
+    return fail(NSA_ERROR_UNSUPPORTED, "(d_qk, d_v) = (%d, %d), only (576, 512)", dims->d_qk, dims->d_v);
+  if (dims->num_heads % 32 != 0 || dims->num_heads > 256)
+    return fail(NSA_ERROR_UNSUPPORTED, "num_heads=%d: a multiple of 32, at most 256", dims->num_heads);
+  if (!(dims->idx_heads == 16 || dims->idx_heads == 32 || dims->idx_heads == 64) ||
+      !(dims->idx_dim == 64 || dims->idx_dim == 128))
+    return fail(NSA_ERROR_UNSUPPORTED, "indexer heads %d x dim %d: heads in {16, 32, 64}, dim in {64, 128}",
+                dims->idx_heads, dims->idx_dim);
+  if (top_k > nsa::kDsaMaxTopk) return fail(NSA_ERROR_UNSUPPORTED, "top_k=%d > %d", top_k, nsa::kDsaMaxTopk);
+  if (cache_len > nsa::kDsaMaxLen)
+    return fail(NSA_ERROR_UNSUPPORTED, "cache_len %lld > %d", (long long)cache_len, nsa::kDsaMaxLen);
+  return NSA_SUCCESS;
+}
+
+struct DsaPlan {
+  int seg, nseg, ts;
+  int64_t sstride;
+  size_t off_scores, off_sel, off_part, total;
+};
+DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
+  DsaPlan pl{};
+  const int B = dims->batch, ngrp = dims->num_heads / 32;
+  // indexer: about 256 workgroups, segments of whole 512-token batches
+  const int want = B >= 256 ? 1 : 256 / B;
+  int64_t seg = (cap + want - 1) / want;
+  seg = (seg + 511) / 512 * 512;
+  pl.seg = (int)seg;
+  pl.nseg = (int)((cap + seg - 1) / seg);
+  // attention: at most 512 selected tokens per workgroup, about 256 workgroups
+  const int tmin = (top_k + 511) / 512, tmax = (top_k + 63) / 64;
+  int ts = 256 / (B * ngrp);
+  ts = ts < tmin ? tmin : ts;
+  ts = ts > tmax ? tmax : ts;
+  pl.ts = ts;
+  pl.sstride = (cap + 3) / 4 * 4;
+  pl.off_scores = 0;
+  pl.off_sel = align256((size_t)B * pl.sstride * 4);
+  pl.off_part = pl.off_sel + align256((size_t)B * top_k * 4);
+  pl.total = pl.off_part + align256((size_t)B * ngrp * ts * 32 * 520 * 4);
+  return pl;
+}
+
 nsa_status_t hip_fail(hipError_t e, const char* what) {
   return fail(NSA_ERROR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -364,6 +413,59 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+nsa_status_t nsa_dsa_decode_workspace_size(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_len,
+                                           size_t* bytes) {
+  nsa_status_t st = check_dsa(dims, top_k, cache_len);
+  if (st != NSA_SUCCESS) return st;
+  if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
+  *bytes = dsa_plan(dims, top_k, cache_len).total;
+  return ok();
+}
+
+nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float softmax_scale, const uint16_t* q,
+                                const uint8_t* q_idx, const float* w_idx, const uint16_t* latent,
+                                const uint8_t* k_idx, const int32_t* seq_lens, int64_t cache_len, uint16_t* out,
+                                int32_t* sel_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  nsa_status_t st = check_dsa(dims, top_k, cache_len);
+  if (st != NSA_SUCCESS) return st;
+  if (!q || !q_idx || !w_idx || !latent || !k_idx || !seq_lens || !out)
+    return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale))
+    return fail(NSA_ERROR_INVALID_VALUE, "softmax_scale must be finite and >= 0");
+  const DsaPlan plan = dsa_plan(dims, top_k, cache_len);
+  if (!workspace || workspace_bytes < plan.total)
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  nsa::DsaParams p{};
+  p.B = dims->batch;
+  p.H = dims->num_heads;
+  p.HI = dims->idx_heads;
+  p.DI = dims->idx_dim;
+  p.topk = top_k;
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)dims->d_qk);
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.cap = cache_len;
+  p.q = q;
+  p.qi = q_idx;
+  p.wi = w_idx;
+  p.c = latent;
+  p.ki = k_idx;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.scores = reinterpret_cast<float*>(ws + plan.off_scores);
+  p.sstride = plan.sstride;
+  p.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t*>(ws + plan.off_sel);
+  p.part = reinterpret_cast<float*>(ws + plan.off_part);
+  p.seg = plan.seg;
+  p.nseg = plan.nseg;
+  p.ts = plan.ts;
+  const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
+  hipError_t e = nsa::launch_dsa_decode(p, static_cast<hipStream_t>(stream), ev);
+  if (e != hipSuccess) return hip_fail(e, "DSA decode launch");
   return ok();
 }
 

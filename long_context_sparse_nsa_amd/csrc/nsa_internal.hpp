@@ -125,6 +125,30 @@ struct AppendParams {
 int append_chunks(int l, int D);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
+// DeepSeek Sparse Attention decode step (lightning indexer + token top-k +
+// MQA attention over one shared latent per token).
+constexpr int kDsaDqk = 576, kDsaDv = 512, kDsaMaxLen = 65536, kDsaMaxTopk = 4096;
+constexpr int kDsaSelThreads = 1024, kDsaKeysPerThread = kDsaMaxLen / kDsaSelThreads;
+struct DsaParams {
+  int B, H, HI, DI, topk;
+  float scale_log2;
+  int64_t cap;                       // tokens per sequence in the caches
+  const uint16_t* q;                 // [B, H, 576] bf16
+  const uint8_t* qi;                 // [B, HI, DI] fp8 e4m3
+  const float* wi;                   // [B, HI]
+  const uint16_t* c;                 // [B, cap, 576] bf16 latent cache
+  const uint8_t* ki;                 // [B, cap, DI] fp8 e4m3 indexer keys
+  const int32_t* seq_lens;           // [B]
+  uint16_t* out;                     // [B, H, 512] bf16
+  float* scores;                     // workspace [B, sstride]
+  int64_t sstride;                   // cap rounded up to a multiple of 4
+  int32_t* sel;                      // [B, topk] (caller's or workspace), ascending, -1 padded
+  float* part;                       // workspace [B, H/32, ts, 32, 2 + 512]
+  int seg;                           // indexer tokens per workgroup (multiple of 512)
+  int nseg;                          // indexer workgroups per sequence
+  int ts;                            // attention token splits per (sequence, 32 heads)
+};
+
 DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len);
 
 // Optional events recorded between the kernels of one call (null = none).
@@ -133,6 +157,7 @@ struct PhaseEvents {
 };
 
 hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);
+hipError_t launch_dsa_decode(const DsaParams& p, hipStream_t s, const PhaseEvents* ev);
 // With events, ev[2] is recorded after the first prefill kernel and ev[3] after
 // the second (the caller records ev[0] and ev[1] around the compression).
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);

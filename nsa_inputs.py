@@ -265,3 +265,101 @@ def workload(name: str, **overrides) -> Workload:
         overrides["params"] = dataclasses.replace(wl.params, **overrides["params"])
     return wl.with_(**overrides) if overrides else wl
 
+
+
+# --------------------------------------------------------------------------- DSA decode workloads
+#
+# DeepSeek Sparse Attention as described in lesson 5.5/02 (section "DSA:
+# молниеносный индексатор"): an FP8 lightning indexer with a few small heads,
+# 2048 selected tokens per query, MLA in MQA mode over one 576-number latent per
+# token (512 of them the values).  Draw order (one default_rng(seed) stream):
+#   1. lengths (ragged workloads only)
+#   2. q [B, H, 576], latent c [B, cap, 576]      ~ N(0, 1), rounded to bf16
+#   3. q_idx [B, HI, DI], k_idx [B, cap, DI]      ~ N(0, 1), rounded to FP8 E4M3
+#   4. w_idx [B, HI]                              ~ N(0, 1/HI)
+#   5. needles: positions uniform without replacement over [0, L_b); their
+#      indexer keys point along sum_j max(w_j, 0) q_idx_j (length 2 sqrt(DI)) and
+#      their latents along the mean query (length sqrt(576)), plus 0.1 noise
+
+
+@dataclass(frozen=True)
+class DsaWorkload:
+    name: str
+    batch: int
+    num_heads: int
+    d_qk: int
+    d_v: int
+    idx_heads: int
+    idx_dim: int
+    top_k: int
+    seq_len: int              # cache length per sequence (the largest length)
+    needles: int
+    ragged_min: Optional[int] = None
+    kind: str = "dsa_decode"
+    description: str = ""
+
+    def with_(self, **kw) -> "DsaWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DSA_WORKLOADS = {
+    "dsa_decode_64k_b8": DsaWorkload(
+        "dsa_decode_64k_b8", 8, 128, 576, 512, 16, 128, 2048, 65536, 32,
+        description="DSA decode step, batch 8, 64k context, 128 heads over a 576-number latent, "
+                    "16 x 128 FP8 indexer heads, top-2048"),
+}
+
+
+def fp8_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to FP8 E4M3 (OCP, round to nearest even); uint8 bit patterns."""
+    import torch
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@dataclass
+class DsaCase:
+    wl: DsaWorkload
+    seed: int
+    q: np.ndarray           # bf16 bits [B, H, d_qk]
+    c: np.ndarray           # bf16 bits [B, cap, d_qk]
+    q_idx: np.ndarray       # FP8 bits [B, HI, DI]
+    k_idx: np.ndarray       # FP8 bits [B, cap, DI]
+    w_idx: np.ndarray       # float32 [B, HI]
+    seq_lens: np.ndarray    # int32 [B]
+    needle_pos: list = field(default_factory=list)
+
+
+def generate_dsa(wl: DsaWorkload, seed: int) -> DsaCase:
+    rng = np.random.default_rng(seed)
+    B, H, D, HI, DI, cap = wl.batch, wl.num_heads, wl.d_qk, wl.idx_heads, wl.idx_dim, wl.seq_len
+    if wl.ragged_min is not None:
+        lens = rng.integers(wl.ragged_min, cap + 1, size=B).astype(np.int64)
+    else:
+        lens = np.full(B, cap, dtype=np.int64)
+    q = rng.standard_normal(size=(B, H, D), dtype=np.float32)
+    c = rng.standard_normal(size=(B, cap, D), dtype=np.float32)
+    q_idx = rng.standard_normal(size=(B, HI, DI), dtype=np.float32)
+    k_idx = rng.standard_normal(size=(B, cap, DI), dtype=np.float32)
+    w_idx = (rng.standard_normal(size=(B, HI), dtype=np.float32) / np.float32(np.sqrt(HI)))
+    needle_pos = []
+    for b in range(B):
+        L = int(lens[b])
+        cnt = min(wl.needles, L)
+        pos = np.sort(rng.choice(L, size=cnt, replace=False)) if cnt else np.zeros(0, np.int64)
+        needle_pos.append(pos)
+        if cnt == 0:
+            continue
+        ui = (np.maximum(w_idx[b], 0.0)[:, None] * q_idx[b]).sum(axis=0)
+        ui = ui / max(np.linalg.norm(ui), 1e-6)
+        uq = q[b].mean(axis=0)
+        uq = uq / np.linalg.norm(uq)
+        k_idx[b, pos] = (2.0 * np.sqrt(DI) * ui)[None, :] + 0.1 * rng.standard_normal((cnt, DI), dtype=np.float32)
+        c[b, pos] = (np.sqrt(D) * uq)[None, :] + 0.1 * rng.standard_normal((cnt, D), dtype=np.float32)
+    return DsaCase(wl=wl, seed=seed, q=_round(q), c=_round(c), q_idx=fp8_bits(q_idx), k_idx=fp8_bits(k_idx),
+                   w_idx=w_idx, seq_lens=lens.astype(np.int32), needle_pos=needle_pos)
+
+
+def dsa_workload(name: str, **overrides) -> DsaWorkload:
+    wl = DSA_WORKLOADS[name]
+    return wl.with_(**overrides) if overrides else wl

@@ -1,0 +1,129 @@
+"""GPU parity of nsa_dsa_decode_fwd (DSA decode: FP8 lightning indexer, token
+top-k, MQA attention over the selected latents) against the float64 oracle.
+
+Indexer scores: the products of two FP8 E4M3 numbers are exact, but the FP8
+matrix instruction adds the 32 products of a k-step inside the matrix unit, and
+that sum is not a rounded IEEE fp32 sum (observed: up to 4.4e-6 of the sum of
+absolute terms over ~60k tokens); the bound used is 2^-16 of sum_j |w_j| *
+sum_d |q_jd k_sd| per token, against the oracle's float64.  Selection: the
+GPU's set must equal the top-k of its own fp32 scores exactly (both sides decide
+in the kernel's precision), and may differ from the oracle's float64 top-k only
+in tokens whose oracle score lies within that tolerance of the k-th score.
+Output: against the oracle re-run on the GPU's selection, max-abs <= 2e-2 and
+mean-abs <= 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_nsa_amd as N
+import nsa_inputs as I
+from oracle import dsa_oracle as D
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+HEAD = "dsa_decode_64k_b8"
+
+
+def run_dsa(case, top_k=None, repeat=1):
+    wl = case.wl
+    k = wl.top_k if top_k is None else top_k
+    cap = wl.seq_len
+    dims = N.make_dsa_dims(wl.batch, wl.num_heads, wl.d_qk, wl.d_v, wl.idx_heads, wl.idx_dim)
+    q, c = U.dev_bits(case.q), U.dev_bits(case.c)
+    qi, ki = torch.from_numpy(case.q_idx).cuda(), torch.from_numpy(case.k_idx).cuda()
+    wi, seq = torch.from_numpy(case.w_idx).cuda(), torch.from_numpy(case.seq_lens).cuda()
+    out = torch.empty((wl.batch, wl.num_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    sel = torch.full((wl.batch, k), -7, dtype=torch.int32, device="cuda")
+    ws = N.new_workspace(N.nsa_dsa_decode_workspace_size(dims, k, cap))
+    outs = []
+    for _ in range(repeat):
+        N.nsa_dsa_decode_fwd(dims, k, q, qi, wi, c, ki, seq, cap, out, sel, ws)
+        torch.cuda.synchronize()
+        outs.append(U.host_bits(out).copy())
+    stride = (cap + 3) // 4 * 4
+    scores = ws[:wl.batch * stride * 4].view(torch.float32).reshape(wl.batch, stride).cpu().numpy()
+    return U.bits_to_f64(outs[-1]), sel.cpu().numpy(), scores, outs
+
+
+def check_dsa(case, out, sel, scores, top_k=None, seqs=None):
+    wl = case.wl
+    k = wl.top_k if top_k is None else top_k
+    wl_k = wl.with_(top_k=k)
+    case_k = I.DsaCase(**{**case.__dict__, "wl": wl_k})
+    for b in (range(wl.batch) if seqs is None else seqs):
+        L = int(case.seq_lens[b])
+        t = L - 1
+        res_out, idx_o, I_o = D.decode_sequence(case_k, b)
+        qI = D.fp8_e4m3_to_float(case.q_idx[b])
+        kI = D.fp8_e4m3_to_float(case.k_idx[b, :L])
+        w = np.asarray(case.w_idx[b], np.float64)
+        bound = np.abs(kI) @ np.abs(qI).T @ np.abs(w)
+        tol = 2.0 ** -16 * bound + 1e-6
+        I_g = scores[b, :L].astype(np.float64)
+        assert np.all(np.abs(I_g - I_o) <= tol), f"b={b}: indexer scores"
+        s_g = sel[b]
+        if L <= k:
+            np.testing.assert_array_equal(s_g[:L], np.arange(L))
+            assert np.all(s_g[L:] == -1)
+        else:
+            np.testing.assert_array_equal(s_g, D.topk_tokens(I_g, t, k), err_msg=f"b={b}: top-k of own scores")
+            theta = np.sort(I_o)[::-1][k - 1]
+            diff = np.setxor1d(s_g, idx_o)
+            assert np.all(np.abs(I_o[diff] - theta) <= tol[diff] + tol.max()), f"b={b}: selection beyond tolerance"
+        gsel = s_g[s_g >= 0]
+        want, _, _ = D.decode_sequence(case_k, b, override_idx=gsel)
+        U.assert_close(out[b], want, f"b={b} L={L}")
+
+
+def test_dsa_small_ragged():
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=3, seq_len=6000, ragged_min=2500, num_heads=32, needles=8), 51)
+    out, sel, scores, _ = run_dsa(case)
+    check_dsa(case, out, sel, scores)
+
+
+def test_dsa_takes_every_token_when_short():
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=1500, ragged_min=700, num_heads=32, needles=4), 52)
+    out, sel, scores, _ = run_dsa(case)
+    check_dsa(case, out, sel, scores)
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 2047, 2048, 2049, 4097])
+def test_dsa_edge_lengths(L):
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=1, seq_len=L, num_heads=32, needles=2), 60 + L)
+    out, sel, scores, _ = run_dsa(case)
+    check_dsa(case, out, sel, scores)
+
+
+@pytest.mark.parametrize("shape,k", [
+    (dict(num_heads=64, idx_heads=64, idx_dim=64), 100),
+    (dict(num_heads=96, idx_heads=32, idx_dim=128), 4096),
+    (dict(num_heads=128, idx_heads=16, idx_dim=64), 512),
+], ids=["h64_i64x64_k100", "h96_i32x128_k4096", "h128_i16x64_k512"])
+def test_dsa_shapes(shape, k):
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=9000, ragged_min=5000, needles=8, **shape), 53)
+    out, sel, scores, _ = run_dsa(case, top_k=k)
+    check_dsa(case, out, sel, scores, top_k=k)
+
+
+def test_dsa_equal_scores_take_the_lowest_positions():
+    """Every indexer key equal: all scores tie, so the selection is positions 0..k-1."""
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=5000, num_heads=32, needles=0), 54)
+    case.k_idx[:] = case.k_idx[:, :1, :]
+    out, sel, scores, _ = run_dsa(case)
+    for b in range(2):
+        np.testing.assert_array_equal(sel[b], np.arange(2048))
+    check_dsa(case, out, sel, scores)
+
+
+def test_dsa_repeat_is_bitwise_identical():
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=7000, num_heads=64, needles=8), 55)
+    _, _, _, outs = run_dsa(case, repeat=2)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_dsa_full_size_64k_batch8():
+    """The benchmarked shape and launch plan: 8 x 65536 tokens, 128 heads, top-2048."""
+    case = I.generate_dsa(I.dsa_workload(HEAD), list(I.DSA_WORKLOADS).index(HEAD))
+    out, sel, scores, _ = run_dsa(case)
+    check_dsa(case, out, sel, scores, seqs=[0, 3, 7])
