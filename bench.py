@@ -439,6 +439,94 @@ def bench_prefill(args, torch, N, I):
     return res
 
 
+def dsa_upload(case, torch, N):
+    wl = case.wl
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    dims = N.make_dsa_dims(wl.batch, wl.num_heads, wl.d_qk, wl.d_v, wl.idx_heads, wl.idx_dim)
+    T = dict(q=dev(case.q), c=dev(case.c), qi=torch.from_numpy(case.q_idx).cuda(),
+             ki=torch.from_numpy(case.k_idx).cuda(), wi=torch.from_numpy(case.w_idx).cuda(),
+             seq=torch.from_numpy(case.seq_lens).cuda())
+    return dims, T
+
+
+def dsa_bytes(case):
+    """Algorithmic HBM bytes of one DSA decode step: every indexer key of the
+    context, the selected tokens' latents, q (both), the indexer weights, out."""
+    wl = case.wl
+    keys = sum(int(L) for L in case.seq_lens) * wl.idx_dim
+    sel = sum(min(int(L), wl.top_k) for L in case.seq_lens) * wl.d_qk * 2
+    io = wl.batch * (wl.num_heads * (wl.d_qk + wl.d_v) * 2 + wl.idx_heads * (wl.idx_dim + 4))
+    return keys, sel, keys + sel + io
+
+
+def bench_dsa(args, torch, N, I):
+    """DSA decode step (second workload): graph replays over rotating cache copies."""
+    wl = I.dsa_workload("dsa_decode_64k_b8")
+    t0 = time.time()
+    case = I.generate_dsa(wl, list(I.DSA_WORKLOADS).index(wl.name))
+    log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s")
+    dims, T = dsa_upload(case, torch, N)
+    cap, k = wl.seq_len, wl.top_k
+    ws = N.new_workspace(N.nsa_dsa_decode_workspace_size(dims, k, cap))
+    out = torch.empty((wl.batch, wl.num_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    copies = [(T["c"], T["ki"])] + [(T["c"].clone(), T["ki"].clone()) for _ in range(args.copies - 1)]
+
+    def step(i):
+        c, ki = copies[i % len(copies)]
+        N.nsa_dsa_decode_fwd(dims, k, T["q"], T["qi"], T["wi"], c, ki, T["seq"], cap, out, None, ws)
+
+    for i in range(len(copies)):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for i in range(len(copies)):
+                step(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, (args.steps + len(copies) - 1) // len(copies))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / (reps * len(copies))
+    # per-phase durations: events before the indexer, after it, after the selection, at the end
+    n_ph = 30
+    hev = HipEvents(4 * n_ph)
+    try:
+        torch.cuda._sleep(int(2e7))
+        for i in range(n_ph):
+            N.nsa_set_phase_events(hev.ev[4 * i:4 * i + 4])
+            step(i)
+        N.nsa_set_phase_events(None)
+        torch.cuda.synchronize()
+        ph = [float(np.mean([hev.ms(4 * i + a, 4 * i + a + 1) for i in range(n_ph)])) for a in range(3)]
+    finally:
+        N.nsa_set_phase_events(None)
+        hev.close()
+    b_keys, b_sel, b_step = dsa_bytes(case)
+    flops = 2 * wl.batch * wl.num_heads * k * (wl.d_qk + wl.d_v)
+    res = dict(workload=wl.name, ms_per_step=ms, tokens_per_s=wl.batch / (ms * 1e-3), step_bytes=b_step,
+               gbs=b_step / (ms * 1e-3) / 1e9,
+               kernel_us=dict(indexer=ph[0] * 1e3, select=ph[1] * 1e3, attention_and_combine=ph[2] * 1e3),
+               indexer_gbs=b_keys / (ph[0] * 1e-3) / 1e9, attention_tflops=flops / (ph[2] * 1e-3) / 1e12,
+               attention_bytes=b_sel, attention_flops=flops)
+    res["hbm_frac"] = res["gbs"] / HBM_PEAK_GBS
+    log(f"[bench] dsa {wl.name}: {ms * 1e3:.1f} us/step, {res['tokens_per_s']:.4g} tok/s, {res['gbs']:.0f} GB/s "
+        f"({100 * res['hbm_frac']:.1f}%); indexer {ph[0] * 1e3:.1f} us ({res['indexer_gbs']:.0f} GB/s), select "
+        f"{ph[1] * 1e3:.1f} us, attention+combine {ph[2] * 1e3:.1f} us ({res['attention_tflops']:.0f} TFLOP/s)")
+    return res
+
+
 def cpu_baseline(case, min_seconds):
     """The float64 oracle on a bounded sample of the decode workload (this host's cores)."""
     from oracle import nsa_oracle as O
@@ -474,6 +562,20 @@ def cpu_baseline(case, min_seconds):
 def kernels_only(args, torch, N, I):
     """A few eager calls and nothing else (for profiler runs): decode steps over
     the cache copies, or, with --prefill, prefill calls."""
+    if args.dsa:
+        wl = I.dsa_workload("dsa_decode_64k_b8")
+        case = I.generate_dsa(wl, list(I.DSA_WORKLOADS).index(wl.name))
+        dims, T = dsa_upload(case, torch, N)
+        ws = N.new_workspace(N.nsa_dsa_decode_workspace_size(dims, wl.top_k, wl.seq_len))
+        out = torch.empty((wl.batch, wl.num_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
+        copies = [(T["c"], T["ki"])] + [(T["c"].clone(), T["ki"].clone()) for _ in range(args.copies - 1)]
+        for i in range(args.kernels_only):
+            c, ki = copies[i % len(copies)]
+            N.nsa_dsa_decode_fwd(dims, wl.top_k, T["q"], T["qi"], T["wi"], c, ki, T["seq"], wl.seq_len, out, None,
+                                 ws)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.kernels_only} DSA decode steps of {wl.name} done")
+        return
     if args.prefill:
         wl = I.workload("prefill_32k")
         case = I.generate(wl, list(I.WORKLOADS).index("prefill_32k"))
@@ -557,6 +659,8 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-serving", action="store_true", help="skip the append + decode serving-step timing")
+    ap.add_argument("--no-dsa", action="store_true", help="skip the DSA decode workload")
+    ap.add_argument("--dsa", action="store_true", help="with --kernels-only: DSA decode steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
@@ -586,6 +690,7 @@ def main():
 
     case, dec, _ = bench_decode(args, torch, N, I)
     pre = None if args.no_prefill else bench_prefill(args, torch, N, I)
+    dsa = None if args.no_dsa else bench_dsa(args, torch, N, I)
     cpu = None if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']:.3g} tok/s on {cpu['cores']} threads")
@@ -624,6 +729,15 @@ def main():
         "reading": "gate[h, c] = sigmoid(w_gate[h, c] . q[h] + b_gate[h, c]), computed in the kernels that apply it",
         "decode_ms_per_step": dec.get("gate_network_ms_per_step"),
         "prefill_ms": pre.get("gate_network_ms") if pre else None}
+    if dsa:
+        line["dsa_decode"] = {
+            "workload": dsa["workload"], "ms_per_step": dsa["ms_per_step"], "tokens_per_s": dsa["tokens_per_s"],
+            "algorithmic_bytes": dsa["step_bytes"], "GB/s": dsa["gbs"], "hbm_frac": dsa["hbm_frac"],
+            "kernel_us": dsa["kernel_us"],
+            "indexer": {"kernel": "dsa_index_kernel", "bound": "hbm", "GB/s": dsa["indexer_gbs"],
+                        "frac": dsa["indexer_gbs"] / HBM_PEAK_GBS},
+            "attention": {"kernels": "dsa_attn_kernel + dsa_combine_kernel", "TFLOP/s": dsa["attention_tflops"],
+                          "mfma_frac": dsa["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS}}
     if dec.get("serving"):
         sv = dec["serving"]
         line["serving_step"] = {

@@ -251,8 +251,10 @@ nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float
                                 const int32_t* seq_lens, int64_t cache_len,
                                 uint16_t* out, int32_t* sel_idx_out,
                                 void* workspace, size_t workspace_bytes, void* stream);
-/* Workspace bytes for nsa_dsa_decode_fwd (host-only): fp32 scores [B, cache_len],
- * a selection buffer [B, top_k] and the attention partials. */
+/* Workspace bytes for nsa_dsa_decode_fwd (host-only): fp32 scores [B, cache_len]
+ * (row stride cache_len rounded up to 4, at offset 0), a selection buffer
+ * [B, top_k], the attention partials, and the selection's histogram, counters,
+ * position bitmap and candidate list.  Its contents on entry do not matter. */
 nsa_status_t nsa_dsa_decode_workspace_size(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_len,
                                            size_t* bytes);
 

@@ -173,9 +173,9 @@ nsa_status_t check_dsa(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_
 }
 
 struct DsaPlan {
-  int seg, nseg, ts;
+  int seg, nseg, ts, nchunk;
   int64_t sstride;
-  size_t off_scores, off_sel, off_part, total;
+  size_t off_scores, off_sel, off_part, off_hist, off_cnt, off_bits, off_cand, total;
 };
 DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   DsaPlan pl{};
@@ -196,7 +196,12 @@ DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   pl.off_scores = 0;
   pl.off_sel = align256((size_t)B * pl.sstride * 4);
   pl.off_part = pl.off_sel + align256((size_t)B * top_k * 4);
-  pl.total = pl.off_part + align256((size_t)B * ngrp * ts * 32 * 520 * 4);
+  pl.nchunk = (int)((cap + nsa::kDsaChunk - 1) / nsa::kDsaChunk);
+  pl.off_hist = pl.off_part + align256((size_t)B * ngrp * ts * 32 * 520 * 4);
+  pl.off_cnt = pl.off_hist + align256((size_t)B * nsa::kDsaBins * 4);
+  pl.off_bits = pl.off_cnt + align256((size_t)B * (4 + pl.nchunk) * 4);
+  pl.off_cand = pl.off_bits + align256((size_t)B * pl.nchunk * 128 * 4);
+  pl.total = pl.off_cand + align256((size_t)B * cap * 8);
   return pl;
 }
 
@@ -460,6 +465,11 @@ nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float
   p.sstride = plan.sstride;
   p.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t*>(ws + plan.off_sel);
   p.part = reinterpret_cast<float*>(ws + plan.off_part);
+  p.hist = reinterpret_cast<uint32_t*>(ws + plan.off_hist);
+  p.cnt = reinterpret_cast<uint32_t*>(ws + plan.off_cnt);
+  p.bits = reinterpret_cast<uint32_t*>(ws + plan.off_bits);
+  p.cand = reinterpret_cast<uint64_t*>(ws + plan.off_cand);
+  p.nchunk = plan.nchunk;
   p.seg = plan.seg;
   p.nseg = plan.nseg;
   p.ts = plan.ts;

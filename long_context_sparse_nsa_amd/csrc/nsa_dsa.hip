@@ -14,16 +14,21 @@
 //     16-token tiles with v_mfma_f32_16x16x32_fp8_fp8 (indexer heads x tokens),
 //     ReLU, the weighted head sum, and writes fp32 scores.  Tile loads run a
 //     batch of eight tiles ahead of the compute.
-//  2. dsa_select_kernel  one 1024-thread workgroup per sequence holds the
-//     scores as order-preserving integer keys in registers and finds the k-th
-//     largest exactly by radix select (12 + 12 + 8 bits, LDS histograms; a
-//     wave whose active lanes share a digit adds once); ties at the threshold
-//     go to the lower positions; the ids are written ascending.
-//  3. dsa_attn_kernel    workgroup = (sequence, 32 heads, token split); 64-token
-//     tiles of latents are gathered into LDS with the direct global->LDS copy
-//     (two buffers).  Wave (head tile, token half) keeps its own online softmax
-//     over its 32 tokens of each tile, so no per-tile exchange is needed; the
-//     two halves merge through LDS at the end into one partial per workgroup.
+//  2. exact top-k by radix select on order-preserving integer keys of the
+//     scores, over 4096-score chunks: dsa_hist_kernel sums the top-13-bit
+//     histogram of every chunk into one per sequence (zeroed by the indexer
+//     launch); dsa_select_kernel marks the positions above the boundary bin in a
+//     bitmap and collects the boundary bin's scores, and the last workgroup of
+//     the sequence finishes the select on those candidates (13 + 6 more bits),
+//     takes ties at the threshold from the lowest positions and writes the
+//     positions ascending.
+//  3. dsa_attn_kernel    workgroup = (sequence, 32 heads, token split); 32-token
+//     tiles of latents are gathered into LDS with the direct global->LDS copy,
+//     four buffers (three tiles in flight).  Wave (head tile, 16-token row
+//     group) keeps its own online softmax over its 16 tokens of each tile, so no
+//     per-tile exchange is needed: its P^T feeds the 16x16x16 value product as
+//     is.  The two row groups merge through LDS at the end into one partial per
+//     workgroup.
 //  4. dsa_combine_kernel merges the token-split partials exactly and writes bf16.
 #include <hip/hip_runtime.h>
 
@@ -50,6 +55,10 @@ __global__ __launch_bounds__(256) void dsa_index_kernel(DsaParams p) {
   constexpr int RT = HI / 16, KS = DI / 32, BPL = DI / 4, LV = BPL / 16, NT = 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int b = blockIdx.x / p.nseg, sg = blockIdx.x - b * p.nseg;
+  if (sg == 0) {  // the selection's histogram and counters start at zero (used by the next launches)
+    for (int i = tid; i < kDsaBins; i += 256) p.hist[(size_t)b * kDsaBins + i] = 0u;
+    if (tid < 4) p.cnt[4 * b + tid] = 0u;
+  }
   const int64_t L = p.seq_lens[b];
   const int64_t n = L < p.cap ? L : p.cap;
   const int64_t s0 = (int64_t)sg * p.seg;
@@ -126,8 +135,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // larger float -> larger key
 }
 
-// Exclusive prefix over the 1024 threads of the workgroup (16 waves).
-__device__ __forceinline__ int scan1024(int v, int* s_w, int* total) {
+// Exclusive prefix over the 256 threads of a selection workgroup.
+__device__ __forceinline__ int scan256(int v, int* s_w, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -139,7 +148,7 @@ __device__ __forceinline__ int scan1024(int v, int* s_w, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 16; ++w) {
+  for (int w = 0; w < 4; ++w) {
     const int s = s_w[w];
     base += w < wave ? s : 0;
     tot += s;
@@ -149,104 +158,281 @@ __device__ __forceinline__ int scan1024(int v, int* s_w, int* total) {
   return base + x - v;
 }
 
-__global__ __launch_bounds__(kDsaSelThreads) void dsa_select_kernel(DsaParams p) {
-  constexpr int KPT = kDsaKeysPerThread;
-  __shared__ uint32_t hist[4096];
-  __shared__ int s_w[16];
+// The 16 order keys of this thread's positions c0 + 16*tid .. +15 (0 past n):
+// four 16-byte loads, addresses clamped inside the score row.
+__device__ __forceinline__ void load_keys16(const DsaParams& p, int b, int c0, int n, uint32_t (&key)[16], int& nv) {
+  const float* sc = p.scores + (size_t)b * p.sstride;
+  const int base = c0 + 16 * (int)threadIdx.x, last = (int)p.sstride - 4;
+  f32x4_t v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4_t*>(sc + (base + 4 * q < last ? base + 4 * q : last));
+  nv = n - base;
+  nv = nv < 0 ? 0 : (nv > 16 ? 16 : nv);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[4 * q + e] = 4 * q + e < nv ? order_key(v[q][e]) : 0u;
+}
+
+// In a histogram of `nb` bins (nb / 256 per thread, a power of two; the highest
+// bins to thread 0), the bin holding the need-th largest key and the count of
+// keys above it.  Each thread sums its bins starting at a rotated offset, so the
+// lanes of a wave read different LDS banks; only the thread whose segment holds
+// the boundary walks it in order.
+__device__ __forceinline__ void find_bin(const uint32_t* h, int nb, int need, int* s_w, int* s_found) {
+  const int tid = (int)threadIdx.x, per = nb / 256, g0 = per * (255 - tid);
+  int sum = 0;
+#pragma unroll 8
+  for (int e = 0; e < per; ++e) sum += (int)h[g0 + ((e + tid) & (per - 1))];
+  int total;
+  const int above = scan256(sum, s_w, &total);
+  if (above < need && above + sum >= need) {
+    int acc = above;
+    for (int e = per - 1; e >= 0; --e) {
+      const int c = (int)h[g0 + e];
+      if (acc + c >= need) {
+        s_found[0] = g0 + e;
+        s_found[1] = acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+}
+
+// 2a. first-digit histogram of every score, summed over the workgroups of a sequence
+__global__ __launch_bounds__(256) void dsa_hist_kernel(DsaParams p) {
+  __shared__ uint32_t h[kDsaBins];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / p.nchunk, ch = blockIdx.x - b * p.nchunk;
+  const int64_t L = p.seq_lens[b];
+  const int n = (int)(L < p.cap ? L : p.cap);
+  const int c0 = ch * kDsaChunk;
+  if (n <= p.topk || c0 >= n) return;  // workgroup-uniform
+  for (int i = tid; i < kDsaBins; i += 256) h[i] = 0u;
+  uint32_t key[16];
+  int nv;
+  load_keys16(p, b, c0, n, key, nv);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < nv) atomicAdd(&h[key[k] >> 19], 1u);
+  __syncthreads();
+  uint32_t* gh = p.hist + (size_t)b * kDsaBins;
+  for (int i = tid; i < kDsaBins; i += 256) {
+    const uint32_t c = h[i];
+    if (c) atomicAdd(gh + i, c);
+  }
+}
+
+// 2b. every workgroup finds the first digit's boundary bin, marks the positions
+// above it in the bitmap and writes the boundary bin's scores into its own slice
+// of the candidate list; the last workgroup of the sequence resolves the
+// candidates exactly (two more digits, ties to the lower position) and writes
+// the positions ascending.  Bitmap words, candidates and counts are stored with
+// agent-scope atomic stores and read with agent-scope atomic loads after the
+// arrival count (the workgroups of a sequence may sit on different XCDs, whose
+// L2s are not coherent for plain stores).
+constexpr int kCandLds = 4096;  // candidates the last workgroup holds in LDS
+constexpr int kCandPer = 4;     // candidate loads per thread in flight at once
+
+__global__ __launch_bounds__(256) void dsa_select_kernel(DsaParams p) {
+  __shared__ uint32_t h[kDsaBins];
+  __shared__ uint32_t s_bits[2 * kDsaMaxLen / 32];  // this chunk's words; later selected + tie words
+  __shared__ uint64_t s_cand[kCandLds];
+  __shared__ int s_w[4];
   __shared__ int s_found[2];
+  __shared__ int s_last, s_nc;
+  __shared__ uint32_t s_coff[kDsaMaxLen / kDsaChunk + 1];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int b = blockIdx.x;
+  const int b = blockIdx.x / p.nchunk, ch = blockIdx.x - b * p.nchunk;
   const int64_t L = p.seq_lens[b];
   const int n = (int)(L < p.cap ? L : p.cap);
   int32_t* out = p.sel + (size_t)b * p.topk;
   if (n <= p.topk) {  // every past token
-    for (int i = tid; i < p.topk; i += kDsaSelThreads) out[i] = i < n ? i : -1;
+    if (ch == 0)
+      for (int i = tid; i < p.topk; i += 256) out[i] = i < n ? i : -1;
     return;
   }
-  const int base = tid * KPT;  // this thread's positions: base .. base + KPT - 1
-  const float* sc = p.scores + (size_t)b * p.sstride;
-  uint32_t key[KPT];
-#pragma unroll
-  for (int k4 = 0; k4 < KPT / 4; ++k4) {
-    const int i0 = base + 4 * k4;
-    if (i0 + 3 < n) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(sc + i0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) key[4 * k4 + e] = order_key(v[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) key[4 * k4 + e] = i0 + e < n ? order_key(sc[i0 + e]) : 0u;
-    }
-  }
-  int nvalid = n - base;
-  nvalid = nvalid < 0 ? 0 : (nvalid > KPT ? KPT : nvalid);
+  const int c0 = ch * kDsaChunk;
+  uint32_t* bits = p.bits + (size_t)b * p.nchunk * 128;
+  uint64_t* cand = p.cand + (size_t)b * p.cap;       // chunk ch writes entries [c0, c0 + its count)
+  uint32_t* ccount = p.cnt + (size_t)p.B * 4 + (size_t)b * p.nchunk;  // per-chunk candidate counts
+  uint32_t* arrive = p.cnt + 4 * b + 1;
 
-  uint32_t prefix = 0u, pmask = 0u;
-  int need = p.topk;  // still to take among the keys that match the prefix
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const uint32_t dmask = pass == 2 ? 0xFFu : 0xFFFu;
-    for (int i = tid; i < 4096; i += kDsaSelThreads) hist[i] = 0u;
-    __syncthreads();
+  // the first digit's histogram into LDS (eight 16-byte loads per thread, all in flight)
+  {
+    const u32x4_t* gh = reinterpret_cast<const u32x4_t*>(p.hist + (size_t)b * kDsaBins);
+    u32x4_t v[kDsaBins / 4 / 256];
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const bool act = k < nvalid && (key[k] & pmask) == prefix;
-      const uint32_t d = (key[k] >> shift) & dmask;
-      const uint64_t am = __ballot(act);
-      if (am != 0ull) {
-        const int first = __builtin_ctzll(am);
-        const uint32_t d0 = (uint32_t)__shfl((int)d, first);
-        const uint64_t same = __ballot(act && d == d0);
-        if (same == am) {
-          if (lane == first) atomicAdd(&hist[d0], (uint32_t)__popcll(am));
-        } else if (act) {
-          atomicAdd(&hist[d], 1u);
+    for (int q = 0; q < kDsaBins / 4 / 256; ++q) v[q] = gh[tid + 256 * q];
+#pragma unroll
+    for (int q = 0; q < kDsaBins / 4 / 256; ++q) reinterpret_cast<u32x4_t*>(h)[tid + 256 * q] = v[q];
+  }
+  if (tid == 0) s_nc = 0;
+  __syncthreads();
+  find_bin(h, kDsaBins, p.topk, s_w, s_found);
+  const uint32_t T0 = (uint32_t)s_found[0];
+  const int above0 = s_found[1];
+  if (c0 < n) {
+    uint32_t key[16];
+    int nv;
+    load_keys16(p, b, c0, n, key, nv);
+    if (tid < 128) s_bits[tid] = 0u;
+    __syncthreads();
+    uint32_t w = 0u;  // this thread's 16 positions: half of bitmap word tid / 2
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t bin = key[k] >> 19;
+      const bool valid = k < nv;
+      if (valid && bin > T0) w |= 1u << (16 * (tid & 1) + k);
+      const bool cd = valid && bin == T0;
+      const uint64_t m = __ballot(cd);
+      if (m != 0ull) {  // wave-aggregated slot in this chunk's slice
+        const int first = __builtin_ctzll(m);
+        int slot0 = 0;
+        if (lane == first) slot0 = atomicAdd(&s_nc, __popcll(m));
+        slot0 = __shfl(slot0, first);
+        if (cd) {
+          const int slot = slot0 + __popcll(m & ((1ull << lane) - 1ull));
+          __hip_atomic_store(cand + c0 + slot, ((uint64_t)key[k] << 32) | (uint32_t)(c0 + 16 * tid + k),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
+    atomicOr(&s_bits[tid >> 1], w);
     __syncthreads();
-    // bins 4*(1023 - tid) .. +3 per thread: the prefix over threads is the count above
-    const int g0 = 4 * (kDsaSelThreads - 1 - tid);
-    const uint32_t h0 = hist[g0], h1 = hist[g0 + 1], h2 = hist[g0 + 2], h3 = hist[g0 + 3];
-    int total;
-    const int above = scan1024((int)(h0 + h1 + h2 + h3), s_w, &total);
-    int acc = above;
-    const uint32_t hv[4] = {h3, h2, h1, h0};
+    if (tid < 128) __hip_atomic_store(bits + ch * 128 + tid, s_bits[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid == 0) __hip_atomic_store(ccount + ch, (uint32_t)s_nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(p.nchunk - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last workgroup.  Candidate offsets per chunk, then every candidate and
+  // bitmap word loaded in one round trip.
+  if (tid < p.nchunk) s_coff[tid + 1] = __hip_atomic_load(ccount + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid == 0) {  // counts -> offsets (at most 16 chunks)
+    uint32_t acc = 0u;
+    s_coff[0] = 0u;
+    for (int c = 1; c <= p.nchunk; ++c) {
+      acc += s_coff[c];
+      s_coff[c] = acc;
+    }
+  }
+  __syncthreads();
+  const int nc = (int)s_coff[p.nchunk];
+  const bool in_lds = nc <= kCandLds;
+  // candidate e lives in chunk c (s_coff[c] <= e < s_coff[c+1]) at slot e - s_coff[c]
+  auto cand_at = [&](int e) -> const uint64_t* {
+    int c = 0;
+    while (c + 1 < p.nchunk && (int)s_coff[c + 1] <= e) ++c;
+    return cand + c * kDsaChunk + (e - (int)s_coff[c]);
+  };
+  if (in_lds) {  // chunk c's slice is copied by threads 16c .. 16c + 15, four loads in flight each
+    const int c = tid >> 4, j = tid & 15;
+    if (c < p.nchunk) {
+      const int cnt_c = (int)(s_coff[c + 1] - s_coff[c]), off = (int)s_coff[c];
+      for (int i0 = j; i0 < cnt_c; i0 += 16 * kCandPer) {
+        uint64_t v[kCandPer];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // bins from the highest down
-      const int c = (int)hv[e];
-      if (acc < need && acc + c >= need) {
-        s_found[0] = g0 + 3 - e;
-        s_found[1] = acc;
+        for (int u = 0; u < kCandPer; ++u) {
+          const int i = i0 + 16 * u;
+          v[u] = i < cnt_c ? __hip_atomic_load(cand + c * kDsaChunk + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kCandPer; ++u)
+          if (i0 + 16 * u < cnt_c) s_cand[off + i0 + 16 * u] = v[u];
       }
-      acc += c;
+    }
+  }
+  auto cand_get = [&](int e) -> uint64_t {
+    return in_lds ? s_cand[e] : __hip_atomic_load(cand_at(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  int need = p.topk - above0;
+  uint32_t prefix = T0 << 19, pmask = 0xFFF80000u;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 6 : 0;
+    const uint32_t dmask = pass == 0 ? 0x1FFFu : 0x3Fu;
+    __syncthreads();
+    for (int i = tid; i < kDsaBins; i += 256) h[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nc; i += 256) {
+      const uint32_t k = (uint32_t)(cand_get(i) >> 32);
+      if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
     }
     __syncthreads();
+    find_bin(h, pass == 0 ? kDsaBins : 256, need, s_w, s_found);
     prefix |= (uint32_t)s_found[0] << shift;
     pmask |= dmask << shift;
     need -= s_found[1];
     __syncthreads();
   }
-  // prefix is the k-th largest key; take every larger key and the first `need`
-  // equal ones by position
-  int gt = 0, eq = 0;
+  // prefix is the k-th largest key: keys above it are in; `need` ties at it go to
+  // the lowest positions
+  const int nw = (n + 31) / 32;
+  constexpr int WPT = kDsaMaxLen / 32 / 256;
+  uint32_t* sb = s_bits;
+  uint32_t* tb = s_bits + kDsaMaxLen / 32;
+  {
+    uint32_t v[WPT];
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    gt += (k < nvalid && key[k] > prefix) ? 1 : 0;
-    eq += (k < nvalid && key[k] == prefix) ? 1 : 0;
+    for (int e = 0; e < WPT; ++e) {
+      const int i = tid + 256 * e;
+      v[e] = i < nw ? __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < WPT; ++e) {
+      sb[tid + 256 * e] = v[e];
+      tb[tid + 256 * e] = 0u;
+    }
   }
-  int total;
-  const int eb = scan1024(eq, s_w, &total);
-  int take = need - eb;
-  take = take < 0 ? 0 : (take > eq ? eq : take);
-  int o = scan1024(gt + take, s_w, &total);
+  __syncthreads();
+  for (int i = tid; i < nc; i += 256) {
+    const uint64_t e = cand_get(i);
+    const uint32_t k = (uint32_t)(e >> 32), pos = (uint32_t)e;
+    if (k > prefix) atomicOr(&sb[pos >> 5], 1u << (pos & 31));
+    else if (k == prefix) atomicOr(&tb[pos >> 5], 1u << (pos & 31));
+  }
+  __syncthreads();
+  // thread t owns words [WPT*t, WPT*t + WPT): ties taken in position order, then
+  // the selected positions written ascending
+  const int w0 = WPT * tid;
+  int ties = 0;
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    if (k < nvalid) {
-      const bool sel = key[k] > prefix || (key[k] == prefix && take > 0);
-      if (key[k] == prefix && take > 0) --take;
-      if (sel && o < p.topk) out[o++] = base + k;  // o < topk always; the test keeps a bad count in bounds
+  for (int e = 0; e < WPT; ++e) ties += w0 + e < nw ? __popc(tb[w0 + e]) : 0;
+  int total;
+  int tb0 = scan256(ties, s_w, &total);
+  int take = need - tb0;
+  take = take < 0 ? 0 : (take > ties ? ties : take);
+  int cntsel = 0;
+  uint32_t word[WPT];
+#pragma unroll
+  for (int e = 0; e < WPT; ++e) {
+    uint32_t s_ = w0 + e < nw ? sb[w0 + e] : 0u, t_ = w0 + e < nw ? tb[w0 + e] : 0u;
+    while (t_ != 0u && take > 0) {  // lowest tie positions first
+      const uint32_t low = t_ & (~t_ + 1u);
+      s_ |= low;
+      t_ ^= low;
+      --take;
+    }
+    word[e] = s_;
+    cntsel += __popc(s_);
+  }
+  int o = scan256(cntsel, s_w, &total);
+#pragma unroll
+  for (int e = 0; e < WPT; ++e) {
+    uint32_t s_ = word[e];
+    while (s_ != 0u) {
+      const int bit = __builtin_ctz(s_);
+      s_ &= s_ - 1u;
+      if (o < p.topk) out[o++] = 32 * (w0 + e) + bit;
     }
   }
 }
@@ -254,16 +440,19 @@ __global__ __launch_bounds__(kDsaSelThreads) void dsa_select_kernel(DsaParams p)
 // ---------------------------------------------------------------------------
 // 3. attention over the selected tokens
 
-constexpr int kTileTok = 64, kKt = kDsaDqk / 32;  // 18 fragments of 32 dims per 16-row group
-constexpr int kTileBytes = kTileTok * kDsaDqk * 2;  // 72 KB
-constexpr int kMaxTilesPerSplit = 8;
+constexpr int kTileTok = 32, kKt = kDsaDqk / 32;   // 18 fragments of 32 dims per 16-row group
+constexpr int kFrag = (kTileTok / 16) * kKt;         // 36 fragments of 1 KB per tile
+constexpr int kTileBytes = kTileTok * kDsaDqk * 2;   // 36 KB
+constexpr int kNbuf = 4;                             // three tiles in flight while one is used
+constexpr int kMaxSplit = 512;                       // selected tokens per workgroup (host plan)
+constexpr int kCopies = kFrag / 4;                   // copy instructions per wave per tile
 
 __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
-  __shared__ __attribute__((aligned(1024))) char s_buf[2][kTileBytes];
-  __shared__ int s_rows[kMaxTilesPerSplit * kTileTok];
+  __shared__ __attribute__((aligned(1024))) char s_buf[kNbuf][kTileBytes];
+  __shared__ int s_rows[kMaxSplit];
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jt = wave >> 1, hh = wave & 1;  // head tile, token half
+  const int jt = wave >> 1, hh = wave & 1;  // head tile, 16-token row group of each tile
   const int ngrp = p.H / 32, per_b = ngrp * p.ts;
   const int b = blockIdx.x / per_b, r = blockIdx.x - b * per_b;
   const int hg = r / p.ts, sp = r - hg * p.ts;
@@ -280,7 +469,7 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
     }
     return;
   }
-  const int ntl = (t1 - t0 + kTileTok - 1) / kTileTok;  // <= kMaxTilesPerSplit (host plan)
+  const int ntl = (t1 - t0 + kTileTok - 1) / kTileTok;  // <= kMaxSplit / kTileTok (host plan)
   const int32_t* sel = p.sel + (size_t)b * p.topk;
   const uint16_t* cb = p.c + (size_t)b * p.cap * kDsaDqk;
 
@@ -293,20 +482,21 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
 #pragma unroll
     for (int ks = 0; ks < kKt; ++ks) qf[ks] = ld16(qrow + 32 * ks);
   }
-  // 72 fragments of 1 KB per tile; wave w copies fragments w, w+4, ... (18 each):
-  // fragment f = m*18 + ks holds, at 16*lane, dims 32*ks + 8*lg .. of row 16*m + lr
   __syncthreads();
-  auto stage = [&](int it, int buf) {
+  // fragment f = m*18 + ks holds, at 16*lane, dims 32*ks + 8*lg .. of row 16*m + lr;
+  // wave w copies fragments w, w+4, ... (9 per tile)
+  auto stage = [&](int it) {
+    char* dst = s_buf[it % kNbuf];
 #pragma unroll
-    for (int ii = 0; ii < kKt; ++ii) {
+    for (int ii = 0; ii < kCopies; ++ii) {
       const int f = wave + 4 * ii;
       const int m = f / kKt, ks = f - m * kKt;
       const int row = s_rows[kTileTok * it + 16 * m + lr];
-      copy16_to_lds(cb + (size_t)row * kDsaDqk + 32 * ks + 8 * lg, s_buf[buf] + f * 1024);
+      copy16_to_lds(cb + (size_t)row * kDsaDqk + 32 * ks + 8 * lg, dst + f * 1024);
     }
   };
 
-  f32x4_t acc[4][8];  // dim block db (128 dims), tile jj: O^T[128*db + 8*(4lg+i) + jj][head lr]
+  f32x4_t acc[4][8];  // dim block db (128 dims), operand jj: O^T[128*db + 8*(4lg+i) + jj][head lr]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -314,35 +504,29 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
   float mref = -INFINITY, lsum = 0.f;
   const float sc = p.scale_log2;
 
-  stage(0, 0);
+  for (int it = 0; it < kNbuf - 1 && it < ntl; ++it) stage(it);
   for (int it = 0; it < ntl; ++it) {
-    if (it + 1 < ntl) {
-      stage(it + 1, (it + 1) & 1);
-      wait_vmem_le<kKt>();
-    } else {
-      wait_vmem();
-    }
+    if (it + kNbuf - 1 < ntl) stage(it + kNbuf - 1);
+    const int ahead = ntl - 1 - it < kNbuf - 1 ? ntl - 1 - it : kNbuf - 1;  // tiles issued after this one
+    if (ahead >= 3) wait_vmem_le<3 * kCopies>();
+    else if (ahead == 2) wait_vmem_le<2 * kCopies>();
+    else if (ahead == 1) wait_vmem_le<kCopies>();
+    else wait_vmem();
     lds_barrier();
-    const char* kt = s_buf[it & 1];
-    // S^T for this wave's 32 tokens (row groups 2hh, 2hh+1) and 16 heads
-    f32x4_t s[2];
+    const char* kt = s_buf[it % kNbuf];
+    // S^T for this wave's 16 tokens and 16 heads
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      s[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kKt; ++ks) s[mm] = mfma_bf16(lds_k<kDsaDqk>(kt, 2 * hh + mm, ks, lane), qf[ks], s[mm]);
-    }
-    float z[2][4];
+    for (int ks = 0; ks < kKt; ++ks) s = mfma_bf16(lds_k<kDsaDqk>(kt, hh, ks, lane), qf[ks], s);
+    float z[4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = kTileTok * it + 32 * hh + 16 * mm + 4 * lg + i;  // token index within the split
-        z[mm][i] = t0 + tt < t1 ? s[mm][i] * sc : -INFINITY;
-        mx = fmaxf(mx, z[mm][i]);
-      }
-    mx = max_over_groups_swap(mx);  // head lr over the wave's 32 tokens
+    for (int i = 0; i < 4; ++i) {
+      const int tt = kTileTok * it + 16 * hh + 4 * lg + i;  // token index within the split
+      z[i] = t0 + tt < t1 ? s[i] * sc : -INFINITY;
+      mx = fmaxf(mx, z[i]);
+    }
+    mx = max_over_groups_swap(mx);  // head lr over the wave's 16 tokens
     if (mx > mref + 8.f || (mref == -INFINITY && mx > -INFINITY)) {  // move the reference (lazily)
       const float f = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mx);
       lsum *= f;
@@ -353,35 +537,36 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
       mref = mx;
     }
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[mm][i] = z[mm][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[mm][i] - mref);
-        lsum += z[mm][i];
-      }
-    const u32x4_t pb = pack_probs(z[0], z[1]);
-    // O^T += V^T P^T: the values are the first 512 latent dims; lane (lg, lr) reads
-    // the 8 rows of its k-slots, 8 dims 128*db + 8*lr .. of each, from the fragments
+    for (int i = 0; i < 4; ++i) {
+      z[i] = z[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[i] - mref);
+      lsum += z[i];
+    }
+    // P^T in the logit tile's layout is the B operand of the 16x16x16 product
+    // (k-slots 4lg .. 4lg+3 = tokens 4lg + i)
+    const u32x2_t pb = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+    // O^T += V^T P^T: the values are the first 512 latent dims.  Lane (lg, lr) reads
+    // 8 dims 128*db + 8*lr .. of its 4 token rows and transposes them in registers.
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      uint32_t vr[8][4];
       const int c = 16 * db + lr, ks = c >> 2, lgc = c & 3;
+      u32x4_t x[4];
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int R = 32 * hh + step_key(lg, rr);
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(kt + (((R >> 4) * kKt + ks) * 64 + lgc * 16 + (R & 15)) * 16);
-        vr[rr][0] = x[0];
-        vr[rr][1] = x[1];
-        vr[rr][2] = x[2];
-        vr[rr][3] = x[3];
+      for (int rr = 0; rr < 4; ++rr) {
+        const int R = 16 * hh + 4 * lg + rr;
+        x[rr] = *reinterpret_cast<const u32x4_t*>(kt + (((R >> 4) * kKt + ks) * 64 + lgc * 16 + (R & 15)) * 16);
       }
-      pv_step<128>(vr, pb, acc[db]);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int wd = jj >> 1, hf = jj & 1;
+        const u32x2_t va = {pack_halves(x[0][wd], x[1][wd], hf), pack_halves(x[2][wd], x[3][wd], hf)};
+        acc[db][jj] = mfma16_bf16(va, pb, acc[db][jj]);
+      }
     }
     lds_barrier();  // every wave is done with this buffer before it is refilled
   }
   lsum = sum_over_groups_swap(lsum);
 
-  // merge the two token halves of each head tile through LDS, write the partial
+  // merge the two row groups of each head tile through LDS, write the partial
   float* xm = reinterpret_cast<float*>(s_buf[0]) + jt * (16 * 514);  // [16 heads][m, l, 512]
   if (hh == 1) {
     if (lg == 0) {
@@ -426,22 +611,40 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
 // ---------------------------------------------------------------------------
 // 4. exact merge of the token splits: workgroup per (sequence, head), 4 channels per thread
 __global__ __launch_bounds__(128) void dsa_combine_kernel(DsaParams p) {
+  constexpr int MS = 16;  // splits held in registers; more are merged in a second loop
   const int bh = blockIdx.x, b = bh / p.H, h = bh - b * p.H;
   const int ngrp = p.H / 32, hg = h >> 5, hl = h & 31;
   const float* src = p.part + ((size_t)(b * ngrp + hg) * p.ts * 32 + hl) * kPartStride;
   const size_t sstep = (size_t)32 * kPartStride;
+  const int c = 4 * threadIdx.x;
+  float m[MS], l[MS];
+  f32x4_t v[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {  // every load issued before any is used
+    const bool in = s < p.ts;
+    m[s] = in ? src[s * sstep] : -INFINITY;
+    l[s] = in ? src[s * sstep + 1] : 0.f;
+    v[s] = in ? *reinterpret_cast<const f32x4_t*>(src + s * sstep + kPartOut + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   float M = -INFINITY;
-  for (int s = 0; s < p.ts; ++s) M = fmaxf(M, src[s * sstep]);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) M = fmaxf(M, m[s]);
+  for (int s = MS; s < p.ts; ++s) M = fmaxf(M, src[s * sstep]);
   float Ls = 0.f;
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-  const int c = 4 * threadIdx.x;
-  for (int s = 0; s < p.ts; ++s) {
-    const float m = src[s * sstep];
-    if (m == -INFINITY) continue;
-    const float a = __builtin_amdgcn_exp2f(m - M);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const float a = m[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[s] - M);
+    Ls += a * l[s];
+    o = f32x4_t{o[0] + a * v[s][0], o[1] + a * v[s][1], o[2] + a * v[s][2], o[3] + a * v[s][3]};
+  }
+  for (int s = MS; s < p.ts; ++s) {
+    const float ms = src[s * sstep];
+    if (ms == -INFINITY) continue;
+    const float a = __builtin_amdgcn_exp2f(ms - M);
     Ls += a * src[s * sstep + 1];
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + s * sstep + kPartOut + c);
-    o = f32x4_t{o[0] + a * v[0], o[1] + a * v[1], o[2] + a * v[2], o[3] + a * v[3]};
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + s * sstep + kPartOut + c);
+    o = f32x4_t{o[0] + a * x[0], o[1] + a * x[1], o[2] + a * x[2], o[3] + a * x[3]};
   }
   const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
   u32x2_t w;
@@ -455,7 +658,8 @@ hipError_t launch_dsa_t(const DsaParams& p, hipStream_t s, const PhaseEvents* ev
   if (ev) (void)hipEventRecord(ev->ev[0], s);
   hipLaunchKernelGGL((dsa_index_kernel<HI, DI>), dim3((unsigned)(p.B * p.nseg)), dim3(256), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[1], s);
-  hipLaunchKernelGGL(dsa_select_kernel, dim3((unsigned)p.B), dim3(kDsaSelThreads), 0, s, p);
+  hipLaunchKernelGGL(dsa_hist_kernel, dim3((unsigned)(p.B * p.nchunk)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(dsa_select_kernel, dim3((unsigned)(p.B * p.nchunk)), dim3(256), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[2], s);
   hipLaunchKernelGGL(dsa_attn_kernel, dim3((unsigned)(p.B * (p.H / 32) * p.ts)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(dsa_combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(128), 0, s, p);

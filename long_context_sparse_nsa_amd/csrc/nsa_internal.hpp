@@ -128,7 +128,8 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // DeepSeek Sparse Attention decode step (lightning indexer + token top-k +
 // MQA attention over one shared latent per token).
 constexpr int kDsaDqk = 576, kDsaDv = 512, kDsaMaxLen = 65536, kDsaMaxTopk = 4096;
-constexpr int kDsaSelThreads = 1024, kDsaKeysPerThread = kDsaMaxLen / kDsaSelThreads;
+constexpr int kDsaChunk = 4096;     // scores per selection workgroup (256 threads x 16)
+constexpr int kDsaBins = 8192;      // first radix digit: the top 13 bits of a score's order key
 struct DsaParams {
   int B, H, HI, DI, topk;
   float scale_log2;
@@ -144,6 +145,11 @@ struct DsaParams {
   int64_t sstride;                   // cap rounded up to a multiple of 4
   int32_t* sel;                      // [B, topk] (caller's or workspace), ascending, -1 padded
   float* part;                       // workspace [B, H/32, ts, 32, 2 + 512]
+  uint32_t* hist;                    // workspace [B, kDsaBins] (zeroed by the indexer kernel)
+  uint32_t* cnt;                     // workspace [B, 4] (arrivals; zeroed likewise), then [B, nchunk] counts
+  uint32_t* bits;                    // workspace [B, nchunk * 128]: selected-position bitmap
+  uint64_t* cand;                    // workspace [B, cap]: (key << 32 | position) of boundary-bin scores
+  int nchunk;                        // selection workgroups per sequence: ceil(cap / kDsaChunk)
   int seg;                           // indexer tokens per workgroup (multiple of 512)
   int nseg;                          // indexer workgroups per sequence
   int ts;                            // attention token splits per (sequence, 32 heads)
