@@ -173,20 +173,22 @@ nsa_status_t check_dsa(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_
 }
 
 struct DsaPlan {
-  int seg, nseg, ts, nchunk;
+  int seg, nseg, ts, nchunk, hpg;
   int64_t sstride;
   size_t off_scores, off_sel, off_part, off_hist, off_cnt, off_bits, off_cand, total;
 };
 DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   DsaPlan pl{};
-  const int B = dims->batch, ngrp = dims->num_heads / 32;
+  const int B = dims->batch, hpg = dims->num_heads % 64 == 0 ? 64 : 32, ngrp = dims->num_heads / hpg;
+  pl.hpg = hpg;
   // indexer: about 256 workgroups, segments of whole 512-token batches
   const int want = B >= 256 ? 1 : 256 / B;
   int64_t seg = (cap + want - 1) / want;
   seg = (seg + 511) / 512 * 512;
   pl.seg = (int)seg;
   pl.nseg = (int)((cap + seg - 1) / seg);
-  // attention: at most 512 selected tokens per workgroup, about 256 workgroups
+  // attention: at most 512 selected tokens per workgroup, about 128 workgroups
+  // (more splits add partial traffic faster than they add parallelism)
   const int tmin = (top_k + 511) / 512, tmax = (top_k + 63) / 64;
   int ts = 256 / (B * ngrp);
   ts = ts < tmin ? tmin : ts;
@@ -197,7 +199,7 @@ DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   pl.off_sel = align256((size_t)B * pl.sstride * 4);
   pl.off_part = pl.off_sel + align256((size_t)B * top_k * 4);
   pl.nchunk = (int)((cap + nsa::kDsaChunk - 1) / nsa::kDsaChunk);
-  pl.off_hist = pl.off_part + align256((size_t)B * ngrp * ts * 32 * 520 * 4);
+  pl.off_hist = pl.off_part + align256((size_t)B * ngrp * ts * hpg * 520 * 4);
   pl.off_cnt = pl.off_hist + align256((size_t)B * nsa::kDsaBins * 4);
   pl.off_bits = pl.off_cnt + align256((size_t)B * (4 + pl.nchunk) * 4);
   pl.off_cand = pl.off_bits + align256((size_t)B * pl.nchunk * 128 * 4);
@@ -473,6 +475,7 @@ nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float
   p.seg = plan.seg;
   p.nseg = plan.nseg;
   p.ts = plan.ts;
+  p.hpg = plan.hpg;
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_dsa_decode(p, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "DSA decode launch");

@@ -22,13 +22,12 @@
 //     the sequence finishes the select on those candidates (13 + 6 more bits),
 //     takes ties at the threshold from the lowest positions and writes the
 //     positions ascending.
-//  3. dsa_attn_kernel    workgroup = (sequence, 32 heads, token split); 32-token
-//     tiles of latents are gathered into LDS with the direct global->LDS copy,
-//     four buffers (three tiles in flight).  Wave (head tile, 16-token row
-//     group) keeps its own online softmax over its 16 tokens of each tile, so no
-//     per-tile exchange is needed: its P^T feeds the 16x16x16 value product as
-//     is.  The two row groups merge through LDS at the end into one partial per
-//     workgroup.
+//  3. dsa_attn_kernel    workgroup = (sequence, 64 heads -- 32 when the head
+//     count is not a multiple of 64 --, token split); 32-token tiles of latents
+//     are gathered into LDS with the direct global->LDS copy, four buffers
+//     (three tiles in flight), and every wave reads each tile for its own 16
+//     heads: one online softmax per wave, no exchange between waves, and the
+//     tile's latents are gathered once per 64 heads.
 //  4. dsa_combine_kernel merges the token-split partials exactly and writes bf16.
 #include <hip/hip_runtime.h>
 
@@ -447,13 +446,15 @@ constexpr int kNbuf = 4;                             // three tiles in flight wh
 constexpr int kMaxSplit = 512;                       // selected tokens per workgroup (host plan)
 constexpr int kCopies = kFrag / 4;                   // copy instructions per wave per tile
 
-__global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
+template <int NW>  // waves per workgroup; each owns 16 heads over every token of the split
+__global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
+  constexpr int NT = 64 * NW, HPG = 16 * NW, NCP = kFrag / NW;  // threads, heads, copies per wave per tile
+  static_assert(kFrag % NW == 0, "whole fragments per wave");
   __shared__ __attribute__((aligned(1024))) char s_buf[kNbuf][kTileBytes];
   __shared__ int s_rows[kMaxSplit];
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jt = wave >> 1, hh = wave & 1;  // head tile, 16-token row group of each tile
-  const int ngrp = p.H / 32, per_b = ngrp * p.ts;
+  const int ngrp = p.H / HPG, per_b = ngrp * p.ts;
   const int b = blockIdx.x / per_b, r = blockIdx.x - b * per_b;
   const int hg = r / p.ts, sp = r - hg * p.ts;
   const int64_t L = p.seq_lens[b];
@@ -461,9 +462,9 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
   const int nsel = n < p.topk ? n : p.topk;
   const int per = ((nsel + p.ts - 1) / p.ts + kTileTok - 1) / kTileTok * kTileTok;
   const int t0 = sp * per, t1 = t0 + per < nsel ? t0 + per : nsel;
-  float* part = p.part + ((size_t)(b * ngrp + hg) * p.ts + sp) * 32 * kPartStride;
+  float* part = p.part + ((size_t)(b * ngrp + hg) * p.ts + sp) * HPG * kPartStride;
   if (t0 >= t1) {  // empty split
-    if (tid < 32) {
+    if (tid < HPG) {
       part[tid * kPartStride] = -INFINITY;
       part[tid * kPartStride + 1] = 0.f;
     }
@@ -474,24 +475,30 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
   const uint16_t* cb = p.c + (size_t)b * p.cap * kDsaDqk;
 
   // the split's selected positions, in LDS (rows past the end repeat the last one)
-  for (int i = tid; i < ntl * kTileTok; i += 256) s_rows[i] = sel[t0 + i < t1 ? t0 + i : t1 - 1];
+  for (int i = tid; i < ntl * kTileTok; i += NT) s_rows[i] = sel[t0 + i < t1 ? t0 + i : t1 - 1];
   // q fragments of this wave's 16 heads: B operand, head lr, dims 32*ks + 8*lg .. +8
   u32x4_t qf[kKt];
   {
-    const uint16_t* qrow = p.q + ((size_t)b * p.H + 32 * hg + 16 * jt + lr) * kDsaDqk + 8 * lg;
+    const uint16_t* qrow = p.q + ((size_t)b * p.H + HPG * hg + 16 * wave + lr) * kDsaDqk + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < kKt; ++ks) qf[ks] = ld16(qrow + 32 * ks);
   }
   __syncthreads();
-  // fragment f = m*18 + ks holds, at 16*lane, dims 32*ks + 8*lg .. of row 16*m + lr;
-  // wave w copies fragments w, w+4, ... (9 per tile)
+  // Fragment f = m*18 + ks holds the 16-byte chunks (dims 32*ks + 8*g .. of row
+  // 16*m + R) for g < 4, R < 16 in the 64 slots of 1 KB, chunk (g, R) at slot
+  // swz(g, R, ks) = (16*g + R) ^ ((2*g + ks) & 7): the S^T reads (lane (g, R))
+  // stay a permutation of the slots, and the V reads -- 16 lanes on one row
+  // across 16 chunks -- spread over the LDS banks (two lanes per bank group
+  // instead of sixteen).  The copy writes lane i's chunk at slot i, so lane i
+  // fetches the chunk that belongs there.  Wave w copies fragments w, w+NW, ...
   auto stage = [&](int it) {
     char* dst = s_buf[it % kNbuf];
 #pragma unroll
-    for (int ii = 0; ii < kCopies; ++ii) {
-      const int f = wave + 4 * ii;
+    for (int ii = 0; ii < NCP; ++ii) {
+      const int f = wave + NW * ii;
       const int m = f / kKt, ks = f - m * kKt;
-      const int row = s_rows[kTileTok * it + 16 * m + lr];
+      const int R = lr ^ ((2 * lg + ks) & 7);
+      const int row = s_rows[kTileTok * it + 16 * m + R];
       copy16_to_lds(cb + (size_t)row * kDsaDqk + 32 * ks + 8 * lg, dst + f * 1024);
     }
   };
@@ -508,25 +515,33 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
   for (int it = 0; it < ntl; ++it) {
     if (it + kNbuf - 1 < ntl) stage(it + kNbuf - 1);
     const int ahead = ntl - 1 - it < kNbuf - 1 ? ntl - 1 - it : kNbuf - 1;  // tiles issued after this one
-    if (ahead >= 3) wait_vmem_le<3 * kCopies>();
-    else if (ahead == 2) wait_vmem_le<2 * kCopies>();
-    else if (ahead == 1) wait_vmem_le<kCopies>();
+    if (ahead >= 3) wait_vmem_le<3 * NCP>();
+    else if (ahead == 2) wait_vmem_le<2 * NCP>();
+    else if (ahead == 1) wait_vmem_le<NCP>();
     else wait_vmem();
     lds_barrier();
     const char* kt = s_buf[it % kNbuf];
-    // S^T for this wave's 16 tokens and 16 heads
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    // S^T for the tile's 32 tokens (row groups 0 and 1) and this wave's 16 heads
+    f32x4_t s[2];
 #pragma unroll
-    for (int ks = 0; ks < kKt; ++ks) s = mfma_bf16(lds_k<kDsaDqk>(kt, hh, ks, lane), qf[ks], s);
-    float z[4];
+    for (int mm = 0; mm < 2; ++mm) {
+      s[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKt; ++ks)
+        s[mm] = mfma_bf16(*reinterpret_cast<const u32x4_t*>(kt + ((mm * kKt + ks) * 64 + (lane ^ ((2 * lg + ks) & 7))) * 16),
+                          qf[ks], s[mm]);
+    }
+    float z[2][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = kTileTok * it + 16 * hh + 4 * lg + i;  // token index within the split
-      z[i] = t0 + tt < t1 ? s[i] * sc : -INFINITY;
-      mx = fmaxf(mx, z[i]);
-    }
-    mx = max_over_groups_swap(mx);  // head lr over the wave's 16 tokens
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = kTileTok * it + 16 * mm + 4 * lg + i;  // token index within the split
+        z[mm][i] = t0 + tt < t1 ? s[mm][i] * sc : -INFINITY;
+        mx = fmaxf(mx, z[mm][i]);
+      }
+    mx = max_over_groups_swap(mx);  // head lr over the tile's 32 tokens
     if (mx > mref + 8.f || (mref == -INFINITY && mx > -INFINITY)) {  // move the reference (lazily)
       const float f = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mx);
       lsum *= f;
@@ -537,75 +552,48 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
       mref = mx;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = z[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[i] - mref);
-      lsum += z[i];
-    }
-    // P^T in the logit tile's layout is the B operand of the 16x16x16 product
-    // (k-slots 4lg .. 4lg+3 = tokens 4lg + i)
-    const u32x2_t pb = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-    // O^T += V^T P^T: the values are the first 512 latent dims.  Lane (lg, lr) reads
-    // 8 dims 128*db + 8*lr .. of its 4 token rows and transposes them in registers.
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[mm][i] = z[mm][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[mm][i] - mref);
+        lsum += z[mm][i];
+      }
+    const u32x4_t pb = pack_probs(z[0], z[1]);
+    // O^T += V^T P^T: the values are the first 512 latent dims; lane (lg, lr) reads
+    // the 8 rows of its k-slots, 8 dims 128*db + 8*lr .. of each, from the fragments
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
+      uint32_t vr[8][4];
       const int c = 16 * db + lr, ks = c >> 2, lgc = c & 3;
-      u32x4_t x[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int R = 16 * hh + 4 * lg + rr;
-        x[rr] = *reinterpret_cast<const u32x4_t*>(kt + (((R >> 4) * kKt + ks) * 64 + lgc * 16 + (R & 15)) * 16);
+      for (int rr = 0; rr < 8; ++rr) {
+        const int R = step_key(lg, rr);
+        const int slot = (lgc * 16 + (R & 15)) ^ ((2 * lgc + ks) & 7);
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(kt + (((R >> 4) * kKt + ks) * 64 + slot) * 16);
+        vr[rr][0] = x[0];
+        vr[rr][1] = x[1];
+        vr[rr][2] = x[2];
+        vr[rr][3] = x[3];
       }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int wd = jj >> 1, hf = jj & 1;
-        const u32x2_t va = {pack_halves(x[0][wd], x[1][wd], hf), pack_halves(x[2][wd], x[3][wd], hf)};
-        acc[db][jj] = mfma16_bf16(va, pb, acc[db][jj]);
-      }
+      pv_step<128>(vr, pb, acc[db]);
     }
     lds_barrier();  // every wave is done with this buffer before it is refilled
   }
   lsum = sum_over_groups_swap(lsum);
-
-  // merge the two row groups of each head tile through LDS, write the partial
-  float* xm = reinterpret_cast<float*>(s_buf[0]) + jt * (16 * 514);  // [16 heads][m, l, 512]
-  if (hh == 1) {
-    if (lg == 0) {
-      xm[lr * 514] = mref;
-      xm[lr * 514 + 1] = lsum;
-    }
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xm[lr * 514 + 2 + 128 * db + acc_channel<128>(lg, i, jj)] = acc[db][jj][i];
+  // this wave's 16 heads: (m, l, O) to the partial
+  float* dst = part + (size_t)(16 * wave + lr) * kPartStride;
+  if (lg == 0) {
+    dst[0] = mref;
+    dst[1] = lsum;
   }
-  lds_barrier();
-  if (hh == 0) {
-    const float m1 = xm[lr * 514], l1 = xm[lr * 514 + 1];
-    const float M = fmaxf(mref, m1);
-    const float a0 = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - M);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-    float* dst = part + (size_t)(16 * jt + lr) * kPartStride;
-    if (lg == 0) {
-      dst[0] = M;
-      dst[1] = a0 * lsum + a1 * l1;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* o = dst + kPartOut + 128 * db + acc_channel<128>(lg, i, 0);  // 8 consecutive channels
+      *reinterpret_cast<f32x4_t*>(o) = f32x4_t{acc[db][0][i], acc[db][1][i], acc[db][2][i], acc[db][3][i]};
+      *reinterpret_cast<f32x4_t*>(o + 4) = f32x4_t{acc[db][4][i], acc[db][5][i], acc[db][6][i], acc[db][7][i]};
     }
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int ch = 128 * db + acc_channel<128>(lg, i, jj);
-          v[jj] = a0 * acc[db][jj][i] + a1 * xm[lr * 514 + 2 + ch];
-        }
-        float* o = dst + kPartOut + 128 * db + acc_channel<128>(lg, i, 0);  // 8 consecutive channels
-        *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4_t*>(o + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
-      }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -613,9 +601,9 @@ __global__ __launch_bounds__(256, 1) void dsa_attn_kernel(DsaParams p) {
 __global__ __launch_bounds__(128) void dsa_combine_kernel(DsaParams p) {
   constexpr int MS = 16;  // splits held in registers; more are merged in a second loop
   const int bh = blockIdx.x, b = bh / p.H, h = bh - b * p.H;
-  const int ngrp = p.H / 32, hg = h >> 5, hl = h & 31;
-  const float* src = p.part + ((size_t)(b * ngrp + hg) * p.ts * 32 + hl) * kPartStride;
-  const size_t sstep = (size_t)32 * kPartStride;
+  const int ngrp = p.H / p.hpg, hg = h / p.hpg, hl = h - hg * p.hpg;
+  const float* src = p.part + ((size_t)(b * ngrp + hg) * p.ts * p.hpg + hl) * kPartStride;
+  const size_t sstep = (size_t)p.hpg * kPartStride;
   const int c = 4 * threadIdx.x;
   float m[MS], l[MS];
   f32x4_t v[MS];
@@ -661,7 +649,10 @@ hipError_t launch_dsa_t(const DsaParams& p, hipStream_t s, const PhaseEvents* ev
   hipLaunchKernelGGL(dsa_hist_kernel, dim3((unsigned)(p.B * p.nchunk)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(dsa_select_kernel, dim3((unsigned)(p.B * p.nchunk)), dim3(256), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[2], s);
-  hipLaunchKernelGGL(dsa_attn_kernel, dim3((unsigned)(p.B * (p.H / 32) * p.ts)), dim3(256), 0, s, p);
+  if (p.hpg == 64)
+    hipLaunchKernelGGL((dsa_attn_kernel<4>), dim3((unsigned)(p.B * (p.H / 64) * p.ts)), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((dsa_attn_kernel<2>), dim3((unsigned)(p.B * (p.H / 32) * p.ts)), dim3(128), 0, s, p);
   hipLaunchKernelGGL(dsa_combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(128), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[3], s);
   return hipGetLastError();

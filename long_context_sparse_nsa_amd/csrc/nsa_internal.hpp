@@ -144,7 +144,7 @@ struct DsaParams {
   float* scores;                     // workspace [B, sstride]
   int64_t sstride;                   // cap rounded up to a multiple of 4
   int32_t* sel;                      // [B, topk] (caller's or workspace), ascending, -1 padded
-  float* part;                       // workspace [B, H/32, ts, 32, 2 + 512]
+  float* part;                       // workspace [B, H/hpg, ts, hpg, 520]: m, l, pad, 512 outputs
   uint32_t* hist;                    // workspace [B, kDsaBins] (zeroed by the indexer kernel)
   uint32_t* cnt;                     // workspace [B, 4] (arrivals; zeroed likewise), then [B, nchunk] counts
   uint32_t* bits;                    // workspace [B, nchunk * 128]: selected-position bitmap
@@ -152,7 +152,8 @@ struct DsaParams {
   int nchunk;                        // selection workgroups per sequence: ceil(cap / kDsaChunk)
   int seg;                           // indexer tokens per workgroup (multiple of 512)
   int nseg;                          // indexer workgroups per sequence
-  int ts;                            // attention token splits per (sequence, 32 heads)
+  int ts;                            // attention token splits per (sequence, head group)
+  int hpg;                           // heads per attention workgroup: 64, or 32 when H % 64 != 0
 };
 
 DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len);
