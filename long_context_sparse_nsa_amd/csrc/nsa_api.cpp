@@ -199,7 +199,7 @@ DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   pl.off_sel = align256((size_t)B * pl.sstride * 4);
   pl.off_part = pl.off_sel + align256((size_t)B * top_k * 4);
   pl.nchunk = (int)((cap + nsa::kDsaChunk - 1) / nsa::kDsaChunk);
-  pl.off_hist = pl.off_part + align256((size_t)B * ngrp * ts * hpg * 520 * 4);
+  pl.off_hist = pl.off_part + align256((size_t)B * ngrp * ts * hpg * (8 + 256) * 4);
   pl.off_cnt = pl.off_hist + align256((size_t)B * nsa::kDsaBins * 4);
   pl.off_bits = pl.off_cnt + align256((size_t)B * (4 + pl.nchunk) * 4);
   pl.off_cand = pl.off_bits + align256((size_t)B * pl.nchunk * 128 * 4);

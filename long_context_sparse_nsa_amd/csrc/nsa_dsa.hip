@@ -40,8 +40,20 @@ namespace nsa {
 
 namespace {
 
-constexpr int kPartStride = 520;  // floats per (head) partial: m, l, 6 pad, 512 outputs
+// Per (head, split) partial: m and l (fp32), 6 floats of padding, then the split's
+// output divided by its own l as 512 fp16 values (weighted averages of bf16
+// values: fp16's 11-bit significand adds about 2^-12 relative error, well below
+// the bf16 rounding of the result, at half the bytes of fp32).
+constexpr int kPartStride = 8 + 512 / 2;  // floats
 constexpr int kPartOut = 8;
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
+__device__ __forceinline__ f32x2_t unpack_f16x2(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+}
 
 __device__ __forceinline__ f32x4_t mfma_fp8(long a, long b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
@@ -580,19 +592,22 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
     lds_barrier();  // every wave is done with this buffer before it is refilled
   }
   lsum = sum_over_groups_swap(lsum);
-  // this wave's 16 heads: (m, l, O) to the partial
+  // this wave's 16 heads: (m, l, O / l) to the partial
   float* dst = part + (size_t)(16 * wave + lr) * kPartStride;
   if (lg == 0) {
     dst[0] = mref;
     dst[1] = lsum;
   }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  uint16_t* oh = reinterpret_cast<uint16_t*>(dst + kPartOut);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* o = dst + kPartOut + 128 * db + acc_channel<128>(lg, i, 0);  // 8 consecutive channels
-      *reinterpret_cast<f32x4_t*>(o) = f32x4_t{acc[db][0][i], acc[db][1][i], acc[db][2][i], acc[db][3][i]};
-      *reinterpret_cast<f32x4_t*>(o + 4) = f32x4_t{acc[db][4][i], acc[db][5][i], acc[db][6][i], acc[db][7][i]};
+    for (int i = 0; i < 4; ++i) {  // 8 consecutive channels 128*db + 8*(4lg+i) .. in one 16-byte store
+      const f32x4_t* a = &acc[db][0];
+      *reinterpret_cast<u32x4_t*>(oh + 128 * db + acc_channel<128>(lg, i, 0)) =
+          u32x4_t{pack_f16x2(a[0][i] * inv, a[1][i] * inv), pack_f16x2(a[2][i] * inv, a[3][i] * inv),
+                  pack_f16x2(a[4][i] * inv, a[5][i] * inv), pack_f16x2(a[6][i] * inv, a[7][i] * inv)};
     }
 }
 
@@ -604,15 +619,16 @@ __global__ __launch_bounds__(128) void dsa_combine_kernel(DsaParams p) {
   const int ngrp = p.H / p.hpg, hg = h / p.hpg, hl = h - hg * p.hpg;
   const float* src = p.part + ((size_t)(b * ngrp + hg) * p.ts * p.hpg + hl) * kPartStride;
   const size_t sstep = (size_t)p.hpg * kPartStride;
-  const int c = 4 * threadIdx.x;
+  const int c = 4 * threadIdx.x;  // this thread's 4 channels
   float m[MS], l[MS];
-  f32x4_t v[MS];
+  u32x2_t v[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {  // every load issued before any is used
     const bool in = s < p.ts;
     m[s] = in ? src[s * sstep] : -INFINITY;
     l[s] = in ? src[s * sstep + 1] : 0.f;
-    v[s] = in ? *reinterpret_cast<const f32x4_t*>(src + s * sstep + kPartOut + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    v[s] = in ? *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(src + s * sstep + kPartOut) + c)
+              : u32x2_t{0u, 0u};
   }
   float M = -INFINITY;
 #pragma unroll
@@ -620,20 +636,18 @@ __global__ __launch_bounds__(128) void dsa_combine_kernel(DsaParams p) {
   for (int s = MS; s < p.ts; ++s) M = fmaxf(M, src[s * sstep]);
   float Ls = 0.f;
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](float ms, float ls, u32x2_t w) {
+    if (ms == -INFINITY) return;
+    const float a = __builtin_amdgcn_exp2f(ms - M) * ls;  // the split's weight: exp(m - M) * l
+    const f32x2_t x0 = unpack_f16x2(w[0]), x1 = unpack_f16x2(w[1]);
+    Ls += a;
+    o = f32x4_t{o[0] + a * x0[0], o[1] + a * x0[1], o[2] + a * x1[0], o[3] + a * x1[1]};
+  };
 #pragma unroll
-  for (int s = 0; s < MS; ++s) {
-    const float a = m[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[s] - M);
-    Ls += a * l[s];
-    o = f32x4_t{o[0] + a * v[s][0], o[1] + a * v[s][1], o[2] + a * v[s][2], o[3] + a * v[s][3]};
-  }
-  for (int s = MS; s < p.ts; ++s) {
-    const float ms = src[s * sstep];
-    if (ms == -INFINITY) continue;
-    const float a = __builtin_amdgcn_exp2f(ms - M);
-    Ls += a * src[s * sstep + 1];
-    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + s * sstep + kPartOut + c);
-    o = f32x4_t{o[0] + a * x[0], o[1] + a * x[1], o[2] + a * x[2], o[3] + a * x[3]};
-  }
+  for (int s = 0; s < MS; ++s) add(m[s], l[s], v[s]);
+  for (int s = MS; s < p.ts; ++s)
+    add(src[s * sstep], src[s * sstep + 1],
+        *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(src + s * sstep + kPartOut) + c));
   const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
   u32x2_t w;
   w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);

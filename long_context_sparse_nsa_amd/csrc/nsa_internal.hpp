@@ -144,7 +144,7 @@ struct DsaParams {
   float* scores;                     // workspace [B, sstride]
   int64_t sstride;                   // cap rounded up to a multiple of 4
   int32_t* sel;                      // [B, topk] (caller's or workspace), ascending, -1 padded
-  float* part;                       // workspace [B, H/hpg, ts, hpg, 520]: m, l, pad, 512 outputs
+  float* part;                       // workspace [B, H/hpg, ts, hpg, 264]: m, l, pad, 512 fp16 outputs / l
   uint32_t* hist;                    // workspace [B, kDsaBins] (zeroed by the indexer kernel)
   uint32_t* cnt;                     // workspace [B, 4] (arrivals; zeroed likewise), then [B, nchunk] counts
   uint32_t* bits;                    // workspace [B, nchunk * 128]: selected-position bitmap
