@@ -155,6 +155,41 @@ def test_append_workspace_size_and_validation():
                                    f, need, None) == A.NSA_ERROR_UNSUPPORTED
 
 
+def _dsa_dims(**kw):
+    a = dict(batch=8, num_heads=128, d_qk=576, d_v=512, idx_heads=16, idx_dim=128)
+    a.update(kw)
+    return N.make_dsa_dims(**a)
+
+
+def test_dsa_workspace_and_validation():
+    ws = N.nsa_dsa_decode_workspace_size(_dsa_dims(), 2048, 65536)
+    # at least the fp32 scores and the selection buffer
+    assert ws >= 8 * 65536 * 4 + 8 * 2048 * 4
+    assert N.nsa_dsa_decode_workspace_size(_dsa_dims(batch=1), 2048, 4096) < ws
+    for kw, k, L, status in [
+        (dict(d_qk=512), 2048, 4096, A.NSA_ERROR_UNSUPPORTED),
+        (dict(num_heads=48), 2048, 4096, A.NSA_ERROR_UNSUPPORTED),
+        (dict(idx_heads=8), 2048, 4096, A.NSA_ERROR_UNSUPPORTED),
+        (dict(idx_dim=96), 2048, 4096, A.NSA_ERROR_UNSUPPORTED),
+        ({}, 4097, 4096, A.NSA_ERROR_UNSUPPORTED),
+        ({}, 2048, 65537, A.NSA_ERROR_UNSUPPORTED),
+        ({}, 0, 4096, A.NSA_ERROR_INVALID_VALUE),
+        (dict(batch=0), 2048, 4096, A.NSA_ERROR_INVALID_VALUE),
+    ]:
+        with pytest.raises(N.NSAError) as e:
+            N.nsa_dsa_decode_workspace_size(_dsa_dims(**kw), k, L)
+        assert e.value.status == status
+    lib = A.load_library()
+    d = _dsa_dims()
+    f = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    need = N.nsa_dsa_decode_workspace_size(d, 2048, 65536)
+    call = lambda q, ws, nb: lib.nsa_dsa_decode_fwd(ctypes.byref(d), 2048, 0.0, q, f, f, f, f, f, 65536, f, None, ws,
+                                                    nb, None)
+    assert call(None, f, need) == A.NSA_ERROR_INVALID_VALUE and "NULL" in N.nsa_last_error()
+    assert call(f, f, need - 1) == A.NSA_ERROR_WORKSPACE
+    assert call(f, None, need) == A.NSA_ERROR_WORKSPACE
+
+
 def test_null_dims_and_config():
     lib = A.load_library()
     out = ctypes.c_size_t(0)
