@@ -521,6 +521,8 @@ def bench_dsa(args, torch, N, I):
                indexer_gbs=b_keys / (ph[0] * 1e-3) / 1e9, attention_tflops=flops / (ph[2] * 1e-3) / 1e12,
                attention_bytes=b_sel, attention_flops=flops)
     res["hbm_frac"] = res["gbs"] / HBM_PEAK_GBS
+    if not args.no_cpu:
+        res["cpu"] = dsa_cpu_baseline(case, args.cpu_seconds / 2)
     log(f"[bench] dsa {wl.name}: {ms * 1e3:.1f} us/step, {res['tokens_per_s']:.4g} tok/s, {res['gbs']:.0f} GB/s "
         f"({100 * res['hbm_frac']:.1f}%); indexer {ph[0] * 1e3:.1f} us ({res['indexer_gbs']:.0f} GB/s), select "
         f"{ph[1] * 1e3:.1f} us, attention+combine {ph[2] * 1e3:.1f} us ({res['attention_tflops']:.0f} TFLOP/s)")
@@ -557,6 +559,28 @@ def cpu_baseline(case, min_seconds):
     return dict(value=tokens / elapsed, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"{tokens} decode tokens (sequences {seqs} x {wl.num_kv_heads} KV groups, repeated) of "
                        f"{wl.name}; oracle-compressed cache precomputed untimed; {elapsed:.1f} s of CPU work")
+
+
+def dsa_cpu_baseline(case, min_seconds):
+    """The float64 DSA oracle on a bounded sample of decode queries (this host's cores)."""
+    from oracle import dsa_oracle as D
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    tokens, elapsed = 0, 0.0
+    while elapsed < min_seconds:
+        for b in range(case.wl.batch):
+            t0 = time.perf_counter()
+            D.decode_sequence(case, b)
+            elapsed += time.perf_counter() - t0
+            tokens += 1
+            if elapsed >= min_seconds:
+                break
+    return dict(value=tokens / elapsed, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{tokens} DSA decode queries of {case.wl.name} (indexer over the full context, top-k, "
+                       f"attention); {elapsed:.1f} s of CPU work")
 
 
 def kernels_only(args, torch, N, I):
@@ -737,7 +761,8 @@ def main():
             "indexer": {"kernel": "dsa_index_kernel", "bound": "hbm", "GB/s": dsa["indexer_gbs"],
                         "frac": dsa["indexer_gbs"] / HBM_PEAK_GBS},
             "attention": {"kernels": "dsa_attn_kernel + dsa_combine_kernel", "TFLOP/s": dsa["attention_tflops"],
-                          "mfma_frac": dsa["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS}}
+                          "mfma_frac": dsa["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS},
+            "cpu_oracle": dsa.get("cpu")}
     if dec.get("serving"):
         sv = dec["serving"]
         line["serving_step"] = {
