@@ -13,9 +13,11 @@ through the selected and window branches.  [FLI] lesson 5.5/02, section
 
 The forward of nsa_oracle.nsa_query is restated with float64 torch tensors so
 that autograd takes the derivative of the scalar  sum_{t,h} dout[t,h] . out[t,h].
-The selected block ids are constants (from the forward oracle's top-n); the bf16
-rounding of the compressed cache is taken as the identity (its derivative is not
-defined; a rounding step passes the gradient through unchanged).
+The selected block ids are constants (from the forward oracle's top-n).  The
+forward stores the compressed cache in bf16, so by default the values used here
+are the rounded ones (exactly the forward oracle's), while the derivative of the
+rounding is taken as the identity (it is zero almost everywhere, and a rounding
+step passes the gradient through unchanged).
 """
 from __future__ import annotations
 
@@ -29,13 +31,20 @@ from oracle import nsa_oracle as O
 F64 = torch.float64
 
 
-def compress_t(K: torch.Tensor, W: torch.Tensor, PE: torch.Tensor, l: int, d: int) -> torch.Tensor:
-    """Compressed keys (or values) of one sequence and head: (K[i*d : i*d+l] + PE) flattened, times W."""
+def compress_t(K: torch.Tensor, W: torch.Tensor, PE: torch.Tensor, l: int, d: int,
+               round_bf16: bool = False) -> torch.Tensor:
+    """Compressed keys (or values) of one sequence and head: (K[i*d : i*d+l] + PE) flattened, times W.
+
+    With round_bf16 the value is rounded to bf16 as the forward stores it; the
+    gradient passes through the rounding unchanged."""
     nc = O.n_compressed(K.shape[0], l, d)
     if nc == 0:
         return torch.zeros((0, W.shape[1]), dtype=F64)
     X = torch.stack([(K[i * d:i * d + l] + PE).reshape(-1) for i in range(nc)])
-    return X @ W
+    Y = X @ W
+    if round_bf16:
+        Y = Y + (torch.from_numpy(O.round_to_bf16(Y.detach().numpy())) - Y).detach()
+    return Y
 
 
 def attend_t(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale: float) -> torch.Tensor:
@@ -59,12 +68,14 @@ def query_out_t(q, K, V, Kc, Vc, t: int, gates, p, idx: Sequence[int], scale: fl
 
 def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarray, PEk: np.ndarray,
                       Wv: np.ndarray, PEv: np.ndarray, gates: np.ndarray, dout: np.ndarray, rows: Sequence[int],
-                      p, sel: Optional[Sequence[Sequence[int]]] = None, scale: Optional[float] = None) -> dict:
+                      p, sel: Optional[Sequence[Sequence[int]]] = None, scale: Optional[float] = None,
+                      round_cmp: bool = True) -> dict:
     """Gradients of  sum_{t in rows} sum_h dout[t,h] . out[t,h]  for one sequence and KV group.
 
     Q [T, G, dk] (the group's query heads per position), K [T, dk], V [T, dv], Wk [l*dk, dk],
     PEk [l, dk], Wv [l*dv, dv], PEv [l, dv], gates [T, G, 3], dout [T, G, dv].
     ``sel`` gives the selected block ids per row; by default the forward oracle's top-n.
+    ``round_cmp`` uses the bf16-rounded compressed cache values (as the forward does).
     Returns float64 numpy arrays: dQ, dK, dV, dWk, dPEk, dWv, dPEv, dgates (shapes of the inputs).
     """
     dk_ = Q.shape[2]
@@ -77,8 +88,8 @@ def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarra
     Wvt = torch.tensor(Wv, dtype=F64, requires_grad=True)
     PEvt = torch.tensor(PEv, dtype=F64, requires_grad=True)
     Gt = torch.tensor(gates, dtype=F64, requires_grad=True)
-    Kc = compress_t(Kt, Wkt, PEkt, p.l, p.d)
-    Vc = compress_t(Vt, Wvt, PEvt, p.l, p.d)
+    Kc = compress_t(Kt, Wkt, PEkt, p.l, p.d, round_cmp)
+    Vc = compress_t(Vt, Wvt, PEvt, p.l, p.d, round_cmp)
     if sel is None:  # the forward oracle's selection (with the bf16-rounded compressed cache)
         Kc_o = O.compress(K, Wk, PEk, p.l, p.d)
         Vc_o = O.compress(V, Wv, PEv, p.l, p.d)
