@@ -270,6 +270,75 @@ nsa_status_t nsa_decode_workspace_size(const nsa_dims_t* dims, const nsa_config_
 nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                         int64_t seq_len, int32_t compress_in_call, size_t* bytes);
 
+/*
+ * nsa_prefill_bwd — gradients of the causal prefill for training.  The pages fix
+ * what flows where ("Native Sparse Attention (DeepSeek NSA)" lesson, the section
+ * on native trainability): the top-n choice only picks which blocks are read and
+ * is held constant, the compressed branch passes gradient to the compressed
+ * cache, the selected and window branches to the raw keys and values; the
+ * output is sum_c g_c o_c ("NSA: три ветви").  For every position t, head h
+ * and branch c (softmax o_c over the branch's keys, lse_c its log-sum-exp):
+ *   dgates[t, h, c] = dout . o_c
+ *   dq    = s sum_c sum_k P (g_c dout.v_k - g_c dout.o_c) k
+ *   dk, dv (raw) from the selected and window branches; dk_cmp, dv_cmp from the
+ *   compressed branch (feed them to nsa_compress_bwd for the compression MLP).
+ * The branch statistics (lse_c, D_c = g_c dout . o_c) are recomputed from the
+ * inputs in a first pass and kept in the workspace.
+ *
+ *   q, k, v, k_cmp, v_cmp  as for nsa_prefill_fwd; the compressed cache is the
+ *          one the forward used (required when seq_len >= l).
+ *   gates  float32 [B, T, Hq, 3] the forward's gate values (with the gate
+ *          network, its sigmoid outputs; its own chain rule is the caller's).
+ *   sel_idx  int32 [B, T, Hkv, n_sel]: the forward's sel_idx_out (ascending,
+ *          -1 padded; any other content gives undefined gradients).
+ *   dout   bf16 [B, T, Hq, d_v] gradient of the output.
+ *   dq     float32 [B, T, Hq, d_k]             (written)
+ *   dk, dv float32 [B, Hkv, T, d_k / d_v]       (written)
+ *   dk_cmp, dv_cmp  float32 [B, Hkv, nc, d_k / d_v], nc = floor((T-l)/d)+1
+ *          (written; may be NULL when T < l)
+ *   dgates float32 [B, T, Hq, 3]               (written)
+ * Products are bf16 MFMA with fp32 sums (probabilities and dS rounded to bf16
+ * as operands).  The selected and compressed contributions are added with fp32
+ * atomics, so the last bits of dk, dv, dk_cmp and dv_cmp may vary between runs.
+ */
+nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
+                             const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* k_cmp, const uint16_t* v_cmp,
+                             const float* gates, const int32_t* sel_idx, const uint16_t* dout,
+                             float* dq, float* dk, float* dv, float* dk_cmp, float* dv_cmp,
+                             float* dgates, void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes for nsa_prefill_bwd (host-only): lse and D [3, B, T, Hq] fp32
+ * and a selection bitmap [B, Hkv, ceil(T/l_sel), ceil(T/32)] uint32.  Contents
+ * on entry do not matter. */
+nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                                            int64_t seq_len, size_t* bytes);
+
+/*
+ * nsa_compress_bwd — backward of nsa_compress_kv for one cache (which = 0:
+ * keys with w_k, pe_k, d_k; which = 1: values with w_v, pe_v, d_v), dense layout
+ * of nsa_prefill_fwd ([B, Hkv, T, D] raw rows, [B, Hkv, nc, D] compressed rows).
+ * With X_i = (x[i*d : i*d+l] + pe) flattened and y_i = X_i w ("NSA: три ветви",
+ * compressed branch; "Build it" step 1 of the NSA lesson):
+ *   dx[t] += sum over the blocks i covering t of (dy_i w^T)[t - i*d]   (added)
+ *   dw     = sum_i X_i^T dy_i                                           (written)
+ *   dpe    = sum_i dy_i w^T                                             (written)
+ * summed over all sequences and heads, in fp32, in a fixed order (run-to-run
+ * identical).  The bf16 rounding of the forward's compressed rows is taken as
+ * the identity.
+ *   x      bf16 raw rows; w bf16 [l*D, D]; pe bf16 [l, D]
+ *   dy     float32 [B, Hkv, nc, D] (e.g. nsa_prefill_bwd's dk_cmp); may be NULL when T < l
+ *   dx     float32 [B, Hkv, T, D], accumulated into (e.g. nsa_prefill_bwd's dk)
+ *   dw     float32 [l*D, D]; dpe float32 [l, D]
+ */
+nsa_status_t nsa_compress_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
+                              int32_t which, const uint16_t* x, const uint16_t* w, const uint16_t* pe,
+                              const float* dy, float* dx, float* dw, float* dpe,
+                              void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes for nsa_compress_bwd (host-only): dX [B*Hkv*nc, l*D] fp32 and
+ * 64 x D fp32 partial column sums. */
+nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                                             int64_t seq_len, int32_t which, size_t* bytes);
+
 /* Profiling hook: until called again on this thread, every nsa_decode_fwd and
  * nsa_prefill_fwd on this thread records the caller-owned hipEvent_t handles
  * events[0..3] on the call's stream between its kernels, so a caller can time

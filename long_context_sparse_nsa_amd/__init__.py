@@ -1,4 +1,4 @@
-"""MI355X (gfx950) Native Sparse Attention forward pass.
+"""MI355X (gfx950) Native Sparse Attention: forward and backward passes.
 
 The compute lives in libnsa.so (hand-written HIP kernels behind the C ABI of
 include/nsa.h); this package only marshals torch tensors into that ABI.
@@ -14,6 +14,8 @@ from ._abi import (  # noqa: F401
     new_workspace,
     nsa_compress_append,
     nsa_compress_append_workspace_size,
+    nsa_compress_bwd,
+    nsa_compress_bwd_workspace_size,
     nsa_compress_kv,
     nsa_config_t,
     make_dsa_dims,
@@ -24,6 +26,8 @@ from ._abi import (  # noqa: F401
     nsa_decode_workspace_size,
     nsa_dims_t,
     nsa_last_error,
+    nsa_prefill_bwd,
+    nsa_prefill_bwd_workspace_size,
     nsa_prefill_fwd,
     nsa_prefill_workspace_size,
     nsa_set_phase_events,

@@ -72,6 +72,12 @@ _SIGS = {
                         _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "nsa_prefill_bwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                        _VP, _VP, ctypes.c_size_t, _VP],
+    "nsa_prefill_bwd_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
+    "nsa_compress_bwd": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                         ctypes.c_size_t, _VP],
+    "nsa_compress_bwd_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_dsa_decode_fwd": [_VP, ctypes.c_int32, ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP,
                            _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_dsa_decode_workspace_size": [_VP, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
@@ -222,6 +228,57 @@ def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, p
                                _ptr(workspace, "workspace"),
                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                _stream(stream)))
+
+
+def nsa_prefill_bwd_workspace_size(dims: nsa_dims_t, cfg: nsa_config_t, seq_len: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().nsa_prefill_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(cfg), int(seq_len),
+                                                         ctypes.byref(out)))
+    return int(out.value)
+
+
+def nsa_prefill_bwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, gates, sel_idx, dout, dq, dk, dv, dk_cmp, dv_cmp,
+                    dgates, workspace, stream=None):
+    """Gradients of nsa_prefill_fwd; dq/dk/dv/dk_cmp/dv_cmp/dgates are float32 outputs."""
+    lib = load_library()
+    B, Hq, H, T = dims.batch, dims.num_q_heads, dims.num_kv_heads, int(seq_len)
+    nc = compressed_count(T, cfg.l, cfg.d)
+    _check(lib.nsa_prefill_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, _ptr(q, "q", 2, B * T * Hq * dims.d_k),
+                               _ptr(k, "k", 2, B * H * T * dims.d_k), _ptr(v, "v", 2, B * H * T * dims.d_v),
+                               _ptr(k_cmp, "k_cmp", 2, B * H * nc * dims.d_k),
+                               _ptr(v_cmp, "v_cmp", 2, B * H * nc * dims.d_v),
+                               _ptr(gates, "gates", 4, B * T * Hq * 3),
+                               _ptr(sel_idx, "sel_idx", 4, B * T * H * cfg.n_sel),
+                               _ptr(dout, "dout", 2, B * T * Hq * dims.d_v),
+                               _ptr(dq, "dq", 4, B * T * Hq * dims.d_k), _ptr(dk, "dk", 4, B * H * T * dims.d_k),
+                               _ptr(dv, "dv", 4, B * H * T * dims.d_v),
+                               _ptr(dk_cmp, "dk_cmp", 4, B * H * nc * dims.d_k),
+                               _ptr(dv_cmp, "dv_cmp", 4, B * H * nc * dims.d_v),
+                               _ptr(dgates, "dgates", 4, B * T * Hq * 3), _ptr(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                               _stream(stream)))
+
+
+def nsa_compress_bwd_workspace_size(dims: nsa_dims_t, cfg: nsa_config_t, seq_len: int, which: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().nsa_compress_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(cfg), int(seq_len),
+                                                          int(which), ctypes.byref(out)))
+    return int(out.value)
+
+
+def nsa_compress_bwd(dims, cfg, seq_len, which, x, w, pe, dy, dx, dw, dpe, workspace, stream=None):
+    """which = 0: keys (d_k), 1: values (d_v).  dx is accumulated into; dw, dpe are written."""
+    lib = load_library()
+    B, H, T = dims.batch, dims.num_kv_heads, int(seq_len)
+    D = dims.d_k if which == 0 else dims.d_v
+    nc = compressed_count(T, cfg.l, cfg.d)
+    _check(lib.nsa_compress_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, int(which),
+                                _ptr(x, "x", 2, B * H * T * D), _ptr(w, "w", 2, cfg.l * D * D),
+                                _ptr(pe, "pe", 2, cfg.l * D), _ptr(dy, "dy", 4, B * H * nc * D),
+                                _ptr(dx, "dx", 4, B * H * T * D), _ptr(dw, "dw", 4, cfg.l * D * D),
+                                _ptr(dpe, "dpe", 4, cfg.l * D), _ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                _stream(stream)))
 
 
 def nsa_dsa_decode_workspace_size(dims: nsa_dsa_dims_t, top_k: int, cache_len: int) -> int:

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnsa.so")
 
-SOURCES = ["nsa_api.cpp", "nsa_append.hip", "nsa_compress.hip", "nsa_decode.hip", "nsa_dsa.hip", "nsa_prefill.hip"]
+SOURCES = ["nsa_api.cpp", "nsa_append.hip", "nsa_backward.hip", "nsa_compress.hip", "nsa_compress_bwd.hip",
+           "nsa_decode.hip", "nsa_dsa.hip", "nsa_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 VALU ops are kept out of every kernel (explicitly disabled).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

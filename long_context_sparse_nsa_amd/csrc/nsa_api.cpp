@@ -551,3 +551,168 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward (training).
+
+namespace {
+
+// Prefill-backward workspace: per-branch lse and D [3, B, T, Hq] fp32, then the
+// selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32.
+struct BwdWs {
+  size_t off_lse, off_delta, off_bits, total;
+};
+BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
+  BwdWs w{};
+  const size_t rows = (size_t)3 * dims->batch * (size_t)T * dims->num_q_heads;
+  const size_t nblk = (size_t)((T + cfg->l_sel - 1) / cfg->l_sel), nwords = (size_t)((T + 31) / 32);
+  w.off_lse = 0;
+  w.off_delta = align256(rows * 4);
+  w.off_bits = w.off_delta + align256(rows * 4);
+  w.total = w.off_bits + align256((size_t)dims->batch * dims->num_kv_heads * nblk * nwords * 4);
+  return w;
+}
+
+constexpr int kBwdQWords = 64;    // selected-branch key side: 2048 positions per workgroup
+constexpr int kBwdQChunk = 1024;  // compressed-branch key side: positions per workgroup
+
+// Compression-backward workspace: dX [B*Hkv*nc, l*D] fp32, then 64 column-sum partials [64, D].
+size_t cbwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, int D) {
+  const int64_t nc = n_compressed(T, cfg->l, cfg->d);
+  return align256((size_t)dims->batch * dims->num_kv_heads * (size_t)nc * cfg->l * D * 4) +
+         align256((size_t)64 * D * 4);
+}
+
+nsa_status_t check_cbwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, int32_t which) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (which != 0 && which != 1) return fail(NSA_ERROR_INVALID_VALUE, "which must be 0 (keys) or 1 (values)");
+  if (T < 1) return fail(NSA_ERROR_INVALID_VALUE, "seq_len must be >= 1");
+  const int D = which == 0 ? dims->d_k : dims->d_v;
+  const int64_t rows = (int64_t)dims->batch * dims->num_kv_heads * n_compressed(T, cfg->l, cfg->d);
+  if ((rows + 63) / 64 > 65535 || (int64_t)dims->batch * dims->num_kv_heads * T * D / 256 > INT32_MAX)
+    return fail(NSA_ERROR_UNSUPPORTED, "compression backward launch too large");
+  return NSA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
+                                            size_t* bytes) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
+  if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
+  *bytes = bwd_ws(dims, cfg, seq_len).total;
+  return ok();
+}
+
+nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len, const uint16_t* q,
+                             const uint16_t* k, const uint16_t* v, const uint16_t* k_cmp, const uint16_t* v_cmp,
+                             const float* gates, const int32_t* sel_idx, const uint16_t* dout, float* dq, float* dk,
+                             float* dv, float* dk_cmp, float* dv_cmp, float* dgates, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  nsa_status_t st = check_common(dims, cfg, true);
+  if (st != NSA_SUCCESS) return st;
+  if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
+  if (!q || !k || !v || !gates || !sel_idx || !dout || !dq || !dk || !dv || !dgates)
+    return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  const int64_t nc = n_compressed(seq_len, cfg->l, cfg->d);
+  if (nc > 0 && (!k_cmp || !v_cmp || !dk_cmp || !dv_cmp))
+    return fail(NSA_ERROR_INVALID_VALUE, "the compressed cache and its gradient buffers are required (%lld blocks)",
+                (long long)nc);
+  const BwdWs lay = bwd_ws(dims, cfg, seq_len);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  nsa::BwdParams p{};
+  p.B = dims->batch;
+  p.T = (int)seq_len;
+  p.Hq = dims->num_q_heads;
+  p.H = dims->num_kv_heads;
+  p.G = p.Hq / p.H;
+  p.l = cfg->l;
+  p.d = cfg->d;
+  p.lsel = cfg->l_sel;
+  p.n = cfg->n_sel;
+  p.w = cfg->w;
+  p.scale_log2 = scale_log2(dims, cfg);
+  p.scale = p.scale_log2 / 1.4426950408889634f;
+  p.nc = (int)nc;
+  p.nqt = (int)((seq_len + 3) / 4);
+  p.nblk = (int)((seq_len + cfg->l_sel - 1) / cfg->l_sel);
+  p.nwords = (int)((seq_len + 31) / 32);
+  p.qwords = kBwdQWords;
+  p.nqw = (p.nwords + kBwdQWords - 1) / kBwdQWords;
+  p.qchunk = kBwdQChunk;
+  p.ncq = (int)((seq_len + kBwdQChunk - 1) / kBwdQChunk);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.kc = nc > 0 ? k_cmp : k;  // never read without a compressed block
+  p.vc = nc > 0 ? v_cmp : v;
+  p.gates = gates;
+  p.sel = sel_idx;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dkc = dk_cmp;
+  p.dvc = dv_cmp;
+  p.dgates = dgates;
+  p.lse = reinterpret_cast<float*>(ws + lay.off_lse);
+  p.delta = reinterpret_cast<float*>(ws + lay.off_delta);
+  p.bits = reinterpret_cast<uint32_t*>(ws + lay.off_bits);
+  hipError_t e = nsa::launch_prefill_bwd(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill backward launch");
+  return ok();
+}
+
+nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
+                                             int32_t which, size_t* bytes) {
+  nsa_status_t st = check_cbwd(dims, cfg, seq_len, which);
+  if (st != NSA_SUCCESS) return st;
+  if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
+  *bytes = cbwd_ws(dims, cfg, seq_len, which == 0 ? dims->d_k : dims->d_v);
+  return ok();
+}
+
+nsa_status_t nsa_compress_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len, int32_t which,
+                              const uint16_t* x, const uint16_t* w, const uint16_t* pe, const float* dy, float* dx,
+                              float* dw, float* dpe, void* workspace, size_t workspace_bytes, void* stream) {
+  nsa_status_t st = check_cbwd(dims, cfg, seq_len, which);
+  if (st != NSA_SUCCESS) return st;
+  const int64_t nc = n_compressed(seq_len, cfg->l, cfg->d);
+  if (!x || !w || !pe || !dx || !dw || !dpe || (nc > 0 && !dy))
+    return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  const int D = which == 0 ? dims->d_k : dims->d_v;
+  const size_t need = cbwd_ws(dims, cfg, seq_len, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  nsa::CompressBwdParams p{};
+  p.BH = dims->batch * dims->num_kv_heads;
+  p.D = D;
+  p.l = cfg->l;
+  p.d = cfg->d;
+  p.nc = (int)nc;
+  p.T = seq_len;
+  p.x = x;
+  p.w = w;
+  p.pe = pe;
+  p.dy = dy;
+  p.dx = dx;
+  p.dw = dw;
+  p.dpe = dpe;
+  p.dX = reinterpret_cast<float*>(ws);
+  p.part = reinterpret_cast<float*>(ws + align256((size_t)p.BH * (size_t)nc * cfg->l * D * 4));
+  hipError_t e = nsa::launch_compress_bwd(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "compression backward launch");
+  return ok();
+}
+
+}  // extern "C"

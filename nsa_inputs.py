@@ -259,6 +259,16 @@ def generate(wl: Workload, seed: int, keep_fp32: bool = False) -> Case:
     return case
 
 
+def output_gradient(case: Case, seed: int) -> np.ndarray:
+    """Seeded gradient of a prefill case's output for the backward pass: bf16 bits
+    [B, T, Hq, d_v] of standard normal values, drawn from its own stream
+    default_rng([seed, 1]) so that the forward inputs do not change."""
+    wl = case.wl
+    rng = np.random.default_rng([seed, 1])
+    g = rng.standard_normal(size=(wl.batch, wl.seq_len, wl.num_q_heads, wl.d_v), dtype=np.float32)
+    return bf16_bits(g)
+
+
 def workload(name: str, **overrides) -> Workload:
     wl = WORKLOADS[name]
     if "params" in overrides and isinstance(overrides["params"], dict):

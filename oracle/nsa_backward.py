@@ -76,7 +76,8 @@ def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarra
     PEk [l, dk], Wv [l*dv, dv], PEv [l, dv], gates [T, G, 3], dout [T, G, dv].
     ``sel`` gives the selected block ids per row; by default the forward oracle's top-n.
     ``round_cmp`` uses the bf16-rounded compressed cache values (as the forward does).
-    Returns float64 numpy arrays: dQ, dK, dV, dWk, dPEk, dWv, dPEv, dgates (shapes of the inputs).
+    Returns float64 numpy arrays: dQ, dK, dV, dWk, dPEk, dWv, dPEv, dgates (shapes of the inputs), and
+    dKc, dVc: the gradients reaching the compressed cache [nc, dk] / [nc, dv].
     """
     dk_ = Q.shape[2]
     s = 1.0 / np.sqrt(dk_) if scale is None else scale
@@ -90,6 +91,9 @@ def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarra
     Gt = torch.tensor(gates, dtype=F64, requires_grad=True)
     Kc = compress_t(Kt, Wkt, PEkt, p.l, p.d, round_cmp)
     Vc = compress_t(Vt, Wvt, PEvt, p.l, p.d, round_cmp)
+    for c in (Kc, Vc):
+        if c.requires_grad:
+            c.retain_grad()
     if sel is None:  # the forward oracle's selection (with the bf16-rounded compressed cache)
         Kc_o = O.compress(K, Wk, PEk, p.l, p.d)
         Vc_o = O.compress(V, Wv, PEv, p.l, p.d)
@@ -102,4 +106,4 @@ def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarra
     loss.backward()
     g = lambda x: (x.grad if x.grad is not None else torch.zeros_like(x)).detach().numpy()
     return dict(dQ=g(Qt), dK=g(Kt), dV=g(Vt), dWk=g(Wkt), dPEk=g(PEkt), dWv=g(Wvt), dPEv=g(PEvt), dgates=g(Gt),
-                sel=sel)
+                dKc=g(Kc), dVc=g(Vc), sel=sel)

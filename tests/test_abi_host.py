@@ -201,3 +201,36 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         A._ptr(torch.zeros(4), "x")
+
+
+def test_backward_workspace_sizes_and_validation():
+    dims, cfg = _dims(batch=1), _cfg()
+    T = 32768
+    # lse and D [3, 1, T, 64] fp32 each, bitmap [1, 4, T/64, T/32] uint32
+    assert N.nsa_prefill_bwd_workspace_size(dims, cfg, T) == 2 * 3 * T * 64 * 4 + 4 * 512 * 1024 * 4
+    nc = (T - 32) // 16 + 1
+    assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0) == -(-(4 * nc * 32 * 192 * 4) // 256) * 256 + 64 * 192 * 4
+    assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 1) == -(-(4 * nc * 32 * 128 * 4) // 256) * 256 + 64 * 128 * 4
+    lib = A.load_library()
+    f = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    need = N.nsa_prefill_bwd_workspace_size(dims, cfg, T)
+
+    def bwd(q=f, kc=f, sel=f, ws=f, nb=need, T=T):
+        return lib.nsa_prefill_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, q, f, f, kc, f, f, sel, f, f, f, f, f, f,
+                                   f, ws, nb, None)
+    assert bwd(q=None) == A.NSA_ERROR_INVALID_VALUE and "NULL" in N.nsa_last_error()
+    assert bwd(sel=None) == A.NSA_ERROR_INVALID_VALUE
+    assert bwd(kc=None) == A.NSA_ERROR_INVALID_VALUE and "compressed" in N.nsa_last_error()
+    assert bwd(nb=need - 1) == A.NSA_ERROR_WORKSPACE
+    assert bwd(ws=None) == A.NSA_ERROR_WORKSPACE
+    assert bwd(T=0) == A.NSA_ERROR_INVALID_VALUE
+    assert bwd(T=70000) == A.NSA_ERROR_UNSUPPORTED  # more than 1024 selection blocks
+    cneed = N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0)
+
+    def cbwd(which=0, x=f, dy=f, ws=f, nb=cneed):
+        return lib.nsa_compress_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, which, x, f, f, dy, f, f, f, ws, nb,
+                                    None)
+    assert cbwd(which=2) == A.NSA_ERROR_INVALID_VALUE
+    assert cbwd(x=None) == A.NSA_ERROR_INVALID_VALUE
+    assert cbwd(dy=None) == A.NSA_ERROR_INVALID_VALUE
+    assert cbwd(nb=cneed - 1) == A.NSA_ERROR_WORKSPACE
