@@ -363,6 +363,103 @@ def prefill_flops(wl):
                 compress=float(comp))
 
 
+def backward_flops(wl):
+    """Algorithmic FLOPs of the prefill backward: per key visit per head, the five
+    products of an attention backward (logits again, dO.v, dq, dk: 2*d_k each;
+    dO.v and dv: 2*d_v each) = 2*(3*d_k + 2*d_v); the compression backward is
+    twice the compression's products (dX = dY W^T and dW)."""
+    f = prefill_flops(wl)
+    visits = (f["cmp"] + f["slc"] + f["win"]) / (2 * (wl.d_k + wl.d_v))
+    return dict(attention=float(visits * 2 * (3 * wl.d_k + 2 * wl.d_v)), compress=float(2 * f["compress"]))
+
+
+def backward_setup(torch, N, I):
+    """prefill_32k inputs resident on the GPU, the compressed cache and the forward's
+    selection, an output gradient and the backward's buffers."""
+    wl = I.workload("prefill_32k")
+    seed = list(I.WORKLOADS).index("prefill_32k")
+    case = I.generate(wl, seed)
+    p = wl.params
+    B, T, Hq, H, dk, dv = wl.batch, wl.seq_len, wl.num_q_heads, wl.num_kv_heads, wl.d_k, wl.d_v
+    nc = N.compressed_count(T, p.l, p.d)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    dims = N.make_dims(B, Hq, H, dk, dv)
+    cfg = N.make_config(p.l, p.d, p.l_sel, p.n_sel, p.n_local, p.force_initial, p.w)
+    X = dict(q=dev(case.q), k=dev(case.k), v=dev(case.v), wk=dev(case.w_k), pk=dev(case.pe_k), wv=dev(case.w_v),
+             pv=dev(case.pe_v), gates=torch.from_numpy(case.gates).cuda(), dout=dev(I.output_gradient(case, seed)))
+    X["kc"] = torch.empty((B, H, nc, dk), dtype=torch.bfloat16, device="cuda")
+    X["vc"] = torch.empty((B, H, nc, dv), dtype=torch.bfloat16, device="cuda")
+    N.nsa_compress_kv(dims, cfg, X["k"], X["v"], None, None, T, X["wk"], X["pk"], X["wv"], X["pv"], X["kc"], X["vc"],
+                      None)
+    X["sel"] = torch.empty((B, T, H, p.n_sel), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, T, Hq, dv), dtype=torch.bfloat16, device="cuda")
+    ws = N.new_workspace(N.nsa_prefill_workspace_size(dims, cfg, T, False))
+    N.nsa_prefill_fwd(dims, cfg, T, X["q"], X["k"], X["v"], X["kc"], X["vc"], None, None, None, None, X["gates"],
+                      out, X["sel"], ws)
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
+    X.update(dq=f32(B, T, Hq, dk), dk=f32(B, H, T, dk), dv=f32(B, H, T, dv), dkc=f32(B, H, nc, dk),
+             dvc=f32(B, H, nc, dv), dg=f32(B, T, Hq, 3), dwk=f32(p.l * dk, dk), dpk=f32(p.l, dk),
+             dwv=f32(p.l * dv, dv), dpv=f32(p.l, dv))
+    X["ws"] = N.new_workspace(N.nsa_prefill_bwd_workspace_size(dims, cfg, T))
+    X["wsc"] = N.new_workspace(max(N.nsa_compress_bwd_workspace_size(dims, cfg, T, w) for w in (0, 1)))
+    torch.cuda.synchronize()
+
+    def attn():
+        N.nsa_prefill_bwd(dims, cfg, T, X["q"], X["k"], X["v"], X["kc"], X["vc"], X["gates"], X["sel"], X["dout"],
+                          X["dq"], X["dk"], X["dv"], X["dkc"], X["dvc"], X["dg"], X["ws"])
+
+    def comp():
+        N.nsa_compress_bwd(dims, cfg, T, 0, X["k"], X["wk"], X["pk"], X["dkc"], X["dk"], X["dwk"], X["dpk"], X["wsc"])
+        N.nsa_compress_bwd(dims, cfg, T, 1, X["v"], X["wv"], X["pv"], X["dvc"], X["dv"], X["dwv"], X["dpv"], X["wsc"])
+
+    return wl, attn, comp
+
+
+def bench_backward(args, torch, N, I):
+    t0 = time.time()
+    wl, attn, comp = backward_setup(torch, N, I)
+    log(f"[bench] backward inputs of {wl.name} ready in {time.time() - t0:.1f}s")
+    attn()
+    comp()
+    torch.cuda.synchronize()
+    reps = args.prefill_reps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(reps):
+        attn()
+    ev[1].record()
+    for _ in range(reps):
+        comp()
+    ev[2].record()
+    torch.cuda.synchronize()
+    attn_ms, comp_ms = ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
+    hev = HipEvents(4 * reps)
+    try:
+        for i in range(reps):
+            N.nsa_set_phase_events(hev.ev[4 * i:4 * i + 4])
+            attn()
+        N.nsa_set_phase_events(None)
+        torch.cuda.synchronize()
+        ph = [float(np.median([hev.ms(4 * i + a, 4 * i + a + 1) for i in range(reps)])) for a in range(3)]
+    finally:
+        N.nsa_set_phase_events(None)
+        hev.close()
+    f = backward_flops(wl)
+    ms = attn_ms + comp_ms
+    res = dict(workload=wl.name, ms=ms, attention_ms=attn_ms, compress_ms=comp_ms, flops=f,
+               tflops=(f["attention"] + f["compress"]) / (ms * 1e-3) / 1e12,
+               attention_tflops=f["attention"] / (attn_ms * 1e-3) / 1e12,
+               kernel_ms=dict(bwd_query_kernel=ph[0], bwd_kv_kernel_raw=ph[1], bwd_kv_kernel_cmp=ph[2]))
+    res["mfma_frac"] = res["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    log(f"[bench] backward {wl.name}: {ms:.2f} ms ({res['tflops']:.1f} TFLOP/s); attention {attn_ms:.2f} ms "
+        f"({res['attention_tflops']:.0f} TFLOP/s, {100 * res['mfma_frac']:.1f}% of bf16 peak): query side "
+        f"{ph[0]:.2f} ms, raw keys {ph[1]:.2f} ms, compressed keys {ph[2]:.2f} ms; compression {comp_ms:.2f} ms")
+    return res
+
+
 def bench_prefill(args, torch, N, I):
     wl = I.workload("prefill_32k")
     seed = list(I.WORKLOADS).index("prefill_32k")
@@ -600,6 +697,14 @@ def kernels_only(args, torch, N, I):
         torch.cuda.synchronize()
         log(f"[bench] {args.kernels_only} DSA decode steps of {wl.name} done")
         return
+    if args.backward:
+        _, attn, comp = backward_setup(torch, N, I)
+        for i in range(args.kernels_only):
+            attn()
+            comp()
+            torch.cuda.synchronize()
+            log(f"[bench] backward call {i + 1}/{args.kernels_only} done")
+        return
     if args.prefill:
         wl = I.workload("prefill_32k")
         case = I.generate(wl, list(I.WORKLOADS).index("prefill_32k"))
@@ -690,6 +795,9 @@ def main():
     ap.add_argument("--kernels-only", type=int, default=0, metavar="N",
                     help="run N eager calls and exit (for profiler runs; no timing, no JSON line)")
     ap.add_argument("--prefill", action="store_true", help="with --kernels-only: prefill calls instead of decode")
+    ap.add_argument("--backward", action="store_true",
+                    help="with --kernels-only: prefill backward calls (attention and compression)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward")
     ap.add_argument("--serving", action="store_true",
                     help="with --kernels-only: nsa_compress_append before every decode call")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -714,6 +822,7 @@ def main():
 
     case, dec, _ = bench_decode(args, torch, N, I)
     pre = None if args.no_prefill else bench_prefill(args, torch, N, I)
+    bwd = None if args.no_backward else bench_backward(args, torch, N, I)
     dsa = None if args.no_dsa else bench_dsa(args, torch, N, I)
     cpu = None if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
     if cpu:
@@ -779,6 +888,14 @@ def main():
                                                "mfma_frac": pre["sel_mfma_frac"]},
                            "cmp_win_topn": {"kernel": "pf_cmp_win_kernel", "TFLOP/s": pre["cmp_win_tflops"],
                                             "mfma_frac": pre["cmp_win_tflops"] / MFMA_BF16_PEAK_TFLOPS}}
+    if bwd:
+        line["prefill_backward"] = {
+            "workload": bwd["workload"], "calls": "nsa_prefill_bwd + nsa_compress_bwd (keys, values)",
+            "ms": bwd["ms"], "TFLOP/s": bwd["tflops"], "flops": bwd["flops"],
+            "attention": {"ms": bwd["attention_ms"], "TFLOP/s": bwd["attention_tflops"],
+                          "mfma_frac": bwd["mfma_frac"], "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
+                          "kernel_ms": bwd["kernel_ms"]},
+            "compression_ms": bwd["compress_ms"]}
     print(json.dumps(line), flush=True)
 
 

@@ -339,8 +339,8 @@ nsa_status_t nsa_compress_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, i
 nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                              int64_t seq_len, int32_t which, size_t* bytes);
 
-/* Profiling hook: until called again on this thread, every nsa_decode_fwd and
- * nsa_prefill_fwd on this thread records the caller-owned hipEvent_t handles
+/* Profiling hook: until called again on this thread, every nsa_decode_fwd,
+ * nsa_prefill_fwd and nsa_prefill_bwd on this thread records the caller-owned hipEvent_t handles
  * events[0..3] on the call's stream between its kernels, so a caller can time
  * each kernel with hipEventElapsedTime:
  *   decode:  events[0] / events[1] are the start / stop events of the
@@ -350,7 +350,10 @@ nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_c
  *            exact merge and the gated sum), so each pair times one kernel;
  *   prefill: before the in-call compression, after it (or right away when the
  *            cache is given), after the compressed + window + top-n kernel, after
- *            the selected-branch kernel (which writes the gated sum).
+ *            the selected-branch kernel (which writes the gated sum);
+ *   prefill backward: before the query-side kernel (dq and the branch
+ *            statistics), after it, after the raw-key kernels (window and
+ *            selected branches), after the compressed-key kernel.
  * count = 0 (the default) records nothing; any count other than 0 or 4, or a
  * NULL handle, is NSA_ERROR_INVALID_VALUE.  The array is copied; the events are
  * not. */

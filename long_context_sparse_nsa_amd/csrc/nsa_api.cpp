@@ -9,7 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "nsa.h"
-#include "nsa_internal.hpp"
+#include "nsa_train.hpp"
 
 namespace {
 
@@ -666,7 +666,8 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.lse = reinterpret_cast<float*>(ws + lay.off_lse);
   p.delta = reinterpret_cast<float*>(ws + lay.off_delta);
   p.bits = reinterpret_cast<uint32_t*>(ws + lay.off_bits);
-  hipError_t e = nsa::launch_prefill_bwd(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream));
+  const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
+  hipError_t e = nsa::launch_prefill_bwd(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "prefill backward launch");
   return ok();
 }

@@ -27,7 +27,7 @@
 // Products are bf16 MFMA (P and dS rounded to bf16 as operands) with fp32 sums.
 #include <algorithm>
 
-#include "nsa_internal.hpp"
+#include "nsa_train.hpp"
 #include "nsa_tiles.hpp"
 
 namespace nsa {
@@ -427,7 +427,7 @@ hipError_t zero_words(void* a, int64_t n, hipStream_t s) {
 }
 
 template <int DK, int DV>
-hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s, const PhaseEvents* ev) {
   const int nbg = p.B * p.H;
   hipError_t e;
   if ((e = zero_words(p.bits, (int64_t)nbg * p.nblk * p.nwords, s)) != hipSuccess) return e;
@@ -435,23 +435,27 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   if ((e = zero_words(p.dvc, (int64_t)nbg * p.nc * DV, s)) != hipSuccess) return e;
   const int64_t nsel = (int64_t)p.B * p.T * p.H * p.n;
   hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((nsel + 255) / 256)), dim3(256), 0, s, p);
+  if (ev) hipEventRecord(ev->ev[0], s);
   hipLaunchKernelGGL((bwd_query_kernel<DK, DV>), dim3((unsigned)(nbg * p.nqt)), dim3(256), 0, s, p);
+  if (ev) hipEventRecord(ev->ev[1], s);
   const int kraw = (p.T + 63) / 64, kcmp = (p.nc + 63) / 64;
   hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kWin>), dim3((unsigned)(nbg * kraw)), dim3(256), 0, s, p);
   hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kSlc>), dim3((unsigned)(nbg * kraw), (unsigned)p.nqw), dim3(256), 0, s,
                      p);
+  if (ev) hipEventRecord(ev->ev[2], s);
   if (p.nc > 0)
     hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kCmp>), dim3((unsigned)(nbg * kcmp), (unsigned)p.ncq), dim3(256), 0,
                        s, p);
+  if (ev) hipEventRecord(ev->ev[3], s);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bwd(const BwdParams& p, int DK, int DV, hipStream_t s) {
-  if (DK == 192 && DV == 128) return launch_bwd_t<192, 128>(p, s);
-  if (DK == 128 && DV == 128) return launch_bwd_t<128, 128>(p, s);
-  if (DK == 64 && DV == 64) return launch_bwd_t<64, 64>(p, s);
+hipError_t launch_prefill_bwd(const BwdParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev) {
+  if (DK == 192 && DV == 128) return launch_bwd_t<192, 128>(p, s, ev);
+  if (DK == 128 && DV == 128) return launch_bwd_t<128, 128>(p, s, ev);
+  if (DK == 64 && DV == 64) return launch_bwd_t<64, 64>(p, s, ev);
   return hipErrorInvalidValue;
 }
 

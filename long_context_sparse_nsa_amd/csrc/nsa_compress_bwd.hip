@@ -14,7 +14,7 @@
 //   dW     = sum_i X_i^T dY_i = sum_i x-rows^T dY_i + PE (x) s,  s = sum_i dY_i
 //   dPE    = sum_i dX_i = s W^T
 // All sums run in fp32 in a fixed order (no atomics), so results are reproducible.
-#include "nsa_internal.hpp"
+#include "nsa_train.hpp"
 #include "nsa_device.hpp"
 
 namespace nsa {

@@ -1,0 +1,54 @@
+// Parameters and launchers of the training kernels: the prefill backward and
+// the compression backward.
+#pragma once
+#include "nsa_internal.hpp"
+
+namespace nsa {
+
+// Prefill backward (gradients of the three-branch output).
+struct BwdParams {
+  int B, T, Hq, H, G;
+  int l, d, lsel, n, w;
+  float scale, scale_log2;           // softmax scale and scale * log2(e)
+  int nc;                            // compressed blocks per sequence
+  int nqt;                           // query workgroups per (b, g): ceil(T / 4)
+  int nblk, nwords;                  // selection blocks ceil(T / lsel); 32-position words ceil(T / 32)
+  int qwords, nqw;                   // selected-branch key side: words per workgroup, workgroups per key tile
+  int qchunk, ncq;                   // compressed-branch key side: positions per workgroup, workgroups per tile
+  const uint16_t* q;                 // [B, T, Hq, DK]
+  const uint16_t* k;                 // [B, H, T, DK]
+  const uint16_t* v;                 // [B, H, T, DV]
+  const uint16_t* kc;                // [B, H, nc, DK]
+  const uint16_t* vc;                // [B, H, nc, DV]
+  const float* gates;                // [B, T, Hq, 3]
+  const int32_t* sel;                // [B, T, H, n] the forward's selected block ids
+  const uint16_t* dout;              // [B, T, Hq, DV]
+  float* dq;                         // [B, T, Hq, DK]
+  float* dk;                         // [B, H, T, DK]
+  float* dv;                         // [B, H, T, DV]
+  float* dkc;                        // [B, H, nc, DK]
+  float* dvc;                        // [B, H, nc, DV]
+  float* dgates;                     // [B, T, Hq, 3]
+  float* lse;                        // workspace [3, B, T, Hq]: per-branch log2-sum-exp2 of the logits
+  float* delta;                      // workspace [3, B, T, Hq]: g_c (dO . o_c)
+  uint32_t* bits;                    // workspace [B, H, nblk, nwords]: position t selected block j
+};
+
+// Compression backward of one compressed cache (keys or values).
+struct CompressBwdParams {
+  int BH, D, l, d, nc;
+  int64_t T;
+  const uint16_t* x;                 // raw rows [BH, T, D]
+  const uint16_t* w;                 // [l*D, D]
+  const uint16_t* pe;                // [l, D]
+  const float* dy;                   // [BH, nc, D]
+  float* dx;                         // [BH, T, D], accumulated
+  float* dw;                         // [l*D, D]
+  float* dpe;                        // [l, D]
+  float* dX;                         // workspace [BH*nc, l*D]
+  float* part;                       // workspace [64, D]
+};
+hipError_t launch_compress_bwd(const CompressBwdParams& p, hipStream_t s);
+hipError_t launch_prefill_bwd(const BwdParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);
+
+}  // namespace nsa
