@@ -283,7 +283,9 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
  *   dk, dv (raw) from the selected and window branches; dk_cmp, dv_cmp from the
  *   compressed branch (feed them to nsa_compress_bwd for the compression MLP).
  * The branch statistics (lse_c, D_c = g_c dout . o_c) are recomputed from the
- * inputs in a first pass and kept in the workspace.
+ * inputs in a first pass and kept in the workspace.  With nsa_set_phase_events
+ * the events mark: before the query-side kernel, after it, after the raw-key
+ * kernels, after the compressed-key kernel.
  *
  *   q, k, v, k_cmp, v_cmp  as for nsa_prefill_fwd; the compressed cache is the
  *          one the forward used (required when seq_len >= l).
@@ -307,9 +309,10 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
                              const float* gates, const int32_t* sel_idx, const uint16_t* dout,
                              float* dq, float* dk, float* dv, float* dk_cmp, float* dv_cmp,
                              float* dgates, void* workspace, size_t workspace_bytes, void* stream);
-/* Workspace bytes for nsa_prefill_bwd (host-only): lse and D [3, B, T, Hq] fp32
- * and a selection bitmap [B, Hkv, ceil(T/l_sel), ceil(T/32)] uint32.  Contents
- * on entry do not matter. */
+/* Workspace bytes for nsa_prefill_bwd (host-only): per (branch, position, KV
+ * group) a record of 48 fp32 (the heads' log-sum-exp, D and gate, padded to 16
+ * heads), [3, B, T, Hkv, 48], and a selection bitmap [B, Hkv, ceil(T/l_sel),
+ * ceil(T/32)] uint32.  Contents on entry do not matter. */
 nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                             int64_t seq_len, size_t* bytes);
 

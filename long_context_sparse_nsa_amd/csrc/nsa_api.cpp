@@ -557,23 +557,22 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
 
 namespace {
 
-// Prefill-backward workspace: per-branch lse and D [3, B, T, Hq] fp32, then the
-// selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32.
+// Prefill-backward workspace: per-branch statistics records [3, B, T, Hkv, 48]
+// fp32, then the selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32.
 struct BwdWs {
-  size_t off_lse, off_delta, off_bits, total;
+  size_t off_stat, off_bits, total;
 };
 BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   BwdWs w{};
-  const size_t rows = (size_t)3 * dims->batch * (size_t)T * dims->num_q_heads;
+  const size_t recs = (size_t)3 * dims->batch * (size_t)T * dims->num_kv_heads;
   const size_t nblk = (size_t)((T + cfg->l_sel - 1) / cfg->l_sel), nwords = (size_t)((T + 31) / 32);
-  w.off_lse = 0;
-  w.off_delta = align256(rows * 4);
-  w.off_bits = w.off_delta + align256(rows * 4);
+  w.off_stat = 0;
+  w.off_bits = align256(recs * nsa::kStatFloats * 4);
   w.total = w.off_bits + align256((size_t)dims->batch * dims->num_kv_heads * nblk * nwords * 4);
   return w;
 }
 
-constexpr int kBwdQWords = 64;    // selected-branch key side: 2048 positions per workgroup
+constexpr int kBwdQWords = nsa::kBwdQWordsMax;  // selected-branch key side: 4096 positions per workgroup
 constexpr int kBwdQChunk = 1024;  // compressed-branch key side: positions per workgroup
 
 // Compression-backward workspace: dX [B*Hkv*nc, l*D] fp32, then 64 column-sum partials [64, D].
@@ -663,8 +662,7 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.dkc = dk_cmp;
   p.dvc = dv_cmp;
   p.dgates = dgates;
-  p.lse = reinterpret_cast<float*>(ws + lay.off_lse);
-  p.delta = reinterpret_cast<float*>(ws + lay.off_delta);
+  p.stat = reinterpret_cast<float*>(ws + lay.off_stat);
   p.bits = reinterpret_cast<uint32_t*>(ws + lay.off_bits);
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_prefill_bwd(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);

@@ -216,11 +216,12 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdParams p) {
     dot = any ? dot / l : 0.f;  // dO . o_c
     lse2[c] = any ? m + __log2f(l) : 0.f;
     dcs[c] = gt[c] * dot;
-    if (lg == 0 && hv) {
-      const int64_t si = (((int64_t)c * p.B + b) * T + t) * Hq + (int64_t)g * G + lr;
-      p.lse[si] = lse2[c];
-      p.delta[si] = dcs[c];
-      p.dgates[(qrow + lr) * 3 + c] = dot;
+    if (lg == 0) {  // statistics record of (c, b, t, g): lse[16] | D[16] | gate[16], zeros past G
+      float* rec = p.stat + ((((int64_t)c * p.B + b) * T + t) * p.H + g) * kStatFloats;
+      rec[lr] = hv ? lse2[c] : 0.f;
+      rec[16 + lr] = hv ? dcs[c] : 0.f;
+      rec[32 + lr] = gt[c];
+      if (hv) p.dgates[(qrow + lr) * 3 + c] = dot;
     }
   }
 
@@ -250,137 +251,225 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Key side.  A wave owns 16 keys (MFMA columns) and takes its queries two at a
-// time: rows (query, head) of both queries form the 32-long contraction of the
-// dK^T and dV^T products.
+// Key side.  A workgroup owns 64 keys, a wave 16 of them (the MFMA columns,
+// K and V fragments held in registers).  The queries that see those keys are
+// taken two at a time: the 32 rows (query, head) of a pair form the contraction
+// of dV^T += dout^T (g P) and dK^T += Q^T dS.  Each pair's Q rows, dout rows and
+// statistics records are copied global -> LDS directly by all four waves,
+// kKvBuf buffers deep; within a row the 16-byte chunks are XOR-swizzled with the
+// row index so that the MFMA operand reads (16 rows at one column) spread over
+// the LDS banks.
 
-template <int DK, int DV, int MODE>
-struct KvWave {
-  const BwdParams& p;
-  int b, g, lg, lr, key, nkeys;
-  int64_t bgl;
-  u32x4_t kf[DK / 32], vf[DV / 32];
-  f32x4_t dka[DK / 16], dva[DV / 16];
+constexpr int kKvBuf = 3;
 
-  __device__ __forceinline__ bool visible(int t) const {
-    if (key >= nkeys) return false;
-    if constexpr (MODE == kWin) return key <= t && key > t - p.w;
-    if constexpr (MODE == kSlc) return key <= t;
-    return key * p.d + p.l - 1 <= t;
-  }
-
-  // P (times the gate) and dS of one query's group heads 4lg+i against this lane's key.
-  __device__ __forceinline__ void query(int t, bool tok, float (&pg)[4], float (&ds)[4]) const {
-    const int G = p.G;
-    const int64_t qrow = ((int64_t)b * p.T + (tok ? t : 0)) * p.Hq + (int64_t)g * G;
-    u32x4_t qa[DK / 32], oa[DV / 32];
-    load_q_frags<DK>(p.q + qrow * DK, tok ? G : 0, lg, lr, qa);
-    load_q_frags<DV>(p.dout + qrow * DV, tok ? G : 0, lg, lr, oa);
-    const f32x4_t s = qk_tile<DK>(qa, kf);   // S[head 4lg+i][key lr]
-    const f32x4_t dp = qk_tile<DV>(oa, vf);  // dO.v
-    const bool vis = tok && visible(t);
-    const int64_t si = (((int64_t)MODE * p.B + b) * p.T + (tok ? t : 0)) * p.Hq + (int64_t)g * G;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * lg + i;
-      const bool ok = vis && h < G;
-      const float lse2 = ok ? p.lse[si + h] : 0.f;
-      const float dc = ok ? p.delta[si + h] : 0.f;
-      const float gate = ok ? p.gates[(qrow + h) * 3 + MODE] : 0.f;
-      const float pr = ok ? __builtin_amdgcn_exp2f(s[i] * p.scale_log2 - lse2) : 0.f;
-      pg[i] = pr * gate;
-      ds[i] = pr * (gate * dp[i] - dc);
-    }
-  }
-
-  __device__ __forceinline__ void pair(int tA, int tB) {
-    const bool okB = tB >= 0;
-    float pgA[4], dsA[4], pgB[4], dsB[4];
-    query(tA, true, pgA, dsA);
-    query(tB, okB, pgB, dsB);
-    const int G = p.G;
-    const int64_t rA = ((int64_t)b * p.T + tA) * p.Hq + (int64_t)g * G;
-    const int64_t rB = ((int64_t)b * p.T + (okB ? tB : tA)) * p.Hq + (int64_t)g * G;
-    uint32_t orow[8][DV / 32], qrow[8][DK / 32];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int h = 4 * lg + (r & 3);
-      const bool ok = h < G && (r < 4 || okB);
-      const int64_t row = (r < 4 ? rA : rB) + h;
-      load_piece<DV>(p.dout + row * DV, ok, lr, orow[r]);
-      load_piece<DK>(p.q + row * DK, ok, lr, qrow[r]);
-    }
-    pv_step<DV>(orow, pack_probs(pgA, pgB), dva);
-    pv_step<DK>(qrow, pack_probs(dsA, dsB), dka);
-  }
+template <int DK, int DV>
+struct KvShape {
+  static constexpr int kQ = 32 * DK;  // bf16 elements of a pair's Q rows
+  static constexpr int kO = 32 * DV;
+  static constexpr int kBuf = 2 * kQ + 2 * kO + 2 * kStatFloats * 4;  // bytes per buffer
+  static constexpr int kCpQ = 32 * DK / 8 / 256;                       // copies per wave
+  static constexpr int kCpO = 32 * DV / 8 / 256;
+  static constexpr int kCopies = kCpQ + kCpO + 1;
+  static_assert(32 * DK % 2048 == 0 && 32 * DV % 2048 == 0, "whole copy instructions per wave");
 };
+
+// Byte offset in LDS of channel e (a multiple of 4) of row r of a block of D-wide rows.
+template <int D>
+__device__ __forceinline__ int sw_off(int r, int e) {
+  return r * D * 2 + ((((e >> 3) ^ (r & 7))) << 4) + ((e & 7) << 1);
+}
+
+template <int D>
+__device__ __forceinline__ u32x4_t lds_frag(const char* blk, int r, int e) {  // 8 channels, e % 8 == 0
+  return *reinterpret_cast<const u32x4_t*>(blk + sw_off<D>(r, e));
+}
+
+template <int D>
+__device__ __forceinline__ void lds_piece(const char* blk, int r, int lr, uint32_t (&w)[D / 32]) {
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) {
+    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(blk + sw_off<D>(r, (D / 16) * lr + 4 * u));
+    w[2 * u] = x[0];
+    w[2 * u + 1] = x[1];
+  }
+}
 
 template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
-  const int wave = threadIdx.x >> 6;
+  using SH = KvShape<DK, DV>;
+  __shared__ __attribute__((aligned(1024))) char s_buf[kKvBuf][SH::kBuf];
+  __shared__ int32_t s_list[MODE == kSlc ? 32 * kBwdQWordsMax : 1];
+  __shared__ int s_scan[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nbg = p.B * p.H;
   const int bid = (int)blockIdx.x;
   const int kt = bid / nbg;
   const int bg = bid - kt * nbg;
   const int b = bg / p.H, g = bg - (bg / p.H) * p.H;
-  const int k0 = (kt * kBwdWaves + wave) * 16;
+  const int kw0 = kt * 64;  // the workgroup's first key
   const int nkeys = MODE == kCmp ? p.nc : p.T;
-  if (k0 >= nkeys) return;
-  const int T = p.T;
+  if (kw0 >= nkeys) return;
+  const int T = p.T, G = p.G, Hq = p.Hq;
+  const int k0 = kw0 + 16 * wave;
+  const int key = k0 + lr;
   const int64_t bgl = (int64_t)b * p.H + g;
 
-  // Positions this wave visits (inclusive range, before the per-pair mask).
-  int tlo, thi;
+  // Positions visited by the workgroup.
+  int tlo, npos;
   if constexpr (MODE == kWin) {
-    tlo = k0;
-    thi = min(T - 1, k0 + 15 + p.w - 1);
+    tlo = kw0;
+    npos = min(T - 1, kw0 + 63 + p.w - 1) - tlo + 1;
   } else if constexpr (MODE == kCmp) {
-    tlo = k0 * p.d + p.l - 1 + (int)blockIdx.y * p.qchunk;
-    thi = min(T - 1, tlo + p.qchunk - 1);
+    tlo = kw0 * p.d + p.l - 1 + (int)blockIdx.y * p.qchunk;
+    npos = min(T - 1, tlo + p.qchunk - 1) - tlo + 1;
+    if (npos <= 0) return;
   } else {
-    tlo = (k0 / p.lsel) * p.lsel;  // the block's first position
-    thi = T - 1;
+    // The positions that chose one of the workgroup's blocks, from the bitmap
+    // rows, in order; bit 24 + w of an entry: wave w's block was chosen.
+    const int jw[4] = {kw0 / p.lsel, (kw0 + 16) / p.lsel, (kw0 + 32) / p.lsel, (kw0 + 48) / p.lsel};
+    const int first = (kw0 / p.lsel) * p.lsel;  // no earlier position can choose these blocks
+    const int wlo = max(first >> 5, (int)blockIdx.y * p.qwords);
+    const int whi = min(p.nwords, ((int)blockIdx.y + 1) * p.qwords);
+    if (wlo >= whi) return;
+    const uint32_t* rows = p.bits + bgl * p.nblk * p.nwords;
+    const int wi = wlo + tid;
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    if (tid < p.qwords && wi < whi) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) m[w] = jw[w] < p.nblk ? rows[(int64_t)jw[w] * p.nwords + wi] : 0u;
+    }
+    const uint32_t any = m[0] | m[1] | m[2] | m[3];
+    int tot;
+    int off = block_scan<256>(__builtin_popcount(any), s_scan, &tot);
+    uint32_t x = any;
+    while (x) {
+      const int bit = __builtin_ctz(x);
+      x &= x - 1;
+      int mask = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mask |= (int)((m[w] >> bit) & 1u) << w;
+      s_list[off++] = (32 * wi + bit) | (mask << 24);
+    }
+    __syncthreads();
+    tlo = 0;
+    npos = tot;
+    if (npos == 0) return;
   }
-  if (tlo > thi) return;
+  const int npair = (npos + 1) / 2;
 
-  KvWave<DK, DV, MODE> wv{p, b, g, lg, lr, k0 + lr, nkeys, bgl};
+  // Position of entry i and the waves it concerns (all for window / compressed).
+  auto entry = [&](int i, int& t, int& mask) {
+    if (i >= npos) { t = -1; mask = 0; return; }
+    if constexpr (MODE == kSlc) {
+      const int e = s_list[i];
+      t = e & 0xFFFFFF;
+      mask = e >> 24;
+    } else {
+      t = tlo + i;
+      mask = 0xF;
+    }
+  };
+
+  // Copies of pair i into buffer i % kKvBuf (the same number of instructions in every wave).
+  auto issue = [&](int i) {
+    int tA, mA, tB, mB;
+    entry(2 * i, tA, mA);
+    entry(2 * i + 1, tB, mB);
+    if (tB < 0) tB = tA;  // a duplicate, masked out in the compute
+    char* buf = s_buf[i % kKvBuf];
+#pragma unroll
+    for (int j = 0; j < SH::kCpQ; ++j) {
+      const int pch = (wave * SH::kCpQ + j) * 64 + lane;  // LDS chunk: row r, slot s
+      const int r = pch / (DK / 8), sl = pch - r * (DK / 8);
+      const int c = sl ^ (r & 7);
+      const int tt = r < 16 ? tA : tB, h = min(r & 15, G - 1);
+      const uint16_t* src = p.q + (((int64_t)b * T + tt) * Hq + (int64_t)g * G + h) * DK + 8 * c;
+      copy16_to_lds(src, buf + (wave * SH::kCpQ + j) * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < SH::kCpO; ++j) {
+      const int pch = (wave * SH::kCpO + j) * 64 + lane;
+      const int r = pch / (DV / 8), sl = pch - r * (DV / 8);
+      const int c = sl ^ (r & 7);
+      const int tt = r < 16 ? tA : tB, h = min(r & 15, G - 1);
+      const uint16_t* src = p.dout + (((int64_t)b * T + tt) * Hq + (int64_t)g * G + h) * DV + 8 * c;
+      copy16_to_lds(src, buf + 2 * SH::kQ + (wave * SH::kCpO + j) * 1024);
+    }
+    // statistics: 2 records x 12 chunks, 6 lanes per wave
+    if (lane < 6) {
+      const int ch = wave * 6 + lane, x = ch / 12, cc = ch - x * 12;
+      const int tt = x == 0 ? tA : tB;
+      const float* src = p.stat + ((((int64_t)MODE * p.B + b) * T + tt) * p.H + g) * kStatFloats + 4 * cc;
+      copy16_to_lds(src, buf + 2 * SH::kQ + 2 * SH::kO + wave * 96);
+    }
+  };
+
+  u32x4_t kf[DK / 32], vf[DV / 32];
   const uint16_t* kb = MODE == kCmp ? p.kc + bgl * p.nc * DK : p.k + bgl * T * DK;
   const uint16_t* vb = MODE == kCmp ? p.vc + bgl * p.nc * DV : p.v + bgl * T * DV;
-  load_k_tile<DK>(kb, k0 + lr, nkeys, lg, wv.kf);
-  load_k_tile<DV>(vb, k0 + lr, nkeys, lg, wv.vf);
+  load_k_tile<DK>(kb, key, nkeys, lg, kf);
+  load_k_tile<DV>(vb, key, nkeys, lg, vf);
+  f32x4_t dka[DK / 16], dva[DV / 16];
 #pragma unroll
-  for (int j = 0; j < DK / 16; ++j) wv.dka[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < DK / 16; ++j) dka[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < DV / 16; ++j) wv.dva[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < DV / 16; ++j) dva[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  wait_vmem();
 
-  if constexpr (MODE == kSlc) {
-    // Walk the selection bitmap row of this wave's block over this workgroup's
-    // range of 32-position words; positions are taken in pairs.
-    const int j = k0 / p.lsel;
-    const uint32_t* row = p.bits + ((int64_t)bgl * p.nblk + j) * p.nwords;
-    const int w0 = max(tlo >> 5, (int)blockIdx.y * p.qwords);
-    const int w1 = min(p.nwords, ((int)blockIdx.y + 1) * p.qwords);
-    int pend = -1;
-    for (int wi = w0; wi < w1; ++wi) {
-      uint32_t bits = row[wi];
-      while (bits) {
-        const int t = 32 * wi + __builtin_ctz(bits);
-        bits &= bits - 1;
-        if (pend < 0) {
-          pend = t;
-        } else {
-          wv.pair(pend, t);
-          pend = -1;
-        }
+  auto visible = [&](int t) {
+    if (key >= nkeys) return false;
+    if constexpr (MODE == kWin) return key <= t && key > t - p.w;
+    if constexpr (MODE == kSlc) return key <= t;
+    return key * p.d + p.l - 1 <= t;
+  };
+
+  issue(0);
+  if (npair > 1) issue(1);
+  for (int i = 0; i < npair; ++i) {
+    if (i + 1 < npair) wait_vmem_le<SH::kCopies>(); else wait_vmem();
+    lds_barrier();
+    if (i + 2 < npair) issue(i + 2);
+    const char* buf = s_buf[i % kKvBuf];
+    const char* bq = buf;
+    const char* bo = buf + 2 * SH::kQ;
+    const float* bs = reinterpret_cast<const float*>(buf + 2 * SH::kQ + 2 * SH::kO);
+    float pg[2][4], ds[2][4];
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+      int t, mask;
+      entry(2 * i + X, t, mask);
+      const int r = 16 * X + lr;
+      u32x4_t qa[DK / 32], oa[DV / 32];
+#pragma unroll
+      for (int kk = 0; kk < DK / 32; ++kk) qa[kk] = lds_frag<DK>(bq, r, 8 * lg + 32 * kk);
+#pragma unroll
+      for (int kk = 0; kk < DV / 32; ++kk) oa[kk] = lds_frag<DV>(bo, r, 8 * lg + 32 * kk);
+      const f32x4_t s = qk_tile<DK>(qa, kf);   // S[head 4lg+i][key lr]
+      const f32x4_t dp = qk_tile<DV>(oa, vf);  // dout . v
+      const f32x4_t lse = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 4 * lg);
+      const f32x4_t dc = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 16 + 4 * lg);
+      const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 32 + 4 * lg);
+      const bool vis = t >= 0 && ((mask >> wave) & 1) && visible(t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = vis && 4 * lg + e < G;
+        const float pr = ok ? __builtin_amdgcn_exp2f(s[e] * p.scale_log2 - lse[e]) : 0.f;
+        pg[X][e] = pr * gt[e];
+        ds[X][e] = pr * (gt[e] * dp[e] - dc[e]);
       }
     }
-    if (pend >= 0) wv.pair(pend, -1);
-  } else {
-    for (int t = tlo; t <= thi; t += 2) wv.pair(t, t + 1 <= thi ? t + 1 : -1);
+    uint32_t orow[8][DV / 32];
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) lds_piece<DV>(bo, (r8 < 4 ? 0 : 16) + 4 * lg + (r8 & 3), lr, orow[r8]);
+    pv_step<DV>(orow, pack_probs(pg[0], pg[1]), dva);
+    uint32_t qrow[8][DK / 32];
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) lds_piece<DK>(bq, (r8 < 4 ? 0 : 16) + 4 * lg + (r8 & 3), lr, qrow[r8]);
+    pv_step<DK>(qrow, pack_probs(ds[0], ds[1]), dka);
   }
 
-  const int key = k0 + lr;
   if (key >= nkeys) return;
   float* dk = (MODE == kCmp ? p.dkc + bgl * p.nc * DK : p.dk + bgl * T * DK) + (int64_t)key * DK;
   float* dv = (MODE == kCmp ? p.dvc + bgl * p.nc * DV : p.dv + bgl * T * DV) + (int64_t)key * DV;
@@ -388,13 +477,13 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < DK / 16; ++j) {
-      const float x = wv.dka[j][i] * p.scale;
+      const float x = dka[j][i] * p.scale;
       float* a = dk + (DK / 16) * (4 * lg + i) + j;
       if constexpr (MODE == kWin) *a = x; else unsafeAtomicAdd(a, x);
     }
 #pragma unroll
     for (int j = 0; j < DV / 16; ++j) {
-      const float x = wv.dva[j][i];
+      const float x = dva[j][i];
       float* a = dv + (DV / 16) * (4 * lg + i) + j;
       if constexpr (MODE == kWin) *a = x; else unsafeAtomicAdd(a, x);
     }

@@ -5,6 +5,9 @@
 
 namespace nsa {
 
+constexpr int kStatFloats = 48;      // statistics record of one (branch, position, group)
+constexpr int kBwdQWordsMax = 128;   // selected-branch key side: most 32-position words per workgroup
+
 // Prefill backward (gradients of the three-branch output).
 struct BwdParams {
   int B, T, Hq, H, G;
@@ -29,8 +32,8 @@ struct BwdParams {
   float* dkc;                        // [B, H, nc, DK]
   float* dvc;                        // [B, H, nc, DV]
   float* dgates;                     // [B, T, Hq, 3]
-  float* lse;                        // workspace [3, B, T, Hq]: per-branch log2-sum-exp2 of the logits
-  float* delta;                      // workspace [3, B, T, Hq]: g_c (dO . o_c)
+  float* stat;                       // workspace [3, B, T, H, kStatFloats]: per branch and group, the
+                                     // heads' lse (log2 units) [16] | g_c (dO . o_c) [16] | g_c [16]
   uint32_t* bits;                    // workspace [B, H, nblk, nwords]: position t selected block j
 };
 

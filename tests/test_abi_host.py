@@ -206,8 +206,8 @@ def test_binding_refuses_host_tensors():
 def test_backward_workspace_sizes_and_validation():
     dims, cfg = _dims(batch=1), _cfg()
     T = 32768
-    # lse and D [3, 1, T, 64] fp32 each, bitmap [1, 4, T/64, T/32] uint32
-    assert N.nsa_prefill_bwd_workspace_size(dims, cfg, T) == 2 * 3 * T * 64 * 4 + 4 * 512 * 1024 * 4
+    # statistics records [3, 1, T, 4, 48] fp32, bitmap [1, 4, T/64, T/32] uint32
+    assert N.nsa_prefill_bwd_workspace_size(dims, cfg, T) == 3 * T * 4 * 48 * 4 + 4 * 512 * 1024 * 4
     nc = (T - 32) // 16 + 1
     assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0) == -(-(4 * nc * 32 * 192 * 4) // 256) * 256 + 64 * 192 * 4
     assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 1) == -(-(4 * nc * 32 * 128 * 4) // 256) * 256 + 64 * 128 * 4
