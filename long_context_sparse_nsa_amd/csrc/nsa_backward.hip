@@ -37,23 +37,17 @@ constexpr int kCmp = 0, kSlc = 1, kWin = 2;  // branch ids (gate and lse slot or
 constexpr int kBwdWaves = 4;                 // waves per workgroup
 constexpr float kNegInf = -__builtin_inff();
 
-// Row pieces for a product whose contraction runs over 8 rows: lane lr holds the
-// D/16 contiguous channels starting at (D/16)*lr of row `row` (zeros if !ok).
-template <int D>
-__device__ __forceinline__ void load_piece(const uint16_t* row, bool ok, int lr, uint32_t (&w)[D / 32]) {
-  static_assert(D == 64 || D == 128 || D == 192, "row width");
-  if (!ok) {
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) w[i] = 0u;
-    return;
-  }
-  const uint16_t* p = row + (D / 16) * lr;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {  // 8-byte loads: (D/16)*lr elements is 8-byte aligned for every D here
-    const u32x2_t x = ld8(p + 4 * i);
-    w[2 * i] = x[0];
-    w[2 * i + 1] = x[1];
-  }
+// Wait until this wave's copies of at most `later` subsequent steps (C copy
+// instructions each, LATER at most) are still in flight; copies complete in
+// issue order.
+template <int C, int LATER>
+__device__ __forceinline__ void wait_steps(int later) {
+  static_assert(LATER >= 1 && LATER <= 4 && C * LATER < 64, "vmcnt range");
+  if (later >= 4 && LATER >= 4) wait_vmem_le<C * (LATER >= 4 ? 4 : 0)>();
+  else if (later >= 3 && LATER >= 3) wait_vmem_le<C * (LATER >= 3 ? 3 : 0)>();
+  else if (later >= 2 && LATER >= 2) wait_vmem_le<C * (LATER >= 2 ? 2 : 0)>();
+  else if (later >= 1) wait_vmem_le<C>();
+  else wait_vmem();
 }
 
 __device__ __forceinline__ int n_visible(int t, int l, int d, int nc) {
@@ -61,217 +55,9 @@ __device__ __forceinline__ int n_visible(int t, int l, int d, int nc) {
 }
 
 // ---------------------------------------------------------------------------
-// Query side.
-
-// One key range [s0, s1) of a branch, forward recompute: online softmax state
-// (m in log2 units, l) and O^T accumulators (layout of pv_step).
-template <int DK, int DV>
-__device__ __forceinline__ void fwd_range(const uint16_t* kb, const uint16_t* vb, int s0, int s1,
-                                          const u32x4_t (&qf)[DK / 32], float sl2, int lg, int lr, float& m,
-                                          float& l, f32x4_t (&acc)[DV / 16]) {
-  for (int k0 = s0; k0 < s1; k0 += 32) {
-    u32x4_t kf0[DK / 32], kf1[DK / 32];
-    load_k_tile<DK>(kb, k0 + lr, s1, lg, kf0);
-    load_k_tile<DK>(kb, k0 + 16 + lr, s1, lg, kf1);
-    uint32_t vr[8][DV / 32];
-    load_v_step<DV>(vb, k0, s1, lg, lr, vr);
-    const f32x4_t a = qk_tile<DK>(kf0, qf), c = qk_tile<DK>(kf1, qf);
-    float z[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = (k0 + 4 * lg + i < s1) ? a[i] * sl2 : kNegInf;
-      z[4 + i] = (k0 + 16 + 4 * lg + i < s1) ? c[i] * sl2 : kNegInf;
-    }
-    float mx = z[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, z[r]);
-    mx = max_over_groups(mx);
-    const float mn = fmaxf(m, mx);  // finite: key k0 < s1 is always valid
-    const float al = __builtin_amdgcn_exp2f(m - mn);
-    float pr[8], ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      pr[r] = __builtin_amdgcn_exp2f(z[r] - mn);
-      ps += pr[r];
-    }
-    ps = sum_over_groups(ps);
-    l = l * al + ps;
-    m = mn;
-#pragma unroll
-    for (int j = 0; j < DV / 16; ++j) acc[j] *= al;
-    const float lo[4] = {pr[0], pr[1], pr[2], pr[3]}, hi[4] = {pr[4], pr[5], pr[6], pr[7]};
-    pv_step<DV>(vr, pack_probs(lo, hi), acc);
-  }
-}
-
-// One key range of a branch, gradient pass: dq^T += K^T dS^T.
-template <int DK, int DV>
-__device__ __forceinline__ void dq_range(const uint16_t* kb, const uint16_t* vb, int s0, int s1,
-                                         const u32x4_t (&qf)[DK / 32], const u32x4_t (&of)[DV / 32], float sl2,
-                                         float lse2, float gate, float dc, int lg, int lr, f32x4_t (&dqa)[DK / 16]) {
-  for (int k0 = s0; k0 < s1; k0 += 32) {
-    u32x4_t kf0[DK / 32], kf1[DK / 32], vf0[DV / 32], vf1[DV / 32];
-    load_k_tile<DK>(kb, k0 + lr, s1, lg, kf0);
-    load_k_tile<DK>(kb, k0 + 16 + lr, s1, lg, kf1);
-    load_k_tile<DV>(vb, k0 + lr, s1, lg, vf0);
-    load_k_tile<DV>(vb, k0 + 16 + lr, s1, lg, vf1);
-    uint32_t kr[8][DK / 32];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int key = k0 + step_key(lg, r);
-      load_piece<DK>(kb + (int64_t)key * DK, key < s1, lr, kr[r]);
-    }
-    const f32x4_t a = qk_tile<DK>(kf0, qf), c = qk_tile<DK>(kf1, qf);
-    const f32x4_t pa = qk_tile<DV>(vf0, of), pc = qk_tile<DV>(vf1, of);
-    float lo[4], hi[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = (k0 + 4 * lg + i < s1) ? __builtin_amdgcn_exp2f(a[i] * sl2 - lse2) : 0.f;
-      const float p1 = (k0 + 16 + 4 * lg + i < s1) ? __builtin_amdgcn_exp2f(c[i] * sl2 - lse2) : 0.f;
-      lo[i] = p0 * (gate * pa[i] - dc);
-      hi[i] = p1 * (gate * pc[i] - dc);
-    }
-    pv_step<DK>(kr, pack_probs(lo, hi), dqa);
-  }
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_query_kernel(BwdParams p) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15;
-  const int wave = threadIdx.x >> 6;
-  // Consecutive workgroups cycle through the (b, g) pairs; latest positions first.
-  const int nbg = p.B * p.H;
-  const int bid = (int)blockIdx.x;
-  const int tile = p.nqt - 1 - bid / nbg;
-  const int bg = bid - (bid / nbg) * nbg;
-  const int b = bg / p.H, g = bg - (bg / p.H) * p.H;
-  const int t = tile * kBwdWaves + wave;
-  if (t >= p.T) return;
-  const int T = p.T, G = p.G, Hq = p.Hq;
-  const int64_t bgl = (int64_t)b * p.H + g;
-  const uint16_t* kraw = p.k + bgl * T * DK;
-  const uint16_t* vraw = p.v + bgl * T * DV;
-  const uint16_t* kcmp = p.kc + bgl * p.nc * DK;
-  const uint16_t* vcmp = p.vc + bgl * p.nc * DV;
-  const int64_t qrow = ((int64_t)b * T + t) * Hq + (int64_t)g * G;  // the group's first head
-  const bool hv = lr < G;
-
-  u32x4_t qf[DK / 32], of[DV / 32];
-  load_q_frags<DK>(p.q + qrow * DK, G, lg, lr, qf);
-  load_q_frags<DV>(p.dout + qrow * DV, G, lg, lr, of);
-  float gt[3];
-#pragma unroll
-  for (int c = 0; c < 3; ++c) gt[c] = hv ? p.gates[(qrow + lr) * 3 + c] : 0.f;
-  // dO channels of this lane in the O^T accumulator layout: (DV/16)*(4lg+i) + j.
-  float dov[4][DV / 16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t w[DV / 32];
-    const uint16_t* src = p.dout + (qrow + lr) * DV + (DV / 16) * (4 * lg + i);
-#pragma unroll
-    for (int u = 0; u < DV / 64; ++u) {
-      const u32x2_t x = hv ? ld8(src + 4 * u) : u32x2_t{0u, 0u};
-      w[2 * u] = x[0];
-      w[2 * u + 1] = x[1];
-    }
-#pragma unroll
-    for (int u = 0; u < DV / 32; ++u) {
-      dov[i][2 * u] = bf16_lo(w[u]);
-      dov[i][2 * u + 1] = bf16_hi(w[u]);
-    }
-  }
-
-  const int nvis = n_visible(t, p.l, p.d, p.nc);
-  const int32_t* selrow = p.sel + (((int64_t)b * T + t) * p.H + g) * p.n;
-  const int wlo = max(0, t - p.w + 1);
-  const float sl2 = p.scale_log2;
-
-  // Pass 1: per-branch softmax statistics and outputs.
-  float lse2[3], dcs[3];
-#pragma unroll 1
-  for (int c = 0; c < 3; ++c) {
-    float m = kNegInf, l = 0.f;
-    f32x4_t acc[DV / 16];
-#pragma unroll
-    for (int j = 0; j < DV / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (c == kCmp) {
-      if (nvis > 0) fwd_range<DK, DV>(kcmp, vcmp, 0, nvis, qf, sl2, lg, lr, m, l, acc);
-    } else if (c == kWin) {
-      fwd_range<DK, DV>(kraw, vraw, wlo, t + 1, qf, sl2, lg, lr, m, l, acc);
-    } else {
-      for (int s = 0; s < p.n; ++s) {
-        const int j = selrow[s];
-        if (j < 0) break;
-        const int s0 = j * p.lsel, s1 = min(s0 + p.lsel, t + 1);
-        if (s0 < s1) fwd_range<DK, DV>(kraw, vraw, s0, s1, qf, sl2, lg, lr, m, l, acc);
-      }
-    }
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < DV / 16; ++j) dot = fmaf(acc[j][i], dov[i][j], dot);
-    dot = sum_over_groups(dot);
-    const bool any = l > 0.f;
-    dot = any ? dot / l : 0.f;  // dO . o_c
-    lse2[c] = any ? m + __log2f(l) : 0.f;
-    dcs[c] = gt[c] * dot;
-    if (lg == 0) {  // statistics record of (c, b, t, g): lse[16] | D[16] | gate[16], zeros past G
-      float* rec = p.stat + ((((int64_t)c * p.B + b) * T + t) * p.H + g) * kStatFloats;
-      rec[lr] = hv ? lse2[c] : 0.f;
-      rec[16 + lr] = hv ? dcs[c] : 0.f;
-      rec[32 + lr] = gt[c];
-      if (hv) p.dgates[(qrow + lr) * 3 + c] = dot;
-    }
-  }
-
-  // Pass 2: dq over the same key ranges.
-  f32x4_t dqa[DK / 16];
-#pragma unroll
-  for (int j = 0; j < DK / 16; ++j) dqa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (nvis > 0) dq_range<DK, DV>(kcmp, vcmp, 0, nvis, qf, of, sl2, lse2[kCmp], gt[kCmp], dcs[kCmp], lg, lr, dqa);
-  dq_range<DK, DV>(kraw, vraw, wlo, t + 1, qf, of, sl2, lse2[kWin], gt[kWin], dcs[kWin], lg, lr, dqa);
-  for (int s = 0; s < p.n; ++s) {
-    const int j = selrow[s];
-    if (j < 0) break;
-    const int s0 = j * p.lsel, s1 = min(s0 + p.lsel, t + 1);
-    if (s0 < s1) dq_range<DK, DV>(kraw, vraw, s0, s1, qf, of, sl2, lse2[kSlc], gt[kSlc], dcs[kSlc], lg, lr, dqa);
-  }
-  if (hv) {
-    float* dst = p.dq + (qrow + lr) * DK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j4 = 0; j4 < DK / 64; ++j4) {
-        const int j = 4 * j4;
-        *reinterpret_cast<f32x4_t*>(dst + (DK / 16) * (4 * lg + i) + j) =
-            f32x4_t{dqa[j][i], dqa[j + 1][i], dqa[j + 2][i], dqa[j + 3][i]} * p.scale;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Key side.  A workgroup owns 64 keys, a wave 16 of them (the MFMA columns,
-// K and V fragments held in registers).  The queries that see those keys are
-// taken two at a time: the 32 rows (query, head) of a pair form the contraction
-// of dV^T += dout^T (g P) and dK^T += Q^T dS.  Each pair's Q rows, dout rows and
-// statistics records are copied global -> LDS directly by all four waves,
-// kKvBuf buffers deep; within a row the 16-byte chunks are XOR-swizzled with the
-// row index so that the MFMA operand reads (16 rows at one column) spread over
+// LDS blocks of D-wide bf16 rows: the 16-byte chunk c of row r sits at slot
+// c ^ (r & 7), so that MFMA operand reads of 16 rows at one column spread over
 // the LDS banks.
-
-constexpr int kKvBuf = 3;
-
-template <int DK, int DV>
-struct KvShape {
-  static constexpr int kQ = 32 * DK;  // bf16 elements of a pair's Q rows
-  static constexpr int kO = 32 * DV;
-  static constexpr int kBuf = 2 * kQ + 2 * kO + 2 * kStatFloats * 4;  // bytes per buffer
-  static constexpr int kCpQ = 32 * DK / 8 / 256;                       // copies per wave
-  static constexpr int kCpO = 32 * DV / 8 / 256;
-  static constexpr int kCopies = kCpQ + kCpO + 1;
-  static_assert(32 * DK % 2048 == 0 && 32 * DV % 2048 == 0, "whole copy instructions per wave");
-};
 
 // Byte offset in LDS of channel e (a multiple of 4) of row r of a block of D-wide rows.
 template <int D>
@@ -294,8 +80,356 @@ __device__ __forceinline__ void lds_piece(const char* blk, int r, int lr, uint32
   }
 }
 
+// ---------------------------------------------------------------------------
+// Query side.  A workgroup owns 4 consecutive positions of one (b, g); a wave one
+// position, its 16 heads the MFMA columns.  The 32-key tiles of the three
+// branches are copied once into LDS for the four waves, kQtBuf buffers deep:
+// the compressed blocks [0, nvis) and the window's union are contiguous ranges,
+// the selected branch walks the union of the four positions' blocks, each block
+// marked with the waves that chose it.  Pass 1 recomputes every branch's online
+// softmax (statistics record, dgates); pass 2 stages the same tiles again and
+// accumulates dq^T += K^T dS^T.
+
+constexpr int kQtBuf = 3;
+
+template <int DK, int DV>
+struct QtShape {
+  static constexpr int kK = 32 * DK, kV = 32 * DV;  // bf16 elements of a 32-key tile
+  static constexpr int kBuf = 2 * kK + 2 * kV;        // bytes per buffer
+  static constexpr int kCpK = 32 * DK / 8 / 256, kCpV = 32 * DV / 8 / 256;  // copies per wave
+  static constexpr int kCopies = kCpK + kCpV;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
+  using SH = QtShape<DK, DV>;
+  __shared__ __attribute__((aligned(1024))) char s_buf[kQtBuf][SH::kBuf];
+  __shared__ uint32_t s_bm[4][kPfMaxBlocks / 32];  // each wave's selected blocks
+  __shared__ int32_t s_sel[kPfMaxBlocks];          // union, ascending: block | wave mask << 16
+  __shared__ int s_scan[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Consecutive workgroups cycle through the (b, g) pairs; latest positions first.
+  const int nbg = p.B * p.H;
+  const int bid = (int)blockIdx.x;
+  const int tile = p.nqt - 1 - bid / nbg;
+  const int bg = bid - (bid / nbg) * nbg;
+  const int b = bg / p.H, g = bg - (bg / p.H) * p.H;
+  const int T = p.T, G = p.G, Hq = p.Hq, nc = p.nc;
+  const int t0 = tile * kBwdWaves, t = t0 + wave, tl = min(t0 + kBwdWaves - 1, T - 1);
+  const bool tv = t < T;
+  const int64_t bgl = (int64_t)b * p.H + g;
+  const uint16_t* kraw = p.k + bgl * T * DK;
+  const uint16_t* vraw = p.v + bgl * T * DV;
+  const uint16_t* kcmp = p.kc + bgl * nc * DK;
+  const uint16_t* vcmp = p.vc + bgl * nc * DV;
+  const int64_t qrow = ((int64_t)b * T + (tv ? t : tl)) * Hq + (int64_t)g * G;  // the group's first head
+  const bool hv = lr < G;
+
+  // Union of the four positions' selected blocks.
+  for (int i = tid; i < 4 * (kPfMaxBlocks / 32); i += 256) (&s_bm[0][0])[i] = 0u;
+  __syncthreads();
+  if (tv) {
+    for (int s = lane; s < p.n; s += 64) {
+      const int j = p.sel[(((int64_t)b * T + t) * p.H + g) * p.n + s];
+      if (j >= 0 && j < p.nblk) atomicOr(&s_bm[wave][j >> 5], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+  uint32_t mw[4] = {0u, 0u, 0u, 0u}, un = 0u;
+  if (tid < kPfMaxBlocks / 32) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mw[w] = s_bm[w][tid];
+    un = mw[0] | mw[1] | mw[2] | mw[3];
+  }
+  int nsel;
+  int off = block_scan<256>(__builtin_popcount(un), s_scan, &nsel);
+  while (un) {
+    const int bit = __builtin_ctz(un);
+    un &= un - 1;
+    int mask = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mask |= (int)((mw[w] >> bit) & 1u) << w;
+    s_sel[off++] = (32 * tid + bit) | (mask << 16);
+  }
+  __syncthreads();
+
+  // The workgroup's tiles: compressed, selected, window; pass 2 repeats them.
+  const int ncmp = (n_visible(tl, p.l, p.d, nc) + 31) / 32;
+  const int tps = max(1, p.lsel / 32);  // tiles per selected block
+  const int nslc = nsel * tps;
+  const int wlo = max(0, t0 - p.w + 1);
+  const int nwin = (tl - wlo) / 32 + 1;
+  const int ntile = ncmp + nslc + nwin, nstep = 2 * ntile;
+
+  auto desc = [&](int i, int& br, int& k0, int& wm, int& kend) {
+    const int u = i < ntile ? i : i - ntile;
+    if (u < ncmp) {
+      br = kCmp; k0 = 32 * u; wm = 0xF; kend = nc;
+    } else if (u < ncmp + nslc) {
+      const int e = s_sel[(u - ncmp) / tps], j = e & 0xFFFF;
+      br = kSlc; k0 = j * p.lsel + 32 * ((u - ncmp) % tps); wm = e >> 16; kend = min(j * p.lsel + p.lsel, T);
+    } else {
+      br = kWin; k0 = wlo + 32 * (u - ncmp - nslc); wm = 0xF; kend = T;
+    }
+  };
+
+  auto issue = [&](int i) {
+    int br, k0, wm, kend;
+    desc(i, br, k0, wm, kend);
+    const uint16_t* kb = br == kCmp ? kcmp : kraw;
+    const uint16_t* vb = br == kCmp ? vcmp : vraw;
+    const int nk = br == kCmp ? nc : T;
+    char* buf = s_buf[i % kQtBuf];
+#pragma unroll
+    for (int j = 0; j < SH::kCpK; ++j) {
+      const int pch = (wave * SH::kCpK + j) * 64 + lane;
+      const int r = pch / (DK / 8), sl = pch - r * (DK / 8);
+      const int key = min(k0 + r, nk - 1);  // rows past the end: a valid row, masked in the compute
+      copy16_to_lds(kb + (int64_t)key * DK + 8 * (sl ^ (r & 7)), buf + (wave * SH::kCpK + j) * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < SH::kCpV; ++j) {
+      const int pch = (wave * SH::kCpV + j) * 64 + lane;
+      const int r = pch / (DV / 8), sl = pch - r * (DV / 8);
+      const int key = min(k0 + r, nk - 1);
+      copy16_to_lds(vb + (int64_t)key * DV + 8 * (sl ^ (r & 7)), buf + 2 * SH::kK + (wave * SH::kCpV + j) * 1024);
+    }
+  };
+
+  u32x4_t qf[DK / 32], of[DV / 32];
+  load_q_frags<DK>(p.q + qrow * DK, tv ? G : 0, lg, lr, qf);
+  load_q_frags<DV>(p.dout + qrow * DV, tv ? G : 0, lg, lr, of);
+  float gt[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) gt[c] = (tv && hv) ? p.gates[(qrow + lr) * 3 + c] : 0.f;
+  const int nvis = tv ? n_visible(t, p.l, p.d, nc) : 0;
+  const float sl2 = p.scale_log2;
+  wait_vmem();
+
+  // Pass-1 state of the current branch, and the finished branches' statistics.
+  float m = kNegInf, l = 0.f;
+  f32x4_t acc[DV / 16];
+#pragma unroll
+  for (int j = 0; j < DV / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float lse_c[3] = {0.f, 0.f, 0.f}, dc_c[3] = {0.f, 0.f, 0.f};
+  int fin = 0;
+  auto finalize = [&](const int c) {
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* src = p.dout + (qrow + lr) * DV + (DV / 16) * (4 * lg + i);
+#pragma unroll
+      for (int u = 0; u < DV / 64; ++u) {
+        const u32x2_t x = (tv && hv) ? ld8(src + 4 * u) : u32x2_t{0u, 0u};
+        dot = fmaf(acc[4 * u][i], bf16_lo(x[0]), dot);
+        dot = fmaf(acc[4 * u + 1][i], bf16_hi(x[0]), dot);
+        dot = fmaf(acc[4 * u + 2][i], bf16_lo(x[1]), dot);
+        dot = fmaf(acc[4 * u + 3][i], bf16_hi(x[1]), dot);
+      }
+    }
+    dot = sum_over_groups(dot);
+    const bool any = l > 0.f;
+    dot = any ? dot / l : 0.f;  // dout . o_c
+    const float gc = c == kCmp ? gt[0] : (c == kSlc ? gt[1] : gt[2]);
+    const float ls = any ? m + __log2f(l) : 0.f, dcv = gc * dot;
+    if (c == kCmp) { lse_c[0] = ls; dc_c[0] = dcv; }
+    else if (c == kSlc) { lse_c[1] = ls; dc_c[1] = dcv; }
+    else { lse_c[2] = ls; dc_c[2] = dcv; }
+    if (tv && lg == 0) {  // statistics record of (c, b, t, g): lse[16] | D[16] | gate[16], zeros past G
+      float* rec = p.stat + ((((int64_t)c * p.B + b) * T + t) * p.H + g) * kStatFloats;
+      rec[lr] = hv ? ls : 0.f;
+      rec[16 + lr] = hv ? dcv : 0.f;
+      rec[32 + lr] = gc;
+      if (hv) p.dgates[(qrow + lr) * 3 + c] = dot;
+    }
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int j = 0; j < DV / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // One pipeline step: wait for tile i, hand the next buffer to the copies.
+  auto step_begin = [&](int i) {
+    wait_steps<SH::kCopies, kQtBuf - 2>(min(nstep - 1 - i, kQtBuf - 2));
+    lds_barrier();
+    if (i + kQtBuf - 1 < nstep) issue(i + kQtBuf - 1);
+  };
+  // This wave's valid keys of step i's tile: [klo, khi).
+  auto key_range = [&](int br, int k0, int wm, int kend, int& klo, int& khi) {
+    klo = 0;
+    khi = 0;
+    if (tv && ((wm >> wave) & 1)) {
+      if (br == kCmp) khi = nvis;
+      else if (br == kSlc) khi = min(kend, t + 1);
+      else { klo = t - p.w + 1; khi = t + 1; }
+    }
+    klo = max(klo, k0);
+    khi = min(khi, k0 + 32);
+  };
+
+  for (int i = 0; i < kQtBuf - 1 && i < nstep; ++i) issue(i);
+  // Pass 1: each branch's online softmax.
+  for (int i = 0; i < ntile; ++i) {
+    step_begin(i);
+    int br, k0, wm, kend, klo, khi;
+    desc(i, br, k0, wm, kend);
+    if (fin < br) {
+      while (fin < br) finalize(fin++);
+      wait_vmem();  // keep the copy count exact for the next wait
+    }
+    key_range(br, k0, wm, kend, klo, khi);
+    if (klo >= khi) continue;
+    const char* kt = s_buf[i % kQtBuf];
+    const char* vt = kt + 2 * SH::kK;
+    u32x4_t kf0[DK / 32], kf1[DK / 32];
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) {
+      kf0[kk] = lds_frag<DK>(kt, lr, 8 * lg + 32 * kk);
+      kf1[kk] = lds_frag<DK>(kt, 16 + lr, 8 * lg + 32 * kk);
+    }
+    uint32_t vr[8][DV / 32];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) lds_piece<DV>(vt, step_key(lg, r), lr, vr[r]);
+    const f32x4_t a = qk_tile<DK>(kf0, qf), c = qk_tile<DK>(kf1, qf);
+    float z[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x0 = k0 + 4 * lg + e, x1 = x0 + 16;
+      z[e] = (x0 >= klo && x0 < khi) ? a[e] * sl2 : kNegInf;
+      z[4 + e] = (x1 >= klo && x1 < khi) ? c[e] * sl2 : kNegInf;
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, z[r]);
+    mx = max_over_groups(mx);
+    const float mn = fmaxf(m, mx);  // finite: the tile holds a valid key of this wave
+    const float al = __builtin_amdgcn_exp2f(m - mn);
+    float pr[8], ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      pr[r] = __builtin_amdgcn_exp2f(z[r] - mn);
+      ps += pr[r];
+    }
+    ps = sum_over_groups(ps);
+    l = l * al + ps;
+    m = mn;
+#pragma unroll
+    for (int j = 0; j < DV / 16; ++j) acc[j] *= al;
+    const float lo[4] = {pr[0], pr[1], pr[2], pr[3]}, hi[4] = {pr[4], pr[5], pr[6], pr[7]};
+    pv_step<DV>(vr, pack_probs(lo, hi), acc);
+  }
+  while (fin < 3) finalize(fin++);
+  wait_vmem();
+
+  // Pass 2: dq over the same tiles.
+  f32x4_t dqa[DK / 16];
+#pragma unroll
+  for (int j = 0; j < DK / 16; ++j) dqa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = ntile; i < nstep; ++i) {
+    step_begin(i);
+    int br, k0, wm, kend, klo, khi;
+    desc(i, br, k0, wm, kend);
+    key_range(br, k0, wm, kend, klo, khi);
+    if (klo >= khi) continue;
+    const char* kt = s_buf[i % kQtBuf];
+    const char* vt = kt + 2 * SH::kK;
+    const float ls = br == kCmp ? lse_c[0] : (br == kSlc ? lse_c[1] : lse_c[2]);
+    const float dc = br == kCmp ? dc_c[0] : (br == kSlc ? dc_c[1] : dc_c[2]);
+    const float gc = br == kCmp ? gt[0] : (br == kSlc ? gt[1] : gt[2]);
+    u32x4_t kf0[DK / 32], kf1[DK / 32];
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) {
+      kf0[kk] = lds_frag<DK>(kt, lr, 8 * lg + 32 * kk);
+      kf1[kk] = lds_frag<DK>(kt, 16 + lr, 8 * lg + 32 * kk);
+    }
+    const f32x4_t a = qk_tile<DK>(kf0, qf), c = qk_tile<DK>(kf1, qf);
+    u32x4_t vf0[DV / 32], vf1[DV / 32];
+#pragma unroll
+    for (int kk = 0; kk < DV / 32; ++kk) {
+      vf0[kk] = lds_frag<DV>(vt, lr, 8 * lg + 32 * kk);
+      vf1[kk] = lds_frag<DV>(vt, 16 + lr, 8 * lg + 32 * kk);
+    }
+    const f32x4_t pa = qk_tile<DV>(vf0, of), pc = qk_tile<DV>(vf1, of);
+    float lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x0 = k0 + 4 * lg + e, x1 = x0 + 16;
+      const float p0 = (x0 >= klo && x0 < khi) ? __builtin_amdgcn_exp2f(a[e] * sl2 - ls) : 0.f;
+      const float p1 = (x1 >= klo && x1 < khi) ? __builtin_amdgcn_exp2f(c[e] * sl2 - ls) : 0.f;
+      lo[e] = p0 * (gc * pa[e] - dc);
+      hi[e] = p1 * (gc * pc[e] - dc);
+    }
+    uint32_t kr[8][DK / 32];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) lds_piece<DK>(kt, step_key(lg, r), lr, kr[r]);
+    pv_step<DK>(kr, pack_probs(lo, hi), dqa);
+  }
+
+  if (tv && hv) {
+    float* dst = p.dq + (qrow + lr) * DK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < DK / 64; ++j4) {
+        const int j = 4 * j4;
+        *reinterpret_cast<f32x4_t*>(dst + (DK / 16) * (4 * lg + i) + j) =
+            f32x4_t{dqa[j][i], dqa[j + 1][i], dqa[j + 2][i], dqa[j + 3][i]} * p.scale;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side.  A workgroup owns 64 keys, a wave 16 of them (the MFMA columns,
+// K and V fragments held in registers).  The queries that see those keys are
+// taken two at a time: the 32 rows (query, head) of a pair form the contraction
+// of dV^T += dout^T (g P) and dK^T += Q^T dS.  Each pair's Q rows, dout rows and
+// statistics records are copied global -> LDS directly by all four waves,
+// kKvBuf buffers deep (kKvBuf - 1 pairs in flight); within a row the 16-byte chunks are XOR-swizzled with the
+// row index so that the MFMA operand reads (16 rows at one column) spread over
+// the LDS banks.
+
+constexpr int kKvBuf = 3;
+
+template <int DK, int DV>
+struct KvShape {
+  static constexpr int kQ = 32 * DK;  // bf16 elements of a pair's Q rows
+  static constexpr int kO = 32 * DV;
+  static constexpr int kBuf = 2 * kQ + 2 * kO + 2 * kStatFloats * 4;  // bytes per buffer
+  static constexpr int kCpQ = 32 * DK / 8 / 256;                       // copies per wave
+  static constexpr int kCpO = 32 * DV / 8 / 256;
+  static constexpr int kCopies = kCpQ + kCpO + 1;
+  static_assert(32 * DK % 2048 == 0 && 32 * DV % 2048 == 0, "whole copy instructions per wave");
+};
+
+// acc^T += rows^T . pb for 8 rows of an LDS block (the pv_step product), the row
+// pieces read in 8-byte slices: slice u feeds the four MFMAs of output channels
+// (D/16)*m + 4u .. 4u+3, so only 8 x 2 words are live at a time.
+template <int D>
+__device__ __forceinline__ void lds_rows_product(const char* blk, const int (&rows)[8], int lr, const u32x4_t& pb,
+                                                 f32x4_t (&acc)[D / 16]) {
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) {
+    uint32_t w[8][2];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(blk + sw_off<D>(rows[r], (D / 16) * lr + 4 * u));
+      w[r][0] = x[0];
+      w[r][1] = x[1];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int wd = jj >> 1, h = jj & 1;
+      const u32x4_t va = {pack_halves(w[0][wd], w[1][wd], h), pack_halves(w[2][wd], w[3][wd], h),
+                          pack_halves(w[4][wd], w[5][wd], h), pack_halves(w[6][wd], w[7][wd], h)};
+      acc[4 * u + jj] = mfma_bf16(va, pb, acc[4 * u + jj]);
+    }
+  }
+}
+
 template <int DK, int DV, int MODE>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   using SH = KvShape<DK, DV>;
   __shared__ __attribute__((aligned(1024))) char s_buf[kKvBuf][SH::kBuf];
   __shared__ int32_t s_list[MODE == kSlc ? 32 * kBwdQWordsMax : 1];
@@ -425,12 +559,11 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     return key * p.d + p.l - 1 <= t;
   };
 
-  issue(0);
-  if (npair > 1) issue(1);
+  for (int i = 0; i < kKvBuf - 1 && i < npair; ++i) issue(i);
   for (int i = 0; i < npair; ++i) {
-    if (i + 1 < npair) wait_vmem_le<SH::kCopies>(); else wait_vmem();
+    wait_steps<SH::kCopies, kKvBuf - 2>(min(npair - 1 - i, kKvBuf - 2));
     lds_barrier();
-    if (i + 2 < npair) issue(i + 2);
+    if (i + kKvBuf - 1 < npair) issue(i + kKvBuf - 1);
     const char* buf = s_buf[i % kKvBuf];
     const char* bq = buf;
     const char* bo = buf + 2 * SH::kQ;
@@ -460,14 +593,11 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
         ds[X][e] = pr * (gt[e] * dp[e] - dc[e]);
       }
     }
-    uint32_t orow[8][DV / 32];
+    int rows[8];
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) lds_piece<DV>(bo, (r8 < 4 ? 0 : 16) + 4 * lg + (r8 & 3), lr, orow[r8]);
-    pv_step<DV>(orow, pack_probs(pg[0], pg[1]), dva);
-    uint32_t qrow[8][DK / 32];
-#pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) lds_piece<DK>(bq, (r8 < 4 ? 0 : 16) + 4 * lg + (r8 & 3), lr, qrow[r8]);
-    pv_step<DK>(qrow, pack_probs(ds[0], ds[1]), dka);
+    for (int r8 = 0; r8 < 8; ++r8) rows[r8] = (r8 < 4 ? 0 : 16) + 4 * lg + (r8 & 3);
+    lds_rows_product<DV>(bo, rows, lr, pack_probs(pg[0], pg[1]), dva);
+    lds_rows_product<DK>(bq, rows, lr, pack_probs(ds[0], ds[1]), dka);
   }
 
   if (key >= nkeys) return;
