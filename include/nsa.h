@@ -299,9 +299,11 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
  *   dk_cmp, dv_cmp  float32 [B, Hkv, nc, d_k / d_v], nc = floor((T-l)/d)+1
  *          (written; may be NULL when T < l)
  *   dgates float32 [B, T, Hq, 3]               (written)
+ * Supported: the shapes of nsa_prefill_fwd with seq_len * Hq * max(d_k, d_v) * 2
+ * below 2^32 (one sequence's query rows addressable with 32-bit offsets).
  * Products are bf16 MFMA with fp32 sums (probabilities and dS rounded to bf16
- * as operands).  The selected and compressed contributions are added with fp32
- * atomics, so the last bits of dk, dv, dk_cmp and dv_cmp may vary between runs.
+ * as operands).  Partial sums are combined in a fixed order (no atomics), so
+ * repeated calls give identical bits.
  */
 nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
                              const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -311,8 +313,13 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
                              float* dgates, void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes for nsa_prefill_bwd (host-only): per (branch, position, KV
  * group) a record of 48 fp32 (the heads' log-sum-exp, D and gate, padded to 16
- * heads), [3, B, T, Hkv, 48], and a selection bitmap [B, Hkv, ceil(T/l_sel),
- * ceil(T/32)] uint32.  Contents on entry do not matter. */
+ * heads), [3, B, T, Hkv, 48]; a selection bitmap [B, Hkv, ceil(T/l_sel),
+ * ceil(T/32)] uint32; and the key side's fp32 partial sums over position
+ * ranges: [P_s, B, Hkv, T, d_k + d_v] for the selected branch, P_s =
+ * ceil(W / (128 * ceil(ceil(W / 8) / 128))) with W = ceil(T/32) (at most 8),
+ * and [P_c, B, Hkv, nc, d_k + d_v] for the compressed branch, P_c =
+ * ceil(T / q), q = max(1024, ceil(T/32)) rounded up to even (at most 32).
+ * Each part is rounded up to 256 bytes.  Contents on entry do not matter. */
 nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                             int64_t seq_len, size_t* bytes);
 

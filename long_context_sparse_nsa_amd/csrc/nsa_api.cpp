@@ -1,5 +1,6 @@
 // C ABI of the NSA forward pass: argument validation (host only, before any
 // HIP call), workspace planning and kernel launches on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -557,23 +558,46 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
 
 namespace {
 
+// Prefill-backward plan: the key side's position ranges.  The selected branch
+// splits a block's positions into at most kBwdMaxParts ranges of whole 128-word
+// bitmap slices; the compressed branch into ranges of at least 1024 positions,
+// at most 32 of them.
+struct BwdPlan {
+  int qwords, nqw, qchunk, ncq;
+};
+BwdPlan bwd_plan(int64_t T) {
+  BwdPlan pl{};
+  const int nwords = (int)((T + 31) / 32);
+  const int per = (nwords + nsa::kBwdMaxParts - 1) / nsa::kBwdMaxParts;
+  pl.qwords = (per + 127) / 128 * 128;
+  pl.nqw = (nwords + pl.qwords - 1) / pl.qwords;
+  pl.qchunk = (int)std::max<int64_t>(1024, (T + 31) / 32);
+  pl.qchunk += pl.qchunk & 1;
+  pl.ncq = (int)((T + pl.qchunk - 1) / pl.qchunk);
+  return pl;
+}
+
 // Prefill-backward workspace: per-branch statistics records [3, B, T, Hkv, 48]
-// fp32, then the selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32.
+// fp32, the selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32, and
+// the key side's partial sums: selected [nqw, B, Hkv, T, d_k + d_v] and
+// compressed [ncq, B, Hkv, nc, d_k + d_v] fp32.
 struct BwdWs {
-  size_t off_stat, off_bits, total;
+  size_t off_stat, off_bits, off_pslc, off_pcmp, total;
 };
 BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   BwdWs w{};
-  const size_t recs = (size_t)3 * dims->batch * (size_t)T * dims->num_kv_heads;
+  const BwdPlan pl = bwd_plan(T);
+  const size_t bh = (size_t)dims->batch * dims->num_kv_heads, wd = (size_t)(dims->d_k + dims->d_v);
+  const size_t recs = (size_t)3 * bh * (size_t)T;
   const size_t nblk = (size_t)((T + cfg->l_sel - 1) / cfg->l_sel), nwords = (size_t)((T + 31) / 32);
+  const size_t nc = (size_t)n_compressed(T, cfg->l, cfg->d);
   w.off_stat = 0;
   w.off_bits = align256(recs * nsa::kStatFloats * 4);
-  w.total = w.off_bits + align256((size_t)dims->batch * dims->num_kv_heads * nblk * nwords * 4);
+  w.off_pslc = w.off_bits + align256(bh * nblk * nwords * 4);
+  w.off_pcmp = w.off_pslc + align256((size_t)pl.nqw * bh * (size_t)T * wd * 4);
+  w.total = w.off_pcmp + align256((size_t)pl.ncq * bh * nc * wd * 4);
   return w;
 }
-
-constexpr int kBwdQWords = nsa::kBwdQWordsMax;  // selected-branch key side: 4096 positions per workgroup
-constexpr int kBwdQChunk = 1024;  // compressed-branch key side: positions per workgroup
 
 // Compression-backward workspace: dX [B*Hkv*nc, l*D] fp32, then 64 column-sum partials [64, D].
 size_t cbwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, int D) {
@@ -618,6 +642,8 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
   if (!q || !k || !v || !gates || !sel_idx || !dout || !dq || !dk || !dv || !dgates)
     return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if (seq_len * dims->num_q_heads * (int64_t)std::max(dims->d_k, dims->d_v) * 2 >= ((int64_t)1 << 32))
+    return fail(NSA_ERROR_UNSUPPORTED, "seq_len * num_q_heads * max(d_k, d_v) * 2 must stay below 2^32 bytes");
   const int64_t nc = n_compressed(seq_len, cfg->l, cfg->d);
   if (nc > 0 && (!k_cmp || !v_cmp || !dk_cmp || !dv_cmp))
     return fail(NSA_ERROR_INVALID_VALUE, "the compressed cache and its gradient buffers are required (%lld blocks)",
@@ -644,10 +670,11 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.nqt = (int)((seq_len + 3) / 4);
   p.nblk = (int)((seq_len + cfg->l_sel - 1) / cfg->l_sel);
   p.nwords = (int)((seq_len + 31) / 32);
-  p.qwords = kBwdQWords;
-  p.nqw = (p.nwords + kBwdQWords - 1) / kBwdQWords;
-  p.qchunk = kBwdQChunk;
-  p.ncq = (int)((seq_len + kBwdQChunk - 1) / kBwdQChunk);
+  const BwdPlan pl = bwd_plan(seq_len);
+  p.qwords = pl.qwords;
+  p.nqw = pl.nqw;
+  p.qchunk = pl.qchunk;
+  p.ncq = pl.ncq;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -664,6 +691,8 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.dgates = dgates;
   p.stat = reinterpret_cast<float*>(ws + lay.off_stat);
   p.bits = reinterpret_cast<uint32_t*>(ws + lay.off_bits);
+  p.part_slc = reinterpret_cast<float*>(ws + lay.off_pslc);
+  p.part_cmp = reinterpret_cast<float*>(ws + lay.off_pcmp);
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_prefill_bwd(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "prefill backward launch");

@@ -21,10 +21,13 @@
 //                       (lse, D, dg) and then accumulates dq over all branches.
 //   bwd_kv_kernel<WIN>  one wave per 16 raw keys: the window queries; stores dk, dv.
 //   bwd_kv_kernel<SLC>  one wave per 16 raw keys and a range of positions: the
-//                       queries that selected the keys' block; adds into dk, dv.
-//   bwd_kv_kernel<CMP>  one wave per 16 compressed keys and a range of positions:
-//                       adds into dk_cmp, dv_cmp.
-// Products are bf16 MFMA (P and dS rounded to bf16 as operands) with fp32 sums.
+//                       queries that selected the keys' block; partial sums per range.
+//   bwd_kv_kernel<CMP>  one wave per 16 compressed keys and a range of positions;
+//                       partial sums per range.
+//   bwd_kv_reduce_kernel  adds the selected partials to dk, dv and sums the
+//                       compressed ones into dk_cmp, dv_cmp, in a fixed order.
+// Products are bf16 MFMA (P and dS rounded to bf16 as operands) with fp32 sums;
+// no atomics on gradients, so results repeat bit for bit.
 #include <algorithm>
 
 #include "nsa_train.hpp"
@@ -36,6 +39,29 @@ namespace {
 constexpr int kCmp = 0, kSlc = 1, kWin = 2;  // branch ids (gate and lse slot order)
 constexpr int kBwdWaves = 4;                 // waves per workgroup
 constexpr float kNegInf = -__builtin_inff();
+
+// Wave-wide direct global -> LDS copy of 64 x 16 bytes (as copy16_to_lds) to
+// the wave-uniform LDS byte address `lds_addr`: lane l's 16 bytes land at
+// lds_addr + 16 * l.
+__device__ __forceinline__ void copy16_to_lds_at(const void* src, uint32_t lds_addr) {
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+// The same copy from a wave-uniform base address plus this lane's 32-bit byte
+// offset (the scalar-base form of the instruction).
+__device__ __forceinline__ void copy16_sb_at(const void* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(lds)
+               : "memory", "m0");
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* shared_ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)shared_ptr;
+}
 
 // Wait until this wave's copies of at most `later` subsequent steps (C copy
 // instructions each, LATER at most) are still in flight; copies complete in
@@ -107,6 +133,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
   __shared__ uint32_t s_bm[4][kPfMaxBlocks / 32];  // each wave's selected blocks
   __shared__ int32_t s_sel[kPfMaxBlocks];          // union, ascending: block | wave mask << 16
   __shared__ int s_scan[4];
+  const uint32_t lds0 = lds_addr_of(&s_buf[0][0]);
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,20 +208,20 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
     const uint16_t* kb = br == kCmp ? kcmp : kraw;
     const uint16_t* vb = br == kCmp ? vcmp : vraw;
     const int nk = br == kCmp ? nc : T;
-    char* buf = s_buf[i % kQtBuf];
+    const uint32_t buf = lds0 + (uint32_t)((i % kQtBuf) * SH::kBuf);
 #pragma unroll
     for (int j = 0; j < SH::kCpK; ++j) {
       const int pch = (wave * SH::kCpK + j) * 64 + lane;
       const int r = pch / (DK / 8), sl = pch - r * (DK / 8);
       const int key = min(k0 + r, nk - 1);  // rows past the end: a valid row, masked in the compute
-      copy16_to_lds(kb + (int64_t)key * DK + 8 * (sl ^ (r & 7)), buf + (wave * SH::kCpK + j) * 1024);
+      copy16_to_lds_at(kb + (int64_t)key * DK + 8 * (sl ^ (r & 7)), buf + (wave * SH::kCpK + j) * 1024);
     }
 #pragma unroll
     for (int j = 0; j < SH::kCpV; ++j) {
       const int pch = (wave * SH::kCpV + j) * 64 + lane;
       const int r = pch / (DV / 8), sl = pch - r * (DV / 8);
       const int key = min(k0 + r, nk - 1);
-      copy16_to_lds(vb + (int64_t)key * DV + 8 * (sl ^ (r & 7)), buf + 2 * SH::kK + (wave * SH::kCpV + j) * 1024);
+      copy16_to_lds_at(vb + (int64_t)key * DV + 8 * (sl ^ (r & 7)), buf + 2 * SH::kK + (wave * SH::kCpV + j) * 1024);
     }
   };
 
@@ -431,9 +458,11 @@ __device__ __forceinline__ void lds_rows_product(const char* blk, const int (&ro
 template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   using SH = KvShape<DK, DV>;
+  constexpr int kSubWords = 128;  // selected branch: 32-position words listed at a time
   __shared__ __attribute__((aligned(1024))) char s_buf[kKvBuf][SH::kBuf];
-  __shared__ int32_t s_list[MODE == kSlc ? 32 * kBwdQWordsMax : 1];
+  __shared__ int32_t s_list[MODE == kSlc ? 32 * kSubWords : 1];
   __shared__ int s_scan[4];
+  const uint32_t lds0 = lds_addr_of(&s_buf[0][0]);
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -449,96 +478,6 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   const int k0 = kw0 + 16 * wave;
   const int key = k0 + lr;
   const int64_t bgl = (int64_t)b * p.H + g;
-
-  // Positions visited by the workgroup.
-  int tlo, npos;
-  if constexpr (MODE == kWin) {
-    tlo = kw0;
-    npos = min(T - 1, kw0 + 63 + p.w - 1) - tlo + 1;
-  } else if constexpr (MODE == kCmp) {
-    tlo = kw0 * p.d + p.l - 1 + (int)blockIdx.y * p.qchunk;
-    npos = min(T - 1, tlo + p.qchunk - 1) - tlo + 1;
-    if (npos <= 0) return;
-  } else {
-    // The positions that chose one of the workgroup's blocks, from the bitmap
-    // rows, in order; bit 24 + w of an entry: wave w's block was chosen.
-    const int jw[4] = {kw0 / p.lsel, (kw0 + 16) / p.lsel, (kw0 + 32) / p.lsel, (kw0 + 48) / p.lsel};
-    const int first = (kw0 / p.lsel) * p.lsel;  // no earlier position can choose these blocks
-    const int wlo = max(first >> 5, (int)blockIdx.y * p.qwords);
-    const int whi = min(p.nwords, ((int)blockIdx.y + 1) * p.qwords);
-    if (wlo >= whi) return;
-    const uint32_t* rows = p.bits + bgl * p.nblk * p.nwords;
-    const int wi = wlo + tid;
-    uint32_t m[4] = {0u, 0u, 0u, 0u};
-    if (tid < p.qwords && wi < whi) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) m[w] = jw[w] < p.nblk ? rows[(int64_t)jw[w] * p.nwords + wi] : 0u;
-    }
-    const uint32_t any = m[0] | m[1] | m[2] | m[3];
-    int tot;
-    int off = block_scan<256>(__builtin_popcount(any), s_scan, &tot);
-    uint32_t x = any;
-    while (x) {
-      const int bit = __builtin_ctz(x);
-      x &= x - 1;
-      int mask = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) mask |= (int)((m[w] >> bit) & 1u) << w;
-      s_list[off++] = (32 * wi + bit) | (mask << 24);
-    }
-    __syncthreads();
-    tlo = 0;
-    npos = tot;
-    if (npos == 0) return;
-  }
-  const int npair = (npos + 1) / 2;
-
-  // Position of entry i and the waves it concerns (all for window / compressed).
-  auto entry = [&](int i, int& t, int& mask) {
-    if (i >= npos) { t = -1; mask = 0; return; }
-    if constexpr (MODE == kSlc) {
-      const int e = s_list[i];
-      t = e & 0xFFFFFF;
-      mask = e >> 24;
-    } else {
-      t = tlo + i;
-      mask = 0xF;
-    }
-  };
-
-  // Copies of pair i into buffer i % kKvBuf (the same number of instructions in every wave).
-  auto issue = [&](int i) {
-    int tA, mA, tB, mB;
-    entry(2 * i, tA, mA);
-    entry(2 * i + 1, tB, mB);
-    if (tB < 0) tB = tA;  // a duplicate, masked out in the compute
-    char* buf = s_buf[i % kKvBuf];
-#pragma unroll
-    for (int j = 0; j < SH::kCpQ; ++j) {
-      const int pch = (wave * SH::kCpQ + j) * 64 + lane;  // LDS chunk: row r, slot s
-      const int r = pch / (DK / 8), sl = pch - r * (DK / 8);
-      const int c = sl ^ (r & 7);
-      const int tt = r < 16 ? tA : tB, h = min(r & 15, G - 1);
-      const uint16_t* src = p.q + (((int64_t)b * T + tt) * Hq + (int64_t)g * G + h) * DK + 8 * c;
-      copy16_to_lds(src, buf + (wave * SH::kCpQ + j) * 1024);
-    }
-#pragma unroll
-    for (int j = 0; j < SH::kCpO; ++j) {
-      const int pch = (wave * SH::kCpO + j) * 64 + lane;
-      const int r = pch / (DV / 8), sl = pch - r * (DV / 8);
-      const int c = sl ^ (r & 7);
-      const int tt = r < 16 ? tA : tB, h = min(r & 15, G - 1);
-      const uint16_t* src = p.dout + (((int64_t)b * T + tt) * Hq + (int64_t)g * G + h) * DV + 8 * c;
-      copy16_to_lds(src, buf + 2 * SH::kQ + (wave * SH::kCpO + j) * 1024);
-    }
-    // statistics: 2 records x 12 chunks, 6 lanes per wave
-    if (lane < 6) {
-      const int ch = wave * 6 + lane, x = ch / 12, cc = ch - x * 12;
-      const int tt = x == 0 ? tA : tB;
-      const float* src = p.stat + ((((int64_t)MODE * p.B + b) * T + tt) * p.H + g) * kStatFloats + 4 * cc;
-      copy16_to_lds(src, buf + 2 * SH::kQ + 2 * SH::kO + wave * 96);
-    }
-  };
 
   u32x4_t kf[DK / 32], vf[DV / 32];
   const uint16_t* kb = MODE == kCmp ? p.kc + bgl * p.nc * DK : p.k + bgl * T * DK;
@@ -559,64 +498,215 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
     return key * p.d + p.l - 1 <= t;
   };
 
-  for (int i = 0; i < kKvBuf - 1 && i < npair; ++i) issue(i);
-  for (int i = 0; i < npair; ++i) {
-    wait_steps<SH::kCopies, kKvBuf - 2>(min(npair - 1 - i, kKvBuf - 2));
-    lds_barrier();
-    if (i + kKvBuf - 1 < npair) issue(i + kKvBuf - 1);
-    const char* buf = s_buf[i % kKvBuf];
-    const char* bq = buf;
-    const char* bo = buf + 2 * SH::kQ;
-    const float* bs = reinterpret_cast<const float*>(buf + 2 * SH::kQ + 2 * SH::kO);
-    float pg[2][4], ds[2][4];
+  // This lane's copy offsets within a pair (bytes from the first position's
+  // rows; bit 31: the row belongs to the second position).  LDS chunk pch of a
+  // block holds row r = pch / (D/8), slot sl, i.e. global chunk sl ^ (r & 7).
+  uint32_t offq[SH::kCpQ], offo[SH::kCpO], offs;
 #pragma unroll
-    for (int X = 0; X < 2; ++X) {
-      int t, mask;
-      entry(2 * i + X, t, mask);
-      const int r = 16 * X + lr;
-      u32x4_t qa[DK / 32], oa[DV / 32];
+  for (int j = 0; j < SH::kCpQ; ++j) {
+    const int pch = (wave * SH::kCpQ + j) * 64 + lane;
+    const int r = pch / (DK / 8), sl = pch - r * (DK / 8), h = min(r & 15, G - 1);
+    offq[j] = (uint32_t)((((g * G + h) * DK) + 8 * (sl ^ (r & 7))) * 2) | (r >= 16 ? 0x80000000u : 0u);
+  }
 #pragma unroll
-      for (int kk = 0; kk < DK / 32; ++kk) qa[kk] = lds_frag<DK>(bq, r, 8 * lg + 32 * kk);
+  for (int j = 0; j < SH::kCpO; ++j) {
+    const int pch = (wave * SH::kCpO + j) * 64 + lane;
+    const int r = pch / (DV / 8), sl = pch - r * (DV / 8), h = min(r & 15, G - 1);
+    offo[j] = (uint32_t)((((g * G + h) * DV) + 8 * (sl ^ (r & 7))) * 2) | (r >= 16 ? 0x80000000u : 0u);
+  }
+  {
+    const int ch = wave * 6 + min(lane, 5), x = ch / 12, cc = ch - x * 12;
+    offs = (uint32_t)(16 * cc) | (x ? 0x80000000u : 0u);
+  }
+
+  // The workgroup's positions come in segments (one for the window and the
+  // compressed branch; one per 128-word slice of the bitmap for the selected).
+  int nseg = 1, wlo = 0, whi = 0;
+  int jw[4] = {0, 0, 0, 0};
+  if constexpr (MODE == kSlc) {
 #pragma unroll
-      for (int kk = 0; kk < DV / 32; ++kk) oa[kk] = lds_frag<DV>(bo, r, 8 * lg + 32 * kk);
-      const f32x4_t s = qk_tile<DK>(qa, kf);   // S[head 4lg+i][key lr]
-      const f32x4_t dp = qk_tile<DV>(oa, vf);  // dout . v
-      const f32x4_t lse = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 4 * lg);
-      const f32x4_t dc = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 16 + 4 * lg);
-      const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 32 + 4 * lg);
-      const bool vis = t >= 0 && ((mask >> wave) & 1) && visible(t);
+    for (int w = 0; w < 4; ++w) jw[w] = (kw0 + 16 * w) / p.lsel;
+    const int first = jw[0] * p.lsel;  // no earlier position can choose these blocks
+    wlo = max(first >> 5, (int)blockIdx.y * p.qwords);
+    whi = min(p.nwords, ((int)blockIdx.y + 1) * p.qwords);
+    nseg = whi > wlo ? (whi - wlo + kSubWords - 1) / kSubWords : 0;
+  }
+  for (int seg = 0; seg < nseg; ++seg) {
+    int tlo = 0, npos = 0;
+    if constexpr (MODE == kWin) {
+      tlo = kw0;
+      npos = min(T - 1, kw0 + 63 + p.w - 1) - tlo + 1;
+    } else if constexpr (MODE == kCmp) {
+      tlo = kw0 * p.d + p.l - 1 + (int)blockIdx.y * p.qchunk;
+      npos = max(0, min(T - 1, tlo + p.qchunk - 1) - tlo + 1);
+    } else {
+      // The positions that chose one of the workgroup's blocks, in order; bit
+      // 24 + w of an entry: wave w's block was chosen.
+      __syncthreads();  // the previous segment's list is no longer read
+      const int w0 = wlo + seg * kSubWords, w1 = min(whi, w0 + kSubWords);
+      const uint32_t* rows = p.bits + bgl * p.nblk * p.nwords;
+      const int wi = w0 + tid;
+      uint32_t m[4] = {0u, 0u, 0u, 0u};
+      if (tid < kSubWords && wi < w1) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = vis && 4 * lg + e < G;
-        const float pr = ok ? __builtin_amdgcn_exp2f(s[e] * p.scale_log2 - lse[e]) : 0.f;
-        pg[X][e] = pr * gt[e];
-        ds[X][e] = pr * (gt[e] * dp[e] - dc[e]);
+        for (int w = 0; w < 4; ++w) m[w] = jw[w] < p.nblk ? rows[(int64_t)jw[w] * p.nwords + wi] : 0u;
       }
-    }
-    int rows[8];
+      const uint32_t any = m[0] | m[1] | m[2] | m[3];
+      int off = block_scan<256>(__builtin_popcount(any), s_scan, &npos);
+      uint32_t x = any;
+      while (x) {
+        const int bit = __builtin_ctz(x);
+        x &= x - 1;
+        int mask = 0;
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) rows[r8] = (r8 < 4 ? 0 : 16) + 4 * lg + (r8 & 3);
-    lds_rows_product<DV>(bo, rows, lr, pack_probs(pg[0], pg[1]), dva);
-    lds_rows_product<DK>(bq, rows, lr, pack_probs(ds[0], ds[1]), dka);
+        for (int w = 0; w < 4; ++w) mask |= (int)((m[w] >> bit) & 1u) << w;
+        s_list[off++] = (32 * wi + bit) | (mask << 24);
+      }
+      __syncthreads();
+    }
+    if (npos == 0) continue;
+    const int npair = (npos + 1) / 2;
+
+    // Position of entry i and the waves it concerns (all for window / compressed).
+    auto entry = [&](int i, int& t, int& mask) {
+      if (i >= npos) { t = -1; mask = 0; return; }
+      if constexpr (MODE == kSlc) {
+        const int e = s_list[i];
+        t = e & 0xFFFFFF;
+        mask = e >> 24;
+      } else {
+        t = tlo + i;
+        mask = 0xF;
+      }
+    };
+
+    // Copies of pair i into buffer i % kKvBuf (the same number of instructions in
+    // every wave): from the first position's rows plus this lane's offset, which
+    // adds the distance to the second position's rows when its flag bit is set.
+    auto issue = [&](int i) {
+      int tA, mA, tB, mB;
+      entry(2 * i, tA, mA);
+      entry(2 * i + 1, tB, mB);
+      if (tB < 0) tB = tA;  // a duplicate, masked out in the compute
+      const uint32_t buf = lds0 + (uint32_t)((i % kKvBuf) * SH::kBuf);
+      const uint16_t* qA = p.q + ((int64_t)b * T + tA) * Hq * DK;
+      const uint16_t* oA = p.dout + ((int64_t)b * T + tA) * Hq * DV;
+      const uint32_t dq = (uint32_t)(tB - tA) * (uint32_t)(Hq * DK * 2);
+      const uint32_t dov = (uint32_t)(tB - tA) * (uint32_t)(Hq * DV * 2);
+#pragma unroll
+      for (int j = 0; j < SH::kCpQ; ++j)
+        copy16_sb_at(qA, (offq[j] & 0x7FFFFFFFu) + ((offq[j] >> 31) ? dq : 0u), buf + (wave * SH::kCpQ + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < SH::kCpO; ++j)
+        copy16_sb_at(oA, (offo[j] & 0x7FFFFFFFu) + ((offo[j] >> 31) ? dov : 0u),
+                     buf + 2 * SH::kQ + (wave * SH::kCpO + j) * 1024);
+      if (lane < 6) {  // statistics: 2 records x 12 chunks, 6 lanes per wave
+        const float* sA = p.stat + ((((int64_t)MODE * p.B + b) * T + tA) * p.H + g) * kStatFloats;
+        const uint32_t ds = (uint32_t)(tB - tA) * (uint32_t)(p.H * kStatFloats * 4);
+        copy16_sb_at(sA, (offs & 0x7FFFFFFFu) + ((offs >> 31) ? ds : 0u), buf + 2 * SH::kQ + 2 * SH::kO + wave * 96);
+      }
+    };
+
+    for (int i = 0; i < kKvBuf - 1 && i < npair; ++i) issue(i);
+    for (int i = 0; i < npair; ++i) {
+      wait_steps<SH::kCopies, kKvBuf - 2>(min(npair - 1 - i, kKvBuf - 2));
+      lds_barrier();
+      if (i + kKvBuf - 1 < npair) issue(i + kKvBuf - 1);
+      const char* buf = s_buf[i % kKvBuf];
+      const char* bq = buf;
+      const char* bo = buf + 2 * SH::kQ;
+      const float* bs = reinterpret_cast<const float*>(buf + 2 * SH::kQ + 2 * SH::kO);
+      float pg[2][4], ds[2][4];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        int t, mask;
+        entry(2 * i + X, t, mask);
+        const int r = 16 * X + lr;
+        u32x4_t qa[DK / 32], oa[DV / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) qa[kk] = lds_frag<DK>(bq, r, 8 * lg + 32 * kk);
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk) oa[kk] = lds_frag<DV>(bo, r, 8 * lg + 32 * kk);
+        const f32x4_t sc = qk_tile<DK>(qa, kf);  // S[head 4lg+i][key lr]
+        const f32x4_t dp = qk_tile<DV>(oa, vf);  // dout . v
+        const f32x4_t lse = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 4 * lg);
+        const f32x4_t dc = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 16 + 4 * lg);
+        const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(bs + X * kStatFloats + 32 + 4 * lg);
+        const bool vis = t >= 0 && ((mask >> wave) & 1) && visible(t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = vis && 4 * lg + e < G;
+          const float pr = ok ? __builtin_amdgcn_exp2f(sc[e] * p.scale_log2 - lse[e]) : 0.f;
+          pg[X][e] = pr * gt[e];
+          ds[X][e] = pr * (gt[e] * dp[e] - dc[e]);
+        }
+      }
+      int rows[8];
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) rows[r8] = (r8 < 4 ? 0 : 16) + 4 * lg + (r8 & 3);
+      lds_rows_product<DV>(bo, rows, lr, pack_probs(pg[0], pg[1]), dva);
+      lds_rows_product<DK>(bq, rows, lr, pack_probs(ds[0], ds[1]), dka);
+    }
   }
 
   if (key >= nkeys) return;
-  float* dk = (MODE == kCmp ? p.dkc + bgl * p.nc * DK : p.dk + bgl * T * DK) + (int64_t)key * DK;
-  float* dv = (MODE == kCmp ? p.dvc + bgl * p.nc * DV : p.dv + bgl * T * DV) + (int64_t)key * DV;
+  // Window: the owner stores dk, dv.  Selected / compressed: this workgroup's
+  // partial sums go to its slice of the workspace (zeros when it saw no
+  // position), summed by bwd_kv_reduce_kernel in a fixed order.
+  float* dk;
+  float* dv;
+  int stride;
+  if constexpr (MODE == kWin) {
+    dk = p.dk + (bgl * T + key) * DK;
+    dv = p.dv + (bgl * T + key) * DV;
+    stride = 1;
+  } else {
+    const int64_t rows = MODE == kSlc ? (int64_t)nbg * T : (int64_t)nbg * p.nc;
+    const int64_t row = (int64_t)blockIdx.y * rows + bgl * nkeys + key;
+    float* base = (MODE == kSlc ? p.part_slc : p.part_cmp) + row * (DK + DV);
+    dk = base;
+    dv = base + DK;
+    stride = 1;
+  }
+  (void)stride;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < DK / 16; ++j) {
-      const float x = dka[j][i] * p.scale;
-      float* a = dk + (DK / 16) * (4 * lg + i) + j;
-      if constexpr (MODE == kWin) *a = x; else unsafeAtomicAdd(a, x);
+    for (int j4 = 0; j4 < DK / 64; ++j4) {
+      const int j = 4 * j4;
+      *reinterpret_cast<f32x4_t*>(dk + (DK / 16) * (4 * lg + i) + j) =
+          f32x4_t{dka[j][i], dka[j + 1][i], dka[j + 2][i], dka[j + 3][i]} * p.scale;
     }
 #pragma unroll
-    for (int j = 0; j < DV / 16; ++j) {
-      const float x = dva[j][i];
-      float* a = dv + (DV / 16) * (4 * lg + i) + j;
-      if constexpr (MODE == kWin) *a = x; else unsafeAtomicAdd(a, x);
+    for (int j4 = 0; j4 < DV / 64; ++j4) {
+      const int j = 4 * j4;
+      *reinterpret_cast<f32x4_t*>(dv + (DV / 16) * (4 * lg + i) + j) =
+          f32x4_t{dva[j][i], dva[j + 1][i], dva[j + 2][i], dva[j + 3][i]};
     }
+  }
+}
+
+// Sum of the key-side partials in a fixed order: selected -> dk, dv += sum;
+// compressed -> dk_cmp, dv_cmp = sum.  One thread per 4 channels of a key row.
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p) {
+  constexpr int W = DK + DV;
+  const int nbg = p.B * p.H;
+  const int64_t nrow = (int64_t)nbg * (MODE == kSlc ? p.T : p.nc);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nrow * (W / 4)) return;
+  const int64_t row = idx / (W / 4);
+  const int c4 = (int)(idx - row * (W / 4)) * 4;
+  const float* src = (MODE == kSlc ? p.part_slc : p.part_cmp) + row * W + c4;
+  const int nparts = MODE == kSlc ? p.nqw : p.ncq;
+  f32x4_t s = *reinterpret_cast<const f32x4_t*>(src);
+  for (int c = 1; c < nparts; ++c) s += *reinterpret_cast<const f32x4_t*>(src + (int64_t)c * nrow * W);
+  if constexpr (MODE == kSlc) {
+    float* dst = c4 < DK ? p.dk + row * DK + c4 : p.dv + row * DV + (c4 - DK);
+    *reinterpret_cast<f32x4_t*>(dst) += s;
+  } else {
+    float* dst = c4 < DK ? p.dkc + row * DK + c4 : p.dvc + row * DV + (c4 - DK);
+    *reinterpret_cast<f32x4_t*>(dst) = s;
   }
 }
 
@@ -650,21 +740,26 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s, const PhaseEvents* ev
   const int nbg = p.B * p.H;
   hipError_t e;
   if ((e = zero_words(p.bits, (int64_t)nbg * p.nblk * p.nwords, s)) != hipSuccess) return e;
-  if ((e = zero_words(p.dkc, (int64_t)nbg * p.nc * DK, s)) != hipSuccess) return e;
-  if ((e = zero_words(p.dvc, (int64_t)nbg * p.nc * DV, s)) != hipSuccess) return e;
   const int64_t nsel = (int64_t)p.B * p.T * p.H * p.n;
   hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((nsel + 255) / 256)), dim3(256), 0, s, p);
   if (ev) hipEventRecord(ev->ev[0], s);
   hipLaunchKernelGGL((bwd_query_kernel<DK, DV>), dim3((unsigned)(nbg * p.nqt)), dim3(256), 0, s, p);
   if (ev) hipEventRecord(ev->ev[1], s);
   const int kraw = (p.T + 63) / 64, kcmp = (p.nc + 63) / 64;
+  constexpr int W4 = (DK + DV) / 4;
   hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kWin>), dim3((unsigned)(nbg * kraw)), dim3(256), 0, s, p);
   hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kSlc>), dim3((unsigned)(nbg * kraw), (unsigned)p.nqw), dim3(256), 0, s,
                      p);
+  const int64_t rraw = (int64_t)nbg * p.T * W4;
+  hipLaunchKernelGGL((bwd_kv_reduce_kernel<DK, DV, kSlc>), dim3((unsigned)((rraw + 255) / 256)), dim3(256), 0, s, p);
   if (ev) hipEventRecord(ev->ev[2], s);
-  if (p.nc > 0)
+  if (p.nc > 0) {
     hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kCmp>), dim3((unsigned)(nbg * kcmp), (unsigned)p.ncq), dim3(256), 0,
                        s, p);
+    const int64_t rcmp = (int64_t)nbg * p.nc * W4;
+    hipLaunchKernelGGL((bwd_kv_reduce_kernel<DK, DV, kCmp>), dim3((unsigned)((rcmp + 255) / 256)), dim3(256), 0, s,
+                       p);
+  }
   if (ev) hipEventRecord(ev->ev[3], s);
   return hipGetLastError();
 }

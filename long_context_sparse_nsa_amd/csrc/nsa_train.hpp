@@ -6,7 +6,7 @@
 namespace nsa {
 
 constexpr int kStatFloats = 48;      // statistics record of one (branch, position, group)
-constexpr int kBwdQWordsMax = 128;   // selected-branch key side: most 32-position words per workgroup
+constexpr int kBwdMaxParts = 8;      // key side: most partial sums per key (position ranges)
 
 // Prefill backward (gradients of the three-branch output).
 struct BwdParams {
@@ -35,6 +35,8 @@ struct BwdParams {
   float* stat;                       // workspace [3, B, T, H, kStatFloats]: per branch and group, the
                                      // heads' lse (log2 units) [16] | g_c (dO . o_c) [16] | g_c [16]
   uint32_t* bits;                    // workspace [B, H, nblk, nwords]: position t selected block j
+  float* part_slc;                   // workspace [nqw, B, H, T, DK + DV]: selected-branch partials
+  float* part_cmp;                   // workspace [ncq, B, H, nc, DK + DV]: compressed-branch partials
 };
 
 // Compression backward of one compressed cache (keys or values).
