@@ -599,11 +599,12 @@ BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   return w;
 }
 
-// Compression-backward workspace: dX [B*Hkv*nc, l*D] fp32, then 64 column-sum partials [64, D].
+// Compression-backward workspace: dX [B*Hkv*nc, l*D] fp32, then 64 column-sum
+// partials [64, D], then the dW product's split partials [8, l*D, D].
 size_t cbwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, int D) {
   const int64_t nc = n_compressed(T, cfg->l, cfg->d);
   return align256((size_t)dims->batch * dims->num_kv_heads * (size_t)nc * cfg->l * D * 4) +
-         align256((size_t)64 * D * 4);
+         align256((size_t)64 * D * 4) + align256((size_t)nsa::kCbwdSplit * cfg->l * D * D * 4);
 }
 
 nsa_status_t check_cbwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, int32_t which) {
@@ -738,6 +739,8 @@ nsa_status_t nsa_compress_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, i
   p.dpe = dpe;
   p.dX = reinterpret_cast<float*>(ws);
   p.part = reinterpret_cast<float*>(ws + align256((size_t)p.BH * (size_t)nc * cfg->l * D * 4));
+  p.dwpart = reinterpret_cast<float*>(ws + align256((size_t)p.BH * (size_t)nc * cfg->l * D * 4) +
+                                      align256((size_t)64 * D * 4));
   hipError_t e = nsa::launch_compress_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "compression backward launch");
   return ok();

@@ -54,27 +54,31 @@ struct DyColsB {  // B(k = (bh, i), n = o) = dY[k][o]
   __device__ float at(int64_t k, int64_t n) const { return p[k * D + n]; }
 };
 
-// C[M x N] = A . B (fp32), 64 x 64 tiles, 4 x 4 outputs per thread.
+// C[M x N] = A . B (fp32), 64 x 64 tiles, 4 x 4 outputs per thread.  With
+// gridDim.z > 1 each z takes the contraction range [z*kz, (z+1)*kz) and writes
+// its partial product to C + z*cz.
 template <class OA, class OB>
 __global__ __launch_bounds__(256) void cbwd_gemm_kernel(int64_t M, int64_t N, int64_t K, OA a, OB bm, float* C,
-                                                        int64_t ldc) {
+                                                        int64_t ldc, int64_t kz, int64_t cz) {
   __shared__ float As[kGK][kGT + 4];
   __shared__ float Bs[kGK][kGT + 4];
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.y * kGT, n0 = (int64_t)blockIdx.x * kGT;
   const int tx = tid & 15, ty = tid >> 4;
+  const int64_t kb = (int64_t)blockIdx.z * kz, ke = std::min<int64_t>(K, kb + kz);
+  C += (int64_t)blockIdx.z * cz;
   float acc[4][4] = {};
-  for (int64_t k0 = 0; k0 < K; k0 += kGK) {
+  for (int64_t k0 = kb; k0 < ke; k0 += kGK) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int mm, kk;
       if (OA::kContig) { mm = tid >> 2; kk = (tid & 3) * 4 + r; } else { mm = tid & 63; kk = (tid >> 6) + 4 * r; }
       const int64_t m = m0 + mm, k = k0 + kk;
-      As[kk][mm] = (m < M && k < K) ? a.at(m, k) : 0.f;
-      int nn, kb;
-      if (OB::kContig) { nn = tid >> 2; kb = (tid & 3) * 4 + r; } else { nn = tid & 63; kb = (tid >> 6) + 4 * r; }
-      const int64_t n = n0 + nn, k2 = k0 + kb;
-      Bs[kb][nn] = (n < N && k2 < K) ? bm.at(k2, n) : 0.f;
+      As[kk][mm] = (m < M && k < ke) ? a.at(m, k) : 0.f;
+      int nn, kb2;
+      if (OB::kContig) { nn = tid >> 2; kb2 = (tid & 3) * 4 + r; } else { nn = tid & 63; kb2 = (tid >> 6) + 4 * r; }
+      const int64_t n = n0 + nn, k2 = k0 + kb2;
+      Bs[kb2][nn] = (n < N && k2 < ke) ? bm.at(k2, n) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -102,6 +106,15 @@ __global__ __launch_bounds__(256) void cbwd_gemm_kernel(int64_t M, int64_t N, in
       if (n < N) C[m * ldc + n] = acc[u][v];
     }
   }
+}
+
+// dw = sum of the split-contraction partials, in order.
+__global__ __launch_bounds__(256) void cbwd_sum_parts_kernel(const float* part, int nparts, int64_t n, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int z = 1; z < nparts; ++z) s += part[(int64_t)z * n + i];
+  out[i] = s;
 }
 
 // Column sums of dY [rows x D], stage 1: partial sums of row chunks.
@@ -166,7 +179,8 @@ hipError_t launch_compress_bwd(const CompressBwdParams& p, hipStream_t s) {
     // dX = dY W^T  [rows x lD]
     hipLaunchKernelGGL((cbwd_gemm_kernel<DyRowsA, WRowsB>),
                        dim3((unsigned)((lD + kGT - 1) / kGT), (unsigned)((rows + kGT - 1) / kGT)), dim3(256), 0, s,
-                       rows, (int64_t)lD, (int64_t)p.D, DyRowsA{p.dy, p.D}, WRowsB{p.w, p.D}, p.dX, (int64_t)lD);
+                       rows, (int64_t)lD, (int64_t)p.D, DyRowsA{p.dy, p.D}, WRowsB{p.w, p.D}, p.dX, (int64_t)lD,
+                       (int64_t)p.D, (int64_t)0);
     const int64_t nfold = (int64_t)p.BH * p.T * p.D;
     hipLaunchKernelGGL(cbwd_fold_kernel, dim3((unsigned)((nfold + 255) / 256)), dim3(256), 0, s, p.dX, p.dx,
                        (int64_t)p.BH, p.T, p.D, p.l, p.d, p.nc);
@@ -174,11 +188,16 @@ hipError_t launch_compress_bwd(const CompressBwdParams& p, hipStream_t s) {
     hipLaunchKernelGGL(cbwd_colsum_part_kernel, dim3((unsigned)((p.D + 255) / 256), kSumChunks), dim3(256), 0, s,
                        p.dy, (int64_t)0, p.D, p.part);
   }
-  // dW = sum x-rows^T dY  [lD x D]  (zero when there is no block)
+  // dW = sum x-rows^T dY  [lD x D]  (zero when there is no block): kCbwdSplit
+  // contraction ranges of whole 16-row chunks, then their sum in order.
+  const int64_t kz = ((rows + kCbwdSplit - 1) / kCbwdSplit + kGK - 1) / kGK * kGK;
+  const int64_t nw = (int64_t)lD * p.D;
   hipLaunchKernelGGL((cbwd_gemm_kernel<XBlocksA, DyColsB>),
-                     dim3((unsigned)((p.D + kGT - 1) / kGT), (unsigned)((lD + kGT - 1) / kGT)), dim3(256), 0, s,
-                     (int64_t)lD, (int64_t)p.D, rows, XBlocksA{p.x, p.T, p.D, p.d, p.nc > 0 ? p.nc : 1},
-                     DyColsB{p.dy, p.D}, p.dw, (int64_t)p.D);
+                     dim3((unsigned)((p.D + kGT - 1) / kGT), (unsigned)((lD + kGT - 1) / kGT), kCbwdSplit), dim3(256),
+                     0, s, (int64_t)lD, (int64_t)p.D, rows, XBlocksA{p.x, p.T, p.D, p.d, p.nc > 0 ? p.nc : 1},
+                     DyColsB{p.dy, p.D}, p.dwpart, (int64_t)p.D, kz > 0 ? kz : (int64_t)kGK, nw);
+  hipLaunchKernelGGL(cbwd_sum_parts_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, p.dwpart,
+                     kCbwdSplit, nw, p.dw);
   hipLaunchKernelGGL(cbwd_pe_kernel, dim3((unsigned)((lD + 255) / 256)), dim3(256), 0, s, p.part, p.w, p.pe, lD, p.D,
                      p.dw, p.dpe);
   return hipGetLastError();

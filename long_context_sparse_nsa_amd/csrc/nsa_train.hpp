@@ -7,6 +7,7 @@ namespace nsa {
 
 constexpr int kStatFloats = 48;      // statistics record of one (branch, position, group)
 constexpr int kBwdMaxParts = 8;      // key side: most partial sums per key (position ranges)
+constexpr int kCbwdSplit = 8;        // compression backward: contraction ranges of the dW product
 
 // Prefill backward (gradients of the three-branch output).
 struct BwdParams {
@@ -52,6 +53,7 @@ struct CompressBwdParams {
   float* dpe;                        // [l, D]
   float* dX;                         // workspace [BH*nc, l*D]
   float* part;                       // workspace [64, D]
+  float* dwpart;                     // workspace [kCbwdSplit, l*D, D]
 };
 hipError_t launch_compress_bwd(const CompressBwdParams& p, hipStream_t s);
 hipError_t launch_prefill_bwd(const BwdParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);

@@ -213,8 +213,10 @@ def test_backward_workspace_sizes_and_validation():
     r256 = lambda x: -(-x // 256) * 256
     assert N.nsa_prefill_bwd_workspace_size(dims, cfg, T) == (3 * T * 4 * 48 * 4 + 4 * 512 * 1024 * 4 +
                                                              8 * 4 * T * 320 * 4 + r256(32 * 4 * nc * 320 * 4))
-    assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0) == -(-(4 * nc * 32 * 192 * 4) // 256) * 256 + 64 * 192 * 4
-    assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 1) == -(-(4 * nc * 32 * 128 * 4) // 256) * 256 + 64 * 128 * 4
+    assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0) == (r256(4 * nc * 32 * 192 * 4) + 64 * 192 * 4 +
+                                                              8 * 32 * 192 * 192 * 4)
+    assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 1) == (r256(4 * nc * 32 * 128 * 4) + 64 * 128 * 4 +
+                                                              8 * 32 * 128 * 128 * 4)
     lib = A.load_library()
     f = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     need = N.nsa_prefill_bwd_workspace_size(dims, cfg, T)
