@@ -268,3 +268,14 @@ def test_backward_full_size_samples_and_invariants():
     for x, raw, pe in (("dk", "dk_raw", "dpek"), ("dv", "dv_raw", "dpev")):
         added = (got[x].astype(np.float64) - got[raw]).sum(axis=(0, 1, 2))
         close(added, got[pe].astype(np.float64).sum(axis=0), f"fold vs dPE ({x})")
+
+
+def test_prefill_bwd_repeatable():
+    """Partial sums are combined in a fixed order (no floating-point atomics): two
+    backward calls on the same inputs give identical bits."""
+    case = I.generate(I.workload("prefill_32k", seq_len=1200), 7)
+    dout = I.output_gradient(case, 7)
+    a = run_backward(case, dout)
+    b = run_backward(case, dout)
+    for n in ("dq", "dk", "dv", "dkc", "dvc", "dgates", "dwk", "dpek", "dwv", "dpev"):
+        assert np.array_equal(a[n].view(np.uint32), b[n].view(np.uint32)), n
