@@ -279,3 +279,10 @@ def test_prefill_bwd_repeatable():
     b = run_backward(case, dout)
     for n in ("dq", "dk", "dv", "dkc", "dvc", "dgates", "dwk", "dpek", "dwv", "dpev"):
         assert np.array_equal(a[n].view(np.uint32), b[n].view(np.uint32)), n
+
+
+def test_backward_batch_two():
+    """Two sequences in one call: every kernel's (sequence, group) indexing."""
+    case = I.generate(I.workload("prefill_32k", batch=2, seq_len=333), 8)
+    dout = I.output_gradient(case, 8)
+    check_all(case, dout, run_backward(case, dout))
