@@ -388,8 +388,9 @@ def backward_setup(torch, N, I):
 
     dims = N.make_dims(B, Hq, H, dk, dv)
     cfg = N.make_config(p.l, p.d, p.l_sel, p.n_sel, p.n_local, p.force_initial, p.w)
+    dout_bits = I.output_gradient(case, seed)
     X = dict(q=dev(case.q), k=dev(case.k), v=dev(case.v), wk=dev(case.w_k), pk=dev(case.pe_k), wv=dev(case.w_v),
-             pv=dev(case.pe_v), gates=torch.from_numpy(case.gates).cuda(), dout=dev(I.output_gradient(case, seed)))
+             pv=dev(case.pe_v), gates=torch.from_numpy(case.gates).cuda(), dout=dev(dout_bits))
     X["kc"] = torch.empty((B, H, nc, dk), dtype=torch.bfloat16, device="cuda")
     X["vc"] = torch.empty((B, H, nc, dv), dtype=torch.bfloat16, device="cuda")
     N.nsa_compress_kv(dims, cfg, X["k"], X["v"], None, None, T, X["wk"], X["pk"], X["wv"], X["pv"], X["kc"], X["vc"],
@@ -415,12 +416,32 @@ def backward_setup(torch, N, I):
         N.nsa_compress_bwd(dims, cfg, T, 0, X["k"], X["wk"], X["pk"], X["dkc"], X["dk"], X["dwk"], X["dpk"], X["wsc"])
         N.nsa_compress_bwd(dims, cfg, T, 1, X["v"], X["wv"], X["pv"], X["dvc"], X["dv"], X["dwv"], X["dpv"], X["wsc"])
 
-    return wl, attn, comp
+    return wl, attn, comp, case, dout_bits
+
+
+def backward_cpu_baseline(case, dout_bits, torch):
+    """The float64 backward oracle (autograd through every branch and the
+    compression) on a bounded sample: the last position of KV group 0, its
+    selection taken by the oracle itself."""
+    from oracle import nsa_backward as NB
+    wl = case.wl
+    G = wl.num_q_heads // wl.num_kv_heads
+    w = lambda bits: (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    t = wl.seq_len - 1
+    t0 = time.perf_counter()
+    NB.sequence_backward(w(case.q[0, :, :G]), w(case.k[0, 0]), w(case.v[0, 0]), w(case.w_k), w(case.pe_k),
+                         w(case.w_v), w(case.pe_v), np.asarray(case.gates[0, :, :G], dtype=np.float64),
+                         w(dout_bits[0, :, :G]), [t], case.p)
+    el = time.perf_counter() - t0
+    # one position of one group: a position of all wl.num_kv_heads groups costs that many times more
+    return dict(value=1.0 / (el * wl.num_kv_heads), unit="positions/s", cores=int(torch.get_num_threads()),
+                kind="oracle", sample=f"position {t} of {wl.name}, KV group 0 of {wl.num_kv_heads} (dq, dk, dv, "
+                                      f"compression and gate gradients, oracle selection); {el:.1f} s of CPU work")
 
 
 def bench_backward(args, torch, N, I):
     t0 = time.time()
-    wl, attn, comp = backward_setup(torch, N, I)
+    wl, attn, comp, case, dout_bits = backward_setup(torch, N, I)
     log(f"[bench] backward inputs of {wl.name} ready in {time.time() - t0:.1f}s")
     attn()
     comp()
@@ -457,6 +478,10 @@ def bench_backward(args, torch, N, I):
     log(f"[bench] backward {wl.name}: {ms:.2f} ms ({res['tflops']:.1f} TFLOP/s); attention {attn_ms:.2f} ms "
         f"({res['attention_tflops']:.0f} TFLOP/s, {100 * res['mfma_frac']:.1f}% of bf16 peak): query side "
         f"{ph[0]:.2f} ms, raw keys {ph[1]:.2f} ms, compressed keys {ph[2]:.2f} ms; compression {comp_ms:.2f} ms")
+    res["positions_per_s"] = wl.batch * wl.seq_len / (ms * 1e-3)
+    if not args.no_cpu:
+        res["cpu"] = backward_cpu_baseline(case, dout_bits, torch)
+        log(f"[bench] backward cpu oracle: {res['cpu']['value']:.3g} positions/s on {res['cpu']['cores']} threads")
     return res
 
 
@@ -698,7 +723,7 @@ def kernels_only(args, torch, N, I):
         log(f"[bench] {args.kernels_only} DSA decode steps of {wl.name} done")
         return
     if args.backward:
-        _, attn, comp = backward_setup(torch, N, I)
+        _, attn, comp, _, _ = backward_setup(torch, N, I)
         for i in range(args.kernels_only):
             attn()
             comp()
@@ -895,7 +920,8 @@ def main():
             "attention": {"ms": bwd["attention_ms"], "TFLOP/s": bwd["attention_tflops"],
                           "mfma_frac": bwd["mfma_frac"], "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
                           "kernel_ms": bwd["kernel_ms"]},
-            "compression_ms": bwd["compress_ms"]}
+            "compression_ms": bwd["compress_ms"], "positions_per_s": bwd["positions_per_s"],
+            "cpu_oracle": bwd.get("cpu")}
     print(json.dumps(line), flush=True)
 
 
