@@ -195,6 +195,12 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg,
  *          here, and the gates of position t come from q[b, t, h, :])
  *   out    bf16 [B, T, Hq, d_v]
  *   sel_idx_out  nullable int32 [B, T, Hkv, n_sel], ascending, -1 padded.
+ *   lse_out  nullable float32 [B, T, Hq, 3]: each branch's log-sum-exp of its
+ *          scaled logits, natural log, c = cmp, slc, win (what a training step
+ *          keeps from the forward); -inf for a branch with no key (the
+ *          compressed branch before the first complete block).  The window and
+ *          selected sums are those of the bf16 probabilities the value products
+ *          use, the compressed sum is fp32.
  */
 nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
                              const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -202,7 +208,7 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
                              const uint16_t* w_k, const uint16_t* pe_k,
                              const uint16_t* w_v, const uint16_t* pe_v,
                              const float* gates, const uint16_t* w_gate, const float* b_gate,
-                             uint16_t* out, int32_t* sel_idx_out,
+                             uint16_t* out, int32_t* sel_idx_out, float* lse_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -69,7 +69,7 @@ _SIGS = {
     "nsa_decode_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP,
                        _VP, ctypes.c_size_t, _VP],
     "nsa_prefill_fwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                        _VP, _VP, _VP, ctypes.c_size_t, _VP],
+                        _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_bwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -214,8 +214,9 @@ def nsa_decode_fwd(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq
 
 
 def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, pe_v, gates, out, sel_idx_out,
-                    workspace, stream=None, w_gate=None, b_gate=None):
-    """gates=None with w_gate (and optionally b_gate) selects the in-kernel gate network."""
+                    workspace, stream=None, w_gate=None, b_gate=None, lse_out=None):
+    """gates=None with w_gate (and optionally b_gate) selects the in-kernel gate network;
+    lse_out (float32 [B, T, Hq, 3]) receives each branch's log-sum-exp."""
     lib = load_library()
     B, Hq, H, T = dims.batch, dims.num_q_heads, dims.num_kv_heads, int(seq_len)
     _check(lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), T, _ptr(q, "q", 2, B * T * Hq * dims.d_k),
@@ -225,7 +226,7 @@ def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, p
                                _ptr(gates, "gates", 4, B * T * Hq * 3), _ptr(w_gate, "w_gate", 2, Hq * 3 * dims.d_k),
                                _ptr(b_gate, "b_gate", 4, Hq * 3), _ptr(out, "out", 2, B * T * Hq * dims.d_v),
                                _ptr(sel_idx_out, "sel_idx_out", 4, B * T * H * cfg.n_sel),
-                               _ptr(workspace, "workspace"),
+                               _ptr(lse_out, "lse_out", 4, B * T * Hq * 3), _ptr(workspace, "workspace"),
                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                _stream(stream)))
 

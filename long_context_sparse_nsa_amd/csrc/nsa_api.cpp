@@ -487,7 +487,8 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
                              const uint16_t* k, const uint16_t* v, const uint16_t* k_cmp, const uint16_t* v_cmp,
                              const uint16_t* w_k, const uint16_t* pe_k, const uint16_t* w_v, const uint16_t* pe_v,
                              const float* gates, const uint16_t* w_gate, const float* b_gate, uint16_t* out,
-                             int32_t* sel_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t* sel_idx_out, float* lse_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   nsa_status_t st = check_common(dims, cfg, true);
   if (st != NSA_SUCCESS) return st;
   if (!q || !k || !v || !out) return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
@@ -546,6 +547,7 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.out = out;
   p.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t*>(ws + lay.off_sel);
   p.acc = reinterpret_cast<float*>(ws + lay.off_acc);
+  p.lse = lse_out;
   hipError_t e = nsa::launch_prefill(p, dims->d_k, dims->d_v, s, ev);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

@@ -86,6 +86,7 @@ struct PrefillParams {
   uint16_t* out;                     // [B, T, Hq, DV]
   int32_t* sel;                      // [B, T, H, n] selected block ids (caller's or workspace)
   float* acc;                        // [B, T, Hq, DV] workspace: g_win o_win + g_cmp o_cmp
+  float* lse;                        // [B, T, Hq, 3] per-branch log-sum-exp (natural log), or null
 };
 
 struct CompressParams {

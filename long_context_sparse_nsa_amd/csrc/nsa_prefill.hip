@@ -43,6 +43,7 @@ constexpr int kWaveQ = kTileQ / kWaves;  // positions per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1e30f;        // running-reference start: finite, so exp2 never sees inf - inf
 constexpr float kLazy = 8.0f;            // the softmax reference moves only when exceeded by this (log2 units)
+constexpr float kLn2 = 0.6931471805599453f;  // log-sum-exp outputs: log2 units to natural log
 
 template <int DK, int DV>
 struct PfShape {
@@ -348,6 +349,9 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     const float f = lt > 0.f ? gate(q, 2) / lt : 0.f;
 #pragma unroll
     for (int j = 0; j < VC; ++j) acc[q][j] *= f;
+    if (p.lse && act[q] && lg == 0 && lr < p.G)  // window log-sum-exp (natural log)
+      p.lse[(((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * 3 + 2] =
+          lt > 0.f ? (mref[q] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
   }
 
   // ---- C1: exact per-head max and sum over the visible compressed keys
@@ -388,6 +392,9 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     const float L = sum_over_groups_swap(lc[q]);
     bias[q] = (L > 0.f && lr < p.G) ? mref[q] + __builtin_log2f(L) : INFINITY;
     gC[q] = gate(q, 0);
+    if (p.lse && act[q] && lg == 0 && lr < p.G)  // compressed-branch log-sum-exp (natural log)
+      p.lse[(((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * 3] =
+          L > 0.f ? (mref[q] + __builtin_log2f(L)) * kLn2 : -INFINITY;
   }
 
   // ---- C2: normalised p; acc += g_cmp p.Vc; fold p onto selection blocks.
@@ -693,6 +700,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     if (!act[q] || lr >= p.G) continue;
     const int64_t hrow = ((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr;
     const float f = lt > 0.f ? (p.wgate ? gsl[q] : p.gates[hrow * 3 + 1]) / lt : 0.f;
+    if (p.lse && lg == 0)  // selected-branch log-sum-exp (natural log)
+      p.lse[hrow * 3 + 1] = lt > 0.f ? (mref[q] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
     const float* src = p.acc + hrow * DV;
     uint16_t* dst = p.out + hrow * DV;
 #pragma unroll

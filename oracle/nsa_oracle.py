@@ -119,6 +119,17 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
     return p @ np.asarray(V, dtype=np.float64), p
 
 
+def log_sum_exp(q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """Natural log of sum_k exp(scale * q . k) for each query row q [H, dk] over
+    keys K [n, dk] -- the normaliser of the softmax in `attend`; -inf when n == 0."""
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    if K.shape[0] == 0:
+        return np.full(q.shape[0], -np.inf)
+    z = scale * (q @ np.asarray(K, dtype=np.float64).T)
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
 # --------------------------------------------------------------------------- a2 fold + top-n
 
 def fold_weights(n_keys: int, l: int, d: int, l_sel: int, n_blocks: int) -> np.ndarray:
@@ -193,6 +204,7 @@ class QueryResult:
     o_win: np.ndarray
     idx: list                # selected blocks, ascending
     scores: np.ndarray       # group scores S[0..J]
+    lse: np.ndarray = None   # [G, 3] each branch's log-sum-exp (cmp, slc, win), natural log
 
 
 def nsa_query(qg: np.ndarray, K: np.ndarray, V: np.ndarray, Kc: np.ndarray, Vc: np.ndarray,
@@ -223,7 +235,8 @@ def nsa_query(qg: np.ndarray, K: np.ndarray, V: np.ndarray, Kc: np.ndarray, Vc: 
     o_win, _ = attend(qg, K[wt], V[wt], s)
     g = np.asarray(gates, dtype=np.float64)
     out = g[:, 0:1] * o_cmp + g[:, 1:2] * o_slc + g[:, 2:3] * o_win
-    return QueryResult(out, o_cmp, o_slc, o_win, idx, S)
+    lse = np.stack([log_sum_exp(qg, Kc[:nvis], s), log_sum_exp(qg, K[toks], s), log_sum_exp(qg, K[wt], s)], axis=1)
+    return QueryResult(out, o_cmp, o_slc, o_win, idx, S, lse)
 
 
 # --------------------------------------------------------------------------- batch drivers

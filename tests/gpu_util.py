@@ -115,21 +115,25 @@ def gate_args(case, gates=None):
     return g, None, None
 
 
-def run_prefill(case, gates=None, kc_bits=None, vc_bits=None):
+def run_prefill(case, gates=None, kc_bits=None, vc_bits=None, with_lse=False):
     wl = case.wl
     dims, cfg = dims_cfg(case)
     T = wl.seq_len
     g, wg, bgt = gate_args(case, gates)
     out = torch.empty((wl.batch, T, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
     sel = torch.full((wl.batch, T, wl.num_kv_heads, cfg.n_sel), -7, dtype=torch.int32, device="cuda")
+    lse = (torch.full((wl.batch, T, wl.num_q_heads, 3), float("nan"), dtype=torch.float32, device="cuda")
+           if with_lse else None)
     compress = kc_bits is None
     ws = N.new_workspace(N.nsa_prefill_workspace_size(dims, cfg, T, compress))
     kc = None if compress else dev_bits(kc_bits)
     vc = None if compress else dev_bits(vc_bits)
     N.nsa_prefill_fwd(dims, cfg, T, dev_bits(case.q), dev_bits(case.k), dev_bits(case.v), kc, vc,
                       dev_bits(case.w_k), dev_bits(case.pe_k), dev_bits(case.w_v), dev_bits(case.pe_v),
-                      g, out, sel, ws, w_gate=wg, b_gate=bgt)
+                      g, out, sel, ws, w_gate=wg, b_gate=bgt, lse_out=lse)
     torch.cuda.synchronize()
+    if with_lse:
+        return bits_to_f64(host_bits(out)), sel.cpu().numpy(), lse.cpu().numpy()
     return bits_to_f64(host_bits(out)), sel.cpu().numpy()
 
 

@@ -124,13 +124,13 @@ def test_prefill_rejects_half_given_cache_and_missing_weights():
     dims, cfg = _dims(batch=1), _cfg()
     f = ctypes.c_void_p(0x1000)
     st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, f, None, f, f, f, f, f, None, None,
-                             f, None, f, 1 << 30, None)
+                             f, None, None, f, 1 << 30, None)
     assert st == A.NSA_ERROR_INVALID_VALUE
     st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 4096, f, f, f, None, None, None, f, f, f, f, None,
-                             None, f, None, f, 1 << 30, None)
+                             None, f, None, None, f, 1 << 30, None)
     assert st == A.NSA_ERROR_INVALID_VALUE
     st = lib.nsa_prefill_fwd(ctypes.byref(dims), ctypes.byref(cfg), 70000, f, f, f, f, f, None, None, None, None, f,
-                             None, None, f, None, None, 0, None)
+                             None, None, f, None, None, None, 0, None)
     assert st == A.NSA_ERROR_UNSUPPORTED
 
 

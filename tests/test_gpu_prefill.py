@@ -62,3 +62,34 @@ def test_prefill_fine_selection_l32():
     case = I.generate(I.workload("prefill_32k", seq_len=1100, params={"l_sel": 32, "n_sel": 32}), 4)
     out, sel = U.run_prefill(case)
     _check_rows(case, out, sel, range(0, 1100, 3))
+
+
+# Each branch's log-sum-exp (lse_out): the window and selected sums are those of
+# the bf16 probabilities (relative error <= 2^-9 per term, so |d lse| <= 2^-9),
+# the compressed one is fp32; the logits are exact products of bf16 values summed
+# in fp32.  Bound: 4e-3 absolute; -inf exactly where the oracle has no key.
+LSE_ABS = 4e-3
+
+
+@pytest.mark.parametrize("wl_name,T,seed", [("tiny_prefill_512", 512, 5), ("prefill_32k", 1100, 6)])
+def test_prefill_lse_out(wl_name, T, seed):
+    case = I.generate(I.workload(wl_name, seq_len=T), seed)
+    wl, p = case.wl, case.p
+    G = wl.num_q_heads // wl.num_kv_heads
+    _, sel, lse = U.run_prefill(case, with_lse=True)
+    worst = 0.0
+    for g in range(wl.num_kv_heads):
+        K, V, Kc, Vc = O.compress_group(case, 0, g)
+        res = O.prefill_rows(case, 0, g, range(T), K, V, Kc, Vc)
+        for t, r in zip(range(T), res):
+            r = U.check_selection(r, sel[0, t, g], t, p,
+                                  lambda idx, t=t: O.prefill_rows(case, 0, g, [t], K, V, Kc, Vc, [idx])[0])
+            got = lse[0, t, g * G:(g + 1) * G]
+            want = r.lse
+            assert np.array_equal(np.isneginf(got), np.isneginf(want)), (g, t)
+            fin = np.isfinite(want)
+            assert np.all(np.isfinite(got[fin])), (g, t)
+            if fin.any():
+                worst = max(worst, float(np.abs(got[fin] - want[fin]).max()))
+    print(f"lse max-abs error {worst:.2e}")
+    assert worst <= LSE_ABS

@@ -437,3 +437,50 @@ def test_round_to_bf16_matches_torch():
     np.testing.assert_array_equal(O.round_to_bf16(x), want)
     assert O.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0          # tie to even
     assert O.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_log_sum_exp_closed_forms_and_normaliser():
+    """The branch log-sum-exp: closed forms (n equal logits z give z + log n; one
+    key gives its logit; no key gives -inf; huge logits do not overflow), and it is
+    the normaliser of attend's softmax: exp(s q.k - lse) reproduces attend's
+    probabilities and output."""
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((3, 8))
+    K = np.tile(rng.standard_normal((1, 8)), (5, 1))
+    z = 0.25 * (q @ K[0])
+    np.testing.assert_allclose(O.log_sum_exp(q, K, 0.25), z + np.log(5.0), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.log_sum_exp(q, K[:1], 0.25), z, rtol=0, atol=1e-12)
+    assert np.all(O.log_sum_exp(q, K[:0], 0.25) == -np.inf)
+    big = O.log_sum_exp(np.full((1, 1), 1000.0), np.array([[1.0], [1.0]]), 1.0)
+    np.testing.assert_allclose(big, 1000.0 + np.log(2.0), rtol=1e-15)
+    K = rng.standard_normal((7, 8))
+    V = rng.standard_normal((7, 4))
+    out, p = O.attend(q, K, V, 0.3)
+    lse = O.log_sum_exp(q, K, 0.3)
+    p2 = np.exp(0.3 * (q @ K.T) - lse[:, None])
+    np.testing.assert_allclose(p2, p, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(p2 @ V, out, rtol=1e-12, atol=1e-12)
+
+
+def test_query_lse_covers_each_branch_key_set():
+    """nsa_query's per-branch lse: with every block selected and a window as long as
+    the prefix, the selected and window lse are the causal prefix's; the compressed
+    lse is over exactly the visible blocks (-inf before the first one)."""
+    rng = np.random.default_rng(12)
+    T, G, dk = 40, 2, 8
+    K = rng.standard_normal((T, dk))
+    V = rng.standard_normal((T, 3))
+    Kc = rng.standard_normal((O.n_compressed(T, 8, 4), dk))
+    Vc = rng.standard_normal((Kc.shape[0], 3))
+    for t in (3, 17, 39):
+        qg = rng.standard_normal((G, dk))
+        r = O.nsa_query(qg, K, V, Kc, Vc, t, np.ones((G, 3)), 8, 4, 8, 64, 0, 0, 64)
+        s = 1 / np.sqrt(dk)
+        want = O.log_sum_exp(qg, K[:t + 1], s)
+        np.testing.assert_allclose(r.lse[:, 1], want, rtol=1e-12)
+        np.testing.assert_allclose(r.lse[:, 2], want, rtol=1e-12)
+        nvis = O.n_compressed(t + 1, 8, 4)
+        if nvis == 0:
+            assert np.all(r.lse[:, 0] == -np.inf)
+        else:
+            np.testing.assert_allclose(r.lse[:, 0], O.log_sum_exp(qg, Kc[:nvis], s), rtol=1e-12)
