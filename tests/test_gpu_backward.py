@@ -149,9 +149,14 @@ def check_all(case, dout_bits, got):
                 sums[n] = sums[n] + r[n]
             terms["k"] = terms["k"] + np.abs(r["dKc"]).sum(axis=0)
             terms["v"] = terms["v"] + np.abs(r["dVc"]).sum(axis=0)
+    # A gradient that is exactly 0 (e.g. dq, dk when every branch sees one key, so
+    # each dS = P (dP - D) cancels) is measured against the size of the terms that
+    # cancel, bounded below by 1e-6 x the dgates scale (dout . o).
+    floor = 1e-6 * float(np.abs(np.stack(want["dgates"])).max()) / MAX_REL
     for n in acc:
         if acc[n]:
-            close(np.stack(acc[n]), np.stack(want[n]), n)
+            w = np.stack(want[n])
+            close(np.stack(acc[n]), w, n, scale=max(float(np.abs(w).max()), floor))
     close(got["dwk"], sums["dWk"], "dWk")
     # dPE = (sum_i dY_i) W^T.  For keys sum_i dKc_i is 0 up to rounding (every
     # softmax's dS sums to 0 over its keys), so dPE_k is near 0 and its error is
@@ -285,4 +290,19 @@ def test_backward_batch_two():
     """Two sequences in one call: every kernel's (sequence, group) indexing."""
     case = I.generate(I.workload("prefill_32k", batch=2, seq_len=333), 8)
     dout = I.output_gradient(case, 8)
+    check_all(case, dout, run_backward(case, dout))
+
+
+@pytest.mark.parametrize("over", [
+    dict(num_q_heads=8, num_kv_heads=4, seq_len=260),                                  # G = 2
+    dict(seq_len=300, params=dict(l=16, d=8, l_sel=16, n_sel=8, n_local=1)),            # l' = 16
+    dict(seq_len=420, params=dict(l_sel=128, n_sel=3, n_local=1)),                     # l' = 128
+    dict(seq_len=1),
+    dict(seq_len=2),
+])
+def test_backward_shapes(over):
+    """Group sizes that are not a multiple of 4, the smallest and largest selection
+    blocks, and sequences of one and two tokens."""
+    case = I.generate(I.workload("tiny_prefill_512", **over), 9)
+    dout = I.output_gradient(case, 9)
     check_all(case, dout, run_backward(case, dout))
