@@ -69,15 +69,20 @@ def query_out_t(q, K, V, Kc, Vc, t: int, gates, p, idx: Sequence[int], scale: fl
 def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarray, PEk: np.ndarray,
                       Wv: np.ndarray, PEv: np.ndarray, gates: np.ndarray, dout: np.ndarray, rows: Sequence[int],
                       p, sel: Optional[Sequence[Sequence[int]]] = None, scale: Optional[float] = None,
-                      round_cmp: bool = True) -> dict:
+                      round_cmp: bool = True, Wg: Optional[np.ndarray] = None,
+                      bg: Optional[np.ndarray] = None) -> dict:
     """Gradients of  sum_{t in rows} sum_h dout[t,h] . out[t,h]  for one sequence and KV group.
 
     Q [T, G, dk] (the group's query heads per position), K [T, dk], V [T, dv], Wk [l*dk, dk],
     PEk [l, dk], Wv [l*dv, dv], PEv [l, dv], gates [T, G, 3], dout [T, G, dv].
     ``sel`` gives the selected block ids per row; by default the forward oracle's top-n.
     ``round_cmp`` uses the bf16-rounded compressed cache values (as the forward does).
-    Returns float64 numpy arrays: dQ, dK, dV, dWk, dPEk, dWv, dPEv, dgates (shapes of the inputs), and
-    dKc, dVc: the gradients reaching the compressed cache [nc, dk] / [nc, dv].
+    With ``Wg`` [G, 3, dk] (and optionally ``bg`` [G, 3]) the gates come from the gate
+    network, gate[t, h, c] = sigmoid(Wg[h, c] . Q[t, h] + bg[h, c]) (``gates`` is then
+    ignored), and dWg, dbg are returned too; dQ then includes the gates' path.
+    Returns float64 numpy arrays: dQ, dK, dV, dWk, dPEk, dWv, dPEv, dgates (shapes of the inputs; dgates
+    is the gradient reaching the gate values), and dKc, dVc: the gradients reaching the compressed
+    cache [nc, dk] / [nc, dv]; with the gate network also dWg and dbg.
     """
     dk_ = Q.shape[2]
     s = 1.0 / np.sqrt(dk_) if scale is None else scale
@@ -89,6 +94,17 @@ def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarra
     Wvt = torch.tensor(Wv, dtype=F64, requires_grad=True)
     PEvt = torch.tensor(PEv, dtype=F64, requires_grad=True)
     Gt = torch.tensor(gates, dtype=F64, requires_grad=True)
+    Wgt = bgt = None
+    if Wg is not None:
+        Wgt = torch.tensor(Wg, dtype=F64, requires_grad=True)
+        z = torch.einsum("hck,thk->thc", Wgt, Qt)
+        if bg is not None:
+            bgt = torch.tensor(bg, dtype=F64, requires_grad=True)
+            z = z + bgt
+        gate_vals = torch.sigmoid(z)
+        gate_vals.retain_grad()  # dgates: the gradient reaching the gate values, dout . o per branch
+    else:
+        gate_vals = Gt
     Kc = compress_t(Kt, Wkt, PEkt, p.l, p.d, round_cmp)
     Vc = compress_t(Vt, Wvt, PEvt, p.l, p.d, round_cmp)
     for c in (Kc, Vc):
@@ -101,9 +117,14 @@ def sequence_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, Wk: np.ndarra
                            p.force_initial, p.w, scale=s).idx for t in rows]
     loss = torch.zeros((), dtype=F64)
     for r, t in enumerate(rows):
-        out = query_out_t(Qt[t], Kt, Vt, Kc, Vc, int(t), Gt[t], p, sel[r], s)
+        out = query_out_t(Qt[t], Kt, Vt, Kc, Vc, int(t), gate_vals[t], p, sel[r], s)
         loss = loss + (out * torch.tensor(dout[t], dtype=F64)).sum()
     loss.backward()
     g = lambda x: (x.grad if x.grad is not None else torch.zeros_like(x)).detach().numpy()
-    return dict(dQ=g(Qt), dK=g(Kt), dV=g(Vt), dWk=g(Wkt), dPEk=g(PEkt), dWv=g(Wvt), dPEv=g(PEvt), dgates=g(Gt),
-                dKc=g(Kc), dVc=g(Vc), sel=sel)
+    res = dict(dQ=g(Qt), dK=g(Kt), dV=g(Vt), dWk=g(Wkt), dPEk=g(PEkt), dWv=g(Wvt), dPEv=g(PEvt), dgates=g(Gt),
+               dKc=g(Kc), dVc=g(Vc), sel=sel)
+    if Wgt is not None:
+        res["dgates"] = g(gate_vals)
+        res["dWg"] = g(Wgt)
+        res["dbg"] = g(bgt) if bgt is not None else None
+    return res

@@ -116,3 +116,37 @@ def test_top_n_is_a_no_op_on_the_graph():
     g = NB.sequence_backward(**c, rows=[12], p=p)               # blocks 0..4 cover tokens 0..11
     assert np.all(g["dK"][12:] == 0.0) and np.all(g["dV"][12:] == 0.0)
     assert np.any(g["dK"][:12] != 0.0) and np.any(g["dWk"] != 0.0)
+
+
+def test_gate_network_gradients_match_finite_differences():
+    """With the gate network, autograd's derivatives with respect to the queries
+    (both paths), the gate weights and the bias against central differences."""
+    c = _case(4)
+    p = P()
+    rows = [2, 6, 11]
+    rng = np.random.default_rng(5)
+    Wg = rng.standard_normal((2, 3, 4)) * 0.5
+    bg = rng.standard_normal((2, 3)) * 0.5
+    sel = NB.sequence_backward(**c, rows=rows, p=p)["sel"]
+    tens = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (c["Q"], Wg, bg)]
+    K, V = (torch.tensor(c[n], dtype=torch.float64) for n in ("K", "V"))
+    Kc = NB.compress_t(K, torch.tensor(c["Wk"]), torch.tensor(c["PEk"]), p.l, p.d)
+    Vc = NB.compress_t(V, torch.tensor(c["Wv"]), torch.tensor(c["PEv"]), p.l, p.d)
+    dout = torch.tensor(c["dout"], dtype=torch.float64)
+
+    def f(Q, W, b):
+        tot = torch.zeros((), dtype=torch.float64)
+        for r, t in enumerate(rows):
+            gts = torch.sigmoid(torch.einsum("hck,hk->hc", W, Q[t]) + b)
+            tot = tot + (NB.query_out_t(Q[t], K, V, Kc, Vc, t, gts, p, sel[r], 0.5) * dout[t]).sum()
+        return tot
+
+    assert torch.autograd.gradcheck(f, tens, eps=1e-6, atol=1e-7, rtol=1e-5)
+    # and sequence_backward with the gate network returns those same derivatives
+    r = NB.sequence_backward(**c, rows=rows, p=p, sel=sel, scale=0.5, round_cmp=False, Wg=Wg, bg=bg)
+    for x in tens:
+        x.grad = None
+    f(*tens).backward()
+    np.testing.assert_allclose(r["dQ"], tens[0].grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dWg"], tens[1].grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["dbg"], tens[2].grad.numpy(), rtol=1e-12, atol=1e-12)
