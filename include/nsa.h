@@ -295,8 +295,11 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
  *
  *   q, k, v, k_cmp, v_cmp  as for nsa_prefill_fwd; the compressed cache is the
  *          one the forward used (required when seq_len >= l).
- *   gates  float32 [B, T, Hq, 3] the forward's gate values (with the gate
- *          network, its sigmoid outputs; its own chain rule is the caller's).
+ *   gates  float32 [B, T, Hq, 3] the forward's gate values, or NULL with
+ *   w_gate, b_gate  the forward's gate network (as for nsa_prefill_fwd): the
+ *          gates are recomputed, dq gains the gates' path sum_c dz_c w_gate[h, c]
+ *          with dz_c = dgates_c g_c (1 - g_c), and dw_gate = sum_t dz q,
+ *          db_gate = sum_t dz are written.  Exactly one gate source.
  *   sel_idx  int32 [B, T, Hkv, n_sel]: the forward's sel_idx_out (ascending,
  *          -1 padded; any other content gives undefined gradients).
  *   dout   bf16 [B, T, Hq, d_v] gradient of the output.
@@ -304,7 +307,9 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
  *   dk, dv float32 [B, Hkv, T, d_k / d_v]       (written)
  *   dk_cmp, dv_cmp  float32 [B, Hkv, nc, d_k / d_v], nc = floor((T-l)/d)+1
  *          (written; may be NULL when T < l)
- *   dgates float32 [B, T, Hq, 3]               (written)
+ *   dgates float32 [B, T, Hq, 3]               (written; the gradient of the gate values)
+ *   dw_gate, db_gate  float32 [Hq, 3, d_k] and [Hq, 3] (written; required with
+ *          w_gate, db_gate with b_gate; ignored otherwise)
  * Supported: the shapes of nsa_prefill_fwd with seq_len * Hq * max(d_k, d_v) * 2
  * below 2^32 (one sequence's query rows addressable with 32-bit offsets).
  * Products are bf16 MFMA with fp32 sums (probabilities and dS rounded to bf16
@@ -314,9 +319,11 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
 nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len,
                              const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* k_cmp, const uint16_t* v_cmp,
-                             const float* gates, const int32_t* sel_idx, const uint16_t* dout,
+                             const float* gates, const uint16_t* w_gate, const float* b_gate,
+                             const int32_t* sel_idx, const uint16_t* dout,
                              float* dq, float* dk, float* dv, float* dk_cmp, float* dv_cmp,
-                             float* dgates, void* workspace, size_t workspace_bytes, void* stream);
+                             float* dgates, float* dw_gate, float* db_gate,
+                             void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes for nsa_prefill_bwd (host-only): per (branch, position, KV
  * group) a record of 48 fp32 (the heads' log-sum-exp, D and gate, padded to 16
  * heads), [3, B, T, Hkv, 48]; a selection bitmap [B, Hkv, ceil(T/l_sel),
@@ -324,8 +331,9 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
  * ranges: [P_s, B, Hkv, T, d_k + d_v] for the selected branch, P_s =
  * ceil(W / (128 * ceil(ceil(W / 8) / 128))) with W = ceil(T/32) (at most 8),
  * and [P_c, B, Hkv, nc, d_k + d_v] for the compressed branch, P_c =
- * ceil(T / q), q = max(1024, ceil(T/32)) rounded up to even (at most 32).
- * Each part is rounded up to 256 bytes.  Contents on entry do not matter. */
+ * ceil(T / q), q = max(1024, ceil(T/32)) rounded up to even (at most 32); and
+ * the gate network's gradient partials [64, Hq, 3, d_k + 1].  Each part is
+ * rounded up to 256 bytes.  Contents on entry do not matter. */
 nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                             int64_t seq_len, size_t* bytes);
 

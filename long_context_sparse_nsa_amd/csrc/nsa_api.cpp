@@ -582,9 +582,10 @@ BwdPlan bwd_plan(int64_t T) {
 // Prefill-backward workspace: per-branch statistics records [3, B, T, Hkv, 48]
 // fp32, the selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32, and
 // the key side's partial sums: selected [nqw, B, Hkv, T, d_k + d_v] and
-// compressed [ncq, B, Hkv, nc, d_k + d_v] fp32.
+// compressed [ncq, B, Hkv, nc, d_k + d_v] fp32, and the gate-network gradient
+// partials [64, Hq, 3, d_k + 1] fp32.
 struct BwdWs {
-  size_t off_stat, off_bits, off_pslc, off_pcmp, total;
+  size_t off_stat, off_bits, off_pslc, off_pcmp, off_gpart, total;
 };
 BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   BwdWs w{};
@@ -597,7 +598,8 @@ BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   w.off_bits = align256(recs * nsa::kStatFloats * 4);
   w.off_pslc = w.off_bits + align256(bh * nblk * nwords * 4);
   w.off_pcmp = w.off_pslc + align256((size_t)pl.nqw * bh * (size_t)T * wd * 4);
-  w.total = w.off_pcmp + align256((size_t)pl.ncq * bh * nc * wd * 4);
+  w.off_gpart = w.off_pcmp + align256((size_t)pl.ncq * bh * nc * wd * 4);
+  w.total = w.off_gpart + align256((size_t)nsa::kGateChunks * dims->num_q_heads * 3 * (dims->d_k + 1) * 4);
   return w;
 }
 
@@ -637,14 +639,18 @@ nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_co
 
 nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len, const uint16_t* q,
                              const uint16_t* k, const uint16_t* v, const uint16_t* k_cmp, const uint16_t* v_cmp,
-                             const float* gates, const int32_t* sel_idx, const uint16_t* dout, float* dq, float* dk,
-                             float* dv, float* dk_cmp, float* dv_cmp, float* dgates, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             const float* gates, const uint16_t* w_gate, const float* b_gate, const int32_t* sel_idx,
+                             const uint16_t* dout, float* dq, float* dk, float* dv, float* dk_cmp, float* dv_cmp,
+                             float* dgates, float* dw_gate, float* db_gate, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   nsa_status_t st = check_common(dims, cfg, true);
   if (st != NSA_SUCCESS) return st;
   if ((st = check_prefill_sizes(dims, cfg, seq_len)) != NSA_SUCCESS) return st;
-  if (!q || !k || !v || !gates || !sel_idx || !dout || !dq || !dk || !dv || !dgates)
+  if (!q || !k || !v || !sel_idx || !dout || !dq || !dk || !dv || !dgates)
     return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
+  if ((st = check_gates(gates, w_gate, b_gate)) != NSA_SUCCESS) return st;
+  if (w_gate && (!dw_gate || (b_gate && !db_gate)))
+    return fail(NSA_ERROR_INVALID_VALUE, "the gate network needs dw_gate (and db_gate with b_gate)");
   if (seq_len * dims->num_q_heads * (int64_t)std::max(dims->d_k, dims->d_v) * 2 >= ((int64_t)1 << 32))
     return fail(NSA_ERROR_UNSUPPORTED, "seq_len * num_q_heads * max(d_k, d_v) * 2 must stay below 2^32 bytes");
   const int64_t nc = n_compressed(seq_len, cfg->l, cfg->d);
@@ -684,6 +690,11 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.kc = nc > 0 ? k_cmp : k;  // never read without a compressed block
   p.vc = nc > 0 ? v_cmp : v;
   p.gates = gates;
+  p.wgate = w_gate;
+  p.bgate = b_gate;
+  p.dwgate = dw_gate;
+  p.dbgate = b_gate ? db_gate : nullptr;
+  p.gpart = reinterpret_cast<float*>(ws + lay.off_gpart);
   p.sel = sel_idx;
   p.dout = dout;
   p.dq = dq;

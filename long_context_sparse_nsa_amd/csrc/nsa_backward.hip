@@ -229,8 +229,30 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
   load_q_frags<DK>(p.q + qrow * DK, tv ? G : 0, lg, lr, qf);
   load_q_frags<DV>(p.dout + qrow * DV, tv ? G : 0, lg, lr, of);
   float gt[3];
+  if (p.wgate) {  // gate network: sigmoid(w_gate[h, c] . q_h + b_gate[h, c]), lane parts in the q-fragment layout
 #pragma unroll
-  for (int c = 0; c < 3; ++c) gt[c] = (tv && hv) ? p.gates[(qrow + lr) * 3 + c] : 0.f;
+    for (int c = 0; c < 3; ++c) {
+      float z = 0.f;
+      if (tv && hv) {
+        const uint16_t* wr = p.wgate + ((int64_t)(g * G + lr) * 3 + c) * DK + 8 * lg;
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+          const u32x4_t wv = ld16(wr + 32 * kk);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            z = fmaf(bf16_lo(wv[u]), bf16_lo(qf[kk][u]), z);
+            z = fmaf(bf16_hi(wv[u]), bf16_hi(qf[kk][u]), z);
+          }
+        }
+      }
+      z = sum_over_groups(z);
+      if (p.bgate && hv) z += p.bgate[(g * G + lr) * 3 + c];
+      gt[c] = (tv && hv) ? gate_sigmoid(z) : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) gt[c] = (tv && hv) ? p.gates[(qrow + lr) * 3 + c] : 0.f;
+  }
   const int nvis = tv ? n_visible(t, p.l, p.d, nc) : 0;
   const float sl2 = p.scale_log2;
   wait_vmem();
@@ -240,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
   f32x4_t acc[DV / 16];
 #pragma unroll
   for (int j = 0; j < DV / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float lse_c[3] = {0.f, 0.f, 0.f}, dc_c[3] = {0.f, 0.f, 0.f};
+  float lse_c[3] = {0.f, 0.f, 0.f}, dc_c[3] = {0.f, 0.f, 0.f}, dg_c[3] = {0.f, 0.f, 0.f};
   int fin = 0;
   auto finalize = [&](const int c) {
     float dot = 0.f;
@@ -261,9 +283,9 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
     dot = any ? dot / l : 0.f;  // dout . o_c
     const float gc = c == kCmp ? gt[0] : (c == kSlc ? gt[1] : gt[2]);
     const float ls = any ? m + __log2f(l) : 0.f, dcv = gc * dot;
-    if (c == kCmp) { lse_c[0] = ls; dc_c[0] = dcv; }
-    else if (c == kSlc) { lse_c[1] = ls; dc_c[1] = dcv; }
-    else { lse_c[2] = ls; dc_c[2] = dcv; }
+    if (c == kCmp) { lse_c[0] = ls; dc_c[0] = dcv; dg_c[0] = dot; }
+    else if (c == kSlc) { lse_c[1] = ls; dc_c[1] = dcv; dg_c[1] = dot; }
+    else { lse_c[2] = ls; dc_c[2] = dcv; dg_c[2] = dot; }
     if (tv && lg == 0) {  // statistics record of (c, b, t, g): lse[16] | D[16] | gate[16], zeros past G
       float* rec = p.stat + ((((int64_t)c * p.B + b) * T + t) * p.H + g) * kStatFloats;
       rec[lr] = hv ? ls : 0.f;
@@ -396,15 +418,74 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
 
   if (tv && hv) {
     float* dst = p.dq + (qrow + lr) * DK;
+    // gate network: dq_h += sum_c dz_c w_gate[h, c], dz_c = dgates_c g_c (1 - g_c)
+    float dz[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) dz[c] = dg_c[c] * gt[c] * (1.f - gt[c]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j4 = 0; j4 < DK / 64; ++j4) {
-        const int j = 4 * j4;
-        *reinterpret_cast<f32x4_t*>(dst + (DK / 16) * (4 * lg + i) + j) =
-            f32x4_t{dqa[j][i], dqa[j + 1][i], dqa[j + 2][i], dqa[j + 3][i]} * p.scale;
+        const int j = 4 * j4, ch = (DK / 16) * (4 * lg + i) + j;
+        f32x4_t v = f32x4_t{dqa[j][i], dqa[j + 1][i], dqa[j + 2][i], dqa[j + 3][i]} * p.scale;
+        if (p.wgate) {
+#pragma unroll
+          for (int c = 0; c < 3; ++c) {
+            const u32x2_t w = ld8(p.wgate + ((int64_t)(g * G + lr) * 3 + c) * DK + ch);
+            v += f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])} * dz[c];
+          }
+        }
+        *reinterpret_cast<f32x4_t*>(dst + ch) = v;
       }
   }
+}
+
+// Gate-network gradients, partial sums over position range blockIdx.y of the
+// B*T positions for query head blockIdx.x: thread ch < DK sums dz_c q[ch] for
+// c = 0..2 (dw_gate), thread DK sums dz_c (db_gate); dz_c = dgates_c g_c (1 - g_c)
+// with the gates kept in the statistics records.
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_gate_part_kernel(BwdParams p) {
+  static_assert(DK < 256, "one thread per channel plus one");
+  const int h = blockIdx.x, ck = blockIdx.y, ch = threadIdx.x;
+  const int g = h / p.G, hl = h - g * p.G;
+  const int64_t P = (int64_t)p.B * p.T, per = (P + kGateChunks - 1) / kGateChunks;
+  const int64_t r0 = ck * per, r1 = min(P, r0 + per);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+  for (int64_t pos = r0; pos < r1; ++pos) {
+    const int64_t b = pos / p.T, t = pos - b * p.T;
+    const float* dg = p.dgates + (pos * p.Hq + h) * 3;
+    float dz[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const float gc = p.stat[((((int64_t)c * p.B + b) * p.T + t) * p.H + g) * kStatFloats + 32 + hl];
+      dz[c] = dg[c] * gc * (1.f - gc);
+    }
+    const float x = ch < DK ? bf16_to_f32(p.q[(pos * p.Hq + h) * DK + ch]) : 1.f;
+    a0 = fmaf(dz[0], x, a0);
+    a1 = fmaf(dz[1], x, a1);
+    a2 = fmaf(dz[2], x, a2);
+  }
+  if (ch <= DK) {
+    float* dst = p.gpart + ((int64_t)ck * p.Hq + h) * 3 * (DK + 1);
+    dst[ch] = a0;
+    dst[(DK + 1) + ch] = a1;
+    dst[2 * (DK + 1) + ch] = a2;
+  }
+}
+
+// dw_gate, db_gate = sum of the partials in range order.
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_gate_sum_kernel(BwdParams p) {
+  const int64_t n = (int64_t)p.Hq * 3 * (DK + 1);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int ck = 0; ck < kGateChunks; ++ck) s += p.gpart[ck * n + i];
+  const int64_t hc = i / (DK + 1);
+  const int ch = (int)(i - hc * (DK + 1));
+  if (ch < DK) p.dwgate[hc * DK + ch] = s;
+  else if (p.dbgate) p.dbgate[hc] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -744,6 +825,11 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s, const PhaseEvents* ev
   hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((nsel + 255) / 256)), dim3(256), 0, s, p);
   if (ev) hipEventRecord(ev->ev[0], s);
   hipLaunchKernelGGL((bwd_query_kernel<DK, DV>), dim3((unsigned)(nbg * p.nqt)), dim3(256), 0, s, p);
+  if (p.wgate) {
+    hipLaunchKernelGGL((bwd_gate_part_kernel<DK>), dim3((unsigned)p.Hq, kGateChunks), dim3(256), 0, s, p);
+    const int64_t ng = (int64_t)p.Hq * 3 * (DK + 1);
+    hipLaunchKernelGGL((bwd_gate_sum_kernel<DK>), dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, s, p);
+  }
   if (ev) hipEventRecord(ev->ev[1], s);
   const int kraw = (p.T + 63) / 64, kcmp = (p.nc + 63) / 64;
   constexpr int W4 = (DK + DV) / 4;

@@ -7,7 +7,8 @@ namespace nsa {
 
 constexpr int kStatFloats = 48;      // statistics record of one (branch, position, group)
 constexpr int kBwdMaxParts = 8;      // key side: most partial sums per key (position ranges)
-constexpr int kCbwdSplit = 8;        // compression backward: contraction ranges of the dW product
+constexpr int kCbwdSplit = 8;
+constexpr int kGateChunks = 64;      // gate-network gradients: position ranges summed in order        // compression backward: contraction ranges of the dW product
 
 // Prefill backward (gradients of the three-branch output).
 struct BwdParams {
@@ -24,7 +25,12 @@ struct BwdParams {
   const uint16_t* v;                 // [B, H, T, DV]
   const uint16_t* kc;                // [B, H, nc, DK]
   const uint16_t* vc;                // [B, H, nc, DV]
-  const float* gates;                // [B, T, Hq, 3]
+  const float* gates;                // [B, T, Hq, 3], or null with the gate network
+  const uint16_t* wgate;             // gate network [Hq, 3, DK] (null: gates are given)
+  const float* bgate;                // [Hq, 3] or null
+  float* dwgate;                     // [Hq, 3, DK] (gate network only)
+  float* dbgate;                     // [Hq, 3] or null
+  float* gpart;                      // workspace [kGateChunks, Hq, 3, DK + 1]: gate-gradient partials
   const int32_t* sel;                // [B, T, H, n] the forward's selected block ids
   const uint16_t* dout;              // [B, T, Hq, DV]
   float* dq;                         // [B, T, Hq, DK]

@@ -208,11 +208,12 @@ def test_backward_workspace_sizes_and_validation():
     T = 32768
     # statistics records [3, 1, T, 4, 48] fp32, bitmap [1, 4, T/64, T/32] uint32, selected-branch
     # partials [8, 1, 4, T, 320] fp32 (1024 words in 8 ranges of 128), compressed-branch partials
-    # [32, 1, 4, nc, 320] fp32 (ranges of 1024 positions)
+    # [32, 1, 4, nc, 320] fp32 (ranges of 1024 positions), gate-gradient partials [64, 64, 3, 193] fp32
     nc = (T - 32) // 16 + 1
     r256 = lambda x: -(-x // 256) * 256
     assert N.nsa_prefill_bwd_workspace_size(dims, cfg, T) == (3 * T * 4 * 48 * 4 + 4 * 512 * 1024 * 4 +
-                                                             8 * 4 * T * 320 * 4 + r256(32 * 4 * nc * 320 * 4))
+                                                             8 * 4 * T * 320 * 4 + r256(32 * 4 * nc * 320 * 4) +
+                                                             r256(64 * 64 * 3 * 193 * 4))
     assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0) == (r256(4 * nc * 32 * 192 * 4) + 64 * 192 * 4 +
                                                               8 * 32 * 192 * 192 * 4)
     assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 1) == (r256(4 * nc * 32 * 128 * 4) + 64 * 128 * 4 +
@@ -221,9 +222,9 @@ def test_backward_workspace_sizes_and_validation():
     f = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     need = N.nsa_prefill_bwd_workspace_size(dims, cfg, T)
 
-    def bwd(q=f, kc=f, sel=f, ws=f, nb=need, T=T):
-        return lib.nsa_prefill_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, q, f, f, kc, f, f, sel, f, f, f, f, f, f,
-                                   f, ws, nb, None)
+    def bwd(q=f, kc=f, sel=f, ws=f, nb=need, T=T, gates=f, wg=None, bg=None, dwg=None):
+        return lib.nsa_prefill_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, q, f, f, kc, f, gates, wg, bg, sel, f,
+                                   f, f, f, f, f, f, dwg, None, ws, nb, None)
     assert bwd(q=None) == A.NSA_ERROR_INVALID_VALUE and "NULL" in N.nsa_last_error()
     assert bwd(sel=None) == A.NSA_ERROR_INVALID_VALUE
     assert bwd(kc=None) == A.NSA_ERROR_INVALID_VALUE and "compressed" in N.nsa_last_error()
@@ -231,6 +232,10 @@ def test_backward_workspace_sizes_and_validation():
     assert bwd(ws=None) == A.NSA_ERROR_WORKSPACE
     assert bwd(T=0) == A.NSA_ERROR_INVALID_VALUE
     assert bwd(T=70000) == A.NSA_ERROR_UNSUPPORTED  # more than 1024 selection blocks
+    assert bwd(gates=None) == A.NSA_ERROR_INVALID_VALUE  # no gate source
+    assert bwd(wg=f, dwg=f) == A.NSA_ERROR_INVALID_VALUE  # two gate sources
+    assert bwd(gates=None, wg=f) == A.NSA_ERROR_INVALID_VALUE and "dw_gate" in N.nsa_last_error()
+    assert bwd(gates=None, wg=f, bg=f, dwg=f) == A.NSA_ERROR_INVALID_VALUE  # b_gate without db_gate
     cneed = N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0)
 
     def cbwd(which=0, x=f, dy=f, ws=f, nb=cneed):

@@ -72,16 +72,18 @@ def run_backward(case, dout_bits):
     q, k, v = U.dev_bits(case.q), U.dev_bits(case.k), U.dev_bits(case.v)
     kc = U.dev_bits(kc_bits) if nc > 0 else None
     vc = U.dev_bits(vc_bits) if nc > 0 else None
-    gates = torch.from_numpy(np.ascontiguousarray(case.gates, dtype=np.float32)).cuda()
+    gates, wg, bgt = U.gate_args(case)
     sel_t = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
     dq, dK, dV, dgates = nanf(B, T, Hq, dk), nanf(B, H, T, dk), nanf(B, H, T, dv), nanf(B, T, Hq, 3)
     dkc = nanf(B, H, nc, dk) if nc > 0 else None
     dvc = nanf(B, H, nc, dv) if nc > 0 else None
+    dwg = nanf(Hq, 3, dk) if wg is not None else None
+    dbg = nanf(Hq, 3) if bgt is not None else None
     ws = N.new_workspace(N.nsa_prefill_bwd_workspace_size(dims, cfg, T))
     N.nsa_prefill_bwd(dims, cfg, T, q, k, v, kc, vc, gates, sel_t, U.dev_bits(dout_bits), dq, dK, dV, dkc, dvc,
-                      dgates, ws)
+                      dgates, ws, w_gate=wg, b_gate=bgt, dw_gate=dwg, db_gate=dbg)
     dk_raw, dv_raw = dK.clone(), dV.clone()
-    res = dict(sel=sel, dq=dq, dk_raw=dk_raw, dv_raw=dv_raw, dkc=dkc, dvc=dvc, dgates=dgates)
+    res = dict(sel=sel, dq=dq, dk_raw=dk_raw, dv_raw=dv_raw, dkc=dkc, dvc=dvc, dgates=dgates, dwg=dwg, dbg=dbg)
     for which, x, w_bits, pe_bits, dy, dx, D in ((0, k, case.w_k, case.pe_k, dkc, dK, dk),
                                                  (1, v, case.w_v, case.pe_v, dvc, dV, dv)):
         dw, dpe = nanf(p.l * D, D), nanf(p.l, D)
@@ -99,10 +101,13 @@ def oracle_group(case, dout_bits, sel, b, g, rows):
     G = wl.num_q_heads // wl.num_kv_heads
     hs = slice(g * G, (g + 1) * G)
     sl = [[int(j) for j in sel[b, t, g] if j >= 0] for t in rows]
+    net = getattr(case, "gate_net", False)
+    Wg = _w(case.w_gate[hs]) if net else None
+    bg = np.asarray(case.b_gate[hs], dtype=np.float64) if net and case.b_gate is not None else None
     return NB.sequence_backward(_w(case.q[b, :, hs]), _w(case.k[b, g]), _w(case.v[b, g]), _w(case.w_k),
                                 _w(case.pe_k), _w(case.w_v), _w(case.pe_v),
                                 np.asarray(case.gates[b, :, hs], dtype=np.float64), _w(dout_bits[b, :, hs]),
-                                list(rows), p, sel=sl)
+                                list(rows), p, sel=sl, Wg=Wg, bg=bg)
 
 
 def oracle_rows(case, dout_bits, sel, b, g, rows):
@@ -133,6 +138,8 @@ def check_all(case, dout_bits, got):
     acc = {n: [] for n in ("dq", "dgates", "dk", "dv", "dkc", "dvc")}
     want = {n: [] for n in acc}
     sums = {n: 0.0 for n in ("dWk", "dPEk", "dWv", "dPEv")}
+    dwg = np.zeros((wl.num_q_heads, 3, wl.d_k))  # gate network: per head, summed over sequences
+    dbg = np.zeros((wl.num_q_heads, 3))
     terms = {"k": 0.0, "v": 0.0}  # sum_i |dY_i| over every (b, g): the size of dPE's terms
     for b in range(wl.batch):
         for g in range(wl.num_kv_heads):
@@ -149,6 +156,10 @@ def check_all(case, dout_bits, got):
                 sums[n] = sums[n] + r[n]
             terms["k"] = terms["k"] + np.abs(r["dKc"]).sum(axis=0)
             terms["v"] = terms["v"] + np.abs(r["dVc"]).sum(axis=0)
+            if "dWg" in r:
+                dwg[hs] += r["dWg"]
+                if r["dbg"] is not None:
+                    dbg[hs] += r["dbg"]
     # A gradient that is exactly 0 (e.g. dq, dk when every branch sees one key, so
     # each dS = P (dP - D) cancels) is measured against the size of the terms that
     # cancel, bounded below by 1e-6 x the dgates scale (dout . o).
@@ -168,6 +179,10 @@ def check_all(case, dout_bits, got):
     close(got["dpek"], sums["dPEk"], "dPEk", scale=max(size_k, float(np.abs(sums["dPEk"]).max())))
     close(got["dwv"], sums["dWv"], "dWv")
     close(got["dpev"], sums["dPEv"], "dPEv", scale=max(size_v, float(np.abs(sums["dPEv"]).max())))
+    if got.get("dwg") is not None:
+        close(got["dwg"], dwg, "dw_gate")
+    if got.get("dbg") is not None:
+        close(got["dbg"], dbg, "db_gate")
 
 
 def test_backward_tiny_all_rows():
@@ -306,3 +321,15 @@ def test_backward_shapes(over):
     case = I.generate(I.workload("tiny_prefill_512", **over), 9)
     dout = I.output_gradient(case, 9)
     check_all(case, dout, run_backward(case, dout))
+
+
+@pytest.mark.parametrize("wl_name,T", [("tiny_prefill_512", 300), ("prefill_32k", 500)])
+def test_backward_gate_network(wl_name, T):
+    """Gates from the gate network: dq includes the gates' path, and dw_gate,
+    db_gate against autograd through the sigmoid layer."""
+    case = I.generate(I.workload(wl_name, seq_len=T), 10)
+    case.gate_net = True
+    dout = I.output_gradient(case, 10)
+    got = run_backward(case, dout)
+    assert got["dwg"] is not None and got["dbg"] is not None
+    check_all(case, dout, got)
