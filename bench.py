@@ -374,8 +374,8 @@ def backward_flops(wl):
 
 
 def backward_setup(torch, N, I):
-    """prefill_32k inputs resident on the GPU, the compressed cache and the forward's
-    selection, an output gradient and the backward's buffers."""
+    """prefill_32k inputs resident on the GPU, the compressed cache, the forward's
+    selection and per-branch log-sum-exp, an output gradient and the backward's buffers."""
     wl = I.workload("prefill_32k")
     seed = list(I.WORKLOADS).index("prefill_32k")
     case = I.generate(wl, seed)
@@ -398,8 +398,9 @@ def backward_setup(torch, N, I):
     X["sel"] = torch.empty((B, T, H, p.n_sel), dtype=torch.int32, device="cuda")
     out = torch.empty((B, T, Hq, dv), dtype=torch.bfloat16, device="cuda")
     ws = N.new_workspace(N.nsa_prefill_workspace_size(dims, cfg, T, False))
+    X["lse"] = torch.empty((B, T, Hq, 3), dtype=torch.float32, device="cuda")
     N.nsa_prefill_fwd(dims, cfg, T, X["q"], X["k"], X["v"], X["kc"], X["vc"], None, None, None, None, X["gates"],
-                      out, X["sel"], ws)
+                      out, X["sel"], ws, lse_out=X["lse"])
     f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
     X.update(dq=f32(B, T, Hq, dk), dk=f32(B, H, T, dk), dv=f32(B, H, T, dv), dkc=f32(B, H, nc, dk),
              dvc=f32(B, H, nc, dv), dg=f32(B, T, Hq, 3), dwk=f32(p.l * dk, dk), dpk=f32(p.l, dk),
@@ -408,9 +409,10 @@ def backward_setup(torch, N, I):
     X["wsc"] = N.new_workspace(max(N.nsa_compress_bwd_workspace_size(dims, cfg, T, w) for w in (0, 1)))
     torch.cuda.synchronize()
 
-    def attn():
+    def attn(saved_lse=True):  # with the forward's log-sum-exp: one pass on the query side
         N.nsa_prefill_bwd(dims, cfg, T, X["q"], X["k"], X["v"], X["kc"], X["vc"], X["gates"], X["sel"], X["dout"],
-                          X["dq"], X["dk"], X["dv"], X["dkc"], X["dvc"], X["dg"], X["ws"])
+                          X["dq"], X["dk"], X["dv"], X["dkc"], X["dvc"], X["dg"], X["ws"],
+                          lse=X["lse"] if saved_lse else None)
 
     def comp():
         N.nsa_compress_bwd(dims, cfg, T, 0, X["k"], X["wk"], X["pk"], X["dkc"], X["dk"], X["dwk"], X["dpk"], X["wsc"])
@@ -457,6 +459,13 @@ def bench_backward(args, torch, N, I):
     ev[2].record()
     torch.cuda.synchronize()
     attn_ms, comp_ms = ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
+    attn(False)  # the same call without the saved log-sum-exp (query side in two passes)
+    ev[0].record()
+    for _ in range(reps):
+        attn(False)
+    ev[1].record()
+    torch.cuda.synchronize()
+    recompute_ms = ev[0].elapsed_time(ev[1]) / reps
     hev = HipEvents(4 * reps)
     try:
         for i in range(reps):
@@ -470,14 +479,15 @@ def bench_backward(args, torch, N, I):
         hev.close()
     f = backward_flops(wl)
     ms = attn_ms + comp_ms
-    res = dict(workload=wl.name, ms=ms, attention_ms=attn_ms, compress_ms=comp_ms, flops=f,
+    res = dict(workload=wl.name, ms=ms, attention_ms=attn_ms, compress_ms=comp_ms, recompute_ms=recompute_ms, flops=f,
                tflops=(f["attention"] + f["compress"]) / (ms * 1e-3) / 1e12,
                attention_tflops=f["attention"] / (attn_ms * 1e-3) / 1e12,
                kernel_ms=dict(bwd_query_kernel=ph[0], bwd_kv_kernel_raw=ph[1], bwd_kv_kernel_cmp=ph[2]))
     res["mfma_frac"] = res["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS
     log(f"[bench] backward {wl.name}: {ms:.2f} ms ({res['tflops']:.1f} TFLOP/s); attention {attn_ms:.2f} ms "
         f"({res['attention_tflops']:.0f} TFLOP/s, {100 * res['mfma_frac']:.1f}% of bf16 peak): query side "
-        f"{ph[0]:.2f} ms, raw keys {ph[1]:.2f} ms, compressed keys {ph[2]:.2f} ms; compression {comp_ms:.2f} ms")
+        f"{ph[0]:.2f} ms, raw keys {ph[1]:.2f} ms, compressed keys {ph[2]:.2f} ms; compression {comp_ms:.2f} ms; "
+        f"without the saved lse {recompute_ms:.2f} ms")
     res["positions_per_s"] = wl.batch * wl.seq_len / (ms * 1e-3)
     if not args.no_cpu:
         res["cpu"] = backward_cpu_baseline(case, dout_bits, torch)
@@ -921,6 +931,7 @@ def main():
                           "mfma_frac": bwd["mfma_frac"], "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS,
                           "kernel_ms": bwd["kernel_ms"]},
             "compression_ms": bwd["compress_ms"], "positions_per_s": bwd["positions_per_s"],
+            "attention_ms_without_saved_lse": bwd["recompute_ms"],
             "cpu_oracle": bwd.get("cpu")}
     print(json.dumps(line), flush=True)
 

@@ -288,8 +288,8 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
  *   dq    = s sum_c sum_k P (g_c dout.v_k - g_c dout.o_c) k
  *   dk, dv (raw) from the selected and window branches; dk_cmp, dv_cmp from the
  *   compressed branch (feed them to nsa_compress_bwd for the compression MLP).
- * The branch statistics (lse_c, D_c = g_c dout . o_c) are recomputed from the
- * inputs in a first pass and kept in the workspace.  With nsa_set_phase_events
+ * The branch statistics (lse_c, D_c = g_c dout . o_c) are kept in the workspace
+ * for the key-side kernels.  With nsa_set_phase_events
  * the events mark: before the query-side kernel, after it, after the raw-key
  * kernels, after the compressed-key kernel.
  *
@@ -302,6 +302,10 @@ nsa_status_t nsa_prefill_workspace_size(const nsa_dims_t* dims, const nsa_config
  *          db_gate = sum_t dz are written.  Exactly one gate source.
  *   sel_idx  int32 [B, T, Hkv, n_sel]: the forward's sel_idx_out (ascending,
  *          -1 padded; any other content gives undefined gradients).
+ *   lse    nullable float32 [B, T, Hq, 3]: the forward's lse_out.  Given, the
+ *          query side walks the key tiles once (P = exp(s q.k - lse); D_c =
+ *          g_c sum P dP accumulates beside dq); NULL recomputes each branch's
+ *          softmax in a first pass.
  *   dout   bf16 [B, T, Hq, d_v] gradient of the output.
  *   dq     float32 [B, T, Hq, d_k]             (written)
  *   dk, dv float32 [B, Hkv, T, d_k / d_v]       (written)
@@ -320,7 +324,7 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
                              const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* k_cmp, const uint16_t* v_cmp,
                              const float* gates, const uint16_t* w_gate, const float* b_gate,
-                             const int32_t* sel_idx, const uint16_t* dout,
+                             const int32_t* sel_idx, const float* lse, const uint16_t* dout,
                              float* dq, float* dk, float* dv, float* dk_cmp, float* dv_cmp,
                              float* dgates, float* dw_gate, float* db_gate,
                              void* workspace, size_t workspace_bytes, void* stream);

@@ -73,7 +73,7 @@ _SIGS = {
     "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_prefill_bwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                        _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
+                        _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_prefill_bwd_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_compress_bwd": [_VP, _VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                          ctypes.c_size_t, _VP],
@@ -239,10 +239,10 @@ def nsa_prefill_bwd_workspace_size(dims: nsa_dims_t, cfg: nsa_config_t, seq_len:
 
 
 def nsa_prefill_bwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, gates, sel_idx, dout, dq, dk, dv, dk_cmp, dv_cmp,
-                    dgates, workspace, stream=None, w_gate=None, b_gate=None, dw_gate=None, db_gate=None):
+                    dgates, workspace, stream=None, w_gate=None, b_gate=None, dw_gate=None, db_gate=None, lse=None):
     """Gradients of nsa_prefill_fwd; dq/dk/dv/dk_cmp/dv_cmp/dgates are float32 outputs.
     gates=None with w_gate (and optionally b_gate) differentiates through the gate network
-    into dw_gate (float32 [Hq, 3, d_k]) and db_gate (float32 [Hq, 3])."""
+    into dw_gate (float32 [Hq, 3, d_k]) and db_gate (float32 [Hq, 3]); lse is the forward's lse_out."""
     lib = load_library()
     B, Hq, H, T = dims.batch, dims.num_q_heads, dims.num_kv_heads, int(seq_len)
     nc = compressed_count(T, cfg.l, cfg.d)
@@ -252,6 +252,7 @@ def nsa_prefill_bwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, gates, sel_idx, d
                                _ptr(v_cmp, "v_cmp", 2, B * H * nc * dims.d_v),
                                _ptr(gates, "gates", 4, B * T * Hq * 3), _ptr(w_gate, "w_gate", 2, Hq * 3 * dims.d_k),
                                _ptr(b_gate, "b_gate", 4, Hq * 3), _ptr(sel_idx, "sel_idx", 4, B * T * H * cfg.n_sel),
+                               _ptr(lse, "lse", 4, B * T * Hq * 3),
                                _ptr(dout, "dout", 2, B * T * Hq * dims.d_v),
                                _ptr(dq, "dq", 4, B * T * Hq * dims.d_k), _ptr(dk, "dk", 4, B * H * T * dims.d_k),
                                _ptr(dv, "dv", 4, B * H * T * dims.d_v),

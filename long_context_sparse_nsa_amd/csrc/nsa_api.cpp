@@ -640,7 +640,7 @@ nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_co
 nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t seq_len, const uint16_t* q,
                              const uint16_t* k, const uint16_t* v, const uint16_t* k_cmp, const uint16_t* v_cmp,
                              const float* gates, const uint16_t* w_gate, const float* b_gate, const int32_t* sel_idx,
-                             const uint16_t* dout, float* dq, float* dk, float* dv, float* dk_cmp, float* dv_cmp,
+                             const float* lse, const uint16_t* dout, float* dq, float* dk, float* dv, float* dk_cmp, float* dv_cmp,
                              float* dgates, float* dw_gate, float* db_gate, void* workspace, size_t workspace_bytes,
                              void* stream) {
   nsa_status_t st = check_common(dims, cfg, true);
@@ -694,6 +694,7 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.bgate = b_gate;
   p.dwgate = dw_gate;
   p.dbgate = b_gate ? db_gate : nullptr;
+  p.lse_in = lse;
   p.gpart = reinterpret_cast<float*>(ws + lay.off_gpart);
   p.sel = sel_idx;
   p.dout = dout;

@@ -126,7 +126,37 @@ struct QtShape {
   static constexpr int kCopies = kCpK + kCpV;
 };
 
-template <int DK, int DV>
+// lds_rows_product with two products sharing the row pieces: acc1 += rows^T pb1,
+// acc2 += rows^T pb2.
+template <int D>
+__device__ __forceinline__ void lds_rows_product2(const char* blk, const int (&rows)[8], int lr, const u32x4_t& pb1,
+                                                  f32x4_t (&acc1)[D / 16], const u32x4_t& pb2,
+                                                  f32x4_t (&acc2)[D / 16]) {
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) {
+    uint32_t w[8][2];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const u32x2_t x = *reinterpret_cast<const u32x2_t*>(blk + sw_off<D>(rows[r], (D / 16) * lr + 4 * u));
+      w[r][0] = x[0];
+      w[r][1] = x[1];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int wd = jj >> 1, h = jj & 1;
+      const u32x4_t va = {pack_halves(w[0][wd], w[1][wd], h), pack_halves(w[2][wd], w[3][wd], h),
+                          pack_halves(w[4][wd], w[5][wd], h), pack_halves(w[6][wd], w[7][wd], h)};
+      acc1[4 * u + jj] = mfma_bf16(va, pb1, acc1[4 * u + jj]);
+      acc2[4 * u + jj] = mfma_bf16(va, pb2, acc2[4 * u + jj]);
+    }
+  }
+}
+
+// ONEPASS: the forward's per-branch log-sum-exp is given (p.lse_in), so one walk
+// over the tiles suffices: with P = exp(s q.k - lse) known, D_c = g_c sum_k P dP
+// accumulates beside dq = s (sum_k g_c P dP k - sum_c D_c sum_{k in c} P k); the
+// second sum is kept per branch and folded in when the branch's tiles end.
+template <int DK, int DV, bool ONEPASS>
 __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
   using SH = QtShape<DK, DV>;
   __shared__ __attribute__((aligned(1024))) char s_buf[kQtBuf][SH::kBuf];
@@ -188,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
   const int nslc = nsel * tps;
   const int wlo = max(0, t0 - p.w + 1);
   const int nwin = (tl - wlo) / 32 + 1;
-  const int ntile = ncmp + nslc + nwin, nstep = 2 * ntile;
+  const int ntile = ncmp + nslc + nwin, nstep = ONEPASS ? ntile : 2 * ntile;
 
   auto desc = [&](int i, int& br, int& k0, int& wm, int& kend) {
     const int u = i < ntile ? i : i - ntile;
@@ -202,27 +232,37 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
     }
   };
 
+  // This lane's share of a tile's copies, computed once: row r (bits 0..7) and the
+  // byte offset of global chunk (slot ^ (r & 7)) within the row (bits 8..).
+  uint32_t cpk[SH::kCpK], cpv[SH::kCpV];
+#pragma unroll
+  for (int j = 0; j < SH::kCpK; ++j) {
+    const int pch = (wave * SH::kCpK + j) * 64 + lane;
+    const int r = pch / (DK / 8), sl = pch - r * (DK / 8);
+    cpk[j] = (uint32_t)r | ((uint32_t)(16 * (sl ^ (r & 7))) << 8);
+  }
+#pragma unroll
+  for (int j = 0; j < SH::kCpV; ++j) {
+    const int pch = (wave * SH::kCpV + j) * 64 + lane;
+    const int r = pch / (DV / 8), sl = pch - r * (DV / 8);
+    cpv[j] = (uint32_t)r | ((uint32_t)(16 * (sl ^ (r & 7))) << 8);
+  }
   auto issue = [&](int i) {
     int br, k0, wm, kend;
     desc(i, br, k0, wm, kend);
-    const uint16_t* kb = br == kCmp ? kcmp : kraw;
-    const uint16_t* vb = br == kCmp ? vcmp : vraw;
     const int nk = br == kCmp ? nc : T;
+    const uint16_t* kb = (br == kCmp ? kcmp : kraw) + (int64_t)k0 * DK;  // the tile's first row
+    const uint16_t* vb = (br == kCmp ? vcmp : vraw) + (int64_t)k0 * DV;
+    const uint32_t lim = (uint32_t)(nk - 1 - k0);  // rows past the end read the last row (masked later)
     const uint32_t buf = lds0 + (uint32_t)((i % kQtBuf) * SH::kBuf);
 #pragma unroll
-    for (int j = 0; j < SH::kCpK; ++j) {
-      const int pch = (wave * SH::kCpK + j) * 64 + lane;
-      const int r = pch / (DK / 8), sl = pch - r * (DK / 8);
-      const int key = min(k0 + r, nk - 1);  // rows past the end: a valid row, masked in the compute
-      copy16_to_lds_at(kb + (int64_t)key * DK + 8 * (sl ^ (r & 7)), buf + (wave * SH::kCpK + j) * 1024);
-    }
+    for (int j = 0; j < SH::kCpK; ++j)
+      copy16_sb_at(kb, min(cpk[j] & 0xFFu, lim) * (uint32_t)(DK * 2) + (cpk[j] >> 8),
+                   buf + (wave * SH::kCpK + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < SH::kCpV; ++j) {
-      const int pch = (wave * SH::kCpV + j) * 64 + lane;
-      const int r = pch / (DV / 8), sl = pch - r * (DV / 8);
-      const int key = min(k0 + r, nk - 1);
-      copy16_to_lds_at(vb + (int64_t)key * DV + 8 * (sl ^ (r & 7)), buf + 2 * SH::kK + (wave * SH::kCpV + j) * 1024);
-    }
+    for (int j = 0; j < SH::kCpV; ++j)
+      copy16_sb_at(vb, min(cpv[j] & 0xFFu, lim) * (uint32_t)(DV * 2) + (cpv[j] >> 8),
+                   buf + 2 * SH::kK + (wave * SH::kCpV + j) * 1024);
   };
 
   u32x4_t qf[DK / 32], of[DV / 32];
@@ -256,6 +296,152 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
   const int nvis = tv ? n_visible(t, p.l, p.d, nc) : 0;
   const float sl2 = p.scale_log2;
   wait_vmem();
+
+  // One pipeline step: wait for tile i, hand the next buffer to the copies.
+  auto step_begin = [&](int i) {
+    wait_steps<SH::kCopies, kQtBuf - 2>(min(nstep - 1 - i, kQtBuf - 2));
+    lds_barrier();
+    if (i + kQtBuf - 1 < nstep) issue(i + kQtBuf - 1);
+  };
+  // This wave's valid keys of step i's tile: [klo, khi).
+  auto key_range = [&](int br, int k0, int wm, int kend, int& klo, int& khi) {
+    klo = 0;
+    khi = 0;
+    if (tv && ((wm >> wave) & 1)) {
+      if (br == kCmp) khi = nvis;
+      else if (br == kSlc) khi = min(kend, t + 1);
+      else { klo = t - p.w + 1; khi = t + 1; }
+    }
+    klo = max(klo, k0);
+    khi = min(khi, k0 + 32);
+  };
+  // dq store (scaled), plus the gate network's path.
+  auto store_dq = [&](const f32x4_t (&dqa)[DK / 16], const float (&dg_c)[3]) {
+    if (!(tv && hv)) return;
+    float* dst = p.dq + (qrow + lr) * DK;
+    float dz[3];  // gate network: dq_h += sum_c dz_c w_gate[h, c], dz_c = dgates_c g_c (1 - g_c)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) dz[c] = dg_c[c] * gt[c] * (1.f - gt[c]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j4 = 0; j4 < DK / 64; ++j4) {
+        const int j = 4 * j4, ch = (DK / 16) * (4 * lg + i) + j;
+        f32x4_t v = f32x4_t{dqa[j][i], dqa[j + 1][i], dqa[j + 2][i], dqa[j + 3][i]} * p.scale;
+        if (p.wgate) {
+#pragma unroll
+          for (int c = 0; c < 3; ++c) {
+            const u32x2_t w = ld8(p.wgate + ((int64_t)(g * G + lr) * 3 + c) * DK + ch);
+            v += f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])} * dz[c];
+          }
+        }
+        *reinterpret_cast<f32x4_t*>(dst + ch) = v;
+      }
+  };
+
+  if constexpr (ONEPASS) {
+    float ls2[3], dg_c[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 3; ++c) ls2[c] = (tv && hv) ? p.lse_in[(qrow + lr) * 3 + c] * kLog2e : 0.f;
+    f32x4_t dqa[DK / 16], bv[DK / 16];
+#pragma unroll
+    for (int j = 0; j < DK / 16; ++j) {
+      dqa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      bv[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float dsum = 0.f;  // this lane's part of sum_k P dP over the current branch
+    int cur = 0;
+    auto close_branch = [&](const int c) {
+      const float ds = sum_over_groups(dsum);  // dout . o_c
+      const float gc = c == kCmp ? gt[0] : (c == kSlc ? gt[1] : gt[2]);
+      const float D = gc * ds;
+#pragma unroll
+      for (int j = 0; j < DK / 16; ++j) {
+        dqa[j] -= bv[j] * D;
+        bv[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      if (c == kCmp) dg_c[0] = ds; else if (c == kSlc) dg_c[1] = ds; else dg_c[2] = ds;
+      if (tv && lg == 0) {
+        float* rec = p.stat + ((((int64_t)c * p.B + b) * T + t) * p.H + g) * kStatFloats;
+        const float lsc = c == kCmp ? ls2[0] : (c == kSlc ? ls2[1] : ls2[2]);
+        rec[lr] = hv ? lsc : 0.f;
+        rec[16 + lr] = hv ? D : 0.f;
+        rec[32 + lr] = gc;
+        if (hv) p.dgates[(qrow + lr) * 3 + c] = ds;
+      }
+      dsum = 0.f;
+    };
+    for (int i = 0; i < kQtBuf - 1 && i < nstep; ++i) issue(i);
+    for (int i = 0; i < nstep; ++i) {
+      step_begin(i);
+      int br, k0, wm, kend, klo, khi;
+      desc(i, br, k0, wm, kend);
+      if (cur < br) {
+        while (cur < br) close_branch(cur++);
+        wait_vmem();  // keep the copy count exact for the next wait
+      }
+      key_range(br, k0, wm, kend, klo, khi);
+      if (klo >= khi) continue;
+      const char* kt = s_buf[i % kQtBuf];
+      const char* vt = kt + 2 * SH::kK;
+      const float ls = br == kCmp ? ls2[0] : (br == kSlc ? ls2[1] : ls2[2]);
+      const float gc = br == kCmp ? gt[0] : (br == kSlc ? gt[1] : gt[2]);
+      // Two 16-key halves: logits and dout.v (16x16x32), then both sums over the
+      // half's keys with 16x16x16 products whose B operand is the half's P tile as
+      // it stands (lane: head lr, keys 4lg .. 4lg+3).
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4_t kf[DK / 32], vf[DV / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) kf[kk] = lds_frag<DK>(kt, 16 * hh + lr, 8 * lg + 32 * kk);
+#pragma unroll
+        for (int kk = 0; kk < DV / 32; ++kk) vf[kk] = lds_frag<DV>(vt, 16 * hh + lr, 8 * lg + 32 * kk);
+        const f32x4_t sv = qk_tile<DK>(kf, qf), dp = qk_tile<DV>(vf, of);
+        float pa[4], pb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = k0 + 16 * hh + 4 * lg + e;
+          const float pr = (x >= klo && x < khi) ? __builtin_amdgcn_exp2f(sv[e] * sl2 - ls) : 0.f;
+          dsum = fmaf(pr, dp[e], dsum);
+          pa[e] = pr * gc * dp[e];
+          pb[e] = pr;
+        }
+        // g P dP as bf16 high + low parts (about 16 significant bits): the two sums
+        // cancel in dq = s (A - D Bv), and with one key per branch (P rounds to
+        // exactly 1) the difference is 0, so A's rounding must stay well below it.
+        // P <= 1 itself enters as one bf16, like the probabilities of the other products.
+        u32x2_t opa, opal, opb;
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          opa[w2] = pack_bf16x2(pa[2 * w2], pa[2 * w2 + 1]);
+          opb[w2] = pack_bf16x2(pb[2 * w2], pb[2 * w2 + 1]);
+          opal[w2] = pack_bf16x2(pa[2 * w2] - bf16_lo(opa[w2]), pa[2 * w2 + 1] - bf16_hi(opa[w2]));
+        }
+#pragma unroll
+        for (int u = 0; u < DK / 64; ++u) {  // channels (DK/16)*lr + 4u .. +3 of keys 16hh + 4lg + r
+          uint32_t w[4][2];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const u32x2_t x2 =
+                *reinterpret_cast<const u32x2_t*>(kt + sw_off<DK>(16 * hh + 4 * lg + r, (DK / 16) * lr + 4 * u));
+            w[r][0] = x2[0];
+            w[r][1] = x2[1];
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int wd = jj >> 1, h = jj & 1;
+            const u32x2_t va = {pack_halves(w[0][wd], w[1][wd], h), pack_halves(w[2][wd], w[3][wd], h)};
+            dqa[4 * u + jj] = mfma16_bf16(va, opa, dqa[4 * u + jj]);
+            dqa[4 * u + jj] = mfma16_bf16(va, opal, dqa[4 * u + jj]);
+            bv[4 * u + jj] = mfma16_bf16(va, opb, bv[4 * u + jj]);
+          }
+        }
+      }
+    }
+    while (cur < 3) close_branch(cur++);
+    store_dq(dqa, dg_c);
+    return;
+  }
 
   // Pass-1 state of the current branch, and the finished branches' statistics.
   float m = kNegInf, l = 0.f;
@@ -297,25 +483,6 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
     l = 0.f;
 #pragma unroll
     for (int j = 0; j < DV / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
-
-  // One pipeline step: wait for tile i, hand the next buffer to the copies.
-  auto step_begin = [&](int i) {
-    wait_steps<SH::kCopies, kQtBuf - 2>(min(nstep - 1 - i, kQtBuf - 2));
-    lds_barrier();
-    if (i + kQtBuf - 1 < nstep) issue(i + kQtBuf - 1);
-  };
-  // This wave's valid keys of step i's tile: [klo, khi).
-  auto key_range = [&](int br, int k0, int wm, int kend, int& klo, int& khi) {
-    klo = 0;
-    khi = 0;
-    if (tv && ((wm >> wave) & 1)) {
-      if (br == kCmp) khi = nvis;
-      else if (br == kSlc) khi = min(kend, t + 1);
-      else { klo = t - p.w + 1; khi = t + 1; }
-    }
-    klo = max(klo, k0);
-    khi = min(khi, k0 + 32);
   };
 
   for (int i = 0; i < kQtBuf - 1 && i < nstep; ++i) issue(i);
@@ -416,28 +583,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
     pv_step<DK>(kr, pack_probs(lo, hi), dqa);
   }
 
-  if (tv && hv) {
-    float* dst = p.dq + (qrow + lr) * DK;
-    // gate network: dq_h += sum_c dz_c w_gate[h, c], dz_c = dgates_c g_c (1 - g_c)
-    float dz[3];
-#pragma unroll
-    for (int c = 0; c < 3; ++c) dz[c] = dg_c[c] * gt[c] * (1.f - gt[c]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j4 = 0; j4 < DK / 64; ++j4) {
-        const int j = 4 * j4, ch = (DK / 16) * (4 * lg + i) + j;
-        f32x4_t v = f32x4_t{dqa[j][i], dqa[j + 1][i], dqa[j + 2][i], dqa[j + 3][i]} * p.scale;
-        if (p.wgate) {
-#pragma unroll
-          for (int c = 0; c < 3; ++c) {
-            const u32x2_t w = ld8(p.wgate + ((int64_t)(g * G + lr) * 3 + c) * DK + ch);
-            v += f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])} * dz[c];
-          }
-        }
-        *reinterpret_cast<f32x4_t*>(dst + ch) = v;
-      }
-  }
+  store_dq(dqa, dg_c);
 }
 
 // Gate-network gradients, partial sums over position range blockIdx.y of the
@@ -824,7 +970,10 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s, const PhaseEvents* ev
   const int64_t nsel = (int64_t)p.B * p.T * p.H * p.n;
   hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((nsel + 255) / 256)), dim3(256), 0, s, p);
   if (ev) hipEventRecord(ev->ev[0], s);
-  hipLaunchKernelGGL((bwd_query_kernel<DK, DV>), dim3((unsigned)(nbg * p.nqt)), dim3(256), 0, s, p);
+  if (p.lse_in)
+    hipLaunchKernelGGL((bwd_query_kernel<DK, DV, true>), dim3((unsigned)(nbg * p.nqt)), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_query_kernel<DK, DV, false>), dim3((unsigned)(nbg * p.nqt)), dim3(256), 0, s, p);
   if (p.wgate) {
     hipLaunchKernelGGL((bwd_gate_part_kernel<DK>), dim3((unsigned)p.Hq, kGateChunks), dim3(256), 0, s, p);
     const int64_t ng = (int64_t)p.Hq * 3 * (DK + 1);

@@ -26,6 +26,7 @@ struct BwdParams {
   const uint16_t* kc;                // [B, H, nc, DK]
   const uint16_t* vc;                // [B, H, nc, DV]
   const float* gates;                // [B, T, Hq, 3], or null with the gate network
+  const float* lse_in;               // [B, T, Hq, 3] the forward's per-branch log-sum-exp, or null
   const uint16_t* wgate;             // gate network [Hq, 3, DK] (null: gates are given)
   const float* bgate;                // [Hq, 3] or null
   float* dwgate;                     // [Hq, 3, DK] (gate network only)

@@ -223,8 +223,8 @@ def test_backward_workspace_sizes_and_validation():
     need = N.nsa_prefill_bwd_workspace_size(dims, cfg, T)
 
     def bwd(q=f, kc=f, sel=f, ws=f, nb=need, T=T, gates=f, wg=None, bg=None, dwg=None):
-        return lib.nsa_prefill_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, q, f, f, kc, f, gates, wg, bg, sel, f,
-                                   f, f, f, f, f, f, dwg, None, ws, nb, None)
+        return lib.nsa_prefill_bwd(ctypes.byref(dims), ctypes.byref(cfg), T, q, f, f, kc, f, gates, wg, bg, sel, None,
+                                   f, f, f, f, f, f, f, dwg, None, ws, nb, None)
     assert bwd(q=None) == A.NSA_ERROR_INVALID_VALUE and "NULL" in N.nsa_last_error()
     assert bwd(sel=None) == A.NSA_ERROR_INVALID_VALUE
     assert bwd(kc=None) == A.NSA_ERROR_INVALID_VALUE and "compressed" in N.nsa_last_error()

@@ -57,17 +57,19 @@ def oracle_cache(case):
     return np.stack(kc), np.stack(vc)
 
 
-def run_backward(case, dout_bits):
-    """GPU forward (for the selection) and backward with the oracle's compressed cache."""
+def run_backward(case, dout_bits, saved_lse=True):
+    """GPU forward (for the selection and, with saved_lse, each branch's log-sum-exp)
+    and backward with the oracle's compressed cache."""
     wl, p = case.wl, case.p
     dims, cfg = U.dims_cfg(case)
     B, Hq, H, dk, dv, T = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.d_k, wl.d_v, wl.seq_len
     nc = N.compressed_count(T, p.l, p.d)
     kc_bits, vc_bits = oracle_cache(case) if nc > 0 else (None, None)
     if nc > 0:
-        _, sel = U.run_prefill(case, kc_bits=kc_bits, vc_bits=vc_bits)
+        _, sel, lse = U.run_prefill(case, kc_bits=kc_bits, vc_bits=vc_bits, with_lse=True)
     else:
-        _, sel = U.run_prefill(case)
+        _, sel, lse = U.run_prefill(case, with_lse=True)
+    lse_t = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).cuda() if saved_lse else None
     nanf = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
     q, k, v = U.dev_bits(case.q), U.dev_bits(case.k), U.dev_bits(case.v)
     kc = U.dev_bits(kc_bits) if nc > 0 else None
@@ -81,7 +83,7 @@ def run_backward(case, dout_bits):
     dbg = nanf(Hq, 3) if bgt is not None else None
     ws = N.new_workspace(N.nsa_prefill_bwd_workspace_size(dims, cfg, T))
     N.nsa_prefill_bwd(dims, cfg, T, q, k, v, kc, vc, gates, sel_t, U.dev_bits(dout_bits), dq, dK, dV, dkc, dvc,
-                      dgates, ws, w_gate=wg, b_gate=bgt, dw_gate=dwg, db_gate=dbg)
+                      dgates, ws, w_gate=wg, b_gate=bgt, dw_gate=dwg, db_gate=dbg, lse=lse_t)
     dk_raw, dv_raw = dK.clone(), dV.clone()
     res = dict(sel=sel, dq=dq, dk_raw=dk_raw, dv_raw=dv_raw, dkc=dkc, dvc=dvc, dgates=dgates, dwg=dwg, dbg=dbg)
     for which, x, w_bits, pe_bits, dy, dx, D in ((0, k, case.w_k, case.pe_k, dkc, dK, dk),
@@ -333,3 +335,12 @@ def test_backward_gate_network(wl_name, T):
     got = run_backward(case, dout)
     assert got["dwg"] is not None and got["dbg"] is not None
     check_all(case, dout, got)
+
+
+@pytest.mark.parametrize("wl_name,T,seed", [("tiny_prefill_512", 512, 11), ("prefill_32k", 700, 12)])
+def test_backward_without_saved_lse(wl_name, T, seed):
+    """Without the forward's log-sum-exp the query side recomputes each branch's
+    softmax in a first pass; same gradients."""
+    case = I.generate(I.workload(wl_name, seq_len=T), seed)
+    dout = I.output_gradient(case, seed)
+    check_all(case, dout, run_backward(case, dout, saved_lse=False))
