@@ -331,13 +331,14 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
 /* Workspace bytes for nsa_prefill_bwd (host-only): per (branch, position, KV
  * group) a record of 48 fp32 (the heads' log-sum-exp, D and gate, padded to 16
  * heads), [3, B, T, Hkv, 48]; a selection bitmap [B, Hkv, ceil(T/l_sel),
- * ceil(T/32)] uint32; and the key side's fp32 partial sums over position
- * ranges: [P_s, B, Hkv, T, d_k + d_v] for the selected branch, P_s =
- * ceil(W / (128 * ceil(ceil(W / 8) / 128))) with W = ceil(T/32) (at most 8),
- * and [P_c, B, Hkv, nc, d_k + d_v] for the compressed branch, P_c =
- * ceil(T / q), q = max(1024, ceil(T/32)) rounded up to even (at most 32); and
- * the gate network's gradient partials [64, Hq, 3, d_k + 1].  Each part is
- * rounded up to 256 bytes.  Contents on entry do not matter. */
+ * ceil(T/32)] uint32; the key side's fp32 partial sums: [B*Hkv, S, 64, d_k + d_v]
+ * for the selected branch with S = ceil(T/64) + ceil(T * n_sel * max(1, l_sel/64)
+ * / 512) (one slot per 512 positions of a 64-key tile), and [P_c, B, Hkv, nc,
+ * d_k + d_v] for the compressed branch, P_c = ceil(T / q), q = max(1024,
+ * ceil(T/32)) rounded up to even (at most 32); per-tile counts [B*Hkv,
+ * ceil(T/64)] and slot offsets [B*Hkv, ceil(T/64) + 1] int32; and the gate
+ * network's gradient partials [64, Hq, 3, d_k + 1].  Each part is rounded up
+ * to 256 bytes.  Contents on entry do not matter. */
 nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                             int64_t seq_len, size_t* bytes);
 

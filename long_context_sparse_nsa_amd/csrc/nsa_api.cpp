@@ -560,19 +560,18 @@ nsa_status_t nsa_prefill_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
 
 namespace {
 
-// Prefill-backward plan: the key side's position ranges.  The selected branch
-// splits a block's positions into at most kBwdMaxParts ranges of whole 128-word
-// bitmap slices; the compressed branch into ranges of at least 1024 positions,
-// at most 32 of them.
+// Prefill-backward plan of the key side.  Selected branch: each 64-key tile's
+// positions are split into workgroups of kSlcSplit; slots_max bounds the splits
+// of one (sequence, group): every selection lands in at most max(1, l_sel/64)
+// tiles.  Compressed branch: ranges of at least 1024 positions, at most 32.
 struct BwdPlan {
-  int qwords, nqw, qchunk, ncq;
+  int kraw, slots_max, qchunk, ncq;
 };
-BwdPlan bwd_plan(int64_t T) {
+BwdPlan bwd_plan(const nsa_config_t* cfg, int64_t T) {
   BwdPlan pl{};
-  const int nwords = (int)((T + 31) / 32);
-  const int per = (nwords + nsa::kBwdMaxParts - 1) / nsa::kBwdMaxParts;
-  pl.qwords = (per + 127) / 128 * 128;
-  pl.nqw = (nwords + pl.qwords - 1) / pl.qwords;
+  pl.kraw = (int)((T + 63) / 64);
+  const int64_t sel = T * cfg->n_sel * std::max(1, cfg->l_sel / 64);
+  pl.slots_max = pl.kraw + (int)((sel + nsa::kSlcSplit - 1) / nsa::kSlcSplit);
   pl.qchunk = (int)std::max<int64_t>(1024, (T + 31) / 32);
   pl.qchunk += pl.qchunk & 1;
   pl.ncq = (int)((T + pl.qchunk - 1) / pl.qchunk);
@@ -580,16 +579,17 @@ BwdPlan bwd_plan(int64_t T) {
 }
 
 // Prefill-backward workspace: per-branch statistics records [3, B, T, Hkv, 48]
-// fp32, the selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32, and
-// the key side's partial sums: selected [nqw, B, Hkv, T, d_k + d_v] and
-// compressed [ncq, B, Hkv, nc, d_k + d_v] fp32, and the gate-network gradient
-// partials [64, Hq, 3, d_k + 1] fp32.
+// fp32, the selection bitmap [B, Hkv, ceil(T / l_sel), ceil(T / 32)] uint32, the
+// key side's partial sums: selected [B*Hkv, slots_max, 64, d_k + d_v] and
+// compressed [ncq, B, Hkv, nc, d_k + d_v] fp32, the selected branch's counts
+// [B*Hkv, kraw] and slot offsets [B*Hkv, kraw + 1] int32, and the gate-network
+// gradient partials [64, Hq, 3, d_k + 1] fp32.
 struct BwdWs {
-  size_t off_stat, off_bits, off_pslc, off_pcmp, off_gpart, total;
+  size_t off_stat, off_bits, off_pslc, off_pcmp, off_cnt, off_soff, off_gpart, total;
 };
 BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   BwdWs w{};
-  const BwdPlan pl = bwd_plan(T);
+  const BwdPlan pl = bwd_plan(cfg, T);
   const size_t bh = (size_t)dims->batch * dims->num_kv_heads, wd = (size_t)(dims->d_k + dims->d_v);
   const size_t recs = (size_t)3 * bh * (size_t)T;
   const size_t nblk = (size_t)((T + cfg->l_sel - 1) / cfg->l_sel), nwords = (size_t)((T + 31) / 32);
@@ -597,8 +597,10 @@ BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   w.off_stat = 0;
   w.off_bits = align256(recs * nsa::kStatFloats * 4);
   w.off_pslc = w.off_bits + align256(bh * nblk * nwords * 4);
-  w.off_pcmp = w.off_pslc + align256((size_t)pl.nqw * bh * (size_t)T * wd * 4);
-  w.off_gpart = w.off_pcmp + align256((size_t)pl.ncq * bh * nc * wd * 4);
+  w.off_pcmp = w.off_pslc + align256(bh * (size_t)pl.slots_max * 64 * wd * 4);
+  w.off_cnt = w.off_pcmp + align256((size_t)pl.ncq * bh * nc * wd * 4);
+  w.off_soff = w.off_cnt + align256(bh * (size_t)pl.kraw * 4);
+  w.off_gpart = w.off_soff + align256(bh * (size_t)(pl.kraw + 1) * 4);
   w.total = w.off_gpart + align256((size_t)nsa::kGateChunks * dims->num_q_heads * 3 * (dims->d_k + 1) * 4);
   return w;
 }
@@ -651,6 +653,8 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   if ((st = check_gates(gates, w_gate, b_gate)) != NSA_SUCCESS) return st;
   if (w_gate && (!dw_gate || (b_gate && !db_gate)))
     return fail(NSA_ERROR_INVALID_VALUE, "the gate network needs dw_gate (and db_gate with b_gate)");
+  if ((int64_t)dims->batch * dims->num_kv_heads > 65535)
+    return fail(NSA_ERROR_UNSUPPORTED, "batch * num_kv_heads above 65535");
   if (seq_len * dims->num_q_heads * (int64_t)std::max(dims->d_k, dims->d_v) * 2 >= ((int64_t)1 << 32))
     return fail(NSA_ERROR_UNSUPPORTED, "seq_len * num_q_heads * max(d_k, d_v) * 2 must stay below 2^32 bytes");
   const int64_t nc = n_compressed(seq_len, cfg->l, cfg->d);
@@ -679,9 +683,9 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.nqt = (int)((seq_len + 3) / 4);
   p.nblk = (int)((seq_len + cfg->l_sel - 1) / cfg->l_sel);
   p.nwords = (int)((seq_len + 31) / 32);
-  const BwdPlan pl = bwd_plan(seq_len);
-  p.qwords = pl.qwords;
-  p.nqw = pl.nqw;
+  const BwdPlan pl = bwd_plan(cfg, seq_len);
+  p.kraw = pl.kraw;
+  p.slots_max = pl.slots_max;
   p.qchunk = pl.qchunk;
   p.ncq = pl.ncq;
   p.q = q;
@@ -708,6 +712,8 @@ nsa_status_t nsa_prefill_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, in
   p.bits = reinterpret_cast<uint32_t*>(ws + lay.off_bits);
   p.part_slc = reinterpret_cast<float*>(ws + lay.off_pslc);
   p.part_cmp = reinterpret_cast<float*>(ws + lay.off_pcmp);
+  p.slc_cnt = reinterpret_cast<int32_t*>(ws + lay.off_cnt);
+  p.slc_off = reinterpret_cast<int32_t*>(ws + lay.off_soff);
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_prefill_bwd(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "prefill backward launch");

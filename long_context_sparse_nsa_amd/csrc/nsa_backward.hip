@@ -20,8 +20,9 @@
 //   bwd_query_kernel    one wave per (b, t, g): recomputes every branch's softmax
 //                       (lse, D, dg) and then accumulates dq over all branches.
 //   bwd_kv_kernel<WIN>  one wave per 16 raw keys: the window queries; stores dk, dv.
-//   bwd_kv_kernel<SLC>  one wave per 16 raw keys and a range of positions: the
-//                       queries that selected the keys' block; partial sums per range.
+//   bwd_kv_kernel<SLC>  one wave per 16 raw keys and up to kSlcSplit of the
+//                       positions that selected the keys' block (counted and split by
+//                       bwd_slc_count_kernel / bwd_slc_scan_kernel); partial sums per split.
 //   bwd_kv_kernel<CMP>  one wave per 16 compressed keys and a range of positions;
 //                       partial sums per range.
 //   bwd_kv_reduce_kernel  adds the selected partials to dk, dv and sums the
@@ -685,18 +686,39 @@ __device__ __forceinline__ void lds_rows_product(const char* blk, const int (&ro
 template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   using SH = KvShape<DK, DV>;
-  constexpr int kSubWords = 128;  // selected branch: 32-position words listed at a time
   __shared__ __attribute__((aligned(1024))) char s_buf[kKvBuf][SH::kBuf];
-  __shared__ int32_t s_list[MODE == kSlc ? 32 * kSubWords : 1];
+  __shared__ int32_t s_list[MODE == kSlc ? kSlcSplit : 1];
   __shared__ int s_scan[4];
+  __shared__ int s_kt;
   const uint32_t lds0 = lds_addr_of(&s_buf[0][0]);
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nbg = p.B * p.H;
-  const int bid = (int)blockIdx.x;
-  const int kt = bid / nbg;
-  const int bg = bid - kt * nbg;
+  int kt, bg, split = 0;
+  if constexpr (MODE == kSlc) {
+    // Slot blockIdx.x of sequence-group blockIdx.y: key tile kt with
+    // off[kt] <= slot < off[kt + 1], its split slot - off[kt].
+    bg = (int)blockIdx.y;
+    const int32_t* off = p.slc_off + (int64_t)bg * (p.kraw + 1);
+    const int slot = (int)blockIdx.x;
+    if (slot >= off[p.kraw]) return;
+    if (tid == 0) {
+      int lo = 0, hi = p.kraw;  // off[lo] <= slot < off[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= slot) lo = mid; else hi = mid;
+      }
+      s_kt = lo;
+    }
+    __syncthreads();
+    kt = s_kt;
+    split = slot - off[kt];
+  } else {
+    const int bid = (int)blockIdx.x;
+    kt = bid / nbg;
+    bg = bid - kt * nbg;
+  }
   const int b = bg / p.H, g = bg - (bg / p.H) * p.H;
   const int kw0 = kt * 64;  // the workgroup's first key
   const int nkeys = MODE == kCmp ? p.nc : p.T;
@@ -748,17 +770,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
 
   // The workgroup's positions come in segments (one for the window and the
   // compressed branch; one per 128-word slice of the bitmap for the selected).
-  int nseg = 1, wlo = 0, whi = 0;
-  int jw[4] = {0, 0, 0, 0};
-  if constexpr (MODE == kSlc) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) jw[w] = (kw0 + 16 * w) / p.lsel;
-    const int first = jw[0] * p.lsel;  // no earlier position can choose these blocks
-    wlo = max(first >> 5, (int)blockIdx.y * p.qwords);
-    whi = min(p.nwords, ((int)blockIdx.y + 1) * p.qwords);
-    nseg = whi > wlo ? (whi - wlo + kSubWords - 1) / kSubWords : 0;
-  }
-  for (int seg = 0; seg < nseg; ++seg) {
+  {
     int tlo = 0, npos = 0;
     if constexpr (MODE == kWin) {
       tlo = kw0;
@@ -767,32 +779,50 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
       tlo = kw0 * p.d + p.l - 1 + (int)blockIdx.y * p.qchunk;
       npos = max(0, min(T - 1, tlo + p.qchunk - 1) - tlo + 1);
     } else {
-      // The positions that chose one of the workgroup's blocks, in order; bit
-      // 24 + w of an entry: wave w's block was chosen.
-      __syncthreads();  // the previous segment's list is no longer read
-      const int w0 = wlo + seg * kSubWords, w1 = min(whi, w0 + kSubWords);
+      // This split's positions: ranks [split * kSlcSplit, (split + 1) * kSlcSplit)
+      // among the positions that chose one of the workgroup's blocks, in order;
+      // bit 24 + w of an entry: wave w's block was chosen.
+      int jw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) jw[w] = (kw0 + 16 * w) / p.lsel;
+      const int wfirst = (jw[0] * p.lsel) >> 5;  // no earlier position can choose these blocks
+      const int nw = p.nwords - wfirst, per = (nw + 255) / 256;
+      const int w0 = wfirst + tid * per, w1 = min(p.nwords, w0 + per);
       const uint32_t* rows = p.bits + bgl * p.nblk * p.nwords;
-      const int wi = w0 + tid;
-      uint32_t m[4] = {0u, 0u, 0u, 0u};
-      if (tid < kSubWords && wi < w1) {
+      auto word = [&](int wi, uint32_t (&m)[4]) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) m[w] = jw[w] < p.nblk ? rows[(int64_t)jw[w] * p.nwords + wi] : 0u;
+        return m[0] | m[1] | m[2] | m[3];
+      };
+      int cnt = 0;
+      for (int wi = w0; wi < w1; ++wi) {
+        uint32_t m[4];
+        cnt += __builtin_popcount(word(wi, m));
       }
-      const uint32_t any = m[0] | m[1] | m[2] | m[3];
-      int off = block_scan<256>(__builtin_popcount(any), s_scan, &npos);
-      uint32_t x = any;
-      while (x) {
-        const int bit = __builtin_ctz(x);
-        x &= x - 1;
-        int mask = 0;
+      int total;
+      int rank = block_scan<256>(cnt, s_scan, &total);
+      const int lo = split * kSlcSplit;
+      npos = min(kSlcSplit, total - lo);
+      if (rank < lo + kSlcSplit && rank + cnt > lo) {
+        for (int wi = w0; wi < w1; ++wi) {
+          uint32_t m[4];
+          uint32_t x = word(wi, m);
+          while (x) {
+            const int bit = __builtin_ctz(x);
+            x &= x - 1;
+            if (rank >= lo && rank < lo + kSlcSplit) {
+              int mask = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) mask |= (int)((m[w] >> bit) & 1u) << w;
-        s_list[off++] = (32 * wi + bit) | (mask << 24);
+              for (int w = 0; w < 4; ++w) mask |= (int)((m[w] >> bit) & 1u) << w;
+              s_list[rank - lo] = (32 * wi + bit) | (mask << 24);
+            }
+            ++rank;
+          }
+        }
       }
       __syncthreads();
     }
-    if (npos == 0) continue;
-    const int npair = (npos + 1) / 2;
+    const int npair = (max(npos, 0) + 1) / 2;
 
     // Position of entry i and the waves it concerns (all for window / compressed).
     auto entry = [&](int i, int& t, int& mask) {
@@ -888,8 +918,9 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
     dv = p.dv + (bgl * T + key) * DV;
     stride = 1;
   } else {
-    const int64_t rows = MODE == kSlc ? (int64_t)nbg * T : (int64_t)nbg * p.nc;
-    const int64_t row = (int64_t)blockIdx.y * rows + bgl * nkeys + key;
+    const int64_t row = MODE == kSlc
+                            ? ((int64_t)bg * p.slots_max + blockIdx.x) * 64 + (key - kw0)
+                            : (int64_t)blockIdx.y * nbg * p.nc + bgl * nkeys + key;
     float* base = (MODE == kSlc ? p.part_slc : p.part_cmp) + row * (DK + DV);
     dk = base;
     dv = base + DK;
@@ -924,10 +955,17 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p) {
   if (idx >= nrow * (W / 4)) return;
   const int64_t row = idx / (W / 4);
   const int c4 = (int)(idx - row * (W / 4)) * 4;
-  const float* src = (MODE == kSlc ? p.part_slc : p.part_cmp) + row * W + c4;
-  const int nparts = MODE == kSlc ? p.nqw : p.ncq;
-  f32x4_t s = *reinterpret_cast<const f32x4_t*>(src);
-  for (int c = 1; c < nparts; ++c) s += *reinterpret_cast<const f32x4_t*>(src + (int64_t)c * nrow * W);
+  f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (MODE == kSlc) {  // the key tile's split slots, in order
+    const int64_t bgr = row / p.T;
+    const int key = (int)(row - bgr * p.T), kt = key >> 6;
+    const int32_t* off = p.slc_off + bgr * (p.kraw + 1);
+    for (int sl = off[kt]; sl < off[kt + 1]; ++sl)
+      s += *reinterpret_cast<const f32x4_t*>(p.part_slc + ((bgr * p.slots_max + sl) * 64 + (key & 63)) * W + c4);
+  } else {
+    const float* src = p.part_cmp + row * W + c4;
+    for (int c = 0; c < p.ncq; ++c) s += *reinterpret_cast<const f32x4_t*>(src + (int64_t)c * nrow * W);
+  }
   if constexpr (MODE == kSlc) {
     float* dst = c4 < DK ? p.dk + row * DK + c4 : p.dv + row * DV + (c4 - DK);
     *reinterpret_cast<f32x4_t*>(dst) += s;
@@ -935,6 +973,48 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p) {
     float* dst = c4 < DK ? p.dkc + row * DK + c4 : p.dvc + row * DV + (c4 - DK);
     *reinterpret_cast<f32x4_t*>(dst) = s;
   }
+}
+
+// Selected branch, per (sequence-group, 64-key tile): the number of positions
+// that chose one of the tile's blocks (the union of its bitmap rows).
+__global__ __launch_bounds__(256) void bwd_slc_count_kernel(BwdParams p) {
+  __shared__ int s_scan[4];
+  const int nbg = p.B * p.H;
+  const int bg = (int)blockIdx.x % nbg, kt = (int)blockIdx.x / nbg;
+  const int kw0 = kt * 64;
+  int jw[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) jw[w] = (kw0 + 16 * w) / p.lsel;
+  const uint32_t* rows = p.bits + (int64_t)bg * p.nblk * p.nwords;
+  int cnt = 0;
+  for (int wi = ((jw[0] * p.lsel) >> 5) + (int)threadIdx.x; wi < p.nwords; wi += 256) {
+    uint32_t u = 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) u |= jw[w] < p.nblk ? rows[(int64_t)jw[w] * p.nwords + wi] : 0u;  // as the list
+    cnt += __builtin_popcount(u);
+  }
+  int total;
+  block_scan<256>(cnt, s_scan, &total);
+  if (threadIdx.x == 0) p.slc_cnt[(int64_t)bg * p.kraw + kt] = total;
+}
+
+// Per sequence-group: split slots of each key tile, ceil(count / kSlcSplit),
+// as an exclusive prefix off[0 .. kraw] (off[kraw] = the slots used).
+__global__ __launch_bounds__(256) void bwd_slc_scan_kernel(BwdParams p) {
+  __shared__ int s_scan[4];
+  const int bg = (int)blockIdx.x;
+  const int32_t* cnt = p.slc_cnt + (int64_t)bg * p.kraw;
+  int32_t* off = p.slc_off + (int64_t)bg * (p.kraw + 1);
+  int base = 0;
+  for (int k0 = 0; k0 < p.kraw; k0 += 256) {
+    const int kt = k0 + (int)threadIdx.x;
+    const int ns = kt < p.kraw ? (cnt[kt] + kSlcSplit - 1) / kSlcSplit : 0;
+    int tot;
+    const int ex = block_scan<256>(ns, s_scan, &tot);
+    if (kt < p.kraw) off[kt] = base + ex;
+    base += tot;
+  }
+  if (threadIdx.x == 0) off[p.kraw] = base;
 }
 
 __global__ __launch_bounds__(256) void bwd_bitmap_kernel(BwdParams p) {
@@ -983,8 +1063,9 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s, const PhaseEvents* ev
   const int kraw = (p.T + 63) / 64, kcmp = (p.nc + 63) / 64;
   constexpr int W4 = (DK + DV) / 4;
   hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kWin>), dim3((unsigned)(nbg * kraw)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kSlc>), dim3((unsigned)(nbg * kraw), (unsigned)p.nqw), dim3(256), 0, s,
-                     p);
+  hipLaunchKernelGGL(bwd_slc_count_kernel, dim3((unsigned)(nbg * kraw)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_slc_scan_kernel, dim3((unsigned)nbg), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<DK, DV, kSlc>), dim3((unsigned)p.slots_max, (unsigned)nbg), dim3(256), 0, s, p);
   const int64_t rraw = (int64_t)nbg * p.T * W4;
   hipLaunchKernelGGL((bwd_kv_reduce_kernel<DK, DV, kSlc>), dim3((unsigned)((rraw + 255) / 256)), dim3(256), 0, s, p);
   if (ev) hipEventRecord(ev->ev[2], s);

@@ -6,7 +6,7 @@
 namespace nsa {
 
 constexpr int kStatFloats = 48;      // statistics record of one (branch, position, group)
-constexpr int kBwdMaxParts = 8;      // key side: most partial sums per key (position ranges)
+constexpr int kSlcSplit = 512;       // selected-branch key side: positions per workgroup
 constexpr int kCbwdSplit = 8;
 constexpr int kGateChunks = 64;      // gate-network gradients: position ranges summed in order        // compression backward: contraction ranges of the dW product
 
@@ -18,7 +18,6 @@ struct BwdParams {
   int nc;                            // compressed blocks per sequence
   int nqt;                           // query workgroups per (b, g): ceil(T / 4)
   int nblk, nwords;                  // selection blocks ceil(T / lsel); 32-position words ceil(T / 32)
-  int qwords, nqw;                   // selected-branch key side: words per workgroup, workgroups per key tile
   int qchunk, ncq;                   // compressed-branch key side: positions per workgroup, workgroups per tile
   const uint16_t* q;                 // [B, T, Hq, DK]
   const uint16_t* k;                 // [B, H, T, DK]
@@ -43,7 +42,10 @@ struct BwdParams {
   float* stat;                       // workspace [3, B, T, H, kStatFloats]: per branch and group, the
                                      // heads' lse (log2 units) [16] | g_c (dO . o_c) [16] | g_c [16]
   uint32_t* bits;                    // workspace [B, H, nblk, nwords]: position t selected block j
-  float* part_slc;                   // workspace [nqw, B, H, T, DK + DV]: selected-branch partials
+  float* part_slc;                   // workspace [B*H, slots_max, 64, DK + DV]: selected-branch partials
+  int kraw, slots_max;               // 64-key tiles per sequence; selected-branch split slots per (b, g)
+  int32_t* slc_cnt;                  // workspace [B*H, kraw]: positions per key tile
+  int32_t* slc_off;                  // workspace [B*H, kraw + 1]: first split slot per key tile
   float* part_cmp;                   // workspace [ncq, B, H, nc, DK + DV]: compressed-branch partials
 };
 

@@ -207,12 +207,14 @@ def test_backward_workspace_sizes_and_validation():
     dims, cfg = _dims(batch=1), _cfg()
     T = 32768
     # statistics records [3, 1, T, 4, 48] fp32, bitmap [1, 4, T/64, T/32] uint32, selected-branch
-    # partials [8, 1, 4, T, 320] fp32 (1024 words in 8 ranges of 128), compressed-branch partials
-    # [32, 1, 4, nc, 320] fp32 (ranges of 1024 positions), gate-gradient partials [64, 64, 3, 193] fp32
+    # partials [4, slots, 64, 320] fp32, compressed-branch partials [32, 1, 4, nc, 320] fp32 (ranges
+    # of 1024 positions), tile counts and slot offsets int32, gate-gradient partials [64, 64, 3, 193]
     nc = (T - 32) // 16 + 1
     r256 = lambda x: -(-x // 256) * 256
+    slots = 512 + T * 16 // 512  # key tiles + positions x n_sel / 512
     assert N.nsa_prefill_bwd_workspace_size(dims, cfg, T) == (3 * T * 4 * 48 * 4 + 4 * 512 * 1024 * 4 +
-                                                             8 * 4 * T * 320 * 4 + r256(32 * 4 * nc * 320 * 4) +
+                                                             4 * slots * 64 * 320 * 4 + r256(32 * 4 * nc * 320 * 4) +
+                                                             r256(4 * 512 * 4) + r256(4 * 513 * 4) +
                                                              r256(64 * 64 * 3 * 193 * 4))
     assert N.nsa_compress_bwd_workspace_size(dims, cfg, T, 0) == (r256(4 * nc * 32 * 192 * 4) + 64 * 192 * 4 +
                                                               8 * 32 * 192 * 192 * 4)
