@@ -93,3 +93,20 @@ def test_prefill_lse_out(wl_name, T, seed):
                 worst = max(worst, float(np.abs(got[fin] - want[fin]).max()))
     print(f"lse max-abs error {worst:.2e}")
     assert worst <= LSE_ABS
+
+
+@pytest.mark.parametrize("wl_name,T,batch", [
+    ("tiny_prefill_512", 1, 1),     # one position: window and selection hold only token 0
+    ("tiny_prefill_512", 17, 1),    # shorter than one compression block: no compressed key
+    ("tiny_prefill_512", 33, 1),    # the first compressed block completes at t = l - 1
+    ("tiny_prefill_512", 65, 1),    # one position past a selection block and a 16-position tile
+    ("tiny_prefill_512", 130, 2),   # two sequences, ragged last tile
+    ("prefill_32k", 1, 1),
+    ("prefill_32k", 47, 1),
+    ("prefill_32k", 200, 2),
+])
+def test_prefill_edge_lengths(wl_name, T, batch):
+    case = I.generate(I.workload(wl_name, seq_len=T, batch=batch), 11)
+    print(f"[prefill edge] {wl_name} T={T} batch={batch}", flush=True)
+    out, sel = U.run_prefill(case)
+    _check_rows(case, out, sel, range(T))
