@@ -363,9 +363,9 @@ nsa_status_t nsa_compress_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, i
                               int32_t which, const uint16_t* x, const uint16_t* w, const uint16_t* pe,
                               const float* dy, float* dx, float* dw, float* dpe,
                               void* workspace, size_t workspace_bytes, void* stream);
-/* Workspace bytes for nsa_compress_bwd (host-only): dX [B*Hkv*nc, l*D] fp32,
- * 64 x D fp32 partial column sums and 8 partial products [8, l*D, D] fp32 of dw,
- * each part rounded up to 256 bytes. */
+/* Workspace bytes for nsa_compress_bwd (host-only): 64 x D fp32 partial column
+ * sums and 8 partial products [8, l*D, D] fp32 of dw, each part rounded up to
+ * 256 bytes (independent of seq_len). */
 nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                              int64_t seq_len, int32_t which, size_t* bytes);
 

@@ -605,12 +605,10 @@ BwdWs bwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T) {
   return w;
 }
 
-// Compression-backward workspace: dX [B*Hkv*nc, l*D] fp32, then 64 column-sum
-// partials [64, D], then the dW product's split partials [8, l*D, D].
-size_t cbwd_ws(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, int D) {
-  const int64_t nc = n_compressed(T, cfg->l, cfg->d);
-  return align256((size_t)dims->batch * dims->num_kv_heads * (size_t)nc * cfg->l * D * 4) +
-         align256((size_t)64 * D * 4) + align256((size_t)nsa::kCbwdSplit * cfg->l * D * D * 4);
+// Compression-backward workspace: 64 column-sum partials [64, D], then the dW
+// product's split partials [8, l*D, D].
+size_t cbwd_ws(const nsa_config_t* cfg, int D) {
+  return align256((size_t)64 * D * 4) + align256((size_t)nsa::kCbwdSplit * cfg->l * D * D * 4);
 }
 
 nsa_status_t check_cbwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t T, int32_t which) {
@@ -618,9 +616,8 @@ nsa_status_t check_cbwd(const nsa_dims_t* dims, const nsa_config_t* cfg, int64_t
   if (st != NSA_SUCCESS) return st;
   if (which != 0 && which != 1) return fail(NSA_ERROR_INVALID_VALUE, "which must be 0 (keys) or 1 (values)");
   if (T < 1) return fail(NSA_ERROR_INVALID_VALUE, "seq_len must be >= 1");
-  const int D = which == 0 ? dims->d_k : dims->d_v;
-  const int64_t rows = (int64_t)dims->batch * dims->num_kv_heads * n_compressed(T, cfg->l, cfg->d);
-  if ((rows + 63) / 64 > 65535 || (int64_t)dims->batch * dims->num_kv_heads * T * D / 256 > INT32_MAX)
+  if ((int64_t)dims->batch * dims->num_kv_heads > 65535 ||
+      (int64_t)dims->batch * dims->num_kv_heads * n_compressed(T, cfg->l, cfg->d) > INT32_MAX)
     return fail(NSA_ERROR_UNSUPPORTED, "compression backward launch too large");
   return NSA_SUCCESS;
 }
@@ -725,7 +722,7 @@ nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_c
   nsa_status_t st = check_cbwd(dims, cfg, seq_len, which);
   if (st != NSA_SUCCESS) return st;
   if (!bytes) return fail(NSA_ERROR_INVALID_VALUE, "bytes is NULL");
-  *bytes = cbwd_ws(dims, cfg, seq_len, which == 0 ? dims->d_k : dims->d_v);
+  *bytes = cbwd_ws(cfg, which == 0 ? dims->d_k : dims->d_v);
   return ok();
 }
 
@@ -738,7 +735,7 @@ nsa_status_t nsa_compress_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, i
   if (!x || !w || !pe || !dx || !dw || !dpe || (nc > 0 && !dy))
     return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
   const int D = which == 0 ? dims->d_k : dims->d_v;
-  const size_t need = cbwd_ws(dims, cfg, seq_len, D);
+  const size_t need = cbwd_ws(cfg, D);
   if (!workspace || workspace_bytes < need)
     return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -757,10 +754,8 @@ nsa_status_t nsa_compress_bwd(const nsa_dims_t* dims, const nsa_config_t* cfg, i
   p.dx = dx;
   p.dw = dw;
   p.dpe = dpe;
-  p.dX = reinterpret_cast<float*>(ws);
-  p.part = reinterpret_cast<float*>(ws + align256((size_t)p.BH * (size_t)nc * cfg->l * D * 4));
-  p.dwpart = reinterpret_cast<float*>(ws + align256((size_t)p.BH * (size_t)nc * cfg->l * D * 4) +
-                                      align256((size_t)64 * D * 4));
+  p.part = reinterpret_cast<float*>(ws);
+  p.dwpart = reinterpret_cast<float*>(ws + align256((size_t)64 * D * 4));
   hipError_t e = nsa::launch_compress_bwd(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "compression backward launch");
   return ok();

@@ -9,103 +9,188 @@
 // [i*d, i*d + l) and Y_i = X_i W with X_i = (x[i*d : i*d+l] + PE) flattened.
 //
 // With that forward, summing over every sequence, head and block:
-//   dX_i   = dY_i W^T                                (one fp32 GEMM)
-//   dx[t] += sum over the blocks i that cover t of dX_i[t - i*d]
+//   dX_i   = dY_i W^T
+//   dx[t] += sum over the blocks i that cover t of dX_i[t - i*d]   (fused: no dX)
 //   dW     = sum_i X_i^T dY_i = sum_i x-rows^T dY_i + PE (x) s,  s = sum_i dY_i
 //   dPE    = sum_i dX_i = s W^T
-// All sums run in fp32 in a fixed order (no atomics), so results are reproducible.
+// The two products run on bf16 MFMAs, dY entering as bf16 high + low parts (x and
+// W are bf16 already), with fp32 accumulation.  All sums run in a fixed order (no
+// atomics), so results are reproducible.
 #include "nsa_train.hpp"
 #include "nsa_device.hpp"
 
 namespace nsa {
 namespace {
 
-constexpr int kGT = 64;  // output tile edge
-constexpr int kGK = 16;  // contraction chunk
-
-// Operand views for the two GEMMs.  at(m, k) / at(k, n) give an element; kContig
-// says whether consecutive k are adjacent in memory (it picks the load order).
-struct DyRowsA {  // A(m = (bh, i), k = o) = dY[m][o]
-  const float* p;
-  int D;
-  static constexpr bool kContig = true;
-  __device__ float at(int64_t m, int64_t k) const { return p[m * D + k]; }
-};
-struct WRowsB {  // B(k = o, n = (j, c)) = W[(j, c)][o]
-  const uint16_t* p;
-  int D;
-  static constexpr bool kContig = true;
-  __device__ float at(int64_t k, int64_t n) const { return bf16_to_f32(p[n * D + k]); }
-};
-struct XBlocksA {  // A(m = (j, c), k = (bh, i)) = x[bh][i*d + j][c]
-  const uint16_t* p;
-  int64_t T;
-  int D, d, nc;
-  static constexpr bool kContig = false;
-  __device__ float at(int64_t m, int64_t k) const {
-    const int64_t bh = k / nc, i = k - bh * nc;
-    return bf16_to_f32(p[(bh * T + i * d) * D + m]);
+// fp32 values to bf16 high and low parts: hi = bf16(v), lo = bf16(v - hi).  Two
+// MFMAs against the same bf16 operand then give the fp32 product to about 2^-16
+// relative, in fp32 accumulation.
+__device__ __forceinline__ void split8(const f32x4_t& v0, const f32x4_t& v1, u32x4_t& hi, u32x4_t& lo) {
+  const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+    hi[e] = h;
+    lo[e] = pack_bf16x2(v[2 * e] - bf16_lo(h), v[2 * e + 1] - bf16_hi(h));
   }
-};
-struct DyColsB {  // B(k = (bh, i), n = o) = dY[k][o]
-  const float* p;
-  int D;
-  static constexpr bool kContig = false;
-  __device__ float at(int64_t k, int64_t n) const { return p[k * D + n]; }
-};
+}
 
-// C[M x N] = A . B (fp32), 64 x 64 tiles, 4 x 4 outputs per thread.  With
-// gridDim.z > 1 each z takes the contraction range [z*kz, (z+1)*kz) and writes
-// its partial product to C + z*cz.
-template <class OA, class OB>
-__global__ __launch_bounds__(256) void cbwd_gemm_kernel(int64_t M, int64_t N, int64_t K, OA a, OB bm, float* C,
-                                                        int64_t ldc, int64_t kz, int64_t cz) {
-  __shared__ float As[kGK][kGT + 4];
-  __shared__ float Bs[kGK][kGT + 4];
-  const int tid = threadIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.y * kGT, n0 = (int64_t)blockIdx.x * kGT;
-  const int tx = tid & 15, ty = tid >> 4;
-  const int64_t kb = (int64_t)blockIdx.z * kz, ke = std::min<int64_t>(K, kb + kz);
-  C += (int64_t)blockIdx.z * cz;
-  float acc[4][4] = {};
-  for (int64_t k0 = kb; k0 < ke; k0 += kGK) {
+// dx = the compression's input gradient, accumulated into dx.  Token t = a*d + j
+// (0 <= j < d) lies in the blocks a - u, u = 0 .. R-1 (R = l/d), at in-block row
+// j + u*d, so for one j the tokens a*d + j are the rows of one product over
+// (u, o):   dx[a*d + j][c] += sum_u sum_o dY[a - u][o] W[(j + u*d)*D + c][o].
+// Workgroup: one (bh, j), 4 waves x 32 rows a, all D columns.  A = dY rows
+// (high + low bf16 parts), B = rows of W, contiguous in o.
+template <int D>
+__global__ __launch_bounds__(256) void cbwd_dx_kernel(const float* dy, const uint16_t* w, float* dx, int64_t T, int d,
+                                                      int R, int nc, int na) {
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, lr = lane & 15, wave = threadIdx.x >> 6;
+  const int j = blockIdx.y;
+  const int64_t bh = blockIdx.z;
+  const int a0 = blockIdx.x * 128 + wave * 32;
+  const float* dyb = dy + bh * nc * D;
+  f32x4_t acc[2][NT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int mm, kk;
-      if (OA::kContig) { mm = tid >> 2; kk = (tid & 3) * 4 + r; } else { mm = tid & 63; kk = (tid >> 6) + 4 * r; }
-      const int64_t m = m0 + mm, k = k0 + kk;
-      As[kk][mm] = (m < M && k < ke) ? a.at(m, k) : 0.f;
-      int nn, kb2;
-      if (OB::kContig) { nn = tid >> 2; kb2 = (tid & 3) * 4 + r; } else { nn = tid & 63; kb2 = (tid >> 6) + 4 * r; }
-      const int64_t n = n0 + nn, k2 = k0 + kb2;
-      Bs[kb2][nn] = (n < N && k2 < ke) ? bm.at(k2, n) : 0.f;
-    }
-    __syncthreads();
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int kk = 0; kk < kGK; ++kk) {
-      float av[4], bv[4];
+    for (int ct = 0; ct < NT; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < R; ++u) {
+    const uint16_t* wr = w + (int64_t)(j + u * d) * D * D;
+    for (int o0 = 0; o0 < D; o0 += 32) {
+      u32x4_t ahi[2], alo[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        av[u] = As[kk][ty * 4 + u];
-        bv[u] = Bs[kk][tx * 4 + u];
+      for (int rt = 0; rt < 2; ++rt) {
+        const int i = a0 + 16 * rt + lr - u;  // this lane's row's block
+        f32x4_t v0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (i >= 0 && i < nc) {
+          const f32x4_t* src = reinterpret_cast<const f32x4_t*>(dyb + (int64_t)i * D + o0 + 8 * lg);
+          v0 = src[0];
+          v1 = src[1];
+        }
+        split8(v0, v1, ahi[rt], alo[rt]);
       }
+      u32x4_t bw[NT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int ct = 0; ct < NT; ++ct) bw[ct] = ld16(wr + (int64_t)(16 * ct + lr) * D + o0 + 8 * lg);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          acc[rt][ct] = mfma_bf16(ahi[rt], bw[ct], acc[rt][ct]);
+          acc[rt][ct] = mfma_bf16(alo[rt], bw[ct], acc[rt][ct]);
+        }
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int a = a0 + 16 * rt + 4 * lg + i;
+      const int64_t t = (int64_t)a * d + j;
+      if (a >= na || t >= T) continue;
+      float* dst = dx + (bh * T + t) * D + lr;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) dst[16 * ct] += acc[rt][ct][i];
+    }
+}
+
+// dW without the position-encoding term, per in-block row r:
+//   dW[r*D + c][o] = sum over (bh, i) of x[bh][i*d + r][c] dY[bh][i][o],
+// a product whose contraction runs over rows of both operands.  Workgroup: one
+// r and one of the split contraction ranges (blockIdx.y), written to its own
+// partial.  Each 32-row chunk is staged in LDS transposed (channel-major, 40
+// elements per channel row, so the 16-byte operand reads of 16 lanes hit
+// distinct banks): x as bf16, dY as bf16 high and low parts.  Wave w owns
+// channel tiles CT*w .. CT*w + CT-1 and every o tile.
+constexpr int kXS = 40;  // LDS row stride of the transposed chunks (elements)
+template <int D>
+__global__ __launch_bounds__(256) void cbwd_dw_kernel(const uint16_t* x, const float* dy, float* part, int64_t T,
+                                                      int d, int nc, int64_t K, int64_t kz) {
+  constexpr int NO = D / 16, CT = NO / 4;
+  constexpr int XC = 32 * D / 8 / 256, YC = 32 * D / 4 / 256;  // 16-byte chunks per thread
+  static_assert(XC * 256 * 8 == 32 * D && YC * 256 * 4 == 32 * D, "chunks per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t xt[D * kXS];
+  __shared__ __attribute__((aligned(16))) uint16_t yh[D * kXS];
+  __shared__ __attribute__((aligned(16))) uint16_t yl[D * kXS];
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15, wave = tid >> 6;
+  const int r = blockIdx.x;
+  const int64_t kb = (int64_t)blockIdx.y * kz, ke = std::min<int64_t>(K, kb + kz);
+  u32x4_t xr[XC];
+  f32x4_t yr[YC];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < XC; ++q) {
+      const int e = tid + 256 * q, kk = e / (D / 8), cc = (e - kk * (D / 8)) * 8;
+      const int64_t k = k0 + kk;
+      xr[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (k < ke) {
+        const int64_t bh = k / nc, i = k - bh * nc;
+        xr[q] = ld16(x + (bh * T + i * d + r) * D + cc);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < YC; ++q) {
+      const int e = tid + 256 * q, kk = e / (D / 4), oo = (e - kk * (D / 4)) * 4;
+      const int64_t k = k0 + kk;
+      yr[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (k < ke) yr[q] = *reinterpret_cast<const f32x4_t*>(dy + k * D + oo);
+    }
+  };
+  f32x4_t acc[CT][NO];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int o = 0; o < NO; ++o) acc[c][o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (kb < ke) load(kb);
+  for (int64_t k0 = kb; k0 < ke; k0 += 32) {
+    __syncthreads();  // the previous chunk's operand reads are done
+#pragma unroll
+    for (int q = 0; q < XC; ++q) {
+      const int e = tid + 256 * q, kk = e / (D / 8), cc = (e - kk * (D / 8)) * 8;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        xt[(cc + 2 * m) * kXS + kk] = (uint16_t)(xr[q][m] & 0xFFFFu);
+        xt[(cc + 2 * m + 1) * kXS + kk] = (uint16_t)(xr[q][m] >> 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < YC; ++q) {
+      const int e = tid + 256 * q, kk = e / (D / 4), oo = (e - kk * (D / 4)) * 4;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float v = yr[q][m];
+        const uint32_t h = f32_to_bf16(v);
+        yh[(oo + m) * kXS + kk] = (uint16_t)h;
+        yl[(oo + m) * kXS + kk] = (uint16_t)f32_to_bf16(v - __uint_as_float(h << 16));
+      }
     }
     __syncthreads();
-  }
+    if (k0 + 32 < ke) load(k0 + 32);  // next chunk in flight during the products
+    u32x4_t af[CT];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t m = m0 + ty * 4 + u;
-    if (m >= M) continue;
+    for (int c = 0; c < CT; ++c)
+      af[c] = *reinterpret_cast<const u32x4_t*>(xt + (16 * (CT * wave + c) + lr) * kXS + 8 * lg);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t n = n0 + tx * 4 + v;
-      if (n < N) C[m * ldc + n] = acc[u][v];
+    for (int o = 0; o < NO; ++o) {
+      const u32x4_t yhi = *reinterpret_cast<const u32x4_t*>(yh + (16 * o + lr) * kXS + 8 * lg);
+      const u32x4_t ylo = *reinterpret_cast<const u32x4_t*>(yl + (16 * o + lr) * kXS + 8 * lg);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        acc[c][o] = mfma_bf16(af[c], yhi, acc[c][o]);
+        acc[c][o] = mfma_bf16(af[c], ylo, acc[c][o]);
+      }
     }
   }
+  float* dst = part + (int64_t)blockIdx.y * ((int64_t)gridDim.x * D * D) + (int64_t)r * D * D;
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = 16 * (CT * wave + c) + 4 * lg + i;
+#pragma unroll
+      for (int o = 0; o < NO; ++o) dst[(int64_t)ch * D + 16 * o + lr] = acc[c][o][i];
+    }
 }
 
 // dw = sum of the split-contraction partials, in order.
@@ -152,50 +237,35 @@ __global__ __launch_bounds__(256) void cbwd_pe_kernel(const float* part, const u
   dpe[m] = acc;
 }
 
-// dx[bh][t][c] += sum over covering blocks i of dX[bh*nc + i][(t - i*d)*D + c].
-__global__ __launch_bounds__(256) void cbwd_fold_kernel(const float* dX, float* dx, int64_t BH, int64_t T, int D,
-                                                        int l, int d, int nc) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= BH * T * D) return;
-  const int c = (int)(idx % D);
-  const int64_t r = idx / D;
-  const int t = (int)(r % T);
-  const int64_t bh = r / T;
-  const int ilo = t >= l ? (t - l) / d + 1 : 0;  // first block with i*d + l > t
-  const int ihi = std::min(nc - 1, t / d);
-  float s = 0.f;
-  for (int i = ilo; i <= ihi; ++i) s += dX[(bh * nc + i) * (int64_t)l * D + (int64_t)(t - i * d) * D + c];
-  dx[idx] += s;
-}
-
 }  // namespace
+
+template <int D>
+static void launch_cbwd_t(const CompressBwdParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.BH * p.nc;
+  if (rows > 0) {
+    const int R = p.l / p.d, na = p.nc + R - 1;
+    hipLaunchKernelGGL(cbwd_dx_kernel<D>, dim3((unsigned)((na + 127) / 128), (unsigned)p.d, (unsigned)p.BH), dim3(256),
+                       0, s, p.dy, p.w, p.dx, p.T, p.d, R, p.nc, na);
+  }
+  // kCbwdSplit contraction ranges of whole 32-row chunks (an empty range writes zeros)
+  const int64_t kz = std::max<int64_t>(32, ((rows + kCbwdSplit - 1) / kCbwdSplit + 31) / 32 * 32);
+  hipLaunchKernelGGL(cbwd_dw_kernel<D>, dim3((unsigned)p.l, kCbwdSplit), dim3(256), 0, s, p.x, p.dy, p.dwpart, p.T,
+                     p.d, p.nc > 0 ? p.nc : 1, rows, kz);
+}
 
 hipError_t launch_compress_bwd(const CompressBwdParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.BH * p.nc;
   const int lD = p.l * p.D;
-  if (rows > 0) {
-    hipLaunchKernelGGL(cbwd_colsum_part_kernel, dim3((unsigned)((p.D + 255) / 256), kSumChunks), dim3(256), 0, s,
-                       p.dy, rows, p.D, p.part);
-    // dX = dY W^T  [rows x lD]
-    hipLaunchKernelGGL((cbwd_gemm_kernel<DyRowsA, WRowsB>),
-                       dim3((unsigned)((lD + kGT - 1) / kGT), (unsigned)((rows + kGT - 1) / kGT)), dim3(256), 0, s,
-                       rows, (int64_t)lD, (int64_t)p.D, DyRowsA{p.dy, p.D}, WRowsB{p.w, p.D}, p.dX, (int64_t)lD,
-                       (int64_t)p.D, (int64_t)0);
-    const int64_t nfold = (int64_t)p.BH * p.T * p.D;
-    hipLaunchKernelGGL(cbwd_fold_kernel, dim3((unsigned)((nfold + 255) / 256)), dim3(256), 0, s, p.dX, p.dx,
-                       (int64_t)p.BH, p.T, p.D, p.l, p.d, p.nc);
-  } else {
-    hipLaunchKernelGGL(cbwd_colsum_part_kernel, dim3((unsigned)((p.D + 255) / 256), kSumChunks), dim3(256), 0, s,
-                       p.dy, (int64_t)0, p.D, p.part);
+  hipLaunchKernelGGL(cbwd_colsum_part_kernel, dim3((unsigned)((p.D + 255) / 256), kSumChunks), dim3(256), 0, s, p.dy,
+                     rows, p.D, p.part);
+  switch (p.D) {
+    case 64: launch_cbwd_t<64>(p, s); break;
+    case 128: launch_cbwd_t<128>(p, s); break;
+    case 192: launch_cbwd_t<192>(p, s); break;
+    default: return hipErrorInvalidValue;
   }
-  // dW = sum x-rows^T dY  [lD x D]  (zero when there is no block): kCbwdSplit
-  // contraction ranges of whole 16-row chunks, then their sum in order.
-  const int64_t kz = ((rows + kCbwdSplit - 1) / kCbwdSplit + kGK - 1) / kGK * kGK;
+  // dW = sum of the split partials, in order, then the position-encoding terms
   const int64_t nw = (int64_t)lD * p.D;
-  hipLaunchKernelGGL((cbwd_gemm_kernel<XBlocksA, DyColsB>),
-                     dim3((unsigned)((p.D + kGT - 1) / kGT), (unsigned)((lD + kGT - 1) / kGT), kCbwdSplit), dim3(256),
-                     0, s, (int64_t)lD, (int64_t)p.D, rows, XBlocksA{p.x, p.T, p.D, p.d, p.nc > 0 ? p.nc : 1},
-                     DyColsB{p.dy, p.D}, p.dwpart, (int64_t)p.D, kz > 0 ? kz : (int64_t)kGK, nw);
   hipLaunchKernelGGL(cbwd_sum_parts_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, p.dwpart,
                      kCbwdSplit, nw, p.dw);
   hipLaunchKernelGGL(cbwd_pe_kernel, dim3((unsigned)((lD + 255) / 256)), dim3(256), 0, s, p.part, p.w, p.pe, lD, p.D,

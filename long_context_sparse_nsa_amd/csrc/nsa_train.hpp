@@ -60,7 +60,6 @@ struct CompressBwdParams {
   float* dx;                         // [BH, T, D], accumulated
   float* dw;                         // [l*D, D]
   float* dpe;                        // [l, D]
-  float* dX;                         // workspace [BH*nc, l*D]
   float* part;                       // workspace [64, D]
   float* dwpart;                     // workspace [kCbwdSplit, l*D, D]
 };
