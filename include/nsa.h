@@ -351,9 +351,10 @@ nsa_status_t nsa_prefill_bwd_workspace_size(const nsa_dims_t* dims, const nsa_co
  *   dx[t] += sum over the blocks i covering t of (dy_i w^T)[t - i*d]   (added)
  *   dw     = sum_i X_i^T dy_i                                           (written)
  *   dpe    = sum_i dy_i w^T                                             (written)
- * summed over all sequences and heads, in fp32, in a fixed order (run-to-run
- * identical).  The bf16 rounding of the forward's compressed rows is taken as
- * the identity.
+ * summed over all sequences and heads with fp32 accumulation in a fixed order
+ * (run-to-run identical); in the products dy enters as bf16 high + low parts
+ * (about 2^-16 relative).  The bf16 rounding of the forward's compressed rows is
+ * taken as the identity.
  *   x      bf16 raw rows; w bf16 [l*D, D]; pe bf16 [l, D]
  *   dy     float32 [B, Hkv, nc, D] (e.g. nsa_prefill_bwd's dk_cmp); may be NULL when T < l
  *   dx     float32 [B, Hkv, T, D], accumulated into (e.g. nsa_prefill_bwd's dk)
