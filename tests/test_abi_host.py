@@ -245,3 +245,14 @@ def test_backward_workspace_sizes_and_validation():
     assert cbwd(x=None) == A.NSA_ERROR_INVALID_VALUE
     assert cbwd(dy=None) == A.NSA_ERROR_INVALID_VALUE
     assert cbwd(nb=cneed - 1) == A.NSA_ERROR_WORKSPACE
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point fails loudly: there is no
+    CPU path to fall back on."""
+    monkeypatch.setattr(A, "_LIB", None)
+    monkeypatch.setattr(A, "lib_path", lambda: str(tmp_path / "libnsa_absent.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        A.load_library()
+    with pytest.raises(RuntimeError, match="not found"):
+        N.nsa_decode_workspace_size(_dims(), _cfg(), 512)
