@@ -685,13 +685,15 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
   u32x4_t qf[KT];
   load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
   if (p.wgate) {  // gate network: 3 G dot products of the query with a weight row, four lanes each
-    const int pr = tid >> 2, pt = tid & 3;
-    const int pc = pr < 3 * p.G ? pr : 0;
-    const int hq = g * p.G + pc / 3, br = pc % 3;
-    float z = gate_dot_quarter<DK>(p.q + ((size_t)b * p.Hq + hq) * DK, p.wgate + ((size_t)hq * 3 + br) * DK, pt);
-    z += __shfl_xor(z, 1);
-    z += __shfl_xor(z, 2);
-    if (pr < 3 * p.G && pt == 0) s_gate[pr / 3][br] = gate_sigmoid(z + (p.bgate ? p.bgate[hq * 3 + br] : 0.f));
+    for (int e0 = 0; e0 < 12 * p.G; e0 += NTH) {  // one pass when NTH >= 12 G
+      const int pr = (e0 + tid) >> 2, pt = tid & 3;
+      const int pc = pr < 3 * p.G ? pr : 0;
+      const int hq = g * p.G + pc / 3, br = pc % 3;
+      float z = gate_dot_quarter<DK>(p.q + ((size_t)b * p.Hq + hq) * DK, p.wgate + ((size_t)hq * 3 + br) * DK, pt);
+      z += __shfl_xor(z, 1);
+      z += __shfl_xor(z, 2);
+      if (pr < 3 * p.G && pt == 0) s_gate[pr / 3][br] = gate_sigmoid(z + (p.bgate ? p.bgate[hq * 3 + br] : 0.f));
+    }
   } else {
     const float gv = tid < 3 * p.G ? p.gates[((size_t)b * p.Hq + (size_t)g * p.G) * 3 + tid] : 0.f;
     if (tid < 3 * p.G) s_gate[tid / 3][tid % 3] = gv;
