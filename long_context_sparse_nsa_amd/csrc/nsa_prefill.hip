@@ -511,8 +511,15 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
 // Kernel 2: selected branch over the union of the tile's selected blocks.
 // ROWS keys are used per step: a whole block for l' = 32 or 64, half a block
 // for l' = 128, and for l' = 16 the block plus 16 masked rows.
+#ifndef NSA_PF_SEL_WAVES
+#define NSA_PF_SEL_WAVES 8
+#endif
+constexpr int kSelWaves = NSA_PF_SEL_WAVES;  // waves of the selected-branch workgroup
+constexpr int kSelQ = kTileQ / kSelWaves;    // positions per wave
+constexpr int kSelThreads = 64 * kSelWaves;
+
 template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p) {
   using SH = PfShape<DK, DV>;
   constexpr int KT = SH::KT, VC = SH::VC;
 #ifndef NSA_PF_SEL_ROWS
@@ -525,13 +532,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > RMAX ? RMAX : LSEL);
   constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
   constexpr int NBUF = NSA_PF_SEL_NBUF;      // NBUF - 1 steps in flight
-  using SO = StageOffsets<DK, DV, ROWS, kWaves>;
+  using SO = StageOffsets<DK, DV, ROWS, kSelWaves>;
   constexpr int NLD = SO::kMinCopiesKV;
   constexpr int kStepBytes = SO::kKBytes + SO::kVBytes;
   __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][kStepBytes];
   __shared__ uint32_t s_mask[kPfMaxBlocks];  // per block: bit q set if position t0+q chose it
   __shared__ uint32_t s_list[kPfMaxBlocks];  // the union, ascending: block id << 16 | mask
-  __shared__ int s_scan[kWaves];
+  __shared__ int s_scan[kSelWaves];
   __shared__ int s_nu;
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
@@ -547,13 +554,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
 
   // ---- g_slc from the gate network (when given) for this lane's head lr and
   // both of its positions, before any other load
-  float gsl[kWaveQ];
+  float gsl[kSelQ];
   if (p.wgate) {
     const int hq = g * p.G + (lr < p.G ? lr : 0);
     const uint16_t* wrow = p.wgate + ((size_t)hq * 3 + 1) * DK;
 #pragma unroll
-    for (int q = 0; q < kWaveQ; ++q) {
-      const int tt = min(t0 + kWaveQ * wave + q, T - 1);
+    for (int q = 0; q < kSelQ; ++q) {
+      const int tt = min(t0 + kSelQ * wave + q, T - 1);
       const float z = sum_over_groups_swap(
           gate_dot_quarter<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + hq) * DK, wrow, lg));
       gsl[q] = gate_sigmoid(z + (p.bgate ? p.bgate[hq * 3 + 1] : 0.f));
@@ -561,9 +568,9 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   }
 
   // ---- union of the tile's selections
-  for (int j = tid; j <= Jtile; j += kThreads) s_mask[j] = 0u;
+  for (int j = tid; j <= Jtile; j += kSelThreads) s_mask[j] = 0u;
   __syncthreads();
-  for (int e = tid; e < kTileQ * p.n; e += kThreads) {
+  for (int e = tid; e < kTileQ * p.n; e += kSelThreads) {
     const int q = e / p.n;
     if (t0 + q < T) {
       const int j = p.sel[(((int64_t)b * T + t0 + q) * p.H + g) * p.n + (e - q * p.n)];
@@ -572,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   }
   __syncthreads();
   {
-    constexpr int PER = kPfMaxBlocks / kThreads;
+    constexpr int PER = kPfMaxBlocks / kSelThreads;
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
       cnt += (j <= Jtile && s_mask[j] != 0u) ? 1 : 0;
     }
     int total;
-    int pos = block_scan<kThreads>(cnt, s_scan, &total);
+    int pos = block_scan<kSelThreads>(cnt, s_scan, &total);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = tid * PER + k;
@@ -591,15 +598,15 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
   __syncthreads();
   const int nsteps = s_nu * SPB;
 
-  int tq[kWaveQ];
-  bool act[kWaveQ];
-  u32x4_t qf[kWaveQ][KT];
-  f32x4_t acc[kWaveQ][VC];
-  f32x4_t lsum[kWaveQ];
-  float mref[kWaveQ];
+  int tq[kSelQ];
+  bool act[kSelQ];
+  u32x4_t qf[kSelQ][KT];
+  f32x4_t acc[kSelQ][VC];
+  f32x4_t lsum[kSelQ];
+  float mref[kSelQ];
 #pragma unroll
-  for (int q = 0; q < kWaveQ; ++q) {
-    tq[q] = t0 + kWaveQ * wave + q;
+  for (int q = 0; q < kSelQ; ++q) {
+    tq[q] = t0 + kSelQ * wave + q;
     act[q] = tq[q] < T;
     const int tt = act[q] ? tq[q] : T - 1;
     load_q_frags<DK>(p.q + (((int64_t)b * T + tt) * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf[q]);
@@ -639,13 +646,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
     const char* kt = s_buf[st % NBUF];
     const char* vt = s_buf[st % NBUF] + SO::kKBytes;
     const uint32_t ent = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_list[st / SPB]);
-    const uint32_t mine = (ent >> (kWaveQ * wave)) & ((1u << kWaveQ) - 1u);
+    const uint32_t mine = (ent >> (kSelQ * wave)) & ((1u << kSelQ) - 1u);
     if (mine == 0u) continue;
     const int jblk = (int)(ent >> 16);
     const int x0 = jblk * LSEL + (st % SPB) * ROWS;
     const int xend = (jblk + 1) * LSEL;  // first row past the block
 #pragma unroll
-    for (int q = 0; q < kWaveQ; ++q) {
+    for (int q = 0; q < kSelQ; ++q) {
       if (!((mine >> q) & 1u)) continue;
       f32x4_t s[MT];
 #pragma unroll
@@ -695,7 +702,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_sel_kernel(PrefillParams p) {
 
   // ---- out = bf16(acc_in + g_slc * o_slc)
 #pragma unroll
-  for (int q = 0; q < kWaveQ; ++q) {
+  for (int q = 0; q < kSelQ; ++q) {
     const float lt = __shfl(lsum[q][0], lr);
     if (!act[q] || lr >= p.G) continue;
     const int64_t hrow = ((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr;
@@ -732,11 +739,12 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s, const 
   if ((p.T - 1) / p.lsel < 512) hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV, 3, 512>), grid, blk, 0, s, p);
   else hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV, 2, kPfMaxBlocks>), grid, blk, 0, s, p);
   if (ev) hipEventRecord(ev->ev[2], s);
+  const dim3 sblk(kSelThreads);
   switch (p.lsel) {
-    case 16: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 16>), grid, blk, 0, s, p); break;
-    case 32: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 32>), grid, blk, 0, s, p); break;
-    case 64: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 64>), grid, blk, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 128>), grid, blk, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 16>), grid, sblk, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 32>), grid, sblk, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 64>), grid, sblk, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 128>), grid, sblk, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   if (ev) hipEventRecord(ev->ev[3], s);
