@@ -265,8 +265,18 @@ def test_single_head_ranking_matches_raw_logits():
 
 # ---------------------------------------------------------------- top-n
 
+def _forced_by_definition(J, n_local, force_initial):
+    """The always-taken blocks written out from the selection paragraph, without the
+    oracle: the initial block (when forced) and the n_local blocks ending at the
+    query's own block J, clipped at 0."""
+    F = set(range(max(0, J - n_local + 1), J + 1))
+    if force_initial:
+        F.add(0)
+    return F
+
+
 def _brute_topn(S, J, n, n_local, force_initial):
-    F = set(O.forced_blocks(J, n_local, force_initial))
+    F = _forced_by_definition(J, n_local, force_initial)
     rest = [j for j in range(J + 1) if j not in F]
     best, best_key = None, None
     for comb in itertools.combinations(rest, n - len(F)):
@@ -292,6 +302,26 @@ def test_topn_brute_force(seed):
         return
     assert got == _brute_topn(S, J, n, n_local, force_initial)
     assert len(got) == n and max(got) <= J and got == sorted(got)
+
+
+def test_forced_blocks_hand_examples():
+    """Worked by hand from the selection paragraph ("always the initial block and two
+    local ones"): at J = 10 the local blocks are 9 and 10, so with n = 5 two routed
+    picks remain and go to the two best other blocks (3 and 7 here)."""
+    S = np.array([0.0, 0.1, 0.2, 0.9, 0.1, 0.3, 0.2, 0.8, 0.85, 0.05, 0.95])
+    # the routed picks are the two best of blocks 1..8: 3 (0.9) and 8 (0.85); 10 (0.95) is local anyway
+    assert O.select_blocks(S, 10, 5, 2, 1) == [0, 3, 8, 9, 10]
+    S2 = np.array([0.0, 0.1, 0.2, 0.9, 0.1, 0.3, 0.2, 0.8, 0.05, 0.97, 0.99])
+    assert O.select_blocks(S2, 10, 5, 2, 1) == [0, 3, 7, 9, 10]
+    assert O.forced_blocks(10, 2, 1) == [0, 9, 10]
+    assert O.forced_blocks(1, 2, 1) == [0, 1]            # J - 1 = 0 merges with the initial block
+    assert O.forced_blocks(0, 2, 1) == [0]
+    assert O.forced_blocks(10, 2, 0) == [9, 10]
+    assert O.forced_blocks(10, 1, 1) == [0, 10]
+    # n = 4 at J = 10 with block 0 and two local blocks forced: one routed pick
+    assert O.select_blocks(S2, 10, 4, 2, 1) == [0, 3, 9, 10]
+    # J + 1 <= n: every block, forced or not
+    assert O.select_blocks(S2[:4], 3, 4, 2, 1) == [0, 1, 2, 3]
 
 
 def test_topn_ties_go_to_lower_index():
