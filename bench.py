@@ -108,7 +108,8 @@ def upload_case(case, torch, N):
 
 
 def decode_bytes(case, sel):
-    """Algorithmic HBM bytes of one decode step and of its first kernel.
+    """Algorithmic HBM bytes of one decode step, of its first kernel and of the
+    selected and window tokens.
 
     Step: the compressed cache, the union of selected and window tokens (each
     read once), q, gates, out.  First kernel (compressed-branch and window
@@ -239,6 +240,9 @@ def bench_decode(args, torch, N, I):
     log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step ({timing}), {res['tokens_per_s']:.4g} tok/s, "
         f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: stream {p1 * 1e3:.1f} us "
         f"({gbs_cmp:.0f} GB/s), finish {ph[1] * 1e3:.1f} us")
+    res["phase_clock_us"] = decode_phase_clock(torch, N, step)
+    log("[bench] decode phase clock (us after the first streaming workgroup starts; median / max over "
+        "workgroups): " + ", ".join(f"{k} {v['median_us']}/{v['max_us']}" for k, v in res["phase_clock_us"].items()))
     if timing == "hip_graph":
         res["gate_network_ms_per_step"] = bench_gate_network(args, torch, N, case, dims, cfg, T, max_len, copies,
                                                              out, sel, ws)
@@ -246,6 +250,47 @@ def bench_decode(args, torch, N, I):
     if timing == "hip_graph" and not args.no_serving:
         res["serving"] = bench_serving(args, torch, N, case, dims, cfg, T, max_len, copies, step)
     return case, res, T
+
+
+CLK_SLOTS, CLK_GROUPS = 16, 4096
+K1_PHASES = {0: "start", 1: "last_tile", 2: "stored"}
+K2_PHASES = {0: "start", 1: "loads_arrived", 2: "scores_ready", 3: "topn_done", 4: "steps_done",
+             5: "partials_stored", 6: "merge_start", 7: "out_written"}
+
+
+def decode_phase_clock(torch, N, step, n_steps=12):
+    """Per-workgroup phase clock of the two decode kernels (the library's profiling
+    hook: thread 0 of every workgroup stamps the 100 MHz constant clock at numbered
+    points), over eager steps.  Returns, per phase, the median over steps of the
+    median and the maximum over workgroups of (stamp - first start of the step's
+    streaming kernel), in microseconds."""
+    buf = torch.zeros(2 * CLK_GROUPS * CLK_SLOTS, dtype=torch.int64, device="cuda")
+    N.nsa_set_phase_clock(buf)
+    per = {}
+    try:
+        for i in range(n_steps):
+            buf.zero_()
+            torch.cuda.synchronize()
+            step(i)
+            torch.cuda.synchronize()
+            a = buf.view(2, CLK_GROUPS, CLK_SLOTS).cpu().numpy()
+            starts = a[0, :, 0]
+            t0 = starts[starts > 0].min()
+            for k, names in ((0, K1_PHASES), (1, K2_PHASES)):
+                for s, nm in names.items():
+                    v = a[k, :, s]
+                    v = v[v > 0]
+                    if v.size:
+                        d = (v - t0) / 100.0  # 100 MHz ticks -> us
+                        per.setdefault(f"{'stream' if k == 0 else 'select'}.{nm}", []).append(
+                            (float(np.median(d)), float(d.max())))
+    finally:
+        N.nsa_set_phase_clock(None)
+    out = {}
+    for key, vals in per.items():
+        vals = np.array(vals)
+        out[key] = {"median_us": round(float(np.median(vals[:, 0])), 2), "max_us": round(float(np.median(vals[:, 1])), 2)}
+    return out
 
 
 def bench_gate_network(args, torch, N, case, dims, cfg, T, max_len, copies, out, sel, ws):

@@ -390,6 +390,24 @@ nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_c
  * not. */
 nsa_status_t nsa_set_phase_events(void* const* events, int32_t count);
 
+/*
+ * nsa_set_phase_clock — profiling hook for this thread's nsa_decode_fwd calls:
+ * thread 0 of every workgroup of the two decode kernels writes the device's
+ * constant 100 MHz clock (uint64 ticks) at numbered points of the kernel into
+ * `buffer` (device memory, at least 2 * 4096 * 16 * 8 = 1 MiB): kernel k's
+ * workgroup w writes entries [(k * 4096 + w) * 16, ... + 16).
+ *   kernel 0 (compressed stream): 0 start, 1 last tile computed, 2 outputs stored;
+ *   kernel 1 (selection): 0 start, 1 first loads arrived, 2 group scores ready,
+ *            3 top-n done, 4 selected and window steps computed, 5 partials
+ *            stored, 6 (last workgroup of a (sequence, group) only) merge
+ *            begins, 7 output written.
+ * Entries of workgroups that end early are not written.  Nothing is recorded
+ * when a kernel has more than 4096 workgroups.  buffer NULL or bytes 0
+ * disables it (the default); a smaller buffer is NSA_ERROR_WORKSPACE.  The
+ * buffer is borrowed until the last recording call has finished on its stream.
+ */
+nsa_status_t nsa_set_phase_clock(void* buffer, size_t bytes);
+
 /* Human-readable name of a status code (static storage). */
 const char* nsa_status_string(nsa_status_t status);
 /* Message of the last failed call on this thread ("" if none). */

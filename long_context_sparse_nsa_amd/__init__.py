@@ -30,6 +30,7 @@ from ._abi import (  # noqa: F401
     nsa_prefill_bwd_workspace_size,
     nsa_prefill_fwd,
     nsa_prefill_workspace_size,
+    nsa_set_phase_clock,
     nsa_set_phase_events,
     nsa_status_string,
 )

@@ -82,6 +82,7 @@ _SIGS = {
                            _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_dsa_decode_workspace_size": [_VP, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_set_phase_events": [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32],
+    "nsa_set_phase_clock": [_VP, ctypes.c_size_t],
     "nsa_status_string": [ctypes.c_int],
     "nsa_last_error": [],
 }
@@ -319,6 +320,15 @@ def nsa_set_phase_events(events=None):
         return
     arr = (ctypes.c_void_p * len(events))(*[e.value if isinstance(e, ctypes.c_void_p) else int(e) for e in events])
     _check(load_library().nsa_set_phase_events(arr, len(events)))
+
+
+def nsa_set_phase_clock(buffer=None):
+    """Record the decode kernels' per-workgroup phase clock into a device tensor of at
+    least 1 MiB (uint64 ticks of the 100 MHz constant clock); None disables."""
+    if buffer is None:
+        _check(load_library().nsa_set_phase_clock(None, 0))
+        return
+    _check(load_library().nsa_set_phase_clock(_ptr(buffer, "buffer"), buffer.numel() * buffer.element_size()))
 
 
 def compressed_count(L: int, l: int, d: int) -> int:

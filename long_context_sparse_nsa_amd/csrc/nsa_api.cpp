@@ -17,6 +17,8 @@ namespace {
 thread_local std::string g_last_error;
 thread_local nsa::PhaseEvents g_phase_events{};
 thread_local bool g_phase_on = false;
+thread_local uint64_t* g_clk = nullptr;
+thread_local size_t g_clk_bytes = 0;
 
 nsa_status_t fail(nsa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 nsa_status_t fail(nsa_status_t st, const char* fmt, ...) {
@@ -96,12 +98,12 @@ nsa_status_t check_decode_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg,
   if ((int64_t)lay.nch * lay.seg < nc || lay.nch > nsa::kMaxChunks || lay.nbo + 1 > nsa::kScStrideMax - 3)
     return fail(NSA_ERROR_UNSUPPORTED, "no segment plan for %lld compressed blocks with l_sel/d=%d", (long long)nc,
                 cfg->l_sel / cfg->d);
-  if (lay.nfin > nsa::kMaxFinish)
-    return fail(NSA_ERROR_UNSUPPORTED, "n_sel=%d with l_sel=%d needs more than %d selection workgroups", cfg->n_sel,
-                cfg->l_sel, nsa::kMaxFinish);
   if (lay.nwin > nsa::kMaxWindow)
     return fail(NSA_ERROR_UNSUPPORTED, "w=%d with l_sel=%d needs more than %d window workgroups", cfg->w, cfg->l_sel,
                 nsa::kMaxWindow);
+  if (lay.nfin > nsa::kMaxFinish)
+    return fail(NSA_ERROR_UNSUPPORTED, "n_sel=%d with l_sel=%d needs more than %d selection workgroups", cfg->n_sel,
+                cfg->l_sel, nsa::kMaxFinish);
 
   return NSA_SUCCESS;
 }
@@ -240,6 +242,19 @@ nsa_status_t nsa_set_phase_events(void* const* events, int32_t count) {
     g_phase_events.ev[i] = static_cast<hipEvent_t>(events[i]);
   }
   g_phase_on = true;
+  return ok();
+}
+
+nsa_status_t nsa_set_phase_clock(void* buffer, size_t bytes) {
+  if (!buffer || bytes == 0) {
+    g_clk = nullptr;
+    g_clk_bytes = 0;
+    return ok();
+  }
+  const size_t need = (size_t)2 * nsa::kClkMaxGroups * nsa::kClkSlots * sizeof(uint64_t);
+  if (bytes < need) return fail(NSA_ERROR_WORKSPACE, "phase clock buffer of %zu bytes needed, %zu given", need, bytes);
+  g_clk = static_cast<uint64_t*>(buffer);
+  g_clk_bytes = bytes;
   return ok();
 }
 
@@ -409,15 +424,17 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   p.o1 = reinterpret_cast<float*>(ws + lay.off_o1);
   p.sc1 = reinterpret_cast<float*>(ws + lay.off_sc1);
   p.wpart = reinterpret_cast<float*>(ws + lay.off_wpart);
+  p.nwin = lay.nwin;
+  p.wtiles = lay.wtiles;
   p.rpart = reinterpret_cast<float*>(ws + lay.off_rpart);
   p.ocmp = reinterpret_cast<float*>(ws + lay.off_ocmp);
   p.cnt = reinterpret_cast<uint32_t*>(ws + lay.off_cnt);
   p.nfin = lay.nfin;
-  p.nwin = lay.nwin;
   p.nch = lay.nch;
   p.seg = lay.seg;
   p.nbo = lay.nbo;
-  p.wtiles = lay.wtiles;
+  if (g_clk && (int64_t)p.B * p.H * ((p.nch + p.nwin) > p.nfin ? (p.nch + p.nwin) : p.nfin) <= nsa::kClkMaxGroups)
+    p.clk = g_clk;
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -5,17 +5,17 @@
 // 1. decode_stream_kernel, about one workgroup per compute unit, two kinds:
 //    - segment workgroups: the compressed branch, split over segments of
 //      compressed keys per (sequence, KV group).  Each streams its segment of
-//      the compressed cache once into registers, computes the 16-head logits with
-//      MFMA, the segment's softmax statistics and partial output, and the
+//      the compressed cache once into registers, computes the 16-head logits
+//      with MFMA, the segment's softmax statistics and partial output, and the
 //      per-head probabilities folded onto selection blocks;
 //    - window workgroups: the window branch, which does not depend on the
 //      selection, streamed the same way over the window's raw tokens.
 // 2. decode_finish_kernel: several workgroups per (sequence, group), each
 //    computing the exact per-head normalisers from the segment statistics, the
-//    group scores and the top-n, a slice of the compressed-branch output, and
-//    its share of the selected blocks (one 32-token step per wave); the last
-//    of them to finish merges the partials and applies the gates:
-//    out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
+//    group scores and the top-n (one wave), a slice of the compressed-branch
+//    output, and its share of the selected blocks (one 32-token step per
+//    wave); the last of them to finish merges the partials and applies the
+//    gates: out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 //
 // Sources: lesson 5.5/02 "Разреженное внимание — NSA и DSA" (ai.flicky.cc),
 // section "NSA: три ветви" (output equation; compressed branch l=32, d=16;
@@ -78,9 +78,52 @@ __device__ __forceinline__ int n_visible(const DecodeParams& p, int b, int L) {
   return (int)(nv < ccap ? nv : ccap);
 }
 
+// Profiling hook: thread 0 records the constant 100 MHz clock at point `slot`
+// of this workgroup (clk is null unless the caller asked for a phase clock).
+__device__ __forceinline__ void clk_stamp(uint64_t* clk, int slot) {
+  if (clk != nullptr && threadIdx.x == 0) clk[(size_t)blockIdx.x * kClkSlots + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
 // Stores and loads that are coherent across the whole device without cache
-// maintenance (relaxed atomics at agent scope): the finish workgroups of one
+// maintenance (relaxed atomics at agent scope): the selection workgroups of one
 // (sequence, group) hand their partials to the last of them this way.
+//
+// Why relaxed atomics and a wait are enough here.  The partials are written
+// with agent-scope atomic stores, which the hardware writes through to the
+// device-coherent level (they are never held dirty in an XCD's L2); the writer
+// then waits until all of its stores are acknowledged (s_waitcnt vmcnt(0),
+// written as asm with a memory clobber, so the compiler keeps every store
+// before it) and only then increments the arrival counter.  The workgroup that
+// sees the final count issues its loads only after the counter's value has
+// returned, and reads with agent-scope atomic loads, which bypass the
+// non-coherent caches.  So every partial is in memory before its writer's
+// increment and is read from memory after the last increment.  A release /
+// acquire pair would instead write back and invalidate the whole L2 of the
+// XCD per workgroup, which costs far more than this hand-off.
+__device__ __forceinline__ void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The same device-coherent accesses 16 bytes at a time, through a buffer
+// resource: cache policy sc1 is what the compiler emits for the agent-scope
+// relaxed atomics above (checked in the generated code), which it offers only
+// up to 8 bytes.  Offsets are in bytes; accesses past `bytes` read 0 and are
+// dropped by the hardware's range check.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kCoherent = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4_t ld4_coherent(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
+}
+__device__ __forceinline__ float ld1_coherent(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent));
+}
+__device__ __forceinline__ void st4_coherent(rsrc_t r, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, kCoherent);
+}
+__device__ __forceinline__ void st1_coherent(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kCoherent);
+}
 __device__ __forceinline__ void st_shared_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -155,67 +198,6 @@ __device__ __forceinline__ void step_logits(const Step<DK, DV>& st, const u32x4_
   }
 }
 
-// Workgroup merge of 4 waves' branch states into one partial
-// (m[16], l[16], o[16][DV]) written to `dst`; `buf`/`st` are LDS scratch.
-template <int DV, int NWV, bool DEV_SHARED = false>
-__device__ __forceinline__ void merge_waves_to(const Branch<DV>& br, float* dst, float* buf, float* st) {
-  auto put = [&](float* q, float v) {
-    if constexpr (DEV_SHARED) st_shared_dev(q, v);
-    else *q = v;
-  };
-  auto put2 = [&](float* q, float v0, float v1) {  // q 8-byte aligned
-    if constexpr (DEV_SHARED) {
-      const uint64_t u = (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32);
-      __hip_atomic_store(reinterpret_cast<uint64_t*>(q), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      q[0] = v0;
-      q[1] = v1;
-    }
-  };
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-  constexpr int NTH = 64 * NWV;
-  if (lg == 0) {
-    st[wave * 16 + lr] = br.m;
-    st[(NWV + wave) * 16 + lr] = br.l;
-  }
-  lds_barrier();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NWV; ++w) M = fmaxf(M, st[w * 16 + lr]);
-  const float alpha = br.m == -INFINITY ? 0.f : exp2f(br.m - M);
-#pragma unroll
-  for (int j = 0; j < DV / 16; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) buf[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = alpha * br.acc[j][i];
-  lds_barrier();
-  for (int e = 2 * tid; e < 16 * DV; e += 2 * NTH) {  // two outputs per thread and pass
-    const int h = e / DV, ch = e - h * DV;
-    float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      v0 += buf[(w * 16 + h) * (DV + 1) + ch];
-      v1 += buf[(w * 16 + h) * (DV + 1) + ch + 1];
-    }
-    put2(dst + 32 + e, v0, v1);
-  }
-  if (tid < 16) {
-    float Mh = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) Mh = fmaxf(Mh, st[w * 16 + tid]);
-    float ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      const float mw = st[w * 16 + tid];
-      if (mw != -INFINITY) ls += exp2f(mw - Mh) * st[(NWV + w) * 16 + tid];
-    }
-    put(dst + tid, Mh);
-    put(dst + 16 + tid, ls);
-  }
-  lds_barrier();
-}
-
-
-
 }  // namespace
 
 // ---------------------------------------------------------------- streaming pass
@@ -284,6 +266,32 @@ __device__ __forceinline__ void load_wave_tile(WaveTile<DK, DV>& T, const uint16
   }
 }
 
+// A whole 32-token step [x0, x0 + 32) of the raw cache (every row exists) in
+// the Step layout, addressed as scalar base + this lane's 32-bit offsets:
+// koff = (lr*DK + 8*lg)*2 and voff = (4*lg*DV + (DV/16)*lr)*2 bytes.
+template <int DK, int DV>
+__device__ __forceinline__ void step_load_full(Step<DK, DV>& st, const uint16_t* kb, const uint16_t* vb, int64_t x0,
+                                               uint32_t koff, uint32_t voff) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const gchar_ptr kp = scalar_ptr(kb + (x0 + 16 * tt) * DK) + koff;
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) st.kf[tt][kk] = ld_global<u32x4_t>(kp + 64 * kk);
+  }
+  const gchar_ptr vp = scalar_ptr(vb + x0 * DV) + voff;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int key = r < 4 ? r : 12 + r;  // step_key(lg, r) - 4*lg
+    if constexpr (DV / 32 == 4) {
+      const u32x4_t x = ld_global<u32x4_t>(vp + key * DV * 2);
+      st.vr[r][0] = x[0]; st.vr[r][1] = x[1]; st.vr[r][2] = x[2]; st.vr[r][3] = x[3];
+    } else {
+      const u32x2_t x = ld_global<u32x2_t>(vp + key * DV * 2);
+      st.vr[r][0] = x[0]; st.vr[r][1] = x[1];
+    }
+  }
+}
+
 // Workgroup of the streaming pass: kStreamWaves waves stream the rows of a
 // segment of the compressed cache (or of part of the window of the raw cache)
 // as 64-row tiles; wave w owns rows 16w .. 16w+15 of every tile and loads them
@@ -326,6 +334,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   const int bg = blockIdx.x / per, c = blockIdx.x - bg * per;
   const int g = bg % p.H, b = bg / p.H;
   const bool fold = c < p.nch;  // workgroup-uniform: compressed segment, else window part
+  clk_stamp(p.clk, 0);
   const uint32_t koff = (uint32_t)((lr * DK + 8 * lg) * 2), voff = (uint32_t)((4 * lg * DV + VC * lr) * 2);
   u32x4_t qf[KT];
   WaveTile<DK, DV> tb[kDepth];
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     // past the length are masked (their values are zeroed before use).
     const int k0 = c * p.seg;
     const int64_t ccap_b = p.cuc ? ld_scalar(p.cuc + b + 1) - ld_scalar(p.cuc + b) : p.ccap;
-    if (k0 >= ccap_b) return;  // beyond the slot: never read by the later kernels
+    if (k0 >= ccap_b) return;  // beyond the slot: never read by the selection kernel
     const int64_t rpre = min((int64_t)k0 + p.seg, ccap_b) - 1;
     const int64_t crow = cmp_row0(p, b, g);
     kb = p.kc + crow * DK;
@@ -353,7 +362,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     for (int d = 0; d < kDepth - 1; ++d)
       load_wave_tile<DK, DV>(tb[d], kb, vb, (int64_t)k0 + 64 * d + 16 * wave, rpre, koff, voff, lg, lr);
     const int nvis = n_visible(p, b, L);
-    if (k0 >= nvis) {  // empty segment: never read by the later kernels
+    if (k0 >= nvis) {  // empty segment: never read by the selection kernel
       wait_vmem();
       return;
     }
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     rowmax = nvis - 1;
   } else {
     const int wi = c - p.nch;
-    if (wi == 0 && tid == 0) p.cnt[bg] = 0u;  // arrival counter of the finish workgroups
+    if (wi == 0 && tid == 0) p.cnt[bg] = 0u;  // arrival counter of the selection workgroups
     L = seq_len_clamped(p, b);
     const int t = L - 1;
     const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
@@ -532,6 +541,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
 #pragma unroll
   for (int u = 0; u < kDepth - 1; ++u)
     if (i0 + u < nt) process(i0 + u, tb[u]);  // workgroup-uniform
+  clk_stamp(p.clk, 1);
 
   // ---- workgroup merge: all waves share mref, so outputs and sums just add
   lsum = sum_over_groups_swap(lsum);
@@ -590,37 +600,96 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
         if (e0 + NTH * u < 16 * slots) SC[e0 + NTH * u] = v[u] * invq;
     }
   }
+  clk_stamp(p.clk, 2);
 }
 
-// Finish: nfin workgroups of 4 waves per (sequence, group).  Every one of them
-// computes the exact per-head normalisers of the compressed branch, the group
-// scores and the top-n (identical results, so no exchange is needed); then
-// workgroup k
+// Merges the NWV waves' selected-branch states into one partial and stores it
+// device-coherently at byte offset `off` of r: m[16], l[16] and the output
+// divided by l, o[16][DV] (the last workgroup weights it by its share of the
+// total).  buf holds NWV*16*(DV+1) floats, st 2*NWV*16.
+template <int DV, int NWV>
+__device__ __forceinline__ void merge_store(const Branch<DV>& a, float* buf, float* st, rsrc_t r, uint32_t off) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  constexpr int NTH = 64 * NWV, RS = NWV * 16;
+  if (lg == 0) {
+    st[wave * 16 + lr] = a.m;
+    st[RS + wave * 16 + lr] = a.l;
+  }
+  lds_barrier();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) M = fmaxf(M, st[w * 16 + lr]);
+  const float fa = a.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a.m - M);
+#pragma unroll
+  for (int j = 0; j < DV / 16; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = fa * a.acc[j][i];
+  lds_barrier();
+  // four consecutive outputs of one head per thread and pass
+#pragma unroll
+  for (int q = 0; q < 16 * DV / (4 * NTH); ++q) {
+    const int e = 4 * (tid + NTH * q);
+    const int h = e / DV, ch = e - h * DV;
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) Mh = fmaxf(Mh, st[w * 16 + h]);
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = st[w * 16 + h];
+      if (mw != -INFINITY) ls += __builtin_amdgcn_exp2f(mw - Mh) * st[RS + w * 16 + h];
+    }
+    const float inv = ls > 0.f ? 1.0f / ls : 0.f;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWV; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += buf[(w * 16 + h) * (DV + 1) + ch + i];
+    st4_coherent(r, off + (uint32_t)(32 + e) * 4, v * inv);
+  }
+  if (tid < 16) {
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) Mh = fmaxf(Mh, st[w * 16 + tid]);
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = st[w * 16 + tid];
+      if (mw != -INFINITY) ls += __builtin_amdgcn_exp2f(mw - Mh) * st[RS + w * 16 + tid];
+    }
+    st1_coherent(r, off + (uint32_t)tid * 4, Mh);
+    st1_coherent(r, off + (uint32_t)(16 + tid) * 4, ls);
+  }
+}
+
+// Finish: nfin workgroups of kFinWaves waves per (sequence, group).  Every one
+// of them computes the exact per-head normalisers of the compressed branch,
+// the group scores and the top-n (one wave; identical results in every
+// workgroup, so no exchange is needed); then workgroup k
 //   - sums its slice of the normalised compressed-branch output over the
 //     segments (the loads are issued before the normalisers are known),
 //   - attends the selected steps [4k, 4k+4) (one 32-token step per wave, over
-//     all selected blocks in ascending order) and writes one partial.
+//     all selected blocks in ascending order) and stores one partial.
 // The last of the nfin workgroups to finish (a device-scope counter, cleared
 // by the streaming pass) merges the selected-branch partials and the window
 // partials and writes out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
 template <int DK, int DV, int LSEL>
-#ifndef NSA_FIN_WAVES
-#define NSA_FIN_WAVES 4
-#endif
-__global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(DecodeParams p) {
-  constexpr int NWV = NSA_FIN_WAVES, NTH = 64 * NWV;
+__global__ __launch_bounds__(64 * kFinWaves) void decode_finish_kernel(DecodeParams p) {
+  constexpr int NWV = kFinWaves, NTH = 64 * NWV;
   constexpr int KT = DK / 32;
   constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;   // 32-token steps per selection block
-  constexpr int PSTRIDE = 32 + 16 * DV;
+  constexpr int WSTRIDE = 32 + 16 * DV;              // window partial (fp32 m, l, o), floats
+  constexpr int RSTRIDE = 32 + 16 * DV;              // selected partial (m, l, o / l), floats
   constexpr int RPT = 4;                             // candidate blocks per thread and load round
   constexpr int OB = 8;                              // segments per compressed-output load batch
-  __shared__ float S[kMaxBlocks];
+  __shared__ __attribute__((aligned(16))) float S[kMaxBlocks + 64];
   __shared__ float s_f[kMaxChunks * 16];
   __shared__ float s_ml[2 * kMaxChunks * 16];       // segment m / l, then wave-merge scratch
   __shared__ float s_ov[kMaxChunks * 16];           // overhang score slot of each segment, per head
   __shared__ float s_buf[NWV * 16 * (DV + 1)];
   __shared__ TopnSmem tsm;
   __shared__ TopnFastSmem<NWV> tfs;
+  __shared__ uint64_t s_tw[416];                    // single-wave top-n scratch
   __shared__ int s_sel[kMaxSel];
   __shared__ int s_items[kMaxSel];
   __shared__ int s_nitems;
@@ -630,7 +699,7 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; when the sizes allow,
   // the nfin workgroups of one (sequence, group) get ids on the same XCD, so the
-  // partials they hand over stay in that XCD's L2.  Only speed depends on this.
+  // partials they hand over stay close.  Only speed depends on this.
   int bg, kfin;
   if ((p.B * p.H) % 8 == 0) {
     const int w = blockIdx.x, xcd = w & 7, r = w >> 3;
@@ -640,9 +709,12 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
     bg = blockIdx.x / p.nfin;
     kfin = blockIdx.x - bg * p.nfin;
   }
+  uint64_t* clk = p.clk ? p.clk + (size_t)kClkMaxGroups * kClkSlots : nullptr;
+  clk_stamp(clk, 0);
   const int g = bg % p.H, b = bg / p.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-  const int nch = p.nch, nbo = p.nbo, slots = nbo + 1;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = p.nch, nbo = p.nbo, slots = nbo + 1, nfin = p.nfin;
   const size_t cbase = (size_t)bg * nch;
   float* s_m = s_ml;
   float* s_l = s_ml + kMaxChunks * 16;
@@ -667,26 +739,26 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
       if (cc >= nch) cc = nch - 1, jj = 0;  // beyond every sequence: read in bounds, discarded
       const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.sc1 + ((cbase + cc) * slots + jj) * 16);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vv[r][u] = src[u];
+      for (int q = 0; q < 4; ++q) vv[r][q] = src[q];
     }
   };
   load_scores(0);
   // compressed-branch output slice of this workgroup: outputs [e0, e1) of the
   // group's 16 x DV, one per thread and pass
-  const int per = (16 * DV + p.nfin - 1) / p.nfin;
+  const int per = (16 * DV + nfin - 1) / nfin;
   const int e0 = kfin * per, e1 = min(e0 + per, 16 * DV);
   float vo[OB];
   {
     const int e = e0 + tid;
     const int ee = e < e1 ? e : e0;
 #pragma unroll
-    for (int u = 0; u < OB; ++u) vo[u] = p.o1[(cbase + min(u, nch - 1)) * 16 * DV + ee];
+    for (int q = 0; q < OB; ++q) vo[q] = p.o1[(cbase + min(q, nch - 1)) * 16 * DV + ee];
   }
   u32x4_t qf[KT];
   load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
   if (p.wgate) {  // gate network: 3 G dot products of the query with a weight row, four lanes each
-    for (int e0 = 0; e0 < 12 * p.G; e0 += NTH) {  // one pass when NTH >= 12 G
-      const int pr = (e0 + tid) >> 2, pt = tid & 3;
+    for (int f0 = 0; f0 < 12 * p.G; f0 += NTH) {  // one pass when NTH >= 12 G
+      const int pr = (f0 + tid) >> 2, pt = tid & 3;
       const int pc = pr < 3 * p.G ? pr : 0;
       const int hq = g * p.G + pc / 3, br = pc % 3;
       float z = gate_dot_quarter<DK>(p.q + ((size_t)b * p.Hq + hq) * DK, p.wgate + ((size_t)hq * 3 + br) * DK, pt);
@@ -713,6 +785,7 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
   const int t = L - 1;
   const int J = t / LSEL;
   lds_barrier();
+  clk_stamp(clk, 1);
 
   // ---- exact per-head normalisers (wave 0: lane = head + 16 * segment phase)
   if (wave == 0) {
@@ -738,7 +811,7 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
     float oc = 0.f;
     if (e == e0 + tid) {
 #pragma unroll
-      for (int u = 0; u < OB; ++u) oc += u < nch_b ? s_f[u * 16 + h] * vo[u] : 0.f;
+      for (int q = 0; q < OB; ++q) oc += q < nch_b ? s_f[q * 16 + h] * vo[q] : 0.f;
     } else {
       for (int c = 0; c < min(nch_b, OB); ++c) oc += s_f[c * 16 + h] * p.o1[(cbase + c) * 16 * DV + e];
     }
@@ -758,9 +831,9 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
       float sc = 0.f;
       if (cc < nch_b) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sc += s_f[cc * 16 + 4 * u + e] * vv[r][u][e];
+          for (int e = 0; e < 4; ++e) sc += s_f[cc * 16 + 4 * q + e] * vv[r][q][e];
       }
       if (jj == 0 && cc >= 1 && cc - 1 < nch_b) {  // overhang of the previous segment
 #pragma unroll
@@ -770,104 +843,136 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
     }
   }
   lds_barrier();
+  clk_stamp(clk, 2);
   {
     int32_t* so = (p.sel_out && kfin == 0) ? p.sel_out + (size_t)bg * p.n : nullptr;
-    if (J + 1 <= 4 * NTH) block_topn_fast<NTH, 4, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel, so);
-    else block_topn_fast<NTH, 8, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel, so);
+    if (J + 1 <= 2048) {  // workgroup-uniform: one wave ranks, the others wait
+      if (wave == 0) {
+        const int cnt = J + 1 <= 1024 ? wave_topn_fast<16>(S, J, p.n, p.nloc, p.finit, s_tw, s_items, so)
+                                      : wave_topn_fast<32>(S, J, p.n, p.nloc, p.finit, s_tw, s_items, so);
+        if (lane == 0) s_nitems = cnt;
+      }
+    } else {
+      block_topn_fast<NTH, 8, kMaxBlocks / NTH>(S, J, p.n, p.nloc, p.finit, tfs, tsm, s_sel, so);
+      lds_barrier();
+      if (wave == 0) {  // the selected blocks, ascending (the list ends at the first -1)
+        const int j = lane < p.n ? s_sel[lane] : -1;
+        const uint64_t m = __ballot(j >= 0);
+        if (j >= 0) s_items[__popcll(m & ((1ull << lane) - 1ull))] = j;
+        if (lane == 0) s_nitems = __popcll(m);
+      }
+    }
   }
   lds_barrier();
-  if (wave == 0) {  // the selected blocks, ascending (the list ends at the first -1)
-    const int j = lane < p.n ? s_sel[lane] : -1;
-    const uint64_t m = __ballot(j >= 0);
-    if (j >= 0) s_items[__popcll(m & ((1ull << lane) - 1ull))] = j;
-    if (lane == 0) s_nitems = __popcll(m);
-  }
-  lds_barrier();
+  clk_stamp(clk, 3);
 
-  // ---- this workgroup's share of the selected steps: one 32-token step per wave
+  // ---- this workgroup's share of the selected steps: one 32-token step per
+  // wave.  A full step reads its 32 rows through a scalar base; a step that
+  // ends past the sequence is shifted back to end at its last token (the
+  // earlier rows are masked), so no row past the length is read.
   Branch<DV> br;
   br.init();
   const int si = kfin * NWV + wave;
-  if (si < s_nitems * SPB) {
+  const int nss = s_nitems * SPB;
+  if (si < nss) {
     const int it = si / SPB, half = si - it * SPB;
-    const int64_t xb = (int64_t)s_items[it] * LSEL;
-    const int64_t x0 = xb + 32 * half;
-    const int64_t nv = min((int64_t)L, xb + LSEL);
-    const int64_t row = raw_row0(p, b, g);
-    Step<DK, DV> st;
-    step_load<DK, DV>(st, p.k + row * DK, p.v + row * DV, x0, nv, lg, lr);
-    if (x0 < nv) {
+    const int xb = s_items[it] * LSEL;
+    const int x0 = xb + 32 * half;
+    const int nv = min(L, xb + LSEL);
+    if (x0 < nv) {  // wave-uniform
+      const int64_t row = raw_row0(p, b, g);
+      const uint16_t* kraw = p.k + row * DK;
+      const uint16_t* vraw = p.v + row * DV;
+      Step<DK, DV> st;
+      int xs = x0;
+      if (L >= 32) {
+        xs = max(0, min(x0, nv - 32));
+        step_load_full<DK, DV>(st, kraw, vraw, xs, (uint32_t)((lr * DK + 8 * lg) * 2),
+                               (uint32_t)((4 * lg * DV + (DV / 16) * lr) * 2));
+      } else {
+        step_load<DK, DV>(st, kraw, vraw, x0, nv, lg, lr);
+      }
       float z[2][4];
       step_logits<DK, DV>(st, qf, p.scale_log2, z);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (x0 + 16 * tt + 4 * lg + i >= nv) z[tt][i] = -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          const int x = xs + 16 * tt + 4 * lg + e;
+          if (x < x0 || x >= nv) z[tt][e] = -INFINITY;
+        }
       br.update(z, st.vr);
     }
   }
-  float* rp = p.rpart + (size_t)bg * p.nfin * PSTRIDE;
+  clk_stamp(clk, 4);
+  float* rp = p.rpart + (size_t)bg * nfin * RSTRIDE;
+  const rsrc_t rr = coherent_rsrc(rp, (uint32_t)(nfin * RSTRIDE * 4));
   if (e0 + tid < e1) st_shared_dev(p.ocmp + (size_t)bg * 16 * DV + e0 + tid, oc_first);
-  merge_waves_to<DV, NWV, true>(br, rp + (size_t)kfin * PSTRIDE, s_buf, s_ml);
+  const int nsp = min(nfin, (nss + NWV - 1) / NWV);  // partials that hold a step
+  if (kfin < nsp) merge_store<DV, NWV>(br, s_buf, s_ml, rr, (uint32_t)kfin * RSTRIDE * 4);
 
-  // ---- the last workgroup of this (sequence, group) applies the gates.  The
-  // partial and the output slice were stored coherently; once every thread's
-  // stores have completed, the counter is incremented, and the workgroup that
-  // sees the final count reads the others' results with coherent loads.
-  __builtin_amdgcn_s_waitcnt(0);
+  // ---- the last workgroup of this (sequence, group) applies the gates (the
+  // hand-off is explained at wait_stores_done)
+  wait_stores_done();
   lds_barrier();
+  clk_stamp(clk, 5);
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(p.cnt + bg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(p.nfin - 1);
+             (unsigned)(nfin - 1);
   lds_barrier();
   if (!s_last) return;
-  const float* wp = p.wpart + (size_t)bg * p.nwin * PSTRIDE;
-  const float* oc_src = p.ocmp + (size_t)bg * 16 * DV;
-  constexpr int FF = 8, FW = 2, NP = 16 * DV / 2 / NTH;  // fast-path partial counts; output pairs per thread
-  const bool fast = p.nfin <= FF && p.nwin <= FW;        // workgroup-uniform
-  f32x2_t ro[NP][FF], rw[NP][FW], rc[NP];
+  clk_stamp(clk, 6);
+  const rsrc_t ro = coherent_rsrc(p.ocmp + (size_t)bg * 16 * DV, 16 * DV * 4);
+  const float* wp = p.wpart + (size_t)bg * p.nwin * WSTRIDE;
+  const int nwin = p.nwin;
+  // eight consecutive outputs e8 .. e8+7 of one head per thread (16*DV/8 threads)
+  constexpr int NO = 16 * DV / 8;
+  constexpr int FF = 8, FW = 2;                // fast-path partial counts
+  const bool fast = nfin <= FF && nwin <= FW;  // workgroup-uniform
+  const int e8 = 8 * (tid < NO ? tid : 0), h8 = e8 / DV;
+  f32x4_t ro8[FF][2], rw8[FW][2], rc8[2];
   float fm[FF], fl[FF], wm[FW], wl[FW];
   if (fast) {  // every load of the merge in flight at once
+    rc8[0] = ld4_coherent(ro, (uint32_t)e8 * 4);
+    rc8[1] = ld4_coherent(ro, (uint32_t)(e8 + 4) * 4);
 #pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int e2 = 2 * (tid + NTH * u);
-      rc[u] = ld2_shared_dev(oc_src + e2);
+    for (int k = 0; k < FF; ++k)
 #pragma unroll
-      for (int k = 0; k < FF; ++k) ro[u][k] = k < p.nfin ? ld2_shared_dev(rp + (size_t)k * PSTRIDE + 32 + e2) : f32x2_t{0.f, 0.f};
+      for (int u = 0; u < 2; ++u)
+        ro8[k][u] = k < nsp ? ld4_coherent(rr, (uint32_t)(k * RSTRIDE + 32 + e8 + 4 * u) * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < FW; ++k) {
-        const float* src = wp + (size_t)k * PSTRIDE + 32 + e2;
-        rw[u][k] = k < p.nwin ? f32x2_t{src[0], src[1]} : f32x2_t{0.f, 0.f};
-      }
-    }
+    for (int k = 0; k < FW; ++k)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        rw8[k][u] = k < nwin ? *reinterpret_cast<const f32x4_t*>(wp + (size_t)k * WSTRIDE + 32 + e8 + 4 * u)
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (tid < 16) {
 #pragma unroll
       for (int k = 0; k < FF; ++k) {
-        fm[k] = k < p.nfin ? ld_shared_dev(rp + (size_t)k * PSTRIDE + tid) : -INFINITY;
-        fl[k] = k < p.nfin ? ld_shared_dev(rp + (size_t)k * PSTRIDE + 16 + tid) : 0.f;
+        fm[k] = k < nsp ? ld1_coherent(rr, (uint32_t)(k * RSTRIDE + tid) * 4) : -INFINITY;
+        fl[k] = k < nsp ? ld1_coherent(rr, (uint32_t)(k * RSTRIDE + 16 + tid) * 4) : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < FW; ++k) {
-        wm[k] = k < p.nwin ? wp[(size_t)k * PSTRIDE + tid] : -INFINITY;
-        wl[k] = k < p.nwin ? wp[(size_t)k * PSTRIDE + 16 + tid] : 0.f;
+        wm[k] = k < nwin ? wp[(size_t)k * WSTRIDE + tid] : -INFINITY;
+        wl[k] = k < nwin ? wp[(size_t)k * WSTRIDE + 16 + tid] : 0.f;
       }
     }
   }
-  if (tid < 16) {  // per-head merge factors of the selected and window partials
+  if (tid < 16) {  // per-head merge factors: selected partials (outputs already divided by their l)
     const int h = tid;
     float ls = 0.f, lw = 0.f;
+    float M = -INFINITY, Mw = -INFINITY;
     if (fast) {  // static indexing only: the loaded values stay in registers
-      float M = -INFINITY, Mw = -INFINITY;
 #pragma unroll
       for (int k = 0; k < FF; ++k) M = fmaxf(M, fm[k]);
 #pragma unroll
       for (int k = 0; k < FW; ++k) Mw = fmaxf(Mw, wm[k]);
 #pragma unroll
       for (int k = 0; k < FF; ++k) {
-        const float a = fm[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm[k] - M);
+        const float a = fm[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fm[k] - M) * fl[k];
         s_pf[k][h] = a;
-        ls += a * fl[k];
+        ls += a;
       }
 #pragma unroll
       for (int k = 0; k < FW; ++k) {
@@ -876,63 +981,81 @@ __global__ __launch_bounds__(64 * NSA_FIN_WAVES) void decode_finish_kernel(Decod
         lw += a * wl[k];
       }
     } else {
-      float M = -INFINITY, Mw = -INFINITY;
-      for (int k = 0; k < p.nfin; ++k) M = fmaxf(M, ld_shared_dev(rp + (size_t)k * PSTRIDE + h));
-      for (int k = 0; k < p.nwin; ++k) Mw = fmaxf(Mw, wp[(size_t)k * PSTRIDE + h]);
-      for (int k = 0; k < p.nfin; ++k) {
-        const float mk = ld_shared_dev(rp + (size_t)k * PSTRIDE + h);
-        const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+      for (int k = 0; k < nsp; ++k) M = fmaxf(M, ld1_coherent(rr, (uint32_t)(k * RSTRIDE + h) * 4));
+      for (int k = 0; k < nwin; ++k) Mw = fmaxf(Mw, wp[(size_t)k * WSTRIDE + h]);
+      for (int k = 0; k < nsp; ++k) {
+        const float mk = ld1_coherent(rr, (uint32_t)(k * RSTRIDE + h) * 4);
+        const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M) * ld1_coherent(rr, (uint32_t)(k * RSTRIDE + 16 + h) * 4);
         s_pf[k][h] = a;
-        ls += a * ld_shared_dev(rp + (size_t)k * PSTRIDE + 16 + h);
+        ls += a;
       }
-      for (int k = 0; k < p.nwin; ++k) {
-        const float mk = wp[(size_t)k * PSTRIDE + h];
+      for (int k = 0; k < nwin; ++k) {
+        const float mk = wp[(size_t)k * WSTRIDE + h];
         const float a = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - Mw);
         s_wf[k][h] = a;
-        lw += a * wp[(size_t)k * PSTRIDE + 16 + h];
+        lw += a * wp[(size_t)k * WSTRIDE + 16 + h];
       }
     }
     const float is = ls > 0.f ? 1.0f / ls : 0.f, iw = lw > 0.f ? 1.0f / lw : 0.f;
-    for (int k = 0; k < p.nfin; ++k) s_pf[k][h] *= is;
-    for (int k = 0; k < p.nwin; ++k) s_wf[k][h] *= iw;
+    for (int k = 0; k < nsp; ++k) s_pf[k][h] *= is;
+    for (int k = 0; k < nwin; ++k) s_wf[k][h] *= iw;
   }
   lds_barrier();
-  auto emit = [&](int e, float oc, float os, float ow) {  // output e of the group's 16 x DV
-    const int h = e / DV;
-    if (h >= p.G) return;
-    const int hq = g * p.G + h;
-    p.out[((size_t)b * p.Hq + hq) * DV + (e - h * DV)] =
-        (uint16_t)f32_to_bf16(s_gate[h][0] * oc + s_gate[h][1] * os + s_gate[h][2] * ow);
-  };
-  if (fast) {
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int e2 = 2 * (tid + NTH * u), h = e2 / DV;
-      float os0 = 0.f, os1 = 0.f, ow0 = 0.f, ow1 = 0.f;
+  if (tid < NO && h8 < p.G) {
+    float os[8], ow[8], oc[8];
+    for (int i = 0; i < 8; ++i) os[i] = ow[i] = 0.f;
+    if (fast) {
 #pragma unroll
       for (int k = 0; k < FF; ++k) {
-        const float a = k < p.nfin ? s_pf[k][h] : 0.f;
-        os0 += a * ro[u][k][0];
-        os1 += a * ro[u][k][1];
+        const float a = k < nsp ? s_pf[k][h8] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          os[i] += a * ro8[k][0][i];
+          os[4 + i] += a * ro8[k][1][i];
+        }
       }
 #pragma unroll
       for (int k = 0; k < FW; ++k) {
-        const float a = k < p.nwin ? s_wf[k][h] : 0.f;
-        ow0 += a * rw[u][k][0];
-        ow1 += a * rw[u][k][1];
+        const float a = k < nwin ? s_wf[k][h8] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ow[i] += a * rw8[k][0][i];
+          ow[4 + i] += a * rw8[k][1][i];
+        }
       }
-      emit(e2, rc[u][0], os0, ow0);
-      emit(e2 + 1, rc[u][1], os1, ow1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        oc[i] = rc8[0][i];
+        oc[4 + i] = rc8[1][i];
+      }
+    } else {
+      for (int k = 0; k < nsp; ++k) {
+        const f32x4_t x0 = ld4_coherent(rr, (uint32_t)(k * RSTRIDE + 32 + e8) * 4);
+        const f32x4_t x1 = ld4_coherent(rr, (uint32_t)(k * RSTRIDE + 32 + e8 + 4) * 4);
+        const float a = s_pf[k][h8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          os[i] += a * x0[i];
+          os[4 + i] += a * x1[i];
+        }
+      }
+      for (int k = 0; k < nwin; ++k) {
+        const float a = s_wf[k][h8];
+        for (int i = 0; i < 8; ++i) ow[i] += a * wp[(size_t)k * WSTRIDE + 32 + e8 + i];
+      }
+      const f32x4_t c0 = ld4_coherent(ro, (uint32_t)e8 * 4), c1 = ld4_coherent(ro, (uint32_t)(e8 + 4) * 4);
+      for (int i = 0; i < 4; ++i) {
+        oc[i] = c0[i];
+        oc[4 + i] = c1[i];
+      }
     }
-  } else {
-    for (int e = tid; e < p.G * DV; e += NTH) {
-      const int h = e / DV;
-      float os = 0.f, ow = 0.f;
-      for (int k = 0; k < p.nfin; ++k) os += s_pf[k][h] * ld_shared_dev(rp + (size_t)k * PSTRIDE + 32 + e);
-      for (int k = 0; k < p.nwin; ++k) ow += s_wf[k][h] * wp[(size_t)k * PSTRIDE + 32 + e];
-      emit(e, ld_shared_dev(oc_src + e), os, ow);
-    }
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = s_gate[h8][0] * oc[i] + s_gate[h8][1] * os[i] + s_gate[h8][2] * ow[i];
+    *reinterpret_cast<u32x4_t*>(p.out + ((size_t)b * p.Hq + (size_t)g * p.G + h8) * DV + (e8 - h8 * DV)) =
+        u32x4_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
   }
+  clk_stamp(clk, 7);
 }
 
 // ---------------------------------------------------------------- host side
@@ -973,10 +1096,11 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   lay.off_o1 = off;   off = align256(off + BH * lay.nch * 16 * (size_t)DV * 4);
   lay.off_sc1 = off;  off = align256(off + BH * lay.nch * 16 * (size_t)(lay.nbo + 1) * 4);
   lay.off_wpart = off; off = align256(off + BH * lay.nwin * (32 + 16 * (size_t)DV) * 4);
-  // finish workgroups (4 waves, one 32-token step each): one partial each; the
-  // normalised compressed-branch output; the arrival counters
+  // finish workgroups (kFinWaves waves, one 32-token step each): one partial
+  // each (m, l and the output divided by l); the normalised compressed-branch output;
+  // the arrival counters
   const int spb = lsel >= 32 ? lsel / 32 : 1;
-  lay.nfin = (n * spb + NSA_FIN_WAVES - 1) / NSA_FIN_WAVES;
+  lay.nfin = (n * spb + kFinWaves - 1) / kFinWaves;
   lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
   lay.off_ocmp = off; off = align256(off + BH * 16 * (size_t)DV * 4);
   lay.off_cnt = off; off = align256(off + BH * 4);
@@ -985,8 +1109,8 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
 }
 
 // With events, each kernel is launched with its start / stop events attached
-// to the dispatch (ev[0], ev[1]: streaming kernel; ev[2], ev[3]: finish kernel),
-// so their elapsed times are the kernels' own execution times.
+// to the dispatch (ev[0], ev[1]: streaming kernel; ev[2], ev[3]: finish
+// kernel), so their elapsed times are the kernels' own execution times.
 template <int DK, int DV>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const PhaseEvents* ev) {
   hipEvent_t e0 = ev ? ev->ev[0] : nullptr, e1 = ev ? ev->ev[1] : nullptr;
@@ -995,7 +1119,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const Ph
                         dim3(64 * kStreamWaves), 0, s, e0, e1, 0, p);
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(64 * NSA_FIN_WAVES);
+  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(64 * kFinWaves);
   switch (p.lsel) {
     case 16: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 16>), g2, blk, 0, s, e2, e3, 0, p); break;
     case 32: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 32>), g2, blk, 0, s, e2, e3, 0, p); break;

@@ -21,8 +21,15 @@ constexpr int kMaxBlocks = 8192;     // selection candidates J+1
 constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query
 constexpr int kGPad = 16;            // query heads per group, padded to one MFMA tile
-constexpr int kMaxFinish = 16;       // decode finish workgroups per (sequence, group)
+constexpr int kMaxFinish = 16;       // decode selection workgroups per (sequence, group)
+constexpr int kFinWaves = 4;         // waves per decode selection workgroup
 constexpr int kMaxWindow = 16;       // decode window workgroups per (sequence, group)
+
+// Profiling hook: with a phase-clock buffer, thread 0 of every workgroup of the
+// decode kernels records the 100 MHz constant clock at kClkSlots numbered
+// points; kernel k's workgroup w uses entries [(k*kClkMaxGroups + w)*kClkSlots, +kClkSlots).
+constexpr int kClkSlots = 16;
+constexpr int kClkMaxGroups = 4096;
 
 // Everything the decode kernels need; plain values and device pointers.
 struct DecodeParams {
@@ -49,15 +56,16 @@ struct DecodeParams {
   float* l1;                         // [B*H, nch, 16]
   float* o1;                         // [B*H, nch, 16, DV]
   float* sc1;                        // [B*H, nch, nbo+1, 16] selection-block scores per head
-  float* wpart;                      // [B*H, nwin, 32 + 16*DV] window-workgroup partials
-  float* rpart;                      // [B*H, nfin, 32 + 16*DV] routed-block partials
+  float* wpart;                      // [B*H, nwin, 32 + 16*DV] window-workgroup partials (m, l, o)
+  float* rpart;                      // [B*H, nfin, 32 + 16*DV] selected partials (m, l, o / l)
   float* ocmp;                       // [B*H, 16, DV] normalised compressed-branch output
-  uint32_t* cnt;                     // [B*H] finish-workgroup arrival counters
+  uint32_t* cnt;                     // [B*H] selection-workgroup arrival counters
+  uint64_t* clk;                     // phase clock (profiling) or null
   int nch;                           // compressed segments per (sequence, group)
   int seg;                           // compressed keys per segment (multiple of 64 and of lsel/d)
   int nbo;                           // selection blocks owned by one segment = seg*d/lsel
+  int nfin;                          // selection workgroups per (sequence, group)
   int wtiles;                        // 64-token window tiles per window workgroup
-  int nfin;                          // finish workgroups per (sequence, group)
   int nwin;                          // window workgroups per (sequence, group)
 };
 

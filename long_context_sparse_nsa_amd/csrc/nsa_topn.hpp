@@ -143,7 +143,7 @@ __device__ __forceinline__ void block_topn(const float* S, int J, int n, int nlo
 
 // ---------------------------------------------------------------------------
 // Rank-based block top-n (the fast path for up to 8 candidates per thread and
-// nr <= 16 routed picks).  Keys as above (unique, 0 = no candidate).
+// nr <= 64 routed picks).  Keys as above (unique, 0 = no candidate).
 //  1. every lane takes the maximum of its keys; the nr-th largest lane maximum
 //     of the wave is a threshold tau: every key among the wave's nr largest is
 //     >= tau (otherwise nr lane maxima would exceed it), and at most K*nr keys
@@ -157,7 +157,7 @@ template <int NW>
 struct __attribute__((aligned(16))) TopnFastSmem {
   __attribute__((aligned(16))) uint64_t lmax[NW][64];
   __attribute__((aligned(16))) uint64_t surv[NW][144];  // <= 128 survivors, zero padded to a multiple of 16
-  __attribute__((aligned(16))) uint64_t best[NW * 16];  // the waves' winners, contiguous: wave w at [w*nr, (w+1)*nr)
+  __attribute__((aligned(16))) uint64_t best[NW * kTopnMaxRouted + 16];  // the waves' winners: wave w at [w*nr, (w+1)*nr)
   __attribute__((aligned(16))) int ids[64];
   int fail;
 };
@@ -183,13 +183,14 @@ __device__ __forceinline__ void wave_lds_sync() {  // LDS writes of this wave vi
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Ranks the T (<= 128) keys in surv (zero padded to a multiple of 16) and
+// Ranks the T (<= 64 * SL) keys in surv (zero padded to a multiple of 16) and
 // writes those with rank < nr to dst[rank]; dst[T .. nr) are set to 0.
+template <int SL = 2>
 __device__ __forceinline__ void rank_into(const uint64_t* surv, int T, int nr, uint64_t* dst) {
   const int lane = threadIdx.x & 63;
   const int nb = (T + 15) >> 4;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < SL; ++s) {
     const int idx = lane + 64 * s;
     if (idx < T) {
       const uint64_t x = surv[idx];
@@ -246,7 +247,7 @@ __device__ __forceinline__ bool wave_rank_topn(const uint64_t (&k)[K], int nr, u
 
 // Block top-n with the rank-based fast path; falls back to block_topn (which
 // reads S again) when a wave has more than 128 survivors, more than K
-// candidates per thread are needed, or nr > 16.
+// candidates per thread are needed, or nr > 64.
 template <int NT, int K, int MAXC>
 __device__ __forceinline__ void block_topn_fast(const float* S, int J, int n, int nloc, int finit, TopnFastSmem<NT / 64>& fs,
                                 TopnSmem& sm, int32_t* out, int32_t* out2) {
@@ -257,7 +258,7 @@ __device__ __forceinline__ void block_topn_fast(const float* S, int J, int n, in
   const bool f0 = finit && lo_local > 0;
   const int nf = (J - lo_local + 1) + (f0 ? 1 : 0);
   const int nr = n - nf;
-  if (ncand <= n || nr <= 0 || nr > 16 || ncand > NT * K) {
+  if (ncand <= n || nr <= 0 || nr > kTopnMaxRouted || ncand > NT * K) {
     block_topn<NT, MAXC>(S, J, n, nloc, finit, sm, out, out2);
     return;
   }
@@ -284,7 +285,8 @@ __device__ __forceinline__ void block_topn_fast(const float* S, int J, int n, in
     pad16(fs.best, T);
     wave_lds_sync();
     uint64_t* win = fs.surv[0];
-    rank_into(fs.best, T, nr, win);
+    if (T <= 128) rank_into<2>(fs.best, T, nr, win);
+    else rank_into<4>(fs.best, T, nr, win);
     wave_lds_sync();
     int v = INT32_MAX;
     if (lane < nr) v = (int)(0xFFFFFFFFu - (uint32_t)(win[lane] & 0xFFFFFFFFull));
@@ -345,6 +347,298 @@ __device__ __forceinline__ void wave_topn(const float* S, int J, int n, int nloc
   int rank = 0;
   for (int q = 0; q < n; ++q) rank += __builtin_amdgcn_readlane(v, q) < v;
   if (lane < n) out[rank] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Single-wave top-n with an in-register bitonic network (no barrier).
+//
+// Lane l holds candidates j = 256*c + 4*l + e (c < K/4, e < 4) as the unique
+// keys above.  1. the lane maxima are sorted across the wave (descending); the
+// n_r-th of them, tau, is a lower bound of the n_r-th largest key (the n_r
+// largest lane maxima are n_r distinct keys), and every key >= tau lies in one
+// of those n_r lanes, so at most K*n_r keys survive (about n_r + a few for
+// scores in random order).  2. up to 64 survivors are sorted across the wave
+// by the same network (up to 256 are ranked by counting); the first n_r are
+// the routed picks.  3. the picks and the forced blocks are sorted ascending.
+// Exact and deterministic; a fallback extracts the maxima one by one when more
+// than 256 keys survive.
+
+// Value of lane (lane ^ J) for J = 1, 2, 4, 8 (DPP within a row of 16),
+// 16 and 32 (gfx950 permlane swaps, which give each lane its own and its
+// partner's value).
+template <int J>
+__device__ __forceinline__ uint32_t xor_partner(uint32_t x) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x104, 0xF, 0xF, false);  // row_shl:4
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (J == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return a[0] ^ a[1] ^ x;
+  } else {
+    static_assert(J == 32, "partner distance");
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return a[0] ^ a[1] ^ x;
+  }
+}
+
+// One compare-exchange stage of a bitonic network over the wave (merge size
+// KB, partner distance J) on 64-bit keys; DESC: the whole sort is descending.
+template <int KB, int J, bool DESC>
+__device__ __forceinline__ void bitonic_stage(uint32_t& hi, uint32_t& lo) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t ph = xor_partner<J>(hi), pl = xor_partner<J>(lo);
+  const bool gt = hi > ph || (hi == ph && lo > pl);
+  const bool first_half = (lane & KB) == 0;         // this block runs in the sort's direction
+  const bool lower = (lane & J) == 0;
+  const bool keep_big = (lower == first_half) == DESC;
+  if (keep_big ? !gt : gt) {
+    hi = ph;
+    lo = pl;
+  }
+}
+
+template <int KB, int J, bool DESC>
+__device__ __forceinline__ void bitonic_merge(uint32_t& hi, uint32_t& lo) {
+  bitonic_stage<KB, J, DESC>(hi, lo);
+  if constexpr (J > 1) bitonic_merge<KB, J / 2, DESC>(hi, lo);
+}
+
+// Sorts the 64 lanes' keys (hi:lo) across the wave; lane r ends with the
+// r-th largest (DESC) or smallest.
+template <bool DESC, int KB = 2>
+__device__ __forceinline__ void wave_bitonic_sort(uint32_t& hi, uint32_t& lo) {
+  bitonic_merge<KB, KB / 2, DESC>(hi, lo);
+  if constexpr (KB < 64) wave_bitonic_sort<DESC, KB * 2>(hi, lo);
+}
+
+__device__ __forceinline__ uint64_t u64_of(uint32_t hi, uint32_t lo) { return ((uint64_t)hi << 32) | lo; }
+
+// Top-n for one (query, KV group) by wave 0 of a workgroup alone: candidates
+// 0..J (J + 1 <= 16 * K) with group scores S[j] >= 0 in LDS.  Writes the
+// selected ids ascending to items[0 .. count) (LDS) and, when sel_out is not
+// null, to sel_out[0 .. n) padded with -1; returns count (wave-uniform).
+// scratch: LDS of at least 320 64-bit words.
+template <int K>
+__device__ __forceinline__ int wave_topn_sorted(const float* S, int J, int n, int nloc, int finit, uint64_t* scratch,
+                                                int* items, int32_t* sel_out) {
+  static_assert(K % 4 == 0 && K <= 32, "candidates per lane");
+  const int lane = threadIdx.x & 63;
+  const int ncand = J + 1;
+  if (ncand <= n) {
+    for (int r = lane; r < n; r += 64) {
+      if (r < ncand) items[r] = r;
+      if (sel_out) sel_out[r] = r < ncand ? r : -1;
+    }
+    return ncand;
+  }
+  const int lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;  // local blocks are [lo_local, J]
+  const bool f0 = finit && lo_local > 0;
+  const int nf = (J - lo_local + 1) + (f0 ? 1 : 0);
+  const int nr = n - nf;
+  uint32_t idv = 0xFFFFFFFFu;  // this lane's id in the final ascending sort (lanes < n)
+  if (nr > 0) {
+    // ---- the candidates' keys (0 = not a candidate)
+    uint64_t k[K];
+#pragma unroll
+    for (int c = 0; c < K / 4; ++c) {
+      const int j0 = 256 * c + 4 * lane;
+      float4 s4 = {0.f, 0.f, 0.f, 0.f};
+      if (j0 < ncand) s4 = *reinterpret_cast<const float4*>(S + j0);  // S is padded to a multiple of 4
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        const bool ok = j < lo_local && !(f0 && j == 0);
+        k[4 * c + e] = ok ? u64_of(__float_as_uint(sv[e]), 0xFFFFFFFFu - (uint32_t)j) : 0ull;
+      }
+    }
+    // ---- 1. threshold: the nr-th largest lane maximum
+    uint64_t km = k[0];
+#pragma unroll
+    for (int c = 1; c < K; ++c) km = k[c] > km ? k[c] : km;
+    uint32_t th = (uint32_t)(km >> 32), tl = (uint32_t)km;
+    wave_bitonic_sort<true>(th, tl);
+    uint64_t tau = u64_of((uint32_t)__builtin_amdgcn_readlane((int)th, nr - 1),
+                          (uint32_t)__builtin_amdgcn_readlane((int)tl, nr - 1));
+    if (tau == 0ull) tau = 1ull;  // fewer than nr lanes hold candidates: all of them survive
+    // ---- 2. survivors, compacted into scratch
+    const uint64_t below = (1ull << lane) - 1ull;
+    int T = 0;
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      const bool sv = k[c] >= tau;  // tau >= 1, so never a non-candidate
+      const uint64_t m = __ballot(sv);
+      const int pos = T + __popcll(m & below);
+      if (sv && pos < 256) scratch[pos] = k[c];
+      T += __popcll(m);
+    }
+    uint64_t win = 0ull;  // lane r < nr: the r-th largest routed key
+    if (T <= 64) {
+      wave_lds_sync();
+      const uint64_t x = lane < T ? scratch[lane] : 0ull;
+      uint32_t xh = (uint32_t)(x >> 32), xl = (uint32_t)x;
+      wave_bitonic_sort<true>(xh, xl);
+      win = u64_of(xh, xl);
+    } else if (T <= 256) {
+      pad16(scratch, T);
+      wave_lds_sync();
+      uint64_t* dst = scratch + 256;  // 16 words after the padded list
+      rank_into<4>(scratch, T, nr, dst);
+      wave_lds_sync();
+      win = lane < nr ? dst[lane] : 0ull;
+    } else {  // many equal-score keys can defeat the threshold: extract the maxima one by one
+      win = wave_extract<K>(k, nr);
+    }
+    if (lane < nr) idv = 0xFFFFFFFFu - (uint32_t)win;
+  }
+  if (lane >= (nr > 0 ? nr : 0) && lane < n) {
+    const int i = lane - (nr > 0 ? nr : 0);  // forced block i
+    if (i < nf) idv = (uint32_t)(f0 ? (i == 0 ? 0 : lo_local + i - 1) : lo_local + i);
+  }
+  // ---- 3. ascending ids (unused lanes hold 0xFFFFFFFF and sort last)
+  uint32_t z = 0;
+  wave_bitonic_sort<false>(idv, z);
+  const int cnt = n < nf + (nr > 0 ? nr : 0) ? n : nf + (nr > 0 ? nr : 0);
+  if (lane < cnt) items[lane] = (int)idv;
+  if (sel_out && lane < n) sel_out[lane] = lane < cnt ? (int)idv : -1;
+  return cnt;
+}
+
+// Wave-wide minimum of an unsigned value (DPP row shifts and broadcasts as in
+// wave_max_u32, on the complement).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return 0xFFFFFFFFu - wave_max_u32(0xFFFFFFFFu - x); }
+
+// Top-n for one (query, KV group) by one wave, without sorting networks:
+// candidates 0..J (J + 1 <= 16 * K) with group scores S[j] >= 0 in LDS, lane l
+// holding j = 256*c + 4*l + e (c < K/4, e < 4).
+//  1. threshold: with v_0 >= v_1 >= ... the lanes' maximum scores (32-bit, ties
+//     allowed), tau = v_{nr-1} is found as the minimum over the lanes whose
+//     maximum is exceeded by fewer than nr others (counted with broadcast LDS
+//     reads); every score among the nr largest is >= tau, and only the nr
+//     lanes whose maximum is >= tau can hold such scores;
+//  2. the survivors (score >= tau, usually about nr + a few) are compacted by
+//     ballot into LDS as 64-bit keys (score bits << 32 | ~j, so equal scores
+//     prefer the lower id) and ranked exactly by counting larger keys;
+//  3. the routed picks and the forced blocks are put in ascending order by
+//     counting smaller ids.
+// Writes the ids ascending to items[0 .. count) (LDS) and, when sel_out is not
+// null, to sel_out[0 .. n) padded with -1; returns count (wave-uniform).
+// scratch: LDS of at least 416 64-bit words.  Exact and deterministic; more
+// than 256 survivors (possible only with many equal scores) take the one-by-one
+// extraction instead.
+template <int K>
+__device__ __forceinline__ int wave_topn_fast(const float* S, int J, int n, int nloc, int finit, uint64_t* scratch,
+                                              int* items, int32_t* sel_out) {
+  static_assert(K % 4 == 0 && K <= 32, "candidates per lane");
+  const int lane = threadIdx.x & 63;
+  const int ncand = J + 1;
+  if (ncand <= n) {
+    for (int r = lane; r < n; r += 64) {
+      if (r < ncand) items[r] = r;
+      if (sel_out) sel_out[r] = r < ncand ? r : -1;
+    }
+    return ncand;
+  }
+  const int lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;  // local blocks are [lo_local, J]
+  const bool f0 = finit && lo_local > 0;
+  const int nf = (J - lo_local + 1) + (f0 ? 1 : 0);
+  const int nr = n - nf;
+  uint32_t* lmax = reinterpret_cast<uint32_t*>(scratch);      // 64 words (as 32 64-bit words)
+  uint64_t* surv = scratch + 32;                              // up to 256 keys + 16 of padding
+  uint64_t* win = scratch + 32 + 272;                         // nr <= 64 winners
+  int* ids = reinterpret_cast<int*>(scratch + 32 + 272 + 64);  // n <= 64 ids (32 words)
+  int myid = INT32_MAX;
+  if (nr > 0) {
+    // ---- scores as 32-bit keys: bits + 1 (0 = not a candidate)
+    uint32_t k[K];
+#pragma unroll
+    for (int c = 0; c < K / 4; ++c) {
+      const int j0 = 256 * c + 4 * lane;
+      float4 s4 = {0.f, 0.f, 0.f, 0.f};
+      if (j0 < ncand) s4 = *reinterpret_cast<const float4*>(S + j0);  // S is padded to a multiple of 4
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        const bool ok = j < lo_local && !(f0 && j == 0);
+        k[4 * c + e] = ok ? __float_as_uint(sv[e]) + 1u : 0u;
+      }
+    }
+    // ---- 1. threshold
+    uint32_t km = k[0];
+#pragma unroll
+    for (int c = 1; c < K; ++c) km = max(km, k[c]);
+    lmax[lane] = km;
+    wave_lds_sync();
+    int above = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint4 a = reinterpret_cast<const uint4*>(lmax)[q];
+      above += (a.x > km) + (a.y > km) + (a.z > km) + (a.w > km);
+    }
+    uint32_t tau = wave_min_u32(above < nr ? km : 0xFFFFFFFFu);
+    if (tau == 0u) tau = 1u;  // fewer than nr lanes hold candidates: all of them survive
+    // ---- 2. survivors, compacted by ballot, then ranked exactly
+    const uint64_t below = (1ull << lane) - 1ull;
+    int T = 0;
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      const bool sv = k[c] >= tau;
+      const uint64_t m = __ballot(sv);
+      const int pos = T + __popcll(m & below);
+      if (sv && pos < 256) {
+        const uint32_t j = (uint32_t)(256 * (c >> 2) + 4 * lane + (c & 3));
+        surv[pos] = ((uint64_t)(k[c] - 1u) << 32) | (uint64_t)(0xFFFFFFFFu - j);
+      }
+      T += __popcll(m);
+    }
+    if (T <= 256) {
+      pad16(surv, T);
+      wave_lds_sync();
+      rank_into<4>(surv, T, nr, win);
+      wave_lds_sync();
+      if (lane < nr) myid = (int)(0xFFFFFFFFu - (uint32_t)win[lane]);
+    } else {  // many equal scores: extract the maxima one by one from 64-bit keys
+      uint64_t kk[K];
+#pragma unroll
+      for (int c = 0; c < K; ++c) {
+        const uint32_t j = (uint32_t)(256 * (c >> 2) + 4 * lane + (c & 3));
+        kk[c] = k[c] ? ((uint64_t)(k[c] - 1u) << 32) | (uint64_t)(0xFFFFFFFFu - j) : 0ull;
+      }
+      const uint64_t w = wave_extract<K>(kk, nr);
+      if (lane < nr) myid = (int)(0xFFFFFFFFu - (uint32_t)w);
+    }
+  }
+  const int nrp = nr > 0 ? nr : 0;
+  if (lane >= nrp && lane < nrp + nf) {
+    const int i = lane - nrp;  // forced block i
+    myid = f0 ? (i == 0 ? 0 : lo_local + i - 1) : lo_local + i;
+  }
+  // ---- 3. ascending order: the rank of each id among the cnt (distinct) ids
+  const int cnt = nrp + nf < n ? nrp + nf : n;
+  ids[lane] = myid;
+  wave_lds_sync();
+  int rk = 0;
+  for (int q0 = 0; q0 < cnt; q0 += 16) {
+    int4 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = reinterpret_cast<const int4*>(ids)[q0 / 4 + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rk += (a[i].x < myid) + (a[i].y < myid) + (a[i].z < myid) + (a[i].w < myid);
+  }
+  if (lane < cnt) {
+    items[rk] = myid;
+    if (sel_out) sel_out[rk] = myid;
+  }
+  if (sel_out && lane >= cnt && lane < n) sel_out[lane] = -1;
+  return cnt;
 }
 
 }  // namespace nsa

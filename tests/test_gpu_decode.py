@@ -127,3 +127,16 @@ def test_decode_block_shapes(params, L):
     kc, vc, _ = U.oracle_cmp_cache(case)
     out, sel, _ = U.run_decode(case, kc, vc)
     _check_decode(case, out, sel)
+
+
+@pytest.mark.parametrize("name", [STD, "decode_ragged_16"])
+def test_decode_tied_scores(name):
+    """Zero queries give every visible compressed block the same probability, so
+    the group scores of whole selection blocks tie up to rounding: the top-n's
+    tie rule and its many-survivor paths run.  The selection must be a valid
+    top-n under the tie tolerance and the output must match the oracle."""
+    case = I.generate(I.workload(name, batch=2, seq_len=9000, ragged_min=5000 if name != STD else None), 21)
+    case.q = np.zeros_like(case.q)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    out, sel, _ = U.run_decode(case, kc, vc)
+    _check_decode(case, out, sel)
