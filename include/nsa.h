@@ -181,6 +181,30 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg,
                             void* stream);
 
 /*
+ * nsa_decode_fwd_noalloc — nsa_decode_fwd without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, layouts,
+ * validation and results are those of nsa_decode_fwd (the same kernels run);
+ * the workspace is instead a fixed array of 32 MiB that the library holds in
+ * device memory, one copy per GPU, until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ * A step whose workspace (nsa_decode_workspace_size) exceeds 32 MiB returns
+ * NSA_ERROR_UNSUPPORTED with the sizes in nsa_last_error(); the 64k / batch 8,
+ * 128k / batch 4 and ragged 16-sequence workloads need 6.5, 5.3 and 15.6 MiB.
+ * Every call on a GPU shares that GPU's array and nothing in it needs to start
+ * at a particular value, but calls that overlap in time on one GPU (other
+ * streams, other threads) race on it: order them on one stream.
+ */
+nsa_status_t nsa_decode_fwd_noalloc(const nsa_dims_t* dims, const nsa_config_t* cfg,
+                                    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                    const uint16_t* k_cmp_cache, const uint16_t* v_cmp_cache,
+                                    const int32_t* seq_lens, const int64_t* cu_seqlens, const int64_t* cu_cmp,
+                                    int64_t max_seq_len, const float* gates,
+                                    const uint16_t* w_gate, const float* b_gate, uint16_t* out,
+                                    int32_t* sel_idx_out, void* stream);
+
+/*
  * nsa_prefill_fwd — causal prefill of B sequences of seq_len tokens each: every
  * position t attends per the three branches (compressed blocks whose last token
  * is <= t; the selected blocks' tokens <= t; the window t-w < x <= t).

@@ -20,6 +20,7 @@ from ._abi import (  # noqa: F401
     nsa_config_t,
     make_dsa_dims,
     nsa_decode_fwd,
+    nsa_decode_fwd_noalloc,
     nsa_dsa_decode_fwd,
     nsa_dsa_decode_workspace_size,
     nsa_dsa_dims_t,

@@ -68,6 +68,8 @@ _SIGS = {
     "nsa_compress_append_workspace_size": [_VP, _VP, ctypes.POINTER(ctypes.c_size_t)],
     "nsa_decode_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP,
                        _VP, ctypes.c_size_t, _VP],
+    "nsa_decode_fwd_noalloc": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP,
+                               _VP, _VP, _VP],
     "nsa_prefill_fwd": [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                         _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP],
     "nsa_decode_workspace_size": [_VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
@@ -212,6 +214,21 @@ def nsa_decode_fwd(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq
                               _ptr(workspace, "workspace"),
                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
                               _stream(stream)))
+
+
+def nsa_decode_fwd_noalloc(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, cu_seqlens, cu_cmp,
+                           max_seq_len, gates, out, sel_idx_out, stream=None, w_gate=None, b_gate=None):
+    """nsa_decode_fwd with the library's own device-resident scratch instead of a workspace."""
+    lib = load_library()
+    B, Hq, H = dims.batch, dims.num_q_heads, dims.num_kv_heads
+    _check(lib.nsa_decode_fwd_noalloc(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q, "q", 2, B * Hq * dims.d_k),
+                                      _ptr(k_cache, "k_cache", 2), _ptr(v_cache, "v_cache", 2),
+                                      _ptr(k_cmp_cache, "k_cmp_cache", 2), _ptr(v_cmp_cache, "v_cmp_cache", 2),
+                                      _ptr(seq_lens, "seq_lens", 4, B), _ptr(cu_seqlens, "cu_seqlens", 8, B + 1),
+                                      _ptr(cu_cmp, "cu_cmp", 8, B + 1), int(max_seq_len),
+                                      _ptr(gates, "gates", 4, B * Hq * 3), _ptr(w_gate, "w_gate", 2, Hq * 3 * dims.d_k),
+                                      _ptr(b_gate, "b_gate", 4, Hq * 3), _ptr(out, "out", 2, B * Hq * dims.d_v),
+                                      _ptr(sel_idx_out, "sel_idx_out", 4, B * H * cfg.n_sel), _stream(stream)))
 
 
 def nsa_prefill_fwd(dims, cfg, seq_len, q, k, v, k_cmp, v_cmp, w_k, pe_k, w_v, pe_v, gates, out, sel_idx_out,

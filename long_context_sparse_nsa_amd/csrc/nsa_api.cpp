@@ -373,23 +373,29 @@ nsa_status_t nsa_compress_append(const nsa_dims_t* dims, const nsa_config_t* cfg
   return ok();
 }
 
-nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* q,
-                            const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_cmp_cache,
-                            const uint16_t* v_cmp_cache, const int32_t* seq_lens, const int64_t* cu_seqlens,
-                            const int64_t* cu_cmp, int64_t max_seq_len, const float* gates,
-                            const uint16_t* w_gate, const float* b_gate, uint16_t* out,
-                            int32_t* sel_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks of a decode call that do not depend on where its workspace lives.
+nsa_status_t check_decode_call(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* q,
+                               const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_cmp_cache,
+                               const uint16_t* v_cmp_cache, const int32_t* seq_lens, int64_t max_seq_len,
+                               const float* gates, const uint16_t* w_gate, const float* b_gate,
+                               const uint16_t* out) {
   nsa_status_t st = check_common(dims, cfg, true);
   if (st != NSA_SUCCESS) return st;
   if (!q || !k_cache || !v_cache || !k_cmp_cache || !v_cmp_cache || !seq_lens || !out)
     return fail(NSA_ERROR_INVALID_VALUE, "a tensor pointer is NULL");
   if ((st = check_gates(gates, w_gate, b_gate)) != NSA_SUCCESS) return st;
-  if ((st = check_decode_sizes(dims, cfg, max_seq_len)) != NSA_SUCCESS) return st;
-  const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
-                                                   cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
-  if (!workspace || workspace_bytes < lay.total)
-    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
-                workspace ? workspace_bytes : (size_t)0);
+  return check_decode_sizes(dims, cfg, max_seq_len);
+}
+
+// Launches a validated decode step with the workspace at `workspace`.
+nsa_status_t decode_launch(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* q,
+                           const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_cmp_cache,
+                           const uint16_t* v_cmp_cache, const int32_t* seq_lens, const int64_t* cu_seqlens,
+                           const int64_t* cu_cmp, int64_t max_seq_len, const float* gates,
+                           const uint16_t* w_gate, const float* b_gate, uint16_t* out, int32_t* sel_idx_out,
+                           const nsa::DecodeLayout& lay, void* workspace, void* stream) {
   char* ws = static_cast<char*>(workspace);
   nsa::DecodeParams p{};
   p.B = dims->batch;
@@ -439,6 +445,49 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, con
   hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+}  // namespace
+
+nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* q,
+                            const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_cmp_cache,
+                            const uint16_t* v_cmp_cache, const int32_t* seq_lens, const int64_t* cu_seqlens,
+                            const int64_t* cu_cmp, int64_t max_seq_len, const float* gates,
+                            const uint16_t* w_gate, const float* b_gate, uint16_t* out,
+                            int32_t* sel_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  nsa_status_t st = check_decode_call(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, max_seq_len,
+                                      gates, w_gate, b_gate, out);
+  if (st != NSA_SUCCESS) return st;
+  const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
+                                                   cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(NSA_ERROR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : (size_t)0);
+  return decode_launch(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, cu_seqlens, cu_cmp,
+                       max_seq_len, gates, w_gate, b_gate, out, sel_idx_out, lay, workspace, stream);
+}
+
+nsa_status_t nsa_decode_fwd_noalloc(const nsa_dims_t* dims, const nsa_config_t* cfg, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_cmp_cache,
+                                    const uint16_t* v_cmp_cache, const int32_t* seq_lens, const int64_t* cu_seqlens,
+                                    const int64_t* cu_cmp, int64_t max_seq_len, const float* gates,
+                                    const uint16_t* w_gate, const float* b_gate, uint16_t* out,
+                                    int32_t* sel_idx_out, void* stream) {
+  nsa_status_t st = check_decode_call(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, max_seq_len,
+                                      gates, w_gate, b_gate, out);
+  if (st != NSA_SUCCESS) return st;
+  const nsa::DecodeLayout lay = nsa::decode_layout(dims->batch, dims->num_kv_heads, dims->d_v, cfg->l, cfg->d,
+                                                   cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
+  if (lay.total > nsa::kNoAllocScratchBytes)
+    return fail(NSA_ERROR_UNSUPPORTED,
+                "this decode step needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                "(use nsa_decode_fwd with a workspace)",
+                lay.total, nsa::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = nsa::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "locating the scratch array");
+  return decode_launch(dims, cfg, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, seq_lens, cu_seqlens, cu_cmp,
+                       max_seq_len, gates, w_gate, b_gate, out, sel_idx_out, lay, ws, stream);
 }
 
 nsa_status_t nsa_dsa_decode_workspace_size(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_len,

@@ -173,6 +173,12 @@ struct PhaseEvents {
 };
 
 hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev);
+
+// The allocation-free decode entry point keeps its workspace in one fixed
+// device array per GPU (nsa_noalloc.hip); noalloc_scratch returns its device
+// address on the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_dsa_decode(const DsaParams& p, hipStream_t s, const PhaseEvents* ev);
 // With events, ev[2] is recorded after the first prefill kernel and ev[3] after
 // the second (the caller records ev[0] and ev[1] around the compression).

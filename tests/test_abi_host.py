@@ -256,3 +256,23 @@ def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
         A.load_library()
     with pytest.raises(RuntimeError, match="not found"):
         N.nsa_decode_workspace_size(_dims(), _cfg(), 512)
+
+
+def test_decode_noalloc_rejects_steps_beyond_its_scratch():
+    """The allocation-free decode entry point checks everything nsa_decode_fwd checks
+    and refuses, before any HIP call, a step whose workspace exceeds its 32 MiB array."""
+    lib = A.load_library()
+    f = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    cfg = _cfg()
+    big = _dims(batch=64)
+    assert _ws(big, cfg) > 32 << 20 >= _ws(_dims(), cfg)
+
+    def call(dims, q=f, gates=f, L=65536):
+        return lib.nsa_decode_fwd_noalloc(ctypes.byref(dims), ctypes.byref(cfg), q, f, f, f, f, f, None, None, L,
+                                          gates, None, None, f, None, None)
+    assert call(big) == A.NSA_ERROR_UNSUPPORTED
+    msg = N.nsa_last_error()
+    assert "allocation-free" in msg and str(_ws(big, cfg)) in msg
+    assert call(_dims(), q=None) == A.NSA_ERROR_INVALID_VALUE
+    assert call(_dims(), gates=None) == A.NSA_ERROR_INVALID_VALUE
+    assert call(_dims(d_k=100)) == A.NSA_ERROR_UNSUPPORTED
