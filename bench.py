@@ -136,12 +136,48 @@ def decode_bytes(case, sel):
     return cmp_b + sw_b + io, cmp_b + w_b + q_bytes, sw_b
 
 
-def bench_decode(args, torch, N, I):
-    wl = I.workload(args.workload)
-    seed = list(I.WORKLOADS).index(args.workload)
-    t0 = time.time()
-    case = I.generate(wl, seed)
-    log(f"[bench] generated {wl.name} (seed {seed}) in {time.time() - t0:.1f}s")
+def graph_of_steps(torch, step, idx):
+    """A HIP graph of the decode steps step(i) for i in idx (captured once, replayed)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in idx:
+                step(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps=3):
+    """Median over reps of one replay's elapsed time (ms), each replay bracketed by
+    events with a synchronisation on both sides; also the wall time of the first."""
+    times, wall = [], None
+    for r in range(reps):
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        if wall is None:
+            wall = time.perf_counter() - w0
+        times.append(ev0.elapsed_time(ev1))
+    return float(np.median(times)), wall
+
+
+def bench_decode(args, torch, N, I, name, case=None, headline=False):
+    """One decode workload: K steps replayed from a graph over rotating cache copies
+    (cold caches: the copies exceed the 256 MB Infinity Cache), the same K steps on
+    one copy (warm), 100 steps timed one by one (median, p10, p90), and the two
+    kernels' own durations from events attached to their dispatches."""
+    wl = I.workload(name)
+    seed = list(I.WORKLOADS).index(name)
+    if case is None:
+        t0 = time.time()
+        case = I.generate(wl, seed)
+        log(f"[bench] generated {wl.name} (seed {seed}) in {time.time() - t0:.1f}s")
     dims, cfg, T, max_len, cuc = upload_case(case, torch, N)
     ws = N.new_workspace(N.nsa_decode_workspace_size(dims, cfg, max_len))
     out = torch.empty((wl.batch, wl.num_q_heads, wl.d_v), dtype=torch.bfloat16, device="cuda")
@@ -150,7 +186,7 @@ def bench_decode(args, torch, N, I):
     for _ in range(args.copies - 1):
         copies.append(tuple(x.clone() for x in copies[0]))
     torch.cuda.synchronize()
-    log(f"[bench] {len(copies)} cache copies resident "
+    log(f"[bench] {wl.name}: {len(copies)} cache copies resident "
         f"({sum(x.numel() * 2 for x in copies[0]) * len(copies) / 1e9:.1f} GB)")
 
     def step(i):
@@ -162,94 +198,90 @@ def bench_decode(args, torch, N, I):
         step(i)
     torch.cuda.synchronize()
     ref_out = out.clone()
-
-    # graph of one step per copy, replayed
-    timing = "hip_graph"
     K = args.steps
-    try:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(len(copies)):
-                    step(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(out, ref_out):
-            raise RuntimeError("graph replay differs from eager result")
-        reps = max(1, (K + len(copies) - 1) // len(copies))
-        K = reps * len(copies)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        ev0.record()
-        for _ in range(reps):
-            g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        total_ms = ev0.elapsed_time(ev1)
-        if not torch.equal(out, ref_out):
-            raise RuntimeError("graph replay differs from eager result")
-    except Exception as e:  # graph capture unavailable: eager steps queued behind a sleep kernel
-        log(f"[bench] graph timing unavailable ({e}); eager timing")
-        timing = "eager_queued"
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        torch.cuda._sleep(int(2e7))
-        ev0.record()
-        for i in range(K):
-            step(i)
-        ev1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        total_ms = ev0.elapsed_time(ev1)
+    g = graph_of_steps(torch, step, range(K))
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref_out):
+        raise RuntimeError("graph replay differs from eager result")
+    total_ms, wall = time_graph(torch, g)
+    if not torch.equal(out, ref_out):
+        raise RuntimeError("graph replay differs from eager result")
     ms_step = total_ms / K
+    gw = graph_of_steps(torch, step, [0] * K)  # warm: every step on the same copy
+    warm_ms = time_graph(torch, gw)[0] / K
+    del g, gw
 
-    # per-pass durations from the library's phase events (eager, queued behind a sleep)
-    n_ph = min(K, 60)
+    # 100 steps timed one by one (eager, queued behind a sleep so that the GPU
+    # runs them back to back), each on the next cache copy
+    n_one = 100
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_one)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e7))
+    for i in range(n_one):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    one = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    dist = {"median_us": float(np.median(one)), "p10_us": float(np.percentile(one, 10)),
+            "p90_us": float(np.percentile(one, 90)), "samples": n_one}
+
+    # the kernels' own durations: events attached to each dispatch (eager, queued behind a sleep)
+    n_ph = 60
     hev = HipEvents(4 * n_ph)
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e7))
-    for i in range(n_ph):
-        N.nsa_set_phase_events(hev.ev[4 * i:4 * i + 4])
-        step(i)
-    N.nsa_set_phase_events(None)
+    try:
+        for i in range(n_ph):
+            N.nsa_set_phase_events(hev.ev[4 * i:4 * i + 4])
+            step(i)
+    finally:
+        N.nsa_set_phase_events(None)
     torch.cuda.synchronize()
-    # start / stop events attached to each kernel's dispatch: (0, 1) streaming, (2, 3) finish
     ph = [float(np.mean([hev.ms(4 * i + k, 4 * i + k + 1) for i in range(n_ph)])) for k in (0, 2)]
     hev.close()
-    p1 = ph[0]
-    p2 = ph[1]
+    p1, p2 = ph
     sel_h = sel.cpu().numpy()
     b_step, b_cmp, b_sw = decode_bytes(case, sel_h)
     gbs_step = b_step / (ms_step * 1e-3) / 1e9
     gbs_cmp = b_cmp / (p1 * 1e-3) / 1e9
     res = dict(
-        ms_per_step=ms_step, wall_s=wall, steps=K, timing=timing,
-        tokens_per_s=wl.batch / (ms_step * 1e-3),
+        workload=wl.name, ms_per_step=ms_step, wall_s=wall, steps=K, timing="hip_graph",
+        tokens_per_s=wl.batch / (ms_step * 1e-3), warm_ms_per_step=warm_ms, step_distribution=dist,
         step_bytes=b_step, step_gbs=gbs_step, step_frac=gbs_step / HBM_PEAK_GBS,
         pass1_us=p1 * 1e3, pass2_us=p2 * 1e3, pass1_bytes=b_cmp, pass2_bytes=b_sw,
-        finish_us=ph[1] * 1e3,
-
-        pass1_gbs=gbs_cmp, pass2_gbs=b_sw / (p2 * 1e-3) / 1e9,
-    )
-    log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step ({timing}), {res['tokens_per_s']:.4g} tok/s, "
-        f"{gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); kernels: stream {p1 * 1e3:.1f} us "
-        f"({gbs_cmp:.0f} GB/s), finish {ph[1] * 1e3:.1f} us")
+        finish_us=p2 * 1e3, pass1_gbs=gbs_cmp, pass2_gbs=b_sw / (p2 * 1e-3) / 1e9,
+        needle_hit_gpu=needle_hits(case, sel_h))
+    log(f"[bench] decode {wl.name}: {ms_step * 1e3:.1f} us/step over {K} steps (warm {warm_ms * 1e3:.1f}; one by one "
+        f"median {dist['median_us']:.1f}, p10 {dist['p10_us']:.1f}, p90 {dist['p90_us']:.1f}), "
+        f"{res['tokens_per_s']:.4g} tok/s, {gbs_step:.0f} GB/s step ({100 * gbs_step / HBM_PEAK_GBS:.1f}%); "
+        f"kernels: stream {p1 * 1e3:.1f} us ({gbs_cmp:.0f} GB/s), selection {p2 * 1e3:.1f} us")
+    if not headline:
+        return case, res, T
     res["phase_clock_us"] = decode_phase_clock(torch, N, step)
     log("[bench] decode phase clock (us after the first streaming workgroup starts; median / max over "
         "workgroups): " + ", ".join(f"{k} {v['median_us']}/{v['max_us']}" for k, v in res["phase_clock_us"].items()))
-    if timing == "hip_graph":
-        res["gate_network_ms_per_step"] = bench_gate_network(args, torch, N, case, dims, cfg, T, max_len, copies,
-                                                             out, sel, ws)
-        log(f"[bench] decode step with the gate network: {res['gate_network_ms_per_step'] * 1e3:.1f} us")
-    if timing == "hip_graph" and not args.no_serving:
+    res["gate_network_ms_per_step"] = bench_gate_network(args, torch, N, case, dims, cfg, T, max_len, copies,
+                                                         out, sel, ws)
+    log(f"[bench] decode step with the gate network: {res['gate_network_ms_per_step'] * 1e3:.1f} us")
+    if not args.no_serving:
         res["serving"] = bench_serving(args, torch, N, case, dims, cfg, T, max_len, copies, step)
     return case, res, T
+
+
+def needle_hits(case, sel):
+    """Fraction of the planted needle blocks (l'-aligned) that a selection [B, H, n] took."""
+    p = case.p
+    H = case.wl.num_kv_heads
+    hit = tot = 0
+    for b in range(case.wl.batch):
+        for g in range(H):
+            picks = set(int(j) for j in sel[b, g] if j >= 0)
+            nb = case.needle_blocks[b * H + g]
+            tot += len(nb)
+            hit += sum(1 for j in nb if int(j) in picks)
+    return hit / tot if tot else None
 
 
 CLK_SLOTS, CLK_GROUPS = 16, 4096
@@ -593,6 +625,16 @@ def bench_prefill(args, torch, N, I):
                cmp_win_tflops=(f["cmp"] + f["win"]) / (ph[1] * 1e-3) / 1e12,
                sel_tflops=f["slc"] / (ph[2] * 1e-3) / 1e12)
     res["sel_mfma_frac"] = res["sel_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    # reuse of the staged selected blocks: the selection of one more call, per tile of
+    # positions: the union of the tile's selected blocks (one staged copy each) against
+    # the positions that use them
+    sel = torch.empty((wl.batch, wl.seq_len, wl.num_kv_heads, p.n_sel), dtype=torch.int32, device="cuda")
+    N.nsa_prefill_fwd(dims, cfg, wl.seq_len, q, k, v, None, None, wk, pk, wv, pv, gates, out, sel, ws)
+    torch.cuda.synchronize()
+    res["selected_reuse"] = selection_reuse(sel.cpu().numpy(), p)
+    log("[bench] prefill selected-block reuse: " + ", ".join(
+        f"{k}: union {v['mean_union_blocks']:.1f} blocks, {v['positions_per_staged_block']:.2f} positions per block"
+        for k, v in res["selected_reuse"].items()))
     # the same call with the gates computed in the kernels by the gate network
     wg = dev(case.w_gate)
     bgt = torch.from_numpy(case.b_gate).cuda()
@@ -614,6 +656,27 @@ def bench_prefill(args, torch, N, I):
         f"peak); compress {ph[0]:.3f} ms, cmp+win+top-n {ph[1]:.3f} ms ({res['cmp_win_tflops']:.0f} TFLOP/s), "
         f"selected {ph[2]:.3f} ms ({res['sel_tflops']:.0f} TFLOP/s, {100 * res['sel_mfma_frac']:.1f}%)")
     return res
+
+
+def selection_reuse(sel, p, tiles=(16, 32, 64)):
+    """For position tiles of each size: the mean number of distinct selected blocks of a
+    tile (the blocks one workgroup stages per (sequence, KV group)) and the positions
+    served per staged block (selections made in the tile / distinct blocks), over every
+    tile of every sequence and KV group.  sel is [B, T, H, n], -1 padded."""
+    B, T, H, n = sel.shape
+    out = {}
+    for tile in tiles:
+        nt = T // tile
+        uni = used = 0
+        for b in range(B):
+            for g in range(H):
+                s = sel[b, :nt * tile, g].reshape(nt, tile * n)
+                for row in s:
+                    v = row[row >= 0]
+                    uni += np.unique(v).size
+                    used += v.size
+        out[f"tile_{tile}"] = {"mean_union_blocks": uni / (B * H * nt), "positions_per_staged_block": used / uni}
+    return out
 
 
 def dsa_upload(case, torch, N):
@@ -706,36 +769,89 @@ def bench_dsa(args, torch, N, I):
     return res
 
 
-def cpu_baseline(case, min_seconds):
-    """The float64 oracle on a bounded sample of the decode workload (this host's cores)."""
+_POOL_CASE = None   # the case the forked oracle workers read (shared copy-on-write)
+
+
+def _oracle_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)          # one BLAS thread per worker
+    except Exception:
+        pass
+
+
+def _oracle_pair(task):
+    """One (sequence, KV group) of the decode workload: its compressed cache
+    (untimed: the decode workload holds it precomputed), then the float64 decode
+    query repeated until `seconds` of work.  Returns (queries, seconds, selection)."""
     from oracle import nsa_oracle as O
+    b, g, seconds = task
+    case = _POOL_CASE
+    p = case.p
+    G = case.wl.num_q_heads // case.wl.num_kv_heads
+    K, V, Kc, Vc = O.compress_group(case, b, g)
+    t = int(case.seq_lens[b]) - 1
+    qg = O._widen(case.q[b, g * G:(g + 1) * G])
+    gates = np.asarray(case.gates[b, g * G:(g + 1) * G], np.float64)
+    n, el, idx = 0, 0.0, None
+    while el < seconds or n == 0:
+        t0 = time.perf_counter()
+        r = O.nsa_query(qg, K, V, Kc, Vc, t, gates, p.l, p.d, p.l_sel, p.n_sel, p.n_local, p.force_initial, p.w)
+        el += time.perf_counter() - t0
+        n += 1
+        idx = r.idx
+    return n, el, idx
+
+
+def host_info():
+    """CPU model and the NumPy / BLAS build the oracle ran on."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = [{k: i.get(k) for k in ("internal_api", "version", "architecture")} for i in threadpool_info()]
     except Exception:
-        threads = 1
-    wl, p = case.wl, case.p
-    G = wl.num_q_heads // wl.num_kv_heads
-    seqs = [0, 1]
-    prep = {}
-    for b in seqs:
-        for g in range(wl.num_kv_heads):
-            prep[(b, g)] = O.compress_group(case, b, g)          # cache precompute, untimed
-    tokens, elapsed = 0, 0.0
-    while elapsed < min_seconds:
-        for b in seqs:
-            t = int(case.seq_lens[b]) - 1
-            t0 = time.perf_counter()
-            for g in range(wl.num_kv_heads):
-                K, V, Kc, Vc = prep[(b, g)]
-                O.nsa_query(O._widen(case.q[b, g * G:(g + 1) * G]), K, V, Kc, Vc, t,
-                            np.asarray(case.gates[b, g * G:(g + 1) * G], np.float64), p.l, p.d, p.l_sel,
-                            p.n_sel, p.n_local, p.force_initial, p.w)
-            elapsed += time.perf_counter() - t0
-            tokens += 1
-    return dict(value=tokens / elapsed, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{tokens} decode tokens (sequences {seqs} x {wl.num_kv_heads} KV groups, repeated) of "
-                       f"{wl.name}; oracle-compressed cache precomputed untimed; {elapsed:.1f} s of CPU work")
+        pass
+    return {"cpu_model": model, "numpy": np.__version__, "blas": blas}
+
+
+def cpu_baseline(case, min_seconds):
+    """The float64 oracle on the decode workload, on this host's cores: a pool of
+    one single-threaded worker per core (of this process's affinity set, at most
+    16), each taking (sequence, KV group) pairs of the workload and repeating its
+    decode query for a bounded time.  Throughput = the workers' summed query
+    rates / KV groups per token.  Runs before the GPU is touched (the workers are
+    forked)."""
+    import multiprocessing as mp
+    global _POOL_CASE
+    wl = case.wl
+    cores = min(16, len(os.sched_getaffinity(0)))
+    pairs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    per_task = max(0.5, min_seconds * cores / len(pairs))
+    _POOL_CASE = case
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores, initializer=_oracle_worker_init) as pool:
+        res = pool.map(_oracle_pair, [(b, g, per_task) for b, g in pairs], chunksize=1)
+    wall = time.perf_counter() - t0
+    _POOL_CASE = None
+    rate = sum(n / el for n, el, _ in res) / wl.num_kv_heads      # tokens/s with every worker busy
+    sel = np.full((wl.batch, wl.num_kv_heads, wl.params.n_sel), -1, np.int64)
+    for (b, g), (_, _, idx) in zip(pairs, res):
+        sel[b, g, :len(idx)] = idx
+    work = sum(el for _, el, _ in res)
+    out = dict(value=rate, unit="tokens/s", cores=cores, kind="oracle",
+               sample=f"every (sequence, KV group) pair of {wl.name} ({len(pairs)}), each decode query repeated for "
+                      f"about {per_task:.1f} s on one of {cores} single-threaded workers ({work:.1f} s of CPU work, "
+                      f"{wall:.1f} s wall including the untimed compression of each pair's cache)")
+    out.update(host_info())
+    return out, needle_hits(case, sel)
 
 
 def dsa_cpu_baseline(case, min_seconds):
@@ -826,6 +942,44 @@ def kernels_only(args, torch, N, I):
     log(f"[bench] {args.kernels_only} {'serving' if args.serving else 'decode'} steps of {wl.name} done")
 
 
+def measured_peaks(torch):
+    """Peaks measured on this GPU: HBM by a 4 GiB device copy (read + write) and a
+    4 GiB read-only reduction, bf16 MFMA by a large torch.matmul (hipBLASLt);
+    best of several runs each."""
+    n = 1 << 31  # bf16 elements = 4 GiB
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            ev0.record()
+            fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            t.append(ev0.elapsed_time(ev1))
+        return min(t) * 1e-3
+
+    copy_gbs = 2 * 2 * n / best(lambda: y.copy_(x)) / 1e9
+    xf = x.view(torch.float32)
+    read_gbs = 2 * n / best(lambda: torch.sum(xf)) / 1e9
+    del x, y, xf
+    m = 8192
+    a = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    gemm = 2 * m ** 3 / best(lambda: torch.matmul(a, b), reps=10) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    res = {"hbm_copy_GB/s": copy_gbs, "hbm_read_GB/s": read_gbs, "bf16_gemm_TFLOP/s": gemm,
+           "how": "4 GiB torch copy_ (bytes read + written) and torch.sum over the same 4 GiB (bytes read); "
+                  "torch.matmul 8192^3 bf16; best of 5 / 10"}
+    log(f"[bench] measured peaks: copy {copy_gbs:.0f} GB/s, read {read_gbs:.0f} GB/s, bf16 GEMM {gemm:.0f} TFLOP/s")
+    return res
+
+
 def copy_calibration(torch, mib=256, reps=4):
     """A plain device copy of known size (torch's copy kernel), for scaling the
     HBM byte counters of a profiler run: each launch reads and writes mib MiB."""
@@ -867,6 +1021,7 @@ def main():
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the 128k and ragged decode workloads")
     ap.add_argument("--no-serving", action="store_true", help="skip the append + decode serving-step timing")
     ap.add_argument("--no-dsa", action="store_true", help="skip the DSA decode workload")
     ap.add_argument("--dsa", action="store_true", help="with --kernels-only: DSA decode steps")
@@ -892,25 +1047,49 @@ def main():
     import long_context_sparse_nsa_amd as N
     import nsa_inputs as I
     N.load_library()
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        copy_calibration(torch)
-        return
-    if args.kernels_only:
-        kernels_only(args, torch, N, I)
+    if args.copy_calibration or args.kernels_only:
+        torch.cuda.set_device(0)
+        if args.copy_calibration:
+            copy_calibration(torch)
+        else:
+            kernels_only(args, torch, N, I)
         return
 
-    case, dec, _ = bench_decode(args, torch, N, I)
+    # the headline workload's inputs, and the float64 oracle on this host's cores
+    # (forked workers: before anything touches the GPU)
+    wl = I.workload(args.workload)
+    t0 = time.time()
+    case = I.generate(wl, list(I.WORKLOADS).index(args.workload))
+    log(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s")
+    cpu, needle_oracle = (None, None) if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
+    if cpu:
+        log(f"[bench] cpu oracle: {cpu['value']:.3g} tok/s on {cpu['cores']} single-threaded workers "
+            f"({cpu['cpu_model']}); oracle needle-hit rate {needle_oracle}")
+
+    torch.cuda.set_device(0)
+    peaks = measured_peaks(torch)
+    case, dec, _ = bench_decode(args, torch, N, I, args.workload, case=case, headline=True)
+    others = {}
+    if not args.no_configs:
+        for name in ("decode_128k_b4", "decode_ragged_16"):
+            if name != args.workload:
+                others[name] = bench_decode(args, torch, N, I, name)[1]
+                torch.cuda.empty_cache()
     pre = None if args.no_prefill else bench_prefill(args, torch, N, I)
     bwd = None if args.no_backward else bench_backward(args, torch, N, I)
     dsa = None if args.no_dsa else bench_dsa(args, torch, N, I)
-    cpu = None if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
-    if cpu:
-        log(f"[bench] cpu oracle: {cpu['value']:.3g} tok/s on {cpu['cores']} threads")
 
     khash = src_hash(*DECODE_SOURCES)
-    wl = case.wl
     p = wl.params
+
+    def decode_entry(d):
+        return {"ms_per_step": d["ms_per_step"], "tokens_per_s": d["tokens_per_s"],
+                "warm_ms_per_step": d["warm_ms_per_step"], "step_distribution": d["step_distribution"],
+                "algorithmic_bytes": d["step_bytes"], "GB/s": d["step_gbs"], "hbm_frac": d["step_frac"],
+                "hbm_frac_of_measured_copy": d["step_gbs"] / peaks["hbm_copy_GB/s"],
+                "kernel_us": {"decode_stream_kernel": d["pass1_us"], "decode_finish_kernel": d["finish_us"]},
+                "needle_hit_rate_gpu": d["needle_hit_gpu"]}
+
     line = {
         "metric": METRIC,
         "value": dec["tokens_per_s"],
@@ -931,11 +1110,15 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_stream_kernel (compressed branch, folded scores, window)",
                      "achieved": dec["pass1_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dec["pass1_gbs"] / HBM_PEAK_GBS, "traffic": roofline_from_profiles(khash),
-                     "duration_us": dec["pass1_us"], "algorithmic_bytes": dec["pass1_bytes"]},
-        "decode_step": {"algorithmic_bytes": dec["step_bytes"], "GB/s": dec["step_gbs"],
-                        "hbm_frac": dec["step_frac"],
-                        "kernel_us": {"decode_stream_kernel": dec["pass1_us"], "decode_finish_kernel": dec["finish_us"]},
-                        "wall_s_timed_region": dec["wall_s"]},
+                     "duration_us": dec["pass1_us"], "algorithmic_bytes": dec["pass1_bytes"],
+                     "frac_of_measured_copy": dec["pass1_gbs"] / peaks["hbm_copy_GB/s"],
+                     "step": {"achieved": dec["step_gbs"], "frac": dec["step_frac"],
+                              "frac_of_measured_copy": dec["step_gbs"] / peaks["hbm_copy_GB/s"],
+                              "algorithmic_bytes": dec["step_bytes"], "duration_us": dec["ms_per_step"] * 1e3}},
+        "decode_step": dict(decode_entry(dec), wall_s_timed_region=dec["wall_s"],
+                            phase_clock_us=dec.get("phase_clock_us"), needle_hit_rate_oracle=needle_oracle),
+        "decode_configs": {k: decode_entry(v) for k, v in others.items()},
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     line["gate_network"] = {
@@ -964,8 +1147,12 @@ def main():
         line["prefill"] = {"workload": pre["workload"], "ms": pre["ms"], "TFLOP/s": pre["tflops"],
                            "mfma_frac": pre["mfma_frac"], "flops": pre["flops"],
                            "peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS, "kernel_ms": pre["kernel_ms"],
+                           "mfma_frac_of_measured_gemm": pre["tflops"] / peaks["bf16_gemm_TFLOP/s"],
                            "selected_branch": {"kernel": "pf_sel_kernel", "TFLOP/s": pre["sel_tflops"],
-                                               "mfma_frac": pre["sel_mfma_frac"]},
+                                               "mfma_frac": pre["sel_mfma_frac"],
+                                               "mfma_frac_of_measured_gemm":
+                                                   pre["sel_tflops"] / peaks["bf16_gemm_TFLOP/s"],
+                                               "reuse": pre["selected_reuse"]},
                            "cmp_win_topn": {"kernel": "pf_cmp_win_kernel", "TFLOP/s": pre["cmp_win_tflops"],
                                             "mfma_frac": pre["cmp_win_tflops"] / MFMA_BF16_PEAK_TFLOPS}}
     if bwd:

@@ -682,14 +682,27 @@ __global__ __launch_bounds__(64 * kFinWaves) void decode_finish_kernel(DecodePar
   constexpr int RSTRIDE = 32 + 16 * DV;              // selected partial (m, l, o / l), floats
   constexpr int RPT = 4;                             // candidate blocks per thread and load round
   constexpr int OB = 8;                              // segments per compressed-output load batch
-  __shared__ __attribute__((aligned(16))) float S[kMaxBlocks + 64];
+  // The candidates' scores (until the top-n) share their LDS with the wave-merge
+  // buffer (after the selected steps), and the two top-n paths share theirs, so
+  // that two workgroups fit on a compute unit.
+  constexpr int MB = NWV * 16 * (DV + 1);
+  __shared__ __attribute__((aligned(16))) float s_big[MB > kMaxBlocks + 64 ? MB : kMaxBlocks + 64];
   __shared__ float s_f[kMaxChunks * 16];
   __shared__ float s_ml[2 * kMaxChunks * 16];       // segment m / l, then wave-merge scratch
   __shared__ float s_ov[kMaxChunks * 16];           // overhang score slot of each segment, per head
-  __shared__ float s_buf[NWV * 16 * (DV + 1)];
-  __shared__ TopnSmem tsm;
-  __shared__ TopnFastSmem<NWV> tfs;
-  __shared__ uint64_t s_tw[416];                    // single-wave top-n scratch
+  struct TopnBlock {
+    TopnSmem tsm;
+    TopnFastSmem<NWV> tfs;
+  };
+  __shared__ union TopnLds {
+    TopnBlock blk;                                  // the workgroup's top-n (more than 2048 candidates)
+    uint64_t tw[416];                               // the single-wave top-n
+  } s_topn;
+  float* S = s_big;
+  float* s_buf = s_big;
+  TopnSmem& tsm = s_topn.blk.tsm;
+  TopnFastSmem<NWV>& tfs = s_topn.blk.tfs;
+  uint64_t* s_tw = s_topn.tw;
   __shared__ int s_sel[kMaxSel];
   __shared__ int s_items[kMaxSel];
   __shared__ int s_nitems;
@@ -1074,8 +1087,13 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   // one window workgroup).
   const int64_t win_tiles = (w + 63) / 64 + 1;
   const int64_t bh = (int64_t)B * H;
-  const int64_t per_bg = bh >= kStreamSlots / 2 ? 2 : kStreamSlots / bh;
-  int64_t seg = up((nc + 64 * win_tiles + per_bg - 1) / per_bg);
+  // At least about one workgroup per compute unit, and segments of at most
+  // about kSegTiles tiles, so that the longest sequence of a ragged batch does
+  // not set a long critical path (segments past a shorter sequence end at once).
+  const int64_t rows = nc + 64 * win_tiles;
+  int64_t per_bg = bh >= kStreamSlots / 2 ? 2 : kStreamSlots / bh;
+  if (per_bg < (rows + 64 * kSegTiles - 1) / (64 * kSegTiles)) per_bg = (rows + 64 * kSegTiles - 1) / (64 * kSegTiles);
+  int64_t seg = up((rows + per_bg - 1) / per_bg);
   const int64_t seg_min = up((nc + kMaxChunks - 1) / kMaxChunks);
   const int64_t seg_max = (int64_t)(kScStrideMax - 4) * r / gran * gran;  // score rows fit the LDS table
   if (seg < seg_min) seg = seg_min;

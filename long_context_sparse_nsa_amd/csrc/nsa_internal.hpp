@@ -16,7 +16,8 @@ constexpr int kStreamSlots = 256;
 constexpr int kScStrideMax = 548;     // LDS score row stride limit (floats): selection blocks per segment + 1
 // Limits of the on-chip tables (checked by the host before any launch).
 constexpr int kMaxCompressed = 32768;                 // compressed blocks per sequence in decode
-constexpr int kMaxChunks = 128;                       // compressed segments per sequence in decode
+constexpr int kMaxChunks = 64;                        // compressed segments per sequence in decode
+constexpr int kSegTiles = 10;                         // 64-row tiles per decode segment aimed at (at most)
 constexpr int kMaxBlocks = 8192;     // selection candidates J+1
 constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query

@@ -349,168 +349,6 @@ __device__ __forceinline__ void wave_topn(const float* S, int J, int n, int nloc
   if (lane < n) out[rank] = v;
 }
 
-// ---------------------------------------------------------------------------
-// Single-wave top-n with an in-register bitonic network (no barrier).
-//
-// Lane l holds candidates j = 256*c + 4*l + e (c < K/4, e < 4) as the unique
-// keys above.  1. the lane maxima are sorted across the wave (descending); the
-// n_r-th of them, tau, is a lower bound of the n_r-th largest key (the n_r
-// largest lane maxima are n_r distinct keys), and every key >= tau lies in one
-// of those n_r lanes, so at most K*n_r keys survive (about n_r + a few for
-// scores in random order).  2. up to 64 survivors are sorted across the wave
-// by the same network (up to 256 are ranked by counting); the first n_r are
-// the routed picks.  3. the picks and the forced blocks are sorted ascending.
-// Exact and deterministic; a fallback extracts the maxima one by one when more
-// than 256 keys survive.
-
-// Value of lane (lane ^ J) for J = 1, 2, 4, 8 (DPP within a row of 16),
-// 16 and 32 (gfx950 permlane swaps, which give each lane its own and its
-// partner's value).
-template <int J>
-__device__ __forceinline__ uint32_t xor_partner(uint32_t x) {
-  if constexpr (J == 1) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  } else if constexpr (J == 2) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  } else if constexpr (J == 4) {
-    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x104, 0xF, 0xF, false);  // row_shl:4
-    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
-    return (threadIdx.x & 4) ? dn : up;
-  } else if constexpr (J == 8) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
-  } else if constexpr (J == 16) {
-    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return a[0] ^ a[1] ^ x;
-  } else {
-    static_assert(J == 32, "partner distance");
-    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return a[0] ^ a[1] ^ x;
-  }
-}
-
-// One compare-exchange stage of a bitonic network over the wave (merge size
-// KB, partner distance J) on 64-bit keys; DESC: the whole sort is descending.
-template <int KB, int J, bool DESC>
-__device__ __forceinline__ void bitonic_stage(uint32_t& hi, uint32_t& lo) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t ph = xor_partner<J>(hi), pl = xor_partner<J>(lo);
-  const bool gt = hi > ph || (hi == ph && lo > pl);
-  const bool first_half = (lane & KB) == 0;         // this block runs in the sort's direction
-  const bool lower = (lane & J) == 0;
-  const bool keep_big = (lower == first_half) == DESC;
-  if (keep_big ? !gt : gt) {
-    hi = ph;
-    lo = pl;
-  }
-}
-
-template <int KB, int J, bool DESC>
-__device__ __forceinline__ void bitonic_merge(uint32_t& hi, uint32_t& lo) {
-  bitonic_stage<KB, J, DESC>(hi, lo);
-  if constexpr (J > 1) bitonic_merge<KB, J / 2, DESC>(hi, lo);
-}
-
-// Sorts the 64 lanes' keys (hi:lo) across the wave; lane r ends with the
-// r-th largest (DESC) or smallest.
-template <bool DESC, int KB = 2>
-__device__ __forceinline__ void wave_bitonic_sort(uint32_t& hi, uint32_t& lo) {
-  bitonic_merge<KB, KB / 2, DESC>(hi, lo);
-  if constexpr (KB < 64) wave_bitonic_sort<DESC, KB * 2>(hi, lo);
-}
-
-__device__ __forceinline__ uint64_t u64_of(uint32_t hi, uint32_t lo) { return ((uint64_t)hi << 32) | lo; }
-
-// Top-n for one (query, KV group) by wave 0 of a workgroup alone: candidates
-// 0..J (J + 1 <= 16 * K) with group scores S[j] >= 0 in LDS.  Writes the
-// selected ids ascending to items[0 .. count) (LDS) and, when sel_out is not
-// null, to sel_out[0 .. n) padded with -1; returns count (wave-uniform).
-// scratch: LDS of at least 320 64-bit words.
-template <int K>
-__device__ __forceinline__ int wave_topn_sorted(const float* S, int J, int n, int nloc, int finit, uint64_t* scratch,
-                                                int* items, int32_t* sel_out) {
-  static_assert(K % 4 == 0 && K <= 32, "candidates per lane");
-  const int lane = threadIdx.x & 63;
-  const int ncand = J + 1;
-  if (ncand <= n) {
-    for (int r = lane; r < n; r += 64) {
-      if (r < ncand) items[r] = r;
-      if (sel_out) sel_out[r] = r < ncand ? r : -1;
-    }
-    return ncand;
-  }
-  const int lo_local = J - nloc + 1 > 0 ? J - nloc + 1 : 0;  // local blocks are [lo_local, J]
-  const bool f0 = finit && lo_local > 0;
-  const int nf = (J - lo_local + 1) + (f0 ? 1 : 0);
-  const int nr = n - nf;
-  uint32_t idv = 0xFFFFFFFFu;  // this lane's id in the final ascending sort (lanes < n)
-  if (nr > 0) {
-    // ---- the candidates' keys (0 = not a candidate)
-    uint64_t k[K];
-#pragma unroll
-    for (int c = 0; c < K / 4; ++c) {
-      const int j0 = 256 * c + 4 * lane;
-      float4 s4 = {0.f, 0.f, 0.f, 0.f};
-      if (j0 < ncand) s4 = *reinterpret_cast<const float4*>(S + j0);  // S is padded to a multiple of 4
-      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + e;
-        const bool ok = j < lo_local && !(f0 && j == 0);
-        k[4 * c + e] = ok ? u64_of(__float_as_uint(sv[e]), 0xFFFFFFFFu - (uint32_t)j) : 0ull;
-      }
-    }
-    // ---- 1. threshold: the nr-th largest lane maximum
-    uint64_t km = k[0];
-#pragma unroll
-    for (int c = 1; c < K; ++c) km = k[c] > km ? k[c] : km;
-    uint32_t th = (uint32_t)(km >> 32), tl = (uint32_t)km;
-    wave_bitonic_sort<true>(th, tl);
-    uint64_t tau = u64_of((uint32_t)__builtin_amdgcn_readlane((int)th, nr - 1),
-                          (uint32_t)__builtin_amdgcn_readlane((int)tl, nr - 1));
-    if (tau == 0ull) tau = 1ull;  // fewer than nr lanes hold candidates: all of them survive
-    // ---- 2. survivors, compacted into scratch
-    const uint64_t below = (1ull << lane) - 1ull;
-    int T = 0;
-#pragma unroll
-    for (int c = 0; c < K; ++c) {
-      const bool sv = k[c] >= tau;  // tau >= 1, so never a non-candidate
-      const uint64_t m = __ballot(sv);
-      const int pos = T + __popcll(m & below);
-      if (sv && pos < 256) scratch[pos] = k[c];
-      T += __popcll(m);
-    }
-    uint64_t win = 0ull;  // lane r < nr: the r-th largest routed key
-    if (T <= 64) {
-      wave_lds_sync();
-      const uint64_t x = lane < T ? scratch[lane] : 0ull;
-      uint32_t xh = (uint32_t)(x >> 32), xl = (uint32_t)x;
-      wave_bitonic_sort<true>(xh, xl);
-      win = u64_of(xh, xl);
-    } else if (T <= 256) {
-      pad16(scratch, T);
-      wave_lds_sync();
-      uint64_t* dst = scratch + 256;  // 16 words after the padded list
-      rank_into<4>(scratch, T, nr, dst);
-      wave_lds_sync();
-      win = lane < nr ? dst[lane] : 0ull;
-    } else {  // many equal-score keys can defeat the threshold: extract the maxima one by one
-      win = wave_extract<K>(k, nr);
-    }
-    if (lane < nr) idv = 0xFFFFFFFFu - (uint32_t)win;
-  }
-  if (lane >= (nr > 0 ? nr : 0) && lane < n) {
-    const int i = lane - (nr > 0 ? nr : 0);  // forced block i
-    if (i < nf) idv = (uint32_t)(f0 ? (i == 0 ? 0 : lo_local + i - 1) : lo_local + i);
-  }
-  // ---- 3. ascending ids (unused lanes hold 0xFFFFFFFF and sort last)
-  uint32_t z = 0;
-  wave_bitonic_sort<false>(idv, z);
-  const int cnt = n < nf + (nr > 0 ? nr : 0) ? n : nf + (nr > 0 ? nr : 0);
-  if (lane < cnt) items[lane] = (int)idv;
-  if (sel_out && lane < n) sel_out[lane] = lane < cnt ? (int)idv : -1;
-  return cnt;
-}
-
 // Wave-wide minimum of an unsigned value (DPP row shifts and broadcasts as in
 // wave_max_u32, on the complement).
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return 0xFFFFFFFFu - wave_max_u32(0xFFFFFFFFu - x); }

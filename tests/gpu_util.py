@@ -71,8 +71,9 @@ def f64_to_bits(x: np.ndarray) -> np.ndarray:
     return (np.asarray(x, dtype=np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def run_decode(case, kc_bits=None, vc_bits=None, gates=None, ws=None):
-    """Decode step on the GPU.  Without kc/vc the GPU compresses the cache first."""
+def run_decode(case, kc_bits=None, vc_bits=None, gates=None, ws=None, max_len=None):
+    """Decode step on the GPU.  Without kc/vc the GPU compresses the cache first.
+    max_len (default: the largest capacity) also sets the launch plan."""
     wl = case.wl
     dims, cfg = dims_cfg(case)
     cuc = cmp_offsets(case)
@@ -82,12 +83,13 @@ def run_decode(case, kc_bits=None, vc_bits=None, gates=None, ws=None):
     seq = torch.from_numpy(case.seq_lens).cuda()
     cu = torch.from_numpy(case.cu_seqlens).cuda()
     cu_c = torch.from_numpy(cuc).cuda()
-    max_len = int(np.diff(case.cu_seqlens).max())
+    cap_max = int(np.diff(case.cu_seqlens).max())
+    max_len = cap_max if max_len is None else int(max_len)
     if kc_bits is None:
         rows = int(wl.num_kv_heads * cuc[-1])
         kc = torch.zeros((max(rows, 1), wl.d_k), dtype=torch.bfloat16, device="cuda")
         vc = torch.zeros((max(rows, 1), wl.d_v), dtype=torch.bfloat16, device="cuda")
-        N.nsa_compress_kv(dims, cfg, k, v, cu, seq, max_len, dev_bits(case.w_k), dev_bits(case.pe_k),
+        N.nsa_compress_kv(dims, cfg, k, v, cu, seq, cap_max, dev_bits(case.w_k), dev_bits(case.pe_k),
                           dev_bits(case.w_v), dev_bits(case.pe_v), kc, vc, cu_c)
     else:
         if kc_bits.shape[0] == 0:  # no complete block yet: the cache is never read, but must not be NULL

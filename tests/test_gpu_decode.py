@@ -2,6 +2,7 @@
 import numpy as np
 import pytest
 
+import long_context_sparse_nsa_amd as N
 import nsa_inputs as I
 from oracle import nsa_oracle as O
 from tests import gpu_util as U
@@ -140,3 +141,23 @@ def test_decode_tied_scores(name):
     kc, vc, _ = U.oracle_cmp_cache(case)
     out, sel, _ = U.run_decode(case, kc, vc)
     _check_decode(case, out, sel)
+
+
+def test_decode_two_launch_plans_each_repeat_and_match_the_oracle():
+    """Two launch plans for the same inputs: the capacity the call is planned for
+    (max_seq_len) sets the segment length of the compressed stream, so 4x the
+    capacity splits the same cache into fewer, longer segments.  Each plan must
+    repeat bit for bit, and both must match the oracle."""
+    case = I.generate(I.workload(STD, batch=2, seq_len=12000), 22)
+    dims, cfg = U.dims_cfg(case)
+    kc, vc, _ = U.oracle_cmp_cache(case)
+    cap = int(np.diff(case.cu_seqlens).max())
+    sizes = []
+    for max_len in (cap, 4 * cap):
+        sizes.append(N.nsa_decode_workspace_size(dims, cfg, max_len))
+        a = U.run_decode(case, kc, vc, max_len=max_len)
+        b = U.run_decode(case, kc, vc, max_len=max_len)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+        _check_decode(case, a[0], a[1])
+    assert sizes[0] != sizes[1]  # a different segment plan
