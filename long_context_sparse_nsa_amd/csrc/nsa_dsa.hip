@@ -317,7 +317,16 @@ __global__ __launch_bounds__(256) void dsa_select_kernel(DsaParams p) {
     if (tid < 128) __hip_atomic_store(bits + ch * 128 + tid, s_bits[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tid == 0) __hip_atomic_store(ccount + ch, (uint32_t)s_nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  // Hand-off to the last workgroup of the sequence without a release / acquire
+  // pair: the candidates, bitmap words and counts above are agent-scope atomic
+  // stores, which the hardware writes through to the device-coherent level
+  // (sc1); each thread waits until its stores are acknowledged (asm with a
+  // memory clobber, so the compiler keeps them before it) and only then is the
+  // arrival counter incremented; the last workgroup issues its agent-scope
+  // atomic loads (sc1, past the non-coherent caches) only after the counter's
+  // value has returned.  A release / acquire fence pair would write back and
+  // invalidate the whole L2 of the XCD for every workgroup.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(p.nchunk - 1);
