@@ -44,6 +44,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1e30f;        // running-reference start: finite, so exp2 never sees inf - inf
 constexpr float kLazy = 8.0f;            // the softmax reference moves only when exceeded by this (log2 units)
 constexpr float kLn2 = 0.6931471805599453f;  // log-sum-exp outputs: log2 units to natural log
+constexpr int kReadAhead = 2;  // k-steps of K operand reads issued ahead of their MFMAs
 
 template <int DK, int DV>
 struct PfShape {
@@ -286,17 +287,29 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   };
   // logits of one 32-key half of the staged chunk for the wave's positions
   // (each K fragment read once from LDS and used for all of them)
-  auto logits_half = [&](const char* kt, int hh, f32x4_t (&sv)[kWaveQ][2]) {
+  // Both halves at once, k-step by k-step over the four 16-key row blocks (eight
+  // independent MFMA chains), with the reads of the next KD k-steps in flight.
+  auto logits = [&](const char* kt, f32x4_t (&s0)[kWaveQ][2], f32x4_t (&s1)[kWaveQ][2]) {
 #pragma unroll
-    for (int q = 0; q < kWaveQ; ++q) sv[q][0] = sv[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < kWaveQ; ++q) s0[q][0] = s0[q][1] = s1[q][0] = s1[q][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
+    for (int ks = 0; ks < KT; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KT; ++ks) {
-        const u32x4_t a = lds_k<DK>(kt, 2 * hh + mm, ks, lane);
+      for (int m = 0; m < 4; ++m) {
+        const u32x4_t a = lds_k<DK>(kt, m, ks, lane);
 #pragma unroll
-        for (int q = 0; q < kWaveQ; ++q) sv[q][mm] = mfma_bf16(a, qf[q][ks], sv[q][mm]);
+        for (int q = 0; q < kWaveQ; ++q) {
+          f32x4_t& d = m < 2 ? s0[q][m] : s1[q][m - 2];
+          d = mfma_bf16(a, qf[q][ks], d);
+        }
       }
+    constexpr int KD = KT < kReadAhead ? KT : kReadAhead;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * KD, 0);
+#pragma unroll
+    for (int ks = 0; ks < KT; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * kWaveQ, 0);
+      if (ks + KD < KT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
   };
 
   // The query fragments must have arrived before the tile copies are queued: the
@@ -317,8 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     const char* kt = begin_chunk(c);
     const char* vt = kt + SH::kKBytes;
     f32x4_t s0[kWaveQ][2], s1[kWaveQ][2];
-    logits_half(kt, 0, s0);
-    logits_half(kt, 1, s1);
+    logits(kt, s0, s1);
     const int x0 = xlo + 64 * cw;
     float z0[kWaveQ][2][4], z1[kWaveQ][2][4], ms[kWaveQ];
 #pragma unroll
@@ -364,8 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   for (int c1 = 0; c1 < nC; ++c1, ++c) {
     const char* kt = begin_chunk(c);
     f32x4_t s0[kWaveQ][2], s1[kWaveQ][2];
-    logits_half(kt, 0, s0);
-    logits_half(kt, 1, s1);
+    logits(kt, s0, s1);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int i0 = 64 * c1 + 32 * hh;
@@ -426,8 +437,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     const char* kt = begin_chunk(c);
     const char* vt = kt + SH::kKBytes;
     f32x4_t s0[kWaveQ][2], s1[kWaveQ][2];
-    logits_half(kt, 0, s0);
-    logits_half(kt, 1, s1);
+    logits(kt, s0, s1);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int i0 = 64 * c2 + 32 * hh;
@@ -511,29 +521,74 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
 // Kernel 2: selected branch over the union of the tile's selected blocks.
 // ROWS keys are used per step: a whole block for l' = 32 or 64, half a block
 // for l' = 128, and for l' = 16 the block plus 16 masked rows.
-#ifndef NSA_PF_SEL_WAVES
-#define NSA_PF_SEL_WAVES 8
-#endif
-constexpr int kSelWaves = NSA_PF_SEL_WAVES;  // waves of the selected-branch workgroup
+//
+// Two waves per SIMD, two positions per wave.  A step's work usually falls on
+// one or two positions, so the step's critical path is one wave's chain of LDS
+// reads and MFMAs: each position's logits run k-step by k-step over the four
+// 16-key row blocks (four independent MFMA chains), so the operand reads of the
+// next k-steps are in flight while the current ones multiply.
+constexpr int kSelWaves = 8;                 // waves of the selected-branch workgroup
 constexpr int kSelQ = kTileQ / kSelWaves;    // positions per wave
 constexpr int kSelThreads = 64 * kSelWaves;
+
+// The K rows of a step are staged row-major (DK*2 bytes per row) by copies that
+// each read 1 KB of contiguous source, so every 128-byte line is fetched whole
+// by one instruction.  Row-major MFMA operand reads (16 rows x 16 bytes per lane
+// group) would hit the same LDS banks, so 16-byte pieces are placed with an XOR
+// swizzle inside each 256-byte group: tile piece P sits at slot
+// (P & ~15) | ((P & 15) ^ ((P >> 4) & SWZ)).  The map is its own inverse, so
+// lane i of copy c loads the piece that belongs in slot 64c + i.  SWZ is chosen
+// per row length so that the 16 lanes of a lane group read 16 different bank
+// groups; it leaves the term added by whole 16-row blocks unchanged, so the
+// operand (m, ks) of a lane sits at its (0, ks) offset + 256*R*m bytes.
+template <int DK>
+struct SelSwizzle {
+  static constexpr int R = DK / 8;                // 16-byte pieces per row
+  static constexpr int SWZ = DK == 128 ? 15 : 7;
+  static_assert(R % (SWZ + 1) == 0, "16-row blocks must keep the swizzle");
+  __device__ static int slot(int P) { return (P & ~15) | ((P & 15) ^ ((P >> 4) & SWZ)); }
+};
+
+// Stages K rows [row0, row0 + ROWS) as above.  Wave w issues copies c = w,
+// w + NW, ... (NW a multiple of 4); 4c mod 16 depends only on w, so one per-lane source offset
+// (voff) serves all of its copies when the whole tile lies inside the array.
+// Rows past rowmax are replaced by row rowmax.
+template <int DK, int ROWS, int NW>
+__device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst,
+                                                 int wave, int lane, uint32_t voff) {
+  using SW = SelSwizzle<DK>;
+  constexpr int NI = ROWS * SW::R / 64, PW = (NI + NW - 1) / NW;
+  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform
+    const char* tile = reinterpret_cast<const char*>(base + row0 * DK);
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int c = wave + NW * k;
+      if (NI % NW != 0 && c >= NI) break;
+      copy16_to_lds_sb(tile + 1024 * c, voff, dst + 1024 * c);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int c = wave + NW * k;
+      if (NI % NW != 0 && c >= NI) break;
+      const int P = SW::slot(64 * c + lane);
+      int64_t row = row0 + P / SW::R;
+      row = row < rowmax ? row : rowmax;
+      copy16_to_lds(base + row * DK + 8 * (P % SW::R), dst + 1024 * c);
+    }
+  }
+}
 
 template <int DK, int DV, int LSEL>
 __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p) {
   using SH = PfShape<DK, DV>;
+  using SW = SelSwizzle<DK>;
   constexpr int KT = SH::KT, VC = SH::VC;
-#ifndef NSA_PF_SEL_ROWS
-#define NSA_PF_SEL_ROWS 64
-#endif
-#ifndef NSA_PF_SEL_NBUF
-#define NSA_PF_SEL_NBUF 3
-#endif
-  constexpr int RMAX = NSA_PF_SEL_ROWS;      // rows per step (at most)
-  constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > RMAX ? RMAX : LSEL);
+  constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > 64 ? 64 : LSEL);
   constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
-  constexpr int NBUF = NSA_PF_SEL_NBUF;      // NBUF - 1 steps in flight
+  constexpr int NBUF = 3;                     // NBUF - 1 steps in flight
   using SO = StageOffsets<DK, DV, ROWS, kSelWaves>;
-  constexpr int NLD = SO::kMinCopiesKV;
+  constexpr int NLD = SO::kMinCopiesKV;       // copies per wave per step (K and V), at least
   constexpr int kStepBytes = SO::kKBytes + SO::kVBytes;
   __shared__ __attribute__((aligned(1024))) char s_buf[NBUF][kStepBytes];
   __shared__ uint32_t s_mask[kPfMaxBlocks];  // per block: bit q set if position t0+q chose it
@@ -553,7 +608,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
   const uint16_t* vraw = p.v + bg * T * DV;
 
   // ---- g_slc from the gate network (when given) for this lane's head lr and
-  // both of its positions, before any other load
+  // the wave's positions, before any other load
   float gsl[kSelQ];
   if (p.wgate) {
     const int hq = g * p.G + (lr < p.G ? lr : 0);
@@ -618,14 +673,21 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
   const float sc = p.scale_log2;
   const u32x4_t ones_a = ones_row_operand(lr);
 
+  // this lane's byte offsets of its K operands (m = 0) in a staged step, and of
+  // its K copies' source pieces
+  uint32_t koff[KT];
+#pragma unroll
+  for (int ks = 0; ks < KT; ++ks) koff[ks] = 16u * (uint32_t)SW::slot(SW::R * lr + 4 * ks + lg);
+  const uint32_t kcopy = 16u * (uint32_t)SW::slot(64 * wave + lane) - 1024u * (uint32_t)wave;
+  const SO so(lane);
+
   auto step_row0 = [&](int st) -> int64_t {
     const int u = st / SPB;
     return (int64_t)(s_list[u] >> 16) * LSEL + (int64_t)(st - u * SPB) * ROWS;
   };
-  const SO so(lane);
   auto stage = [&](int st, int buf) {
     const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane((int)step_row0(st));
-    stage_k(kraw, r0, T - 1, s_buf[buf], wave, lane, so);
+    stage_k_rowmajor<DK, ROWS, kSelWaves>(kraw, r0, T - 1, s_buf[buf], wave, lane, kcopy);
     stage_v(vraw, r0, T - 1, s_buf[buf] + SO::kKBytes, wave, lane, so);
   };
 
@@ -634,23 +696,20 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
   for (int s0 = 0; s0 < NBUF - 1; ++s0)
     if (s0 < nsteps) stage(s0, s0);
   for (int st = 0; st < nsteps; ++st) {
-    // step st has landed once at most the later steps' copies are outstanding
-    const int later = min(nsteps - 1 - st, NBUF - 2);
-    if (later <= 0) wait_vmem_le<0>();
-    else if (NBUF < 4 || later == 1) wait_vmem_le<NLD>();
-    else if (NBUF < 5 || later == 2) wait_vmem_le<2 * NLD>();
-    else if (NBUF < 6 || later == 3) wait_vmem_le<3 * NLD>();
-    else wait_vmem_le<4 * NLD>();
+    // step st has landed once at most the later step's copies are outstanding
+    if (st + 1 < nsteps) wait_vmem_le<NLD>();
+    else wait_vmem_le<0>();
     lds_barrier();
     if (st + NBUF - 1 < nsteps) stage(st + NBUF - 1, (st + NBUF - 1) % NBUF);
-    const char* kt = s_buf[st % NBUF];
-    const char* vt = s_buf[st % NBUF] + SO::kKBytes;
     const uint32_t ent = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_list[st / SPB]);
     const uint32_t mine = (ent >> (kSelQ * wave)) & ((1u << kSelQ) - 1u);
     if (mine == 0u) continue;
+    const char* kt = s_buf[st % NBUF];
+    const char* vt = s_buf[st % NBUF] + SO::kKBytes;
     const int jblk = (int)(ent >> 16);
     const int x0 = jblk * LSEL + (st % SPB) * ROWS;
     const int xend = (jblk + 1) * LSEL;  // first row past the block
+
 #pragma unroll
     for (int q = 0; q < kSelQ; ++q) {
       if (!((mine >> q) & 1u)) continue;
@@ -658,9 +717,27 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
 #pragma unroll
       for (int m = 0; m < MT; ++m) s[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+      for (int ks = 0; ks < KT; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KT; ++ks) s[m] = mfma_bf16(lds_k<DK>(kt, m, ks, lane), qf[q][ks], s[m]);
+        for (int m = 0; m < MT; ++m)
+          s[m] = mfma_bf16(*reinterpret_cast<const u32x4_t*>(kt + koff[ks] + 256 * SW::R * m), qf[q][ks], s[m]);
+      // the V operands of the step, in flight during the softmax
+      uint32_t vr[NKS][8][DV / 32];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) lds_v_step<DV>(vt, ks, lg, lr, vr[ks]);
+      // Instruction order: the K operands of the first KD k-steps, then each
+      // k-step's MFMAs followed by the reads of the k-step KD later, then the V
+      // reads -- so about KD k-steps of operand reads are always in flight.
+      {
+        constexpr int KD = KT < 3 ? KT : 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, MT * KD, 0);
+#pragma unroll
+        for (int ks = 0; ks < KT; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+          if (ks + KD < KT) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS * 8, 0);
+      }
       float z[MT][4];
       if (x0 + ROWS - 1 <= tq[q] && x0 + ROWS <= xend) {  // wave-uniform: no row masked
 #pragma unroll
@@ -690,11 +767,9 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
         for (int i = 0; i < 4; ++i) z[m][i] = __builtin_amdgcn_exp2f(fmaf(z[m][i], sc, nm));
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        uint32_t vr[8][DV / 32];
-        lds_v_step<DV>(vt, ks, lg, lr, vr);
         const u32x4_t pk = pack_probs(z[2 * ks], z[2 * ks + 1]);
 #pragma unroll
-        for (int j = 0; j < VC; ++j) acc[q][j] = mfma_bf16(v_operand<DV>(vr, j), pk, acc[q][j]);
+        for (int j = 0; j < VC; ++j) acc[q][j] = mfma_bf16(v_operand<DV>(vr[ks], j), pk, acc[q][j]);
         lsum[q] = mfma_bf16(ones_a, pk, lsum[q]);
       }
     }
