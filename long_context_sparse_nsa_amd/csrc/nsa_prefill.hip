@@ -1,11 +1,12 @@
 // NSA causal prefill on gfx950, tiled over query positions.
 //
-// Both kernels run one workgroup (8 waves, two per SIMD) per (sequence, KV
-// group, tile of 16 consecutive positions t0 .. t0+15).  Wave w owns positions
-// t0+2w and t0+2w+1 and keeps, for each, the group's query fragments and a
-// 16-head x d_v fp32 accumulator in registers.  Key/value tiles of 64 rows are copied straight
-// from global memory into LDS (no register round trip), double buffered, and
-// each staged tile serves every position of the workgroup that needs it.
+// Kernel 1 runs one workgroup (8 waves, two per SIMD) per (sequence, KV group,
+// tile of 16 consecutive positions t0 .. t0+15), kernel 2 one workgroup of 4
+// waves per 8 positions.  Wave w owns two consecutive positions and keeps, for
+// each, the group's query fragments and a 16-head x d_v fp32 accumulator in
+// registers.  Key/value rows are copied straight from global memory into LDS
+// (no register round trip), several steps ahead, and each staged tile serves
+// every position of the workgroup that needs it.
 //
 // Kernel 1 (compressed + window branches, group scores, selection):
 //   W   sliding window (t - w, t] over the raw keys, online softmax; the
@@ -17,8 +18,8 @@
 //       position's score row in LDS;
 //   top-n per position (initial and local blocks forced) -> selected ids;
 //   the accumulator (g_win o_win + g_cmp o_cmp, fp32) goes to the workspace.
-// Kernel 2 (selected branch): the union of the tile's selected blocks is
-// staged block by block; each wave runs the online softmax for those of its
+// Kernel 2 (selected branch): the union of the 8 positions' selected blocks is
+// staged 32 rows at a time; each wave runs the online softmax for those of its
 // positions that chose the block, then writes bf16(acc + g_slc o_slc).
 //
 // Sources: lesson 5.5/02 "Разреженное внимание — NSA и DSA" (ai.flicky.cc),
@@ -519,52 +520,59 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
 
 // ---------------------------------------------------------------------------
 // Kernel 2: selected branch over the union of the tile's selected blocks.
-// ROWS keys are used per step: a whole block for l' = 32 or 64, half a block
-// for l' = 128, and for l' = 16 the block plus 16 masked rows.
+// ROWS = 32 keys are used per step (a block of l' > 32 takes several steps; for
+// l' = 16 the block plus 16 masked rows).
 //
-// Two waves per SIMD, two positions per wave.  A step's work usually falls on
-// one or two positions, so the step's critical path is one wave's chain of LDS
-// reads and MFMAs: each position's logits run k-step by k-step over the four
-// 16-key row blocks (four independent MFMA chains), so the operand reads of the
-// next k-steps are in flight while the current ones multiply.
-constexpr int kSelWaves = 8;                 // waves of the selected-branch workgroup
-constexpr int kSelQ = kTileQ / kSelWaves;    // positions per wave
+// A step's work usually falls on one or two positions, so within a workgroup the
+// step's critical path is one wave's chain of LDS reads, MFMAs and softmax while
+// the other waves wait at the step's barrier.  The workgroup is therefore small
+// (8 positions, 4 waves of two positions each, 68 KB of LDS) so that two of them
+// share a compute unit and each fills the other's waits; each position's logits
+// run k-step by k-step over the 16-key row blocks (independent MFMA chains),
+// with the operand reads of the next k-steps in flight.
+constexpr int kSelTile = 8;                  // positions per selected-branch workgroup
+constexpr int kSelWaves = 4;                 // waves of the selected-branch workgroup
+constexpr int kSelRows = 32;                 // keys per step
+constexpr int kSelQ = kSelTile / kSelWaves;  // positions per wave
+static_assert(kSelTile <= 16 && kSelQ * kSelWaves == kSelTile, "position masks are 16 bits");
 constexpr int kSelThreads = 64 * kSelWaves;
 
 // The K rows of a step are staged row-major (DK*2 bytes per row) by copies that
 // each read 1 KB of contiguous source, so every 128-byte line is fetched whole
-// by one instruction.  Row-major MFMA operand reads (16 rows x 16 bytes per lane
-// group) would hit the same LDS banks, so 16-byte pieces are placed with an XOR
-// swizzle inside each 256-byte group: tile piece P sits at slot
-// (P & ~15) | ((P & 15) ^ ((P >> 4) & SWZ)).  The map is its own inverse, so
-// lane i of copy c loads the piece that belongs in slot 64c + i.  SWZ is chosen
-// per row length so that the 16 lanes of a lane group read 16 different bank
-// groups; it leaves the term added by whole 16-row blocks unchanged, so the
+// by 8 lanes of one instruction.  Row-major MFMA operand reads (16 rows x 16
+// bytes per lane group) would hit the same LDS banks, so inside each 128-byte
+// line the 16-byte pieces of row r are XOR-permuted by r mod 8: tile piece P
+// sits at slot (P & ~7) | ((P & 7) ^ ((P / R) & 7)).  The map is its own
+// inverse, so lane i of copy c loads the piece that belongs in slot 64c + i;
+// any 8 consecutive lanes of an operand read (8 rows, one piece each) then hit
+// 8 different bank groups, and whole 16-row blocks keep the permutation, so the
 // operand (m, ks) of a lane sits at its (0, ks) offset + 256*R*m bytes.
 template <int DK>
 struct SelSwizzle {
-  static constexpr int R = DK / 8;                // 16-byte pieces per row
-  static constexpr int SWZ = DK == 128 ? 15 : 7;
-  static_assert(R % (SWZ + 1) == 0, "16-row blocks must keep the swizzle");
-  __device__ static int slot(int P) { return (P & ~15) | ((P & 15) ^ ((P >> 4) & SWZ)); }
+  static constexpr int R = DK / 8;  // 16-byte pieces per row
+  static_assert(R % 8 == 0, "rows of whole 128-byte lines");
+  __device__ static int slot(int P) { return (P & ~7) | ((P & 7) ^ ((P / R) & 7)); }
 };
 
 // Stages K rows [row0, row0 + ROWS) as above.  Wave w issues copies c = w,
-// w + NW, ... (NW a multiple of 4); 4c mod 16 depends only on w, so one per-lane source offset
-// (voff) serves all of its copies when the whole tile lies inside the array.
+// w + NW, ...; kcopy[k] is this lane's source byte offset within copy w + NW*k.
 // Rows past rowmax are replaced by row rowmax.
 template <int DK, int ROWS, int NW>
+struct SelKCopies {
+  static constexpr int NI = ROWS * SelSwizzle<DK>::R / 64, PW = (NI + NW - 1) / NW;
+};
+template <int DK, int ROWS, int NW>
 __device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst,
-                                                 int wave, int lane, uint32_t voff) {
+                                                 int wave, int lane, const uint32_t (&kcopy)[SelKCopies<DK, ROWS, NW>::PW]) {
   using SW = SelSwizzle<DK>;
-  constexpr int NI = ROWS * SW::R / 64, PW = (NI + NW - 1) / NW;
+  constexpr int NI = SelKCopies<DK, ROWS, NW>::NI, PW = SelKCopies<DK, ROWS, NW>::PW;
   if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform
     const char* tile = reinterpret_cast<const char*>(base + row0 * DK);
 #pragma unroll
     for (int k = 0; k < PW; ++k) {
       const int c = wave + NW * k;
       if (NI % NW != 0 && c >= NI) break;
-      copy16_to_lds_sb(tile + 1024 * c, voff, dst + 1024 * c);
+      copy16_to_lds_sb(tile + 1024 * c, kcopy[k], dst + 1024 * c);
     }
   } else {
 #pragma unroll
@@ -579,12 +587,81 @@ __device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t r
   }
 }
 
+// The V rows of a step, staged row-major with the 16-byte pieces of row r
+// XOR-permuted by f(r) (a permutation inside the row), and read back as V^T
+// MFMA operands with the LDS transpose read: the 16 lanes of a lane group point
+// at 4 rows x 16 channels (4 lanes per row, 4 channels each) and lane i receives
+// channel i of the 4 rows.  f spreads the 32 lanes of each half-wave over all 16
+// bank groups of 16 bytes.
+template <int DV>
+struct VSwizzle {
+  static_assert(DV == 64 || DV == 128, "transposed V reads are laid out for d_v = 64 or 128");
+  static constexpr int PR = DV / 8;  // 16-byte pieces per row
+  __device__ static int f(int r) { return DV == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+  // lane's byte offset of its piece in copy c's 1 KB (full tiles): depends on c
+  // only through c mod 2, so one value serves all copies of a wave when NW is even
+  __device__ static uint32_t copy_offset(int c, int lane) {
+    const int r = (64 * c + lane) / PR;
+    return 16u * (uint32_t)((lane - lane % PR) + ((lane % PR) ^ f(r)));
+  }
+};
+
+template <int DV, int ROWS, int NW>
+__device__ __forceinline__ void stage_v_swizzled(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst,
+                                                 int wave, int lane, uint32_t voff) {
+  using VS = VSwizzle<DV>;
+  constexpr int NI = ROWS * VS::PR / 64, PW = (NI + NW - 1) / NW;
+  static_assert(NW % 2 == 0, "one copy offset per wave");
+  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform
+    const char* tile = reinterpret_cast<const char*>(base + row0 * DV);
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int c = wave + NW * k;
+      if (NI % NW != 0 && c >= NI) break;
+      copy16_to_lds_sb(tile + 1024 * c, voff, dst + 1024 * c);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int c = wave + NW * k;
+      if (NI % NW != 0 && c >= NI) break;
+      const int sl = 64 * c + lane, r = sl / VS::PR;
+      int64_t row = row0 + r;
+      row = row < rowmax ? row : rowmax;
+      copy16_to_lds(base + row * DV + 8 * ((sl % VS::PR) ^ VS::f(r)), dst + 1024 * c);
+    }
+  }
+}
+
+// This lane's part of the transposed-read addresses: row 4*lg + lr/4 of a
+// 16-row half, 8 bytes at channel 4*(lr%4) of a 16-channel block, before the
+// block index j is XOR-ed into bits 5.. (32*j).
+template <int DV>
+__device__ __forceinline__ uint32_t vt_lane_offset(int lg, int lr) {
+  const int r = 4 * lg + lr / 4;
+  return (uint32_t)(r * DV * 2 + 16 * (VSwizzle<DV>::f(r) + (lr % 4) / 2) + 8 * (lr % 2));
+}
+
+// V^T operand of channels 16j .. 16j+15 for the 32-key step at row 32*ks of the
+// staged tile: element e of lane (lg, lr) is channel 16j + lr of key
+// step_key(lg, e).
+template <int DV>
+__device__ __forceinline__ u32x4_t lds_vt_operand(const char* vt, int ks, int j, uint32_t vlane) {
+  typedef short v4i16_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16_t* lds_v4_t;
+  const char* pa = vt + 32 * ks * DV * 2 + (vlane ^ (32u * (uint32_t)j));
+  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(pa));
+  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(pa + 16 * DV * 2));
+  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
+  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+}
+
 template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kSelThreads, 2) void pf_sel_kernel(PrefillParams p) {
   using SH = PfShape<DK, DV>;
   using SW = SelSwizzle<DK>;
   constexpr int KT = SH::KT, VC = SH::VC;
-  constexpr int ROWS = LSEL < 32 ? 32 : (LSEL > 64 ? 64 : LSEL);
+  constexpr int ROWS = kSelRows;
   constexpr int MT = ROWS / 16, NKS = ROWS / 32, SPB = LSEL > ROWS ? LSEL / ROWS : 1;
   constexpr int NBUF = 3;                     // NBUF - 1 steps in flight
   using SO = StageOffsets<DK, DV, ROWS, kSelWaves>;
@@ -598,10 +675,12 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const TileId ti = tile_id(p);
-  const int b = ti.b, g = ti.g, t0 = ti.t0;
   const int T = p.T;
-  const int tlast = min(t0 + kTileQ - 1, T - 1);
+  const int nbg = p.B * p.H, bid = (int)blockIdx.x;
+  const int bgi = bid % nbg;
+  const int b = bgi / p.H, g = bgi % p.H;
+  const int t0 = ((T + kSelTile - 1) / kSelTile - 1 - bid / nbg) * kSelTile;  // latest tiles first
+  const int tlast = min(t0 + kSelTile - 1, T - 1);
   const int Jtile = tlast / LSEL;
   const int64_t bg = (int64_t)b * p.H + g;
   const uint16_t* kraw = p.k + bg * T * DK;
@@ -625,7 +704,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
   // ---- union of the tile's selections
   for (int j = tid; j <= Jtile; j += kSelThreads) s_mask[j] = 0u;
   __syncthreads();
-  for (int e = tid; e < kTileQ * p.n; e += kSelThreads) {
+  for (int e = tid; e < kSelTile * p.n; e += kSelThreads) {
     const int q = e / p.n;
     if (t0 + q < T) {
       const int j = p.sel[(((int64_t)b * T + t0 + q) * p.H + g) * p.n + (e - q * p.n)];
@@ -678,8 +757,15 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
   uint32_t koff[KT];
 #pragma unroll
   for (int ks = 0; ks < KT; ++ks) koff[ks] = 16u * (uint32_t)SW::slot(SW::R * lr + 4 * ks + lg);
-  const uint32_t kcopy = 16u * (uint32_t)SW::slot(64 * wave + lane) - 1024u * (uint32_t)wave;
-  const SO so(lane);
+  constexpr int KPW = SelKCopies<DK, ROWS, kSelWaves>::PW;
+  uint32_t kcopy[KPW];
+#pragma unroll
+  for (int k = 0; k < KPW; ++k) {
+    const int c = wave + kSelWaves * k;
+    kcopy[k] = 16u * (uint32_t)SW::slot(64 * c + lane) - 1024u * (uint32_t)c;
+  }
+  const uint32_t vcopy = VSwizzle<DV>::copy_offset(wave, lane);
+  const uint32_t vlane = vt_lane_offset<DV>(lg, lr);
 
   auto step_row0 = [&](int st) -> int64_t {
     const int u = st / SPB;
@@ -688,7 +774,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
   auto stage = [&](int st, int buf) {
     const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane((int)step_row0(st));
     stage_k_rowmajor<DK, ROWS, kSelWaves>(kraw, r0, T - 1, s_buf[buf], wave, lane, kcopy);
-    stage_v(vraw, r0, T - 1, s_buf[buf] + SO::kKBytes, wave, lane, so);
+    stage_v_swizzled<DV, ROWS, kSelWaves>(vraw, r0, T - 1, s_buf[buf] + SO::kKBytes, wave, lane, vcopy);
   };
 
   wait_vmem_le<0>();  // query fragments in (see the compressed-branch kernel)
@@ -721,22 +807,22 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
           s[m] = mfma_bf16(*reinterpret_cast<const u32x4_t*>(kt + koff[ks] + 256 * SW::R * m), qf[q][ks], s[m]);
-      // the V operands of the step, in flight during the softmax
-      uint32_t vr[NKS][8][DV / 32];
+      // the V^T operands of the first 32 keys, in flight during the softmax
+      u32x4_t vop[VC];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) lds_v_step<DV>(vt, ks, lg, lr, vr[ks]);
+      for (int j = 0; j < VC; ++j) vop[j] = lds_vt_operand<DV>(vt, 0, j, vlane);
       // Instruction order: the K operands of the first KD k-steps, then each
       // k-step's MFMAs followed by the reads of the k-step KD later, then the V
       // reads -- so about KD k-steps of operand reads are always in flight.
       {
-        constexpr int KD = KT < 3 ? KT : 3;
+        constexpr int KD = KT < kReadAhead ? KT : kReadAhead;
         __builtin_amdgcn_sched_group_barrier(0x100, MT * KD, 0);
 #pragma unroll
         for (int ks = 0; ks < KT; ++ks) {
           __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
           if (ks + KD < KT) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, NKS * 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, VC * 2, 0);
       }
       float z[MT][4];
       if (x0 + ROWS - 1 <= tq[q] && x0 + ROWS <= xend) {  // wave-uniform: no row masked
@@ -768,14 +854,19 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const u32x4_t pk = pack_probs(z[2 * ks], z[2 * ks + 1]);
+        if (ks > 0) {
 #pragma unroll
-        for (int j = 0; j < VC; ++j) acc[q][j] = mfma_bf16(v_operand<DV>(vr[ks], j), pk, acc[q][j]);
+          for (int j = 0; j < VC; ++j) vop[j] = lds_vt_operand<DV>(vt, ks, j, vlane);
+        }
+#pragma unroll
+        for (int j = 0; j < VC; ++j) acc[q][j] = mfma_bf16(vop[j], pk, acc[q][j]);
         lsum[q] = mfma_bf16(ones_a, pk, lsum[q]);
       }
     }
   }
 
-  // ---- out = bf16(acc_in + g_slc * o_slc)
+  // ---- out = bf16(acc_in + g_slc * o_slc); acc[q][j] element i is channel
+  // 16j + 4*lg + i of head lr
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q) {
     const float lt = __shfl(lsum[q][0], lr);
@@ -784,25 +875,14 @@ __global__ __launch_bounds__(kSelThreads, 1) void pf_sel_kernel(PrefillParams p)
     const float f = lt > 0.f ? (p.wgate ? gsl[q] : p.gates[hrow * 3 + 1]) / lt : 0.f;
     if (p.lse && lg == 0)  // selected-branch log-sum-exp (natural log)
       p.lse[hrow * 3 + 1] = lt > 0.f ? (mref[q] + __builtin_log2f(lt)) * kLn2 : -INFINITY;
-    const float* src = p.acc + hrow * DV;
-    uint16_t* dst = p.out + hrow * DV;
+    const float* src = p.acc + hrow * DV + 4 * lg;
+    uint16_t* dst = p.out + hrow * DV + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch0 = acc_channel<DV>(lg, i, 0);
-      float v[VC];
-#pragma unroll
-      for (int j = 0; j < VC; j += 4) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + ch0 + j);
-        v[j] = a[0]; v[j + 1] = a[1]; v[j + 2] = a[2]; v[j + 3] = a[3];
-      }
-      uint32_t w[VC / 2];
-#pragma unroll
-      for (int j = 0; j < VC; j += 2) w[j / 2] = pack_bf16x2(v[j] + f * acc[q][j][i], v[j + 1] + f * acc[q][j + 1][i]);
-      if constexpr (VC == 8) {
-        *reinterpret_cast<u32x4_t*>(dst + ch0) = u32x4_t{w[0], w[1], w[2], w[3]};
-      } else {
-        *reinterpret_cast<u32x2_t*>(dst + ch0) = u32x2_t{w[0], w[1]};
-      }
+    for (int j = 0; j < VC; ++j) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + 16 * j);
+      *reinterpret_cast<u32x2_t*>(dst + 16 * j) =
+          u32x2_t{pack_bf16x2(a[0] + f * acc[q][j][0], a[1] + f * acc[q][j][1]),
+                  pack_bf16x2(a[2] + f * acc[q][j][2], a[3] + f * acc[q][j][3])};
     }
   }
 }
@@ -814,12 +894,12 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s, const 
   if ((p.T - 1) / p.lsel < 512) hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV, 3, 512>), grid, blk, 0, s, p);
   else hipLaunchKernelGGL((pf_cmp_win_kernel<DK, DV, 2, kPfMaxBlocks>), grid, blk, 0, s, p);
   if (ev) hipEventRecord(ev->ev[2], s);
-  const dim3 sblk(kSelThreads);
+  const dim3 sgrid((unsigned)((int64_t)p.B * p.H * ((p.T + kSelTile - 1) / kSelTile))), sblk(kSelThreads);
   switch (p.lsel) {
-    case 16: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 16>), grid, sblk, 0, s, p); break;
-    case 32: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 32>), grid, sblk, 0, s, p); break;
-    case 64: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 64>), grid, sblk, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 128>), grid, sblk, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 16>), sgrid, sblk, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 32>), sgrid, sblk, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 64>), sgrid, sblk, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((pf_sel_kernel<DK, DV, 128>), sgrid, sblk, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   if (ev) hipEventRecord(ev->ev[3], s);
