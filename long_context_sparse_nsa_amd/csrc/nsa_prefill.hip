@@ -83,16 +83,84 @@ __device__ __forceinline__ void lazy_rescale(float ms, float& m, f32x4_t (&acc)[
   }
 }
 
-// acc[q] += V^T . P_q^T over the 32-key step `ks` of the staged V tile, for the
-// wave's positions; each V^T operand is built once and used for all of them.
+// The V rows of a step, staged row-major with the 16-byte pieces of row r
+// XOR-permuted by f(r) (a permutation inside the row), and read back as V^T
+// MFMA operands with the LDS transpose read: the 16 lanes of a lane group point
+// at 4 rows x 16 channels (4 lanes per row, 4 channels each) and lane i receives
+// channel i of the 4 rows.  f spreads the 32 lanes of each half-wave over all 16
+// bank groups of 16 bytes.
+template <int DV>
+struct VSwizzle {
+  static_assert(DV == 64 || DV == 128, "transposed V reads are laid out for d_v = 64 or 128");
+  static constexpr int PR = DV / 8;  // 16-byte pieces per row
+  __device__ static int f(int r) { return DV == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+  // lane's byte offset of its piece in copy c's 1 KB (full tiles): depends on c
+  // only through c mod 2, so one value serves all copies of a wave when NW is even
+  __device__ static uint32_t copy_offset(int c, int lane) {
+    const int r = (64 * c + lane) / PR;
+    return 16u * (uint32_t)((lane - lane % PR) + ((lane % PR) ^ f(r)));
+  }
+};
+
+template <int DV, int ROWS, int NW>
+__device__ __forceinline__ void stage_v_swizzled(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst,
+                                                 int wave, int lane, uint32_t voff) {
+  using VS = VSwizzle<DV>;
+  constexpr int NI = ROWS * VS::PR / 64, PW = (NI + NW - 1) / NW;
+  static_assert(NW % 2 == 0, "one copy offset per wave");
+  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform
+    const char* tile = reinterpret_cast<const char*>(base + row0 * DV);
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int c = wave + NW * k;
+      if (NI % NW != 0 && c >= NI) break;
+      copy16_to_lds_sb(tile + 1024 * c, voff, dst + 1024 * c);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int c = wave + NW * k;
+      if (NI % NW != 0 && c >= NI) break;
+      const int sl = 64 * c + lane, r = sl / VS::PR;
+      int64_t row = row0 + r;
+      row = row < rowmax ? row : rowmax;
+      copy16_to_lds(base + row * DV + 8 * ((sl % VS::PR) ^ VS::f(r)), dst + 1024 * c);
+    }
+  }
+}
+
+// This lane's part of the transposed-read addresses: row 4*lg + lr/4 of a
+// 16-row half, 8 bytes at channel 4*(lr%4) of a 16-channel block, before the
+// block index j is XOR-ed into bits 5.. (32*j).
+template <int DV>
+__device__ __forceinline__ uint32_t vt_lane_offset(int lg, int lr) {
+  const int r = 4 * lg + lr / 4;
+  return (uint32_t)(r * DV * 2 + 16 * (VSwizzle<DV>::f(r) + (lr % 4) / 2) + 8 * (lr % 2));
+}
+
+// V^T operand of channels 16j .. 16j+15 for the 32-key step at row 32*ks of the
+// staged tile: element e of lane (lg, lr) is channel 16j + lr of key
+// step_key(lg, e).
+template <int DV>
+__device__ __forceinline__ u32x4_t lds_vt_operand(const char* vt, int ks, int j, uint32_t vlane) {
+  typedef short v4i16_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16_t* lds_v4_t;
+  const char* pa = vt + 32 * ks * DV * 2 + (vlane ^ (32u * (uint32_t)j));
+  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(pa));
+  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(pa + 16 * DV * 2));
+  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
+  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// acc[q] += V^T . P_q^T over the 32-key step `ks` of the staged V tile (rows
+// swizzled as above), for the wave's positions; each V^T operand is read once
+// and used for all of them.  acc[q][j] element i is channel 16j + 4*lg + i.
 template <int DV, int NQ>
-__device__ __forceinline__ void pv_half(const char* vt, int ks, int lg, int lr, const u32x4_t (&pk)[NQ],
+__device__ __forceinline__ void pv_half(const char* vt, int ks, uint32_t vlane, const u32x4_t (&pk)[NQ],
                                         f32x4_t (&acc)[NQ][DV / 16]) {
-  uint32_t vr[8][DV / 32];
-  lds_v_step<DV>(vt, ks, lg, lr, vr);
 #pragma unroll
   for (int j = 0; j < DV / 16; ++j) {
-    const u32x4_t va = v_operand<DV>(vr, j);
+    const u32x4_t va = lds_vt_operand<DV>(vt, ks, j, vlane);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) acc[q][j] = mfma_bf16(va, pk[q], acc[q][j]);
   }
@@ -207,6 +275,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   for (int e = tid; e < kTileQ * (Jtile + 1); e += kThreads) s_score[e / (Jtile + 1)][e % (Jtile + 1)] = 0.f;
 
   const SO so(lane);
+  const uint32_t vcopy = VSwizzle<DV>::copy_offset(wave, lane);
+  const uint32_t vlane = vt_lane_offset<DV>(lg, lr);
   auto stage = [&](int c, int buf) {
     char* kt = s_buf[buf];
     char* vt = s_buf[buf] + SH::kKBytes;
@@ -214,13 +284,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     if (c < nW) {
       const int64_t r0 = xlo + 64 * c;
       stage_k(kraw, r0, T - 1, kt, wave, lane, so);
-      stage_v(vraw, r0, T - 1, vt, wave, lane, so);
+      stage_v_swizzled<DV, 64, kWaves>(vraw, r0, T - 1, vt, wave, lane, vcopy);
     } else if (c < nW + nC) {
       stage_k(kcmp, 64 * (c - nW), p.nc - 1, kt, wave, lane, so);
     } else {
       const int64_t r0 = 64 * (c - nW - nC);
       stage_k(kcmp, r0, p.nc - 1, kt, wave, lane, so);
-      stage_v(vcmp, r0, p.nc - 1, vt, wave, lane, so);
+      stage_v_swizzled<DV, 64, kWaves>(vcmp, r0, p.nc - 1, vt, wave, lane, vcopy);
     }
   };
 
@@ -304,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
           d = mfma_bf16(a, qf[q][ks], d);
         }
       }
-    constexpr int KD = KT < kReadAhead ? KT : kReadAhead;
+    constexpr int KD = 1;  // registers are nearly all taken by the two positions' state
     __builtin_amdgcn_sched_group_barrier(0x100, 4 * KD, 0);
 #pragma unroll
     for (int ks = 0; ks < KT; ++ks) {
@@ -346,12 +416,12 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
     u32x4_t pk[kWaveQ];
 #pragma unroll
     for (int q = 0; q < kWaveQ; ++q) pk[q] = exp_pack(z0[q], sc, -mref[q]);
-    pv_half<DV>(vt, 0, lg, lr, pk, acc);
+    pv_half<DV>(vt, 0, vlane, pk, acc);
 #pragma unroll
     for (int q = 0; q < kWaveQ; ++q) lsum[q] = mfma_bf16(ones_a, pk[q], lsum[q]);
 #pragma unroll
     for (int q = 0; q < kWaveQ; ++q) pk[q] = exp_pack(z1[q], sc, -mref[q]);
-    pv_half<DV>(vt, 1, lg, lr, pk, acc);
+    pv_half<DV>(vt, 1, vlane, pk, acc);
 #pragma unroll
     for (int q = 0; q < kWaveQ; ++q) lsum[q] = mfma_bf16(ones_a, pk[q], lsum[q]);
   }
@@ -468,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
           }
         pl[q] = pack_probs(ra[0], ra[1]);
       }
-      pv_half<DV>(vt, hh, lg, lr, pg, acc);
+      pv_half<DV>(vt, hh, vlane, pg, acc);
       const int jb = i0 / rd;
       const int nrows = (i0 - jb * rd + 31 + qd - 1) / rd + 1;  // blocks the step touches (<= 32)
 #pragma unroll
@@ -506,15 +576,9 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
 #pragma unroll
   for (int q = 0; q < kWaveQ; ++q) {
     if (!act[q] || lr >= p.G) continue;
-    float* dst = p.acc + (((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * DV;
+    float* dst = p.acc + (((int64_t)b * T + tq[q]) * p.Hq + (int64_t)g * p.G + lr) * DV + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* d = dst + acc_channel<DV>(lg, i, 0);
-#pragma unroll
-      for (int j = 0; j < VC; j += 4)
-        *reinterpret_cast<f32x4_t*>(d + j) =
-            f32x4_t{acc[q][j][i], acc[q][j + 1][i], acc[q][j + 2][i], acc[q][j + 3][i]};
-    }
+    for (int j = 0; j < VC; ++j) *reinterpret_cast<f32x4_t*>(dst + 16 * j) = acc[q][j];
   }
 }
 
@@ -585,75 +649,6 @@ __device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t r
       copy16_to_lds(base + row * DK + 8 * (P % SW::R), dst + 1024 * c);
     }
   }
-}
-
-// The V rows of a step, staged row-major with the 16-byte pieces of row r
-// XOR-permuted by f(r) (a permutation inside the row), and read back as V^T
-// MFMA operands with the LDS transpose read: the 16 lanes of a lane group point
-// at 4 rows x 16 channels (4 lanes per row, 4 channels each) and lane i receives
-// channel i of the 4 rows.  f spreads the 32 lanes of each half-wave over all 16
-// bank groups of 16 bytes.
-template <int DV>
-struct VSwizzle {
-  static_assert(DV == 64 || DV == 128, "transposed V reads are laid out for d_v = 64 or 128");
-  static constexpr int PR = DV / 8;  // 16-byte pieces per row
-  __device__ static int f(int r) { return DV == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
-  // lane's byte offset of its piece in copy c's 1 KB (full tiles): depends on c
-  // only through c mod 2, so one value serves all copies of a wave when NW is even
-  __device__ static uint32_t copy_offset(int c, int lane) {
-    const int r = (64 * c + lane) / PR;
-    return 16u * (uint32_t)((lane - lane % PR) + ((lane % PR) ^ f(r)));
-  }
-};
-
-template <int DV, int ROWS, int NW>
-__device__ __forceinline__ void stage_v_swizzled(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst,
-                                                 int wave, int lane, uint32_t voff) {
-  using VS = VSwizzle<DV>;
-  constexpr int NI = ROWS * VS::PR / 64, PW = (NI + NW - 1) / NW;
-  static_assert(NW % 2 == 0, "one copy offset per wave");
-  if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform
-    const char* tile = reinterpret_cast<const char*>(base + row0 * DV);
-#pragma unroll
-    for (int k = 0; k < PW; ++k) {
-      const int c = wave + NW * k;
-      if (NI % NW != 0 && c >= NI) break;
-      copy16_to_lds_sb(tile + 1024 * c, voff, dst + 1024 * c);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < PW; ++k) {
-      const int c = wave + NW * k;
-      if (NI % NW != 0 && c >= NI) break;
-      const int sl = 64 * c + lane, r = sl / VS::PR;
-      int64_t row = row0 + r;
-      row = row < rowmax ? row : rowmax;
-      copy16_to_lds(base + row * DV + 8 * ((sl % VS::PR) ^ VS::f(r)), dst + 1024 * c);
-    }
-  }
-}
-
-// This lane's part of the transposed-read addresses: row 4*lg + lr/4 of a
-// 16-row half, 8 bytes at channel 4*(lr%4) of a 16-channel block, before the
-// block index j is XOR-ed into bits 5.. (32*j).
-template <int DV>
-__device__ __forceinline__ uint32_t vt_lane_offset(int lg, int lr) {
-  const int r = 4 * lg + lr / 4;
-  return (uint32_t)(r * DV * 2 + 16 * (VSwizzle<DV>::f(r) + (lr % 4) / 2) + 8 * (lr % 2));
-}
-
-// V^T operand of channels 16j .. 16j+15 for the 32-key step at row 32*ks of the
-// staged tile: element e of lane (lg, lr) is channel 16j + lr of key
-// step_key(lg, e).
-template <int DV>
-__device__ __forceinline__ u32x4_t lds_vt_operand(const char* vt, int ks, int j, uint32_t vlane) {
-  typedef short v4i16_t __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4i16_t* lds_v4_t;
-  const char* pa = vt + 32 * ks * DV * 2 + (vlane ^ (32u * (uint32_t)j));
-  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(pa));
-  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_t)(pa + 16 * DV * 2));
-  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
-  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
 }
 
 template <int DK, int DV, int LSEL>
