@@ -658,7 +658,7 @@ def bench_prefill(args, torch, N, I):
     return res
 
 
-def selection_reuse(sel, p, tiles=(16, 32, 64)):
+def selection_reuse(sel, p, tiles=(8, 16, 32, 64)):
     """For position tiles of each size: the mean number of distinct selected blocks of a
     tile (the blocks one workgroup stages per (sequence, KV group)) and the positions
     served per staged block (selections made in the tile / distinct blocks), over every
