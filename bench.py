@@ -285,7 +285,7 @@ def needle_hits(case, sel):
 
 
 CLK_SLOTS, CLK_GROUPS = 16, 4096
-K1_PHASES = {0: "start", 1: "last_tile", 2: "stored"}
+K1_PHASES = {0: "start", 1: "last_tile", 3: "waves_done", 4: "outputs_merged", 2: "stored"}
 K2_PHASES = {0: "start", 1: "loads_arrived", 2: "scores_ready", 3: "topn_done", 4: "steps_done",
              5: "partials_stored", 6: "merge_start", 7: "out_written"}
 

@@ -420,7 +420,8 @@ nsa_status_t nsa_set_phase_events(void* const* events, int32_t count);
  * constant 100 MHz clock (uint64 ticks) at numbered points of the kernel into
  * `buffer` (device memory, at least 2 * 4096 * 16 * 8 = 1 MiB): kernel k's
  * workgroup w writes entries [(k * 4096 + w) * 16, ... + 16).
- *   kernel 0 (compressed stream): 0 start, 1 last tile computed, 2 outputs stored;
+ *   kernel 0 (compressed stream): 0 start, 1 last tile computed (wave 0), 3 every wave done,
+ *   4 outputs merged, 2 outputs stored;
  *   kernel 1 (selection): 0 start, 1 first loads arrived, 2 group scores ready,
  *            3 top-n done, 4 selected and window steps computed, 5 partials
  *            stored, 6 (last workgroup of a (sequence, group) only) merge

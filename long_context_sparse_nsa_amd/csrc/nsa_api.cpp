@@ -95,7 +95,8 @@ nsa_status_t check_decode_sizes(const nsa_dims_t* dims, const nsa_config_t* cfg,
                                                    cfg->l_sel, cfg->n_sel, cfg->n_local, cfg->w, max_seq_len);
   if ((int64_t)dims->batch * dims->num_kv_heads * (lay.nch + lay.nwin + lay.nfin) > (int64_t)INT32_MAX / 2)
     return fail(NSA_ERROR_UNSUPPORTED, "launch too large");
-  if ((int64_t)lay.nch * lay.seg < nc || lay.nch > nsa::kMaxChunks || lay.nbo + 1 > nsa::kScStrideMax - 3)
+  if ((int64_t)lay.nch * lay.seg < nc || lay.nch > nsa::kMaxChunks || lay.nbo + 1 > nsa::kScStrideMax - 3 ||
+      lay.seg > nsa::kSegRows)
     return fail(NSA_ERROR_UNSUPPORTED, "no segment plan for %lld compressed blocks with l_sel/d=%d", (long long)nc,
                 cfg->l_sel / cfg->d);
   if (lay.nwin > nsa::kMaxWindow)

@@ -202,10 +202,6 @@ __device__ __forceinline__ void step_logits(const Step<DK, DV>& st, const u32x4_
 
 // ---------------------------------------------------------------- streaming pass
 
-// Smallest row stride >= n that is 4 mod 16: the four lane groups of a wave then
-// address disjoint LDS banks when they add into four different head rows.
-__host__ __device__ constexpr int score_stride(int n) { return n + ((20 - n % 16) % 16); }
-
 // The 16 rows of a 64-row tile that one wave owns, held in registers in MFMA
 // operand order: K row lr, dims 32*ks + 8*lg .. (A operand of S^T), and V rows
 // 4*lg + e, channels (DV/16)*lr .. (the values its P^T k-slots pair with).
@@ -294,7 +290,7 @@ __device__ __forceinline__ void step_load_full(Step<DK, DV>& st, const uint16_t*
 
 // Workgroup of the streaming pass: kStreamWaves waves stream the rows of a
 // segment of the compressed cache (or of part of the window of the raw cache)
-// as 64-row tiles; wave w owns rows 16w .. 16w+15 of every tile and loads them
+// as kStreamTile-row tiles; wave w owns rows 16w .. 16w+15 of every tile and loads them
 // straight into registers, kDepth - 1 tiles ahead of the one it computes:
 //   logits  S^T = K . q^T                      (16x16x32 MFMA, d_k/32 k-steps)
 //   values  O^T += V^T . P^T                   (16x16x16 MFMA; P^T is the logit tile)
@@ -302,11 +298,14 @@ __device__ __forceinline__ void step_load_full(Step<DK, DV>& st, const uint16_t*
 //           per-head score rows of the segment's selection blocks in LDS, in a
 //           fixed order, so repeated calls give identical results
 // Omega[key][block] is the number of stride units key and block share (an exact
-// small integer; divided by l/d when the scores are written out).  The four
-// waves keep one softmax reference per head: each tile's per-wave maxima are
-// exchanged through LDS (the only barrier of a tile), and the reference moves
-// (rescaling the outputs, the sums and the scores) only when a tile maximum
-// exceeds it by kLazy.
+// small integer; divided by l/d when the scores are written out).  Each wave
+// keeps its own softmax reference per head, moved (rescaling its outputs and
+// sums) only when a tile maximum exceeds it by kLazy, so the tile loop has no
+// barrier and the waves stream independently.  A wave's fold rows of every tile
+// are kept in LDS with the reference they were computed against; at the end the
+// workgroup merges the waves' (m, l, o) and sums each block's fold rows, scaled
+// to the common reference, in tile and wave order, so repeated calls give
+// identical results.
 //
 // Outputs per compressed segment: the reference m, the sum l of exp2(z - m), the
 // unnormalised output sum, and the selection-block scores (slot nbo is the
@@ -315,18 +314,14 @@ __device__ __forceinline__ void step_load_full(Step<DK, DV>& st, const uint16_t*
 template <int DK, int DV>
 __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(DecodeParams p) {
   constexpr int NW = kStreamWaves, NTH = 64 * NW, KT = DK / 32, VC = DV / 16;
-#ifndef NSA_STREAM_DEPTH
-#define NSA_STREAM_DEPTH 3
-#endif
-  constexpr int kDepth = NSA_STREAM_DEPTH;  // register tiles per wave (kDepth in flight while one is awaited)
+  constexpr int TR = kStreamTile;  // rows per tile
+  constexpr int kDepth = 2;        // register tiles per wave (two waves per SIMD: one in flight while one is computed)
   constexpr int PSTRIDE = 32 + 16 * DV;
   constexpr float kLazy = 8.0f, kNegBig = -1e30f;
-  __shared__ float s_sc[16 * kScStrideMax];
   __shared__ float s_o[NW][16][DV + 1];
-  __shared__ __attribute__((aligned(16))) float s_fw[2][NW][16][16];  // per-wave fold results [head][block row]
-  __shared__ float s_tmax[2][NW][16];
-  __shared__ float s_alpha[16];
-  __shared__ float s_l[NW][16];
+  __shared__ __attribute__((aligned(16))) float s_fw[kSegTiles][NW][16][16];  // fold rows [tile][wave][head][block row]
+  __shared__ float s_fm[kSegTiles][NW][16];  // the reference each tile's fold rows are relative to
+  __shared__ float s_l[NW][16], s_m[NW][16], s_fac[NW][16];
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -340,7 +335,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   WaveTile<DK, DV> tb[kDepth];
   auto load_q = [&]() { load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf); };
 
-  // rows [r0, r0 + 64*nt) are streamed; keys outside [vlo, vhi] are masked
+  // rows [r0, r0 + TR*nt) are streamed; keys outside [vlo, vhi] are masked
   int64_t r0, rowmax;
   int nt, vlo, vhi;
   const uint16_t *kb, *vb;
@@ -360,7 +355,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     load_q();
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d)
-      load_wave_tile<DK, DV>(tb[d], kb, vb, (int64_t)k0 + 64 * d + 16 * wave, rpre, koff, voff, lg, lr);
+      load_wave_tile<DK, DV>(tb[d], kb, vb, (int64_t)k0 + TR * d + 16 * wave, rpre, koff, voff, lg, lr);
     const int nvis = n_visible(p, b, L);
     if (k0 >= nvis) {  // empty segment: never read by the selection kernel
       wait_vmem();
@@ -368,7 +363,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     }
     const int k1 = min(k0 + p.seg, nvis);
     r0 = k0;
-    nt = (k1 - k0 + 63) >> 6;
+    nt = (k1 - k0 + TR - 1) / TR;
     vlo = k0;
     vhi = k1 - 1;
     rowmax = nvis - 1;
@@ -378,8 +373,8 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     L = seq_len_clamped(p, b);
     const int t = L - 1;
     const int wlo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
-    const int T0 = (wlo >> 6) + wi * p.wtiles, T1 = min((wlo >> 6) + (wi + 1) * p.wtiles, (t >> 6) + 1);
-    r0 = (int64_t)T0 * 64;
+    const int T0 = wlo / TR + wi * p.wtiles, T1 = min(wlo / TR + (wi + 1) * p.wtiles, t / TR + 1);
+    r0 = (int64_t)T0 * TR;
     nt = T1 - T0;
     vlo = wlo;
     vhi = t;
@@ -395,44 +390,18 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     load_q();
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d)
-      load_wave_tile<DK, DV>(tb[d], kb, vb, r0 + 64 * d + 16 * wave, min(rowmax, r0 + 64 * (int64_t)nt - 1), koff,
+      load_wave_tile<DK, DV>(tb[d], kb, vb, r0 + TR * d + 16 * wave, min(rowmax, r0 + TR * (int64_t)nt - 1), koff,
                              voff, lg, lr);
   }
 
   // Loads never read past the workgroup's own last row: requests for tiles
   // beyond the range (issued so that every pipeline step has the same loads in
   // flight) re-read that row from cache.
-  const int64_t rlast = min(rowmax, r0 + 64 * (int64_t)nt - 1);
+  const int64_t rlast = min(rowmax, r0 + TR * (int64_t)nt - 1);
 
   const int qd = p.l / p.d, rd = p.lsel / p.d;  // key and block lengths in stride units
   const int rsh = __builtin_ctz(rd);            // rd is a power of two
   const int jseg0 = fold ? (int)(r0 >> rsh) : 0;
-  const int sstride = score_stride(p.nbo + 1);
-  if (fold)
-    for (int e = tid; e < 16 * sstride; e += NTH) s_sc[e] = 0.f;
-
-  // Adds tile i's fold results into the score rows: entry (head h, block j) is
-  // the sum over the waves, in wave order, of the rows their keys give block j
-  // (so the scores do not depend on wave timing).
-  auto fold_flush = [&](int i) {
-    const int kt0 = (int)(r0 + 64 * i);
-    const int jT0 = kt0 >> rsh;
-    const int nr = ((kt0 + 63 + qd - 1) >> rsh) - jT0 + 1;  // blocks the tile's keys touch
-    const float(*fw)[16][16] = s_fw[i & 1];
-    for (int e = tid; e < 16 * nr; e += NTH) {
-      const int h = e & 15, j = jT0 + (e >> 4);
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int kw = kt0 + 16 * w, j0w = kw >> rsh;
-        const int nrw = ((kw + 15 + qd - 1) >> rsh) - j0w + 1;
-        const int row = j - j0w;
-        if (row >= 0 && row < nrw) v += fw[w][h][row];
-      }
-      s_sc[h * sstride + (j - jseg0)] += v;
-    }
-  };
-
   f32x4_t acc[VC];
 #pragma unroll
   for (int j = 0; j < VC; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -440,7 +409,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   const float sc = p.scale_log2;
 
   auto process = [&](int i, const WaveTile<DK, DV>& T) {
-    const int64_t k0 = r0 + 64 * i + 16 * wave;  // the wave's first row
+    const int64_t k0 = r0 + TR * i + 16 * wave;  // the wave's first row
     // ---- logits of the wave's 16 rows; element e is row k0 + 4lg + e, head lr
     f32x4_t sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -456,16 +425,10 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
         z[e] = (x >= vlo && x <= vhi) ? sv[e] * sc : -INFINITY;
       }
     }
-    float mw = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mw = max_over_groups_swap(mw);
-    if (lg == 0) s_tmax[i & 1][wave][lr] = mw;
-    lds_barrier();  // the tile's maxima, and the previous tile's fold results, are complete
-    if (fold && i > 0) fold_flush(i - 1);
-    float mt = s_tmax[i & 1][0][lr];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) mt = fmaxf(mt, s_tmax[i & 1][w][lr]);
+    float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt = max_over_groups_swap(mt);  // head lr's maximum over the wave's 16 rows
 
-    // ---- lazy reference move (identical decision in every wave)
+    // ---- lazy move of this wave's reference
     const bool move = mt > mref + kLazy;
     if (__ballot(move) != 0ull) {
       const float mn = move ? mt : mref;
@@ -474,12 +437,6 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
       for (int j = 0; j < VC; ++j) acc[j] *= alpha;
       lsum *= alpha;
       mref = mn;
-      if (fold && i > 0) {
-        if (wave == 0 && lg == 0) s_alpha[lr] = alpha;
-        lds_barrier();  // also orders every thread's flush before the scaling
-        for (int e = tid; e < 16 * sstride; e += NTH) s_sc[e] *= s_alpha[e / sstride];
-        lds_barrier();
-      }
     }
 
     // ---- probabilities, values (rows past rlast may hold values of rows past the
@@ -521,7 +478,8 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
       f32x4_t f = mfma16_bf16(om, ph, f32x4_t{0.f, 0.f, 0.f, 0.f});
       f = mfma16_bf16(om, pl, f);
       // element e: block j0 + 4lg + e, head lr
-      *reinterpret_cast<f32x4_t*>(&s_fw[i & 1][wave][lr][4 * lg]) = f;
+      *reinterpret_cast<f32x4_t*>(&s_fw[i][wave][lr][4 * lg]) = f;
+      if (lg == 0) s_fm[i][wave][lr] = mref;
     }
   };
 
@@ -533,7 +491,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   for (; i0 + kDepth <= nt; i0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      load_wave_tile<DK, DV>(tb[(u + kDepth - 1) % kDepth], kb, vb, r0 + 64 * (i0 + u + kDepth - 1) + 16 * wave,
+      load_wave_tile<DK, DV>(tb[(u + kDepth - 1) % kDepth], kb, vb, r0 + TR * (i0 + u + kDepth - 1) + 16 * wave,
                              rlast, koff, voff, lg, lr);
       process(i0 + u, tb[u]);
     }
@@ -543,18 +501,27 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     if (i0 + u < nt) process(i0 + u, tb[u]);  // workgroup-uniform
   clk_stamp(p.clk, 1);
 
-  // ---- workgroup merge: all waves share mref, so outputs and sums just add
+  // ---- workgroup merge: the waves' (m, l, o) to the common reference M (per head)
   lsum = sum_over_groups_swap(lsum);
-  if (lg == 0) s_l[wave][lr] = lsum;
+  if (lg == 0) {
+    s_l[wave][lr] = lsum;
+    s_m[wave][lr] = mref;
+  }
 #pragma unroll
   for (int j = 0; j < VC; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) s_o[wave][lr][acc_channel<DV>(lg, e, j)] = acc[j][e];
   lds_barrier();
-  if (fold) {
-    fold_flush(nt - 1);
-    lds_barrier();
+  float Mh = s_m[0][lr];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) Mh = fmaxf(Mh, s_m[w][lr]);  // lane lr: head lr
+  if (tid < 16 * NW) s_fac[tid >> 4][lr] = __builtin_amdgcn_exp2f(s_m[tid >> 4][lr] - Mh);  // (wave, head)
+  if (fold) {  // the fold rows' references become their factors to M (entry e: head e mod 16 = lr)
+    float* fm = &s_fm[0][0][0];
+    for (int e = tid; e < NW * nt * 16; e += NTH) fm[e] = __builtin_amdgcn_exp2f(fm[e] - Mh);
   }
+  clk_stamp(p.clk, 3);
+  lds_barrier();
   float *dm, *dl, *dox;
   if (fold) {
     const size_t slot = (size_t)bg * p.nch + c;
@@ -574,30 +541,40 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
       const int h = wave + NW * hh, ch = lane + 64 * cc;
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v += s_o[w][h][ch];
+      for (int w = 0; w < NW; ++w) v += s_fac[w][h] * s_o[w][h][ch];
       dox[h * DV + ch] = v;
     }
-  if (tid < 16) {  // lane tid holds head tid's reference
+  clk_stamp(p.clk, 4);
+  if (tid < 16) {  // lane tid: head tid (Mh of lane tid is head tid's)
     float ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) ls += s_l[w][tid];
+    for (int w = 0; w < NW; ++w) ls += s_fac[w][tid] * s_l[w][tid];
     dl[tid] = ls;
-    dm[tid] = mref;
+    dm[tid] = Mh;
   }
   if (fold) {
+    // Scores of the segment's blocks jseg0 .. jseg0 + nbo (slot nbo is the
+    // overhang into the next segment's first block): block J sums the fold rows
+    // J - j0 of the wave-tiles whose keys reach into it, each scaled from its
+    // own reference to M, in tile and wave order.
     const int slots = p.nbo + 1;
     const float invq = 1.0f / (float)qd;
     float* SC = p.sc1 + ((size_t)bg * p.nch + c) * slots * 16;  // [slot][head]
-    for (int e0 = tid; e0 < 16 * slots; e0 += 4 * NTH) {  // four entries per thread and pass
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + NTH * u;
-        v[u] = e < 16 * slots ? s_sc[(e & 15) * sstride + (e >> 4)] : 0.f;
+    const float(*fm)[16] = reinterpret_cast<const float(*)[16]>(&s_fm[0][0][0]);        // [u][head]
+    const float(*fw)[16][16] = reinterpret_cast<const float(*)[16][16]>(&s_fw[0][0][0][0]);  // [u][head][row]
+    for (int e = tid; e < 16 * slots; e += NTH) {  // head e mod 16 = lr
+      const int J = jseg0 + (e >> 4);
+      // wave-tiles u = NW*i + w start at key r0 + 16u; their keys [K, K + 15 + qd - 1]
+      // (stride units) reach block J iff K <= J*rd + rd - 1 and K + 15 + qd - 1 >= J*rd
+      const int klo = J * rd - (15 + qd - 1) - (int)r0, khi = J * rd + rd - 1 - (int)r0;
+      const int ulo = klo > 0 ? (klo + 15) >> 4 : 0;
+      const int uhi = khi >= 0 ? min(khi >> 4, NW * nt - 1) : -1;
+      float v = 0.f;
+      for (int u = ulo; u <= uhi; ++u) {
+        const int row = J - (((int)r0 + 16 * u) >> rsh);
+        if (row >= 0 && row < 16) v += fm[u][lr] * fw[u][lr][row];
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (e0 + NTH * u < 16 * slots) SC[e0 + NTH * u] = v[u] * invq;
+      SC[e] = v * invq;
     }
   }
   clk_stamp(p.clk, 2);
@@ -1080,22 +1057,22 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   DecodeLayout lay{};
   const int64_t nc = max_len >= l ? (max_len - l) / d + 1 : 0;
   const int r = lsel / d;
-  const int64_t gran = r > 64 ? r : 64;  // segments hold whole tiles and whole selection blocks
+  const int64_t gran = r > kStreamTile ? r : kStreamTile;  // segments hold whole tiles and whole selection blocks
   auto up = [&](int64_t x) { return (x + gran - 1) / gran * gran; };
   // Rows per (sequence, group): the compressed keys plus the window's tiles,
   // spread over about kStreamSlots / (B*H) workgroups (at least one segment and
   // one window workgroup).
-  const int64_t win_tiles = (w + 63) / 64 + 1;
+  const int64_t win_tiles = (w + kStreamTile - 1) / kStreamTile + 1;
   const int64_t bh = (int64_t)B * H;
   // At least about one workgroup per compute unit, and segments of at most
-  // about kSegTiles tiles, so that the longest sequence of a ragged batch does
-  // not set a long critical path (segments past a shorter sequence end at once).
-  const int64_t rows = nc + 64 * win_tiles;
+  // kSegRows keys, so that the longest sequence of a ragged batch does not set
+  // a long critical path (segments past a shorter sequence end at once).
+  const int64_t rows = nc + kStreamTile * win_tiles;
   int64_t per_bg = bh >= kStreamSlots / 2 ? 2 : kStreamSlots / bh;
-  if (per_bg < (rows + 64 * kSegTiles - 1) / (64 * kSegTiles)) per_bg = (rows + 64 * kSegTiles - 1) / (64 * kSegTiles);
+  if (per_bg < (rows + kSegRows - 1) / kSegRows) per_bg = (rows + kSegRows - 1) / kSegRows;
   int64_t seg = up((rows + per_bg - 1) / per_bg);
   const int64_t seg_min = up((nc + kMaxChunks - 1) / kMaxChunks);
-  const int64_t seg_max = (int64_t)(kScStrideMax - 4) * r / gran * gran;  // score rows fit the LDS table
+  const int64_t seg_max = (int64_t)(kScStrideMax - 4) * r / gran * gran;  // score slots per segment
   if (seg < seg_min) seg = seg_min;
   if (seg > seg_max) seg = seg_max;  // the host rejects seg_min > seg_max
   if (seg < gran) seg = gran;
@@ -1103,7 +1080,7 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   lay.nch = (int)((nc + seg - 1) / seg);
   if (lay.nch < 1) lay.nch = 1;
   lay.nbo = (int)(seg / r);
-  int64_t wt = seg / 64;
+  int64_t wt = seg / kStreamTile;
   if (wt * kMaxWindow < win_tiles) wt = (win_tiles + kMaxWindow - 1) / kMaxWindow;
   lay.wtiles = (int)wt;
   lay.nwin = (int)((win_tiles + wt - 1) / wt);

@@ -7,17 +7,19 @@
 
 namespace nsa {
 
-// Decode streaming pass: workgroups of kStreamWaves waves stream 64-row tiles
+// Decode streaming pass: workgroups of kStreamWaves waves stream kStreamTile-row tiles
 // of one segment of the compressed cache (or of the window); the segment
 // length is chosen so that one launch has about kStreamSlots workgroups (one
 // per compute unit of an MI355X).
-constexpr int kStreamWaves = 4;
+constexpr int kStreamWaves = 8;
 constexpr int kStreamSlots = 256;
-constexpr int kScStrideMax = 548;     // LDS score row stride limit (floats): selection blocks per segment + 1
+constexpr int kStreamTile = 16 * kStreamWaves;  // rows per streamed tile (16 per wave)
+constexpr int kScStrideMax = 548;     // selection blocks per decode segment + 4, at most
 // Limits of the on-chip tables (checked by the host before any launch).
 constexpr int kMaxCompressed = 32768;                 // compressed blocks per sequence in decode
 constexpr int kMaxChunks = 64;                        // compressed segments per sequence in decode
-constexpr int kSegTiles = 10;                         // 64-row tiles per decode segment aimed at (at most)
+constexpr int kSegRows = 640;                         // compressed keys per decode segment, at most
+constexpr int kSegTiles = kSegRows / kStreamTile;     // streamed tiles per segment, at most (LDS fold rows)
 constexpr int kMaxBlocks = 8192;     // selection candidates J+1
 constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query
