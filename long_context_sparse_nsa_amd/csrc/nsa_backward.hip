@@ -41,29 +41,6 @@ constexpr int kCmp = 0, kSlc = 1, kWin = 2;  // branch ids (gate and lse slot or
 constexpr int kBwdWaves = 4;                 // waves per workgroup
 constexpr float kNegInf = -__builtin_inff();
 
-// Wave-wide direct global -> LDS copy of 64 x 16 bytes (as copy16_to_lds) to
-// the wave-uniform LDS byte address `lds_addr`: lane l's 16 bytes land at
-// lds_addr + 16 * l.
-__device__ __forceinline__ void copy16_to_lds_at(const void* src, uint32_t lds_addr) {
-  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-               : "memory", "m0");
-}
-// The same copy from a wave-uniform base address plus this lane's 32-bit byte
-// offset (the scalar-base form of the instruction).
-__device__ __forceinline__ void copy16_sb_at(const void* base, uint32_t voff, uint32_t lds_addr) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
-                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(lds)
-               : "memory", "m0");
-}
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr_of(const void* shared_ptr) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)shared_ptr;
-}
-
 // Wait until this wave's copies of at most `later` subsequent steps (C copy
 // instructions each, LATER at most) are still in flight; copies complete in
 // issue order.

@@ -161,6 +161,26 @@ __device__ __forceinline__ void copy16_to_lds_sb(const void* base, uint32_t voff
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(lds)
                : "memory", "m0");
 }
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* shared_ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)shared_ptr;
+}
+// The two copies above with the LDS destination given as a wave-uniform LDS byte
+// address (lane l's 16 bytes land at lds_addr + 16 * l): no generic-to-LDS
+// pointer conversion per copy.
+__device__ __forceinline__ void copy16_to_lds_at(const void* src, uint32_t lds_addr) {
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy16_sb_at(const void* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(lds)
+               : "memory", "m0");
+}
 // Workgroup barrier that is also a compiler memory barrier, without the implied
 // wait for outstanding vector-memory operations of __syncthreads().  LDS
 // operations issued before it by the compiler are complete once their results

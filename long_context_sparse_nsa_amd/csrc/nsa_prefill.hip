@@ -103,7 +103,7 @@ struct VSwizzle {
 };
 
 template <int DV, int ROWS, int NW>
-__device__ __forceinline__ void stage_v_swizzled(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst,
+__device__ __forceinline__ void stage_v_swizzled(const uint16_t* base, int64_t row0, int64_t rowmax, uint32_t dst,
                                                  int wave, int lane, uint32_t voff) {
   using VS = VSwizzle<DV>;
   constexpr int NI = ROWS * VS::PR / 64, PW = (NI + NW - 1) / NW;
@@ -114,7 +114,7 @@ __device__ __forceinline__ void stage_v_swizzled(const uint16_t* base, int64_t r
     for (int k = 0; k < PW; ++k) {
       const int c = wave + NW * k;
       if (NI % NW != 0 && c >= NI) break;
-      copy16_to_lds_sb(tile + 1024 * c, voff, dst + 1024 * c);
+      copy16_sb_at(tile + 1024 * c, voff, dst + 1024 * c);
     }
   } else {
 #pragma unroll
@@ -124,7 +124,7 @@ __device__ __forceinline__ void stage_v_swizzled(const uint16_t* base, int64_t r
       const int sl = 64 * c + lane, r = sl / VS::PR;
       int64_t row = row0 + r;
       row = row < rowmax ? row : rowmax;
-      copy16_to_lds(base + row * DV + 8 * ((sl % VS::PR) ^ VS::f(r)), dst + 1024 * c);
+      copy16_to_lds_at(base + row * DV + 8 * ((sl % VS::PR) ^ VS::f(r)), dst + 1024 * c);
     }
   }
 }
@@ -277,9 +277,10 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
   const SO so(lane);
   const uint32_t vcopy = VSwizzle<DV>::copy_offset(wave, lane);
   const uint32_t vlane = vt_lane_offset<DV>(lg, lr);
+  const uint32_t lds_buf0 = lds_addr_of(&s_buf[0][0]);
   auto stage = [&](int c, int buf) {
-    char* kt = s_buf[buf];
-    char* vt = s_buf[buf] + SH::kKBytes;
+    const uint32_t kt = lds_buf0 + (uint32_t)(buf * SH::kBuf);
+    const uint32_t vt = kt + SH::kKBytes;
     // rows past the tile's needs but inside the arrays are copied and masked
     if (c < nW) {
       const int64_t r0 = xlo + 64 * c;
@@ -626,7 +627,7 @@ struct SelKCopies {
   static constexpr int NI = ROWS * SelSwizzle<DK>::R / 64, PW = (NI + NW - 1) / NW;
 };
 template <int DK, int ROWS, int NW>
-__device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst,
+__device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t row0, int64_t rowmax, uint32_t dst,
                                                  int wave, int lane, const uint32_t (&kcopy)[SelKCopies<DK, ROWS, NW>::PW]) {
   using SW = SelSwizzle<DK>;
   constexpr int NI = SelKCopies<DK, ROWS, NW>::NI, PW = SelKCopies<DK, ROWS, NW>::PW;
@@ -636,7 +637,7 @@ __device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t r
     for (int k = 0; k < PW; ++k) {
       const int c = wave + NW * k;
       if (NI % NW != 0 && c >= NI) break;
-      copy16_to_lds_sb(tile + 1024 * c, kcopy[k], dst + 1024 * c);
+      copy16_sb_at(tile + 1024 * c, kcopy[k], dst + 1024 * c);
     }
   } else {
 #pragma unroll
@@ -646,7 +647,7 @@ __device__ __forceinline__ void stage_k_rowmajor(const uint16_t* base, int64_t r
       const int P = SW::slot(64 * c + lane);
       int64_t row = row0 + P / SW::R;
       row = row < rowmax ? row : rowmax;
-      copy16_to_lds(base + row * DK + 8 * (P % SW::R), dst + 1024 * c);
+      copy16_to_lds_at(base + row * DK + 8 * (P % SW::R), dst + 1024 * c);
     }
   }
 }
@@ -762,14 +763,16 @@ __global__ __launch_bounds__(kSelThreads, 2) void pf_sel_kernel(PrefillParams p)
   const uint32_t vcopy = VSwizzle<DV>::copy_offset(wave, lane);
   const uint32_t vlane = vt_lane_offset<DV>(lg, lr);
 
+  const uint32_t lds_buf0 = lds_addr_of(&s_buf[0][0]);
   auto step_row0 = [&](int st) -> int64_t {
     const int u = st / SPB;
     return (int64_t)(s_list[u] >> 16) * LSEL + (int64_t)(st - u * SPB) * ROWS;
   };
   auto stage = [&](int st, int buf) {
     const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane((int)step_row0(st));
-    stage_k_rowmajor<DK, ROWS, kSelWaves>(kraw, r0, T - 1, s_buf[buf], wave, lane, kcopy);
-    stage_v_swizzled<DV, ROWS, kSelWaves>(vraw, r0, T - 1, s_buf[buf] + SO::kKBytes, wave, lane, vcopy);
+    const uint32_t kt = lds_buf0 + (uint32_t)(buf * kStepBytes);
+    stage_k_rowmajor<DK, ROWS, kSelWaves>(kraw, r0, T - 1, kt, wave, lane, kcopy);
+    stage_v_swizzled<DV, ROWS, kSelWaves>(vraw, r0, T - 1, kt + SO::kKBytes, wave, lane, vcopy);
   };
 
   wait_vmem_le<0>();  // query fragments in (see the compressed-branch kernel)

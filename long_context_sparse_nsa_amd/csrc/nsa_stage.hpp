@@ -34,7 +34,7 @@ struct StageOffsets {
 };
 
 template <class SO>
-__device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
+__device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int64_t rowmax, uint32_t dst, int wave,
                                         int lane, const SO& so) {
   constexpr int DK = SO::DK, KT = SO::KT, NF = SO::NF, NW = SO::NW, ROWS = SO::ROWS;
   if (row0 + ROWS - 1 <= rowmax) {  // wave-uniform: the whole tile lies inside the array
@@ -44,7 +44,7 @@ __device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int6
       const int f = wave + NW * ii;
       if (NF % NW != 0 && f >= NF) break;
       const int m = f / KT, ks = f - m * KT;
-      copy16_to_lds_sb(tile + 16 * m * DK + 32 * ks, so.k, dst + f * 1024);
+      copy16_sb_at(tile + 16 * m * DK + 32 * ks, so.k, dst + f * 1024);
     }
   } else {
 #pragma unroll
@@ -54,13 +54,13 @@ __device__ __forceinline__ void stage_k(const uint16_t* base, int64_t row0, int6
       const int m = f / KT, ks = f - m * KT;
       int64_t row = row0 + 16 * m + (lane & 15);
       row = row < rowmax ? row : rowmax;
-      copy16_to_lds(base + row * DK + 32 * ks + 8 * (lane >> 4), dst + f * 1024);
+      copy16_to_lds_at(base + row * DK + 32 * ks + 8 * (lane >> 4), dst + f * 1024);
     }
   }
 }
 
 template <class SO>
-__device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int64_t rowmax, char* dst, int wave,
+__device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int64_t rowmax, uint32_t dst, int wave,
                                         int lane, const SO& so) {
   constexpr int NI = SO::NI, RB = SO::DV * 2, NW = SO::NW, ROWS = SO::ROWS;
   const char* bb = reinterpret_cast<const char*>(base);
@@ -70,7 +70,7 @@ __device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int6
     for (int ii = 0; ii < SO::FV; ++ii) {
       const int i = wave + NW * ii;
       if (NI % NW != 0 && i >= NI) break;
-      copy16_to_lds_sb(tile + i * 1024, so.v, dst + i * 1024);
+      copy16_sb_at(tile + i * 1024, so.v, dst + i * 1024);
     }
   } else {
 #pragma unroll
@@ -80,7 +80,7 @@ __device__ __forceinline__ void stage_v(const uint16_t* base, int64_t row0, int6
       const int off = i * 1024 + lane * 16;
       int64_t row = row0 + off / RB;
       row = row < rowmax ? row : rowmax;
-      copy16_to_lds(bb + row * RB + (off % RB), dst + i * 1024);
+      copy16_to_lds_at(bb + row * RB + (off % RB), dst + i * 1024);
     }
   }
 }
