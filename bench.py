@@ -290,12 +290,16 @@ K2_PHASES = {0: "start", 1: "loads_arrived", 2: "scores_ready", 3: "topn_done", 
              5: "partials_stored", 6: "merge_start", 7: "out_written"}
 
 
-def decode_phase_clock(torch, N, step, n_steps=12):
-    """Per-workgroup phase clock of the two decode kernels (the library's profiling
+DSA_K0_PHASES = {0: "start", 1: "loaded", 2: "digit1", 3: "digit2", 4: "digit3", 5: "bitmaps", 6: "written"}
+DSA_K1_PHASES = {0: "start", 1: "rows_loaded", 2: "first_tile", 3: "tiles_done", 4: "stored"}
+
+
+def decode_phase_clock(torch, N, step, n_steps=12, kernels=((0, "stream", K1_PHASES), (1, "select", K2_PHASES))):
+    """Per-workgroup phase clock of two kernels of a step (the library's profiling
     hook: thread 0 of every workgroup stamps the 100 MHz constant clock at numbered
     points), over eager steps.  Returns, per phase, the median over steps of the
     median and the maximum over workgroups of (stamp - first start of the step's
-    streaming kernel), in microseconds."""
+    first recorded kernel), in microseconds."""
     buf = torch.zeros(2 * CLK_GROUPS * CLK_SLOTS, dtype=torch.int64, device="cuda")
     N.nsa_set_phase_clock(buf)
     per = {}
@@ -308,14 +312,13 @@ def decode_phase_clock(torch, N, step, n_steps=12):
             a = buf.view(2, CLK_GROUPS, CLK_SLOTS).cpu().numpy()
             starts = a[0, :, 0]
             t0 = starts[starts > 0].min()
-            for k, names in ((0, K1_PHASES), (1, K2_PHASES)):
+            for k, kname, names in kernels:
                 for s, nm in names.items():
                     v = a[k, :, s]
                     v = v[v > 0]
                     if v.size:
                         d = (v - t0) / 100.0  # 100 MHz ticks -> us
-                        per.setdefault(f"{'stream' if k == 0 else 'select'}.{nm}", []).append(
-                            (float(np.median(d)), float(d.max())))
+                        per.setdefault(f"{kname}.{nm}", []).append((float(np.median(d)), float(d.max())))
     finally:
         N.nsa_set_phase_clock(None)
     out = {}
@@ -761,6 +764,10 @@ def bench_dsa(args, torch, N, I):
                indexer_gbs=b_keys / (ph[0] * 1e-3) / 1e9, attention_tflops=flops / (ph[2] * 1e-3) / 1e12,
                attention_bytes=b_sel, attention_flops=flops)
     res["hbm_frac"] = res["gbs"] / HBM_PEAK_GBS
+    res["phase_clock_us"] = decode_phase_clock(torch, N, step,
+                                               kernels=((0, "topk", DSA_K0_PHASES), (1, "attn", DSA_K1_PHASES)))
+    log("[bench] dsa phase clock (us after the first top-k workgroup starts; median / max over workgroups): " +
+        ", ".join(f"{k} {v['median_us']}/{v['max_us']}" for k, v in res["phase_clock_us"].items()))
     if not args.no_cpu:
         res["cpu"] = dsa_cpu_baseline(case, args.cpu_seconds / 2)
     log(f"[bench] dsa {wl.name}: {ms * 1e3:.1f} us/step, {res['tokens_per_s']:.4g} tok/s, {res['gbs']:.0f} GB/s "
@@ -1134,6 +1141,7 @@ def main():
                         "frac": dsa["indexer_gbs"] / HBM_PEAK_GBS},
             "attention": {"kernels": "dsa_attn_kernel + dsa_combine_kernel", "TFLOP/s": dsa["attention_tflops"],
                           "mfma_frac": dsa["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS},
+            "phase_clock_us": dsa.get("phase_clock_us"),
             "cpu_oracle": dsa.get("cpu")}
     if dec.get("serving"):
         sv = dec["serving"]

@@ -283,8 +283,7 @@ nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float
                                 void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes for nsa_dsa_decode_fwd (host-only): fp32 scores [B, cache_len]
  * (row stride cache_len rounded up to 4, at offset 0), a selection buffer
- * [B, top_k], the attention partials, and the selection's histogram, counters,
- * position bitmap and candidate list.  Its contents on entry do not matter. */
+ * [B, top_k] and the attention partials.  Its contents on entry do not matter. */
 nsa_status_t nsa_dsa_decode_workspace_size(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_len,
                                            size_t* bytes);
 
@@ -415,17 +414,25 @@ nsa_status_t nsa_compress_bwd_workspace_size(const nsa_dims_t* dims, const nsa_c
 nsa_status_t nsa_set_phase_events(void* const* events, int32_t count);
 
 /*
- * nsa_set_phase_clock — profiling hook for this thread's nsa_decode_fwd calls:
- * thread 0 of every workgroup of the two decode kernels writes the device's
- * constant 100 MHz clock (uint64 ticks) at numbered points of the kernel into
- * `buffer` (device memory, at least 2 * 4096 * 16 * 8 = 1 MiB): kernel k's
- * workgroup w writes entries [(k * 4096 + w) * 16, ... + 16).
+ * nsa_set_phase_clock — profiling hook for this thread's nsa_decode_fwd and
+ * nsa_dsa_decode_fwd calls: thread 0 of every workgroup of two of a step's
+ * kernels writes the device's constant 100 MHz clock (uint64 ticks) at
+ * numbered points of the kernel into `buffer` (device memory, at least
+ * 2 * 4096 * 16 * 8 = 1 MiB): kernel k's workgroup w writes entries
+ * [(k * 4096 + w) * 16, ... + 16).  For the NSA decode step:
  *   kernel 0 (compressed stream): 0 start, 1 last tile computed (wave 0), 3 every wave done,
  *   4 outputs merged, 2 outputs stored;
  *   kernel 1 (selection): 0 start, 1 first loads arrived, 2 group scores ready,
  *            3 top-n done, 4 selected and window steps computed, 5 partials
  *            stored, 6 (last workgroup of a (sequence, group) only) merge
- *            begins, 7 output written.
+ *            begins, 7 output written;
+ * and of the DSA step:
+ *   kernel 0 (top-k, one workgroup per sequence): 0 start, 1 scores loaded,
+ *            2, 3, 4 first, second and third radix digit found, 5 position
+ *            bitmaps built, 6 positions written (1..6 only when the sequence
+ *            has more than top_k positions);
+ *   kernel 1 (attention): 0 start, 1 positions and queries loaded, 2 first
+ *            tile staged, 3 every tile done, 4 partial stored.
  * Entries of workgroups that end early are not written.  Nothing is recorded
  * when a kernel has more than 4096 workgroups.  buffer NULL or bytes 0
  * disables it (the default); a smaller buffer is NSA_ERROR_WORKSPACE.  The

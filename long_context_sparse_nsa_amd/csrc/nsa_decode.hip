@@ -78,12 +78,6 @@ __device__ __forceinline__ int n_visible(const DecodeParams& p, int b, int L) {
   return (int)(nv < ccap ? nv : ccap);
 }
 
-// Profiling hook: thread 0 records the constant 100 MHz clock at point `slot`
-// of this workgroup (clk is null unless the caller asked for a phase clock).
-__device__ __forceinline__ void clk_stamp(uint64_t* clk, int slot) {
-  if (clk != nullptr && threadIdx.x == 0) clk[(size_t)blockIdx.x * kClkSlots + slot] = __builtin_amdgcn_s_memrealtime();
-}
-
 // Stores and loads that are coherent across the whole device without cache
 // maintenance (relaxed atomics at agent scope): the selection workgroups of one
 // (sequence, group) hand their partials to the last of them this way.

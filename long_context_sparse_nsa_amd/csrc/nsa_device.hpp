@@ -11,7 +11,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "nsa_internal.hpp"
+
 namespace nsa {
+
+// Profiling hook: thread 0 records the constant 100 MHz clock at point `slot`
+// of this workgroup (clk is null unless the caller asked for a phase clock).
+__device__ __forceinline__ void clk_stamp(uint64_t* clk, int slot) {
+  if (clk != nullptr && threadIdx.x == 0) clk[(size_t)blockIdx.x * kClkSlots + slot] = __builtin_amdgcn_s_memrealtime();
+}
 
 typedef short bf16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));

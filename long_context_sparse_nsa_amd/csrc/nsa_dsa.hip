@@ -14,14 +14,11 @@
 //     16-token tiles with v_mfma_f32_16x16x32_fp8_fp8 (indexer heads x tokens),
 //     ReLU, the weighted head sum, and writes fp32 scores.  Tile loads run a
 //     batch of eight tiles ahead of the compute.
-//  2. exact top-k by radix select on order-preserving integer keys of the
-//     scores, over 4096-score chunks: dsa_hist_kernel sums the top-13-bit
-//     histogram of every chunk into one per sequence (zeroed by the indexer
-//     launch); dsa_select_kernel marks the positions above the boundary bin in a
-//     bitmap and collects the boundary bin's scores, and the last workgroup of
-//     the sequence finishes the select on those candidates (13 + 6 more bits),
-//     takes ties at the threshold from the lowest positions and writes the
-//     positions ascending.
+//  2. dsa_topk_kernel    exact top-k by radix select on order-preserving integer
+//     keys of the scores, one 1024-thread workgroup per sequence holding all of
+//     its scores in registers: three digit histograms in LDS (13, 13 and 6 bits)
+//     find the k-th largest key, ties at it go to the lowest positions, and the
+//     positions are written ascending from a bitmap in LDS.
 //  3. dsa_attn_kernel    workgroup = (sequence, 64 heads -- 32 when the head
 //     count is not a multiple of 64 --, token split); 32-token tiles of latents
 //     are gathered into LDS with the direct global->LDS copy, four buffers
@@ -66,10 +63,6 @@ __global__ __launch_bounds__(256) void dsa_index_kernel(DsaParams p) {
   constexpr int RT = HI / 16, KS = DI / 32, BPL = DI / 4, LV = BPL / 16, NT = 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int b = blockIdx.x / p.nseg, sg = blockIdx.x - b * p.nseg;
-  if (sg == 0) {  // the selection's histogram and counters start at zero (used by the next launches)
-    for (int i = tid; i < kDsaBins; i += 256) p.hist[(size_t)b * kDsaBins + i] = 0u;
-    if (tid < 4) p.cnt[4 * b + tid] = 0u;
-  }
   const int64_t L = p.seq_lens[b];
   const int64_t n = L < p.cap ? L : p.cap;
   const int64_t s0 = (int64_t)sg * p.seg;
@@ -139,15 +132,34 @@ __global__ __launch_bounds__(256) void dsa_index_kernel(DsaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. exact top-k of the scores
+// 2. exact top-k of the scores: one workgroup of 1024 threads per sequence
+//
+// Radix select on order-preserving integer keys (a larger float gives a larger
+// key), three digits of 13, 13 and 6 bits: each digit's histogram in LDS finds
+// the bin that holds the k-th largest key among the keys that match the digits
+// found so far.  Keys above the final threshold are taken, and the remaining
+// picks come from the keys equal to it, lowest positions first.  Every score of
+// the sequence stays in registers from the single load to the output, and no
+// other workgroup takes part, so there is no hand-off between workgroups.  The
+// workgroup's time goes to instructions per key (a 64-wide instruction takes
+// four cycles of a 16-lane SIMD), so only the first digit's histogram and one
+// classification visit every key: the boundary bin's keys are copied to a
+// candidate list in LDS, and the later digits and the ties are found there.
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkLoads = kDsaMaxLen / (4 * kTopkThreads);  // four-score loads per thread
+constexpr int kTopkWords = kDsaMaxLen / 32;                  // bitmap words per sequence
+constexpr int kTopkWpt = kTopkWords / kTopkThreads;          // bitmap words per thread
+constexpr int kTopkCand = 4096;                              // boundary-bin keys held in LDS
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // larger float -> larger key
 }
 
-// Exclusive prefix over the 256 threads of a selection workgroup.
-__device__ __forceinline__ int scan256(int v, int* s_w, int* total) {
+// Exclusive prefix over the workgroup's threads; *total gets the sum.
+__device__ __forceinline__ int scan_wg(int v, int* s_w, int* total) {
+  constexpr int NW = kTopkThreads / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -159,7 +171,7 @@ __device__ __forceinline__ int scan256(int v, int* s_w, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int s = s_w[w];
     base += w < wave ? s : 0;
     tot += s;
@@ -169,37 +181,22 @@ __device__ __forceinline__ int scan256(int v, int* s_w, int* total) {
   return base + x - v;
 }
 
-// The 16 order keys of this thread's positions c0 + 16*tid .. +15 (0 past n):
-// four 16-byte loads, addresses clamped inside the score row.
-__device__ __forceinline__ void load_keys16(const DsaParams& p, int b, int c0, int n, uint32_t (&key)[16], int& nv) {
-  const float* sc = p.scores + (size_t)b * p.sstride;
-  const int base = c0 + 16 * (int)threadIdx.x, last = (int)p.sstride - 4;
-  f32x4_t v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4_t*>(sc + (base + 4 * q < last ? base + 4 * q : last));
-  nv = n - base;
-  nv = nv < 0 ? 0 : (nv > 16 ? 16 : nv);
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) key[4 * q + e] = 4 * q + e < nv ? order_key(v[q][e]) : 0u;
-}
-
-// In a histogram of `nb` bins (nb / 256 per thread, a power of two; the highest
-// bins to thread 0), the bin holding the need-th largest key and the count of
-// keys above it.  Each thread sums its bins starting at a rotated offset, so the
-// lanes of a wave read different LDS banks; only the thread whose segment holds
-// the boundary walks it in order.
-__device__ __forceinline__ void find_bin(const uint32_t* h, int nb, int need, int* s_w, int* s_found) {
-  const int tid = (int)threadIdx.x, per = nb / 256, g0 = per * (255 - tid);
+// In the kDsaBins-bin histogram h, the bin holding the need-th largest key and
+// the count of keys in higher bins, to s_found[0..1].  Thread t sums bins
+// [kPer*(NT-1-t), +kPer) (thread 0 the highest), starting at a rotated bin so
+// that the lanes of a wave read different LDS banks; only the thread whose bins
+// hold the boundary walks them in order.
+__device__ __forceinline__ void find_bin(const uint32_t* h, int need, int* s_w, int* s_found) {
+  constexpr int kPer = kDsaBins / kTopkThreads;
+  const int tid = (int)threadIdx.x, g0 = kPer * (kTopkThreads - 1 - tid);
   int sum = 0;
-#pragma unroll 8
-  for (int e = 0; e < per; ++e) sum += (int)h[g0 + ((e + tid) & (per - 1))];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) sum += (int)h[g0 + ((e + tid) & (kPer - 1))];
   int total;
-  const int above = scan256(sum, s_w, &total);
+  const int above = scan_wg(sum, s_w, &total);
   if (above < need && above + sum >= need) {
     int acc = above;
-    for (int e = per - 1; e >= 0; --e) {
+    for (int e = kPer - 1; e >= 0; --e) {
       const int c = (int)h[g0 + e];
       if (acc + c >= need) {
         s_found[0] = g0 + e;
@@ -212,230 +209,173 @@ __device__ __forceinline__ void find_bin(const uint32_t* h, int nb, int need, in
   __syncthreads();
 }
 
-// 2a. first-digit histogram of every score, summed over the workgroups of a sequence
-__global__ __launch_bounds__(256) void dsa_hist_kernel(DsaParams p) {
+__global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   __shared__ uint32_t h[kDsaBins];
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x / p.nchunk, ch = blockIdx.x - b * p.nchunk;
-  const int64_t L = p.seq_lens[b];
-  const int n = (int)(L < p.cap ? L : p.cap);
-  const int c0 = ch * kDsaChunk;
-  if (n <= p.topk || c0 >= n) return;  // workgroup-uniform
-  for (int i = tid; i < kDsaBins; i += 256) h[i] = 0u;
-  uint32_t key[16];
-  int nv;
-  load_keys16(p, b, c0, n, key, nv);
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 16; ++k)
-    if (k < nv) atomicAdd(&h[key[k] >> 19], 1u);
-  __syncthreads();
-  uint32_t* gh = p.hist + (size_t)b * kDsaBins;
-  for (int i = tid; i < kDsaBins; i += 256) {
-    const uint32_t c = h[i];
-    if (c) atomicAdd(gh + i, c);
-  }
-}
-
-// 2b. every workgroup finds the first digit's boundary bin, marks the positions
-// above it in the bitmap and writes the boundary bin's scores into its own slice
-// of the candidate list; the last workgroup of the sequence resolves the
-// candidates exactly (two more digits, ties to the lower position) and writes
-// the positions ascending.  Bitmap words, candidates and counts are stored with
-// agent-scope atomic stores and read with agent-scope atomic loads after the
-// arrival count (the workgroups of a sequence may sit on different XCDs, whose
-// L2s are not coherent for plain stores).
-constexpr int kCandLds = 4096;  // candidates the last workgroup holds in LDS
-constexpr int kCandPer = 4;     // candidate loads per thread in flight at once
-
-__global__ __launch_bounds__(256) void dsa_select_kernel(DsaParams p) {
-  __shared__ uint32_t h[kDsaBins];
-  __shared__ uint32_t s_bits[2 * kDsaMaxLen / 32];  // this chunk's words; later selected + tie words
-  __shared__ uint64_t s_cand[kCandLds];
-  __shared__ int s_w[4];
+  __shared__ uint32_t s_sb[kTopkWords], s_tb[kTopkWords];  // selected / tied positions
+  __shared__ uint32_t s_ck[kTopkCand], s_cp[kTopkCand];  // candidates: key, position
+  __shared__ int s_w[kTopkThreads / 64];
   __shared__ int s_found[2];
-  __shared__ int s_last, s_nc;
-  __shared__ uint32_t s_coff[kDsaMaxLen / kDsaChunk + 1];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int b = blockIdx.x / p.nchunk, ch = blockIdx.x - b * p.nchunk;
+  __shared__ int s_nc;
+  const int tid = threadIdx.x, b = blockIdx.x;
+  clk_stamp(p.clk, 0);
   const int64_t L = p.seq_lens[b];
   const int n = (int)(L < p.cap ? L : p.cap);
   int32_t* out = p.sel + (size_t)b * p.topk;
   if (n <= p.topk) {  // every past token
-    if (ch == 0)
-      for (int i = tid; i < p.topk; i += 256) out[i] = i < n ? i : -1;
+    for (int i = tid; i < p.topk; i += kTopkThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const int c0 = ch * kDsaChunk;
-  uint32_t* bits = p.bits + (size_t)b * p.nchunk * 128;
-  uint64_t* cand = p.cand + (size_t)b * p.cap;       // chunk ch writes entries [c0, c0 + its count)
-  uint32_t* ccount = p.cnt + (size_t)p.B * 4 + (size_t)b * p.nchunk;  // per-chunk candidate counts
-  uint32_t* arrive = p.cnt + 4 * b + 1;
-
-  // the first digit's histogram into LDS (eight 16-byte loads per thread, all in flight)
+  // key (q, e) of this thread is position 4*(tid + NT*q) + e: each load
+  // instruction of a wave reads 1 KB of consecutive scores
+  const float* sc = p.scores + (size_t)b * p.sstride;
+  const int last = (int)p.sstride - 4;
+  uint32_t key[kTopkLoads][4];
   {
-    const u32x4_t* gh = reinterpret_cast<const u32x4_t*>(p.hist + (size_t)b * kDsaBins);
-    u32x4_t v[kDsaBins / 4 / 256];
+    f32x4_t v[kTopkLoads];
 #pragma unroll
-    for (int q = 0; q < kDsaBins / 4 / 256; ++q) v[q] = gh[tid + 256 * q];
+    for (int q = 0; q < kTopkLoads; ++q) {
+      const int pos = 4 * (tid + kTopkThreads * q);
+      v[q] = 4 * kTopkThreads * q < n ? *reinterpret_cast<const f32x4_t*>(sc + (pos < last ? pos : last))
+                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
+    // Positions past n get key 0 and take no part: the first histogram adds 0
+    // for them, and every score's key is at least 2^19 (only NaNs with the sign
+    // bit set have smaller keys; they are raised to 2^19 and tie), so the
+    // boundary bin is never bin 0 and no later digit or comparison matches 0.
+    const int r = n - 4 * tid;  // key (q, e) exists iff 4*NT*q + e < r
 #pragma unroll
-    for (int q = 0; q < kDsaBins / 4 / 256; ++q) reinterpret_cast<u32x4_t*>(h)[tid + 256 * q] = v[q];
+    for (int q = 0; q < kTopkLoads; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        key[q][e] = max(order_key(v[q][e]), 1u << 19) & (uint32_t)((4 * kTopkThreads * q + e - r) >> 31);
+  }
+  __syncthreads();
+  clk_stamp(p.clk, 1);
+  // ---- first digit (top 13 bits) over every key, without branches: key 0 adds 0
+#pragma unroll
+  for (int q = 0; q < kTopkLoads; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(&h[key[q][e] >> 19], (uint32_t)(key[q][e] != 0u));
+#pragma unroll
+  for (int e = 0; e < kTopkWpt; ++e) {
+    s_sb[tid + kTopkThreads * e] = 0u;
+    s_tb[tid + kTopkThreads * e] = 0u;
   }
   if (tid == 0) s_nc = 0;
   __syncthreads();
-  find_bin(h, kDsaBins, p.topk, s_w, s_found);
+  find_bin(h, p.topk, s_w, s_found);
   const uint32_t T0 = (uint32_t)s_found[0];
-  const int above0 = s_found[1];
-  if (c0 < n) {
-    uint32_t key[16];
-    int nv;
-    load_keys16(p, b, c0, n, key, nv);
-    if (tid < 128) s_bits[tid] = 0u;
-    __syncthreads();
-    uint32_t w = 0u;  // this thread's 16 positions: half of bitmap word tid / 2
+  int need = p.topk - s_found[1];
+  const uint32_t in_bin = h[T0];  // keys in the boundary bin
+  __syncthreads();                // h and s_found are rewritten below
+  clk_stamp(p.clk, 2);
+  uint32_t prefix = T0 << 19;
+  if (in_bin <= (uint32_t)kTopkCand) {  // workgroup-uniform
+    // Keys above the boundary bin are selected; the bin's keys (with their
+    // positions) become the candidates, and the other two digits and the ties
+    // are found among them alone.
+    const uint32_t lim = prefix | 0x7FFFFu;  // the bin's largest key
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t bin = key[k] >> 19;
-      const bool valid = k < nv;
-      if (valid && bin > T0) w |= 1u << (16 * (tid & 1) + k);
-      const bool cd = valid && bin == T0;
-      const uint64_t m = __ballot(cd);
-      if (m != 0ull) {  // wave-aggregated slot in this chunk's slice
-        const int first = __builtin_ctzll(m);
-        int slot0 = 0;
-        if (lane == first) slot0 = atomicAdd(&s_nc, __popcll(m));
-        slot0 = __shfl(slot0, first);
-        if (cd) {
-          const int slot = slot0 + __popcll(m & ((1ull << lane) - 1ull));
-          __hip_atomic_store(cand + c0 + slot, ((uint64_t)key[k] << 32) | (uint32_t)(c0 + 16 * tid + k),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    for (int q = 0; q < kTopkLoads; ++q) {
+      const uint32_t* k = key[q];
+      uint32_t ns = 0u, nb = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ns |= k[e] > lim ? 1u << e : 0u;
+        nb |= k[e] - prefix <= 0x7FFFFu ? 1u << e : 0u;
+      }
+      const int word = (kTopkThreads * q + tid) >> 3, sh = 4 * (tid & 7);
+      if (ns) atomicOr(&s_sb[word], ns << sh);
+      if (nb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((nb >> e) & 1u) {
+            const int slot = atomicAdd(&s_nc, 1);
+            s_ck[slot] = k[e];
+            s_cp[slot] = 4 * (tid + kTopkThreads * q) + e;
+          }
       }
     }
-    atomicOr(&s_bits[tid >> 1], w);
+    for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
     __syncthreads();
-    if (tid < 128) __hip_atomic_store(bits + ch * 128 + tid, s_bits[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (tid == 0) __hip_atomic_store(ccount + ch, (uint32_t)s_nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // Hand-off to the last workgroup of the sequence without a release / acquire
-  // pair: the candidates, bitmap words and counts above are agent-scope atomic
-  // stores, which the hardware writes through to the device-coherent level
-  // (sc1); each thread waits until its stores are acknowledged (asm with a
-  // memory clobber, so the compiler keeps them before it) and only then is the
-  // arrival counter incremented; the last workgroup issues its agent-scope
-  // atomic loads (sc1, past the non-coherent caches) only after the counter's
-  // value has returned.  A release / acquire fence pair would write back and
-  // invalidate the whole L2 of the XCD for every workgroup.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(p.nchunk - 1);
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---- last workgroup.  Candidate offsets per chunk, then every candidate and
-  // bitmap word loaded in one round trip.
-  if (tid < p.nchunk) s_coff[tid + 1] = __hip_atomic_load(ccount + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (tid == 0) {  // counts -> offsets (at most 16 chunks)
-    uint32_t acc = 0u;
-    s_coff[0] = 0u;
-    for (int c = 1; c <= p.nchunk; ++c) {
-      acc += s_coff[c];
-      s_coff[c] = acc;
-    }
-  }
-  __syncthreads();
-  const int nc = (int)s_coff[p.nchunk];
-  const bool in_lds = nc <= kCandLds;
-  // candidate e lives in chunk c (s_coff[c] <= e < s_coff[c+1]) at slot e - s_coff[c]
-  auto cand_at = [&](int e) -> const uint64_t* {
-    int c = 0;
-    while (c + 1 < p.nchunk && (int)s_coff[c + 1] <= e) ++c;
-    return cand + c * kDsaChunk + (e - (int)s_coff[c]);
-  };
-  if (in_lds) {  // chunk c's slice is copied by threads 16c .. 16c + 15, four loads in flight each
-    const int c = tid >> 4, j = tid & 15;
-    if (c < p.nchunk) {
-      const int cnt_c = (int)(s_coff[c + 1] - s_coff[c]), off = (int)s_coff[c];
-      for (int i0 = j; i0 < cnt_c; i0 += 16 * kCandPer) {
-        uint64_t v[kCandPer];
-#pragma unroll
-        for (int u = 0; u < kCandPer; ++u) {
-          const int i = i0 + 16 * u;
-          v[u] = i < cnt_c ? __hip_atomic_load(cand + c * kDsaChunk + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           : 0ull;
-        }
-#pragma unroll
-        for (int u = 0; u < kCandPer; ++u)
-          if (i0 + 16 * u < cnt_c) s_cand[off + i0 + 16 * u] = v[u];
+    const int nc = s_nc;
+    // second digit (13 bits) and third (6 bits), among the candidates
+#pragma unroll 1
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = pass == 1 ? 6 : 0;
+      const uint32_t dmask = pass == 1 ? 0x1FFFu : 0x3Fu, pmask = pass == 1 ? 0xFFF80000u : 0xFFFFFFC0u;
+      for (int i = tid; i < nc; i += kTopkThreads) {
+        const uint32_t k = s_ck[i];
+        if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
       }
+      __syncthreads();
+      find_bin(h, need, s_w, s_found);
+      prefix |= (uint32_t)s_found[0] << shift;
+      need -= s_found[1];
+      for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
+      __syncthreads();
+      clk_stamp(p.clk, 2 + pass);
     }
-  }
-  auto cand_get = [&](int e) -> uint64_t {
-    return in_lds ? s_cand[e] : __hip_atomic_load(cand_at(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  int need = p.topk - above0;
-  uint32_t prefix = T0 << 19, pmask = 0xFFF80000u;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 6 : 0;
-    const uint32_t dmask = pass == 0 ? 0x1FFFu : 0x3Fu;
-    __syncthreads();
-    for (int i = tid; i < kDsaBins; i += 256) h[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < nc; i += 256) {
-      const uint32_t k = (uint32_t)(cand_get(i) >> 32);
-      if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
+    for (int i = tid; i < nc; i += kTopkThreads) {
+      const uint32_t k = s_ck[i], pos = s_cp[i];
+      if (k > prefix) atomicOr(&s_sb[pos >> 5], 1u << (pos & 31));
+      else if (k == prefix) atomicOr(&s_tb[pos >> 5], 1u << (pos & 31));
     }
+  } else {
+    // more keys in the boundary bin than the candidate list holds (many equal
+    // or nearly equal scores): the other digits over every key in registers
+    for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
     __syncthreads();
-    find_bin(h, pass == 0 ? kDsaBins : 256, need, s_w, s_found);
-    prefix |= (uint32_t)s_found[0] << shift;
-    pmask |= dmask << shift;
-    need -= s_found[1];
-    __syncthreads();
-  }
-  // prefix is the k-th largest key: keys above it are in; `need` ties at it go to
-  // the lowest positions
-  const int nw = (n + 31) / 32;
-  constexpr int WPT = kDsaMaxLen / 32 / 256;
-  uint32_t* sb = s_bits;
-  uint32_t* tb = s_bits + kDsaMaxLen / 32;
-  {
-    uint32_t v[WPT];
+#pragma unroll 1
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = pass == 1 ? 6 : 0;
+      const uint32_t dmask = pass == 1 ? 0x1FFFu : 0x3Fu, pmask = pass == 1 ? 0xFFF80000u : 0xFFFFFFC0u;
 #pragma unroll
-    for (int e = 0; e < WPT; ++e) {
-      const int i = tid + 256 * e;
-      v[e] = i < nw ? __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      for (int q = 0; q < kTopkLoads; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((key[q][e] & pmask) == prefix) atomicAdd(&h[(key[q][e] >> shift) & dmask], 1u);
+      __syncthreads();
+      find_bin(h, need, s_w, s_found);
+      prefix |= (uint32_t)s_found[0] << shift;
+      need -= s_found[1];
+      for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
+      __syncthreads();
+      clk_stamp(p.clk, 2 + pass);
     }
 #pragma unroll
-    for (int e = 0; e < WPT; ++e) {
-      sb[tid + 256 * e] = v[e];
-      tb[tid + 256 * e] = 0u;
+    for (int q = 0; q < kTopkLoads; ++q) {
+      uint32_t ns = 0u, nt = 0u;  // the four positions' bits
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ns |= key[q][e] > prefix ? 1u << e : 0u;
+        nt |= key[q][e] == prefix ? 1u << e : 0u;
+      }
+      const int word = (kTopkThreads * q + tid) >> 3, sh = 4 * (tid & 7);
+      if (ns) atomicOr(&s_sb[word], ns << sh);
+      if (nt) atomicOr(&s_tb[word], nt << sh);
     }
   }
+  // prefix is the k-th largest key: the keys above it are marked in s_sb, and
+  // `need` of the keys equal to it (s_tb) are taken, the lowest positions first
   __syncthreads();
-  for (int i = tid; i < nc; i += 256) {
-    const uint64_t e = cand_get(i);
-    const uint32_t k = (uint32_t)(e >> 32), pos = (uint32_t)e;
-    if (k > prefix) atomicOr(&sb[pos >> 5], 1u << (pos & 31));
-    else if (k == prefix) atomicOr(&tb[pos >> 5], 1u << (pos & 31));
-  }
-  __syncthreads();
-  // thread t owns words [WPT*t, WPT*t + WPT): ties taken in position order, then
-  // the selected positions written ascending
-  const int w0 = WPT * tid;
+  clk_stamp(p.clk, 5);
+  // thread t owns words [kTopkWpt*t, +kTopkWpt): ties taken in position order,
+  // then the selected positions written ascending
+  const int nw = (n + 31) / 32, w0 = kTopkWpt * tid;
   int ties = 0;
 #pragma unroll
-  for (int e = 0; e < WPT; ++e) ties += w0 + e < nw ? __popc(tb[w0 + e]) : 0;
+  for (int e = 0; e < kTopkWpt; ++e) ties += w0 + e < nw ? __popc(s_tb[w0 + e]) : 0;
   int total;
-  int tb0 = scan256(ties, s_w, &total);
+  const int tb0 = scan_wg(ties, s_w, &total);
   int take = need - tb0;
   take = take < 0 ? 0 : (take > ties ? ties : take);
   int cntsel = 0;
-  uint32_t word[WPT];
+  uint32_t word[kTopkWpt];
 #pragma unroll
-  for (int e = 0; e < WPT; ++e) {
-    uint32_t s_ = w0 + e < nw ? sb[w0 + e] : 0u, t_ = w0 + e < nw ? tb[w0 + e] : 0u;
+  for (int e = 0; e < kTopkWpt; ++e) {
+    uint32_t s_ = w0 + e < nw ? s_sb[w0 + e] : 0u, t_ = w0 + e < nw ? s_tb[w0 + e] : 0u;
     while (t_ != 0u && take > 0) {  // lowest tie positions first
       const uint32_t low = t_ & (~t_ + 1u);
       s_ |= low;
@@ -445,9 +385,9 @@ __global__ __launch_bounds__(256) void dsa_select_kernel(DsaParams p) {
     word[e] = s_;
     cntsel += __popc(s_);
   }
-  int o = scan256(cntsel, s_w, &total);
+  int o = scan_wg(cntsel, s_w, &total);
 #pragma unroll
-  for (int e = 0; e < WPT; ++e) {
+  for (int e = 0; e < kTopkWpt; ++e) {
     uint32_t s_ = word[e];
     while (s_ != 0u) {
       const int bit = __builtin_ctz(s_);
@@ -455,6 +395,7 @@ __global__ __launch_bounds__(256) void dsa_select_kernel(DsaParams p) {
       if (o < p.topk) out[o++] = 32 * (w0 + e) + bit;
     }
   }
+  clk_stamp(p.clk, 6);
 }
 
 // ---------------------------------------------------------------------------
@@ -478,6 +419,8 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
   const int ngrp = p.H / HPG, per_b = ngrp * p.ts;
   const int b = blockIdx.x / per_b, r = blockIdx.x - b * per_b;
   const int hg = r / p.ts, sp = r - hg * p.ts;
+  uint64_t* clk = p.clk ? p.clk + (size_t)kClkMaxGroups * kClkSlots : nullptr;
+  clk_stamp(clk, 0);
   const int64_t L = p.seq_lens[b];
   const int n = (int)(L < p.cap ? L : p.cap);
   const int nsel = n < p.topk ? n : p.topk;
@@ -505,6 +448,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
     for (int ks = 0; ks < kKt; ++ks) qf[ks] = ld16(qrow + 32 * ks);
   }
   __syncthreads();
+  clk_stamp(clk, 1);
   // Fragment f = m*18 + ks holds the 16-byte chunks (dims 32*ks + 8*g .. of row
   // 16*m + R) for g < 4, R < 16 in the 64 slots of 1 KB, chunk (g, R) at slot
   // swz(g, R, ks) = (16*g + R) ^ ((2*g + ks) & 7): the S^T reads (lane (g, R))
@@ -541,6 +485,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
     else if (ahead == 1) wait_vmem_le<NCP>();
     else wait_vmem();
     lds_barrier();
+    if (it == 0) clk_stamp(clk, 2);
     const char* kt = s_buf[it % kNbuf];
     // S^T for the tile's 32 tokens (row groups 0 and 1) and this wave's 16 heads
     f32x4_t s[2];
@@ -600,6 +545,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
     }
     lds_barrier();  // every wave is done with this buffer before it is refilled
   }
+  clk_stamp(clk, 3);
   lsum = sum_over_groups_swap(lsum);
   // this wave's 16 heads: (m, l, O / l) to the partial
   float* dst = part + (size_t)(16 * wave + lr) * kPartStride;
@@ -618,6 +564,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
           u32x4_t{pack_f16x2(a[0][i] * inv, a[1][i] * inv), pack_f16x2(a[2][i] * inv, a[3][i] * inv),
                   pack_f16x2(a[4][i] * inv, a[5][i] * inv), pack_f16x2(a[6][i] * inv, a[7][i] * inv)};
     }
+  clk_stamp(clk, 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -669,8 +616,7 @@ hipError_t launch_dsa_t(const DsaParams& p, hipStream_t s, const PhaseEvents* ev
   if (ev) (void)hipEventRecord(ev->ev[0], s);
   hipLaunchKernelGGL((dsa_index_kernel<HI, DI>), dim3((unsigned)(p.B * p.nseg)), dim3(256), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[1], s);
-  hipLaunchKernelGGL(dsa_hist_kernel, dim3((unsigned)(p.B * p.nchunk)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(dsa_select_kernel, dim3((unsigned)(p.B * p.nchunk)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(dsa_topk_kernel, dim3((unsigned)p.B), dim3(kTopkThreads), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[2], s);
   if (p.hpg == 64)
     hipLaunchKernelGGL((dsa_attn_kernel<4>), dim3((unsigned)(p.B * (p.H / 64) * p.ts)), dim3(256), 0, s, p);

@@ -29,7 +29,7 @@ constexpr int kFinWaves = 4;         // waves per decode selection workgroup
 constexpr int kMaxWindow = 16;       // decode window workgroups per (sequence, group)
 
 // Profiling hook: with a phase-clock buffer, thread 0 of every workgroup of the
-// decode kernels records the 100 MHz constant clock at kClkSlots numbered
+// decode kernels (and of the DSA top-k and attention kernels) records the 100 MHz constant clock at kClkSlots numbered
 // points; kernel k's workgroup w uses entries [(k*kClkMaxGroups + w)*kClkSlots, +kClkSlots).
 constexpr int kClkSlots = 16;
 constexpr int kClkMaxGroups = 4096;
@@ -140,8 +140,7 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // DeepSeek Sparse Attention decode step (lightning indexer + token top-k +
 // MQA attention over one shared latent per token).
 constexpr int kDsaDqk = 576, kDsaDv = 512, kDsaMaxLen = 65536, kDsaMaxTopk = 4096;
-constexpr int kDsaChunk = 4096;     // scores per selection workgroup (256 threads x 16)
-constexpr int kDsaBins = 8192;      // first radix digit: the top 13 bits of a score's order key
+constexpr int kDsaBins = 8192;      // radix digits of the top-k: 13, 13 and 6 bits of a score's order key
 struct DsaParams {
   int B, H, HI, DI, topk;
   float scale_log2;
@@ -157,15 +156,11 @@ struct DsaParams {
   int64_t sstride;                   // cap rounded up to a multiple of 4
   int32_t* sel;                      // [B, topk] (caller's or workspace), ascending, -1 padded
   float* part;                       // workspace [B, H/hpg, ts, hpg, 264]: m, l, pad, 512 fp16 outputs / l
-  uint32_t* hist;                    // workspace [B, kDsaBins] (zeroed by the indexer kernel)
-  uint32_t* cnt;                     // workspace [B, 4] (arrivals; zeroed likewise), then [B, nchunk] counts
-  uint32_t* bits;                    // workspace [B, nchunk * 128]: selected-position bitmap
-  uint64_t* cand;                    // workspace [B, cap]: (key << 32 | position) of boundary-bin scores
-  int nchunk;                        // selection workgroups per sequence: ceil(cap / kDsaChunk)
   int seg;                           // indexer tokens per workgroup (multiple of 512)
   int nseg;                          // indexer workgroups per sequence
   int ts;                            // attention token splits per (sequence, head group)
   int hpg;                           // heads per attention workgroup: 64, or 32 when H % 64 != 0
+  uint64_t* clk;                     // phase clock (null = off): top-k kernel, then attention kernel
 };
 
 DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, int nloc, int w, int64_t max_len);

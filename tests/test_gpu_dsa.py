@@ -116,6 +116,33 @@ def test_dsa_equal_scores_take_the_lowest_positions():
     check_dsa(case, out, sel, scores)
 
 
+def test_dsa_few_distinct_scores():
+    """Three distinct indexer keys repeated along a 20k sequence: thousands of equal
+    scores share the boundary bin (more than the selection keeps on chip), so the
+    threshold is found over every score and the ties go to the lowest positions."""
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=20000, ragged_min=15000, num_heads=32,
+                                         needles=0), 56)
+    for b in range(2):
+        case.k_idx[b] = case.k_idx[b, np.arange(case.k_idx.shape[1]) % 3]
+    out, sel, scores, _ = run_dsa(case)
+    check_dsa(case, out, sel, scores)
+
+
+def test_dsa_scores_sorted_along_the_sequence():
+    """Indexer keys permuted so that the scores fall along the sequence: the top-k
+    are the first positions, away from the rows the selection samples to bound the
+    k-th score, so the bound misses and the select runs over every score."""
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=30000, num_heads=32, needles=0), 57)
+    for b in range(2):
+        L = int(case.seq_lens[b])
+        qI = D.fp8_e4m3_to_float(case.q_idx[b])
+        kI = D.fp8_e4m3_to_float(case.k_idx[b, :L])
+        score = np.maximum(kI @ qI.T, 0.0) @ np.asarray(case.w_idx[b], np.float64)
+        case.k_idx[b, :L] = case.k_idx[b, np.argsort(-score, kind="stable")]
+    out, sel, scores, _ = run_dsa(case)
+    check_dsa(case, out, sel, scores)
+
+
 def test_dsa_repeat_is_bitwise_identical():
     case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=7000, num_heads=64, needles=8), 55)
     _, _, _, outs = run_dsa(case, repeat=2)
