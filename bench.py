@@ -290,7 +290,8 @@ K2_PHASES = {0: "start", 1: "loads_arrived", 2: "scores_ready", 3: "topn_done", 
              5: "partials_stored", 6: "merge_start", 7: "out_written"}
 
 
-DSA_K0_PHASES = {0: "start", 1: "loaded", 2: "digit1", 3: "digit2", 4: "digit3", 5: "bitmaps", 6: "written"}
+DSA_K0_PHASES = {0: "start", 1: "bound", 2: "arrived", 3: "candidates_loaded", 4: "bitmaps", 5: "written",
+                 6: "written_full_select"}
 DSA_K1_PHASES = {0: "start", 1: "rows_loaded", 2: "first_tile", 3: "tiles_done", 4: "stored"}
 
 

@@ -283,7 +283,8 @@ nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float
                                 void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes for nsa_dsa_decode_fwd (host-only): fp32 scores [B, cache_len]
  * (row stride cache_len rounded up to 4, at offset 0), a selection buffer
- * [B, top_k] and the attention partials.  Its contents on entry do not matter. */
+ * [B, top_k], the attention partials, and the top-k's counters, position
+ * bitmap and candidate list.  Its contents on entry do not matter. */
 nsa_status_t nsa_dsa_decode_workspace_size(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_len,
                                            size_t* bytes);
 
@@ -427,10 +428,12 @@ nsa_status_t nsa_set_phase_events(void* const* events, int32_t count);
  *            stored, 6 (last workgroup of a (sequence, group) only) merge
  *            begins, 7 output written;
  * and of the DSA step:
- *   kernel 0 (top-k, one workgroup per sequence): 0 start, 1 scores loaded,
- *            2, 3, 4 first, second and third radix digit found, 5 position
- *            bitmaps built, 6 positions written (1..6 only when the sequence
- *            has more than top_k positions);
+ *   kernel 0 (top-k, one workgroup per 4096-score chunk): 0 start,
+ *            1 sampled bound found, 2 chunk counted and arrived; the last
+ *            workgroup of a sequence: 3 candidates loaded (bounded path),
+ *            4 position bitmaps built, 5 positions written (bounded path) or
+ *            6 (select over every score); 1..6 only when the sequence has more
+ *            than top_k positions;
  *   kernel 1 (attention): 0 start, 1 positions and queries loaded, 2 first
  *            tile staged, 3 every tile done, 4 partial stored.
  * Entries of workgroups that end early are not written.  Nothing is recorded

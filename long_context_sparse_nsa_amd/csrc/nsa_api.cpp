@@ -177,9 +177,9 @@ nsa_status_t check_dsa(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cache_
 }
 
 struct DsaPlan {
-  int seg, nseg, ts, hpg;
+  int seg, nseg, ts, hpg, nchunk;
   int64_t sstride;
-  size_t off_scores, off_sel, off_part, total;
+  size_t off_scores, off_sel, off_part, off_cnt, off_bits, off_cand, total;
 };
 DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   DsaPlan pl{};
@@ -202,7 +202,11 @@ DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   pl.off_scores = 0;
   pl.off_sel = align256((size_t)B * pl.sstride * 4);
   pl.off_part = pl.off_sel + align256((size_t)B * top_k * 4);
-  pl.total = pl.off_part + align256((size_t)B * ngrp * ts * hpg * (8 + 256) * 4);
+  pl.nchunk = (int)((cap + nsa::kDsaChunk - 1) / nsa::kDsaChunk);
+  pl.off_cnt = pl.off_part + align256((size_t)B * ngrp * ts * hpg * (8 + 256) * 4);
+  pl.off_bits = pl.off_cnt + align256((size_t)B * (4 + 2 * pl.nchunk) * 4);
+  pl.off_cand = pl.off_bits + align256((size_t)B * pl.nchunk * (nsa::kDsaChunk / 32) * 4);
+  pl.total = pl.off_cand + align256((size_t)B * pl.nchunk * nsa::kDsaChunk * 8);
   return pl;
 }
 
@@ -534,7 +538,13 @@ nsa_status_t nsa_dsa_decode_fwd(const nsa_dsa_dims_t* dims, int32_t top_k, float
   p.nseg = plan.nseg;
   p.ts = plan.ts;
   p.hpg = plan.hpg;
-  if (g_clk && (int64_t)p.B * (p.H / p.hpg) * p.ts <= nsa::kClkMaxGroups) p.clk = g_clk;
+  p.nchunk = plan.nchunk;
+  p.cnt = reinterpret_cast<uint32_t*>(ws + plan.off_cnt);
+  p.bits = reinterpret_cast<uint32_t*>(ws + plan.off_bits);
+  p.cand = reinterpret_cast<uint64_t*>(ws + plan.off_cand);
+  if (g_clk && (int64_t)p.B * (p.H / p.hpg) * p.ts <= nsa::kClkMaxGroups &&
+      (int64_t)p.B * p.nchunk <= nsa::kClkMaxGroups)
+    p.clk = g_clk;
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_dsa_decode(p, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "DSA decode launch");

@@ -15,10 +15,12 @@
 //     ReLU, the weighted head sum, and writes fp32 scores.  Tile loads run a
 //     batch of eight tiles ahead of the compute.
 //  2. dsa_topk_kernel    exact top-k by radix select on order-preserving integer
-//     keys of the scores, one 1024-thread workgroup per sequence holding all of
-//     its scores in registers: three digit histograms in LDS (13, 13 and 6 bits)
-//     find the k-th largest key, ties at it go to the lowest positions, and the
-//     positions are written ascending from a bitmap in LDS.
+//     keys of the scores, one workgroup per 4096-score chunk: a sampled
+//     histogram bounds the k-th key between two bins, each chunk marks its keys
+//     above the bound and lists those within it, and the last workgroup of the
+//     sequence finds the k-th key among the listed ones (or, when the bound did
+//     not hold, over every score), takes ties at it from the lowest positions
+//     and writes the positions ascending.
 //  3. dsa_attn_kernel    workgroup = (sequence, 64 heads -- 32 when the head
 //     count is not a multiple of 64 --, token split); 32-token tiles of latents
 //     are gathered into LDS with the direct global->LDS copy, four buffers
@@ -63,6 +65,7 @@ __global__ __launch_bounds__(256) void dsa_index_kernel(DsaParams p) {
   constexpr int RT = HI / 16, KS = DI / 32, BPL = DI / 4, LV = BPL / 16, NT = 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int b = blockIdx.x / p.nseg, sg = blockIdx.x - b * p.nseg;
+  if (sg == 0 && tid < 4) p.cnt[4 * b + tid] = 0u;  // the top-k launch's arrival counters
   const int64_t L = p.seq_lens[b];
   const int64_t n = L < p.cap ? L : p.cap;
   const int64_t s0 = (int64_t)sg * p.seg;
@@ -132,34 +135,51 @@ __global__ __launch_bounds__(256) void dsa_index_kernel(DsaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. exact top-k of the scores: one workgroup of 1024 threads per sequence
+// 2. exact top-k of the scores: 4096-score chunks, one 256-thread workgroup each
 //
 // Radix select on order-preserving integer keys (a larger float gives a larger
-// key), three digits of 13, 13 and 6 bits: each digit's histogram in LDS finds
-// the bin that holds the k-th largest key among the keys that match the digits
-// found so far.  Keys above the final threshold are taken, and the remaining
-// picks come from the keys equal to it, lowest positions first.  Every score of
-// the sequence stays in registers from the single load to the output, and no
-// other workgroup takes part, so there is no hand-off between workgroups.  The
-// workgroup's time goes to instructions per key (a 64-wide instruction takes
-// four cycles of a 16-lane SIMD), so only the first digit's histogram and one
-// classification visit every key: the boundary bin's keys are copied to a
-// candidate list in LDS, and the later digits and the ties are found there.
+// key), in three steps that keep every workgroup's work per key small:
+//  - bound: every workgroup of a sequence builds the same histogram of the first
+//    digit (top 13 bits) over a fixed sample of the sequence's scores (16
+//    evenly spaced runs of 256) and takes the bins of two sample ranks around
+//    the expected rank of the k-th key, a margin of four standard deviations
+//    and 16 apart: lo is the lower bin's first key, hi the upper bin's last;
+//  - chunk pass: each workgroup marks its keys above hi in the position bitmap,
+//    copies its keys in [lo, hi] with their positions to its slice of the
+//    candidate list, and stores both counts (agent-scope stores);
+//  - the last workgroup of the sequence (an arrival counter, zeroed by the
+//    indexer launch) checks that the bound held -- fewer than k keys above hi,
+//    at least k above or at lo, and the candidates fit in LDS -- and finds the
+//    k-th key among the candidates (digits of the key relative to lo, 13 bits
+//    at a time); keys above it are taken, and the rest from the keys equal to
+//    it, lowest positions first; the positions are written ascending from the
+//    bitmap.  When the bound did not hold, that workgroup runs the select over
+//    every score of the sequence instead (three digit histograms, 13, 13 and
+//    6 bits), which is slower but exact.
+// Coherence across XCDs as in the decode selection: agent-scope atomic stores
+// and loads, the writers wait for their stores before the arrival increment.
 
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkLoads = kDsaMaxLen / (4 * kTopkThreads);  // four-score loads per thread
-constexpr int kTopkWords = kDsaMaxLen / 32;                  // bitmap words per sequence
-constexpr int kTopkWpt = kTopkWords / kTopkThreads;          // bitmap words per thread
-constexpr int kTopkCand = 4096;                              // boundary-bin keys held in LDS
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkPer = kDsaChunk / kTopkThreads;         // keys per thread in a chunk (4)
+constexpr int kTopkRun = 256;                              // sample run length
+constexpr int kTopkRuns = 16;                              // sample runs
+constexpr int kTopkSamples = kTopkRun * kTopkRuns / kTopkThreads;  // sampled keys per thread (4)
+constexpr int kTopkCandLds = 4096;                         // candidates the last workgroup holds
+constexpr int kTopkWpt = kDsaMaxLen / 32 / kTopkThreads;   // bitmap words per thread at the end
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // larger float -> larger key
 }
 
+// Every score's key is raised to at least 2^19 (only NaNs with the sign bit set
+// have smaller keys; they tie there), so bin 0 holds no key and key 0 can stand
+// for "no key".
+__device__ __forceinline__ uint32_t score_key(float f) { return max(order_key(f), 1u << 19); }
+
 // Exclusive prefix over the workgroup's threads; *total gets the sum.
 __device__ __forceinline__ int scan_wg(int v, int* s_w, int* total) {
-  constexpr int NW = kTopkThreads / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -171,7 +191,7 @@ __device__ __forceinline__ int scan_wg(int v, int* s_w, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < kTopkWaves; ++w) {
     const int s = s_w[w];
     base += w < wave ? s : 0;
     tot += s;
@@ -181,191 +201,293 @@ __device__ __forceinline__ int scan_wg(int v, int* s_w, int* total) {
   return base + x - v;
 }
 
-// In the kDsaBins-bin histogram h, the bin holding the need-th largest key and
-// the count of keys in higher bins, to s_found[0..1].  Thread t sums bins
-// [kPer*(NT-1-t), +kPer) (thread 0 the highest), starting at a rotated bin so
-// that the lanes of a wave read different LDS banks; only the thread whose bins
-// hold the boundary walks them in order.
-__device__ __forceinline__ void find_bin(const uint32_t* h, int need, int* s_w, int* s_found) {
+// In the kDsaBins-bin histogram h, the bins holding the ra-th and rb-th largest
+// keys (ranks from 1) to s_out[0] and s_out[2], the counts of keys in higher
+// bins to s_out[1] and s_out[3].  With `sampled` the ranks come from the
+// histogram's total instead: the expected rank of the k-th key of n among the
+// sample, minus and plus four standard deviations and 16, clamped to
+// [1, total]; s_out[4] gets the total.  Thread t sums bins [kPer*(NT-1-t),
+// +kPer) (thread 0 the highest) from a rotated start, so that the lanes of a
+// wave read different LDS banks; only threads whose bins hold a rank walk them.
+__device__ __forceinline__ void find_bins(const uint32_t* h, int ra, int rb, bool sampled, int k, int n, int* s_w,
+                                          int* s_out) {
   constexpr int kPer = kDsaBins / kTopkThreads;
   const int tid = (int)threadIdx.x, g0 = kPer * (kTopkThreads - 1 - tid);
   int sum = 0;
-#pragma unroll
   for (int e = 0; e < kPer; ++e) sum += (int)h[g0 + ((e + tid) & (kPer - 1))];
   int total;
   const int above = scan_wg(sum, s_w, &total);
-  if (above < need && above + sum >= need) {
-    int acc = above;
-    for (int e = kPer - 1; e >= 0; --e) {
-      const int c = (int)h[g0 + e];
-      if (acc + c >= need) {
-        s_found[0] = g0 + e;
-        s_found[1] = acc;
-        break;
+  if (sampled) {  // a heuristic bound (the result does not depend on it)
+    const float kp = (float)k * (float)total * __builtin_amdgcn_rcpf((float)n);
+    const float d = 4.f * __builtin_amdgcn_sqrtf(kp) + 16.f;
+    ra = max(1, (int)(kp - d));
+    rb = min(total, (int)(kp + d) + 1);
+    if (tid == 0) s_out[4] = total;
+  }
+  for (int j = 0; j < 2; ++j) {
+    const int need = j == 0 ? ra : rb;
+    if (above < need && above + sum >= need) {  // one thread: its bins read at once, then walked
+      uint32_t hv[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) hv[e] = h[g0 + e];
+      int acc = above, bin = g0, acc_at = above;
+      bool found = false;
+#pragma unroll
+      for (int e = kPer - 1; e >= 0; --e) {
+        if (!found && acc + (int)hv[e] >= need) {
+          found = true;
+          bin = g0 + e;
+          acc_at = acc;
+        }
+        acc += (int)hv[e];
       }
-      acc += c;
+      s_out[2 * j] = bin;
+      s_out[2 * j + 1] = acc_at;
     }
   }
   __syncthreads();
 }
 
+__device__ __forceinline__ void zero_hist(uint32_t* h) {
+  for (int i = threadIdx.x; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
+}
+
 __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   __shared__ uint32_t h[kDsaBins];
-  __shared__ uint32_t s_sb[kTopkWords], s_tb[kTopkWords];  // selected / tied positions
-  __shared__ uint32_t s_ck[kTopkCand], s_cp[kTopkCand];  // candidates: key, position
-  __shared__ int s_w[kTopkThreads / 64];
-  __shared__ int s_found[2];
-  __shared__ int s_nc;
-  const int tid = threadIdx.x, b = blockIdx.x;
+  __shared__ uint32_t s_sb[kDsaMaxLen / 32], s_tb[kDsaMaxLen / 32];  // selected / tied positions
+  __shared__ uint64_t s_cand[kTopkCandLds];                          // (key << 32) | position
+  __shared__ int s_w[kTopkWaves];
+  __shared__ int s_out[5];
+  __shared__ uint32_t s_coff[kDsaMaxLen / kDsaChunk + 1];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int b = blockIdx.x / p.nchunk, ch = blockIdx.x - b * p.nchunk;
   clk_stamp(p.clk, 0);
   const int64_t L = p.seq_lens[b];
   const int n = (int)(L < p.cap ? L : p.cap);
-  int32_t* out = p.sel + (size_t)b * p.topk;
-  if (n <= p.topk) {  // every past token
-    for (int i = tid; i < p.topk; i += kTopkThreads) out[i] = i < n ? i : -1;
+  const int k = p.topk;
+  int32_t* out = p.sel + (size_t)b * k;
+  if (n <= k) {  // every past token
+    if (ch == 0)
+      for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
     return;
   }
-  // key (q, e) of this thread is position 4*(tid + NT*q) + e: each load
-  // instruction of a wave reads 1 KB of consecutive scores
   const float* sc = p.scores + (size_t)b * p.sstride;
+  const int c0 = ch * kDsaChunk;
+  uint32_t* bits = p.bits + (size_t)b * p.nchunk * (kDsaChunk / 32);
+  uint64_t* cand = p.cand + (size_t)b * p.nchunk * kDsaChunk;  // chunk ch: entries [c0, c0 + its count)
+  uint32_t* counts = p.cnt + (size_t)p.B * 4 + (size_t)b * p.nchunk * 2;  // per chunk: above, candidates
+  uint32_t* arrive = p.cnt + 4 * b;
+
+  // ---- loads, all issued at once: the sample (run r starts at r*n/16; sample
+  // s = t + NT*j is score s % 256 of run s / 256) and this chunk (key (i, e) is
+  // position c0 + 4*(t + NT*i) + e: 1 KB of consecutive scores per wave and load)
+  float sv[kTopkSamples];
+#pragma unroll
+  for (int j = 0; j < kTopkSamples; ++j) {
+    const int s = tid + kTopkThreads * j, run = s / kTopkRun;
+    const int pos = (int)(((int64_t)run * n) / kTopkRuns) + (s - run * kTopkRun);
+    sv[j] = sc[pos < n ? pos : n - 1];
+  }
+  f32x4_t cv[kTopkPer / 4];
   const int last = (int)p.sstride - 4;
-  uint32_t key[kTopkLoads][4];
-  {
-    f32x4_t v[kTopkLoads];
 #pragma unroll
-    for (int q = 0; q < kTopkLoads; ++q) {
-      const int pos = 4 * (tid + kTopkThreads * q);
-      v[q] = 4 * kTopkThreads * q < n ? *reinterpret_cast<const f32x4_t*>(sc + (pos < last ? pos : last))
-                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
-    // Positions past n get key 0 and take no part: the first histogram adds 0
-    // for them, and every score's key is at least 2^19 (only NaNs with the sign
-    // bit set have smaller keys; they are raised to 2^19 and tie), so the
-    // boundary bin is never bin 0 and no later digit or comparison matches 0.
-    const int r = n - 4 * tid;  // key (q, e) exists iff 4*NT*q + e < r
-#pragma unroll
-    for (int q = 0; q < kTopkLoads; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        key[q][e] = max(order_key(v[q][e]), 1u << 19) & (uint32_t)((4 * kTopkThreads * q + e - r) >> 31);
+  for (int i = 0; i < kTopkPer / 4; ++i) {
+    const int pos = c0 + 4 * (tid + kTopkThreads * i);
+    cv[i] = c0 < n ? *reinterpret_cast<const f32x4_t*>(sc + (pos < last ? pos : last)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  zero_hist(h);
+  if (tid < kDsaChunk / 32) s_sb[tid] = 0u;
   __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kTopkSamples; ++j) atomicAdd(&h[score_key(sv[j]) >> 19], 1u);
+  __syncthreads();
+  find_bins(h, 0, 0, true, k, n, s_w, s_out);
+  const uint32_t lo = (uint32_t)s_out[2] << 19, hi = ((uint32_t)s_out[0] << 19) | 0x7FFFFu;
   clk_stamp(p.clk, 1);
-  // ---- first digit (top 13 bits) over every key, without branches: key 0 adds 0
+
+  // ---- chunk pass
+  int above = 0, nc = 0;
+  uint32_t ck[kTopkPer];  // this thread's keys (0 past n)
 #pragma unroll
-  for (int q = 0; q < kTopkLoads; ++q)
+  for (int i = 0; i < kTopkPer / 4; ++i) {
+    uint32_t ns = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) atomicAdd(&h[key[q][e] >> 19], (uint32_t)(key[q][e] != 0u));
-#pragma unroll
-  for (int e = 0; e < kTopkWpt; ++e) {
-    s_sb[tid + kTopkThreads * e] = 0u;
-    s_tb[tid + kTopkThreads * e] = 0u;
+    for (int e = 0; e < 4; ++e) {
+      const int pos = c0 + 4 * (tid + kTopkThreads * i) + e;
+      const uint32_t kk = pos < n ? score_key(cv[i][e]) : 0u;
+      ck[4 * i + e] = kk;
+      ns |= kk > hi ? 1u << e : 0u;
+      nc += kk - lo <= hi - lo ? 1 : 0;
+    }
+    above += __popc(ns);
+    if (ns) atomicOr(&s_sb[(tid + kTopkThreads * i) >> 3], ns << (4 * (tid & 7)));
   }
-  if (tid == 0) s_nc = 0;
+  int ntot;
+  int slot = scan_wg(nc, s_w, &ntot);  // this thread's first candidate slot in the chunk's slice
+#pragma unroll
+  for (int i = 0; i < kTopkPer; ++i) {
+    if (ck[i] - lo <= hi - lo) {
+      const uint32_t pos = (uint32_t)(c0 + 4 * (tid + kTopkThreads * (i >> 2)) + (i & 3));
+      __hip_atomic_store(cand + c0 + slot, ((uint64_t)ck[i] << 32) | pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ++slot;
+    }
+  }
+  int atot;
+  (void)scan_wg(above, s_w, &atot);  // also orders the bitmap's atomics before its store below
+  if (tid < kDsaChunk / 32)
+    __hip_atomic_store(bits + ch * (kDsaChunk / 32) + tid, s_sb[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_store(counts + 2 * ch, (uint32_t)atot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(counts + 2 * ch + 1, (uint32_t)ntot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Hand-off to the last workgroup of the sequence without a release / acquire
+  // pair: the stores above are agent-scope atomic stores, written through to
+  // the device-coherent level; each thread waits until its stores are
+  // acknowledged (asm with a memory clobber, so the compiler keeps them before
+  // it) and only then is the arrival counter incremented; the last workgroup
+  // issues its agent-scope atomic loads only after the counter's value has
+  // returned.  A fence pair would write back and invalidate the whole L2 of
+  // the XCD for every workgroup.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  find_bin(h, p.topk, s_w, s_found);
-  const uint32_t T0 = (uint32_t)s_found[0];
-  int need = p.topk - s_found[1];
-  const uint32_t in_bin = h[T0];  // keys in the boundary bin
-  __syncthreads();                // h and s_found are rewritten below
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(p.nchunk - 1);
+  __syncthreads();
   clk_stamp(p.clk, 2);
-  uint32_t prefix = T0 << 19;
-  if (in_bin <= (uint32_t)kTopkCand) {  // workgroup-uniform
-    // Keys above the boundary bin are selected; the bin's keys (with their
-    // positions) become the candidates, and the other two digits and the ties
-    // are found among them alone.
-    const uint32_t lim = prefix | 0x7FFFFu;  // the bin's largest key
+  if (!s_last) return;
+
+  // ---- last workgroup of the sequence
+  const int nch = (n + kDsaChunk - 1) / kDsaChunk;  // chunks holding positions < n
+  if (tid <= nch) {
+    uint32_t a = 0u, m = 0u;
+    if (tid < nch) {
+      a = __hip_atomic_load(counts + 2 * tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      m = __hip_atomic_load(counts + 2 * tid + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s_coff[tid] = m;
+    h[tid] = a;  // scratch for the totals
+  }
+  __syncthreads();
+  if (tid == 0) {  // candidate counts -> offsets; totals
+    uint32_t acc = 0u, asum = 0u;
+    for (int c = 0; c < nch; ++c) {
+      const uint32_t m = s_coff[c];
+      s_coff[c] = acc;
+      acc += m;
+      asum += h[c];
+    }
+    s_coff[nch] = acc;
+    s_out[0] = (int)asum;
+  }
+  __syncthreads();
+  const int A = s_out[0], M = (int)s_coff[nch];
+  const bool exact = A < k && A + M >= k && M <= kTopkCandLds;  // workgroup-uniform
+  const int nw = (n + 31) / 32;
+  int need;
+  uint32_t prefix;
+  __syncthreads();  // s_out is rewritten below
+  if (exact) {
+    // candidates and bitmap words in one round of loads
+    {
+      // 64 threads per chunk (at most 16 chunks), four loads in flight each
+      const int c = tid >> 6, j0 = tid & 63;
+      const int cnt_c = c < nch ? (int)(s_coff[c + 1] - s_coff[c]) : 0, off = c < nch ? (int)s_coff[c] : 0;
+      for (int j = j0; j < cnt_c; j += 4 * 64) {
+        uint64_t v[4];
 #pragma unroll
-    for (int q = 0; q < kTopkLoads; ++q) {
-      const uint32_t* k = key[q];
-      uint32_t ns = 0u, nb = 0u;
+        for (int u = 0; u < 4; ++u)
+          v[u] = j + 64 * u < cnt_c ? __hip_atomic_load(cand + c * kDsaChunk + j + 64 * u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0ull;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ns |= k[e] > lim ? 1u << e : 0u;
-        nb |= k[e] - prefix <= 0x7FFFFu ? 1u << e : 0u;
+        for (int u = 0; u < 4; ++u)
+          if (j + 64 * u < cnt_c) s_cand[off + j + 64 * u] = v[u];
       }
-      const int word = (kTopkThreads * q + tid) >> 3, sh = 4 * (tid & 7);
-      if (ns) atomicOr(&s_sb[word], ns << sh);
-      if (nb) {
+      uint32_t w[kTopkWpt];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((nb >> e) & 1u) {
-            const int slot = atomicAdd(&s_nc, 1);
-            s_ck[slot] = k[e];
-            s_cp[slot] = 4 * (tid + kTopkThreads * q) + e;
-          }
+      for (int u = 0; u < kTopkWpt; ++u) {
+        const int i = tid + kTopkThreads * u;
+        w[u] = i < nw ? __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kTopkWpt; ++u) {
+        s_sb[tid + kTopkThreads * u] = w[u];
+        s_tb[tid + kTopkThreads * u] = 0u;
       }
     }
-    for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
-    __syncthreads();
-    const int nc = s_nc;
-    // second digit (13 bits) and third (6 bits), among the candidates
-#pragma unroll 1
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = pass == 1 ? 6 : 0;
-      const uint32_t dmask = pass == 1 ? 0x1FFFu : 0x3Fu, pmask = pass == 1 ? 0xFFF80000u : 0xFFFFFFC0u;
-      for (int i = tid; i < nc; i += kTopkThreads) {
-        const uint32_t k = s_ck[i];
-        if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
+    clk_stamp(p.clk, 3);
+    // The k-th key among the candidates, digit by digit on the key relative to
+    // lo (below 2^hb): 13 bits at a time from the top.
+    need = k - A;
+    int hb = 32 - __clz(hi - lo);
+    int shift = hb > 13 ? hb - 13 : 0;
+    uint32_t pm = 0u, pf = 0u;  // relative-key bits found so far: mask and value
+    while (true) {  // workgroup-uniform
+      const uint32_t dm = (1u << (hb - shift)) - 1u;  // hb - shift <= 13
+      zero_hist(h);
+      __syncthreads();
+      for (int i = tid; i < M; i += kTopkThreads) {
+        const uint32_t r = (uint32_t)(s_cand[i] >> 32) - lo;
+        if ((r & pm) == pf) atomicAdd(&h[(r >> shift) & dm], 1u);
       }
       __syncthreads();
-      find_bin(h, need, s_w, s_found);
-      prefix |= (uint32_t)s_found[0] << shift;
-      need -= s_found[1];
-      for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
-      __syncthreads();
-      clk_stamp(p.clk, 2 + pass);
+      find_bins(h, need, need, false, 0, 0, s_w, s_out);
+      pf |= (uint32_t)s_out[0] << shift;
+      pm |= dm << shift;
+      need -= s_out[1];
+      __syncthreads();  // s_out is rewritten by the next pass
+      if (shift == 0) break;
+      hb = shift;
+      shift = hb > 13 ? hb - 13 : 0;
     }
-    for (int i = tid; i < nc; i += kTopkThreads) {
-      const uint32_t k = s_ck[i], pos = s_cp[i];
-      if (k > prefix) atomicOr(&s_sb[pos >> 5], 1u << (pos & 31));
-      else if (k == prefix) atomicOr(&s_tb[pos >> 5], 1u << (pos & 31));
+    prefix = lo + pf;
+    for (int i = tid; i < M; i += kTopkThreads) {
+      const uint64_t c = s_cand[i];
+      const uint32_t kc = (uint32_t)(c >> 32), pos = (uint32_t)c;
+      if (kc > prefix) atomicOr(&s_sb[pos >> 5], 1u << (pos & 31));
+      else if (kc == prefix) atomicOr(&s_tb[pos >> 5], 1u << (pos & 31));
     }
   } else {
-    // more keys in the boundary bin than the candidate list holds (many equal
-    // or nearly equal scores): the other digits over every key in registers
-    for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
-    __syncthreads();
-#pragma unroll 1
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = pass == 1 ? 6 : 0;
-      const uint32_t dmask = pass == 1 ? 0x1FFFu : 0x3Fu, pmask = pass == 1 ? 0xFFF80000u : 0xFFFFFFC0u;
-#pragma unroll
-      for (int q = 0; q < kTopkLoads; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((key[q][e] & pmask) == prefix) atomicAdd(&h[(key[q][e] >> shift) & dmask], 1u);
-      __syncthreads();
-      find_bin(h, need, s_w, s_found);
-      prefix |= (uint32_t)s_found[0] << shift;
-      need -= s_found[1];
-      for (int i = tid; i < kDsaBins; i += kTopkThreads) h[i] = 0u;
-      __syncthreads();
-      clk_stamp(p.clk, 2 + pass);
+    // The bound did not hold: three digit histograms (13, 13, 6 bits) over
+    // every score of the sequence, read from the score row in rolled loops.
+    for (int u = 0; u < kTopkWpt; ++u) {
+      s_sb[tid + kTopkThreads * u] = 0u;
+      s_tb[tid + kTopkThreads * u] = 0u;
     }
-#pragma unroll
-    for (int q = 0; q < kTopkLoads; ++q) {
-      uint32_t ns = 0u, nt = 0u;  // the four positions' bits
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ns |= key[q][e] > prefix ? 1u << e : 0u;
-        nt |= key[q][e] == prefix ? 1u << e : 0u;
+    need = k;
+    prefix = 0u;
+    uint32_t pmask = 0u;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 19 : (pass == 1 ? 6 : 0);
+      const uint32_t dmask = pass == 2 ? 0x3Fu : 0x1FFFu;
+      zero_hist(h);
+      __syncthreads();
+      for (int pos = tid; pos < n; pos += kTopkThreads) {
+        const uint32_t kk = score_key(sc[pos]);
+        if ((kk & pmask) == prefix) atomicAdd(&h[(kk >> shift) & dmask], 1u);
       }
-      const int word = (kTopkThreads * q + tid) >> 3, sh = 4 * (tid & 7);
-      if (ns) atomicOr(&s_sb[word], ns << sh);
-      if (nt) atomicOr(&s_tb[word], nt << sh);
+      __syncthreads();
+      find_bins(h, need, need, false, 0, 0, s_w, s_out);
+      prefix |= (uint32_t)s_out[0] << shift;
+      pmask |= dmask << shift;
+      need -= s_out[1];
+      __syncthreads();
+    }
+    for (int pos = tid; pos < n; pos += kTopkThreads) {
+      const uint32_t kk = score_key(sc[pos]);
+      if (kk > prefix) atomicOr(&s_sb[pos >> 5], 1u << (pos & 31));
+      else if (kk == prefix) atomicOr(&s_tb[pos >> 5], 1u << (pos & 31));
     }
   }
   // prefix is the k-th largest key: the keys above it are marked in s_sb, and
   // `need` of the keys equal to it (s_tb) are taken, the lowest positions first
   __syncthreads();
-  clk_stamp(p.clk, 5);
+  clk_stamp(p.clk, 4);
   // thread t owns words [kTopkWpt*t, +kTopkWpt): ties taken in position order,
   // then the selected positions written ascending
-  const int nw = (n + 31) / 32, w0 = kTopkWpt * tid;
+  const int w0 = kTopkWpt * tid;
   int ties = 0;
-#pragma unroll
   for (int e = 0; e < kTopkWpt; ++e) ties += w0 + e < nw ? __popc(s_tb[w0 + e]) : 0;
   int total;
   const int tb0 = scan_wg(ties, s_w, &total);
@@ -392,10 +514,10 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
     while (s_ != 0u) {
       const int bit = __builtin_ctz(s_);
       s_ &= s_ - 1u;
-      if (o < p.topk) out[o++] = 32 * (w0 + e) + bit;
+      if (o < k) out[o++] = 32 * (w0 + e) + bit;
     }
   }
-  clk_stamp(p.clk, 6);
+  clk_stamp(p.clk, exact ? 5 : 6);
 }
 
 // ---------------------------------------------------------------------------
@@ -616,7 +738,7 @@ hipError_t launch_dsa_t(const DsaParams& p, hipStream_t s, const PhaseEvents* ev
   if (ev) (void)hipEventRecord(ev->ev[0], s);
   hipLaunchKernelGGL((dsa_index_kernel<HI, DI>), dim3((unsigned)(p.B * p.nseg)), dim3(256), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[1], s);
-  hipLaunchKernelGGL(dsa_topk_kernel, dim3((unsigned)p.B), dim3(kTopkThreads), 0, s, p);
+  hipLaunchKernelGGL(dsa_topk_kernel, dim3((unsigned)(p.B * p.nchunk)), dim3(kTopkThreads), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[2], s);
   if (p.hpg == 64)
     hipLaunchKernelGGL((dsa_attn_kernel<4>), dim3((unsigned)(p.B * (p.H / 64) * p.ts)), dim3(256), 0, s, p);

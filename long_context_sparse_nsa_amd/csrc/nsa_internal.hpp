@@ -140,7 +140,8 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // DeepSeek Sparse Attention decode step (lightning indexer + token top-k +
 // MQA attention over one shared latent per token).
 constexpr int kDsaDqk = 576, kDsaDv = 512, kDsaMaxLen = 65536, kDsaMaxTopk = 4096;
-constexpr int kDsaBins = 8192;      // radix digits of the top-k: 13, 13 and 6 bits of a score's order key
+constexpr int kDsaChunk = 4096;     // scores per top-k workgroup
+constexpr int kDsaBins = 8192;      // radix digit histograms of the top-k: 13 bits
 struct DsaParams {
   int B, H, HI, DI, topk;
   float scale_log2;
@@ -160,6 +161,11 @@ struct DsaParams {
   int nseg;                          // indexer workgroups per sequence
   int ts;                            // attention token splits per (sequence, head group)
   int hpg;                           // heads per attention workgroup: 64, or 32 when H % 64 != 0
+  int nchunk;                        // top-k workgroups per sequence: ceil(cap / kDsaChunk)
+  uint32_t* cnt;                     // workspace [B, 4] arrival counters (zeroed by the indexer launch),
+                                     // then [B, nchunk, 2] per-chunk counts
+  uint32_t* bits;                    // workspace [B, nchunk * kDsaChunk / 32]: positions above the bound
+  uint64_t* cand;                    // workspace [B, nchunk * kDsaChunk]: (key << 32 | position) candidates
   uint64_t* clk;                     // phase clock (null = off): top-k kernel, then attention kernel
 };
 
