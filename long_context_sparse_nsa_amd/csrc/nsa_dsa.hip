@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void dsa_index_kernel(DsaParams p) {
 //  - the last workgroup of the sequence (an arrival counter, zeroed by the
 //    indexer launch) checks that the bound held -- fewer than k keys above hi,
 //    at least k above or at lo, and the candidates fit in LDS -- and finds the
-//    k-th key among the candidates (digits of the key relative to lo, 13 bits
+//    k-th key among the candidates (digits of the key relative to lo, 11 bits
 //    at a time); keys above it are taken, and the rest from the keys equal to
 //    it, lowest positions first; the positions are written ascending from the
 //    bitmap.  When the bound did not hold, that workgroup runs the select over
@@ -201,7 +201,7 @@ __device__ __forceinline__ int scan_wg(int v, int* s_w, int* total) {
   return base + x - v;
 }
 
-// In the kDsaBins-bin histogram h, the bins holding the ra-th and rb-th largest
+// In the NB-bin histogram h, the bins holding the ra-th and rb-th largest
 // keys (ranks from 1) to s_out[0] and s_out[2], the counts of keys in higher
 // bins to s_out[1] and s_out[3].  With `sampled` the ranks come from the
 // histogram's total instead: the expected rank of the k-th key of n among the
@@ -209,9 +209,10 @@ __device__ __forceinline__ int scan_wg(int v, int* s_w, int* total) {
 // [1, total]; s_out[4] gets the total.  Thread t sums bins [kPer*(NT-1-t),
 // +kPer) (thread 0 the highest) from a rotated start, so that the lanes of a
 // wave read different LDS banks; only threads whose bins hold a rank walk them.
+template <int NB = kDsaBins>
 __device__ __forceinline__ void find_bins(const uint32_t* h, int ra, int rb, bool sampled, int k, int n, int* s_w,
                                           int* s_out) {
-  constexpr int kPer = kDsaBins / kTopkThreads;
+  constexpr int kPer = NB / kTopkThreads;
   const int tid = (int)threadIdx.x, g0 = kPer * (kTopkThreads - 1 - tid);
   int sum = 0;
   for (int e = 0; e < kPer; ++e) sum += (int)h[g0 + ((e + tid) & (kPer - 1))];
@@ -418,28 +419,29 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
     }
     clk_stamp(p.clk, 3);
     // The k-th key among the candidates, digit by digit on the key relative to
-    // lo (below 2^hb): 13 bits at a time from the top.
+    // lo (below 2^hb): 11 bits at a time from the top (2048-bin histograms).
+    constexpr int kCB = 11, kCBins = 1 << kCB;
     need = k - A;
     int hb = 32 - __clz(hi - lo);
-    int shift = hb > 13 ? hb - 13 : 0;
+    int shift = hb > kCB ? hb - kCB : 0;
     uint32_t pm = 0u, pf = 0u;  // relative-key bits found so far: mask and value
     while (true) {  // workgroup-uniform
-      const uint32_t dm = (1u << (hb - shift)) - 1u;  // hb - shift <= 13
-      zero_hist(h);
+      const uint32_t dm = (1u << (hb - shift)) - 1u;  // hb - shift <= kCB
+      for (int i = tid; i < kCBins; i += kTopkThreads) h[i] = 0u;
       __syncthreads();
       for (int i = tid; i < M; i += kTopkThreads) {
         const uint32_t r = (uint32_t)(s_cand[i] >> 32) - lo;
         if ((r & pm) == pf) atomicAdd(&h[(r >> shift) & dm], 1u);
       }
       __syncthreads();
-      find_bins(h, need, need, false, 0, 0, s_w, s_out);
+      find_bins<kCBins>(h, need, need, false, 0, 0, s_w, s_out);
       pf |= (uint32_t)s_out[0] << shift;
       pm |= dm << shift;
       need -= s_out[1];
       __syncthreads();  // s_out is rewritten by the next pass
       if (shift == 0) break;
       hb = shift;
-      shift = hb > 13 ? hb - 13 : 0;
+      shift = hb > kCB ? hb - kCB : 0;
     }
     prefix = lo + pf;
     for (int i = tid; i < M; i += kTopkThreads) {
