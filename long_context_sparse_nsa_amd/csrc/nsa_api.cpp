@@ -191,9 +191,10 @@ DsaPlan dsa_plan(const nsa_dsa_dims_t* dims, int32_t top_k, int64_t cap) {
   seg = (seg + 511) / 512 * 512;
   pl.seg = (int)seg;
   pl.nseg = (int)((cap + seg - 1) / seg);
-  // attention: at most 512 selected tokens per workgroup, about 128 workgroups
-  // (more splits add partial traffic faster than they add parallelism)
-  const int tmin = (top_k + 511) / 512, tmax = (top_k + 63) / 64;
+  // attention: at most 128 selected tokens per workgroup (the kernel holds all
+  // of a split's tiles at once), about 256 workgroups (more splits add partial
+  // traffic faster than they add parallelism)
+  const int tmin = (top_k + 127) / 128, tmax = (top_k + 63) / 64;
   int ts = 256 / (B * ngrp);
   ts = ts < tmin ? tmin : ts;
   ts = ts > tmax ? tmax : ts;

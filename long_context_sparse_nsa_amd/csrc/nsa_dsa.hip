@@ -22,11 +22,12 @@
 //     not hold, over every score), takes ties at it from the lowest positions
 //     and writes the positions ascending.
 //  3. dsa_attn_kernel    workgroup = (sequence, 64 heads -- 32 when the head
-//     count is not a multiple of 64 --, token split); 32-token tiles of latents
-//     are gathered into LDS with the direct global->LDS copy, four buffers
-//     (three tiles in flight), and every wave reads each tile for its own 16
-//     heads: one online softmax per wave, no exchange between waves, and the
-//     tile's latents are gathered once per 64 heads.
+//     count is not a multiple of 64 --, token split of at most 128 tokens); the
+//     split's 32-token tiles of latents are all gathered into LDS at once with
+//     the direct global->LDS copy, and every wave reads each tile for its own 16
+//     heads: logits of every tile first (exact maximum per head), then the
+//     probabilities and the values, with no exchange between waves; the tile's
+//     latents are gathered once per 64 heads.
 //  4. dsa_combine_kernel merges the token-split partials exactly and writes bf16.
 #include <hip/hip_runtime.h>
 
@@ -528,8 +529,8 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
 constexpr int kTileTok = 32, kKt = kDsaDqk / 32;   // 18 fragments of 32 dims per 16-row group
 constexpr int kFrag = (kTileTok / 16) * kKt;         // 36 fragments of 1 KB per tile
 constexpr int kTileBytes = kTileTok * kDsaDqk * 2;   // 36 KB
-constexpr int kNbuf = 4;                             // three tiles in flight while one is used
-constexpr int kMaxSplit = 512;                       // selected tokens per workgroup (host plan)
+constexpr int kNbuf = 4;                             // tiles of a split, all in flight at once
+constexpr int kMaxSplit = kNbuf * kTileTok;          // selected tokens per workgroup (host plan: 128)
 constexpr int kCopies = kFrag / 4;                   // copy instructions per wave per tile
 
 template <int NW>  // waves per workgroup; each owns 16 heads over every token of the split
@@ -592,63 +593,64 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
     }
   };
 
+  // Every tile of the split is in flight at once (a split holds at most kNbuf
+  // tiles), so no buffer is reused and the logits of all tiles fit in
+  // registers: pass 1 computes them as the tiles land and takes the exact
+  // maximum per head; pass 2 forms P = 2^(z - max) and O^T += V^T P^T.  With the
+  // maximum known there is no rescaling of the accumulators, which then stay
+  // in the matrix unit's registers, and the query fragments are dead in pass 2.
+  for (int it = 0; it < ntl; ++it) stage(it);
+  const float sc = p.scale_log2;
+  float z[kNbuf][2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < kNbuf; ++it) {
+    if (it >= ntl) break;  // workgroup-uniform
+    const int ahead = ntl - 1 - it;  // tiles issued after this one
+    if (ahead >= 3) wait_vmem_le<3 * NCP>();
+    else if (ahead == 2) wait_vmem_le<2 * NCP>();
+    else if (ahead == 1) wait_vmem_le<NCP>();
+    else wait_vmem();
+    lds_barrier();  // every wave's copies of tile it have landed
+    if (it == 0) clk_stamp(clk, 2);
+    const char* kt = s_buf[it];
+    // S^T for the tile's 32 tokens (row groups 0 and 1) and this wave's 16 heads
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKt; ++ks)
+        s = mfma_bf16(*reinterpret_cast<const u32x4_t*>(kt + ((mm * kKt + ks) * 64 + (lane ^ ((2 * lg + ks) & 7))) * 16),
+                      qf[ks], s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = kTileTok * it + 16 * mm + 4 * lg + i;  // token index within the split
+        z[it][mm][i] = t0 + tt < t1 ? s[i] * sc : -INFINITY;
+        mx = fmaxf(mx, z[it][mm][i]);
+      }
+    }
+  }
+  mx = max_over_groups_swap(mx);  // head lr over every token of the split (finite: the split is not empty)
+
   f32x4_t acc[4][8];  // dim block db (128 dims), operand jj: O^T[128*db + 8*(4lg+i) + jj][head lr]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) acc[db][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mref = -INFINITY, lsum = 0.f;
-  const float sc = p.scale_log2;
-
-  for (int it = 0; it < kNbuf - 1 && it < ntl; ++it) stage(it);
-  for (int it = 0; it < ntl; ++it) {
-    if (it + kNbuf - 1 < ntl) stage(it + kNbuf - 1);
-    const int ahead = ntl - 1 - it < kNbuf - 1 ? ntl - 1 - it : kNbuf - 1;  // tiles issued after this one
-    if (ahead >= 3) wait_vmem_le<3 * NCP>();
-    else if (ahead == 2) wait_vmem_le<2 * NCP>();
-    else if (ahead == 1) wait_vmem_le<NCP>();
-    else wait_vmem();
-    lds_barrier();
-    if (it == 0) clk_stamp(clk, 2);
-    const char* kt = s_buf[it % kNbuf];
-    // S^T for the tile's 32 tokens (row groups 0 and 1) and this wave's 16 heads
-    f32x4_t s[2];
+  float lsum = 0.f;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      s[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kKt; ++ks)
-        s[mm] = mfma_bf16(*reinterpret_cast<const u32x4_t*>(kt + ((mm * kKt + ks) * 64 + (lane ^ ((2 * lg + ks) & 7))) * 16),
-                          qf[ks], s[mm]);
-    }
-    float z[2][4];
-    float mx = -INFINITY;
+  for (int it = 0; it < kNbuf; ++it) {
+    if (it >= ntl) break;  // workgroup-uniform
+    const char* kt = s_buf[it];
+    float e[2][4];
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tt = kTileTok * it + 16 * mm + 4 * lg + i;  // token index within the split
-        z[mm][i] = t0 + tt < t1 ? s[mm][i] * sc : -INFINITY;
-        mx = fmaxf(mx, z[mm][i]);
+        e[mm][i] = z[it][mm][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[it][mm][i] - mx);
+        lsum += e[mm][i];
       }
-    mx = max_over_groups_swap(mx);  // head lr over the tile's 32 tokens
-    if (mx > mref + 8.f || (mref == -INFINITY && mx > -INFINITY)) {  // move the reference (lazily)
-      const float f = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mx);
-      lsum *= f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc[db][jj] *= f;
-      mref = mx;
-    }
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[mm][i] = z[mm][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[mm][i] - mref);
-        lsum += z[mm][i];
-      }
-    const u32x4_t pb = pack_probs(z[0], z[1]);
+    const u32x4_t pb = pack_probs(e[0], e[1]);
     // O^T += V^T P^T: the values are the first 512 latent dims; lane (lg, lr) reads
     // the 8 rows of its k-slots, 8 dims 128*db + 8*lr .. of each, from the fragments
 #pragma unroll
@@ -667,14 +669,13 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
       }
       pv_step<128>(vr, pb, acc[db]);
     }
-    lds_barrier();  // every wave is done with this buffer before it is refilled
   }
   clk_stamp(clk, 3);
   lsum = sum_over_groups_swap(lsum);
   // this wave's 16 heads: (m, l, O / l) to the partial
   float* dst = part + (size_t)(16 * wave + lr) * kPartStride;
   if (lg == 0) {
-    dst[0] = mref;
+    dst[0] = mx;
     dst[1] = lsum;
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
