@@ -28,7 +28,8 @@
 //     heads: logits of every tile first (exact maximum per head), then the
 //     probabilities and the values, with no exchange between waves; the tile's
 //     latents are gathered once per 64 heads.
-//  4. dsa_combine_kernel merges the token-split partials exactly and writes bf16.
+//  4. dsa_combine_kernel merges the token-split partials exactly and writes bf16
+//     (one wave per (sequence, head), 16-byte loads of 8 channels per lane).
 #include <hip/hip_runtime.h>
 
 #include "nsa_device.hpp"
@@ -693,47 +694,54 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. exact merge of the token splits: workgroup per (sequence, head), 4 channels per thread
-__global__ __launch_bounds__(128) void dsa_combine_kernel(DsaParams p) {
+// 4. exact merge of the token splits: one wave per (sequence, head), 8 channels per lane
+__global__ __launch_bounds__(256) void dsa_combine_kernel(DsaParams p) {
   constexpr int MS = 16;  // splits held in registers; more are merged in a second loop
-  const int bh = blockIdx.x, b = bh / p.H, h = bh - b * p.H;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int bh = 4 * blockIdx.x + wave;
+  if (bh >= p.B * p.H) return;
+  const int b = bh / p.H, h = bh - b * p.H;
   const int ngrp = p.H / p.hpg, hg = h / p.hpg, hl = h - hg * p.hpg;
   const float* src = p.part + ((size_t)(b * ngrp + hg) * p.ts * p.hpg + hl) * kPartStride;
   const size_t sstep = (size_t)p.hpg * kPartStride;
-  const int c = 4 * threadIdx.x;  // this thread's 4 channels
+  const int c = 8 * lane;  // this lane's 8 channels
   float m[MS], l[MS];
-  u32x2_t v[MS];
+  u32x4_t v[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {  // every load issued before any is used
     const bool in = s < p.ts;
     m[s] = in ? src[s * sstep] : -INFINITY;
     l[s] = in ? src[s * sstep + 1] : 0.f;
-    v[s] = in ? *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(src + s * sstep + kPartOut) + c)
-              : u32x2_t{0u, 0u};
+    v[s] = in ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(src + s * sstep + kPartOut) + c)
+              : u32x4_t{0u, 0u, 0u, 0u};
   }
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < MS; ++s) M = fmaxf(M, m[s]);
   for (int s = MS; s < p.ts; ++s) M = fmaxf(M, src[s * sstep]);
   float Ls = 0.f;
-  f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-  auto add = [&](float ms, float ls, u32x2_t w) {
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](float ms, float ls, u32x4_t w) {
     if (ms == -INFINITY) return;
     const float a = __builtin_amdgcn_exp2f(ms - M) * ls;  // the split's weight: exp(m - M) * l
-    const f32x2_t x0 = unpack_f16x2(w[0]), x1 = unpack_f16x2(w[1]);
     Ls += a;
-    o = f32x4_t{o[0] + a * x0[0], o[1] + a * x0[1], o[2] + a * x1[0], o[3] + a * x1[1]};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x2_t x = unpack_f16x2(w[q]);
+      o[2 * q] += a * x[0];
+      o[2 * q + 1] += a * x[1];
+    }
   };
 #pragma unroll
   for (int s = 0; s < MS; ++s) add(m[s], l[s], v[s]);
   for (int s = MS; s < p.ts; ++s)
     add(src[s * sstep], src[s * sstep + 1],
-        *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(src + s * sstep + kPartOut) + c));
+        *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(src + s * sstep + kPartOut) + c));
   const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
-  u32x2_t w;
-  w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
-  w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
-  *reinterpret_cast<u32x2_t*>(p.out + ((size_t)b * p.H + h) * kDsaDv + c) = w;
+  u32x4_t w;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(o[2 * q] * inv, o[2 * q + 1] * inv);
+  *reinterpret_cast<u32x4_t*>(p.out + ((size_t)b * p.H + h) * kDsaDv + c) = w;
 }
 
 template <int HI, int DI>
@@ -747,7 +755,7 @@ hipError_t launch_dsa_t(const DsaParams& p, hipStream_t s, const PhaseEvents* ev
     hipLaunchKernelGGL((dsa_attn_kernel<4>), dim3((unsigned)(p.B * (p.H / 64) * p.ts)), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((dsa_attn_kernel<2>), dim3((unsigned)(p.B * (p.H / 32) * p.ts)), dim3(128), 0, s, p);
-  hipLaunchKernelGGL(dsa_combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(dsa_combine_kernel, dim3((unsigned)((p.B * p.H + 3) / 4)), dim3(256), 0, s, p);
   if (ev) (void)hipEventRecord(ev->ev[3], s);
   return hipGetLastError();
 }
