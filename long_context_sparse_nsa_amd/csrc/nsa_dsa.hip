@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   __shared__ int s_out[5];
   __shared__ uint32_t s_coff[kDsaMaxLen / kDsaChunk + 1];
   __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int b = blockIdx.x / p.nchunk, ch = blockIdx.x - b * p.nchunk;
   clk_stamp(p.clk, 0);
   const int64_t L = p.seq_lens[b];
@@ -532,7 +532,6 @@ constexpr int kFrag = (kTileTok / 16) * kKt;         // 36 fragments of 1 KB per
 constexpr int kTileBytes = kTileTok * kDsaDqk * 2;   // 36 KB
 constexpr int kNbuf = 4;                             // tiles of a split, all in flight at once
 constexpr int kMaxSplit = kNbuf * kTileTok;          // selected tokens per workgroup (host plan: 128)
-constexpr int kCopies = kFrag / 4;                   // copy instructions per wave per tile
 
 template <int NW>  // waves per workgroup; each owns 16 heads over every token of the split
 __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
