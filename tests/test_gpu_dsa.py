@@ -106,6 +106,28 @@ def test_dsa_shapes(shape, k):
     check_dsa(case, out, sel, scores, top_k=k)
 
 
+@pytest.mark.parametrize("k", [1, 7])
+def test_dsa_small_top_k(k):
+    """Top-1 and top-7 over ~12k scores: the bound's margin covers most of the sample."""
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=12000, ragged_min=9000, num_heads=32, needles=4),
+                          58 + k)
+    out, sel, scores, _ = run_dsa(case, top_k=k)
+    check_dsa(case, out, sel, scores, top_k=k)
+
+
+def test_dsa_bound_missed_in_one_sequence_only():
+    """Sequence 0's scores ordered along the sequence (the sampled bound misses and its
+    last workgroup selects over every score), sequence 1's left as drawn (the bound holds)."""
+    case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=30000, num_heads=32, needles=4), 59)
+    L = int(case.seq_lens[0])
+    qI = D.fp8_e4m3_to_float(case.q_idx[0])
+    kI = D.fp8_e4m3_to_float(case.k_idx[0, :L])
+    score = np.maximum(kI @ qI.T, 0.0) @ np.asarray(case.w_idx[0], np.float64)
+    case.k_idx[0, :L] = case.k_idx[0, np.argsort(-score, kind="stable")]
+    out, sel, scores, _ = run_dsa(case)
+    check_dsa(case, out, sel, scores)
+
+
 def test_dsa_equal_scores_take_the_lowest_positions():
     """Every indexer key equal: all scores tie, so the selection is positions 0..k-1."""
     case = I.generate_dsa(I.dsa_workload(HEAD, batch=2, seq_len=5000, num_heads=32, needles=0), 54)
