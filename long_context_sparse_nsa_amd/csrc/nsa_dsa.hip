@@ -262,7 +262,8 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   __shared__ int s_w[kTopkWaves];
   __shared__ int s_out[5];
   __shared__ uint32_t s_coff[kDsaMaxLen / kDsaChunk + 1];
-  __shared__ int s_last;
+  __shared__ uint32_t s_small[64];  // the boundary bin's keys, once at most 64
+  __shared__ int s_last, s_nb;
   const int tid = threadIdx.x;
   const int b = blockIdx.x / p.nchunk, ch = blockIdx.x - b * p.nchunk;
   clk_stamp(p.clk, 0);
@@ -422,11 +423,14 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
     clk_stamp(p.clk, 3);
     // The k-th key among the candidates, digit by digit on the key relative to
     // lo (below 2^hb): 11 bits at a time from the top (2048-bin histograms).
+    // Once the boundary bin holds at most 64 candidates, one wave ranks them
+    // directly instead of another histogram pass.
     constexpr int kCB = 11, kCBins = 1 << kCB;
     need = k - A;
     int hb = 32 - __clz(hi - lo);
     int shift = hb > kCB ? hb - kCB : 0;
     uint32_t pm = 0u, pf = 0u;  // relative-key bits found so far: mask and value
+    bool ranked = false;
     while (true) {  // workgroup-uniform
       const uint32_t dm = (1u << (hb - shift)) - 1u;  // hb - shift <= kCB
       for (int i = tid; i < kCBins; i += kTopkThreads) h[i] = 0u;
@@ -437,15 +441,46 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
       }
       __syncthreads();
       find_bins<kCBins>(h, need, need, false, 0, 0, s_w, s_out);
+      const int cb = (int)h[s_out[0]];  // candidates in the boundary bin
       pf |= (uint32_t)s_out[0] << shift;
       pm |= dm << shift;
       need -= s_out[1];
-      __syncthreads();  // s_out is rewritten by the next pass
+      __syncthreads();  // s_out and h are rewritten below
       if (shift == 0) break;
+      if (cb <= 64) {  // workgroup-uniform
+        if (tid == 0) s_nb = 0;
+        __syncthreads();
+        for (int i = tid; i < M; i += kTopkThreads) {
+          const uint32_t kc = (uint32_t)(s_cand[i] >> 32);
+          if (((kc - lo) & pm) == pf) s_small[atomicAdd(&s_nb, 1)] = kc;
+        }
+        __syncthreads();
+        if (tid < cb) {  // the need-th largest key: fewer than need above it, need at or above
+          const uint32_t kc = s_small[tid];
+          int gt = 0, ge = 0;
+          for (int j = 0; j < cb; ++j) {
+            const uint32_t v = s_small[j];
+            gt += v > kc ? 1 : 0;
+            ge += v >= kc ? 1 : 0;
+          }
+          if (gt < need && need <= ge) {  // every lane holding that key writes the same
+            s_out[0] = (int)kc;
+            s_out[1] = gt;
+          }
+        }
+        __syncthreads();
+        ranked = true;
+        break;
+      }
       hb = shift;
       shift = hb > kCB ? hb - kCB : 0;
     }
-    prefix = lo + pf;
+    if (ranked) {
+      prefix = (uint32_t)s_out[0];
+      need -= s_out[1];
+    } else {
+      prefix = lo + pf;
+    }
     for (int i = tid; i < M; i += kTopkThreads) {
       const uint64_t c = s_cand[i];
       const uint32_t kc = (uint32_t)(c >> 32), pos = (uint32_t)c;
