@@ -361,8 +361,25 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   clk_stamp(p.clk, 2);
   if (!s_last) return;
 
-  // ---- last workgroup of the sequence
+  // ---- last workgroup of the sequence.  One round of loads before any wait:
+  // the chunks' counts, the first kPre candidates of every chunk (64 threads per
+  // chunk; entries past a chunk's count are read but never used) and the
+  // position bitmap.
+  constexpr int kPre = 4 * 64;
   const int nch = (n + kDsaChunk - 1) / kDsaChunk;  // chunks holding positions < n
+  const int cc = tid >> 6, j0 = tid & 63;           // this thread's chunk and first entry
+  uint64_t pre[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    pre[u] = cc < nch ? __hip_atomic_load(cand + cc * kDsaChunk + j0 + 64 * u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : 0ull;
+  const int nw = (n + 31) / 32;
+  uint32_t wv[kTopkWpt];
+#pragma unroll
+  for (int u = 0; u < kTopkWpt; ++u) {
+    const int i = tid + kTopkThreads * u;
+    wv[u] = i < nw ? __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  }
   if (tid <= nch) {
     uint32_t a = 0u, m = 0u;
     if (tid < nch) {
@@ -387,36 +404,20 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   __syncthreads();
   const int A = s_out[0], M = (int)s_coff[nch];
   const bool exact = A < k && A + M >= k && M <= kTopkCandLds;  // workgroup-uniform
-  const int nw = (n + 31) / 32;
   int need;
   uint32_t prefix;
   __syncthreads();  // s_out is rewritten below
   if (exact) {
-    // candidates and bitmap words in one round of loads
     {
-      // 64 threads per chunk (at most 16 chunks), four loads in flight each
-      const int c = tid >> 6, j0 = tid & 63;
-      const int cnt_c = c < nch ? (int)(s_coff[c + 1] - s_coff[c]) : 0, off = c < nch ? (int)s_coff[c] : 0;
-      for (int j = j0; j < cnt_c; j += 4 * 64) {
-        uint64_t v[4];
+      const int cnt_c = cc < nch ? (int)(s_coff[cc + 1] - s_coff[cc]) : 0, off = cc < nch ? (int)s_coff[cc] : 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[u] = j + 64 * u < cnt_c ? __hip_atomic_load(cand + c * kDsaChunk + j + 64 * u, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT)
-                                    : 0ull;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (j + 64 * u < cnt_c) s_cand[off + j + 64 * u] = v[u];
-      }
-      uint32_t w[kTopkWpt];
+      for (int u = 0; u < 4; ++u)
+        if (j0 + 64 * u < cnt_c) s_cand[off + j0 + 64 * u] = pre[u];
+      for (int j = j0 + kPre; j < cnt_c; j += 64)  // chunks with more than kPre candidates
+        s_cand[off + j] = __hip_atomic_load(cand + cc * kDsaChunk + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int u = 0; u < kTopkWpt; ++u) {
-        const int i = tid + kTopkThreads * u;
-        w[u] = i < nw ? __hip_atomic_load(bits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kTopkWpt; ++u) {
-        s_sb[tid + kTopkThreads * u] = w[u];
+        s_sb[tid + kTopkThreads * u] = wv[u];
         s_tb[tid + kTopkThreads * u] = 0u;
       }
     }
