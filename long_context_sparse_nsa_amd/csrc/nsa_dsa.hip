@@ -180,21 +180,23 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // for "no key".
 __device__ __forceinline__ uint32_t score_key(float f) { return max(order_key(f), 1u << 19); }
 
-// Exclusive prefix over the workgroup's threads; *total gets the sum.
-__device__ __forceinline__ int scan_wg(int v, int* s_w, int* total) {
+// Exclusive prefix over the workgroup's threads; *total gets the sum.  T is
+// int, or uint32_t for sums taken modulo 2^32 (packed fields).
+template <class T>
+__device__ __forceinline__ T scan_wg(T v, T* s_w, T* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+  T x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
+    const T y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
   if (lane == 63) s_w[wave] = x;
   __syncthreads();
-  int base = 0, tot = 0;
+  T base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) {
-    const int s = s_w[w];
+    const T s = s_w[w];
     base += w < wave ? s : 0;
     tot += s;
   }
@@ -260,6 +262,7 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   __shared__ uint32_t s_sb[kDsaMaxLen / 32], s_tb[kDsaMaxLen / 32];  // selected / tied positions
   __shared__ uint64_t s_cand[kTopkCandLds];                          // (key << 32) | position
   __shared__ int s_w[kTopkWaves];
+  __shared__ uint32_t s_wu[kTopkWaves];
   __shared__ int s_out[5];
   __shared__ uint32_t s_coff[kDsaMaxLen / kDsaChunk + 1];
   __shared__ uint32_t s_small[64];  // the boundary bin's keys, once at most 64
@@ -524,16 +527,24 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
   // `need` of the keys equal to it (s_tb) are taken, the lowest positions first
   __syncthreads();
   clk_stamp(p.clk, 4);
-  // thread t owns words [kTopkWpt*t, +kTopkWpt): ties taken in position order,
-  // then the selected positions written ascending
+  // Thread t owns words [kTopkWpt*t, +kTopkWpt).  One scan gives both the
+  // marked positions (above the k-th key) and the ties before this thread,
+  // packed as ties << 16 | marked: the marked total is below k <= 4096, so the
+  // low field never carries, and a prefix of ties is below 2^16.  The first
+  // `need` ties in position order are taken, so the ties taken before this
+  // thread are min(need, its tie prefix), and its output offset follows.
   const int w0 = kTopkWpt * tid;
-  int ties = 0;
-  for (int e = 0; e < kTopkWpt; ++e) ties += w0 + e < nw ? __popc(s_tb[w0 + e]) : 0;
-  int total;
-  const int tb0 = scan_wg(ties, s_w, &total);
+  uint32_t marked = 0u, ties = 0u;
+  for (int e = 0; e < kTopkWpt; ++e) {
+    marked += w0 + e < nw ? (uint32_t)__popc(s_sb[w0 + e]) : 0u;
+    ties += w0 + e < nw ? (uint32_t)__popc(s_tb[w0 + e]) : 0u;
+  }
+  uint32_t ptotal;
+  const uint32_t pfx = scan_wg<uint32_t>((ties << 16) | marked, s_wu, &ptotal);
+  const int tb0 = (int)(pfx >> 16);
   int take = need - tb0;
-  take = take < 0 ? 0 : (take > ties ? ties : take);
-  int cntsel = 0;
+  take = take < 0 ? 0 : (take > (int)ties ? (int)ties : take);
+  int o = (int)(pfx & 0xFFFFu) + (tb0 < need ? tb0 : need);
   uint32_t word[kTopkWpt];
 #pragma unroll
   for (int e = 0; e < kTopkWpt; ++e) {
@@ -545,9 +556,7 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
       --take;
     }
     word[e] = s_;
-    cntsel += __popc(s_);
   }
-  int o = scan_wg(cntsel, s_w, &total);
 #pragma unroll
   for (int e = 0; e < kTopkWpt; ++e) {
     uint32_t s_ = word[e];
