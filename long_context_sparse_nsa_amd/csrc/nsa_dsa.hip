@@ -330,8 +330,13 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
     above += __popc(ns);
     if (ns) atomicOr(&s_sb[(tid + kTopkThreads * i) >> 3], ns << (4 * (tid & 7)));
   }
-  int ntot;
-  int slot = scan_wg(nc, s_w, &ntot);  // this thread's first candidate slot in the chunk's slice
+  // one scan for both counts, packed as above << 16 | candidates (each at most
+  // 4096 per chunk); its barriers also order the bitmap's atomics before its
+  // store below
+  uint32_t ptot;
+  const uint32_t cpfx = scan_wg<uint32_t>(((uint32_t)above << 16) | (uint32_t)nc, s_wu, &ptot);
+  int slot = (int)(cpfx & 0xFFFFu);  // this thread's first candidate slot in the chunk's slice
+  const int ntot = (int)(ptot & 0xFFFFu), atot = (int)(ptot >> 16);
 #pragma unroll
   for (int i = 0; i < kTopkPer; ++i) {
     if (ck[i] - lo <= hi - lo) {
@@ -340,8 +345,6 @@ __global__ __launch_bounds__(kTopkThreads) void dsa_topk_kernel(DsaParams p) {
       ++slot;
     }
   }
-  int atot;
-  (void)scan_wg(above, s_w, &atot);  // also orders the bitmap's atomics before its store below
   if (tid < kDsaChunk / 32)
     __hip_atomic_store(bits + ch * (kDsaChunk / 32) + tid, s_sb[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (tid == 0) {
