@@ -440,8 +440,15 @@ nsa_status_t decode_launch(const nsa_dims_t* dims, const nsa_config_t* cfg, cons
   p.nch = lay.nch;
   p.seg = lay.seg;
   p.nbo = lay.nbo;
-  if (g_clk && (int64_t)p.B * p.H * ((p.nch + p.nwin) > p.nfin ? (p.nch + p.nwin) : p.nfin) <= nsa::kClkMaxGroups)
-    p.clk = g_clk;
+  p.bal = lay.bal;
+  p.nslot = lay.nslot;
+  p.bal_fill = lay.bal_fill;
+  p.tmin = lay.tmin;
+  p.tcap = lay.tcap;
+  p.scs = lay.scs;
+  const int64_t g1 = std::max<int64_t>((int64_t)p.B * p.H * (p.nch + p.nwin),
+                                       lay.bal ? (int64_t)p.B * p.H * p.nwin + p.nslot : 0);
+  if (g_clk && std::max<int64_t>(g1, (int64_t)p.B * p.H * p.nfin) <= nsa::kClkMaxGroups) p.clk = g_clk;
   const nsa::PhaseEvents* ev = g_phase_on ? &g_phase_events : nullptr;
   hipError_t e = nsa::launch_decode(p, dims->d_k, dims->d_v, static_cast<hipStream_t>(stream), ev);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -22,6 +22,8 @@
 // selection of n l'-blocks re-using the compressed-branch weights, shared by a
 // GQA group so each KV block is read once per group; window of w tokens) and
 // section "Сколько это экономит" (decode is bound by reading the KV cache).
+#include <algorithm>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -76,6 +78,97 @@ __device__ __forceinline__ int n_visible(const DecodeParams& p, int b, int L) {
   int64_t nv = L >= p.l ? (L - p.l) / p.d + 1 : 0;
   const int64_t ccap = p.cuc ? ld_scalar(p.cuc + b + 1) - ld_scalar(p.cuc + b) : p.ccap;
   return (int)(nv < ccap ? nv : ccap);
+}
+
+// ---- balanced plan of a ragged batch (p.bal): every compressed segment holds
+// T tiles of kStreamTile keys (a sequence's last one fewer), with T chosen from
+// the actual lengths so that the segments of all units fill about p.bal_fill
+// slots.  Sequence b has tiles_b = ceil(n_visible / kStreamTile) tiles and
+// c_b = ceil(tiles_b / T) segments per group; unit (b, g) owns the slots
+// [base_b + g*c_b, base_b + (g+1)*c_b), base_b = H * sum over b' < b of c_b'.
+// The helpers are wave-wide (every lane of the calling wave takes part; the
+// results are wave-uniform) and read the lengths with one vector load per lane
+// and 64 sequences.
+__device__ __forceinline__ int lane_tiles(const DecodeParams& p, int b) {
+  int64_t cap = p.cap, ccap = p.ccap;
+  if (p.cu) {
+    const int64_t c = p.cu[b + 1] - p.cu[b];
+    if (c < cap) cap = c;
+  }
+  if (p.cuc) ccap = p.cuc[b + 1] - p.cuc[b];
+  int64_t L = p.seq_lens[b];
+  if (L > cap) L = cap;
+  if (L < 1) L = 1;
+  int64_t nv = L >= p.l ? (L - p.l) / p.d + 1 : 0;
+  if (nv > ccap) nv = ccap;
+  return (int)((nv + kStreamTile - 1) / kStreamTile);
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+// T, or 0 when even segments of tcap tiles would not fit in about one round
+// (every sequence long): then the fixed plan is used.  With at most 64
+// sequences, *tl gets the lane's own sequence's tiles, so that the calls below
+// need no second round of loads.
+__device__ __forceinline__ int bal_tiles_per_segment(const DecodeParams& p, int* tl) {
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int x = b0 + lane < p.B ? lane_tiles(p, b0 + lane) : 0;
+    tot += wave_sum_int(x);
+    *tl = x;
+  }
+  int T = (p.H * tot + p.bal_fill - 1) / p.bal_fill;
+  if (T < p.tmin) T = p.tmin;
+  if (T > p.tcap) T = 0;
+  return __builtin_amdgcn_readfirstlane(T);
+}
+// The unit and segment of compressed slot s; false for a slot past every unit's segments.
+__device__ __forceinline__ bool bal_slot(const DecodeParams& p, int T, int tl, int s, int& b, int& g, int& k) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int cb = bb < p.B ? ((p.B <= 64 ? tl : lane_tiles(p, bb)) + T - 1) / T : 0;
+    const int incl = wave_incl_scan(p.H * cb);
+    const int excl = incl - p.H * cb;
+    const uint64_t hit = __ballot(cb > 0 && s >= base + excl && s < base + incl);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int c = __builtin_amdgcn_readlane(cb, src);
+      const int off = s - base - __builtin_amdgcn_readlane(excl, src);
+      b = b0 + src;
+      g = off / c;
+      k = off - g * c;
+      return true;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return false;
+}
+// The first slot and the number of segments of unit (b, g).
+__device__ __forceinline__ void bal_unit(const DecodeParams& p, int T, int tl, int b, int g, int& first, int& count) {
+  const int lane = threadIdx.x & 63;
+  int base = 0, cnt = 0;
+  for (int b0 = 0; b0 <= b; b0 += 64) {
+    const int bb = b0 + lane;
+    const int cb = bb < p.B ? ((p.B <= 64 ? tl : lane_tiles(p, bb)) + T - 1) / T : 0;
+    base += wave_sum_int(bb < b ? p.H * cb : 0);
+    if (b < b0 + 64) cnt = __builtin_amdgcn_readlane(cb, b - b0);
+  }
+  first = __builtin_amdgcn_readfirstlane(base + g * cnt);
+  count = __builtin_amdgcn_readfirstlane(cnt);
 }
 
 // Stores and loads that are coherent across the whole device without cache
@@ -319,8 +412,32 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
 
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int per = p.nch + p.nwin;
-  const int bg = blockIdx.x / per, c = blockIdx.x - bg * per;
+  // workgroup -> unit bg and compressed segment (c < nch: keys [k0, k0 + seg) into
+  // output slot `slot`) or window part c - nch
+  int bg, c, seg, k0 = 0, slot = 0;
+  int tl = 0;
+  const int T = p.bal ? bal_tiles_per_segment(p, &tl) : 0;
+  if (T == 0) {  // the fixed plan
+    const int per = p.nch + p.nwin;
+    bg = blockIdx.x / per;
+    if (bg >= p.B * p.H) return;  // the launch is sized for either plan
+    c = blockIdx.x - bg * per;
+    seg = p.seg;
+    k0 = c * seg;
+    slot = bg * p.nch + c;
+  } else if ((int)blockIdx.x < p.B * p.H * p.nwin) {  // window parts first
+    bg = blockIdx.x / p.nwin;
+    c = p.nch + (blockIdx.x - bg * p.nwin);
+    seg = 0;
+  } else {
+    slot = blockIdx.x - p.B * p.H * p.nwin;
+    int sb, sg, sk;
+    if (!bal_slot(p, T, tl, slot, sb, sg, sk)) return;  // a slot past every unit's segments
+    bg = sb * p.H + sg;
+    c = 0;
+    seg = T * kStreamTile;
+    k0 = sk * seg;
+  }
   const int g = bg % p.H, b = bg / p.H;
   const bool fold = c < p.nch;  // workgroup-uniform: compressed segment, else window part
   clk_stamp(p.clk, 0);
@@ -338,10 +455,9 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     // A segment's rows and its slot's capacity do not depend on the sequence
     // length, so the first tiles are requested while the length is read; rows
     // past the length are masked (their values are zeroed before use).
-    const int k0 = c * p.seg;
     const int64_t ccap_b = p.cuc ? ld_scalar(p.cuc + b + 1) - ld_scalar(p.cuc + b) : p.ccap;
     if (k0 >= ccap_b) return;  // beyond the slot: never read by the selection kernel
-    const int64_t rpre = min((int64_t)k0 + p.seg, ccap_b) - 1;
+    const int64_t rpre = min((int64_t)k0 + seg, ccap_b) - 1;
     const int64_t crow = cmp_row0(p, b, g);
     kb = p.kc + crow * DK;
     vb = p.vc + crow * DV;
@@ -355,7 +471,7 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
       wait_vmem();
       return;
     }
-    const int k1 = min(k0 + p.seg, nvis);
+    const int k1 = min(k0 + seg, nvis);
     r0 = k0;
     nt = (k1 - k0 + TR - 1) / TR;
     vlo = k0;
@@ -518,10 +634,9 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   lds_barrier();
   float *dm, *dl, *dox;
   if (fold) {
-    const size_t slot = (size_t)bg * p.nch + c;
-    dm = p.m1 + slot * 16;
-    dl = p.l1 + slot * 16;
-    dox = p.o1 + slot * 16 * DV;
+    dm = p.m1 + (size_t)slot * 16;
+    dl = p.l1 + (size_t)slot * 16;
+    dox = p.o1 + (size_t)slot * 16 * DV;
   } else {
     float* dst = p.wpart + ((size_t)bg * p.nwin + (c - p.nch)) * PSTRIDE;
     dm = dst;
@@ -551,9 +666,9 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     // overhang into the next segment's first block): block J sums the fold rows
     // J - j0 of the wave-tiles whose keys reach into it, each scaled from its
     // own reference to M, in tile and wave order.
-    const int slots = p.nbo + 1;
+    const int slots = seg / rd + 1;  // the segment's blocks and the overhang
     const float invq = 1.0f / (float)qd;
-    float* SC = p.sc1 + ((size_t)bg * p.nch + c) * slots * 16;  // [slot][head]
+    float* SC = p.sc1 + (size_t)slot * p.scs * 16;  // [slot][head]
     const float(*fm)[16] = reinterpret_cast<const float(*)[16]>(&s_fm[0][0][0]);        // [u][head]
     const float(*fw)[16][16] = reinterpret_cast<const float(*)[16][16]>(&s_fw[0][0][0][0]);  // [u][head][row]
     for (int e = tid; e < 16 * slots; e += NTH) {  // head e mod 16 = lr
@@ -698,8 +813,22 @@ __global__ __launch_bounds__(64 * kFinWaves) void decode_finish_kernel(DecodePar
   const int g = bg % p.H, b = bg / p.H;
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nch = p.nch, nbo = p.nbo, slots = nbo + 1, nfin = p.nfin;
-  const size_t cbase = (size_t)bg * nch;
+  // the unit's segment slots: nch segments of segk keys from slot cbase, nbo
+  // selection blocks each, score rows `slots` apart
+  int nch = p.nch, nbo = p.nbo, segk = p.seg;
+  size_t cbase = (size_t)bg * nch;
+  int tl = 0;
+  const int T = p.bal ? bal_tiles_per_segment(p, &tl) : 0;
+  if (T > 0) {  // from the balanced plan (every wave computes the same)
+    int first, count;
+    bal_unit(p, T, tl, b, g, first, count);
+    nch = count;
+    cbase = count > 0 ? (size_t)first : 0;  // no compressed block yet: nothing is read
+    segk = T * kStreamTile;
+    nbo = segk / (LSEL / p.d);
+  }
+  const int nchr = nch > 0 ? nch : 1;  // in-bounds clamp of the discarded loads
+  const int slots = p.scs, nfin = p.nfin;
   float* s_m = s_ml;
   float* s_l = s_ml + kMaxChunks * 16;
 
@@ -720,7 +849,7 @@ __global__ __launch_bounds__(64 * kFinWaves) void decode_finish_kernel(DecodePar
     for (int r = 0; r < RPT; ++r) {
       const int j = j0 + tid + NTH * r;
       int cc = j / nbo, jj = j - cc * nbo;
-      if (cc >= nch) cc = nch - 1, jj = 0;  // beyond every sequence: read in bounds, discarded
+      if (cc >= nchr) cc = nchr - 1, jj = 0;  // beyond every sequence: read in bounds, discarded
       const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.sc1 + ((cbase + cc) * slots + jj) * 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q) vv[r][q] = src[q];
@@ -736,7 +865,7 @@ __global__ __launch_bounds__(64 * kFinWaves) void decode_finish_kernel(DecodePar
     const int e = e0 + tid;
     const int ee = e < e1 ? e : e0;
 #pragma unroll
-    for (int q = 0; q < OB; ++q) vo[q] = p.o1[(cbase + min(q, nch - 1)) * 16 * DV + ee];
+    for (int q = 0; q < OB; ++q) vo[q] = p.o1[(cbase + min(q, nchr - 1)) * 16 * DV + ee];
   }
   u32x4_t qf[KT];
   load_q_frags<DK>(p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G) * DK, p.G, lg, lr, qf);
@@ -765,7 +894,7 @@ __global__ __launch_bounds__(64 * kFinWaves) void decode_finish_kernel(DecodePar
     s_ov[idx] = p.sc1[((cbase + (idx >> 4)) * slots + nbo) * 16 + (idx & 15)];
   }
   const int nvis = n_visible(p, b, L);
-  const int nch_b = (nvis + p.seg - 1) / p.seg;
+  const int nch_b = (nvis + segk - 1) / segk;
   const int t = L - 1;
   const int J = t / LSEL;
   lds_barrier();
@@ -1078,12 +1207,35 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   if (wt * kMaxWindow < win_tiles) wt = (win_tiles + kMaxWindow - 1) / kMaxWindow;
   lay.wtiles = (int)wt;
   lay.nwin = (int)((win_tiles + wt - 1) / wt);
+  lay.scs = lay.nbo + 1;
   const size_t BH = (size_t)B * H;
+  size_t nslots = BH * lay.nch;
+  // A plan that needs more than one round of workgroups (a batch longer than
+  // the compute units can stream at once) is balanced on the device instead:
+  // the fixed plan cuts every sequence as if it had the longest length, so in a
+  // ragged batch the long sequences' segments run a second round while the
+  // short ones' slots sit empty.  Balanced segments of T tiles are cut from the
+  // actual lengths so that all of them fill about one round.
+  lay.bal = 0;
+  if ((int64_t)BH * (lay.nch + lay.nwin) > kStreamSlots) {
+    const int64_t tiles_max = (nc + kStreamTile - 1) / kStreamTile;
+    const int64_t tcap = std::min<int64_t>(kBalTiles, (int64_t)(kScStrideMax - 4) * r / kStreamTile);
+    const int64_t tmin = std::max<int64_t>(1, (tiles_max + kMaxChunks - 1) / kMaxChunks);
+    if (tmin <= tcap) {  // the device falls back to the fixed plan when T would exceed tcap
+      lay.bal = 1;
+      lay.tcap = (int)tcap;
+      lay.tmin = (int)tmin;
+      lay.bal_fill = (int)std::max<int64_t>(kStreamSlots - (int64_t)BH * lay.nwin, (int64_t)BH);
+      lay.nslot = lay.bal_fill + (int)BH;
+      lay.scs = std::max(lay.scs, (int)(tcap * kStreamTile / r) + 1);
+      nslots = std::max(nslots, (size_t)lay.nslot);
+    }
+  }
   size_t off = 0;
-  lay.off_m1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
-  lay.off_l1 = off;   off = align256(off + BH * lay.nch * 16 * 4);
-  lay.off_o1 = off;   off = align256(off + BH * lay.nch * 16 * (size_t)DV * 4);
-  lay.off_sc1 = off;  off = align256(off + BH * lay.nch * 16 * (size_t)(lay.nbo + 1) * 4);
+  lay.off_m1 = off;   off = align256(off + nslots * 16 * 4);
+  lay.off_l1 = off;   off = align256(off + nslots * 16 * 4);
+  lay.off_o1 = off;   off = align256(off + nslots * 16 * (size_t)DV * 4);
+  lay.off_sc1 = off;  off = align256(off + nslots * 16 * (size_t)lay.scs * 4);
   lay.off_wpart = off; off = align256(off + BH * lay.nwin * (32 + 16 * (size_t)DV) * 4);
   // finish workgroups (kFinWaves waves, one 32-token step each): one partial
   // each (m, l and the output divided by l); the normalised compressed-branch output;
@@ -1104,8 +1256,8 @@ template <int DK, int DV>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const PhaseEvents* ev) {
   hipEvent_t e0 = ev ? ev->ev[0] : nullptr, e1 = ev ? ev->ev[1] : nullptr;
   hipEvent_t e2 = ev ? ev->ev[2] : nullptr, e3 = ev ? ev->ev[3] : nullptr;
-  hipExtLaunchKernelGGL((decode_stream_kernel<DK, DV>), dim3((unsigned)(p.B * p.H * (p.nch + p.nwin))),
-                        dim3(64 * kStreamWaves), 0, s, e0, e1, 0, p);
+  const unsigned g1 = (unsigned)std::max(p.B * p.H * (p.nch + p.nwin), p.bal ? p.B * p.H * p.nwin + p.nslot : 0);
+  hipExtLaunchKernelGGL((decode_stream_kernel<DK, DV>), dim3(g1), dim3(64 * kStreamWaves), 0, s, e0, e1, 0, p);
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(64 * kFinWaves);

@@ -18,8 +18,9 @@ constexpr int kScStrideMax = 548;     // selection blocks per decode segment + 4
 // Limits of the on-chip tables (checked by the host before any launch).
 constexpr int kMaxCompressed = 32768;                 // compressed blocks per sequence in decode
 constexpr int kMaxChunks = 64;                        // compressed segments per sequence in decode
-constexpr int kSegRows = 640;                         // compressed keys per decode segment, at most
-constexpr int kSegTiles = kSegRows / kStreamTile;     // streamed tiles per segment, at most (LDS fold rows)
+constexpr int kSegRows = 640;                         // compressed keys per decode segment, at most (fixed plan)
+constexpr int kBalTiles = 8;                          // streamed tiles per segment, at most (balanced plan)
+constexpr int kSegTiles = kBalTiles;                  // streamed tiles per segment, at most (LDS fold rows)
 constexpr int kMaxBlocks = 8192;     // selection candidates J+1
 constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query
@@ -55,10 +56,10 @@ struct DecodeParams {
   uint16_t* out;                     // [B, Hq, DV]
   int32_t* sel_out;                  // [B, H, n] or null
   // workspace (contents on entry are irrelevant)
-  float* m1;                         // [B*H, nch, 16]
-  float* l1;                         // [B*H, nch, 16]
-  float* o1;                         // [B*H, nch, 16, DV]
-  float* sc1;                        // [B*H, nch, nbo+1, 16] selection-block scores per head
+  float* m1;                         // [segment slot, 16]: B*H*nch slots (fixed plan) or nslot (balanced)
+  float* l1;                         // [segment slot, 16]
+  float* o1;                         // [segment slot, 16, DV]
+  float* sc1;                        // [segment slot, scs, 16] selection-block scores per head
   float* wpart;                      // [B*H, nwin, 32 + 16*DV] window-workgroup partials (m, l, o)
   float* rpart;                      // [B*H, nfin, 32 + 16*DV] selected partials (m, l, o / l)
   float* ocmp;                       // [B*H, 16, DV] normalised compressed-branch output
@@ -70,11 +71,20 @@ struct DecodeParams {
   int nfin;                          // selection workgroups per (sequence, group)
   int wtiles;                        // 64-token window tiles per window workgroup
   int nwin;                          // window workgroups per (sequence, group)
+  // Balanced plan (bal = 1; ragged batches whose fixed plan needs more than one
+  // round of workgroups): the window workgroups come first, then nslot
+  // compressed slots; the segments hold T tiles, T chosen on the device from
+  // the actual lengths to fill about bal_fill slots, at least tmin; when T
+  // would exceed tcap the device keeps the fixed plan (the launch and the
+  // buffers are sized for either).
+  int bal, nslot, bal_fill, tmin, tcap;
+  int scs;                           // score slots per segment in sc1 (stride): nbo + 1, or the balanced maximum
 };
 
 struct DecodeLayout {
   size_t off_m1, off_l1, off_o1, off_sc1, off_wpart, off_rpart, off_ocmp, off_cnt, total;
   int nch, seg, nbo, nfin, nwin, wtiles;
+  int bal, nslot, bal_fill, tmin, tcap, scs;
 };
 
 // Parameters of the prefill kernels and the compression kernel.

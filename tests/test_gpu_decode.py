@@ -80,6 +80,25 @@ def test_decode_ragged_fine_selection():
     _check_decode(case, out, sel)
 
 
+@pytest.mark.parametrize("batch,L,rmin,seed", [(16, 20000, 1000, 51), (24, 30000, None, 52)],
+                         ids=["ragged_balanced_plan", "long_batch_keeps_fixed_plan"])
+def test_decode_large_batch_plans(batch, L, rmin, seed):
+    """Batches whose fixed segment plan needs more than one round of workgroups.
+    A ragged one is re-planned on the device from the actual lengths (segments
+    of equal tile counts); one whose sequences are all long keeps the fixed plan
+    (balanced segments would not fit one round either).  The GPU compresses the
+    cache; the shortest and longest sequences and a few others are checked
+    against the oracle in every group."""
+    kw = dict(batch=batch, seq_len=L, needles=0)
+    if rmin:
+        kw["ragged_min"] = rmin
+    case = I.generate(I.workload(STD, **kw), seed)
+    out, sel, _ = U.run_decode(case)
+    lens = case.seq_lens
+    bs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, batch // 2, batch - 1})
+    _check_decode(case, out, sel, groups=[(b, g) for b in bs for g in range(case.wl.num_kv_heads)])
+
+
 @pytest.mark.parametrize("L", [1, 5, 31, 32, 33, 64, 65, 1024, 1025, 4096 + 16, 16 * 256 + 32])
 def test_decode_edge_lengths(L):
     """No complete compressed block, exactly one, all candidates selected, chunk edges."""
@@ -112,6 +131,23 @@ def test_decode_repeat_is_bitwise_identical():
     np.testing.assert_array_equal(a[1], b[1])
 
 
+def test_decode_workspace_contents_on_entry_do_not_matter():
+    """One workspace serves calls of other batch sizes and lengths in turn, and
+    whatever it holds on entry (here all bytes 0xFF, or another call's data) does
+    not change the result: every call is checked against the oracle."""
+    a = I.generate(I.workload(STD, batch=2, seq_len=7000), 21)
+    b = I.generate(I.workload(STD, batch=1, seq_len=2500), 22)
+    c = I.generate(I.workload(STD, batch=3, seq_len=5000), 23)
+    size = max(N.nsa_decode_workspace_size(*U.dims_cfg(x), int(np.diff(x.cu_seqlens).max())) for x in (a, b, c))
+    ws = N.new_workspace(size)
+    for i, case in enumerate((a, b, c, a)):
+        if i % 2 == 0:
+            ws.fill_(0xFF)
+        kc, vc, _ = U.oracle_cmp_cache(case)
+        out, sel, _ = U.run_decode(case, kc, vc, ws=ws)
+        _check_decode(case, out, sel)
+
+
 @pytest.mark.parametrize("params,L", [
     # selection blocks of 32 stride units (l'/d = 32 > 16 keys of a wave's row tile), keys of 2 units
     ({"l": 8, "d": 4, "l_sel": 128, "n_sel": 8, "n_local": 1, "w": 256}, 7000),
@@ -119,7 +155,7 @@ def test_decode_repeat_is_bitwise_identical():
     ({"l": 16, "d": 16, "l_sel": 16, "n_sel": 16, "n_local": 2, "w": 128}, 5000),
     # compressed blocks as long as selection blocks (l = l')
     ({"l": 64, "d": 16, "l_sel": 64, "n_sel": 16, "n_local": 2, "w": 512}, 9000),
-    # 16 finish workgroups and more than two window partials (the general merge)
+    # 8 gather workgroups and more than two window partials (the general merge)
     ({"l": 32, "d": 16, "l_sel": 64, "n_sel": 32, "n_local": 2, "w": 2048}, 9000),
 ])
 def test_decode_block_shapes(params, L):
