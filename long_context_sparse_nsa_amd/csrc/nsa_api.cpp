@@ -437,6 +437,7 @@ nsa_status_t decode_launch(const nsa_dims_t* dims, const nsa_config_t* cfg, cons
   p.ocmp = reinterpret_cast<float*>(ws + lay.off_ocmp);
   p.cnt = reinterpret_cast<uint32_t*>(ws + lay.off_cnt);
   p.nfin = lay.nfin;
+  p.finw = lay.finw;
   p.nch = lay.nch;
   p.seg = lay.seg;
   p.nbo = lay.nbo;

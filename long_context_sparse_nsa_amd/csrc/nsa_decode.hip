@@ -712,9 +712,7 @@ __device__ __forceinline__ void merge_store(const Branch<DV>& a, float* buf, flo
     for (int i = 0; i < 4; ++i) buf[(wave * 16 + lr) * (DV + 1) + acc_channel<DV>(lg, i, j)] = fa * a.acc[j][i];
   lds_barrier();
   // four consecutive outputs of one head per thread and pass
-#pragma unroll
-  for (int q = 0; q < 16 * DV / (4 * NTH); ++q) {
-    const int e = 4 * (tid + NTH * q);
+  for (int e = 4 * tid; e < 16 * DV; e += 4 * NTH) {
     const int h = e / DV, ch = e - h * DV;
     float Mh = -INFINITY;
 #pragma unroll
@@ -748,7 +746,9 @@ __device__ __forceinline__ void merge_store(const Branch<DV>& a, float* buf, flo
   }
 }
 
-// Finish: nfin workgroups of kFinWaves waves per (sequence, group).  Every one
+// Finish: nfin workgroups of NWV waves per (sequence, group) (NWV = 4, or 8
+// when 4-wave workgroups would be more than one per compute unit: fewer
+// workgroups then read the group scores again).  Every one
 // of them computes the exact per-head normalisers of the compressed branch,
 // the group scores and the top-n (one wave; identical results in every
 // workgroup, so no exchange is needed); then workgroup k
@@ -759,9 +759,9 @@ __device__ __forceinline__ void merge_store(const Branch<DV>& a, float* buf, flo
 // The last of the nfin workgroups to finish (a device-scope counter, cleared
 // by the streaming pass) merges the selected-branch partials and the window
 // partials and writes out = g_cmp*o_cmp + g_slc*o_slc + g_win*o_win in bf16.
-template <int DK, int DV, int LSEL>
-__global__ __launch_bounds__(64 * kFinWaves) void decode_finish_kernel(DecodeParams p) {
-  constexpr int NWV = kFinWaves, NTH = 64 * NWV;
+template <int DK, int DV, int LSEL, int NWV>
+__global__ __launch_bounds__(64 * NWV) void decode_finish_kernel(DecodeParams p) {
+  constexpr int NTH = 64 * NWV;
   constexpr int KT = DK / 32;
   constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;   // 32-token steps per selection block
   constexpr int WSTRIDE = 32 + 16 * DV;              // window partial (fp32 m, l, o), floats
@@ -1237,16 +1237,31 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   lay.off_o1 = off;   off = align256(off + nslots * 16 * (size_t)DV * 4);
   lay.off_sc1 = off;  off = align256(off + nslots * 16 * (size_t)lay.scs * 4);
   lay.off_wpart = off; off = align256(off + BH * lay.nwin * (32 + 16 * (size_t)DV) * 4);
-  // finish workgroups (kFinWaves waves, one 32-token step each): one partial
-  // each (m, l and the output divided by l); the normalised compressed-branch output;
-  // the arrival counters
+  // finish workgroups (finw waves, one 32-token step each): one partial each
+  // (m, l and the output divided by l); the normalised compressed-branch output;
+  // the arrival counters.  Four waves, or eight when 4-wave workgroups would be
+  // more than one per compute unit (each of them reads all the group scores).
   const int spb = lsel >= 32 ? lsel / 32 : 1;
-  lay.nfin = (n * spb + kFinWaves - 1) / kFinWaves;
+  lay.finw = (int64_t)BH * ((n * spb + 3) / 4) > kStreamSlots ? 8 : 4;
+  lay.nfin = (n * spb + lay.finw - 1) / lay.finw;
   lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
   lay.off_ocmp = off; off = align256(off + BH * 16 * (size_t)DV * 4);
   lay.off_cnt = off; off = align256(off + BH * 4);
   lay.total = off;
   return lay;
+}
+
+template <int DK, int DV, int NWV>
+static hipError_t launch_finish(const DecodeParams& p, hipStream_t s, hipEvent_t e2, hipEvent_t e3) {
+  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(64 * NWV);
+  switch (p.lsel) {
+    case 16: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 16, NWV>), g2, blk, 0, s, e2, e3, 0, p); break;
+    case 32: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 32, NWV>), g2, blk, 0, s, e2, e3, 0, p); break;
+    case 64: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 64, NWV>), g2, blk, 0, s, e2, e3, 0, p); break;
+    case 128: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 128, NWV>), g2, blk, 0, s, e2, e3, 0, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // With events, each kernel is launched with its start / stop events attached
@@ -1260,15 +1275,8 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s, const Ph
   hipExtLaunchKernelGGL((decode_stream_kernel<DK, DV>), dim3(g1), dim3(64 * kStreamWaves), 0, s, e0, e1, 0, p);
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 g2((unsigned)(p.B * p.H * p.nfin)), blk(64 * kFinWaves);
-  switch (p.lsel) {
-    case 16: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 16>), g2, blk, 0, s, e2, e3, 0, p); break;
-    case 32: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 32>), g2, blk, 0, s, e2, e3, 0, p); break;
-    case 64: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 64>), g2, blk, 0, s, e2, e3, 0, p); break;
-    case 128: hipExtLaunchKernelGGL((decode_finish_kernel<DK, DV, 128>), g2, blk, 0, s, e2, e3, 0, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (p.finw == 8) return launch_finish<DK, DV, 8>(p, s, e2, e3);
+  return launch_finish<DK, DV, 4>(p, s, e2, e3);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int DK, int DV, hipStream_t s, const PhaseEvents* ev) {

@@ -26,7 +26,6 @@ constexpr int kMaxSel = 64;          // n_sel
 constexpr int kMaxUnion = 256;       // selected + window blocks per query
 constexpr int kGPad = 16;            // query heads per group, padded to one MFMA tile
 constexpr int kMaxFinish = 16;       // decode selection workgroups per (sequence, group)
-constexpr int kFinWaves = 4;         // waves per decode selection workgroup
 constexpr int kMaxWindow = 16;       // decode window workgroups per (sequence, group)
 
 // Profiling hook: with a phase-clock buffer, thread 0 of every workgroup of the
@@ -69,6 +68,7 @@ struct DecodeParams {
   int seg;                           // compressed keys per segment (multiple of 64 and of lsel/d)
   int nbo;                           // selection blocks owned by one segment = seg*d/lsel
   int nfin;                          // selection workgroups per (sequence, group)
+  int finw;                          // waves per selection workgroup (4 or 8)
   int wtiles;                        // 64-token window tiles per window workgroup
   int nwin;                          // window workgroups per (sequence, group)
   // Balanced plan (bal = 1; ragged batches whose fixed plan needs more than one
@@ -83,7 +83,7 @@ struct DecodeParams {
 
 struct DecodeLayout {
   size_t off_m1, off_l1, off_o1, off_sc1, off_wpart, off_rpart, off_ocmp, off_cnt, total;
-  int nch, seg, nbo, nfin, nwin, wtiles;
+  int nch, seg, nbo, nfin, nwin, wtiles, finw;
   int bal, nslot, bal_fill, tmin, tcap, scs;
 };
 
