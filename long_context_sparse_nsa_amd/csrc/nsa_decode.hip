@@ -211,6 +211,22 @@ __device__ __forceinline__ void st4_coherent(rsrc_t r, uint32_t off, f32x4_t v) 
 __device__ __forceinline__ void st1_coherent(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kCoherent);
 }
+// The selected-branch partials keep o / l as fp16: weighted averages of bf16
+// values, so fp16's 11-bit significand adds about 2^-12 relative error, well
+// below the bf16 rounding of the result, at half the bytes of fp32.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
+__device__ __forceinline__ f32x2_t unpack_f16x2(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+}
+__device__ __forceinline__ void st8_coherent(rsrc_t r, uint32_t off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kCoherent);
+}
+__device__ __forceinline__ u32x4_t ld16_coherent(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent);
+}
 __device__ __forceinline__ void st_shared_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -690,9 +706,10 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
 }
 
 // Merges the NWV waves' selected-branch states into one partial and stores it
-// device-coherently at byte offset `off` of r: m[16], l[16] and the output
-// divided by l, o[16][DV] (the last workgroup weights it by its share of the
-// total).  buf holds NWV*16*(DV+1) floats, st 2*NWV*16.
+// device-coherently at byte offset `off` of r: m[16], l[16] (fp32) and the
+// output divided by l, o[16][DV] (fp16, from byte 128; the last workgroup
+// weights it by its share of the total).  buf holds NWV*16*(DV+1) floats,
+// st 2*NWV*16.
 template <int DV, int NWV>
 __device__ __forceinline__ void merge_store(const Branch<DV>& a, float* buf, float* st, rsrc_t r, uint32_t off) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
@@ -729,7 +746,8 @@ __device__ __forceinline__ void merge_store(const Branch<DV>& a, float* buf, flo
     for (int w = 0; w < NWV; ++w)
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] += buf[(w * 16 + h) * (DV + 1) + ch + i];
-    st4_coherent(r, off + (uint32_t)(32 + e) * 4, v * inv);
+    v *= inv;
+    st8_coherent(r, off + 128 + (uint32_t)e * 2, u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])});
   }
   if (tid < 16) {
     float Mh = -INFINITY;
@@ -765,7 +783,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_finish_kernel(DecodeParams p)
   constexpr int KT = DK / 32;
   constexpr int SPB = LSEL >= 32 ? LSEL / 32 : 1;   // 32-token steps per selection block
   constexpr int WSTRIDE = 32 + 16 * DV;              // window partial (fp32 m, l, o), floats
-  constexpr int RSTRIDE = 32 + 16 * DV;              // selected partial (m, l, o / l), floats
+  constexpr int RSTRIDE = 32 + 8 * DV;               // selected partial (m, l fp32; o / l fp16), in floats
   constexpr int RPT = 4;                             // candidate blocks per thread and load round
   constexpr int OB = 8;                              // segments per compressed-output load batch
   // The candidates' scores (until the top-n) share their LDS with the wave-merge
@@ -1043,16 +1061,15 @@ __global__ __launch_bounds__(64 * NWV) void decode_finish_kernel(DecodeParams p)
   constexpr int FF = 8, FW = 2;                // fast-path partial counts
   const bool fast = nfin <= FF && nwin <= FW;  // workgroup-uniform
   const int e8 = 8 * (tid < NO ? tid : 0), h8 = e8 / DV;
-  f32x4_t ro8[FF][2], rw8[FW][2], rc8[2];
+  u32x4_t ro8[FF];
+  f32x4_t rw8[FW][2], rc8[2];
   float fm[FF], fl[FF], wm[FW], wl[FW];
   if (fast) {  // every load of the merge in flight at once
     rc8[0] = ld4_coherent(ro, (uint32_t)e8 * 4);
     rc8[1] = ld4_coherent(ro, (uint32_t)(e8 + 4) * 4);
 #pragma unroll
     for (int k = 0; k < FF; ++k)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        ro8[k][u] = k < nsp ? ld4_coherent(rr, (uint32_t)(k * RSTRIDE + 32 + e8 + 4 * u) * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      ro8[k] = k < nsp ? ld16_coherent(rr, (uint32_t)(k * RSTRIDE * 4 + 128 + e8 * 2)) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < FW; ++k)
 #pragma unroll
@@ -1123,8 +1140,9 @@ __global__ __launch_bounds__(64 * NWV) void decode_finish_kernel(DecodeParams p)
         const float a = k < nsp ? s_pf[k][h8] : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          os[i] += a * ro8[k][0][i];
-          os[4 + i] += a * ro8[k][1][i];
+          const f32x2_t x = unpack_f16x2(ro8[k][i]);
+          os[2 * i] += a * x[0];
+          os[2 * i + 1] += a * x[1];
         }
       }
 #pragma unroll
@@ -1143,13 +1161,13 @@ __global__ __launch_bounds__(64 * NWV) void decode_finish_kernel(DecodeParams p)
       }
     } else {
       for (int k = 0; k < nsp; ++k) {
-        const f32x4_t x0 = ld4_coherent(rr, (uint32_t)(k * RSTRIDE + 32 + e8) * 4);
-        const f32x4_t x1 = ld4_coherent(rr, (uint32_t)(k * RSTRIDE + 32 + e8 + 4) * 4);
+        const u32x4_t x = ld16_coherent(rr, (uint32_t)(k * RSTRIDE * 4 + 128 + e8 * 2));
         const float a = s_pf[k][h8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          os[i] += a * x0[i];
-          os[4 + i] += a * x1[i];
+          const f32x2_t y = unpack_f16x2(x[i]);
+          os[2 * i] += a * y[0];
+          os[2 * i + 1] += a * y[1];
         }
       }
       for (int k = 0; k < nwin; ++k) {
@@ -1244,7 +1262,7 @@ DecodeLayout decode_layout(int B, int H, int DV, int l, int d, int lsel, int n, 
   const int spb = lsel >= 32 ? lsel / 32 : 1;
   lay.finw = (int64_t)BH * ((n * spb + 3) / 4) > kStreamSlots ? 8 : 4;
   lay.nfin = (n * spb + lay.finw - 1) / lay.finw;
-  lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 16 * (size_t)DV) * 4);
+  lay.off_rpart = off; off = align256(off + BH * lay.nfin * (32 + 8 * (size_t)DV) * 4);
   lay.off_ocmp = off; off = align256(off + BH * 16 * (size_t)DV * 4);
   lay.off_cnt = off; off = align256(off + BH * 4);
   lay.total = off;

@@ -60,7 +60,7 @@ struct DecodeParams {
   float* o1;                         // [segment slot, 16, DV]
   float* sc1;                        // [segment slot, scs, 16] selection-block scores per head
   float* wpart;                      // [B*H, nwin, 32 + 16*DV] window-workgroup partials (m, l, o)
-  float* rpart;                      // [B*H, nfin, 32 + 16*DV] selected partials (m, l, o / l)
+  float* rpart;                      // [B*H, nfin, 32 + 8*DV] selected partials (m, l fp32; o / l fp16)
   float* ocmp;                       // [B*H, 16, DV] normalised compressed-branch output
   uint32_t* cnt;                     // [B*H] selection-workgroup arrival counters
   uint64_t* clk;                     // phase clock (profiling) or null
