@@ -118,6 +118,20 @@ def test_decode_small_heads_group4():
     _check_decode(case, out, sel)
 
 
+def test_decode_small_heads_many_units():
+    """d_k = d_v = 64, 4 query heads per KV head, 64 ragged sequences x 2 KV heads:
+    128 units, so the streaming pass takes the balanced plan and the selection
+    kernel its 8-wave workgroups (one 32-token step per wave, 16 heads x 64
+    channels merged by 512 threads).  Sampled sequences in every group."""
+    wl = I.workload(STD, batch=64, seq_len=2600, num_q_heads=8, num_kv_heads=2, d_k=64, d_v=64,
+                    ragged_min=700, needles=0, params={"n_sel": 16, "n_local": 2, "w": 512})
+    case = I.generate(wl, 61)
+    out, sel, _ = U.run_decode(case)
+    lens = case.seq_lens
+    bs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 31, 63})
+    _check_decode(case, out, sel, groups=[(b, g) for b in bs for g in range(2)])
+
+
 def test_decode_repeat_is_bitwise_identical():
     """Same inputs twice through the same workspace: identical bits (no atomics in sums)."""
     case = I.generate(I.workload(STD, batch=2, seq_len=7000), 7)
