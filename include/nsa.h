@@ -191,7 +191,7 @@ nsa_status_t nsa_decode_fwd(const nsa_dims_t* dims, const nsa_config_t* cfg,
  *
  * A step whose workspace (nsa_decode_workspace_size) exceeds 32 MiB returns
  * NSA_ERROR_UNSUPPORTED with the sizes in nsa_last_error(); the 64k / batch 8,
- * 128k / batch 4 and ragged 16-sequence workloads need 6.5, 5.3 and 17.4 MiB.
+ * 128k / batch 4 and ragged 16-sequence workloads need 5.5, 4.5 and 19.6 MiB.
  * Every call on a GPU shares that GPU's array and nothing in it needs to start
  * at a particular value, but calls that overlap in time on one GPU (other
  * streams, other threads) race on it: order them on one stream.
