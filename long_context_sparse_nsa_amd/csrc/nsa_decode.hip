@@ -10,7 +10,11 @@
 //      per-head probabilities folded onto selection blocks;
 //    - window workgroups: the window branch, which does not depend on the
 //      selection, streamed the same way over the window's raw tokens.
-// 2. decode_finish_kernel: several workgroups per (sequence, group), each
+//    The segments are planned on the host from the longest length, or, when
+//    that plan needs more workgroups than compute units (a ragged batch of
+//    many long slots), on the device from the actual lengths (balanced plan).
+// 2. decode_finish_kernel: several workgroups of 4 waves (8 when 4-wave ones
+//    would be more than one per compute unit) per (sequence, group), each
 //    computing the exact per-head normalisers from the segment statistics, the
 //    group scores and the top-n (one wave), a slice of the compressed-branch
 //    output, and its share of the selected blocks (one 32-token step per
