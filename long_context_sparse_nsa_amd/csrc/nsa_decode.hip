@@ -426,7 +426,8 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
   constexpr int PSTRIDE = 32 + 16 * DV;
   constexpr float kLazy = 8.0f, kNegBig = -1e30f;
   __shared__ float s_o[NW][16][DV + 1];
-  __shared__ __attribute__((aligned(16))) float s_fw[kSegTiles][NW][16][16];  // fold rows [tile][wave][head][block row]
+  constexpr int FWP = 20;  // each head's fold rows padded: distinct LDS banks for the 16 heads
+  __shared__ __attribute__((aligned(16))) float s_fw[kSegTiles][NW][16][FWP];  // fold rows [tile][wave][head][block row]
   __shared__ float s_fm[kSegTiles][NW][16];  // the reference each tile's fold rows are relative to
   __shared__ float s_l[NW][16], s_m[NW][16], s_fac[NW][16];
 
@@ -690,20 +691,52 @@ __global__ __launch_bounds__(64 * kStreamWaves, 1) void decode_stream_kernel(Dec
     const float invq = 1.0f / (float)qd;
     float* SC = p.sc1 + (size_t)slot * p.scs * 16;  // [slot][head]
     const float(*fm)[16] = reinterpret_cast<const float(*)[16]>(&s_fm[0][0][0]);        // [u][head]
-    const float(*fw)[16][16] = reinterpret_cast<const float(*)[16][16]>(&s_fw[0][0][0][0]);  // [u][head][row]
-    for (int e = tid; e < 16 * slots; e += NTH) {  // head e mod 16 = lr
-      const int J = jseg0 + (e >> 4);
-      // wave-tiles u = NW*i + w start at key r0 + 16u; their keys [K, K + 15 + qd - 1]
-      // (stride units) reach block J iff K <= J*rd + rd - 1 and K + 15 + qd - 1 >= J*rd
-      const int klo = J * rd - (15 + qd - 1) - (int)r0, khi = J * rd + rd - 1 - (int)r0;
-      const int ulo = klo > 0 ? (klo + 15) >> 4 : 0;
-      const int uhi = khi >= 0 ? min(khi >> 4, NW * nt - 1) : -1;
-      float v = 0.f;
-      for (int u = ulo; u <= uhi; ++u) {
-        const int row = J - (((int)r0 + 16 * u) >> rsh);
-        if (row >= 0 && row < 16) v += fm[u][lr] * fw[u][lr][row];
+    const float(*fw)[16][FWP] = reinterpret_cast<const float(*)[16][FWP]>(&s_fw[0][0][0][0]);  // [u][head][row]
+    // With l <= l' (qd <= rd) and rd <= 16, every wave-tile starts on a block
+    // boundary, own = 16/rd blocks apart, and at most two wave-tiles reach a
+    // block: slot s = u*own + k takes row k of wave-tile u and row k + own of
+    // wave-tile u - 1 (rows past the keys' reach are exact zeros).  Four entries
+    // per thread and pass, all their reads issued before any is used; the two
+    // terms are added in wave-tile order.
+    if (rd <= 16) {
+      const int osh = 4 - rsh, own = 1 << osh, nu = NW * nt;
+      constexpr int EB = 4;
+      for (int e0 = tid; e0 < 16 * slots; e0 += EB * NTH) {
+        float x0[EB], x1[EB];
+#pragma unroll
+        for (int q = 0; q < EB; ++q) {
+          const int e = e0 + q * NTH;
+          const int sl = e >> 4, u = sl >> osh, k = sl & (own - 1);
+          const bool in = e < 16 * slots;
+          const bool ok0 = in && u < nu;
+          const bool ok1 = in && u >= 1 && u - 1 < nu && k + own < 16;
+          const int ua = ok0 ? u : 0, ka = ok0 ? k : 0, ub = ok1 ? u - 1 : 0, kb = ok1 ? k + own : 0;
+          const float a = fm[ua][lr] * fw[ua][lr][ka];
+          const float c = fm[ub][lr] * fw[ub][lr][kb];
+          x0[q] = ok0 ? a : 0.f;
+          x1[q] = ok1 ? c : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < EB; ++q) {
+          const int e = e0 + q * NTH;
+          if (e < 16 * slots) SC[e] = (x1[q] + x0[q]) * invq;
+        }
       }
-      SC[e] = v * invq;
+    } else {
+      for (int e = tid; e < 16 * slots; e += NTH) {  // head e mod 16 = lr
+        const int J = jseg0 + (e >> 4);
+        // wave-tiles u = NW*i + w start at key r0 + 16u; their keys [K, K + 15 + qd - 1]
+        // (stride units) reach block J iff K <= J*rd + rd - 1 and K + 15 + qd - 1 >= J*rd
+        const int klo = J * rd - (15 + qd - 1) - (int)r0, khi = J * rd + rd - 1 - (int)r0;
+        const int ulo = klo > 0 ? (klo + 15) >> 4 : 0;
+        const int uhi = khi >= 0 ? min(khi >> 4, NW * nt - 1) : -1;
+        float v = 0.f;
+        for (int u = ulo; u <= uhi; ++u) {
+          const int row = J - (((int)r0 + 16 * u) >> rsh);
+          if (row >= 0 && row < 16) v += fm[u][lr] * fw[u][lr][row];
+        }
+        SC[e] = v * invq;
+      }
     }
   }
   clk_stamp(p.clk, 2);
