@@ -727,16 +727,29 @@ __global__ __launch_bounds__(64 * NW, 1) void dsa_attn_kernel(DsaParams p) {
     dst[1] = lsum;
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  uint16_t* oh = reinterpret_cast<uint16_t*>(dst + kPartOut);
+  // The output rows go through LDS (the tiles are dead once every wave is past
+  // its value products), so that each store writes one head's 1 KB row:
+  // row 16*wave + lr at byte kOutRow*(16*wave + lr), padded so that the 16 rows
+  // a wave writes at once fall on different LDS banks.
+  constexpr int kOutRow = 1024 + 16;
+  __syncthreads();
+  char* so = &s_buf[0][0];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // 8 consecutive channels 128*db + 8*(4lg+i) .. in one 16-byte store
+    for (int i = 0; i < 4; ++i) {  // 8 consecutive channels 128*db + 8*(4lg+i) ..
       const f32x4_t* a = &acc[db][0];
-      *reinterpret_cast<u32x4_t*>(oh + 128 * db + acc_channel<128>(lg, i, 0)) =
+      *reinterpret_cast<u32x4_t*>(so + (16 * wave + lr) * kOutRow + 2 * (128 * db + acc_channel<128>(lg, i, 0))) =
           u32x4_t{pack_f16x2(a[0][i] * inv, a[1][i] * inv), pack_f16x2(a[2][i] * inv, a[3][i] * inv),
                   pack_f16x2(a[4][i] * inv, a[5][i] * inv), pack_f16x2(a[6][i] * inv, a[7][i] * inv)};
     }
+  lds_barrier();  // this wave's rows (each wave stores only the rows it wrote)
+  float* wdst = part + (size_t)(16 * wave) * kPartStride;
+#pragma unroll
+  for (int hh = 0; hh < 16; ++hh) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(so + (16 * wave + hh) * kOutRow + 16 * lane);
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(wdst + (size_t)hh * kPartStride + kPartOut) + 8 * lane) = x;
+  }
   clk_stamp(clk, 4);
 }
 
