@@ -480,6 +480,20 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
           L > 0.f ? (mref[q] + __builtin_log2f(L)) * kLn2 : -INFINITY;
   }
 
+  // The value products of the second pass take the bf16 p the fold uses: acc
+  // (g_win o_win so far) is divided by g_cmp of head lr first and multiplied by
+  // it afterwards, so acc = g_win o_win + g_cmp o_cmp.  A head whose g_cmp is
+  // zero or below 2^-60 takes no compressed-branch values (its contribution is
+  // below any bf16 output's resolution).
+  bool gz[kWaveQ];
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    gz[q] = !(gC[q] >= 0x1p-60f);
+    const float r = gz[q] ? 1.0f : 1.0f / gC[q];
+#pragma unroll
+    for (int j = 0; j < VC; ++j) acc[q][j] *= r;
+  }
+
   // ---- C2: normalised p; acc += g_cmp p.Vc; fold p onto selection blocks.
   // Fold: key i covers stride units [i, i+qd), block j covers [j*rd, (j+1)*rd).
   // F[head][block] = sum over a 32-key step of p * overlap (the overlap counts are
@@ -519,16 +533,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
         float a[2][4];
         mask_range(hh ? s1[q] : s0[q], i0, -1, nvq[q] - 1, lg, a);
         const float nb = -bias[q];
-        float ga[2][4], ra[2][4];
+        float ra[2][4];
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a[mm][i] = __builtin_amdgcn_exp2f(fmaf(a[mm][i], sc, nb));
-            ga[mm][i] = a[mm][i] * gC[q];
-          }
-        pg[q] = pack_probs(ga[0], ga[1]);
+          for (int i = 0; i < 4; ++i) a[mm][i] = __builtin_amdgcn_exp2f(fmaf(a[mm][i], sc, nb));
         ph[q] = pack_probs(a[0], a[1]);
+        pg[q] = gz[q] ? u32x4_t{0u, 0u, 0u, 0u} : ph[q];  // B operand: this lane's elements are head lr's
         // rounding residual, so that hi + lo carries p to about 16 bits
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
@@ -558,6 +569,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_cmp_win_kernel(PrefillParams p
         }
       }
     }
+  }
+
+#pragma unroll
+  for (int q = 0; q < kWaveQ; ++q) {
+    const float f = gz[q] ? 1.0f : gC[q];
+#pragma unroll
+    for (int j = 0; j < VC; ++j) acc[q][j] *= f;
   }
 
   // ---- top-n per position
